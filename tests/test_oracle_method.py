@@ -1,0 +1,379 @@
+"""Pins of the oracle's method steps against closed forms, independent libraries (torch
+rms_norm / scaled_dot_product_attention in float64), exact integer arithmetic, brute force,
+and invariants of the method.  CPU only."""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import qsa as oq
+from oracle.numerics import bf16_bits_to_f64, f64_to_bf16_bits, round_bf16
+from sparse_attention_qsa_amd.workloads import make_workload, rotary_table
+from tests.oracle_io import oracle_step, to_np
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+RNG = np.random.default_rng(12345)
+
+
+def rand_bf16(shape, std=1.0):
+    return round_bf16(RNG.standard_normal(shape) * std)
+
+
+def ulp_diff_bf16(a, b):
+    ia = f64_to_bf16_bits(a).astype(np.int64)
+    ib = f64_to_bf16_bits(b).astype(np.int64)
+    return np.abs(ia - ib)
+
+
+# ----------------------------------------------------------------------------- sums
+
+
+def test_halving_sum_is_exact_on_integers_and_has_the_stated_order():
+    x = RNG.integers(-1000, 1000, size=(50, 128)).astype(np.float64)
+    assert np.array_equal(oq.halving_sum(x), x.sum(axis=1))
+    # Order pin: big terms at dims 0 and 64 cancel only if they meet early.
+    v = np.zeros(128)
+    v[0], v[1], v[64] = 2.0 ** 60, 1.0, -(2.0 ** 60)
+    # pairs: (0,1) -> 2^60 (1 is lost); the halvings then bring dim 64's pair onto it -> 0.
+    assert oq.halving_sum(v[None])[0] == 0.0
+
+
+# ----------------------------------------------------------------------------- RMSNorm
+
+
+def test_rmsnorm_constant_vector_closed_form():
+    w = rand_bf16(128, std=0.1)
+    eps = 1e-6
+    for a in [0.75, -3.0, 1.0 / 1024, 17.5]:
+        x = np.full((1, 128), a)
+        y = oq.gemma_rmsnorm(x, w, eps)[0]
+        expect = a / np.sqrt(a * a + float(np.float32(eps))) * (1.0 + w)
+        assert ulp_diff_bf16(y, expect).max() <= 1
+
+
+def test_rmsnorm_zero_weight_gives_unit_rms():
+    x = rand_bf16((64, 128))
+    y = oq.gemma_rmsnorm(x, np.zeros(128), 1e-6)
+    rms = np.sqrt((y * y).mean(axis=1))
+    assert np.all(np.abs(rms - 1.0) < 2 ** -7)
+
+
+def test_rmsnorm_matches_torch_rms_norm_float64():
+    x = rand_bf16((4000, 128))
+    w = rand_bf16(128, std=0.1)
+    eps = 1e-6
+    ref = F.rms_norm(torch.from_numpy(x), (128,), weight=torch.from_numpy(1.0 + w),
+                     eps=float(np.float32(eps))).numpy()
+    mine = oq.gemma_rmsnorm(x, w, eps)
+    d = ulp_diff_bf16(mine, ref)
+    assert d.max() <= 1            # only the last bit of a near-tie may differ
+    assert (d == 0).mean() > 0.999
+
+
+# ----------------------------------------------------------------------------- RoPE
+
+
+def test_rotary_table_is_on_the_unit_circle():
+    t = rotary_table(4096).numpy().astype(np.float64)
+    assert np.abs(t[:, :32] ** 2 + t[:, 32:] ** 2 - 1).max() < 1e-6
+    assert np.all(t[0, :32] == 1.0) and np.all(t[0, 32:] == 0.0)
+
+
+def test_rope_position_zero_is_identity_and_pass_through_dims_untouched():
+    tab = rotary_table(4096).numpy()
+    y = rand_bf16((10, 128))
+    cos, sin = oq.gather_cos_sin(tab, np.zeros(10, np.int64))
+    assert np.array_equal(oq.neox_rope(y, cos, sin), y)
+    cos, sin = oq.gather_cos_sin(tab, np.arange(10) * 97)
+    assert np.array_equal(oq.neox_rope(y, cos, sin)[:, 64:], y[:, 64:])
+
+
+def test_rope_is_a_rotation_of_pairs_i_and_i_plus_32():
+    tab = rotary_table(8192).numpy()
+    y = rand_bf16((200, 128))
+    pos = RNG.integers(0, 8000, 200)
+    cos, sin = oq.gather_cos_sin(tab, pos)
+    z = oq.neox_rope(y, cos, sin)
+    # Complex form: (a + i b) * e^{i theta}; norms of the pairs are preserved.
+    a = y[:, :32] + 1j * y[:, 32:64]
+    rot = a * (cos + 1j * sin)
+    assert np.abs(z[:, :32] - rot.real).max() < 2 ** -7 * np.abs(rot.real).max()
+    assert np.abs(z[:, 32:64] - rot.imag).max() < 2 ** -7 * np.abs(rot.imag).max()
+    assert np.allclose(np.abs(a), np.abs(z[:, :32] + 1j * z[:, 32:64]), rtol=2 ** -7)
+
+
+def test_rope_inner_product_depends_only_on_relative_position():
+    tab = rotary_table(8192).numpy()
+    q = rand_bf16((1, 128))
+    k = rand_bf16((1, 128))
+
+    def rot(v, p):
+        c, s = oq.gather_cos_sin(tab, np.array([p]))
+        return oq.neox_rope(v, c, s)[0]
+    base = rot(q, 300) @ rot(k, 100)
+    for m, n in [(1200, 1000), (5200, 5000), (200, 0)]:
+        assert abs(rot(q, m) @ rot(k, n) - base) < 0.05 * (np.abs(q[0]) @ np.abs(k[0]))
+
+
+def test_mrope_sections_and_equal_axes_reduce_to_1d():
+    axis = oq.mrope_axis_of_pair((12, 10, 10))
+    assert np.bincount(axis, minlength=3).tolist() == [12, 10, 10]
+    tab = rotary_table(8192).numpy()
+    y = rand_bf16((30, 128))
+    p = RNG.integers(0, 8000, 30)
+    c1, s1 = oq.gather_cos_sin(tab, p)
+    c3, s3 = oq.gather_cos_sin(tab, np.stack([p, p, p], 1), (12, 10, 10))
+    assert np.array_equal(oq.neox_rope(y, c1, s1), oq.neox_rope(y, c3, s3))
+    # Moving only the H position changes exactly the H frequencies.
+    trip = np.stack([p, p + 7, p], 1)
+    c3, s3 = oq.gather_cos_sin(tab, trip, (12, 10, 10))
+    changed = np.any(c3 != c1, axis=0)
+    assert np.array_equal(changed, axis == 1)
+
+
+# ----------------------------------------------------------------------------- compress
+
+
+def _one_request_compress(raw, chunks, c, mrope=None, trip=None, ckv_pages=64):
+    """Run compress_step over `raw` [L, 128] in the given chunks; returns the final state."""
+    L = raw.shape[0]
+    S, Pc = 16, 16
+    tab = rotary_table(L + 256).numpy()
+    w = f64_to_bf16_bits(rand_bf16(128, std=0.1)) if not hasattr(_one_request_compress, "w") \
+        else _one_request_compress.w
+    _one_request_compress.w = w
+    state = oq.CompressState(ring=np.zeros((1, S, 128), np.uint16),
+                             ring_pos=np.zeros((1, S, 3), np.int64) if mrope else None,
+                             ckv=np.zeros((ckv_pages, Pc, 128), np.uint16))
+    table = np.arange(ckv_pages, dtype=np.int32)[::-1].copy()[None, :]
+    start = 0
+    raw_bits = f64_to_bf16_bits(raw)
+    for n in chunks:
+        end = start + n
+        pos = trip[start:end] if mrope else np.arange(start, end)
+        state = oq.compress_step(np.array([0, n]), np.array([end]), raw_bits[start:end], pos,
+                                 mrope, tab, w, 1e-6, np.array([0]), table, c, "bf16", state)
+        start = end
+    assert start == L
+    return state
+
+
+@pytest.mark.parametrize("c", [4, 8])
+def test_compress_cache_bytes_do_not_depend_on_chunking(c):
+    L = 203
+    raw = rand_bf16((L, 128))
+    whole = _one_request_compress(raw, [L], c)
+    for chunks in ([1] * L, [5, 3, 1, 1, 7, 16, 2, 100, 68], [c - 1, 1, L - c]):
+        part = _one_request_compress(raw, chunks, c)
+        assert np.array_equal(part.ckv, whole.ckv)
+        assert np.array_equal(part.ring, whole.ring)
+    # The ring holds the last 16 raw keys in slots t % 16.
+    bits = f64_to_bf16_bits(raw)
+    for t in range(L - 16, L):
+        assert np.array_equal(whole.ring[0, t % 16], bits[t])
+
+
+def test_compress_mrope_chunking_invariance_uses_first_token_triples():
+    L, c = 77, 8
+    raw = rand_bf16((L, 128))
+    t = np.arange(L)
+    trip = np.stack([t, t + RNG.integers(0, 64, L), t + RNG.integers(0, 64, L)], 1)
+    whole = _one_request_compress(raw, [L], c, (12, 10, 10), trip)
+    part = _one_request_compress(raw, [3, 4, 4, 4, 4, 58], c, (12, 10, 10), trip)
+    assert np.array_equal(part.ckv, whole.ckv)
+    assert np.array_equal(part.ring_pos, whole.ring_pos)
+
+
+def test_compress_of_identical_group_members_is_that_key_normalised_and_rotated():
+    c, L = 4, 32
+    keys = rand_bf16((L // c, 128))
+    raw = np.repeat(keys, c, axis=0)
+    st = _one_request_compress(raw, [L], c)
+    w = bf16_bits_to_f64(_one_request_compress.w)
+    tab = rotary_table(L + 256).numpy()
+    cos, sin = oq.gather_cos_sin(tab, np.arange(0, L, c))
+    expect = oq.neox_rope(oq.gemma_rmsnorm(keys, w, 1e-6), cos, sin)
+    table = np.arange(64)[::-1]
+    got = np.stack([bf16_bits_to_f64(st.ckv[table[g // 16], g % 16]) for g in range(L // c)])
+    assert np.array_equal(got, expect)
+
+
+# ----------------------------------------------------------------------------- scores / select
+
+
+def test_scores_are_exact_on_small_integers():
+    Hi, n = 4, 300
+    q = RNG.integers(-8, 9, size=(Hi, 128)).astype(np.float64)
+    k = RNG.integers(-8, 9, size=(n, 128)).astype(np.float64)
+    exact = (k.astype(np.int64) @ q.astype(np.int64).T).sum(axis=1)
+    assert np.array_equal(oq.index_scores(q, k), exact.astype(np.float64))
+
+
+def test_scores_one_head_is_a_dot_product():
+    q = rand_bf16((1, 128))
+    k = rand_bf16((500, 128))
+    assert np.allclose(oq.index_scores(q, k), k @ q[0], rtol=1e-13, atol=1e-12)
+
+
+def test_select_matches_brute_force_sort_with_ties():
+    for trial in range(20):
+        n = int(RNG.integers(1, 400))
+        kb = int(RNG.integers(1, 64))
+        s = np.round(RNG.standard_normal(n), 1)      # many exact ties
+        brute = sorted(range(n), key=lambda j: (-s[j], j))[:kb]
+        assert np.array_equal(oq.select_blocks(s, kb), np.sort(brute))
+
+
+def test_select_all_tied_takes_lowest_indices():
+    assert np.array_equal(oq.select_blocks(np.zeros(100), 7), np.arange(7))
+
+
+# ----------------------------------------------------------------------------- expand
+
+
+def test_expand_closed_form_and_golden_tiny_decode_counts():
+    with open(os.path.join(GOLDEN, "tiny_decode_counts.json")) as f:
+        gold = json.load(f)
+    c, budget = gold["compress_ratio"], gold["budget"]
+    assert budget + c - 1 == gold["output_width"]
+    for row in gold["rows"]:
+        p = row["p"]
+        vis = (p + 1) // c
+        assert vis == row["visible_blocks"]
+        blocks = np.arange(min(vis, budget // c)) * 3 % vis    # any kb distinct blocks
+        blocks = np.unique(blocks)
+        if len(blocks) < min(vis, budget // c):
+            blocks = np.arange(min(vis, budget // c))
+        packed = oq.expand_row(np.sort(blocks), p, c, budget)
+        W = gold["output_width"]
+        cnt = packed[W]
+        assert cnt == row["count"]
+        assert np.all(np.diff(packed[:cnt]) > 0) and packed[cnt - 1] <= p
+        assert np.all(packed[cnt:W] == -1)
+        assert np.array_equal(packed[cnt - row["tail"]:cnt], np.arange(vis * c, p + 1))
+
+
+# ----------------------------------------------------------------------------- attention
+
+
+def _dense_reference(q, K, V, scale):
+    """torch SDPA (float64) of one row's heads over contiguous K/V [n, Hkv, D]."""
+    Hq, Hkv = q.shape[0], K.shape[1]
+    G = Hq // Hkv
+    qt = torch.from_numpy(q)[:, None, :]                      # [Hq, 1, D]
+    kt = torch.from_numpy(K).permute(1, 0, 2).repeat_interleave(G, 0)
+    vt = torch.from_numpy(V).permute(1, 0, 2).repeat_interleave(G, 0)
+    return F.scaled_dot_product_attention(qt, kt, vt, scale=scale)[:, 0, :].numpy()
+
+
+def _tiny_attention_case(L=100, Hq=8, Hkv=2, P=16, seed=5):
+    rng = np.random.default_rng(seed)
+    pages_needed = (L + P - 1) // P
+    pages = pages_needed + 3
+    perm = rng.permutation(pages)[:pages_needed].astype(np.int32)
+    kv = round_bf16(rng.standard_normal((pages, Hkv, P, 256)))
+    bt = perm[None, :]
+    q = round_bf16(rng.standard_normal((3, Hq, 128)))
+    K = np.stack([kv[perm[t // P], :, t % P, :128] for t in range(L)])
+    V = np.stack([kv[perm[t // P], :, t % P, 128:] for t in range(L)])
+    return kv, bt, q, K, V
+
+
+def test_sparse_gqa_dense_selection_matches_torch_sdpa():
+    L, W = 100, 120
+    kv, bt, q, K, V = _tiny_attention_case(L)
+    ps = [99, 50, 0]
+    packed = np.full((3, W + 1), -1, np.int32)
+    for i, p in enumerate(ps):
+        packed[i, :p + 1] = np.arange(p + 1)
+        packed[i, W] = p + 1
+    out = oq.sparse_gqa(f64_to_bf16_bits(q), f64_to_bf16_bits(kv), bt, np.zeros(3, np.int32),
+                        packed)
+    for i, p in enumerate(ps):
+        ref = _dense_reference(q[i], K[:p + 1], V[:p + 1], 128 ** -0.5)
+        assert np.abs(out[i] - ref).max() < 1e-12
+
+
+def test_sparse_gqa_masks_invalid_entries_and_empty_rows():
+    L, W = 100, 40
+    kv, bt, q, K, V = _tiny_attention_case(L)
+    sel = np.array([3, 17, 40, 41, 99])
+    packed = np.full((3, W + 1), -1, np.int32)
+    # row 0: the selection; row 1: same with -1 and out-of-table entries mixed in;
+    # row 2: count 0.
+    packed[0, :5] = sel
+    packed[0, W] = 5
+    packed[1, :9] = [3, -1, 17, 40, 5000, 41, -7, 99, -1]
+    packed[1, W] = 9
+    packed[2, W] = 0
+    kvb = f64_to_bf16_bits(kv)
+    out = oq.sparse_gqa(f64_to_bf16_bits(q[[0, 0, 0]]), kvb, bt, np.zeros(3, np.int32), packed)
+    ref = _dense_reference(q[0], K[sel], V[sel], 128 ** -0.5)
+    assert np.abs(out[0] - ref).max() < 1e-12
+    assert np.abs(out[1] - ref).max() < 1e-12
+    assert np.all(out[2] == 0.0)
+
+
+def test_sparse_gqa_gate_zero_halves_and_page_permutation_invariance():
+    L, W = 100, 64
+    kv, bt, q, K, V = _tiny_attention_case(L)
+    packed = np.full((1, W + 1), -1, np.int32)
+    packed[0, :10] = np.arange(0, 100, 10)
+    packed[0, W] = 10
+    kvb = f64_to_bf16_bits(kv)
+    qb = f64_to_bf16_bits(q[:1])
+    plain = oq.sparse_gqa(qb, kvb, bt, np.zeros(1, np.int32), packed)
+    gated = oq.sparse_gqa(qb, kvb, bt, np.zeros(1, np.int32), packed,
+                          gate=np.zeros((1, 8, 128), np.uint16))
+    assert np.array_equal(gated, plain * 0.5)
+    # Move every page elsewhere and renumber the table: same result.
+    perm = np.random.default_rng(9).permutation(kv.shape[0])
+    kv2 = np.empty_like(kvb)
+    kv2[perm] = kvb
+    out2 = oq.sparse_gqa(qb, kv2, perm[bt].astype(np.int32), np.zeros(1, np.int32), packed)
+    assert np.array_equal(out2, plain)
+
+
+# ----------------------------------------------------------------------------- end to end
+
+
+def test_budget_at_least_context_reproduces_full_causal_attention():
+    wl = make_workload("tiny_decode", budget=4096)
+    st = oracle_step(wl)
+    T = wl.num_tokens
+    W = wl.output_width
+    q = bf16_bits_to_f64(to_np(wl.q))
+    kv = bf16_bits_to_f64(to_np(wl.kv_cache))
+    bt = to_np(wl.block_table)[0]
+    L = int(wl.seq_lens_host[0])
+    K = np.stack([kv[bt[t // 16], :, t % 16, :128] for t in range(L)])
+    V = np.stack([kv[bt[t // 16], :, t % 16, 128:] for t in range(L)])
+    gate = bf16_bits_to_f64(to_np(wl.gate))
+    for i in range(T):
+        p = L - T + i
+        assert st.packed[i, W] == p + 1
+        assert np.array_equal(st.packed[i, :p + 1], np.arange(p + 1))
+        ref = _dense_reference(q[i], K[:p + 1], V[:p + 1], 128 ** -0.5)
+        ref = ref / (1.0 + np.exp(-gate[i]))
+        assert np.abs(st.out[i] - ref).max() < 1e-12
+
+
+def test_tiny_decode_selection_invariants_and_no_poison_read():
+    wl = make_workload("tiny_decode")
+    st = oracle_step(wl)
+    W = wl.output_width
+    L = int(wl.seq_lens_host[0])
+    for i in range(wl.num_tokens):
+        p = L - wl.num_tokens + i
+        cnt = st.packed[i, W]
+        row = st.packed[i, :cnt]
+        assert np.all(np.diff(row) > 0) and row[0] >= 0 and row[-1] <= p
+        tail = (p + 1) % wl.compress_ratio
+        assert np.array_equal(row[cnt - tail:], np.arange(p + 1 - tail, p + 1))
+        assert np.all(st.packed[i, cnt:W] == -1)
+    assert np.all(np.isfinite(st.out))
+    assert np.all(np.isfinite(bf16_bits_to_f64(st.q_codes)))
