@@ -1,0 +1,259 @@
+/*
+ * qsa.h -- C ABI of libqsa.so, the MI355X (gfx950) implementation of the QSA sparse-attention
+ * hot path:
+ *
+ *   qsa_compress           indexer Q prep, key pooling into the compressed-key cache, raw-key
+ *                          ring update
+ *   qsa_index_logits_topk  indexer logits, block top-k, expansion into the packed selection
+ *                          buffer
+ *   qsa_sparse_gqa         paged sparse GQA over the selected tokens, split across the
+ *                          selection with a log-sum-exp merge, optional sigmoid output gate
+ *
+ * Pages the calls follow (cited by title and section):
+ *   "vllm.models.qwen4_exp.nvidia.qsa" (newest revision): QSAIndexer.forward -- the indexer
+ *       contract, its unfused reference path and the packed selection buffer;
+ *       Qwen4ExpQSAImpl.forward -- the attention contract.
+ *   "vllm.models.qwen4_exp.nvidia.qsa" (docs.vllm.ai): QSAIndexer.forward with the fused
+ *       qsa_pre_indexer launch, the model for qsa_compress.
+ *   "indexer_qsa.py": apply_qsa_rope, _supports_fused_pre_indexer.
+ *   "vllm.models.qwen4_exp.nvidia.ops.qsa": qsa_compress_groups_with_ratio,
+ *       qsa_store_cache_rows, qsa_sparse_paged_attention, _select_config.
+ *   patch "qwen4_exp: FP8 E4M3 KV reader for QSA with a static scale sidecar": the body of
+ *       _qsa_sparse_paged_gqa_splitk_kernel.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every data pointer is DEVICE memory owned by the caller; the library never allocates,
+ *    frees, synchronises, or reads device data on the host.  Calls are asynchronous on the
+ *    given stream (a hipStream_t; NULL = the default stream) and are safe to capture in a
+ *    HIP graph (no memset nodes, no host reads).
+ *  - bf16 tensors are passed as uint16_t bit patterns, fp8 tensors as uint8_t OCP e4m3fn
+ *    codes.  Strides are in ELEMENTS; the innermost dimension is always contiguous.
+ *  - Index tensors are int32, positions int64 (as on the pages).
+ *  - Every argument is validated on the host before any launch: an error returns
+ *    QSA_ERR_INVALID_ARGUMENT (shape / stride / metadata inconsistencies the host can see,
+ *    the pages' ValueError), QSA_ERR_NOT_SUPPORTED (dtype, head_dim, rotary_dim or feature
+ *    outside what is built, the pages' NotImplementedError), or QSA_ERR_WORKSPACE_TOO_SMALL,
+ *    and leaves nothing launched.  QSA_ERR_HIP reports a failed launch.
+ *  - Device metadata the host cannot see (request lengths, page tables, positions, packed
+ *    indices) is bounds-checked in the kernels: an out-of-range page or index is masked
+ *    exactly as documented per call, and no kernel ever reads or writes outside the buffers
+ *    the sizes describe.  Faults inside a kernel surface at the caller's next stream sync.
+ *  - num_tokens == 0 returns QSA_OK and launches nothing.
+ *  - Calls that write overlapping buffers must not run concurrently on different streams.
+ */
+#ifndef QSA_H_
+#define QSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QSA_ABI_VERSION 1
+
+typedef enum qsa_status {
+  QSA_OK = 0,
+  QSA_ERR_INVALID_ARGUMENT = 1,
+  QSA_ERR_NOT_SUPPORTED = 2,
+  QSA_ERR_WORKSPACE_TOO_SMALL = 3,
+  QSA_ERR_HIP = 4
+} qsa_status;
+
+/* Indexer storage type: bf16, or OCP e4m3fn "without scales" (page
+ * "vllm.models.qwen4_exp.nvidia.qsa", QSAIndexer.__init__, the indexer_kv_dtype branch). */
+typedef enum qsa_dtype { QSA_DTYPE_BF16 = 0, QSA_DTYPE_FP8_E4M3 = 1 } qsa_dtype;
+
+/* ------------------------------------------------------------------------------------------
+ * qsa_compress
+ *
+ * Follows QSAIndexer.forward's unfused reference path (page "vllm.models.qwen4_exp.nvidia.qsa")
+ * and the fused qsa_pre_indexer launch it replaces (docs.vllm.ai revision):
+ *   (1) indexer Q: per head, Gemma RMSNorm with q_norm_weight -> bf16 -> NeoX RoPE on dims
+ *       0..63 at the row's rotary position (1-D, or interleaved MRoPE) -> bf16 -> [e4m3fn];
+ *   (2) every group of compress_ratio raw keys that this step's rows complete (group g ends
+ *       at token (g+1)*c - 1) is averaged -> bf16 -> RMSNorm with k_norm_weight -> bf16 ->
+ *       RoPE at the position of token g*c (its logical position for 1-D RoPE, its position
+ *       triple for MRoPE) -> bf16 -> [e4m3fn] and stored as compressed row g of the request
+ *       (qsa_compress_groups_with_ratio + qsa_store_cache_rows, "vllm.models.qwen4_exp.
+ *       nvidia.ops.qsa");
+ *   (3) the raw-key ring then receives the step's last min(S, rows) keys (and their position
+ *       triples for MRoPE) in slot token % S.  All ring reads of step (2) complete before any
+ *       ring write.
+ * Arithmetic is the canonical float64 chain of this project (halving sums over the 128 dims,
+ * correctly rounded sqrt and divide, float64 -> float32 -> bf16 rounding, RNE e4m3fn cast that
+ * maps overflow to NaN), so q_idx and the cache bytes are reproducible bit for bit.
+ * ------------------------------------------------------------------------------------------ */
+typedef struct qsa_compress_args {
+  int32_t num_tokens;               /* T: rows of this step                                  */
+  int32_t num_requests;             /* R                                                     */
+  const int32_t* query_start_loc;   /* [R+1] row offsets, non-decreasing, [R] == T           */
+  const int32_t* seq_lens;          /* [R] tokens of the request INCLUDING this step's rows;
+                                       row i of request r sits at p = seq_lens[r]-n_r+i      */
+  int32_t max_query_len;            /* host upper bound of n_r (selects the ring-write plan) */
+  const uint16_t* q_proj;           /* [T, Hi*128] bf16 indexer Q (pre-projected)            */
+  int64_t q_proj_row_stride;
+  const uint16_t* k_proj;           /* [T, 128] bf16 raw indexer keys                        */
+  int64_t k_proj_row_stride;
+  const int64_t* positions;         /* [T] rotary positions, or [T,3] (T,H,W) for MRoPE      */
+  int32_t mrope_section[3];         /* all zero: 1-D RoPE; else interleaved MRoPE sections,
+                                       summing to rotary_dim/2                               */
+  const float* cos_sin;             /* [max_position, 64]: cos in cols 0..31, sin in 32..63;
+                                       positions are clamped into [0, max_position)          */
+  int32_t max_position;
+  const uint16_t* q_norm_weight;    /* [128] bf16 (Gemma convention: scale is 1 + w)        */
+  const uint16_t* k_norm_weight;    /* [128] bf16                                            */
+  float eps;                        /* RMSNorm epsilon (rms_norm_eps, 1e-6 by default)       */
+  uint16_t* ring;                   /* [ring_pages, ring_size, 128] bf16 raw-key ring        */
+  int64_t* ring_pos;                /* [ring_pages, ring_size, 3] int64, MRoPE only, else NULL */
+  const int32_t* ring_page;         /* [R] ring page of each request; out of range: the
+                                       request's ring is neither read (reads as 0) nor written */
+  int32_t ring_pages;
+  int32_t ring_size;                /* S >= compress_ratio (the pages require the ring to be
+                                       wider than a group)                                   */
+  void* ckv;                        /* [c_pages, c_page_size, 128] bf16 or e4m3fn            */
+  const int32_t* c_block_table;     /* [R, c_block_table_stride] compressed-cache pages      */
+  int32_t c_block_table_stride;
+  int32_t c_block_table_width;      /* valid columns of c_block_table; a group whose page
+                                       column or page is out of range is not stored          */
+  int32_t c_page_size;              /* compressed rows per page                              */
+  int32_t c_pages;
+  int32_t num_index_heads;          /* Hi (1..16)                                            */
+  int32_t head_dim;                 /* must be 128                                           */
+  int32_t rotary_dim;               /* must be 64                                            */
+  int32_t compress_ratio;           /* c: power of two, 2..64                                */
+  qsa_dtype index_dtype;
+  void* q_idx;                      /* OUT [T, Hi, 128] in index_dtype, contiguous           */
+} qsa_compress_args;
+
+qsa_status qsa_compress(const qsa_compress_args* args, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * qsa_index_logits_topk
+ *
+ * Follows QSAIndexer.forward's selection (qsa_select_paged_decode / qsa_select_paged_prefill /
+ * expand_qsa_block_indices) and the packed-buffer contract of QSAIndexer.output_width and
+ * packed_output_width (page "vllm.models.qwen4_exp.nvidia.qsa"):
+ *   a row at position p sees vis = floor((p+1)/c) compressed blocks; its score for block j is
+ *   the sum over the Hi indexer heads of q_idx[row,h,:] . ckv[j,:] (weight-free); it keeps
+ *   every block if vis <= budget/c, else the budget/c best (higher score first, an exactly
+ *   equal score to the lower block index).  The packed row (W = budget + c - 1 columns + 1):
+ *   the kept blocks' tokens g*c..g*c+c-1 in ascending order, then the tail tokens
+ *   vis*c..p, then -1 padding, and the number of valid entries in column W.
+ * The selected set is EXACT with respect to the float64 score summed in the canonical order
+ * (per head a halving sum over the 128 dims, heads added in order): the kernels rank fast
+ * float32 scores, certify every block outside a proven error band, and re-score only the
+ * band in float64.
+ * Decode requests (the leading num_decode_requests, each with decode_query_len rows) and the
+ * remaining prefill requests may be mixed in one call.
+ * A visible block whose page is out of range scores as an all-zero key.
+ * ------------------------------------------------------------------------------------------ */
+typedef struct qsa_topk_args {
+  int32_t num_tokens;               /* T                                                     */
+  int32_t num_requests;             /* R                                                     */
+  const int32_t* query_start_loc;   /* [R+1]                                                 */
+  const int32_t* seq_lens;          /* [R] (as for qsa_compress)                             */
+  int32_t num_decode_requests;      /* leading requests with decode_query_len rows each      */
+  int32_t decode_query_len;
+  int32_t max_query_len;            /* host upper bound of n_r over all requests             */
+  int32_t max_seq_len;              /* host upper bound of seq_lens (sizes the workspace)    */
+  const void* q_idx;                /* [T, Hi, 128] index_dtype (qsa_compress's output)      */
+  const void* ckv;                  /* [c_pages, c_page_size, 128] index_dtype               */
+  const int32_t* c_block_table;
+  int32_t c_block_table_stride;
+  int32_t c_block_table_width;
+  int32_t c_page_size;
+  int32_t c_pages;
+  int32_t num_index_heads;          /* Hi (1..16)                                            */
+  int32_t head_dim;                 /* must be 128                                           */
+  int32_t compress_ratio;           /* c (power of two)                                      */
+  int32_t budget;                   /* token budget B, a multiple of c                       */
+  qsa_dtype index_dtype;
+  int32_t* packed;                  /* OUT [T, B + c] int32 (W + 1 columns), row stride below */
+  int64_t packed_row_stride;
+} qsa_topk_args;
+
+size_t qsa_index_logits_topk_workspace_size(const qsa_topk_args* args);
+qsa_status qsa_index_logits_topk(const qsa_topk_args* args, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * qsa_sparse_gqa
+ *
+ * Follows qsa_sparse_paged_attention ("vllm.models.qwen4_exp.nvidia.ops.qsa") and the body of
+ * _qsa_sparse_paged_gqa_splitk_kernel (FP8 KV reader patch page, bf16 branch): for every row
+ * and Q head hq (KV head hq / (Hq/Hkv)), attend over entries 0..min(count, W)-1 of the row's
+ * packed buffer, where count is its column W; entry t maps to page block_table[req, t / P],
+ * slot t % P.  Negative entries, entries whose page column or page is out of range are
+ * masked.  Softmax scale = `scale` (0: head_dim^-0.5); a row with no valid entry yields 0.
+ * The selection is split across `num_splits` workgroups per (row, KV head) whose float32
+ * partials are merged by log-sum-exp; the sigmoid of `gate` (if not NULL) multiplies the
+ * merged output; the result is written as bf16.
+ * KV cache layout: token row of KV head h on page pg starts at
+ *     kv_cache + pg*kv_page_stride + h*kv_head_stride + slot*kv_token_stride
+ * and holds K in its first head_dim values and V in the next head_dim (the pages' kv_cache
+ * [pages, Hkv, P, 2*head_dim], split at head_size after transpose(1, 2)).
+ * ------------------------------------------------------------------------------------------ */
+typedef struct qsa_gqa_args {
+  int32_t num_tokens;               /* T                                                     */
+  int32_t num_requests;             /* R (rows of block_table)                               */
+  int32_t num_q_heads;              /* Hq                                                    */
+  int32_t num_kv_heads;             /* Hkv; Hq / Hkv in {1, 2, 4, 8, 16}                     */
+  int32_t head_dim;                 /* must be 128                                           */
+  const uint16_t* q;                /* [T, Hq, 128] bf16                                     */
+  int64_t q_row_stride;
+  int64_t q_head_stride;
+  const uint16_t* kv_cache;         /* bf16, layout above                                    */
+  int64_t kv_page_stride;           /* strides: multiples of 8 elements                      */
+  int64_t kv_head_stride;
+  int64_t kv_token_stride;
+  int32_t num_pages;
+  int32_t page_size;                /* P: a multiple of 16                                   */
+  const int32_t* block_table;       /* [R, block_table_stride]                               */
+  int32_t block_table_stride;
+  int32_t block_table_width;        /* valid columns                                         */
+  const int32_t* token_to_req;      /* [T]; a request outside [0, R) masks the whole row     */
+  const int32_t* packed;            /* [T, W + 1] packed selection buffer                    */
+  int64_t packed_row_stride;
+  int32_t packed_width;             /* W (selection columns; the count is column W)          */
+  const uint16_t* gate;             /* [T, Hq, 128] bf16 or NULL                             */
+  int64_t gate_row_stride;
+  int64_t gate_head_stride;
+  float scale;                      /* 0 -> head_dim^-0.5                                    */
+  int32_t num_splits;               /* 0: automatic; >= 1 forces (clamped to the tile count) */
+  uint16_t* out;                    /* OUT [T, Hq, 128] bf16, fully overwritten              */
+  int64_t out_row_stride;
+  int64_t out_head_stride;
+} qsa_gqa_args;
+
+/* Splits the call will use (after the automatic choice and clamping). */
+int32_t qsa_sparse_gqa_num_splits(const qsa_gqa_args* args);
+size_t qsa_sparse_gqa_workspace_size(const qsa_gqa_args* args);
+qsa_status qsa_sparse_gqa(const qsa_gqa_args* args, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Diagnostics: the device arithmetic the bit-exact parts of the path rest on, exposed so a test
+ * can compare it with the host's IEEE results.
+ *
+ * qsa_diag_e4m3_decode: out [512] float (device): out[c] is e4m3fn code c through the hardware
+ *   converter of the logits kernels, out[256 + c] through the definitional decoder used by the
+ *   float64 re-scoring (OCP e4m3fn, as torch.float8_e4m3fn decodes it).
+ * qsa_diag_fp64_sqrt_div: for n doubles in[i] (device), writes out[3i] = sqrt(x),
+ *   out[3i+1] = 1/x, out[3i+2] = 1/sqrt(x) (device) -- the operations of the RMSNorm chain,
+ *   which must be correctly rounded.
+ * ------------------------------------------------------------------------------------------ */
+qsa_status qsa_diag_e4m3_decode(float* out, void* stream);
+qsa_status qsa_diag_fp64_sqrt_div(const double* in, double* out, int64_t n, void* stream);
+
+/* ------------------------------------------------------------------------------------------ */
+const char* qsa_status_string(qsa_status status);
+int32_t qsa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSA_H_ */

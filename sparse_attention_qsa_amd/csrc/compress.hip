@@ -1,0 +1,250 @@
+// qsa_compress kernels: indexer Q prep, pooling of completed key groups into the compressed-key
+// cache, and the raw-key ring update.
+//
+// Follows QSAIndexer.forward's unfused reference path (page "vllm.models.qwen4_exp.nvidia.qsa")
+// and qsa_compress_groups_with_ratio / qsa_store_cache_rows (page
+// "vllm.models.qwen4_exp.nvidia.ops.qsa").  One wavefront owns one 128-dim vector: lane l holds
+// dims 2l and 2l+1, which is also the layout of the canonical halving sum (adjacent pairs first,
+// then the upper half of the lanes onto the lower half), so every value is bit-identical to the
+// float64 chain the oracle defines.  The work is a few MB at most per step: the kernels are
+// latency-bound and kept simple.
+#include "qsa_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace qsa {
+namespace {
+
+struct CompressParams {
+  int T, R, Hi, c, S, ring_pages, Pc, c_pages, cbt_stride, cbt_width, max_pos;
+  int sec_h, sec_w;  // MRoPE sections (H, W); T takes the remaining frequencies
+  bool mrope, fp8, fuse_ring;
+  const int32_t* qsl;
+  const int32_t* seq_lens;
+  const uint32_t* q_proj;  // bf16 pairs
+  int64_t q_rs;            // row stride in pairs
+  const uint32_t* k_proj;
+  int64_t k_rs;
+  const int64_t* pos;
+  const float* cos_sin;
+  const uint16_t* qw;
+  const uint16_t* kw;
+  double eps;
+  uint32_t* ring;  // bf16 pairs [ring_pages, S, 64]
+  int64_t* ring_pos;
+  const int32_t* ring_page;
+  void* ckv;
+  const int32_t* cbt;
+  void* q_idx;
+};
+
+// Position axis (0 = T, 1 = H, 2 = W) of rotary frequency f under interleaved MRoPE.
+__device__ __forceinline__ int mrope_axis(int f, int sec_h, int sec_w) {
+  if (f % 3 == 1 && f < 3 * sec_h) return 1;
+  if (f % 3 == 2 && f < 3 * sec_w) return 2;
+  return 0;
+}
+
+__device__ __forceinline__ int64_t clamp_pos(int64_t p, int max_pos) {
+  return p < 0 ? 0 : (p >= max_pos ? (int64_t)max_pos - 1 : p);
+}
+
+// Gemma RMSNorm of the wave's vector (x0, x1 = dims 2l, 2l+1) with weight pair w (bf16 pair),
+// rounded float64 -> float32 -> bf16.  Returns the bf16 values as floats.
+__device__ __forceinline__ void rmsnorm_pair(float x0f, float x1f, uint32_t wpair, double eps,
+                                             float& y0, float& y1) {
+  const double x0 = x0f, x1 = x1f;
+  double t = x0 * x0 + x1 * x1;  // squares exact; one rounding
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) t = t + shfl_xor_f64(t, m);
+  const double var = t / 128.0 + eps;
+  const double inv = 1.0 / sqrt(var);
+  const double w0 = bf16lo(wpair), w1 = bf16hi(wpair);
+  y0 = bf16_to_f32(f64_to_bf16((x0 * inv) * (1.0 + w0)));
+  y1 = bf16_to_f32(f64_to_bf16((x1 * inv) * (1.0 + w1)));
+}
+
+// NeoX rotation of dims 0..63 (pairs (i, i+32)) at per-frequency positions; dims 64..127 pass
+// through.  `posf(f)` gives the (clamped) position of frequency f.
+template <typename PosFn>
+__device__ __forceinline__ void rope_pair(const CompressParams& P, int lane, float& y0,
+                                          float& y1, PosFn posf) {
+  const float p0 = __shfl_xor(y0, 16, kWave);  // partner dims: lane l <-> lane l ^ 16
+  const float p1 = __shfl_xor(y1, 16, kWave);
+  if (lane < 32) {
+    const int f0 = (2 * lane) & 31;
+    const int64_t q0 = posf(f0), q1 = posf(f0 + 1);
+    const double c0 = P.cos_sin[q0 * 64 + f0], s0 = P.cos_sin[q0 * 64 + 32 + f0];
+    const double c1 = P.cos_sin[q1 * 64 + f0 + 1], s1 = P.cos_sin[q1 * 64 + 32 + f0 + 1];
+    const double sgn = lane < 16 ? -1.0 : 1.0;  // first half: a*cos - b*sin; second: b*cos + a*sin
+    const double r0 = (double)y0 * c0 + sgn * ((double)p0 * s0);
+    const double r1 = (double)y1 * c1 + sgn * ((double)p1 * s1);
+    y0 = bf16_to_f32(f64_to_bf16(r0));
+    y1 = bf16_to_f32(f64_to_bf16(r1));
+  }
+}
+
+__device__ __forceinline__ void store_index_pair(const CompressParams& P, void* base,
+                                                 int64_t vec, int lane, float y0, float y1) {
+  if (P.fp8) {
+    const uint32_t code = f32_to_e4m3(y0) | (f32_to_e4m3(y1) << 8);
+    reinterpret_cast<uint16_t*>(base)[vec * 64 + lane] = (uint16_t)code;
+  } else {
+    const uint32_t bits = (f32_to_bf16(y0) & 0xFFFFu) | (f32_to_bf16(y1) << 16);
+    reinterpret_cast<uint32_t*>(base)[vec * 64 + lane] = bits;
+  }
+}
+
+__device__ __forceinline__ void ring_store_row(const CompressParams& P, int row, int r, int p,
+                                               int L, int lane) {
+  if (p < L - P.S) return;
+  const int rp = P.ring_page[r];
+  if (rp < 0 || rp >= P.ring_pages) return;
+  const int64_t slot = (int64_t)rp * P.S + (p % P.S);
+  P.ring[slot * 64 + lane] = P.k_proj[(int64_t)row * P.k_rs + lane];
+  if (P.mrope && lane < 3) P.ring_pos[slot * 3 + lane] = P.pos[(int64_t)row * 3 + lane];
+}
+
+// Waves [0, T*Hi): indexer Q vectors.  Waves [T*Hi, T*Hi + T): the group (if any) completed by
+// row (wave - T*Hi), and -- when fuse_ring -- that row's ring write.
+__global__ __launch_bounds__(256) void prep_compress_kernel(CompressParams P) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int64_t nq = (int64_t)P.T * P.Hi;
+  if (wave < nq) {
+    const int row = (int)(wave / P.Hi), h = (int)(wave % P.Hi);
+    const uint32_t u = P.q_proj[(int64_t)row * P.q_rs + h * 64 + lane];
+    float y0, y1;
+    rmsnorm_pair(bf16lo(u), bf16hi(u), reinterpret_cast<const uint32_t*>(P.qw)[lane], P.eps,
+                 y0, y1);
+    if (P.mrope) {
+      rope_pair(P, lane, y0, y1, [&](int f) {
+        return clamp_pos(P.pos[(int64_t)row * 3 + mrope_axis(f, P.sec_h, P.sec_w)], P.max_pos);
+      });
+    } else {
+      const int64_t q = clamp_pos(P.pos[row], P.max_pos);
+      rope_pair(P, lane, y0, y1, [&](int) { return q; });
+    }
+    store_index_pair(P, P.q_idx, wave, lane, y0, y1);
+    return;
+  }
+  const int64_t row64 = wave - nq;
+  if (row64 >= P.T) return;
+  const int row = (int)row64;
+  const int r = find_request(P.qsl, P.R, row);
+  if (r < 0) return;
+  const int q0 = P.qsl[r], n = P.qsl[r + 1] - q0, L = P.seq_lens[r];
+  const int start = L - n;
+  if (start < 0) return;
+  const int p = start + (row - q0);
+  const int rp = P.ring_page[r];
+  const bool ring_ok = rp >= 0 && rp < P.ring_pages;
+
+  if ((p + 1) % P.c == 0) {
+    const int g = (p + 1) / P.c - 1;
+    const int t0 = g * P.c;
+    double a0 = 0.0, a1 = 0.0;
+    for (int m = 0; m < P.c; ++m) {
+      const int t = t0 + m;
+      uint32_t u = 0;
+      if (t >= start) {
+        u = P.k_proj[(int64_t)(q0 + t - start) * P.k_rs + lane];
+      } else if (ring_ok) {
+        u = P.ring[((int64_t)rp * P.S + (t % P.S)) * 64 + lane];
+      }
+      const double v0 = bf16lo(u), v1 = bf16hi(u);
+      if (m == 0) { a0 = v0; a1 = v1; } else { a0 = a0 + v0; a1 = a1 + v1; }
+    }
+    const float m0 = bf16_to_f32(f64_to_bf16(a0 / (double)P.c));
+    const float m1 = bf16_to_f32(f64_to_bf16(a1 / (double)P.c));
+    float y0, y1;
+    rmsnorm_pair(m0, m1, reinterpret_cast<const uint32_t*>(P.kw)[lane], P.eps, y0, y1);
+    if (P.mrope) {
+      const bool in_step = t0 >= start;
+      const int64_t base = in_step ? (int64_t)(q0 + t0 - start) * 3
+                                   : ((int64_t)rp * P.S + (t0 % P.S)) * 3;
+      const int64_t* src = in_step ? P.pos : P.ring_pos;
+      const bool ok = in_step || ring_ok;
+      rope_pair(P, lane, y0, y1, [&](int f) {
+        return ok ? clamp_pos(src[base + mrope_axis(f, P.sec_h, P.sec_w)], P.max_pos)
+                  : (int64_t)0;
+      });
+    } else {
+      const int64_t q = clamp_pos(t0, P.max_pos);
+      rope_pair(P, lane, y0, y1, [&](int) { return q; });
+    }
+    const int col = g / P.Pc;
+    if (col < P.cbt_width) {
+      const int page = P.cbt[(int64_t)r * P.cbt_stride + col];
+      if (page >= 0 && page < P.c_pages) {
+        store_index_pair(P, P.ckv, (int64_t)page * P.Pc + (g % P.Pc), lane, y0, y1);
+      }
+    }
+  }
+  if (P.fuse_ring) ring_store_row(P, row, r, p, L, lane);
+}
+
+// Separate ring update, launched after prep_compress_kernel when the step's writes could alias
+// slots that its reads still need (long prefill chunks).
+__global__ __launch_bounds__(256) void ring_store_kernel(CompressParams P) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row64 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  if (row64 >= P.T) return;
+  const int row = (int)row64;
+  const int r = find_request(P.qsl, P.R, row);
+  if (r < 0) return;
+  const int q0 = P.qsl[r], n = P.qsl[r + 1] - q0, L = P.seq_lens[r];
+  if (L - n < 0) return;
+  ring_store_row(P, row, r, L - n + (row - q0), L, lane);
+}
+
+}  // namespace
+
+hipError_t launch_compress(const qsa_compress_args& a, hipStream_t s) {
+  CompressParams P{};
+  P.T = a.num_tokens;
+  P.R = a.num_requests;
+  P.Hi = a.num_index_heads;
+  P.c = a.compress_ratio;
+  P.S = a.ring_size;
+  P.ring_pages = a.ring_pages;
+  P.Pc = a.c_page_size;
+  P.c_pages = a.c_pages;
+  P.cbt_stride = a.c_block_table_stride;
+  P.cbt_width = a.c_block_table_width;
+  P.max_pos = a.max_position;
+  P.mrope = a.mrope_section[0] || a.mrope_section[1] || a.mrope_section[2];
+  P.sec_h = a.mrope_section[1];
+  P.sec_w = a.mrope_section[2];
+  P.fp8 = a.index_dtype == QSA_DTYPE_FP8_E4M3;
+  // Reads of the ring reach back at most c-1 tokens before the step, writes cover its last
+  // min(S, n) tokens: they cannot share a slot when n + c - 2 < S.
+  P.fuse_ring = (int64_t)a.max_query_len + a.compress_ratio - 2 < a.ring_size;
+  P.qsl = a.query_start_loc;
+  P.seq_lens = a.seq_lens;
+  P.q_proj = reinterpret_cast<const uint32_t*>(a.q_proj);
+  P.q_rs = a.q_proj_row_stride / 2;
+  P.k_proj = reinterpret_cast<const uint32_t*>(a.k_proj);
+  P.k_rs = a.k_proj_row_stride / 2;
+  P.pos = a.positions;
+  P.cos_sin = a.cos_sin;
+  P.qw = a.q_norm_weight;
+  P.kw = a.k_norm_weight;
+  P.eps = (double)a.eps;
+  P.ring = reinterpret_cast<uint32_t*>(a.ring);
+  P.ring_pos = a.ring_pos;
+  P.ring_page = a.ring_page;
+  P.ckv = a.ckv;
+  P.cbt = a.c_block_table;
+  P.q_idx = a.q_idx;
+
+  const int64_t waves = (int64_t)P.T * P.Hi + P.T;
+  const int64_t blocks = (waves + 3) / 4;
+  hipLaunchKernelGGL(prep_compress_kernel, dim3((unsigned)blocks), dim3(256), 0, s, P);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || P.fuse_ring) return e;
+  hipLaunchKernelGGL(ring_store_kernel, dim3((unsigned)((P.T + 3) / 4)), dim3(256), 0, s, P);
+  return hipGetLastError();
+}
+
+}  // namespace qsa

@@ -1,0 +1,123 @@
+"""Host-side checks of libqsa.so that need no GPU: the library loads, exports every symbol the
+header declares, its argument blocks have the C layout, and invalid calls are rejected before any
+launch (so they run on a CPU-only machine)."""
+
+import ctypes as C
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+from sparse_attention_qsa_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qsa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH), reason="libqsa.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:const\s+)?[a-z_0-9]+[\s\*]+(qsa_[a-z_0-9]+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"qsa_compress", "qsa_index_logits_topk", "qsa_sparse_gqa"} <= set(names)
+    lib = B.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(B.EXPORTED)
+    assert lib.qsa_abi_version() == 1
+    assert lib.qsa_status_string(3) == b"QSA_ERR_WORKSPACE_TOO_SMALL"
+
+
+STRUCTS = {"qsa_compress_args": B.CompressArgs, "qsa_topk_args": B.TopkArgs,
+           "qsa_gqa_args": B.GqaArgs}
+
+
+def test_argument_blocks_have_the_c_layout():
+    lines = ['#include <stdio.h>', '#include <stddef.h>', f'#include "{HEADER}"', "int main(){"]
+    for cname, cls in STRUCTS.items():
+        lines.append(f'printf("{cname} %zu\\n", sizeof({cname}));')
+        for f, _ in cls._fields_:
+            lines.append(f'printf("{cname}.{f} %zu\\n", offsetof({cname}, {f}));')
+    lines.append("return 0;}")
+    with tempfile.TemporaryDirectory() as d:
+        src, exe = os.path.join(d, "l.c"), os.path.join(d, "l")
+        open(src, "w").write("\n".join(lines))
+        subprocess.run(["gcc", "-std=c99", src, "-o", exe], check=True)
+        out = subprocess.run([exe], check=True, capture_output=True, text=True).stdout
+    got = dict(line.rsplit(" ", 1) for line in out.strip().splitlines())
+    for cname, cls in STRUCTS.items():
+        assert int(got[cname]) == C.sizeof(cls), cname
+        for f, _ in cls._fields_:
+            assert int(got[f"{cname}.{f}"]) == getattr(cls, f).offset, f"{cname}.{f}"
+
+
+FAKE = 1 << 20   # a non-null, 256-byte-aligned stand-in pointer; never dereferenced here
+
+
+def _gqa(**over):
+    a = B.GqaArgs(num_tokens=64, num_requests=64, num_q_heads=16, num_kv_heads=2, head_dim=128,
+                  q=FAKE, q_row_stride=16 * 128, q_head_stride=128, kv_cache=FAKE,
+                  kv_page_stride=2 * 16 * 256, kv_head_stride=16 * 256, kv_token_stride=256,
+                  num_pages=131072, page_size=16, block_table=FAKE, block_table_stride=2048,
+                  block_table_width=2048, token_to_req=FAKE, packed=FAKE,
+                  packed_row_stride=2052, packed_width=2051, out=FAKE,
+                  out_row_stride=16 * 128, out_head_stride=128)
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+def _topk(**over):
+    a = B.TopkArgs(num_tokens=64, num_requests=64, query_start_loc=FAKE, seq_lens=FAKE,
+                   num_decode_requests=64, decode_query_len=1, max_query_len=1,
+                   max_seq_len=32768, q_idx=FAKE, ckv=FAKE, c_block_table=FAKE,
+                   c_block_table_stride=512, c_block_table_width=512, c_page_size=16,
+                   c_pages=32768, num_index_heads=8, head_dim=128, compress_ratio=4,
+                   budget=2048, index_dtype=0, packed=FAKE, packed_row_stride=2052)
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_split_plan_and_workspace_sizes():
+    lib = B.lib()
+    a = _gqa()
+    # 33 tiles of 64 tokens; 128 (row, KV head) units -> 16 splits wanted -> 3 tiles each.
+    assert lib.qsa_sparse_gqa_num_splits(C.byref(a)) == 11
+    assert lib.qsa_sparse_gqa_workspace_size(C.byref(a)) >= 11 * 64 * 16 * 128 * 4
+    one = _gqa(num_splits=1)
+    assert lib.qsa_sparse_gqa_num_splits(C.byref(one)) == 1
+    assert lib.qsa_sparse_gqa_workspace_size(C.byref(one)) == 0
+    big = _gqa(num_tokens=4096)
+    assert lib.qsa_sparse_gqa_num_splits(C.byref(big)) == 1
+    t = _topk()
+    ws = lib.qsa_index_logits_topk_workspace_size(C.byref(t))
+    assert ws >= 64 * 8192 * (4 + 4 + 8)    # logits + band index + band score per column
+
+
+def test_invalid_calls_are_rejected_before_any_launch():
+    lib = B.lib()
+    INVAL, NOTSUP, SMALL = 1, 2, 3
+    assert lib.qsa_sparse_gqa(C.byref(_gqa(head_dim=64)), None, 0, None) == NOTSUP
+    assert lib.qsa_sparse_gqa(C.byref(_gqa(num_q_heads=12)), None, 0, None) == NOTSUP
+    assert lib.qsa_sparse_gqa(C.byref(_gqa(page_size=8)), None, 0, None) == NOTSUP
+    assert lib.qsa_sparse_gqa(C.byref(_gqa(q=None)), None, 0, None) == INVAL
+    assert lib.qsa_sparse_gqa(C.byref(_gqa(kv_token_stride=100)), None, 0, None) == INVAL
+    assert lib.qsa_sparse_gqa(C.byref(_gqa(packed_row_stride=2051)), None, 0, None) == INVAL
+    assert lib.qsa_sparse_gqa(C.byref(_gqa()), None, 0, None) == SMALL      # needs partials
+    assert lib.qsa_sparse_gqa(C.byref(_gqa(num_tokens=0)), None, 0, None) == 0
+    assert lib.qsa_index_logits_topk(C.byref(_topk(budget=2047)), None, 0, None) == INVAL
+    assert lib.qsa_index_logits_topk(C.byref(_topk(compress_ratio=3)), None, 0, None) == NOTSUP
+    assert lib.qsa_index_logits_topk(C.byref(_topk(index_dtype=7)), None, 0, None) == NOTSUP
+    assert lib.qsa_index_logits_topk(C.byref(_topk()), None, 0, None) == SMALL
+    assert lib.qsa_index_logits_topk(C.byref(_topk(num_tokens=0)), None, 0, None) == 0
+    assert lib.qsa_index_logits_topk_workspace_size(C.byref(_topk(head_dim=64))) == 0
+    c = B.CompressArgs()
+    assert lib.qsa_compress(C.byref(c), None) == INVAL
+    assert lib.qsa_compress(None, None) == INVAL

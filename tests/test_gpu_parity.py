@@ -1,0 +1,164 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Bars: prepared Q, compressed-cache and ring bytes bit-exact; packed selection int-exact;
+attention output within max-abs 2e-2 (bf16 indexer) or 6e-2 (fp8 indexer) of the float64
+oracle.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import qsa as oq
+from oracle.numerics import bf16_bits_to_f64, e4m3_bits_to_f64
+from sparse_attention_qsa_amd import binding as B
+from tests.gpu_util import (SCALED, TOL, gpu_out_f64, log, max_abs, oracle_step, run_gpu,
+                            to_np, workload)
+
+pytestmark = pytest.mark.gpu
+
+NAMES = list(SCALED)
+
+
+# ----------------------------------------------------------------------------- device arithmetic
+
+
+def test_device_e4m3_decoders_match_the_definition():
+    log("diag: e4m3 decode of all 256 codes")
+    out = B.qsa_diag_e4m3_decode().cpu().numpy().astype(np.float64)
+    ref = e4m3_bits_to_f64(np.arange(256, dtype=np.uint32).astype(np.uint8))
+    assert np.array_equal(out[:256], ref, equal_nan=True), "hardware e4m3 converter"
+    assert np.array_equal(out[256:], ref, equal_nan=True), "definitional e4m3 decoder"
+
+
+def test_device_fp64_sqrt_and_divide_are_correctly_rounded():
+    log("diag: fp64 sqrt / divide on 2M inputs")
+    rng = np.random.default_rng(7)
+    x = np.concatenate([
+        np.exp(rng.uniform(-40, 40, 1_000_000)),
+        rng.uniform(1e-6, 300.0, 1_000_000),          # the range RMSNorm variances live in
+    ])
+    got = B.qsa_diag_fp64_sqrt_div(torch.from_numpy(x).cuda()).cpu().numpy().reshape(-1, 3)
+    r = np.sqrt(x)
+    assert np.array_equal(got[:, 0], r)
+    assert np.array_equal(got[:, 1], 1.0 / x)
+    assert np.array_equal(got[:, 2], 1.0 / r)
+
+
+# ----------------------------------------------------------------------------- the three calls
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_compress_bytes_match_oracle(name):
+    wl = workload(name)
+    log(f"compress parity {name}: T={wl.num_tokens} R={wl.num_requests}")
+    ref = oracle_step(wl, with_attention=False)        # reads the pre-state first
+    st = run_gpu(wl)
+    assert np.array_equal(to_np(st.q_idx).view(np.uint8), ref.q_codes.view(np.uint8))
+    assert np.array_equal(to_np(wl.ckv).view(np.uint8), ref.state_after.ckv.view(np.uint8))
+    assert np.array_equal(to_np(wl.ring), ref.state_after.ring)
+    if wl.ring_pos is not None:
+        assert np.array_equal(to_np(wl.ring_pos), ref.state_after.ring_pos)
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_selection_is_exact_and_attention_within_tolerance(name):
+    wl = workload(name)
+    log(f"step parity {name}: T={wl.num_tokens} R={wl.num_requests}")
+    ref = oracle_step(wl)
+    st = run_gpu(wl)
+    packed = to_np(st.packed)
+    assert np.array_equal(packed, ref.packed), (
+        f"{int((packed != ref.packed).any(axis=1).sum())} rows differ")
+    err = max_abs(gpu_out_f64(st), ref.out)
+    log(f"  max-abs {err:.3e}")
+    assert err <= TOL[wl.index_dtype]
+
+
+@pytest.mark.parametrize("name", ["tiny_decode", "decode_32k", "spec_verify_mrope"])
+def test_attention_alone_on_oracle_indices_and_split_invariance(name):
+    wl = workload(name)
+    log(f"gqa parity {name}")
+    ref = oracle_step(wl)
+    st = run_gpu(wl)
+    st.packed.copy_(torch.from_numpy(ref.packed).cuda())
+    outs = []
+    for splits in (1, 0, 1000):
+        st.g_args.num_splits = splits
+        st.gqa()
+        torch.cuda.synchronize()
+        o = gpu_out_f64(st)
+        assert max_abs(o, ref.out) <= TOL[wl.index_dtype]
+        outs.append(o)
+    # Split count changes only float32 summation order and one bf16 rounding.
+    assert max_abs(outs[0], outs[2]) <= 2 ** -6
+
+
+def test_full_size_decode_32k_on_sampled_rows():
+    wl = workload("decode_32k", num_requests=64, lengths=("fixed", 32768))
+    rows = [0, 17, 42, 63]
+    log(f"full-size decode_32k, sampled rows {rows}")
+    ref = oracle_step(wl, rows=rows)
+    st = run_gpu(wl)
+    packed = to_np(st.packed)
+    assert np.array_equal(packed[rows], ref.packed[rows])
+    err = max_abs(gpu_out_f64(st)[rows], ref.out[rows])
+    log(f"  max-abs {err:.3e}")
+    assert err <= TOL["bf16"]
+    # Every row: count, ascending indices, -1 padding (properties that hold at any size).
+    W = wl.output_width
+    assert np.all(packed[:, W] == 2048)
+    assert np.all(np.diff(packed[:, :2048], axis=1) > 0)
+    assert np.all(packed[:, 2048:W] == -1)
+
+
+# ----------------------------------------------------------------------------- edge cases
+
+
+def test_budget_at_least_context_gives_every_token():
+    wl = workload("tiny_decode", budget=4096)
+    ref = oracle_step(wl)
+    st = run_gpu(wl)
+    assert np.array_equal(to_np(st.packed), ref.packed)
+    assert max_abs(gpu_out_f64(st), ref.out) <= TOL["bf16"]
+
+
+def test_exact_ties_go_to_the_lower_block():
+    # Every compressed row of the pre-state is the same key: all visible blocks tie exactly
+    # (except the ones this step writes), so the selection is decided by block index alone.
+    wl = workload("decode_32k", num_requests=3, lengths=("fixed", 5000))
+    row = wl.ckv[wl.c_block_table[0, 0], 0].clone()
+    wl.ckv[:] = row
+    ref = oracle_step(wl, with_attention=False)
+    st = run_gpu(wl)
+    assert np.array_equal(to_np(st.packed), ref.packed)
+
+
+def test_inert_rows_invalid_entries_and_empty_requests():
+    wl = workload("tiny_decode")
+    ref = oracle_step(wl)
+    st = run_gpu(wl)
+    W = wl.output_width
+    packed = ref.packed.copy()
+    packed[0, W] = 0                              # count 0 -> zero output
+    packed[1, 5] = -1                             # a masked entry
+    packed[2, 7] = 10 ** 6                        # past the block table -> masked
+    st.packed.copy_(torch.from_numpy(packed).cuda())
+    st.gqa()
+    torch.cuda.synchronize()
+    ref_out = oq.sparse_gqa(to_np(wl.q), to_np(wl.kv_cache), to_np(wl.block_table),
+                            to_np(wl.token_to_req), packed, gate=to_np(wl.gate))
+    out = gpu_out_f64(st)
+    assert np.all(out[0] == 0.0)
+    assert max_abs(out, ref_out) <= TOL["bf16"]
+
+
+def test_zero_rows_is_a_no_op():
+    wl = workload("tiny_decode")
+    st = run_gpu(wl)
+    before = st.out.clone()
+    a = B.gqa_args(q=wl.q[:0], kv_cache=wl.kv_cache, block_table=wl.block_table,
+                   token_to_req=wl.token_to_req[:0], packed=st.packed[:0], out=st.out[:0])
+    assert B.lib().qsa_sparse_gqa(B.C.byref(a), None, 0, None) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(before, st.out)
