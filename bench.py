@@ -1,0 +1,230 @@
+"""Benchmark of the QSA hot path on one MI355X.
+
+A step is one pass of the whole path -- qsa_compress, qsa_index_logits_topk, qsa_sparse_gqa --
+over one batch of the decode_32k workload: 64 requests at 32768 tokens of context, one query
+row each; indexer 8 heads, compress ratio 4, budget 2048, bf16; attention 16 Q / 2 KV heads,
+head_dim 128, page 16.  Inputs are seeded synthetic tensors resident in HBM.  Several copies of
+the inputs are rotated step by step so that a step never finds its ~270 MB working set in the
+256 MB Infinity Cache.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+Prints one JSON line: rows/s for the whole step, the step's algorithmic HBM GB/s, per-call
+times, the roofline of the dominant call, and the CPU oracle timed on the host beside it.
+"""
+
+from __future__ import annotations
+
+import argparse
+import copy
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
+METRIC = "decode rows/sec + achieved HBM GB/s, QSA indexer+sparse GQA at 32k ctx"
+KERNEL_SOURCES = {
+    "qsa_compress": ["compress.hip"],
+    "qsa_index_logits_topk": ["select.hip"],
+    "qsa_sparse_gqa": ["gqa.hip"],
+}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="decode_32k")
+    p.add_argument("--rotate", type=int, default=4, help="input copies cycled through")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--profile-only", action="store_true",
+                   help="warm up and run the timed steps only (for rocprofv3)")
+    return p.parse_args()
+
+
+def clone_workload(wl):
+    """An independent copy of every tensor of the workload (same contents)."""
+    import torch
+    c = copy.copy(wl)
+    for k, v in vars(wl).items():
+        if isinstance(v, torch.Tensor):
+            setattr(c, k, v.clone())
+    return c
+
+
+def algorithmic_bytes(wl, packed):
+    """Bytes each call must move at minimum (read + write), from the workload's shapes and the
+    selection it produced.  Compressed keys count once per request (every visible key, read
+    once); K/V count once per selected token per KV head (the union of a request's rows'
+    selections; one row per request here); partials, logits scratch and re-reads are not
+    algorithmic."""
+    import numpy as np
+    T, Hi, Hq, Hkv = wl.num_tokens, wl.index_heads, wl.q_heads, wl.kv_heads
+    elt = 1 if wl.index_dtype == "fp8" else 2
+    W = wl.output_width
+    c = wl.compress_ratio
+    lens = wl.seq_lens_host
+    rows = wl.rows_host
+    groups = int(sum(L // c - (L - n) // c for L, n in zip(lens, rows)))
+    b_compress = (T * Hi * 128 * 2 + T * 128 * 2          # q_proj, k_proj
+                  + T * Hi * 128 * elt                     # q_idx written
+                  + groups * 128 * elt                     # compressed rows written
+                  + int(sum(min(16, n) for n in rows)) * 128 * 2)   # ring rows written
+    b_logits = (int(sum(L // c for L in lens)) * 128 * elt  # every visible compressed key
+                + T * Hi * 128 * elt + T * (W + 1) * 4)    # q_idx read, packed written
+    pk = packed.cpu().numpy()
+    req = wl.token_to_req.cpu().numpy()
+    kv_tokens = 0
+    for r in range(wl.num_requests):
+        sel = pk[req == r]
+        toks = set()
+        for row in sel:
+            toks.update(row[:row[W]].tolist())
+        kv_tokens += len(toks)
+    b_gqa = (kv_tokens * Hkv * 512                          # K and V rows of selected tokens
+             + T * Hq * 128 * 2 * 3                         # q, gate read; out written
+             + T * (W + 1) * 4)                             # packed read
+    return {"qsa_compress": b_compress, "qsa_index_logits_topk": b_logits,
+            "qsa_sparse_gqa": b_gqa}, int(np.int64(kv_tokens))
+
+
+def traffic_record(call):
+    """Per-launch HBM bytes measured by rocprofv3 counters for `call`, if the committed record
+    was taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(call)
+    if not rec:
+        return None
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[call]:
+        h.update(open(os.path.join(ROOT, "sparse_attention_qsa_amd", "csrc", f), "rb").read())
+    return rec["bytes_per_launch"] if rec.get("source_sha256") == h.hexdigest() else None
+
+
+def cpu_baseline(host_inputs, wl_meta):
+    """The oracle, as it stands, on the whole step of the same workload (host inputs taken
+    before any GPU step), single-threaded."""
+    from threadpoolctl import threadpool_limits
+
+    from tests.oracle_io import oracle_step
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        oracle_step(host_inputs)
+        dt = time.perf_counter() - t0
+    return {"value": round(wl_meta.num_tokens / dt, 3), "unit": "rows/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"the whole step ({wl_meta.num_tokens} rows of {wl_meta.name}) once, "
+                      f"{dt:.2f} s wall on one host core"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from sparse_attention_qsa_amd.step import QsaStep
+    from sparse_attention_qsa_amd.workloads import make_workload
+
+    dev = "cuda:0"
+    wl0 = make_workload(args.workload, device=dev)
+    host = None
+    if not args.no_cpu_baseline and not args.profile_only:
+        host = clone_workload(wl0)          # pre-state for the oracle (moved to the host below)
+        for k, v in vars(host).items():
+            if isinstance(v, torch.Tensor):
+                setattr(host, k, v.cpu())
+    wls = [wl0] + [clone_workload(wl0) for _ in range(max(0, args.rotate - 1))]
+    steps = [QsaStep(w) for w in wls]
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    for i in range(args.warmup):
+        steps[i % len(steps)].run(stream)
+    torch.cuda.synchronize()
+
+    # ---- the timed region: exactly K steps
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(args.steps):
+        steps[i % len(steps)].run(stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    if args.profile_only:
+        print(json.dumps({"profile_only": True, "ms_per_step": ms_step}))
+        return
+
+    # ---- per-call times (HIP events on the launch stream around each call)
+    per_call = {}
+    for call in ("qsa_compress", "qsa_index_logits_topk", "qsa_sparse_gqa"):
+        fn = {"qsa_compress": "compress", "qsa_index_logits_topk": "topk",
+              "qsa_sparse_gqa": "gqa"}[call]
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(evs):
+            st = steps[i % len(steps)]
+            a.record(stream)
+            getattr(st, fn)(stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        per_call[call] = sum(a.elapsed_time(b) for a, b in evs) / len(evs) * 1e3   # us
+
+    alg, kv_tokens = algorithmic_bytes(wl0, steps[0].packed)
+    step_bytes = sum(alg.values())
+    rows_per_s = wl0.num_tokens / (ms_step * 1e-3)
+    dom = max(per_call, key=per_call.get)
+    achieved = alg[dom] / (per_call[dom] * 1e-6) / 1e9
+    traffic = traffic_record(dom)
+
+    out = {
+        "metric": METRIC,
+        "value": round(rows_per_s, 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl0.name, "requests": wl0.num_requests,
+                   "context": int(wl0.max_seq_len), "rows_per_request": int(wl0.rows_host[0]),
+                   "index_heads": wl0.index_heads, "compress_ratio": wl0.compress_ratio,
+                   "budget": wl0.budget, "index_dtype": wl0.index_dtype,
+                   "q_heads": wl0.q_heads, "kv_heads": wl0.kv_heads, "head_dim": 128,
+                   "page_size": 16, "input_copies_rotated": len(steps),
+                   "gqa_splits": steps[0].num_splits},
+        "hbm_gbps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "step_algorithmic_bytes": int(step_bytes),
+        "per_call_us": {k: round(v, 2) for k, v in per_call.items()},
+        "per_call_algorithmic_bytes": {k: int(v) for k, v in alg.items()},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
+    }
+    if host is not None:
+        del steps, wls
+        torch.cuda.empty_cache()
+        out["cpu_baseline"] = cpu_baseline(host, wl0)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

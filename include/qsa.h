@@ -39,7 +39,8 @@
  *    indices) is bounds-checked in the kernels: an out-of-range page or index is masked
  *    exactly as documented per call, and no kernel ever reads or writes outside the buffers
  *    the sizes describe.  Faults inside a kernel surface at the caller's next stream sync.
- *  - num_tokens == 0 returns QSA_OK and launches nothing.
+ *  - num_tokens == 0 returns QSA_OK and launches nothing; no other argument is examined, so
+ *    empty tensors may pass NULL pointers.
  *  - Calls that write overlapping buffers must not run concurrently on different streams.
  */
 #ifndef QSA_H_

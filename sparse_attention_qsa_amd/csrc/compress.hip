@@ -108,9 +108,13 @@ __device__ __forceinline__ void ring_store_row(const CompressParams& P, int row,
 // Waves [0, T*Hi): indexer Q vectors.  Waves [T*Hi, T*Hi + T): the group (if any) completed by
 // row (wave - T*Hi), and -- when fuse_ring -- that row's ring write.
 __global__ __launch_bounds__(256) void prep_compress_kernel(CompressParams P) {
+  __shared__ int32_t qsl_s[kQslCap];
   const int lane = threadIdx.x & 63;
   const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const int64_t nq = (int64_t)P.T * P.Hi;
+  // Blocks holding compress waves stage the row offsets for the request lookups (block-uniform).
+  const int32_t* qsl = P.qsl;
+  if ((int64_t)(blockIdx.x + 1) * (blockDim.x >> 6) > nq) qsl = stage_qsl(P.qsl, P.R, qsl_s);
   if (wave < nq) {
     const int row = (int)(wave / P.Hi), h = (int)(wave % P.Hi);
     const uint32_t u = P.q_proj[(int64_t)row * P.q_rs + h * 64 + lane];
@@ -131,9 +135,9 @@ __global__ __launch_bounds__(256) void prep_compress_kernel(CompressParams P) {
   const int64_t row64 = wave - nq;
   if (row64 >= P.T) return;
   const int row = (int)row64;
-  const int r = find_request(P.qsl, P.R, row);
+  const int r = find_request(qsl, P.R, row);
   if (r < 0) return;
-  const int q0 = P.qsl[r], n = P.qsl[r + 1] - q0, L = P.seq_lens[r];
+  const int q0 = qsl[r], n = qsl[r + 1] - q0, L = P.seq_lens[r];
   const int start = L - n;
   if (start < 0) return;
   const int p = start + (row - q0);
@@ -187,13 +191,15 @@ __global__ __launch_bounds__(256) void prep_compress_kernel(CompressParams P) {
 // Separate ring update, launched after prep_compress_kernel when the step's writes could alias
 // slots that its reads still need (long prefill chunks).
 __global__ __launch_bounds__(256) void ring_store_kernel(CompressParams P) {
+  __shared__ int32_t qsl_s[kQslCap];
+  const int32_t* qsl = stage_qsl(P.qsl, P.R, qsl_s);
   const int lane = threadIdx.x & 63;
   const int64_t row64 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   if (row64 >= P.T) return;
   const int row = (int)row64;
-  const int r = find_request(P.qsl, P.R, row);
+  const int r = find_request(qsl, P.R, row);
   if (r < 0) return;
-  const int q0 = P.qsl[r], n = P.qsl[r + 1] - q0, L = P.seq_lens[r];
+  const int q0 = qsl[r], n = qsl[r + 1] - q0, L = P.seq_lens[r];
   if (L - n < 0) return;
   ring_store_row(P, row, r, L - n + (row - q0), L, lane);
 }

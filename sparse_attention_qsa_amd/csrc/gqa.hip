@@ -190,27 +190,28 @@ __global__ __launch_bounds__(64) void gqa_partial_kernel(GqaParams P) {
   }
 }
 
-// Grid (T, Hq), one wavefront: lane l merges dims 2l, 2l+1 of every split.
+// Grid (T, Hq), one wavefront.  Lane s reads split s's log-sum-exp (all splits at once), the
+// weights are formed in-wave, then lane l merges dims 2l, 2l+1 of every split with independent
+// loads.  splits <= 64.
 __global__ __launch_bounds__(64) void gqa_merge_kernel(GqaParams P) {
   const int row = blockIdx.x, hq = blockIdx.y, lane = threadIdx.x;
-  float M = -INFINITY;
-  for (int s = 0; s < P.splits; ++s)
-    M = fmaxf(M, P.part_lse[((int64_t)s * P.T + row) * P.Hq + hq]);
+  const int64_t stride = (int64_t)P.T * P.Hq;   // between splits
+  const int64_t pi0 = (int64_t)row * P.Hq + hq;
+  const float lse = lane < P.splits ? P.part_lse[lane * stride + pi0] : -INFINITY;
+  const float M = wave_max(lse);
   float o0 = 0.0f, o1 = 0.0f;
   if (M != -INFINITY) {
-    float den = 0.0f;
+    const float wgt = lse == -INFINITY ? 0.0f : exp2f(lse - M);
+    const float inv = 1.0f / wave_sum(wgt);
+#pragma unroll 8
     for (int s = 0; s < P.splits; ++s) {
-      const int64_t pi = ((int64_t)s * P.T + row) * P.Hq + hq;
-      const float lse = P.part_lse[pi];
-      if (lse == -INFINITY) continue;
-      const float wgt = exp2f(lse - M);
-      const float2 o = reinterpret_cast<const float2*>(P.part_o + pi * kHeadDim)[lane];
-      o0 += wgt * o.x;
-      o1 += wgt * o.y;
-      den += wgt;
+      const float ws = __shfl(wgt, s, kWave);
+      const float2 o = reinterpret_cast<const float2*>(P.part_o + (s * stride + pi0) * kHeadDim)[lane];
+      o0 += ws * o.x;
+      o1 += ws * o.y;
     }
-    o0 /= den;
-    o1 /= den;
+    o0 *= inv;
+    o1 *= inv;
     if (P.gate) {
       const uint32_t gp = reinterpret_cast<const uint32_t*>(
           P.gate + (int64_t)row * P.g_rs + (int64_t)hq * P.g_hs)[lane];
@@ -241,6 +242,7 @@ GqaPlan gqa_plan(const qsa_gqa_args& a) {
     target = base >= 2048 ? 1 : (int)((2048 + base - 1) / base);
   }
   if (target > p.tiles) target = p.tiles;
+  if (target > 64) target = 64;  // the merge reads one split per lane
   p.tiles_per_split = (p.tiles + target - 1) / target;
   p.splits = (p.tiles + p.tiles_per_split - 1) / p.tiles_per_split;
   p.ws_bytes = 0;

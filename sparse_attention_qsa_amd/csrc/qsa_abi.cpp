@@ -81,8 +81,8 @@ qsa_status validate_topk(const qsa_topk_args* a) {
                   a->c_block_table_stride >= a->c_block_table_width,
               kInval);
   QSA_REQUIRE(aligned(a->ckv, 16) && aligned(a->q_idx, 4) && aligned(a->packed, 4), kInval);
-  // The per-row selection mask lives in LDS.
-  QSA_REQUIRE((int64_t)(a->max_seq_len / a->compress_ratio + 31) / 32 * 4 <= 48 * 1024, kNotSup);
+  // A row's fast scores are held in the registers of one workgroup.
+  QSA_REQUIRE(a->max_seq_len / a->compress_ratio <= qsa::kTopkMaxCols, kNotSup);
   return QSA_OK;
 }
 
@@ -149,8 +149,9 @@ const char* qsa_status_string(qsa_status s) {
 }
 
 qsa_status qsa_compress(const qsa_compress_args* a, void* stream) {
+  if (a == nullptr || a->num_tokens < 0) return kInval;
+  if (a->num_tokens == 0) return QSA_OK;  // nothing else is examined
   if (qsa_status s = validate_compress(a)) return s;
-  if (a->num_tokens == 0) return QSA_OK;
   return from_hip(qsa::launch_compress(*a, reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -161,8 +162,9 @@ size_t qsa_index_logits_topk_workspace_size(const qsa_topk_args* a) {
 
 qsa_status qsa_index_logits_topk(const qsa_topk_args* a, void* ws, size_t ws_bytes,
                                  void* stream) {
+  if (a == nullptr || a->num_tokens < 0) return kInval;
+  if (a->num_tokens == 0) return QSA_OK;  // nothing else is examined
   if (qsa_status s = validate_topk(a)) return s;
-  if (a->num_tokens == 0) return QSA_OK;
   const qsa::TopkLayout L = qsa::topk_layout(*a);
   if (ws == nullptr || ws_bytes < L.total) return QSA_ERR_WORKSPACE_TOO_SMALL;
   if (!aligned(ws, 256)) return kInval;
@@ -181,8 +183,9 @@ size_t qsa_sparse_gqa_workspace_size(const qsa_gqa_args* a) {
 }
 
 qsa_status qsa_sparse_gqa(const qsa_gqa_args* a, void* ws, size_t ws_bytes, void* stream) {
+  if (a == nullptr || a->num_tokens < 0) return kInval;
+  if (a->num_tokens == 0) return QSA_OK;  // nothing else is examined
   if (qsa_status s = validate_gqa(a)) return s;
-  if (a->num_tokens == 0) return QSA_OK;
   const qsa::GqaPlan plan = qsa::gqa_plan(*a);
   if (plan.ws_bytes > 0) {
     if (ws == nullptr || ws_bytes < plan.ws_bytes) return QSA_ERR_WORKSPACE_TOO_SMALL;

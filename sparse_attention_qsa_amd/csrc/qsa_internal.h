@@ -25,8 +25,6 @@ struct TopkLayout {
   int32_t col_stride;     // row stride of the per-row arrays (cols rounded up)
   int32_t key_tiles;      // column tiles of the logits kernel per request
   size_t off_logits;      // float  [T, col_stride]
-  size_t off_qfold;       // float  [T, 128]
-  size_t off_qabs;        // double [T]
   size_t off_kmax;        // float  [R, key_tiles]
   size_t off_band_idx;    // int32  [T, col_stride]
   size_t off_band_score;  // double [T, col_stride]
@@ -34,7 +32,7 @@ struct TopkLayout {
 };
 
 constexpr int kLogitsKeysPerWG = 256;  // 4 waves x 64 keys
-constexpr int kTopkThreads = 512;
+constexpr int kTopkMaxCols = 32768;    // register-resident top-k: 1024 threads x 32 scores
 
 TopkLayout topk_layout(const qsa_topk_args& a);
 
@@ -111,6 +109,16 @@ __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
   return v;
+}
+
+// Stages the row offsets qsl[0..R] in LDS (when they fit) so that request lookups do not
+// chain dependent global loads.  Every thread of the block must call it.
+constexpr int kQslCap = 2048;
+__device__ __forceinline__ const int32_t* stage_qsl(const int32_t* qsl, int R, int32_t* lds) {
+  if (R + 1 > kQslCap) return qsl;
+  for (int i = threadIdx.x; i <= R; i += blockDim.x) lds[i] = qsl[i];
+  __syncthreads();
+  return lds;
 }
 
 // Request owning `row`, by binary search over the row offsets [R+1]; -1 if none.

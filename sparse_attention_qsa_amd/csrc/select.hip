@@ -30,8 +30,6 @@ struct SelectParams {
   int32_t* packed;
   int64_t p_rs;
   float* logits;
-  float* qfold;
-  double* qabs;
   float* kmax;
   int32_t* band_idx;
   double* band_score;
@@ -40,27 +38,6 @@ struct SelectParams {
 __device__ __forceinline__ float load_q_value(const SelectParams& P, int64_t idx) {
   if (P.fp8) return e4m3_to_f32_exact(reinterpret_cast<const uint8_t*>(P.q_idx)[idx]);
   return bf16_to_f32(reinterpret_cast<const uint16_t*>(P.q_idx)[idx]);
-}
-
-// Per row: qfold[d] = sum_h q[h, d] (float32, heads in order), qabs = sum_{h,d} |q[h, d]|.
-__global__ __launch_bounds__(128) void fold_q_kernel(SelectParams P) {
-  const int row = blockIdx.x, d = threadIdx.x;
-  const int64_t base = (int64_t)row * P.Hi * kHeadDim;
-  float f = 0.0f;
-  double a = 0.0;
-  for (int h = 0; h < P.Hi; ++h) {
-    const float v = load_q_value(P, base + h * kHeadDim + d);
-    f = (h == 0) ? v : f + v;
-    a += fabs((double)v);
-  }
-  P.qfold[(int64_t)row * kHeadDim + d] = f;
-  __shared__ double red[2];
-  a = __shfl_xor(a, 1, kWave) + a;
-#pragma unroll
-  for (int m = 2; m <= 32; m <<= 1) a += __shfl_xor(a, m, kWave);
-  if ((d & 63) == 0) red[d >> 6] = a;
-  __syncthreads();
-  if (d == 0) P.qabs[row] = red[0] + red[1];
 }
 
 // Compressed row j of request r: element offset of its first value, or -1 if its page is
@@ -73,43 +50,14 @@ __device__ __forceinline__ int64_t key_row(const SelectParams& P, int r, int j) 
   return ((int64_t)page * P.Pc + (j % P.Pc)) * kHeadDim;
 }
 
-// Loads this lane's 16 dims (part*16 .. part*16+15) of key j as floats.
-__device__ __forceinline__ void load_key16(const SelectParams& P, int64_t off, int part,
-                                           float* k) {
-  if (off < 0) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) k[i] = 0.0f;
-    return;
-  }
-  if (P.fp8) {
-    const uint4 v = *reinterpret_cast<const uint4*>(
-        reinterpret_cast<const uint8_t*>(P.ckv) + off + part * 16);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], false);
-      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], true);
-      k[4 * i + 0] = lo[0];
-      k[4 * i + 1] = lo[1];
-      k[4 * i + 2] = hi[0];
-      k[4 * i + 3] = hi[1];
-    }
-  } else {
-    const uint4* src = reinterpret_cast<const uint4*>(
-        reinterpret_cast<const uint16_t*>(P.ckv) + off + part * 16);
-    const uint4 a = src[0], b = src[1];
-    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      k[2 * i] = bf16lo(w[i]);
-      k[2 * i + 1] = bf16hi(w[i]);
-    }
-  }
-}
+// ------------------------------------------------------------------------------ logits
 
-// Grid (key_tiles, R), 256 threads.  Eight lanes share a key (16 dims each), so a wave reads
-// eight consecutive compressed rows -- 2 KiB (bf16) or 1 KiB (fp8) of contiguous cache -- per
-// load.  Every row of the request is scored against the tile's 256 keys.
+// Grid (key_tiles, R), 256 threads: 256 keys of one request per workgroup.  Eight lanes share a
+// key (16 dims each), so one wave load reads eight consecutive compressed rows -- 2 KiB (bf16)
+// or 1 KiB (fp8) of contiguous cache.  Each lane issues all of its 8 keys' loads before any
+// math; the request's rows are folded over the heads into LDS four at a time and scored against
+// the keys held in registers.
+template <bool FP8>
 __global__ __launch_bounds__(256) void logits_valu_kernel(SelectParams P) {
   const int r = blockIdx.y, tile = blockIdx.x;
   // Row range of the request, clamped into [0, T): the metadata is device data the host never
@@ -119,51 +67,83 @@ __global__ __launch_bounds__(256) void logits_valu_kernel(SelectParams P) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, kg = lane >> 3, part = lane & 7;
   const int vis_max = (n > 0 && n <= L) ? min(L / P.c, P.cols) : 0;
   const int j0 = tile * kLogitsKeysPerWG;
+  __shared__ float qf_s[4][kHeadDim];
   __shared__ float red[4];
   float kmax = 0.0f;
-  if (j0 < vis_max) {
-    for (int half = 0; half < 2; ++half) {
-      float k[4][16];
-      int jj[4];
+  if (j0 < vis_max) {  // block-uniform
+    constexpr int kWords = FP8 ? 4 : 8;   // uint32 words of this lane's 16 dims
+    uint32_t raw[8][kWords];
+    int jj[8];
+    const char* base = reinterpret_cast<const char*>(P.ckv);
 #pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const int j = j0 + w * 64 + (half * 4 + it) * 8 + kg;
-        jj[it] = j;
-        load_key16(P, j < vis_max ? key_row(P, r, j) : -1, part, k[it]);
+    for (int it = 0; it < 8; ++it) {
+      const int j = j0 + w * 64 + it * 8 + kg;
+      jj[it] = j;
+      const int64_t off = j < vis_max ? key_row(P, r, j) : -1;
+      // An invalid key reads the cache's first row and is zeroed below.
+      const uint4* src = reinterpret_cast<const uint4*>(
+          base + (off < 0 ? 0 : off) * (FP8 ? 1 : 2) + part * (FP8 ? 16 : 32));
 #pragma unroll
-        for (int i = 0; i < 16; ++i) kmax = fmaxf(kmax, fabsf(k[it][i]));
+      for (int v = 0; v < kWords / 4; ++v) {
+        const uint4 x = src[v];
+        raw[it][4 * v] = off < 0 ? 0u : x.x;
+        raw[it][4 * v + 1] = off < 0 ? 0u : x.y;
+        raw[it][4 * v + 2] = off < 0 ? 0u : x.z;
+        raw[it][4 * v + 3] = off < 0 ? 0u : x.w;
       }
-      for (int rr0 = 0; rr0 < n; rr0 += 4) {
-        float qf[4][16];
+    }
+    for (int rr0 = 0; rr0 < n; rr0 += 4) {
+      const int nr = min(4, n - rr0);
+      __syncthreads();  // the previous chunk's readers are done with qf_s
+      for (int e = threadIdx.x; e < nr * kHeadDim; e += 256) {
+        const int rr = e >> 7, d = e & (kHeadDim - 1);
+        const int64_t qb = (int64_t)(q0 + rr0 + rr) * P.Hi * kHeadDim + d;
+        float f = load_q_value(P, qb);
+        for (int h = 1; h < P.Hi; ++h) f = f + load_q_value(P, qb + h * kHeadDim);
+        qf_s[rr][d] = f;
+      }
+      __syncthreads();
+      float qf[4][16];
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int row = q0 + rr0 + (rr0 + rr < n ? rr : 0);
-          const float4* src =
-              reinterpret_cast<const float4*>(P.qfold + (int64_t)row * kHeadDim + part * 16);
+      for (int rr = 0; rr < 4; ++rr) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) qf[rr][i] = rr < nr ? qf_s[rr][part * 16 + i] : 0.0f;
+      }
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        float k[16];
+        if (FP8) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float4 v = src[i];
-            qf[rr][4 * i] = v.x;
-            qf[rr][4 * i + 1] = v.y;
-            qf[rr][4 * i + 2] = v.z;
-            qf[rr][4 * i + 3] = v.w;
+            const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(raw[it][i], false);
+            const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(raw[it][i], true);
+            k[4 * i] = lo[0];
+            k[4 * i + 1] = lo[1];
+            k[4 * i + 2] = hi[0];
+            k[4 * i + 3] = hi[1];
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            k[2 * i] = bf16lo(raw[it][i]);
+            k[2 * i + 1] = bf16hi(raw[it][i]);
           }
         }
+        if (rr0 == 0) {
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
+          for (int i = 0; i < 16; ++i) kmax = fmaxf(kmax, fabsf(k[i]));
+        }
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            if (rr0 + rr >= n) break;  // wave-uniform
-            float d = 0.0f;
+        for (int rr = 0; rr < 4; ++rr) {
+          if (rr >= nr) break;  // wave-uniform
+          float d = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) d = fmaf(qf[rr][i], k[it][i], d);
-            d += __shfl_xor(d, 1, kWave);
-            d += __shfl_xor(d, 2, kWave);
-            d += __shfl_xor(d, 4, kWave);
-            if (part == rr && rr0 + rr < n && jj[it] < vis_max) {
-              P.logits[(int64_t)(q0 + rr0 + rr) * P.col_stride + jj[it]] = d;
-            }
-          }
+          for (int i = 0; i < 16; ++i) d = fmaf(qf[rr][i], k[i], d);
+          d += __shfl_xor(d, 1, kWave);
+          d += __shfl_xor(d, 2, kWave);
+          d += __shfl_xor(d, 4, kWave);
+          if (part == rr && jj[it] < vis_max)
+            P.logits[(int64_t)(q0 + rr0 + rr) * P.col_stride + jj[it]] = d;
         }
       }
     }
@@ -171,10 +151,11 @@ __global__ __launch_bounds__(256) void logits_valu_kernel(SelectParams P) {
   kmax = wave_max(kmax);
   if (lane == 0) red[w] = kmax;
   __syncthreads();
-  if (threadIdx.x == 0 && tile < P.key_tiles) {
+  if (threadIdx.x == 0)
     P.kmax[(int64_t)r * P.key_tiles + tile] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  }
 }
+
+// ------------------------------------------------------------------------------ top-k
 
 // Order-preserving map of float32 onto uint32 (larger float -> larger key).
 __device__ __forceinline__ uint32_t fkey(float f) {
@@ -185,7 +166,7 @@ __device__ __forceinline__ float fval(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-template <typename T>
+template <int NT, typename T>
 __device__ __forceinline__ T block_sum(T v, T* scratch) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
@@ -194,7 +175,7 @@ __device__ __forceinline__ T block_sum(T v, T* scratch) {
   if (lane == 0) scratch[w] = v;
   __syncthreads();
   T s = 0;
-  for (int i = 0; i < kTopkThreads / 64; ++i) s += scratch[i];
+  for (int i = 0; i < NT / 64; ++i) s += scratch[i];
   return s;
 }
 
@@ -229,49 +210,70 @@ __device__ double canonical_score(const SelectParams& P, const float* qrow, int 
   return s;
 }
 
-// One workgroup per row.
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelectParams P) {
+// One workgroup of NT threads per row; thread t holds the fast scores of blocks
+// t*E .. t*E+E-1 in registers for the whole selection.
+template <int NT, int E>
+__global__ __launch_bounds__(NT) void topk_kernel(SelectParams P) {
   extern __shared__ uint32_t sel_mask[];  // [ceil(cols / 32)] band-selected blocks
+  __shared__ int32_t qsl_s[kQslCap];
   __shared__ int hist[256];
   __shared__ int s_int[4];
-  __shared__ int s_wave[kTopkThreads / 64];
-  __shared__ double s_dbl[kTopkThreads / 64];
+  __shared__ int s_wave[NT / 64];
+  __shared__ double s_dbl[NT / 64];
   __shared__ float qrow[16 * kHeadDim];
 
   const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int W = P.budget + P.c - 1, kb = P.budget / P.c;
   int32_t* out = P.packed + (int64_t)row * P.p_rs;
-  const int r = find_request(P.qsl, P.R, row);
+  const int32_t* qsl = stage_qsl(P.qsl, P.R, qsl_s);
+  const int r = find_request(qsl, P.R, row);
   int p = -1, L = 0;
   if (r >= 0) {
-    const int q0 = P.qsl[r], n = P.qsl[r + 1] - q0;
+    const int q0 = qsl[r], n = qsl[r + 1] - q0;
     L = P.seq_lens[r];
     if (L - n >= 0) p = L - n + (row - q0);
   }
   if (p < 0) {  // inert row: no entries, count 0
-    for (int col = tid; col <= W; col += kTopkThreads) out[col] = col < W ? -1 : 0;
+    for (int col = tid; col <= W; col += NT) out[col] = col < W ? -1 : 0;
     return;
   }
   // seq_lens beyond the max_seq_len the workspace was sized for would overrun the logits
   // row: such rows are clamped (their selection is then undefined but stays in bounds).
   const int vis = min((p + 1) / P.c, P.cols);
   const int tail = min(p + 1 - vis * P.c, P.c - 1);
-  if (vis <= kb) {  // every visible block: tokens 0..p
-    for (int col = tid; col <= W; col += kTopkThreads)
-      out[col] = col <= p ? col : (col < W ? -1 : p + 1);
+  if (vis <= kb) {  // every visible block: tokens 0..vis*c+tail-1
+    const int cnt = vis * P.c + tail;
+    for (int col = tid; col <= W; col += NT) out[col] = col < cnt ? col : (col < W ? -1 : cnt);
     return;
   }
-  const float* lg = P.logits + (int64_t)row * P.col_stride;
 
-  // ---- kb-th largest fast score: 4-pass MSB-first radix select on the order-preserving keys.
+  // ---- this thread's scores (vectorised loads; the row is padded to col_stride)
+  const float* lg = P.logits + (int64_t)row * P.col_stride;
+  const int jb = tid * E;
+  float sc[E];
+#pragma unroll
+  for (int i = 0; i < E; i += 4) {
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (jb + i < P.col_stride) v = *reinterpret_cast<const float4*>(lg + jb + i);
+    sc[i] = v.x;
+    sc[i + 1] = v.y;
+    sc[i + 2] = v.z;
+    sc[i + 3] = v.w;
+  }
+  // Q row (for the band re-scoring and the error bound), float copies of exact values.
+  for (int i = tid; i < P.Hi * kHeadDim; i += NT)
+    qrow[i] = load_q_value(P, (int64_t)row * P.Hi * kHeadDim + i);
+
+  // ---- kb-th largest fast score: 4-pass MSB-first radix select on order-preserving keys
   uint32_t prefix = 0, pmask = 0;
   int krem = kb;
   for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 256; i += kTopkThreads) hist[i] = 0;
+    for (int i = tid; i < 256; i += NT) hist[i] = 0;
     __syncthreads();
-    for (int j = tid; j < vis; j += kTopkThreads) {
-      const uint32_t u = fkey(lg[j]);
-      if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 0xFFu], 1);
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const uint32_t u = fkey(sc[i]);
+      if (jb + i < vis && (u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 0xFFu], 1);
     }
     __syncthreads();
     if (w == 0) {
@@ -298,94 +300,106 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelectParams P) {
     prefix |= (uint32_t)s_int[0] << shift;
     pmask |= 0xFFu << shift;
     krem = s_int[1];
-    __syncthreads();
   }
   const double Tk = (double)fval(prefix);
 
-  // ---- error bound E of the fast scores for this row.
+  // ---- error bound E of the fast scores for this row
   float km = 0.0f;
   const int nt = min(P.key_tiles, (L / P.c + kLogitsKeysPerWG - 1) / kLogitsKeysPerWG);
-  for (int t = tid; t < nt; t += kTopkThreads) km = fmaxf(km, P.kmax[(int64_t)r * P.key_tiles + t]);
+  for (int t = tid; t < nt; t += NT) km = fmaxf(km, P.kmax[(int64_t)r * P.key_tiles + t]);
+  double qa = 0.0;
+  for (int i = tid; i < P.Hi * kHeadDim; i += NT) qa += fabs((double)qrow[i]);
   km = wave_max(km);
   if (lane == 0) s_dbl[w] = km;
   __syncthreads();
   double kappa = 0.0;
-  for (int i = 0; i < kTopkThreads / 64; ++i) kappa = fmax(kappa, s_dbl[i]);
+  for (int i = 0; i < NT / 64; ++i) kappa = fmax(kappa, s_dbl[i]);
+  const double A = block_sum<NT>(qa, s_dbl);
   const double gam = (double)(P.Hi + 130) * 0x1p-24;
-  const double E = 2.0 * gam / (1.0 - gam) * kappa * P.qabs[row] + 1e-30;
-  const double hi = Tk + 2.0 * E, lo = Tk - 2.0 * E;
+  const double Ebound = 2.0 * gam / (1.0 - gam) * kappa * A + 1e-30;
+  const double hi = Tk + 2.0 * Ebound, lo = Tk - 2.0 * Ebound;
 
-  // ---- classify; collect the band.
+  // ---- classify; collect the band
   const int mask_words = (vis + 31) >> 5;
-  for (int i = tid; i < mask_words; i += kTopkThreads) sel_mask[i] = 0u;
-  for (int i = tid; i < 16 * kHeadDim; i += kTopkThreads)
-    qrow[i] = i < P.Hi * kHeadDim ? load_q_value(P, (int64_t)row * P.Hi * kHeadDim + i) : 0.0f;
+  for (int i = tid; i < mask_words; i += NT) sel_mask[i] = 0u;
   if (tid == 0) s_int[2] = 0;
   __syncthreads();
   int32_t* bidx = P.band_idx + (int64_t)row * P.col_stride;
   double* bscore = P.band_score + (int64_t)row * P.col_stride;
   int n_in_local = 0;
-  for (int j = tid; j < vis; j += kTopkThreads) {
-    const double s = lg[j];
-    if (s > hi) {
-      ++n_in_local;
-    } else if (s >= lo) {
-      bidx[atomicAdd(&s_int[2], 1)] = j;
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const double s = sc[i];
+    if (jb + i < vis) {
+      if (s > hi) ++n_in_local;
+      else if (s >= lo) bidx[atomicAdd(&s_int[2], 1)] = jb + i;
     }
   }
-  const int n_in = block_sum(n_in_local, s_wave);
+  const int n_in = block_sum<NT>(n_in_local, s_wave);
   const int nb = s_int[2];
 
-  // ---- re-score the band in float64, canonical order (one wave per block).
-  for (int b = w; b < nb; b += kTopkThreads / 64) {
+  // ---- re-score the band in float64, canonical order (one wave per block)
+  for (int b = w; b < nb; b += NT / 64) {
     const double s = canonical_score(P, qrow, r, bidx[b], lane);
     if (lane == 0) bscore[b] = s;
   }
   __syncthreads();
 
-  // ---- rank the band: keep its (kb - n_in) best by (score desc, block asc).
+  // ---- rank the band: keep its (kb - n_in) best by (score desc, block asc)
   const int need = kb - n_in;
-  for (int b = tid; b < nb; b += kTopkThreads) {
+  for (int b = tid; b < nb; b += NT) {
     const double sb = bscore[b];
-    const int jb = bidx[b];
+    const int jbb = bidx[b];
     int rank = 0;
     for (int b2 = 0; b2 < nb; ++b2) {
       const double s2 = bscore[b2];
-      rank += (s2 > sb) || (s2 == sb && bidx[b2] < jb);
+      rank += (s2 > sb) || (s2 == sb && bidx[b2] < jbb);
     }
-    if (rank < need) atomicOr(&sel_mask[jb >> 5], 1u << (jb & 31));
+    if (rank < need) atomicOr(&sel_mask[jbb >> 5], 1u << (jbb & 31));
   }
   __syncthreads();
 
-  // ---- stable compaction in block order and expansion into tokens.
-  int base = 0;
-  for (int cs = 0; cs < vis; cs += kTopkThreads) {
-    const int j = cs + tid;
-    bool f = false;
-    if (j < vis) f = ((double)lg[j] > hi) || ((sel_mask[j >> 5] >> (j & 31)) & 1u);
-    const uint64_t bal = __ballot(f);
-    const int lp = __popcll(bal & ((1ull << lane) - 1ull));
-    if (lane == 0) s_wave[w] = __popcll(bal);
-    __syncthreads();
-    int woff = 0, total = 0;
-    for (int i = 0; i < kTopkThreads / 64; ++i) {
-      woff += i < w ? s_wave[i] : 0;
-      total += s_wave[i];
-    }
-    if (f) {
-      const int pos = base + woff + lp;
+  // ---- stable compaction in block order (one block-wide scan) and expansion into tokens
+  int cnt = 0;
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const int j = jb + i;
+    cnt += (j < vis) && ((double)sc[i] > hi || ((sel_mask[j >> 5] >> (j & 31)) & 1u));
+  }
+  int incl = cnt;  // inclusive scan within the wave
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(incl, d, kWave);
+    if (lane >= d) incl += y;
+  }
+  if (lane == 63) s_wave[w] = incl;
+  __syncthreads();
+  int pos = incl - cnt, total = 0;
+  for (int i = 0; i < NT / 64; ++i) {
+    pos += i < w ? s_wave[i] : 0;
+    total += s_wave[i];
+  }
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const int j = jb + i;
+    if ((j < vis) && ((double)sc[i] > hi || ((sel_mask[j >> 5] >> (j & 31)) & 1u))) {
       if (pos < kb)
         for (int m = 0; m < P.c; ++m) out[pos * P.c + m] = j * P.c + m;
+      ++pos;
     }
-    base += total;
-    __syncthreads();
   }
-  const int sel = min(base, kb), cnt = sel * P.c + tail;
-  for (int col = tid; col <= W; col += kTopkThreads) {
+  const int sel = min(total, kb), count = sel * P.c + tail;
+  for (int col = tid; col <= W; col += NT) {
     if (col < sel * P.c) continue;
-    if (col < cnt) out[col] = vis * P.c + (col - sel * P.c);
-    else out[col] = col < W ? -1 : cnt;
+    if (col < count) out[col] = vis * P.c + (col - sel * P.c);
+    else out[col] = col < W ? -1 : count;
   }
+}
+
+template <int NT, int E>
+hipError_t launch_topk_kernel(const SelectParams& P, size_t mask_bytes, hipStream_t s) {
+  hipLaunchKernelGGL((topk_kernel<NT, E>), dim3(P.T), dim3(NT), mask_bytes, s, P);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -400,8 +414,6 @@ TopkLayout topk_layout(const qsa_topk_args& a) {
   auto align = [](size_t x) { return (x + 255) / 256 * 256; };
   size_t off = 0;
   L.off_logits = off;     off = align(off + (size_t)T * L.col_stride * sizeof(float));
-  L.off_qfold = off;      off = align(off + (size_t)T * kHeadDim * sizeof(float));
-  L.off_qabs = off;       off = align(off + (size_t)T * sizeof(double));
   L.off_kmax = off;       off = align(off + (size_t)R * L.key_tiles * sizeof(float));
   L.off_band_idx = off;   off = align(off + (size_t)T * L.col_stride * sizeof(int32_t));
   L.off_band_score = off; off = align(off + (size_t)T * L.col_stride * sizeof(double));
@@ -432,21 +444,22 @@ hipError_t launch_topk(const qsa_topk_args& a, const TopkLayout& L, char* ws, hi
   P.packed = a.packed;
   P.p_rs = a.packed_row_stride;
   P.logits = reinterpret_cast<float*>(ws + L.off_logits);
-  P.qfold = reinterpret_cast<float*>(ws + L.off_qfold);
-  P.qabs = reinterpret_cast<double*>(ws + L.off_qabs);
   P.kmax = reinterpret_cast<float*>(ws + L.off_kmax);
   P.band_idx = reinterpret_cast<int32_t*>(ws + L.off_band_idx);
   P.band_score = reinterpret_cast<double*>(ws + L.off_band_score);
 
-  hipLaunchKernelGGL(fold_q_kernel, dim3(P.T), dim3(128), 0, s, P);
+  if (P.fp8) {
+    hipLaunchKernelGGL(logits_valu_kernel<true>, dim3(L.key_tiles, P.R), dim3(256), 0, s, P);
+  } else {
+    hipLaunchKernelGGL(logits_valu_kernel<false>, dim3(L.key_tiles, P.R), dim3(256), 0, s, P);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(logits_valu_kernel, dim3(L.key_tiles, P.R), dim3(256), 0, s, P);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const size_t mask_bytes = (size_t)(L.cols + 31) / 32 * sizeof(uint32_t);
-  hipLaunchKernelGGL(topk_kernel, dim3(P.T), dim3(kTopkThreads), mask_bytes, s, P);
-  return hipGetLastError();
+  if (L.cols <= 512 * 8) return launch_topk_kernel<512, 8>(P, mask_bytes, s);
+  if (L.cols <= 512 * 16) return launch_topk_kernel<512, 16>(P, mask_bytes, s);
+  if (L.cols <= 512 * 32) return launch_topk_kernel<512, 32>(P, mask_bytes, s);
+  return launch_topk_kernel<1024, 32>(P, mask_bytes, s);
 }
 
 }  // namespace qsa

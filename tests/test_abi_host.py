@@ -119,5 +119,9 @@ def test_invalid_calls_are_rejected_before_any_launch():
     assert lib.qsa_index_logits_topk(C.byref(_topk(num_tokens=0)), None, 0, None) == 0
     assert lib.qsa_index_logits_topk_workspace_size(C.byref(_topk(head_dim=64))) == 0
     c = B.CompressArgs()
-    assert lib.qsa_compress(C.byref(c), None) == INVAL
+    assert lib.qsa_compress(C.byref(c), None) == 0           # zero rows: a no-op
+    c.num_tokens, c.num_requests = 1, 1
+    assert lib.qsa_compress(C.byref(c), None) == NOTSUP      # head_dim 0
+    c.head_dim, c.rotary_dim, c.num_index_heads, c.compress_ratio = 128, 64, 8, 4
+    assert lib.qsa_compress(C.byref(c), None) == INVAL       # NULL tensors
     assert lib.qsa_compress(None, None) == INVAL
