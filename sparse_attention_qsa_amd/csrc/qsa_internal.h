@@ -23,15 +23,16 @@ struct CompressPlan {
 struct TopkLayout {
   int32_t cols;           // compressed columns per row (max_seq_len / c, >= 1)
   int32_t col_stride;     // row stride of the per-row arrays (cols rounded up)
-  int32_t key_tiles;      // column tiles of the logits kernel per request
+  int32_t key_tiles;      // logits workgroups per request (kLogitsTilesPerWG tiles each)
   size_t off_logits;      // float  [T, col_stride]
-  size_t off_kmax;        // float  [R, key_tiles]
+  size_t off_kmax;        // float  [R, key_tiles]: max |k| seen by each logits workgroup
   size_t off_band_idx;    // int32  [T, col_stride]
   size_t off_band_score;  // double [T, col_stride]
   size_t total;
 };
 
-constexpr int kLogitsKeysPerWG = 256;  // 4 waves x 64 keys
+constexpr int kLogitsKeysPerWG = 256;  // keys per tile: 4 waves x 64 keys
+constexpr int kLogitsTilesPerWG = 4;   // tiles walked by one logits workgroup
 constexpr int kTopkMaxCols = 32768;    // register-resident top-k: 1024 threads x 32 scores
 
 TopkLayout topk_layout(const qsa_topk_args& a);

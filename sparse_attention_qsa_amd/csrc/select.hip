@@ -52,49 +52,117 @@ __device__ __forceinline__ int64_t key_row(const SelectParams& P, int r, int j) 
 
 // ------------------------------------------------------------------------------ logits
 
-// Grid (key_tiles, R), 256 threads: 256 keys of one request per workgroup.  Eight lanes share a
-// key (16 dims each), so one wave load reads eight consecutive compressed rows -- 2 KiB (bf16)
-// or 1 KiB (fp8) of contiguous cache.  Each lane issues all of its 8 keys' loads before any
-// math; the request's rows are folded over the heads into LDS four at a time and scored against
-// the keys held in registers.
+// Loads this lane's 16 dims of the 8 keys it owns in a 256-key tile (keys j0 + w*64 + it*8 + kg,
+// it = 0..7) into raw 32-bit words.  Pages come from the LDS-staged block-table slice; a key
+// whose page is out of range reads the cache's first row and is zeroed.
 template <bool FP8>
+__device__ __forceinline__ void load_key_tile(const SelectParams& P, const int32_t* pages,
+                                              int col0, int ncols, int j0, int vis_max, int w,
+                                              int kg, int part,
+                                              uint32_t (&raw)[8][FP8 ? 4 : 8]) {
+  constexpr int kWords = FP8 ? 4 : 8;
+  const char* base = reinterpret_cast<const char*>(P.ckv);
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int j = j0 + w * 64 + it * 8 + kg;
+    const int c = j / P.Pc - col0;
+    const int page = (j < vis_max && c >= 0 && c < ncols) ? pages[c] : -1;
+    const bool ok = page >= 0 && page < P.c_pages;
+    const int64_t off = ok ? ((int64_t)page * P.Pc + (j % P.Pc)) * kHeadDim : 0;
+    const uint4* src = reinterpret_cast<const uint4*>(base + off * (FP8 ? 1 : 2) +
+                                                      part * (FP8 ? 16 : 32));
+#pragma unroll
+    for (int v = 0; v < kWords / 4; ++v) {
+      const uint4 x = src[v];
+      raw[it][4 * v] = ok ? x.x : 0u;
+      raw[it][4 * v + 1] = ok ? x.y : 0u;
+      raw[it][4 * v + 2] = ok ? x.z : 0u;
+      raw[it][4 * v + 3] = ok ? x.w : 0u;
+    }
+  }
+}
+
+// Scores the 8 keys of `raw` against NR folded rows (held per lane as 16 dims each) and writes
+// the logits; lanes part == rr write row rr.  Updates the lane's running max |k|.
+template <bool FP8, int NR>
+__device__ __forceinline__ void score_key_tile(const SelectParams& P,
+                                               const uint32_t (&raw)[8][FP8 ? 4 : 8],
+                                               const float (&qf)[NR][16], int nr, int row0,
+                                               int j0, int vis_max, int w, int kg, int part,
+                                               bool track_kmax, float& kmax) {
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int j = j0 + w * 64 + it * 8 + kg;
+    float k[16];
+    if (FP8) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(raw[it][i], false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(raw[it][i], true);
+        k[4 * i] = lo[0];
+        k[4 * i + 1] = lo[1];
+        k[4 * i + 2] = hi[0];
+        k[4 * i + 3] = hi[1];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        k[2 * i] = bf16lo(raw[it][i]);
+        k[2 * i + 1] = bf16hi(raw[it][i]);
+      }
+    }
+    if (track_kmax) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) kmax = fmaxf(kmax, fabsf(k[i]));
+    }
+#pragma unroll
+    for (int rr = 0; rr < NR; ++rr) {
+      if (rr >= nr) break;  // wave-uniform
+      float d = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) d = fmaf(qf[rr][i], k[i], d);
+      d += __shfl_xor(d, 1, kWave);
+      d += __shfl_xor(d, 2, kWave);
+      d += __shfl_xor(d, 4, kWave);
+      if (part == rr && j < vis_max) P.logits[(int64_t)(row0 + rr) * P.col_stride + j] = d;
+    }
+  }
+}
+
+// Grid (wg_per_req, R), 256 threads.  Workgroup k of request r scores the request's keys in
+// tiles 4k .. 4k+3 (256 keys each) against every row of the request, NR rows at a time.  Eight
+// lanes share a key (16 dims each), so one wave load reads eight consecutive compressed rows --
+// 2 KiB (bf16) or 1 KiB (fp8) of contiguous cache.  The block-table slice and the head-folded
+// rows are staged in LDS once; the next tile's keys are in flight while a tile is scored.
+template <bool FP8, int NR>
 __global__ __launch_bounds__(256) void logits_valu_kernel(SelectParams P) {
-  const int r = blockIdx.y, tile = blockIdx.x;
+  constexpr int kWords = FP8 ? 4 : 8;
+  constexpr int kMaxCols = kLogitsTilesPerWG * kLogitsKeysPerWG + 2;
+  __shared__ int32_t pages_s[kMaxCols];
+  __shared__ float qf_s[NR][kHeadDim];
+  __shared__ float red[4];
+  const int r = blockIdx.y, k = blockIdx.x;
   // Row range of the request, clamped into [0, T): the metadata is device data the host never
   // saw, so it is not trusted to stay inside the buffers.
   const int q0 = max(0, min(P.qsl[r], P.T));
   const int n = max(0, min(P.qsl[r + 1], P.T) - q0), L = P.seq_lens[r];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, kg = lane >> 3, part = lane & 7;
   const int vis_max = (n > 0 && n <= L) ? min(L / P.c, P.cols) : 0;
-  const int j0 = tile * kLogitsKeysPerWG;
-  __shared__ float qf_s[4][kHeadDim];
-  __shared__ float red[4];
+  const int t_lo = k * kLogitsTilesPerWG;
+  const int t_hi = min(t_lo + kLogitsTilesPerWG,
+                       (vis_max + kLogitsKeysPerWG - 1) / kLogitsKeysPerWG);
   float kmax = 0.0f;
-  if (j0 < vis_max) {  // block-uniform
-    constexpr int kWords = FP8 ? 4 : 8;   // uint32 words of this lane's 16 dims
-    uint32_t raw[8][kWords];
-    int jj[8];
-    const char* base = reinterpret_cast<const char*>(P.ckv);
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int j = j0 + w * 64 + it * 8 + kg;
-      jj[it] = j;
-      const int64_t off = j < vis_max ? key_row(P, r, j) : -1;
-      // An invalid key reads the cache's first row and is zeroed below.
-      const uint4* src = reinterpret_cast<const uint4*>(
-          base + (off < 0 ? 0 : off) * (FP8 ? 1 : 2) + part * (FP8 ? 16 : 32));
-#pragma unroll
-      for (int v = 0; v < kWords / 4; ++v) {
-        const uint4 x = src[v];
-        raw[it][4 * v] = off < 0 ? 0u : x.x;
-        raw[it][4 * v + 1] = off < 0 ? 0u : x.y;
-        raw[it][4 * v + 2] = off < 0 ? 0u : x.z;
-        raw[it][4 * v + 3] = off < 0 ? 0u : x.w;
-      }
+  if (t_lo < t_hi) {  // block-uniform
+    // Block-table slice covering keys [t_lo*256, t_hi*256).
+    const int col0 = t_lo * kLogitsKeysPerWG / P.Pc;
+    const int ncols = min((t_hi * kLogitsKeysPerWG - 1) / P.Pc - col0 + 1, kMaxCols);
+    for (int c = threadIdx.x; c < ncols; c += 256) {
+      const int col = col0 + c;
+      pages_s[c] = col < P.cbt_width ? P.cbt[(int64_t)r * P.cbt_stride + col] : -1;
     }
-    for (int rr0 = 0; rr0 < n; rr0 += 4) {
-      const int nr = min(4, n - rr0);
-      __syncthreads();  // the previous chunk's readers are done with qf_s
+    for (int rr0 = 0; rr0 < n; rr0 += NR) {
+      const int nr = min(NR, n - rr0);
+      __syncthreads();  // pages staged / the previous chunk's readers are done with qf_s
       for (int e = threadIdx.x; e < nr * kHeadDim; e += 256) {
         const int rr = e >> 7, d = e & (kHeadDim - 1);
         const int64_t qb = (int64_t)(q0 + rr0 + rr) * P.Hi * kHeadDim + d;
@@ -103,48 +171,28 @@ __global__ __launch_bounds__(256) void logits_valu_kernel(SelectParams P) {
         qf_s[rr][d] = f;
       }
       __syncthreads();
-      float qf[4][16];
+      float qf[NR][16];
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
+      for (int rr = 0; rr < NR; ++rr) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) qf[rr][i] = rr < nr ? qf_s[rr][part * 16 + i] : 0.0f;
       }
-#pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        float k[16];
-        if (FP8) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(raw[it][i], false);
-            const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(raw[it][i], true);
-            k[4 * i] = lo[0];
-            k[4 * i + 1] = lo[1];
-            k[4 * i + 2] = hi[0];
-            k[4 * i + 3] = hi[1];
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            k[2 * i] = bf16lo(raw[it][i]);
-            k[2 * i + 1] = bf16hi(raw[it][i]);
-          }
-        }
-        if (rr0 == 0) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) kmax = fmaxf(kmax, fabsf(k[i]));
-        }
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          if (rr >= nr) break;  // wave-uniform
-          float d = 0.0f;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) d = fmaf(qf[rr][i], k[i], d);
-          d += __shfl_xor(d, 1, kWave);
-          d += __shfl_xor(d, 2, kWave);
-          d += __shfl_xor(d, 4, kWave);
-          if (part == rr && jj[it] < vis_max)
-            P.logits[(int64_t)(q0 + rr0 + rr) * P.col_stride + jj[it]] = d;
-        }
+      const bool first = rr0 == 0;
+      uint32_t a[8][kWords], b[8][kWords];
+      load_key_tile<FP8>(P, pages_s, col0, ncols, t_lo * kLogitsKeysPerWG, vis_max, w, kg,
+                         part, a);
+      for (int t = t_lo; t < t_hi; t += 2) {
+        if (t + 1 < t_hi)
+          load_key_tile<FP8>(P, pages_s, col0, ncols, (t + 1) * kLogitsKeysPerWG, vis_max, w,
+                             kg, part, b);
+        score_key_tile<FP8, NR>(P, a, qf, nr, q0 + rr0, t * kLogitsKeysPerWG, vis_max, w, kg,
+                                part, first, kmax);
+        if (t + 2 < t_hi)
+          load_key_tile<FP8>(P, pages_s, col0, ncols, (t + 2) * kLogitsKeysPerWG, vis_max, w,
+                             kg, part, a);
+        if (t + 1 < t_hi)
+          score_key_tile<FP8, NR>(P, b, qf, nr, q0 + rr0, (t + 1) * kLogitsKeysPerWG, vis_max,
+                                  w, kg, part, first, kmax);
       }
     }
   }
@@ -152,7 +200,19 @@ __global__ __launch_bounds__(256) void logits_valu_kernel(SelectParams P) {
   if (lane == 0) red[w] = kmax;
   __syncthreads();
   if (threadIdx.x == 0)
-    P.kmax[(int64_t)r * P.key_tiles + tile] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    P.kmax[(int64_t)r * P.key_tiles + k] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+template <bool FP8>
+hipError_t launch_logits(const SelectParams& P, int rows_per_chunk, hipStream_t s) {
+  const dim3 grid(P.key_tiles, P.R);
+  if (rows_per_chunk <= 1)
+    hipLaunchKernelGGL((logits_valu_kernel<FP8, 1>), grid, dim3(256), 0, s, P);
+  else if (rows_per_chunk <= 2)
+    hipLaunchKernelGGL((logits_valu_kernel<FP8, 2>), grid, dim3(256), 0, s, P);
+  else
+    hipLaunchKernelGGL((logits_valu_kernel<FP8, 4>), grid, dim3(256), 0, s, P);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------------------ top-k
@@ -305,7 +365,8 @@ __global__ __launch_bounds__(NT) void topk_kernel(SelectParams P) {
 
   // ---- error bound E of the fast scores for this row
   float km = 0.0f;
-  const int nt = min(P.key_tiles, (L / P.c + kLogitsKeysPerWG - 1) / kLogitsKeysPerWG);
+  const int nt = min(P.key_tiles, (L / P.c + kLogitsTilesPerWG * kLogitsKeysPerWG - 1) /
+                                      (kLogitsTilesPerWG * kLogitsKeysPerWG));
   for (int t = tid; t < nt; t += NT) km = fmaxf(km, P.kmax[(int64_t)r * P.key_tiles + t]);
   double qa = 0.0;
   for (int i = tid; i < P.Hi * kHeadDim; i += NT) qa += fabs((double)qrow[i]);
@@ -410,7 +471,8 @@ TopkLayout topk_layout(const qsa_topk_args& a) {
   L.cols = a.max_seq_len / a.compress_ratio;
   if (L.cols < 1) L.cols = 1;
   L.col_stride = (L.cols + 63) / 64 * 64;
-  L.key_tiles = (L.cols + kLogitsKeysPerWG - 1) / kLogitsKeysPerWG;
+  L.key_tiles = (L.cols + kLogitsTilesPerWG * kLogitsKeysPerWG - 1) /
+                (kLogitsTilesPerWG * kLogitsKeysPerWG);
   auto align = [](size_t x) { return (x + 255) / 256 * 256; };
   size_t off = 0;
   L.off_logits = off;     off = align(off + (size_t)T * L.col_stride * sizeof(float));
@@ -448,12 +510,9 @@ hipError_t launch_topk(const qsa_topk_args& a, const TopkLayout& L, char* ws, hi
   P.band_idx = reinterpret_cast<int32_t*>(ws + L.off_band_idx);
   P.band_score = reinterpret_cast<double*>(ws + L.off_band_score);
 
-  if (P.fp8) {
-    hipLaunchKernelGGL(logits_valu_kernel<true>, dim3(L.key_tiles, P.R), dim3(256), 0, s, P);
-  } else {
-    hipLaunchKernelGGL(logits_valu_kernel<false>, dim3(L.key_tiles, P.R), dim3(256), 0, s, P);
-  }
-  hipError_t e = hipGetLastError();
+  const int rows_per_chunk = a.max_query_len;
+  hipError_t e = P.fp8 ? launch_logits<true>(P, rows_per_chunk, s)
+                       : launch_logits<false>(P, rows_per_chunk, s);
   if (e != hipSuccess) return e;
   const size_t mask_bytes = (size_t)(L.cols + 31) / 32 * sizeof(uint32_t);
   if (L.cols <= 512 * 8) return launch_topk_kernel<512, 8>(P, mask_bytes, s);
