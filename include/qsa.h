@@ -205,7 +205,7 @@ typedef struct qsa_gqa_args {
   int32_t head_dim;                 /* must be 128                                           */
   const uint16_t* q;                /* [T, Hq, 128] bf16                                     */
   int64_t q_row_stride;
-  int64_t q_head_stride;
+  int64_t q_head_stride;            /* must be 128 (a row's heads contiguous)                */
   const uint16_t* kv_cache;         /* bf16, layout above                                    */
   int64_t kv_page_stride;           /* strides: multiples of 8 elements                      */
   int64_t kv_head_stride;

@@ -49,11 +49,17 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 
 __device__ __forceinline__ float sigmoidf(float x) { return 1.0f / (1.0f + expf(-x)); }
 
+// V tile in LDS, transposed for P.V: token pair u, lane l holds (v[2u][l], v[2u+1][l]) as two
+// adjacent dwords; pair rows are padded to 130 dwords so the writes of the 64 tokens of one dim
+// pair hit 64 distinct banks.
+constexpr int kVRow = 130;
+
 template <int G>
 __global__ __launch_bounds__(64) void gqa_partial_kernel(GqaParams P) {
   const int row = blockIdx.x, kvh = blockIdx.y, split = blockIdx.z;
   const int lane = threadIdx.x;
-  __shared__ uint32_t pb[G][32];  // bf16 probabilities, packed as token pairs
+  __shared__ uint32_t pb[G][32];          // bf16 probabilities, packed as token pairs
+  __shared__ uint32_t vt[32 * kVRow];     // the tile's V, transposed
 
   int count = P.packed[(int64_t)row * P.p_rs + P.W];
   count = count < 0 ? 0 : (count > P.W ? P.W : count);
@@ -65,7 +71,7 @@ __global__ __launch_bounds__(64) void gqa_partial_kernel(GqaParams P) {
 
   // Q heads kvh*G .. kvh*G+G-1 of this row, read through the scalar cache.
   const const_u32_ptr qs = (const_u32_ptr)(P.q + (int64_t)row * P.q_rs + (int64_t)kvh * G * P.q_hs);
-  const int64_t qhs = P.q_hs / 2;  // head stride in bf16 pairs
+  constexpr int qhs = kHeadDim / 2;  // heads are contiguous: head stride in bf16 pairs
 
   float m[G], l[G], acc[G][2];
 #pragma unroll
@@ -75,11 +81,15 @@ __global__ __launch_bounds__(64) void gqa_partial_kernel(GqaParams P) {
   const int32_t* btr = P.bt + (int64_t)(r < 0 ? 0 : r) * P.bt_stride;
   const char* kvb = reinterpret_cast<const char*>(P.kv);
 
-  for (int tile = tile_lo; tile < tile_hi; ++tile) {
-    // ---- map this lane's token to its cache row
-    const int t = tile * 64 + lane;
-    int idx = t < count ? sel[t] : -1;
-    bool valid = idx >= 0;
+  // Selected entry of this lane's token in tile tt (-1 past the count or the split).
+  auto load_idx = [&](int tt) -> int {
+    const int t = tt * 64 + lane;
+    return (tt < tile_hi && t < count) ? sel[t] : -1;
+  };
+  // Cache row of an entry, as a 16-byte offset (strides are multiples of 8 elements); invalid
+  // entries (negative, past the block table, page out of range) map to the first row.
+  auto resolve = [&](int idx, uint32_t& off16, bool& valid) {
+    valid = idx >= 0;
     const int col = valid ? idx / P.P : 0;
     valid = valid && col < P.bt_width;
     const int page = valid ? btr[col] : -1;
@@ -87,30 +97,46 @@ __global__ __launch_bounds__(64) void gqa_partial_kernel(GqaParams P) {
     const int slot = idx - col * P.P;
     const int64_t off = valid ? ((int64_t)page * P.kv_ps + (int64_t)kvh * P.kv_hs +
                                  (int64_t)slot * P.kv_ts) : 0;
-    const uint32_t off16 = (uint32_t)(off >> 3);  // 16-byte units (strides are multiples of 8)
-    const uint64_t vmask = __ballot(valid);
+    off16 = (uint32_t)(off >> 3);
+  };
+  // This lane's token row: K (first 256 bytes) or V (next 256 bytes), 16 x 16-byte loads.
+  auto load_row = [&](uint32_t off16, int half, uint4 (&x)[16]) {
+    const uint4* p = reinterpret_cast<const uint4*>(kvb + (size_t)off16 * 16 + half * 256);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = p[i];
+  };
 
-    // ---- issue the gathers: K row of this lane's token, V rows of every token of the tile.
-    // Invalid tokens read the (always in-bounds) first cache row and are zeroed afterwards, so
-    // all 80 loads issue back to back.
-    uint4 k4[16];
+  // The index of tile t+2 and the cache rows of tile t+1 are resolved while tile t is
+  // computed, so a tile's gathers issue without waiting on the index -> block-table chain.
+  uint32_t off_c = 0, off_n = 0;
+  bool valid_c = false, valid_n = false;
+  resolve(load_idx(tile_lo), off_c, valid_c);
+  resolve(load_idx(tile_lo + 1), off_n, valid_n);
+  int idx_nn = load_idx(tile_lo + 2);
+  for (int tile = tile_lo; tile < tile_hi; ++tile) {
+    // ---- gathers: K and V rows of this lane's token
+    uint4 k4[16], v4[16];
+    load_row(off_c, 0, k4);
+    load_row(off_c, 1, v4);
+    uint32_t off_nn = 0;
+    bool valid_nn = false;
+    resolve(idx_nn, off_nn, valid_nn);
+    idx_nn = load_idx(tile + 3);
+
+    // ---- V into the transposed LDS tile (masked tokens as zeros)
     {
-      const uint4* kp = reinterpret_cast<const uint4*>(kvb + (size_t)off16 * 16);
+      const int u = lane >> 1, h = lane & 1;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) k4[i] = kp[i];
-    }
-    uint32_t v[64];
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t w4[4] = {v4[i].x, v4[i].y, v4[i].z, v4[i].w};
 #pragma unroll
-    for (int u = 0; u < 64; ++u) {
-      const uint32_t o16 = __builtin_amdgcn_readlane(off16, u);
-      v[u] = reinterpret_cast<const uint32_t*>(kvb + (size_t)o16 * 16 + 256)[lane];
+        for (int e = 0; e < 4; ++e) vt[u * kVRow + 2 * (4 * i + e) + h] = valid_c ? w4[e] : 0u;
+      }
     }
-    if (!valid) {
+    if (!valid_c) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) k4[i] = make_uint4(0, 0, 0, 0);
     }
-#pragma unroll
-    for (int u = 0; u < 64; ++u) v[u] = ((vmask >> u) & 1ull) ? v[u] : 0u;
 
     // ---- scores of this lane's token against the G heads.  The Q base is laundered per tile
     // so the compiler re-reads Q from the scalar cache chunk by chunk instead of hoisting all
@@ -134,7 +160,7 @@ __global__ __launch_bounds__(64) void gqa_partial_kernel(GqaParams P) {
     // ---- online softmax (base 2); P rounded to bf16 as the reference does before P.V
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const float z = valid ? s[g] * P.scale_log2 : -INFINITY;
+      const float z = valid_c ? s[g] * P.scale_log2 : -INFINITY;
       const float mn = fmaxf(m[g], wave_max(z));
       float alpha = 1.0f, pr = 0.0f;
       if (mn != -INFINITY) {
@@ -150,12 +176,12 @@ __global__ __launch_bounds__(64) void gqa_partial_kernel(GqaParams P) {
     }
     __syncthreads();
 
-    // ---- P.V over token pairs
+    // ---- P.V over token pairs: lane l owns dims 2l, 2l+1
 #pragma unroll
     for (int u = 0; u < 32; ++u) {
-      const uint32_t a = v[2 * u], b = v[2 * u + 1];
-      const uint32_t vd0 = (a & 0xFFFFu) | (b << 16);          // dim 2l of tokens 2u, 2u+1
-      const uint32_t vd1 = (a >> 16) | (b & 0xFFFF0000u);      // dim 2l+1
+      const uint2 ab = *reinterpret_cast<const uint2*>(&vt[u * kVRow + 2 * lane]);
+      const uint32_t vd0 = __builtin_amdgcn_perm(ab.y, ab.x, 0x05040100u);  // lo halves
+      const uint32_t vd1 = __builtin_amdgcn_perm(ab.y, ab.x, 0x07060302u);  // hi halves
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         const uint32_t pp = pb[g][u];
@@ -164,6 +190,10 @@ __global__ __launch_bounds__(64) void gqa_partial_kernel(GqaParams P) {
       }
     }
     __syncthreads();
+    off_c = off_n;
+    valid_c = valid_n;
+    off_n = off_nn;
+    valid_n = valid_nn;
   }
 
   // ---- epilogue

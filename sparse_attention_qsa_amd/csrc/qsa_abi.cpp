@@ -110,10 +110,11 @@ qsa_status validate_gqa(const qsa_gqa_args* a) {
                        (int64_t)(a->num_kv_heads - 1) * a->kv_head_stride +
                        (int64_t)(a->page_size - 1) * a->kv_token_stride + 2 * kHeadDim;
   QSA_REQUIRE(last < (int64_t(1) << 35), kNotSup);  // 16-byte offsets fit 32 bits
-  QSA_REQUIRE(a->q_row_stride % 2 == 0 && a->q_head_stride % 2 == 0 &&
-                  a->q_head_stride >= kHeadDim &&
+  QSA_REQUIRE(a->q_row_stride % 2 == 0 &&
                   a->q_row_stride >= (int64_t)a->num_q_heads * a->q_head_stride,
               kInval);
+  // The kernels read a row's Q heads through the scalar cache at fixed offsets.
+  QSA_REQUIRE(a->q_head_stride == kHeadDim, kNotSup);
   QSA_REQUIRE(a->out_row_stride % 2 == 0 && a->out_head_stride % 2 == 0 &&
                   a->out_head_stride >= kHeadDim,
               kInval);
