@@ -23,9 +23,10 @@ struct CompressPlan {
 struct TopkLayout {
   int32_t cols;           // compressed columns per row (max_seq_len / c, >= 1)
   int32_t col_stride;     // row stride of the per-row arrays (cols rounded up)
-  int32_t key_tiles;      // logits workgroups per request (kLogitsTilesPerWG tiles each)
+  int32_t key_tiles;      // VALU logits workgroups per request (kLogitsTilesPerWG tiles each)
+  int32_t key_blocks;     // blocks of 128 keys per request
   size_t off_logits;      // float  [T, col_stride]
-  size_t off_kmax;        // float  [R, key_tiles]: max |k| seen by each logits workgroup
+  size_t off_kmax;        // float  [R, key_blocks]: upper bound of max |k| per block of 128 keys
   size_t off_band_idx;    // int32  [T, col_stride]
   size_t off_band_score;  // double [T, col_stride]
   size_t total;

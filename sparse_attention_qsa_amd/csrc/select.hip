@@ -21,6 +21,8 @@ namespace {
 
 struct SelectParams {
   int T, R, Hi, c, budget, Pc, c_pages, cbt_stride, cbt_width, cols, col_stride, key_tiles;
+  int key_blocks;     // 128-key blocks per request in the kmax array
+  int mfma_min_rows;  // requests with more rows than this are scored by the MFMA kernel
   bool fp8;
   const int32_t* qsl;
   const int32_t* seq_lens;
@@ -30,7 +32,7 @@ struct SelectParams {
   int32_t* packed;
   int64_t p_rs;
   float* logits;
-  float* kmax;
+  float* kmax;  // [R, key_blocks]: an upper bound of max |k| over each block of 128 keys
   int32_t* band_idx;
   double* band_score;
 };
@@ -147,6 +149,8 @@ __global__ __launch_bounds__(256) void logits_valu_kernel(SelectParams P) {
   const int q0 = max(0, min(P.qsl[r], P.T));
   const int n = max(0, min(P.qsl[r + 1], P.T) - q0), L = P.seq_lens[r];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, kg = lane >> 3, part = lane & 7;
+  // Requests with many rows are scored by the MFMA kernel.
+  if (n > P.mfma_min_rows) return;  // block-uniform, before any barrier
   const int vis_max = (n > 0 && n <= L) ? min(L / P.c, P.cols) : 0;
   const int t_lo = k * kLogitsTilesPerWG;
   const int t_hi = min(t_lo + kLogitsTilesPerWG,
@@ -199,8 +203,12 @@ __global__ __launch_bounds__(256) void logits_valu_kernel(SelectParams P) {
   kmax = wave_max(kmax);
   if (lane == 0) red[w] = kmax;
   __syncthreads();
-  if (threadIdx.x == 0)
-    P.kmax[(int64_t)r * P.key_tiles + k] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  if (threadIdx.x < kLogitsTilesPerWG * kLogitsKeysPerWG / 128) {
+    const int blk = k * (kLogitsTilesPerWG * kLogitsKeysPerWG / 128) + threadIdx.x;
+    if (blk < P.key_blocks)
+      P.kmax[(int64_t)r * P.key_blocks + blk] =
+          fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  }
 }
 
 template <bool FP8>
@@ -213,6 +221,168 @@ hipError_t launch_logits(const SelectParams& P, int rows_per_chunk, hipStream_t 
   else
     hipLaunchKernelGGL((logits_valu_kernel<FP8, 4>), grid, dim3(256), 0, s, P);
   return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------ prefill logits
+
+// Requests with many rows (chunked prefill) are scored per head on the matrix cores: for a
+// tile of 128 rows x 128 keys, S = sum_h Q_h K^T, the head sum taken in the fp32 accumulator
+// (bf16 products are exact in fp32).  The fp32 result differs from the canonical float64
+// score by at most gamma_{Hi*128} kappa A with u = 2^-23 (any summation order, faithful
+// rounding); the top-k's band covers that.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kMfmaTile = 128;    // rows and keys per workgroup
+constexpr int kMfmaMinRows = 16;  // requests with more rows than this take the MFMA kernel
+
+__device__ __forceinline__ void lds_dma16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
+// Tile buffers hold 128 rows of 256 bytes; row t's 16-byte chunk c sits in slot c ^ (t & 15),
+// so that 16 lanes reading chunk c of 16 consecutive rows hit 16 different slots.  They are
+// filled by LDS-direct loads: wave w's load i writes rows 32w + 4i .. 32w + 4i + 3, lane L
+// landing in row 32w + 4i + L/16, slot L%16.
+__device__ __forceinline__ const bf16x8_t& tile_chunk(const uint8_t* buf, int t, int c) {
+  return *reinterpret_cast<const bf16x8_t*>(buf + t * 256 + 16 * (c ^ (t & 15)));
+}
+
+// One launch covers every request; a 1-D grid of R x row blocks x key blocks, remapped so that
+// the workgroups one XCD receives (ids congruent mod 8) walk consecutive key blocks of the same
+// row block and share its Q in their L2.  256 threads: 2 x 2 waves of 64 rows x 64 keys, each
+// holding 4 x 4 accumulators of 16 x 16 (v_mfma_f32_16x16x32_bf16).  The key tile's B
+// fragments stay in registers for all heads; the heads' Q slabs stream through two LDS
+// buffers, the next head's in flight while one is multiplied.
+__global__ __launch_bounds__(256) void logits_mfma_kernel(SelectParams P, int row_blocks) {
+  __shared__ __attribute__((aligned(16))) uint8_t buf[2][kMfmaTile * 256];
+  __shared__ float red[4];
+  __shared__ uint8_t kok[kMfmaTile];
+  const int key_blocks_all = (P.cols + kMfmaTile - 1) / kMfmaTile;
+  const int64_t ntile = (int64_t)P.R * row_blocks * key_blocks_all;
+  const int64_t per = (ntile + 7) / 8;
+  const int64_t t_id = (int64_t)(blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (t_id >= ntile) return;
+  const int kb = (int)(t_id % key_blocks_all);
+  const int rb = (int)((t_id / key_blocks_all) % row_blocks);
+  const int r = (int)(t_id / ((int64_t)key_blocks_all * row_blocks));
+
+  const int q0 = max(0, min(P.qsl[r], P.T));
+  const int n = max(0, min(P.qsl[r + 1], P.T) - q0), L = P.seq_lens[r];
+  if (n <= P.mfma_min_rows || n > L) return;  // decode request, or inert rows
+  const int row0 = rb * kMfmaTile;
+  if (row0 >= n) return;
+  const int nrows = min(kMfmaTile, n - row0);
+  const int key0 = kb * kMfmaTile;
+  const int vis_max = min(L / P.c, P.cols);
+  // Visible keys of the tile's last row (position L - n + row0 + nrows - 1): none -> nothing.
+  if (key0 >= min((L - n + row0 + nrows) / P.c, P.cols)) return;
+
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int wr = w >> 1, wc = w & 1;
+  const char* ckv = reinterpret_cast<const char*>(P.ckv);
+  const char* qb = reinterpret_cast<const char*>(P.q_idx);
+
+  // ---- K tile (keys key0 .. key0+127) into buf[0]; a key that is not visible or whose page is
+  // outside the cache loads the cache's first row and is masked afterwards.
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int j = 32 * w + 4 * i + (lane >> 4), jk = key0 + j;
+    int page = -1;
+    if (jk < vis_max && jk / P.Pc < P.cbt_width) page = P.cbt[(int64_t)r * P.cbt_stride + jk / P.Pc];
+    const bool ok = page >= 0 && page < P.c_pages;
+    const int64_t off = ok ? ((int64_t)page * P.Pc + jk % P.Pc) * kHeadDim * 2 : 0;
+    lds_dma16(ckv + off + 16 * ((lane & 15) ^ (j & 15)), buf[0] + (32 * w + 4 * i) * 256);
+    if ((lane & 15) == 0) kok[j] = ok;
+  }
+  // ---- Q slab of head h (the tile's rows; rows past the request repeat its last row).
+  auto load_q = [&](int h, uint8_t* dst) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int t = 32 * w + 4 * i + (lane >> 4);
+      const int64_t grow = q0 + row0 + min(t, nrows - 1);
+      lds_dma16(qb + ((grow * P.Hi + h) * kHeadDim) * 2 + 16 * ((lane & 15) ^ (t & 15)),
+                dst + (32 * w + 4 * i) * 256);
+    }
+  };
+  load_q(0, buf[1]);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads have landed
+  __syncthreads();
+
+  // ---- max |k| over the tile's valid keys (an upper bound for its 128-key block)
+  float km = 0.0f;
+  {
+    const int j = tid >> 1;
+    if (kok[j]) {
+      const uint32_t* rowp = reinterpret_cast<const uint32_t*>(buf[0] + j * 256 + (tid & 1) * 128);
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const uint32_t u = rowp[i];
+        km = fmaxf(km, fmaxf(fabsf(bf16lo(u)), fabsf(bf16hi(u))));
+      }
+    }
+  }
+  km = wave_max(km);
+  if (lane == 0) red[w] = km;
+
+  // ---- this wave's B fragments: keys 64wc + 16kk + lane%16, dims 32ks + 8(lane/16) .. +7
+  bf16x8_t bfr[4][4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      bfr[kk][ks] = tile_chunk(buf[0], 64 * wc + 16 * kk + (lane & 15), 4 * ks + (lane >> 4));
+  }
+  __syncthreads();  // buf[0] is free; red[] is complete
+  if (tid == 0 && kb < P.key_blocks)
+    P.kmax[(int64_t)r * P.key_blocks + kb] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  for (int h = 0; h < P.Hi; ++h) {
+    const uint8_t* cur = buf[(h + 1) & 1];
+    if (h + 1 < P.Hi) load_q(h + 1, buf[h & 1]);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8_t afr[4];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+        afr[rr] = tile_chunk(cur, 64 * wr + 16 * rr + (lane & 15), 4 * ks + (lane >> 4));
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          acc[rr][kk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[rr], bfr[kk][ks],
+                                                                acc[rr][kk], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next slab has landed
+    __syncthreads();
+  }
+
+  // ---- write: accumulator element e of block (rr, kk) is row 64wr + 16rr + 4(lane/16) + e,
+  // key 64wc + 16kk + lane%16; only keys visible to the row are written.
+  const int pbase = L - n + row0;
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 64 * wr + 16 * rr + 4 * (lane >> 4) + e;
+      if (t >= nrows) continue;
+      const int vis = min((pbase + t + 1) / P.c, P.cols);
+      float* dst = P.logits + (int64_t)(q0 + row0 + t) * P.col_stride;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int j = 64 * wc + 16 * kk + (lane & 15);
+        if (key0 + j < vis) dst[key0 + j] = kok[j] ? acc[rr][kk][e] : 0.0f;
+      }
+    }
+  }
 }
 
 // ------------------------------------------------------------------------------ top-k
@@ -270,6 +440,25 @@ __device__ double canonical_score(const SelectParams& P, const float* qrow, int 
   return s;
 }
 
+// Head-folded float32 score of compressed row j: (sum_h q_h) . k, the fold held in LDS.  Whole
+// wave; result uniform.  Its error is that of the VALU logits.
+__device__ float folded_score(const SelectParams& P, const float* qfold, int r, int j, int lane) {
+  const int64_t off = key_row(P, r, j);
+  float k0 = 0.0f, k1 = 0.0f;
+  if (off >= 0) {
+    if (P.fp8) {
+      const uint32_t u = reinterpret_cast<const uint16_t*>(P.ckv)[off / 2 + lane];
+      k0 = e4m3_to_f32_exact(u & 0xFFu);
+      k1 = e4m3_to_f32_exact(u >> 8);
+    } else {
+      const uint32_t u = reinterpret_cast<const uint32_t*>(P.ckv)[off / 2 + lane];
+      k0 = bf16lo(u);
+      k1 = bf16hi(u);
+    }
+  }
+  return wave_sum(qfold[2 * lane] * k0 + qfold[2 * lane + 1] * k1);
+}
+
 // One workgroup of NT threads per row; thread t holds the fast scores of blocks
 // t*E .. t*E+E-1 in registers for the whole selection.
 template <int NT, int E>
@@ -281,15 +470,17 @@ __global__ __launch_bounds__(NT) void topk_kernel(SelectParams P) {
   __shared__ int s_wave[NT / 64];
   __shared__ double s_dbl[NT / 64];
   __shared__ float qrow[16 * kHeadDim];
+  __shared__ float qfold[kHeadDim];
 
   const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int W = P.budget + P.c - 1, kb = P.budget / P.c;
   int32_t* out = P.packed + (int64_t)row * P.p_rs;
   const int32_t* qsl = stage_qsl(P.qsl, P.R, qsl_s);
   const int r = find_request(qsl, P.R, row);
-  int p = -1, L = 0;
+  int p = -1, L = 0, n_req = 0;
   if (r >= 0) {
     const int q0 = qsl[r], n = qsl[r + 1] - q0;
+    n_req = n;
     L = P.seq_lens[r];
     if (L - n >= 0) p = L - n + (row - q0);
   }
@@ -365,9 +556,8 @@ __global__ __launch_bounds__(NT) void topk_kernel(SelectParams P) {
 
   // ---- error bound E of the fast scores for this row
   float km = 0.0f;
-  const int nt = min(P.key_tiles, (L / P.c + kLogitsTilesPerWG * kLogitsKeysPerWG - 1) /
-                                      (kLogitsTilesPerWG * kLogitsKeysPerWG));
-  for (int t = tid; t < nt; t += NT) km = fmaxf(km, P.kmax[(int64_t)r * P.key_tiles + t]);
+  const int nt = min(P.key_blocks, (min(L / P.c, P.cols) + 127) / 128);
+  for (int t = tid; t < nt; t += NT) km = fmaxf(km, P.kmax[(int64_t)r * P.key_blocks + t]);
   double qa = 0.0;
   for (int i = tid; i < P.Hi * kHeadDim; i += NT) qa += fabs((double)qrow[i]);
   km = wave_max(km);
@@ -376,8 +566,13 @@ __global__ __launch_bounds__(NT) void topk_kernel(SelectParams P) {
   double kappa = 0.0;
   for (int i = 0; i < NT / 64; ++i) kappa = fmax(kappa, s_dbl[i]);
   const double A = block_sum<NT>(qa, s_dbl);
-  const double gam = (double)(P.Hi + 130) * 0x1p-24;
-  const double Ebound = 2.0 * gam / (1.0 - gam) * kappa * A + 1e-30;
+  // Bound of the head-folded float32 score (the VALU logits, and the second level below), and
+  // of the per-head MFMA score (u = 2^-23 covers any rounding the matrix cores may use).
+  const double gam_f = (double)(P.Hi + 130) * 0x1p-24;
+  const double E_f = 2.0 * gam_f / (1.0 - gam_f) * kappa * A + 1e-30;
+  const bool mfma_row = n_req > P.mfma_min_rows;
+  const double gam_m = (double)(P.Hi * kHeadDim + 2) * 0x1p-23;
+  const double Ebound = mfma_row ? 2.0 * gam_m / (1.0 - gam_m) * kappa * A + 1e-30 : E_f;
   const double hi = Tk + 2.0 * Ebound, lo = Tk - 2.0 * Ebound;
 
   // ---- classify; collect the band
@@ -396,25 +591,71 @@ __global__ __launch_bounds__(NT) void topk_kernel(SelectParams P) {
       else if (s >= lo) bidx[atomicAdd(&s_int[2], 1)] = jb + i;
     }
   }
-  const int n_in = block_sum<NT>(n_in_local, s_wave);
-  const int nb = s_int[2];
+  int need = kb - block_sum<NT>(n_in_local, s_wave);
+  int nb = s_int[2];
+  const int32_t* band = bidx;
+
+  if (mfma_row && need > 0) {
+    // ---- second level: the band's head-folded float32 scores (error <= E_f) select within
+    // the band exactly as the first level selected within the row; the rest of the band goes
+    // to the float64 re-scoring.  The band's new list is kept in the row's logits, which are
+    // no longer needed.
+    for (int d = tid; d < kHeadDim; d += NT) {
+      float f = qrow[d];
+      for (int h = 1; h < P.Hi; ++h) f = f + qrow[h * kHeadDim + d];
+      qfold[d] = f;
+    }
+    __syncthreads();
+    for (int b = w; b < nb; b += NT / 64) {
+      const float fs = folded_score(P, qfold, r, bidx[b], lane);
+      if (lane == 0) bscore[b] = fs;
+    }
+    __syncthreads();
+    // The need-th largest folded score of the band (ranks made unique by position).
+    for (int b = tid; b < nb; b += NT) {
+      const double sb = bscore[b];
+      int rank = 0;
+      for (int b2 = 0; b2 < nb; ++b2) {
+        const double s2 = bscore[b2];
+        rank += (s2 > sb) || (s2 == sb && b2 < b);
+      }
+      if (rank == need - 1) s_dbl[0] = sb;
+    }
+    if (tid == 0) s_int[3] = 0;
+    __syncthreads();
+    const double hi2 = s_dbl[0] + 2.0 * E_f, lo2 = s_dbl[0] - 2.0 * E_f;
+    int32_t* band2 = reinterpret_cast<int32_t*>(P.logits + (int64_t)row * P.col_stride);
+    int n_in2_local = 0;
+    for (int b = tid; b < nb; b += NT) {
+      const double sb = bscore[b];
+      const int j = bidx[b];
+      if (sb > hi2) {
+        atomicOr(&sel_mask[j >> 5], 1u << (j & 31));
+        ++n_in2_local;
+      } else if (sb >= lo2) {
+        band2[atomicAdd(&s_int[3], 1)] = j;
+      }
+    }
+    need -= block_sum<NT>(n_in2_local, s_wave);
+    nb = s_int[3];
+    band = band2;
+  }
 
   // ---- re-score the band in float64, canonical order (one wave per block)
   for (int b = w; b < nb; b += NT / 64) {
-    const double s = canonical_score(P, qrow, r, bidx[b], lane);
+    const double s = canonical_score(P, qrow, r, band[b], lane);
     if (lane == 0) bscore[b] = s;
   }
   __syncthreads();
 
-  // ---- rank the band: keep its (kb - n_in) best by (score desc, block asc)
-  const int need = kb - n_in;
+  // ---- rank the band: keep its `need` best by (score desc, block asc)
   for (int b = tid; b < nb; b += NT) {
     const double sb = bscore[b];
-    const int jbb = bidx[b];
+    const int jbb = band[b];
     int rank = 0;
     for (int b2 = 0; b2 < nb; ++b2) {
       const double s2 = bscore[b2];
-      rank += (s2 > sb) || (s2 == sb && bidx[b2] < jbb);
+      rank += (s2 > sb) || (s2 == sb && band[b2] < jbb);
     }
     if (rank < need) atomicOr(&sel_mask[jbb >> 5], 1u << (jbb & 31));
   }
@@ -476,7 +717,8 @@ TopkLayout topk_layout(const qsa_topk_args& a) {
   auto align = [](size_t x) { return (x + 255) / 256 * 256; };
   size_t off = 0;
   L.off_logits = off;     off = align(off + (size_t)T * L.col_stride * sizeof(float));
-  L.off_kmax = off;       off = align(off + (size_t)R * L.key_tiles * sizeof(float));
+  L.key_blocks = (L.cols + 127) / 128;
+  L.off_kmax = off;       off = align(off + (size_t)R * L.key_blocks * sizeof(float));
   L.off_band_idx = off;   off = align(off + (size_t)T * L.col_stride * sizeof(int32_t));
   L.off_band_score = off; off = align(off + (size_t)T * L.col_stride * sizeof(double));
   L.total = off;
@@ -497,6 +739,7 @@ hipError_t launch_topk(const qsa_topk_args& a, const TopkLayout& L, char* ws, hi
   P.cols = L.cols;
   P.col_stride = L.col_stride;
   P.key_tiles = L.key_tiles;
+  P.key_blocks = L.key_blocks;
   P.fp8 = a.index_dtype == QSA_DTYPE_FP8_E4M3;
   P.qsl = a.query_start_loc;
   P.seq_lens = a.seq_lens;
@@ -510,10 +753,21 @@ hipError_t launch_topk(const qsa_topk_args& a, const TopkLayout& L, char* ws, hi
   P.band_idx = reinterpret_cast<int32_t*>(ws + L.off_band_idx);
   P.band_score = reinterpret_cast<double*>(ws + L.off_band_score);
 
-  const int rows_per_chunk = a.max_query_len;
+  // bf16 requests with more than kMfmaMinRows rows are scored on the matrix cores, the others
+  // (and every fp8 request) by the VALU kernel; each kernel skips the other's requests.
+  const bool mfma = !P.fp8 && a.max_query_len > kMfmaMinRows;
+  P.mfma_min_rows = P.fp8 ? INT32_MAX : kMfmaMinRows;
+  const int rows_per_chunk = mfma ? kMfmaMinRows : a.max_query_len;
   hipError_t e = P.fp8 ? launch_logits<true>(P, rows_per_chunk, s)
                        : launch_logits<false>(P, rows_per_chunk, s);
   if (e != hipSuccess) return e;
+  if (mfma) {
+    const int row_blocks = (a.max_query_len + kMfmaTile - 1) / kMfmaTile;
+    const int64_t tiles = (int64_t)P.R * row_blocks * ((P.cols + kMfmaTile - 1) / kMfmaTile);
+    hipLaunchKernelGGL(logits_mfma_kernel, dim3((unsigned)((tiles + 7) / 8 * 8)), dim3(256), 0, s,
+                       P, row_blocks);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   const size_t mask_bytes = (size_t)(L.cols + 31) / 32 * sizeof(uint32_t);
   if (L.cols <= 512 * 8) return launch_topk_kernel<512, 8>(P, mask_bytes, s);
   if (L.cols <= 512 * 16) return launch_topk_kernel<512, 16>(P, mask_bytes, s);
