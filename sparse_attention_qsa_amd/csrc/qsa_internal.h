@@ -29,6 +29,7 @@ struct TopkLayout {
   size_t off_kmax;        // float  [R, key_blocks]: upper bound of max |k| per block of 128 keys
   size_t off_band_idx;    // int32  [T, col_stride]
   size_t off_band_score;  // double [T, col_stride]
+  size_t off_work;        // int [8]: work counters of the MFMA kernel
   size_t total;
 };
 

@@ -14,6 +14,8 @@
 // score, a block with fast score > T + 2E is certainly kept, one below T - 2E certainly dropped,
 // and only the band in between is re-scored in float64 in the canonical order and ranked by
 // (score desc, block asc).
+#include <type_traits>
+
 #include "qsa_internal.h"
 
 namespace qsa {
@@ -35,6 +37,7 @@ struct SelectParams {
   float* kmax;  // [R, key_blocks]: an upper bound of max |k| over each block of 128 keys
   int32_t* band_idx;
   double* band_score;
+  int* work;  // [8] work counters of the MFMA kernel's queues, zeroed by the VALU kernel
 };
 
 __device__ __forceinline__ float load_q_value(const SelectParams& P, int64_t idx) {
@@ -149,6 +152,8 @@ __global__ __launch_bounds__(256) void logits_valu_kernel(SelectParams P) {
   const int q0 = max(0, min(P.qsl[r], P.T));
   const int n = max(0, min(P.qsl[r + 1], P.T) - q0), L = P.seq_lens[r];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, kg = lane >> 3, part = lane & 7;
+  // The MFMA kernel, which runs next, starts its work queues from zero.
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 8) P.work[threadIdx.x] = 0;
   // Requests with many rows are scored by the MFMA kernel.
   if (n > P.mfma_min_rows) return;  // block-uniform, before any barrier
   const int vis_max = (n > 0 && n <= L) ? min(L / P.c, P.cols) : 0;
@@ -226,161 +231,306 @@ hipError_t launch_logits(const SelectParams& P, int rows_per_chunk, hipStream_t 
 // ------------------------------------------------------------------------------ prefill logits
 
 // Requests with many rows (chunked prefill) are scored per head on the matrix cores: for a
-// tile of 128 rows x 128 keys, S = sum_h Q_h K^T, the head sum taken in the fp32 accumulator
+// tile of 128 rows x 256 keys, S = sum_h Q_h K^T, the head sum taken in the fp32 accumulator
 // (bf16 products are exact in fp32).  The fp32 result differs from the canonical float64
 // score by at most gamma_{Hi*128} kappa A with u = 2^-23 (any summation order, faithful
 // rounding); the top-k's band covers that.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kMfmaTile = 128;    // rows and keys per workgroup
-constexpr int kMfmaMinRows = 16;  // requests with more rows than this take the MFMA kernel
+constexpr int kMfmaRows = 128;        // rows per row block
+constexpr int kMfmaKeys = 256;        // keys per workgroup (its key tile)
+constexpr int kMfmaRowBlocksPerWG = 4;
+constexpr int kMfmaMinRows = 16;      // requests with more rows than this take the MFMA kernel
 
 __device__ __forceinline__ void lds_dma16(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
                                    (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
 }
 
-// Tile buffers hold 128 rows of 256 bytes; row t's 16-byte chunk c sits in slot c ^ (t & 15),
-// so that 16 lanes reading chunk c of 16 consecutive rows hit 16 different slots.  They are
-// filled by LDS-direct loads: wave w's load i writes rows 32w + 4i .. 32w + 4i + 3, lane L
-// landing in row 32w + 4i + L/16, slot L%16.
+// Tiles in LDS hold rows of 256 bytes; row t's 16-byte chunk c sits in slot c ^ (t & 15), so
+// that 16 lanes reading chunk c of 16 consecutive rows hit 16 different slots.  They are
+// filled by LDS-direct loads: a load writes 4 rows (1 KiB), lane L landing in row L/16, slot
+// L%16.
 __device__ __forceinline__ const bf16x8_t& tile_chunk(const uint8_t* buf, int t, int c) {
   return *reinterpret_cast<const bf16x8_t*>(buf + t * 256 + 16 * (c ^ (t & 15)));
 }
+__device__ __forceinline__ uint32_t tile_chunk_addr(const uint8_t* buf, int t, int c) {
+  const __attribute__((address_space(3))) uint8_t* p =
+      (const __attribute__((address_space(3))) uint8_t*)(buf + t * 256 + 16 * (c ^ (t & 15)));
+  return (uint32_t)(uintptr_t)p;
+}
+// 16-byte LDS read at addr + OFF issued as inline assembly; the caller waits (lgkmcnt)
+// before use.
+template <int OFF>
+__device__ __forceinline__ bf16x8_t lds_read16_off(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds_read offset field is 16 bits");
+  bf16x8_t v;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+  return v;
+}
 
-// One launch covers every request; a 1-D grid of R x row blocks x key blocks, remapped so that
-// the workgroups one XCD receives (ids congruent mod 8) walk consecutive key blocks of the same
-// row block and share its Q in their L2.  256 threads: 2 x 2 waves of 64 rows x 64 keys, each
-// holding 4 x 4 accumulators of 16 x 16 (v_mfma_f32_16x16x32_bf16).  The key tile's B
-// fragments stay in registers for all heads; the heads' Q slabs stream through two LDS
-// buffers, the next head's in flight while one is multiplied.
-__global__ __launch_bounds__(256) void logits_mfma_kernel(SelectParams P, int row_blocks) {
-  __shared__ __attribute__((aligned(16))) uint8_t buf[2][kMfmaTile * 256];
-  __shared__ float red[4];
-  __shared__ uint8_t kok[kMfmaTile];
-  const int key_blocks_all = (P.cols + kMfmaTile - 1) / kMfmaTile;
-  const int64_t ntile = (int64_t)P.R * row_blocks * key_blocks_all;
-  const int64_t per = (ntile + 7) / 8;
-  const int64_t t_id = (int64_t)(blockIdx.x & 7) * per + (blockIdx.x >> 3);
-  if (t_id >= ntile) return;
-  const int kb = (int)(t_id % key_blocks_all);
-  const int rb = (int)((t_id / key_blocks_all) % row_blocks);
-  const int r = (int)(t_id / ((int64_t)key_blocks_all * row_blocks));
+// Waits until at most n VMEM operations of this wave are outstanding (n from the small set of
+// counts the MFMA kernel uses; any other count waits for all).
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  switch (n) {
+    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+    case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+    case 16: __builtin_amdgcn_s_waitcnt(0x4F70); break;
+    case 20: __builtin_amdgcn_s_waitcnt(0x4F74); break;
+    case 24: __builtin_amdgcn_s_waitcnt(0x4F78); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+  }
+}
 
-  const int q0 = max(0, min(P.qsl[r], P.T));
-  const int n = max(0, min(P.qsl[r + 1], P.T) - q0), L = P.seq_lens[r];
-  if (n <= P.mfma_min_rows || n > L) return;  // decode request, or inert rows
-  const int row0 = rb * kMfmaTile;
-  if (row0 >= n) return;
-  const int nrows = min(kMfmaTile, n - row0);
-  const int key0 = kb * kMfmaTile;
-  const int vis_max = min(L / P.c, P.cols);
-  // Visible keys of the tile's last row (position L - n + row0 + nrows - 1): none -> nothing.
-  if (key0 >= min((L - n + row0 + nrows) / P.c, P.cols)) return;
+// Persistent workgroups (one per CU; the LDS use allows no more) take work items -- (request,
+// chunk of up to four row blocks, key tile of 256 keys) -- from eight queues, one per XCD:
+// queue x holds the (request, row chunk) pairs x, x+8, ..., each with all its key tiles in
+// order, so that the workgroups of one XCD work on the same rows at once and share their Q in
+// the XCD's L2.  (Workgroup b takes queue b % 8, which is its XCD under round-robin dispatch;
+// any other placement only costs locality.)  An item loads its key tile once and keeps the
+// key fragments in registers (8 waves, 2 x 4 of 64 rows x 64 keys; per wave 4 x 4
+// accumulators of 16 keys x 16 rows, v_mfma_f32_16x16x32_bf16 with the keys as the A operand
+// so that a lane ends up with 4 consecutive keys of one row).  The Q slabs (128 rows of one
+// head) of its row blocks then stream through four 32 KiB LDS buffers (two of them the key
+// tile's), three slabs in flight while one is multiplied.  Stores are unconditional buffer
+// stores (out-of-range lanes are dropped by the buffer's bounds), so that every wave issues a
+// known number of memory operations and the waits for the slabs are exact.
+__global__ __launch_bounds__(512) void logits_mfma_kernel(SelectParams P, int row_blocks) {
+  // Four 32 KiB buffers: 0 and 1 hold Q slabs; 2 and 3 hold the key tile (keys 0..127,
+  // 128..255) and afterwards two more Q slabs.  Slab sl lives in buffer sl % 4.
+  __shared__ __attribute__((aligned(16))) uint8_t lds[4][kMfmaRows * 256];
+  uint8_t* const kl = lds[2];
+  uint8_t* const kh = lds[3];
+  __shared__ float red[2][8];
+  __shared__ __attribute__((aligned(4))) uint8_t kok[kMfmaKeys];
+  __shared__ int s_item;
+  const int key_tiles = (P.cols + kMfmaKeys - 1) / kMfmaKeys;
+  const int row_chunks = (row_blocks + kMfmaRowBlocksPerWG - 1) / kMfmaRowBlocksPerWG;
+  const int pairs = P.R * row_chunks;
+  const int queue = blockIdx.x & 7;
+  const int64_t qlen = (int64_t)((pairs - queue + 7) / 8) * key_tiles;  // items of this queue
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int wr = w >> 1, wc = w & 1;
+  const int wr = w >> 2, wc = w & 3;  // this wave: rows 64wr .. +63, keys 64wc .. +63
   const char* ckv = reinterpret_cast<const char*>(P.ckv);
   const char* qb = reinterpret_cast<const char*>(P.q_idx);
-
-  // ---- K tile (keys key0 .. key0+127) into buf[0]; a key that is not visible or whose page is
-  // outside the cache loads the cache's first row and is masked afterwards.
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int j = 32 * w + 4 * i + (lane >> 4), jk = key0 + j;
-    int page = -1;
-    if (jk < vis_max && jk / P.Pc < P.cbt_width) page = P.cbt[(int64_t)r * P.cbt_stride + jk / P.Pc];
-    const bool ok = page >= 0 && page < P.c_pages;
-    const int64_t off = ok ? ((int64_t)page * P.Pc + jk % P.Pc) * kHeadDim * 2 : 0;
-    lds_dma16(ckv + off + 16 * ((lane & 15) ^ (j & 15)), buf[0] + (32 * w + 4 * i) * 256);
-    if ((lane & 15) == 0) kok[j] = ok;
-  }
-  // ---- Q slab of head h (the tile's rows; rows past the request repeat its last row).
-  auto load_q = [&](int h, uint8_t* dst) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int t = 32 * w + 4 * i + (lane >> 4);
-      const int64_t grow = q0 + row0 + min(t, nrows - 1);
-      lds_dma16(qb + ((grow * P.Hi + h) * kHeadDim) * 2 + 16 * ((lane & 15) ^ (t & 15)),
-                dst + (32 * w + 4 * i) * 256);
-    }
+  // Barrier without a memory fence (a fence would wait for every load in flight); LDS reads
+  // are complete before it, and the loads into LDS are waited for explicitly.
+  auto barrier = [] {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   };
-  load_q(0, buf[1]);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads have landed
-  __syncthreads();
 
-  // ---- max |k| over the tile's valid keys (an upper bound for its 128-key block)
-  float km = 0.0f;
-  {
-    const int j = tid >> 1;
-    if (kok[j]) {
-      const uint32_t* rowp = reinterpret_cast<const uint32_t*>(buf[0] + j * 256 + (tid & 1) * 128);
+  for (;;) {
+    if (tid == 0) s_item = atomicAdd(&P.work[queue], 1);
+    barrier();
+    const int64_t item = s_item;
+    barrier();  // every wave has read s_item (and is done with the previous item's LDS)
+    if (item >= qlen) break;  // workgroup-uniform
+    const int g = queue + 8 * (int)(item / key_tiles);
+    const int kt = (int)(item % key_tiles);
+    const int rc = g % row_chunks, r = g / row_chunks;
+
+    const int q0 = max(0, min(P.qsl[r], P.T));
+    const int n = max(0, min(P.qsl[r + 1], P.T) - q0), L = P.seq_lens[r];
+    if (n <= P.mfma_min_rows || n > L) continue;  // decode request, or inert rows
+    const int key0 = kt * kMfmaKeys;
+    const int vis_max = min(L / P.c, P.cols);
+    // Row blocks of this chunk that see at least one key of the tile (visibility grows with
+    // the row, so they are a suffix of the chunk).
+    const int rb_end = min((rc + 1) * kMfmaRowBlocksPerWG, (n + kMfmaRows - 1) / kMfmaRows);
+    int rb_first = rc * kMfmaRowBlocksPerWG;
+    auto sees_tile = [&](int rb) {
+      const int last = min(kMfmaRows, n - rb * kMfmaRows);
+      return key0 < min((L - n + rb * kMfmaRows + last) / P.c, P.cols);
+    };
+    while (rb_first < rb_end && !sees_tile(rb_first)) ++rb_first;
+    if (rb_first >= rb_end) continue;
+
+    // ---- key tile (keys key0 .. key0+255), 8 loads per wave (wave w: keys 32w .. 32w+31, in
+    // kl for w < 4, else kh); the block-table reads come first, all in flight together.  A
+    // key that is not visible or whose page is outside the cache loads the cache's first row
+    // and is masked afterwards.
+    {
+      int page[8];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const uint32_t u = rowp[i];
-        km = fmaxf(km, fmaxf(fabsf(bf16lo(u)), fabsf(bf16hi(u))));
+      for (int i = 0; i < 8; ++i) {
+        const int jk = key0 + 32 * w + 4 * i + (lane >> 4);
+        const int col = jk < vis_max ? min(jk / P.Pc, P.cbt_width - 1) : 0;
+        page[i] = P.cbt[(int64_t)r * P.cbt_stride + col];
+      }
+      asm volatile("" : "+v"(page[0]), "+v"(page[1]), "+v"(page[2]), "+v"(page[3]),
+                   "+v"(page[4]), "+v"(page[5]), "+v"(page[6]), "+v"(page[7]));
+      uint8_t* const kdst = w < 4 ? kl : kh;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int j = 32 * w + 4 * i + (lane >> 4), jk = key0 + j;
+        const bool ok = jk < vis_max && jk / P.Pc < P.cbt_width && page[i] >= 0 &&
+                        page[i] < P.c_pages;
+        const int64_t off = ok ? ((int64_t)page[i] * P.Pc + jk % P.Pc) * kHeadDim * 2 : 0;
+        lds_dma16(ckv + off + 16 * ((lane & 15) ^ (j & 15)),
+                  kdst + ((32 * w + 4 * i) & 127) * 256);
+        if ((lane & 15) == 0) kok[j] = ok;
       }
     }
-  }
-  km = wave_max(km);
-  if (lane == 0) red[w] = km;
+    // ---- Q slab sl: head sl % Hi of row block rb_first + sl / Hi (rows past the request
+    // repeat its last row), 4 loads per wave.
+    const int nslabs = (rb_end - rb_first) * P.Hi;
+    auto load_q = [&](int sl, uint8_t* dst) {
+      const int rb = rb_first + sl / P.Hi, h = sl % P.Hi;
+      const int last = min(kMfmaRows, n - rb * kMfmaRows) - 1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * w + 4 * i + (lane >> 4);
+        const int64_t grow = q0 + rb * kMfmaRows + min(t, last);
+        lds_dma16(qb + ((grow * P.Hi + h) * kHeadDim) * 2 + 16 * ((lane & 15) ^ (t & 15)),
+                  dst + (16 * w + 4 * i) * 256);
+      }
+    };
+    load_q(0, lds[0]);
+    if (nslabs > 1) load_q(1, lds[1]);
+    wait_vmcnt(nslabs > 1 ? 4 : 0);  // the key tile and slab 0 have landed
+    barrier();
 
-  // ---- this wave's B fragments: keys 64wc + 16kk + lane%16, dims 32ks + 8(lane/16) .. +7
-  bf16x8_t bfr[4][4];
+    // ---- max |k| over the valid keys of each 128-key half (upper bounds for the top-k).
+    // Consecutive lanes read consecutive dwords; dword d of a half belongs to its key d / 64.
+    {
+      float km[2] = {0.0f, 0.0f};
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      bfr[kk][ks] = tile_chunk(buf[0], 64 * wc + 16 * kk + (lane & 15), 4 * ks + (lane >> 4));
-  }
-  __syncthreads();  // buf[0] is free; red[] is complete
-  if (tid == 0 && kb < P.key_blocks)
-    P.kmax[(int64_t)r * P.key_blocks + kb] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-
-  f32x4_t acc[4][4];
-#pragma unroll
-  for (int a = 0; a < 4; ++a) {
-#pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  }
-  for (int h = 0; h < P.Hi; ++h) {
-    const uint8_t* cur = buf[(h + 1) & 1];
-    if (h + 1 < P.Hi) load_q(h + 1, buf[h & 1]);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      bf16x8_t afr[4];
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-        afr[rr] = tile_chunk(cur, 64 * wr + 16 * rr + (lane & 15), 4 * ks + (lane >> 4));
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          acc[rr][kk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[rr], bfr[kk][ks],
-                                                                acc[rr][kk], 0, 0, 0);
+      for (int hf = 0; hf < 2; ++hf) {
+        const uint32_t* kw = reinterpret_cast<const uint32_t*>(hf ? kh : kl);
+#pragma unroll 8
+        for (int i = 0; i < 16; ++i) {
+          const int d = tid + 512 * i;
+          if (kok[128 * hf + (d >> 6)]) {
+            const uint32_t u = kw[d];
+            km[hf] = fmaxf(km[hf], fmaxf(fabsf(bf16lo(u)), fabsf(bf16hi(u))));
+          }
+        }
+      }
+      km[0] = wave_max(km[0]);
+      km[1] = wave_max(km[1]);
+      if (lane == 0) {
+        red[0][w] = km[0];
+        red[1][w] = km[1];
       }
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next slab has landed
-    __syncthreads();
-  }
-
-  // ---- write: accumulator element e of block (rr, kk) is row 64wr + 16rr + 4(lane/16) + e,
-  // key 64wc + 16kk + lane%16; only keys visible to the row are written.
-  const int pbase = L - n + row0;
-#pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int t = 64 * wr + 16 * rr + 4 * (lane >> 4) + e;
-      if (t >= nrows) continue;
-      const int vis = min((pbase + t + 1) / P.c, P.cols);
-      float* dst = P.logits + (int64_t)(q0 + row0 + t) * P.col_stride;
+    // ---- this wave's key fragments: keys 64wc + 16kk + lane%16, dims 32ks + 8(lane/16) .. +7
+    bf16x8_t kfr[4][4];
+    {
+      const uint8_t* kt_half = wc < 2 ? kl : kh;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const int j = 64 * wc + 16 * kk + (lane & 15);
-        if (key0 + j < vis) dst[key0 + j] = kok[j] ? acc[rr][kk][e] : 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          kfr[kk][ks] = tile_chunk(kt_half, 64 * (wc & 1) + 16 * kk + (lane & 15),
+                                   4 * ks + (lane >> 4));
       }
+    }
+    barrier();  // red[] complete; the key tile is free for slabs 2 and 3
+    if (tid < 2 && 2 * kt + tid < P.key_blocks) {
+      float m = red[tid][0];
+      for (int i = 1; i < 8; ++i) m = fmaxf(m, red[tid][i]);
+      P.kmax[(int64_t)r * P.key_blocks + 2 * kt + tid] = m;
+    }
+    if (nslabs > 2) load_q(2, lds[2]);
+
+    f32x4_t acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) acc[a][b] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    // Bit k of `stored`: the iteration k+1 back wrote its row block (16 stores per wave).
+    uint32_t stored = 0;
+    // Per-lane LDS addresses of this wave's Q fragments in buffers 0/1 and 2/3 for each K step
+    // (row 64wr + lane%16, chunk 4ks + lane/16); the buffer and the row block go in the
+    // instruction's offset.
+    uint32_t qaddr[2][4];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        qaddr[hb][ks] = tile_chunk_addr(lds[2 * hb], 64 * wr + (lane & 15), 4 * ks + (lane >> 4));
+    }
+    // One slab: wait for it, load slab sl+3 into the buffer slab sl-1 used, multiply, and
+    // write the row block when its last head is done.
+    auto step = [&](int sl, auto buf_tag) {
+      constexpr int kBuf = decltype(buf_tag)::value;
+      uint8_t* const next = lds[(kBuf + 3) & 3];
+      // Memory operations this wave issued after slab sl's loads: the loads of slabs sl+1
+      // and sl+2 (4 each), and the stores of iterations max(0, sl-3) .. sl-1.
+      const int dmas = 4 * (min(nslabs - 1, sl + 2) - sl);
+      int after = dmas + 16 * __builtin_popcount(stored & 7u);
+      if (after > 24) after = dmas;  // fewer than issued: a stricter wait
+      wait_vmcnt(after);
+      barrier();  // slab sl visible to all waves; slab sl-1's buffer is free
+      if (sl + 3 < nslabs) load_q(sl + 3, next);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        // The slab reads are issued as inline assembly, which the compiler's own wait
+        // insertion does not track: it would otherwise wait for every load into LDS in
+        // flight (including the next slabs') before reading this one, which the wait above
+        // already guarantees has landed.
+        bf16x8_t qfr[4];
+        const uint32_t qa = qaddr[kBuf >> 1][ks];
+        qfr[0] = lds_read16_off<(kBuf & 1) * kMfmaRows * 256 + 0 * 4096>(qa);
+        qfr[1] = lds_read16_off<(kBuf & 1) * kMfmaRows * 256 + 1 * 4096>(qa);
+        qfr[2] = lds_read16_off<(kBuf & 1) * kMfmaRows * 256 + 2 * 4096>(qa);
+        qfr[3] = lds_read16_off<(kBuf & 1) * kMfmaRows * 256 + 3 * 4096>(qa);
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(qfr[0]), "+v"(qfr[1]), "+v"(qfr[2]),
+                     "+v"(qfr[3]));
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk)
+            acc[rr][kk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfr[kk][ks], qfr[rr],
+                                                                  acc[rr][kk], 0, 0, 0);
+        }
+      }
+      const bool last_head = sl % P.Hi == P.Hi - 1;
+      stored = (stored << 1) | (last_head ? 1u : 0u);
+      if (last_head) {
+        // ---- row block done.  Accumulator element e of block (rr, kk) is key 64wc + 16kk +
+        // 4(lane/16) + e of row 64wr + 16rr + lane%16.  A group of 4 keys is written when its
+        // first key is visible to the row (the rest of the group lies inside the row's stride
+        // and past its visible keys, which the top-k does not read).
+        const int rb = rb_first + sl / P.Hi;
+        const int nrows = min(kMfmaRows, n - rb * kMfmaRows);
+        const int pbase = L - n + rb * kMfmaRows;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            P.logits + (int64_t)(q0 + rb * kMfmaRows) * P.col_stride, 0,
+            nrows * P.col_stride * 4, 0x00020000);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int t = 64 * wr + 16 * rr + (lane & 15);
+          const int vis = t < nrows ? min((pbase + t + 1) / P.c, P.cols) : 0;
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) {
+            const int j = 64 * wc + 16 * kk + 4 * (lane >> 4);
+            const uint32_t okm = *reinterpret_cast<const uint32_t*>(kok + j);
+            f32x4_t v = acc[rr][kk];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              if (!((okm >> (8 * e)) & 0xFFu)) v[e] = 0.0f;
+            }
+            const uint32_t off = key0 + j < vis ? (uint32_t)(t * P.col_stride + key0 + j) * 4u
+                                                : 0xFFFFFFF0u;
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), rs, off, 0,
+                                                   0);
+            acc[rr][kk] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+          }
+        }
+      }
+    };
+    for (int sl = 0; sl < nslabs; sl += 4) {
+      step(sl, std::integral_constant<int, 0>{});
+      if (sl + 1 < nslabs) step(sl + 1, std::integral_constant<int, 1>{});
+      if (sl + 2 < nslabs) step(sl + 2, std::integral_constant<int, 2>{});
+      if (sl + 3 < nslabs) step(sl + 3, std::integral_constant<int, 3>{});
     }
   }
 }
@@ -409,55 +559,98 @@ __device__ __forceinline__ T block_sum(T v, T* scratch) {
   return s;
 }
 
-// Canonical float64 score of compressed row j against the row's Q (held in LDS as floats):
-// per head the 128 exact products are summed by halving (adjacent pairs in-lane, then lanes
-// xor 32, 16, ..., 1), and the heads are added in order.  Whole wave; result uniform.
-__device__ double canonical_score(const SelectParams& P, const float* qrow, int r, int j,
-                                  int lane) {
-  const int64_t off = key_row(P, r, j);
-  double k0 = 0.0, k1 = 0.0;
-  if (off >= 0) {
-    if (P.fp8) {
-      const uint32_t u = reinterpret_cast<const uint16_t*>(P.ckv)[off / 2 + lane];
-      k0 = e4m3_to_f32_exact(u & 0xFFu);
-      k1 = e4m3_to_f32_exact(u >> 8);
-    } else {
-      const uint32_t u = reinterpret_cast<const uint32_t*>(P.ckv)[off / 2 + lane];
-      k0 = bf16lo(u);
-      k1 = bf16hi(u);
+// Value of lane l + N of the same row of 16 lanes (DPP row_shl); lanes past the row's end get
+// zero.  Only the lanes whose partner exists use the result.
+template <int N>
+__device__ __forceinline__ double row_down(double x) {
+  const uint64_t u = (uint64_t)__double_as_longlong(x);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, 0x100 + N, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), 0x100 + N, 0xF, 0xF,
+                                             false);
+  return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+template <int N>
+__device__ __forceinline__ float row_down(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x100 + N, 0xF, 0xF,
+                                                    false));
+}
+
+// Key values of the 16-lane group's lane l: dim pairs i = l, l+16, l+32, l+48 (dims 2i, 2i+1),
+// exact as floats; zero for an out-of-range row (j < 0 or its page outside the cache).
+__device__ __forceinline__ void key_pairs16(const SelectParams& P, int r, int j, int l,
+                                           float (&k)[8]) {
+  const int64_t off = j >= 0 ? key_row(P, r, j) : -1;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = l + 16 * q;
+    float k0 = 0.0f, k1 = 0.0f;
+    if (off >= 0) {
+      if (P.fp8) {
+        const uint32_t u = reinterpret_cast<const uint16_t*>(P.ckv)[off / 2 + i];
+        k0 = e4m3_to_f32_exact(u & 0xFFu);
+        k1 = e4m3_to_f32_exact(u >> 8);
+      } else {
+        const uint32_t u = reinterpret_cast<const uint32_t*>(P.ckv)[off / 2 + i];
+        k0 = bf16lo(u);
+        k1 = bf16hi(u);
+      }
     }
+    k[2 * q] = k0;
+    k[2 * q + 1] = k1;
   }
+}
+
+// Canonical float64 score of compressed row j against the row's Q (held in LDS as floats),
+// computed by a group of 16 lanes (l = lane % 16).  Per head the 128 exact products are summed
+// by halving: pairs (2i, 2i+1) give v_i; then v_i += v_{i+32} for i < 32, += v_{i+16} for
+// i < 16, ..., += v_{i+1} for i < 1.  Lane l holds v_l, v_{l+16}, v_{l+32}, v_{l+48}, so the
+// first two halvings are in-lane and the last four take the partner 8, 4, 2, 1 lanes up.
+// The heads are then added in order.  The result is valid in lane l = 0.
+__device__ double canonical_score16(const SelectParams& P, const float* qrow, int r, int j,
+                                    int l) {
+  float k[8];
+  key_pairs16(P, r, j, l, k);
   double s = 0.0;
   for (int h = 0; h < P.Hi; ++h) {
-    const double q0 = qrow[h * kHeadDim + 2 * lane], q1 = qrow[h * kHeadDim + 2 * lane + 1];
-    const double p0 = q0 * k0;  // exact
-    const double p1 = q1 * k1;  // exact
-    double t = p0 + p1;
+    const float* q = qrow + h * kHeadDim;
+    double v[4];
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) t = t + shfl_xor_f64(t, m);
-    s = (h == 0) ? t : s + t;
+    for (int t = 0; t < 4; ++t) {
+      const int i = l + 16 * t;
+      const double p0 = (double)q[2 * i] * (double)k[2 * t];          // exact
+      const double p1 = (double)q[2 * i + 1] * (double)k[2 * t + 1];  // exact
+      v[t] = p0 + p1;
+    }
+    double x = (v[0] + v[2]) + (v[1] + v[3]);
+    x = x + row_down<8>(x);
+    x = x + row_down<4>(x);
+    x = x + row_down<2>(x);
+    x = x + row_down<1>(x);
+    s = (h == 0) ? x : s + x;
   }
   return s;
 }
 
-// Head-folded float32 score of compressed row j: (sum_h q_h) . k, the fold held in LDS.  Whole
-// wave; result uniform.  Its error is that of the VALU logits.
-__device__ float folded_score(const SelectParams& P, const float* qfold, int r, int j, int lane) {
-  const int64_t off = key_row(P, r, j);
-  float k0 = 0.0f, k1 = 0.0f;
-  if (off >= 0) {
-    if (P.fp8) {
-      const uint32_t u = reinterpret_cast<const uint16_t*>(P.ckv)[off / 2 + lane];
-      k0 = e4m3_to_f32_exact(u & 0xFFu);
-      k1 = e4m3_to_f32_exact(u >> 8);
-    } else {
-      const uint32_t u = reinterpret_cast<const uint32_t*>(P.ckv)[off / 2 + lane];
-      k0 = bf16lo(u);
-      k1 = bf16hi(u);
-    }
+// Head-folded float32 score of compressed row j: (sum_h q_h) . k, the fold held in LDS, by a
+// group of 16 lanes; valid in lane l = 0.  Its error is that of the VALU logits.
+__device__ float folded_score16(const SelectParams& P, const float* qfold, int r, int j, int l) {
+  float k[8];
+  key_pairs16(P, r, j, l, k);
+  float x = 0.0f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int i = l + 16 * t;
+    x += qfold[2 * i] * k[2 * t] + qfold[2 * i + 1] * k[2 * t + 1];
   }
-  return wave_sum(qfold[2 * lane] * k0 + qfold[2 * lane + 1] * k1);
+  x = x + row_down<8>(x);
+  x = x + row_down<4>(x);
+  x = x + row_down<2>(x);
+  x = x + row_down<1>(x);
+  return x;
 }
+
+// Band entries kept in LDS; larger bands (adversarial ties) use the workspace.
+constexpr int kBandCap = 1024;
 
 // One workgroup of NT threads per row; thread t holds the fast scores of blocks
 // t*E .. t*E+E-1 in registers for the whole selection.
@@ -471,6 +664,9 @@ __global__ __launch_bounds__(NT) void topk_kernel(SelectParams P) {
   __shared__ double s_dbl[NT / 64];
   __shared__ float qrow[16 * kHeadDim];
   __shared__ float qfold[kHeadDim];
+  __shared__ int32_t band_idx_s[kBandCap];
+  __shared__ int32_t band2_idx_s[kBandCap];
+  __shared__ double band_score_s[kBandCap];
 
   const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int W = P.budget + P.c - 1, kb = P.budget / P.c;
@@ -575,40 +771,49 @@ __global__ __launch_bounds__(NT) void topk_kernel(SelectParams P) {
   const double Ebound = mfma_row ? 2.0 * gam_m / (1.0 - gam_m) * kappa * A + 1e-30 : E_f;
   const double hi = Tk + 2.0 * Ebound, lo = Tk - 2.0 * Ebound;
 
-  // ---- classify; collect the band
+  // ---- classify; collect the band (in LDS when it fits, else in the workspace)
   const int mask_words = (vis + 31) >> 5;
   for (int i = tid; i < mask_words; i += NT) sel_mask[i] = 0u;
-  if (tid == 0) s_int[2] = 0;
-  __syncthreads();
-  int32_t* bidx = P.band_idx + (int64_t)row * P.col_stride;
-  double* bscore = P.band_score + (int64_t)row * P.col_stride;
-  int n_in_local = 0;
+  int n_in_local = 0, nb_local = 0;
 #pragma unroll
   for (int i = 0; i < E; ++i) {
     const double s = sc[i];
     if (jb + i < vis) {
-      if (s > hi) ++n_in_local;
-      else if (s >= lo) bidx[atomicAdd(&s_int[2], 1)] = jb + i;
+      n_in_local += s > hi;
+      nb_local += s <= hi && s >= lo;
     }
   }
   int need = kb - block_sum<NT>(n_in_local, s_wave);
-  int nb = s_int[2];
+  int nb = block_sum<NT>(nb_local, s_wave);
+  const bool in_lds = nb <= kBandCap;
+  int32_t* bidx = in_lds ? band_idx_s : P.band_idx + (int64_t)row * P.col_stride;
+  double* bscore = in_lds ? band_score_s : P.band_score + (int64_t)row * P.col_stride;
+  if (tid == 0) s_int[2] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const double s = sc[i];
+    if (jb + i < vis && s <= hi && s >= lo) bidx[atomicAdd(&s_int[2], 1)] = jb + i;
+  }
+  __syncthreads();
   const int32_t* band = bidx;
+  const int groups = NT / 16;  // 16-lane groups: one band entry each at a time
+  const int grp = tid >> 4, l16 = tid & 15;
 
   if (mfma_row && need > 0) {
     // ---- second level: the band's head-folded float32 scores (error <= E_f) select within
     // the band exactly as the first level selected within the row; the rest of the band goes
-    // to the float64 re-scoring.  The band's new list is kept in the row's logits, which are
-    // no longer needed.
+    // to the float64 re-scoring.
     for (int d = tid; d < kHeadDim; d += NT) {
       float f = qrow[d];
       for (int h = 1; h < P.Hi; ++h) f = f + qrow[h * kHeadDim + d];
       qfold[d] = f;
     }
     __syncthreads();
-    for (int b = w; b < nb; b += NT / 64) {
-      const float fs = folded_score(P, qfold, r, bidx[b], lane);
-      if (lane == 0) bscore[b] = fs;
+    for (int b0 = 0; b0 < nb; b0 += groups) {
+      const int b = b0 + grp;
+      const float fs = folded_score16(P, qfold, r, b < nb ? bidx[b] : -1, l16);
+      if (l16 == 0 && b < nb) bscore[b] = fs;
     }
     __syncthreads();
     // The need-th largest folded score of the band (ranks made unique by position).
@@ -624,7 +829,9 @@ __global__ __launch_bounds__(NT) void topk_kernel(SelectParams P) {
     if (tid == 0) s_int[3] = 0;
     __syncthreads();
     const double hi2 = s_dbl[0] + 2.0 * E_f, lo2 = s_dbl[0] - 2.0 * E_f;
-    int32_t* band2 = reinterpret_cast<int32_t*>(P.logits + (int64_t)row * P.col_stride);
+    // The band's new list: in LDS with the first, or in the row's logits (no longer needed).
+    int32_t* band2 = in_lds ? band2_idx_s
+                            : reinterpret_cast<int32_t*>(P.logits + (int64_t)row * P.col_stride);
     int n_in2_local = 0;
     for (int b = tid; b < nb; b += NT) {
       const double sb = bscore[b];
@@ -641,10 +848,11 @@ __global__ __launch_bounds__(NT) void topk_kernel(SelectParams P) {
     band = band2;
   }
 
-  // ---- re-score the band in float64, canonical order (one wave per block)
-  for (int b = w; b < nb; b += NT / 64) {
-    const double s = canonical_score(P, qrow, r, band[b], lane);
-    if (lane == 0) bscore[b] = s;
+  // ---- re-score the band in float64, canonical order (16 lanes per entry)
+  for (int b0 = 0; b0 < nb; b0 += groups) {
+    const int b = b0 + grp;
+    const double s = canonical_score16(P, qrow, r, b < nb ? band[b] : -1, l16);
+    if (l16 == 0 && b < nb) bscore[b] = s;
   }
   __syncthreads();
 
@@ -721,6 +929,7 @@ TopkLayout topk_layout(const qsa_topk_args& a) {
   L.off_kmax = off;       off = align(off + (size_t)R * L.key_blocks * sizeof(float));
   L.off_band_idx = off;   off = align(off + (size_t)T * L.col_stride * sizeof(int32_t));
   L.off_band_score = off; off = align(off + (size_t)T * L.col_stride * sizeof(double));
+  L.off_work = off;       off = align(off + 8 * sizeof(int));
   L.total = off;
   return L;
 }
@@ -752,6 +961,7 @@ hipError_t launch_topk(const qsa_topk_args& a, const TopkLayout& L, char* ws, hi
   P.kmax = reinterpret_cast<float*>(ws + L.off_kmax);
   P.band_idx = reinterpret_cast<int32_t*>(ws + L.off_band_idx);
   P.band_score = reinterpret_cast<double*>(ws + L.off_band_score);
+  P.work = reinterpret_cast<int*>(ws + L.off_work);
 
   // bf16 requests with more than kMfmaMinRows rows are scored on the matrix cores, the others
   // (and every fp8 request) by the VALU kernel; each kernel skips the other's requests.
@@ -762,10 +972,20 @@ hipError_t launch_topk(const qsa_topk_args& a, const TopkLayout& L, char* ws, hi
                        : launch_logits<false>(P, rows_per_chunk, s);
   if (e != hipSuccess) return e;
   if (mfma) {
-    const int row_blocks = (a.max_query_len + kMfmaTile - 1) / kMfmaTile;
-    const int64_t tiles = (int64_t)P.R * row_blocks * ((P.cols + kMfmaTile - 1) / kMfmaTile);
-    hipLaunchKernelGGL(logits_mfma_kernel, dim3((unsigned)((tiles + 7) / 8 * 8)), dim3(256), 0, s,
-                       P, row_blocks);
+    // One persistent workgroup per CU (a multiple of 8, one set of queues per XCD).
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (cus[dev] == 0) {
+      int n = 0;
+      if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+          n <= 0)
+        n = 256;
+      cus[dev] = n;
+    }
+    const int row_blocks = (a.max_query_len + kMfmaRows - 1) / kMfmaRows;
+    const unsigned grid = (unsigned)((cus[dev] + 7) / 8 * 8);
+    hipLaunchKernelGGL(logits_mfma_kernel, dim3(grid), dim3(512), 0, s, P, row_blocks);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const size_t mask_bytes = (size_t)(L.cols + 31) / 32 * sizeof(uint32_t);
