@@ -8,17 +8,13 @@
 // rounded to bf16, and each split emits float32 (o, lse) partials merged afterwards; with one
 // split the kernel writes the gated bf16 output directly.
 //
-// MI355X layout (VALU only; the work is HBM-bound gather traffic):
-//   * one wavefront per (row, KV head, split); a tile is 64 selected tokens.  The split's
-//     entries are resolved to cache rows up front (index and block-table loads all in flight
-//     together) and kept in LDS;
-//   * K and V are gathered with coalesced 16-byte loads, 16 lanes per 256-byte row.  K goes
-//     straight to LDS (global_load_lds_dwordx4, no registers) one tile ahead; V goes to
-//     registers at the start of its tile and lands while Q.K and the softmax run;
-//   * Q.K: lane <-> token, reading its K row from LDS; Q is wave-uniform and read through the
-//     scalar cache, so v_dot2c_f32_bf16 takes it straight from SGPRs;
-//   * P.V: lane <-> (token quarter, 8 dims); the bf16 probabilities go through LDS packed per
-//     token pair, two tokens' values per dot2; the quarters are summed at the end.
+// MI355X layout: one wavefront per (row, KV head, split), tiles of 32 selected tokens.  The
+// split's entries are resolved to cache rows up front (index and block-table loads all in
+// flight together) and kept in LDS; K and V rows are gathered straight into LDS with
+// coalesced 16-byte LDS-direct loads, a tile ahead; both contractions (Q.K over the G heads
+// of a KV head, and P.V) run on the matrix cores, which leaves the wave's VALU time to the
+// softmax (measured: the dot2 form of these contractions kept the SIMDs busy while the
+// gathers waited on them).
 #include <type_traits>
 
 #include "qsa_internal.h"
@@ -26,8 +22,6 @@
 namespace qsa {
 namespace {
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef const __attribute__((address_space(4))) uint32_t* const_u32_ptr;
 
 struct GqaParams {
   int T, R, Hq, Hkv, pages, P, bt_stride, bt_width, W, splits, tiles_per_split;
@@ -48,10 +42,6 @@ struct GqaParams {
   float* part_lse;  // [splits, T, Hq]
 };
 
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
-                                         __builtin_bit_cast(bf16x2_t, b), c, false);
-}
 
 __device__ __forceinline__ float sigmoidf(float x) { return 1.0f / (1.0f + expf(-x)); }
 
@@ -63,60 +53,50 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
-// Per-head maximum over the wavefront of G values per lane (value g of lane t belongs to head
-// g), returned wave-uniform.  The heads are reduced together: at each exchange across a lane
-// bit a lane keeps one half of the heads it carries and receives the partner's copy of that
-// half, so G = 2^k heads cost 2^k - 1 exchanges plus 6 - k ordinary steps instead of 6G.
-// Afterwards head h is held by lane h * 64 / G.
-template <int G>
-__device__ __forceinline__ void tile_max(const float (&z)[G], float (&mt)[G]) {
-  constexpr int K = G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : G == 8 ? 3 : 4;
-  const int lane = threadIdx.x & 63;
-  float v[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) v[g] = z[g];
-#pragma unroll
-  for (int j = 0; j < K; ++j) {
-    const int bit = 32 >> j;
-    const bool hi = (lane & bit) != 0;
-    constexpr int kMaxN = G / 2;
-#pragma unroll
-    for (int i = 0; i < kMaxN; ++i) {
-      const int n = G >> (j + 1);
-      if (i >= n) break;
-      const float keep = hi ? v[n + i] : v[i];
-      const float send = hi ? v[i] : v[n + i];
-      v[i] = fmaxf(keep, __shfl_xor(send, bit, kWave));
-    }
-  }
-#pragma unroll
-  for (int bit = 32 >> K; bit >= 1; bit >>= 1) v[0] = fmaxf(v[0], __shfl_xor(v[0], bit, kWave));
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-    mt[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[0]), h * (64 / G)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kTile = 32;        // selected tokens per tile (one MFMA K step of P.V)
+constexpr int kChunkTiles = 8;   // tiles whose cache rows are resolved together
+
+__device__ __forceinline__ void lds_dma16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
 }
 
-// K tile in LDS: token t's 256-byte row at 256*t bytes, its 16-byte chunk c stored in slot
-// c ^ (t & 15), so that 16 consecutive lanes reading chunk c of their own rows touch 16
-// different slots (all 64 banks once).  The tile is filled by LDS-direct loads
-// (global_load_lds_dwordx4): load i writes 1 KiB at 1024*i, lane L at 16*L, which is token
-// 4i + L/16, slot L%16.
-constexpr int kKTileDw = 64 * 64;
-constexpr int kChunkTiles = 8;  // tiles whose cache rows are resolved together
+// K and V tiles in LDS: token t's 256-byte row at 256 t, its 16-byte chunk c in slot
+// c ^ (t & 15).  They are filled by LDS-direct loads: load i writes tokens 4i .. 4i+3, lane L
+// landing in token 4i + L/16, slot L%16.
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
 
+// Grid (T, Hkv, splits), one wavefront per (row, KV head, split).  Both contractions run on
+// the matrix cores (v_mfma_f32_16x16x32_bf16), with the G query heads of the KV head padded
+// to the 16 columns of the instruction:
+//   * Q.K: S^T (tokens x heads) = K (tokens x dims) . Q^T; K fragments are read from the LDS
+//     tile, Q^T fragments stay in registers.  Lane l ends up with tokens 16b + 4(l/16) + e,
+//     e < 4, of head l % 16;
+//   * softmax per head across the 64 lanes' 32 tokens (exp2, P rounded to bf16);
+//   * P.V: O^T (dims x heads) += V^T (dims x tokens) . P^T.  P^T's fragment is exactly what
+//     each lane holds after the softmax (token k-slot 8(l/16) + j is token 4(l/16) + j for
+//     j < 4, else 16 + 4(l/16) + j - 4); V^T's fragments come from the V tile through the
+//     transposing LDS read ds_read_b64_tr_b16, whose 16-lane groups return column l % 16 of
+//     the 4 x 16 block their 16 eight-byte reads form.
+// K and V are gathered with LDS-direct 16-byte loads, 16 lanes per 256-byte row; the next
+// tile's K is in flight during the softmax and P.V, its V during Q.K and the softmax.
 template <int G>
 __global__ __launch_bounds__(64) void gqa_partial_kernel(GqaParams P) {
+  static_assert(G <= 16, "the MFMA columns hold at most 16 heads");
   const int row = blockIdx.x, kvh = blockIdx.y, split = blockIdx.z;
-  const int lane = threadIdx.x;
-  const int qq = lane >> 4;   // quarter: the token of a coalesced load within its group of 4
-  const int ch = lane & 15;   // 16-byte chunk of a 256-byte row
-  __shared__ __attribute__((aligned(16))) uint32_t kt[kKTileDw];
-  // bf16 probabilities, packed per P.V token pair: pr[(j*4 + quarter) * G + g] holds
-  // (p[g][8j + quarter], p[g][8j + 4 + quarter]).
-  __shared__ __attribute__((aligned(16))) uint32_t pr[32 * G];
-  // Resolved cache rows (16-byte offsets) of the tiles of the current chunk, and their masks.
-  __shared__ __attribute__((aligned(16))) uint32_t offs[kChunkTiles * 64];
-  __shared__ uint64_t vms[kChunkTiles];
+  const int lane = threadIdx.x, l16 = lane & 15, g4 = lane >> 4;
+  __shared__ __attribute__((aligned(16))) uint8_t kt[kTile * 256];
+  __shared__ __attribute__((aligned(16))) uint8_t vt[kTile * 256];
+  // Resolved cache rows (16-byte offsets) of the chunk's tiles: token 4i + q of tile k at
+  // offs[k * 32 + 8q + i], so that lane group q's 8 rows are contiguous; and validity masks.
+  __shared__ __attribute__((aligned(16))) uint32_t offs[kChunkTiles * kTile];
+  __shared__ uint32_t vms[kChunkTiles];
 
   // The split's tile range comes from the packed width, so that its first index loads need
   // not wait for the count: the count, the request and the first chunk's entries are read in
@@ -124,59 +104,49 @@ __global__ __launch_bounds__(64) void gqa_partial_kernel(GqaParams P) {
   int count = P.packed[(int64_t)row * P.p_rs + P.W];
   const int r = P.t2r[row];
   const int tile_lo = split * P.tiles_per_split;
-  const int tile_end = min((P.W + 63) >> 6, tile_lo + P.tiles_per_split);
-
-  // Q heads kvh*G .. kvh*G+G-1 of this row, read through the scalar cache.
-  const const_u32_ptr qs = (const_u32_ptr)(P.q + (int64_t)row * P.q_rs + (int64_t)kvh * G * P.q_hs);
-  constexpr int qhs = kHeadDim / 2;  // heads are contiguous: head stride in bf16 pairs
-
-  // m, l: running max and (per-lane partial) normaliser per head; acc: this lane's 8 dims
-  // (8*ch .. 8*ch+7) of every head, over the tokens of its quarter.
-  float m[G], l[G], acc[G][8];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m[g] = -INFINITY;
-    l[g] = 0.0f;
-#pragma unroll
-    for (int d = 0; d < 8; ++d) acc[g][d] = 0.0f;
-  }
+  const int tile_end = min((P.W + kTile - 1) / kTile, tile_lo + P.tiles_per_split);
 
   const int32_t* sel = P.packed + (int64_t)row * P.p_rs;
   const int32_t* btr = P.bt + (int64_t)(r < 0 || r >= P.R ? 0 : r) * P.bt_stride;
   const char* kvb = reinterpret_cast<const char*>(P.kv);
 
-  // Cache rows (16-byte offsets) of the 16 tokens this lane loads in chunk tile k.
-  auto row_offsets = [&](int k, uint32_t (&o)[16]) {
-    const uint4* src = reinterpret_cast<const uint4*>(offs + k * 64 + qq * 16);
+  // Q^T fragments: head l16 (zero past G), dims 32ks + 8 g4 .. +7.
+  bf16x8_t qfr[4];
+  {
+    const uint4* qrow = reinterpret_cast<const uint4*>(
+        P.q + (int64_t)row * P.q_rs + (int64_t)(kvh * G + (l16 < G ? l16 : 0)) * P.q_hs);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint4 x = src[i];
-      o[4 * i] = x.x;
-      o[4 * i + 1] = x.y;
-      o[4 * i + 2] = x.z;
-      o[4 * i + 3] = x.w;
+    for (int ks = 0; ks < 4; ++ks) {
+      uint4 v = qrow[4 * ks + g4];
+      if (l16 >= G) v = make_uint4(0, 0, 0, 0);
+      qfr[ks] = __builtin_bit_cast(bf16x8_t, v);
     }
+  }
+
+  // Per head (this lane's l16): running max, this lane's share of the normaliser, and the
+  // output dims 16 db + 4 g4 + e.
+  float m = -INFINITY, lsum = 0.0f;
+  f32x4_t acc[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) acc[db] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // Rows of chunk tile k for this lane's loads: tokens 4i + g4, i < 8.
+  auto row_offsets = [&](int k, uint32_t (&o)[8]) {
+    const uint4* src = reinterpret_cast<const uint4*>(offs + k * kTile + 8 * g4);
+    const uint4 x = src[0], y = src[1];
+    o[0] = x.x; o[1] = x.y; o[2] = x.z; o[3] = x.w;
+    o[4] = y.x; o[5] = y.y; o[6] = y.z; o[7] = y.w;
   };
-  // K rows of chunk tile k into LDS (no registers); coalesced: 16 lanes per 256-byte row.
-  auto issue_k = [&](int k) {
-    uint32_t o[16];
+  // One tile's K (part 0) or V (part 1) rows into LDS: 8 coalesced LDS-direct loads.
+  auto issue_rows = [&](int k, int part, uint8_t* dst) {
+    uint32_t o[8];
     row_offsets(k, o);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int t = 4 * i + qq;
-      const char* src = kvb + (size_t)o[i] * 16 + 16 * (ch ^ (t & 15));
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)src,
-          (__attribute__((address_space(3))) void*)(kt + 256 * i), 16, 0, 0);
+    for (int i = 0; i < 8; ++i) {
+      const int t = 4 * i + g4;
+      lds_dma16(kvb + (size_t)o[i] * 16 + 256 * part + 16 * (l16 ^ (t & 15)),
+                dst + 1024 * i);
     }
-  };
-  // V rows of chunk tile k into registers: v4[i] = chunk ch of token 4i + qq.
-  auto issue_v = [&](int k, uint4 (&v4)[16]) {
-    uint32_t o[16];
-    row_offsets(k, o);
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      v4[i] = (reinterpret_cast<const uint4*>(kvb + (size_t)o[i] * 16) + 16)[ch];
   };
 
   for (int c0 = tile_lo; c0 < tile_end; c0 += kChunkTiles) {
@@ -184,186 +154,152 @@ __global__ __launch_bounds__(64) void gqa_partial_kernel(GqaParams P) {
     // loads, in flight together.  The loads are unconditional, at clamped addresses (the
     // row's W entries and the block table's first column exist).  Invalid entries (negative,
     // past the block table, page out of range, past the count) read the first row and are
-    // masked.
-    int idx[kChunkTiles], page[kChunkTiles];
+    // masked.  Lane l resolves entries l, l+64, l+128, l+192 of the chunk.
+    int idx[4], page[4];
 #pragma unroll
-    for (int k = 0; k < kChunkTiles; ++k) idx[k] = sel[min((c0 + k) * 64 + lane, P.W - 1)];
-    asm volatile("" : "+v"(idx[0]), "+v"(idx[1]), "+v"(idx[2]), "+v"(idx[3]), "+v"(idx[4]),
-                 "+v"(idx[5]), "+v"(idx[6]), "+v"(idx[7]));
+    for (int j = 0; j < 4; ++j) idx[j] = sel[min(c0 * kTile + lane + 64 * j, P.W - 1)];
+    asm volatile("" : "+v"(idx[0]), "+v"(idx[1]), "+v"(idx[2]), "+v"(idx[3]));
     if (c0 == tile_lo) {
       count = count < 0 ? 0 : (count > P.W ? P.W : count);
       if (r < 0 || r >= P.R) count = 0;
     }
-    const int nt = min(kChunkTiles, min(tile_end, (count + 63) >> 6) - c0);
+    const int nt = min(kChunkTiles, min(tile_end, (count + kTile - 1) / kTile) - c0);
     if (nt <= 0) break;  // wave-uniform
 #pragma unroll
-    for (int k = 0; k < kChunkTiles; ++k) {
-      const int t = (c0 + k) * 64 + lane;
-      if (!(k < nt && t < count) || idx[k] < 0) idx[k] = -1;
-      const int col = idx[k] >= 0 ? idx[k] / P.P : 0;
-      page[k] = btr[min(col, P.bt_width - 1)];
+    for (int j = 0; j < 4; ++j) {
+      const int e = c0 * kTile + lane + 64 * j;
+      if (e >= count || idx[j] < 0) idx[j] = -1;
+      const int col = idx[j] >= 0 ? idx[j] / P.P : 0;
+      page[j] = btr[min(col, P.bt_width - 1)];
     }
-    asm volatile("" : "+v"(page[0]), "+v"(page[1]), "+v"(page[2]), "+v"(page[3]),
-                 "+v"(page[4]), "+v"(page[5]), "+v"(page[6]), "+v"(page[7]));
+    asm volatile("" : "+v"(page[0]), "+v"(page[1]), "+v"(page[2]), "+v"(page[3]));
 #pragma unroll
-    for (int k = 0; k < kChunkTiles; ++k) {
-      const int col = idx[k] >= 0 ? idx[k] / P.P : P.bt_width;
-      const bool valid = col < P.bt_width && page[k] >= 0 && page[k] < P.pages;
-      const int slot = idx[k] - col * P.P;
-      const int64_t off = valid ? ((int64_t)page[k] * P.kv_ps + (int64_t)kvh * P.kv_hs +
+    for (int j = 0; j < 4; ++j) {
+      const int col = idx[j] >= 0 ? idx[j] / P.P : P.bt_width;
+      const bool valid = col < P.bt_width && page[j] >= 0 && page[j] < P.pages;
+      const int slot = idx[j] - col * P.P;
+      const int64_t off = valid ? ((int64_t)page[j] * P.kv_ps + (int64_t)kvh * P.kv_hs +
                                    (int64_t)slot * P.kv_ts) : 0;
-      // Stored so that lane L's 16 rows (tokens 4i + L/16) are contiguous.
-      offs[k * 64 + (lane & 3) * 16 + (lane >> 2)] = (uint32_t)(off >> 3);
+      const int e = lane + 64 * j, k = e >> 5, t = e & 31;
+      offs[k * kTile + 8 * (t & 3) + (t >> 2)] = (uint32_t)(off >> 3);
       const uint64_t vm = __ballot(valid);
-      if (lane == 0) vms[k] = vm;
+      if (lane == 0) {
+        vms[2 * j] = (uint32_t)vm;
+        vms[2 * j + 1] = (uint32_t)(vm >> 32);
+      }
     }
     wave_lds_sync();
-    issue_k(0);
+    issue_rows(0, 0, kt);
 
-    // One tile: its V loads are issued first and overlap Q.K and the softmax; its K rows were
-    // loaded into LDS during the previous tile.  With MORE it loads the next tile's K once
-    // Q.K is done.  The last tile of a chunk is a separate instance, so that every path into
-    // a tile has exactly the tile's K loads in flight before its V loads (which lets the wait
-    // below be exact).
+    // One tile: its V loads are issued first and land during Q.K and the softmax; its K rows
+    // were loaded during the previous tile.  With MORE it loads the next tile's K once Q.K is
+    // done and its V once P.V is done.  The last tile of a chunk is a separate instance, so
+    // that every path into a tile has exactly the tile's K loads in flight before its V loads
+    // (which lets the waits below be exact).
     auto tile = [&](int k, auto more_tag) {
       constexpr bool more = decltype(more_tag)::value;
-      uint4 v4[16];
-      asm volatile("" ::: "memory");  // V loads strictly after the K loads
-      issue_v(k, v4);
-      // The 16 V loads of this tile are the only memory loads issued after its K loads.
-      __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16): this tile's K rows have landed
+      if (k == 0) {
+        asm volatile("" ::: "memory");  // V loads strictly after the K loads
+        issue_rows(0, 1, vt);
+      }
+      // The 8 V loads of this tile are the only memory loads issued after its K loads.
+      __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8): this tile's K rows have landed
       wave_lds_sync();
 
-      // ---- scores of this lane's token against the G heads, K read from LDS two chunks at a
-      // time (the next pair in flight while a pair is used).
-      float s[G];
+      // ---- Q.K on the matrix cores: token blocks b = 0, 1 of 16.
+      f32x4_t sacc[2];
 #pragma unroll
-      for (int g = 0; g < G; ++g) s[g] = 0.0f;
-      uint32_t kbase = lane * 256, sw = lane & 15;
-      asm volatile("" : "+v"(kbase), "+v"(sw));
-      auto kread = [&](int i) {
-        return *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(kt) + kbase +
-                                               16 * (i ^ sw));
-      };
-      // Q.K runs in steps of (K chunk i, group of GB heads).  The Q of the next step is
-      // requested through the scalar cache while a step is computed; its base address is
-      // laundered and tied to the running scores, so that only two steps' Q (2 x 4GB dwords)
-      // are live in SGPRs, instead of all G*64 dwords being hoisted (and spilled).
-      constexpr int GB = G < 4 ? G : 4;
-      constexpr int kSteps = 16 * (G / GB);
-      auto load_q = [&](int st, uint32_t (&q)[GB][4]) {
-        const int i = st / (G / GB), g0 = (st % (G / GB)) * GB;
-        uint64_t qaddr = reinterpret_cast<uint64_t>(qs);
-        if constexpr (G == 1) asm volatile("" : "+s"(qaddr), "+v"(s[0]));
-        else if constexpr (G == 2) asm volatile("" : "+s"(qaddr), "+v"(s[0]), "+v"(s[1]));
-        else {
+      for (int bb = 0; bb < 2; ++bb) {
+        sacc[bb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        const int t = 16 * bb + l16;
 #pragma unroll
-          for (int g = 0; g < G; g += 4)
-            asm volatile("" : "+s"(qaddr), "+v"(s[g]), "+v"(s[g + 1]), "+v"(s[g + 2]),
-                         "+v"(s[g + 3]));
-        }
-        const const_u32_ptr qt = reinterpret_cast<const_u32_ptr>(qaddr);
-#pragma unroll
-        for (int g = 0; g < GB; ++g) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) q[g][e] = qt[(g0 + g) * qhs + 4 * i + e];
-        }
-      };
-      uint32_t qc[GB][4];
-      load_q(0, qc);
-      uint4 ka = kread(0), kb = kread(1);
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        const uint4 k0 = ka, k1 = kb;
-        if (i + 2 < 16) {
-          ka = kread(i + 2);
-          kb = kread(i + 3);
-        }
-#pragma unroll
-        for (int st = i * (G / GB); st < (i + 2) * (G / GB); ++st) {
-          uint32_t qn[GB][4];
-          if (st + 1 < kSteps) load_q(st + 1, qn);
-          const uint4 kc = (st / (G / GB)) == i ? k0 : k1;
-          const uint32_t kk[4] = {kc.x, kc.y, kc.z, kc.w};
-          const int g0 = (st % (G / GB)) * GB;
-#pragma unroll
-          for (int g = 0; g < GB; ++g) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) s[g0 + g] = dot2_bf16(qc[g][e], kk[e], s[g0 + g]);
-          }
-          if (st + 1 < kSteps) {
-#pragma unroll
-            for (int g = 0; g < GB; ++g) {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) qc[g][e] = qn[g][e];
-            }
-          }
+        for (int ks = 0; ks < 4; ++ks) {
+          const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(
+              kt + t * 256 + 16 * ((4 * ks + g4) ^ (t & 15)));
+          sacc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qfr[ks], sacc[bb], 0, 0, 0);
         }
       }
-      const uint64_t vmask = vms[k];
-      const bool valid = (vmask >> lane) & 1ull;
-      // Every K read has returned before the next tile's rows overwrite the tile.  The
-      // scheduling barriers keep the phases in order: nothing that needs this tile's V is
-      // moved up into Q.K (which would wait for V early).
+      // Every K read has returned before the next tile's rows overwrite the tile.
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (more) issue_k(k + 1);
-      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (more) issue_rows(k + 1, 0, kt);
 
-      // ---- online softmax (base 2); P rounded to bf16 as the reference does before P.V.
-      // A masked token's score is never used, so its (possibly poisoned) K needs no zeroing.
-      const int pslot = ((lane >> 3) * 4 + (lane & 3)) * G;  // pair of token `lane`
-      const int phalf = (lane >> 2) & 1;                      // its half of the pair
-      float z[G], mt[G];
+      // ---- online softmax (base 2) for head l16; P rounded to bf16 as the reference does
+      // before P.V.  A masked token's score is never used, so its (possibly poisoned) K needs
+      // no zeroing.
+      const uint32_t vmask = vms[k];
+      float z[8];
 #pragma unroll
-      for (int g = 0; g < G; ++g) z[g] = valid ? s[g] * P.scale_log2 : -INFINITY;
-      tile_max<G>(z, mt);
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float mn = fmaxf(m[g], mt[g]);
-        float alpha = 1.0f, pexp = 0.0f;
-        if (mn != -INFINITY) {
-          alpha = exp2f(m[g] - mn);
-          pexp = exp2f(z[g] - mn);
-        }
-        const uint32_t pbits = f32_to_bf16(pexp);
-        l[g] = l[g] * alpha + bf16_to_f32(pbits);
-#pragma unroll
-        for (int d = 0; d < 8; ++d) acc[g][d] *= alpha;
-        m[g] = mn;
-        reinterpret_cast<uint16_t*>(pr)[2 * (pslot + g) + phalf] = (uint16_t)pbits;
-      }
-      // This tile's V has landed (only the next tile's K loads may still be in flight).
-      if constexpr (more) __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16)
-      else __builtin_amdgcn_s_waitcnt(0x0F70);                 // vmcnt(0)
-      // A masked token's V may hold anything (NaN-poisoned slots included): zero it.
-      if (vmask != ~0ull) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (!((vmask >> (4 * i + qq)) & 1ull)) v4[i] = make_uint4(0, 0, 0, 0);
-      }
-      wave_lds_sync();
-
-      // ---- P.V: pair j = tokens 8j+qq and 8j+4+qq (loads 2j and 2j+1 of this lane)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        uint32_t pp[G];
-#pragma unroll
-        for (int g = 0; g < G; ++g) pp[g] = pr[(j * 4 + qq) * G + g];
-        const uint4 a = v4[2 * j], b = v4[2 * j + 1];
-        const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
+      for (int bb = 0; bb < 2; ++bb) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const uint32_t vlo = __builtin_amdgcn_perm(bw[e], aw[e], 0x05040100u);  // dim 2e
-          const uint32_t vhi = __builtin_amdgcn_perm(bw[e], aw[e], 0x07060302u);  // dim 2e+1
+          const int t = 16 * bb + 4 * g4 + e;
+          z[4 * bb + e] = ((vmask >> t) & 1u) ? sacc[bb][e] * P.scale_log2 : -INFINITY;
+        }
+      }
+      float tmax = z[0];
 #pragma unroll
-          for (int g = 0; g < G; ++g) {
-            acc[g][2 * e] = dot2_bf16(pp[g], vlo, acc[g][2 * e]);
-            acc[g][2 * e + 1] = dot2_bf16(pp[g], vhi, acc[g][2 * e + 1]);
-          }
+      for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, z[i]);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+      const float mn = fmaxf(m, tmax);
+      float alpha = 1.0f;
+      uint32_t pb[8];
+      float psum = 0.0f;
+      if (mn != -INFINITY) {
+        alpha = exp2f(m - mn);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          pb[i] = f32_to_bf16(exp2f(z[i] - mn));
+          psum += bf16_to_f32(pb[i]);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pb[i] = 0u;
+      }
+      m = mn;
+      lsum = lsum * alpha + psum;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) acc[db] *= alpha;
+      const uint4 pw = make_uint4(pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16),
+                                  pb[4] | (pb[5] << 16), pb[6] | (pb[7] << 16));
+      const bf16x8_t pfr = __builtin_bit_cast(bf16x8_t, pw);
+
+      // This tile's V has landed (only the next tile's K loads may still be in flight).
+      if constexpr (more) __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8)
+      else __builtin_amdgcn_s_waitcnt(0x0F70);                 // vmcnt(0)
+      // A masked token's V row may hold anything (NaN-poisoned slots included): zero it.
+      if (vmask != 0xFFFFFFFFu) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int t = 4 * i + g4;
+          if (!((vmask >> t) & 1u))
+            *reinterpret_cast<uint4*>(vt + t * 256 + 16 * l16) = make_uint4(0, 0, 0, 0);
         }
       }
       wave_lds_sync();
+
+      // ---- P.V on the matrix cores: dim blocks db of 16.  Transposing reads: lane (g4, l16)
+      // supplies the 8 bytes of token 4 g4 + l16/4 (then 16 + that), dims 16 db + 4 (l16 % 4)
+      // .. +3, and receives dim 16 db + l16 of the group's 4 tokens.
+      const int tr_t0 = 4 * g4 + (l16 >> 2), tr_t1 = tr_t0 + 16, q4 = l16 & 3;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const int c = 2 * db + (q4 >> 1), h8 = 8 * (q4 & 1);
+        const uint32_t a0 = lds_u32(vt + tr_t0 * 256 + 16 * (c ^ (tr_t0 & 15)) + h8);
+        const uint32_t a1 = lds_u32(vt + tr_t1 * 256 + 16 * (c ^ (tr_t1 & 15)) + h8);
+        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4_t*)(uintptr_t)a0);
+        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4_t*)(uintptr_t)a1);
+        const bf16x8_t vf = __builtin_bit_cast(
+            bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pfr, acc[db], 0, 0, 0);
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // V reads done: the tile is free
+      if constexpr (more) {
+        asm volatile("" ::: "memory");  // next V loads strictly after the next K loads
+        issue_rows(k + 1, 1, vt);
+      }
     };
     for (int k = 0; k + 1 < nt; ++k) tile(k, std::true_type{});
     tile(nt - 1, std::false_type{});
@@ -371,50 +307,43 @@ __global__ __launch_bounds__(64) void gqa_partial_kernel(GqaParams P) {
     wave_lds_sync();
   }
 
-  // ---- epilogue: sum the four quarters' accumulators, normalise, write dims 8ch..8ch+7
+  // ---- epilogue: lanes with l16 < G hold head l16, dims 16 db + 4 g4 + e.
+  const float ltot = lsum + __shfl_xor(lsum, 16, kWave) + __shfl_xor(lsum, 32, kWave) +
+                     __shfl_xor(__shfl_xor(lsum, 16, kWave), 32, kWave);
+  if (l16 >= G) return;
+  const int hq = kvh * G + l16;
+  const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
+  if (P.splits == 1) {
+    // Gate and output rows are only 4-byte aligned: dword accesses.
+    const uint32_t* gp = P.gate ? reinterpret_cast<const uint32_t*>(
+                                      P.gate + (int64_t)row * P.g_rs + (int64_t)hq * P.g_hs)
+                                : nullptr;
+    uint32_t* op = reinterpret_cast<uint32_t*>(P.out + (int64_t)row * P.o_rs +
+                                               (int64_t)hq * P.o_hs);
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
+    for (int db = 0; db < 8; ++db) {
+      float o[4];
 #pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      float v = acc[g][d];
-      v += __shfl_xor(v, 16, kWave);
-      v += __shfl_xor(v, 32, kWave);
-      acc[g][d] = v;
-    }
-  }
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const float lsum = wave_sum(l[g]);
-    const int hq = kvh * G + g;
-    const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
-    if (qq != 0) continue;
-    float o[8];
-#pragma unroll
-    for (int d = 0; d < 8; ++d) o[d] = acc[g][d] * inv;
-    if (P.splits == 1) {
-      // Gate and output rows are only 4-byte aligned: dword accesses.
-      if (P.gate) {
-        const uint32_t* gp = reinterpret_cast<const uint32_t*>(
-            P.gate + (int64_t)row * P.g_rs + (int64_t)hq * P.g_hs) + 4 * ch;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t gw = gp[e];
-          o[2 * e] *= sigmoidf(bf16lo(gw));
-          o[2 * e + 1] *= sigmoidf(bf16hi(gw));
-        }
+      for (int e = 0; e < 4; ++e) o[e] = acc[db][e] * inv;
+      const int d0 = 16 * db + 4 * g4;
+      if (gp) {
+        const uint32_t g01 = gp[d0 / 2], g23 = gp[d0 / 2 + 1];
+        o[0] *= sigmoidf(bf16lo(g01));
+        o[1] *= sigmoidf(bf16hi(g01));
+        o[2] *= sigmoidf(bf16lo(g23));
+        o[3] *= sigmoidf(bf16hi(g23));
       }
-      uint32_t* op = reinterpret_cast<uint32_t*>(
-          P.out + (int64_t)row * P.o_rs + (int64_t)hq * P.o_hs) + 4 * ch;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        op[e] = (f32_to_bf16(o[2 * e]) & 0xFFFFu) | (f32_to_bf16(o[2 * e + 1]) << 16);
-    } else {
-      const int64_t pi = ((int64_t)split * P.T + row) * P.Hq + hq;
-      float4* dst = reinterpret_cast<float4*>(P.part_o + pi * kHeadDim) + 2 * ch;
-      dst[0] = make_float4(o[0], o[1], o[2], o[3]);
-      dst[1] = make_float4(o[4], o[5], o[6], o[7]);
-      if (lane == 0) P.part_lse[pi] = lsum > 0.0f ? m[g] + log2f(lsum) : -INFINITY;
+      op[d0 / 2] = (f32_to_bf16(o[0]) & 0xFFFFu) | (f32_to_bf16(o[1]) << 16);
+      op[d0 / 2 + 1] = (f32_to_bf16(o[2]) & 0xFFFFu) | (f32_to_bf16(o[3]) << 16);
     }
+  } else {
+    const int64_t pi = ((int64_t)split * P.T + row) * P.Hq + hq;
+    float4* dst = reinterpret_cast<float4*>(P.part_o + pi * kHeadDim);
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+      dst[4 * db + g4] = make_float4(acc[db][0] * inv, acc[db][1] * inv, acc[db][2] * inv,
+                                     acc[db][3] * inv);
+    if (g4 == 0) P.part_lse[pi] = ltot > 0.0f ? m + log2f(ltot) : -INFINITY;
   }
 }
 
@@ -461,13 +390,14 @@ hipError_t launch_partial(const GqaParams& P, hipStream_t s) {
 
 GqaPlan gqa_plan(const qsa_gqa_args& a) {
   GqaPlan p{};
-  p.tiles = (a.packed_width + 63) / 64;
+  p.tiles = (a.packed_width + kTile - 1) / kTile;
   if (p.tiles < 1) p.tiles = 1;
   int target = a.num_splits;
   if (target <= 0) {
-    // Aim for about 2048 workgroups (8 per CU) so the gathers keep HBM busy.
+    // Aim for about 2304 workgroups (9 per CU, what the LDS holds) so that the gathers keep
+    // HBM busy in one wave of workgroups.
     const int64_t base = (int64_t)a.num_tokens * a.num_kv_heads;
-    target = base >= 2048 ? 1 : (int)((2048 + base - 1) / base);
+    target = base >= 2304 ? 1 : (int)((2304 + base - 1) / base);
   }
   if (target > p.tiles) target = p.tiles;
   if (target > 64) target = 64;  // the merge reads one split per lane

@@ -40,7 +40,7 @@ constexpr int kTopkMaxCols = 32768;    // register-resident top-k: 1024 threads 
 TopkLayout topk_layout(const qsa_topk_args& a);
 
 struct GqaPlan {
-  int32_t tiles;        // ceil(W / 64)
+  int32_t tiles;        // ceil(W / 32)
   int32_t splits;       // workgroups per (row, KV head)
   int32_t tiles_per_split;
   size_t ws_bytes;      // partial outputs + lse when splits > 1
