@@ -242,27 +242,29 @@ __global__ __launch_bounds__(64) void gqa_partial_kernel(GqaParams P) {
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
       const float mn = fmaxf(m, tmax);
+      // exp2 of arguments <= 0 (hardware v_exp_f32; results below 2^-126 flush to zero, far
+      // below the bf16 rounding of P), P rounded to bf16 by v_cvt_pk_bf16_f32 (RNE).
       float alpha = 1.0f;
-      uint32_t pb[8];
+      bf16x8_t pfr;
       float psum = 0.0f;
       if (mn != -INFINITY) {
-        alpha = exp2f(m - mn);
+        alpha = __builtin_amdgcn_exp2f(m - mn);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          pb[i] = f32_to_bf16(exp2f(z[i] - mn));
-          psum += bf16_to_f32(pb[i]);
+          pfr[i] = (__bf16)__builtin_amdgcn_exp2f(z[i] - mn);
+          psum += (float)pfr[i];
         }
       } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) pb[i] = 0u;
+        for (int i = 0; i < 8; ++i) pfr[i] = (__bf16)0.0f;
       }
       m = mn;
       lsum = lsum * alpha + psum;
+      // Rescale the accumulators only when some head's max moved (wave-uniform test).
+      if (__ballot(alpha != 1.0f) != 0ull) {
 #pragma unroll
-      for (int db = 0; db < 8; ++db) acc[db] *= alpha;
-      const uint4 pw = make_uint4(pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16),
-                                  pb[4] | (pb[5] << 16), pb[6] | (pb[7] << 16));
-      const bf16x8_t pfr = __builtin_bit_cast(bf16x8_t, pw);
+        for (int db = 0; db < 8; ++db) acc[db] *= alpha;
+      }
 
       // This tile's V has landed (only the next tile's K loads may still be in flight).
       if constexpr (more) __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8)
@@ -394,10 +396,10 @@ GqaPlan gqa_plan(const qsa_gqa_args& a) {
   if (p.tiles < 1) p.tiles = 1;
   int target = a.num_splits;
   if (target <= 0) {
-    // Aim for about 2304 workgroups (9 per CU, what the LDS holds) so that the gathers keep
-    // HBM busy in one wave of workgroups.
+    // Aim for about 2048 workgroups (8 per CU, what the registers allow) so that the gathers
+    // keep HBM busy in one wave of workgroups.
     const int64_t base = (int64_t)a.num_tokens * a.num_kv_heads;
-    target = base >= 2304 ? 1 : (int)((2304 + base - 1) / base);
+    target = base >= 2048 ? 1 : (int)((2048 + base - 1) / base);
   }
   if (target > p.tiles) target = p.tiles;
   if (target > 64) target = 64;  // the merge reads one split per lane
