@@ -652,16 +652,28 @@ __device__ float folded_score16(const SelectParams& P, const float* qfold, int r
 // Band entries kept in LDS; larger bands (adversarial ties) use the workspace.
 constexpr int kBandCap = 1024;
 
+// Inclusive prefix sum over the 64 lanes of a wavefront: shifts within rows of 16, then the
+// row totals broadcast to the later rows (DPP, no LDS round trips).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15 -> rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31 -> rows 2, 3
+  return v;
+}
+
 // One workgroup of NT threads per row; thread t holds the fast scores of blocks
 // t*E .. t*E+E-1 in registers for the whole selection.
 template <int NT, int E>
 __global__ __launch_bounds__(NT) void topk_kernel(SelectParams P) {
   extern __shared__ uint32_t sel_mask[];  // [ceil(cols / 32)] band-selected blocks
-  __shared__ int32_t qsl_s[kQslCap];
-  __shared__ int hist[256];
+  __shared__ int hist[2][256];
   __shared__ int s_int[4];
   __shared__ int s_wave[NT / 64];
   __shared__ double s_dbl[NT / 64];
+  __shared__ float s_flt[NT / 64];
   __shared__ float qrow[16 * kHeadDim];
   __shared__ float qfold[kHeadDim];
   __shared__ int32_t band_idx_s[kBandCap];
@@ -671,11 +683,42 @@ __global__ __launch_bounds__(NT) void topk_kernel(SelectParams P) {
   const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int W = P.budget + P.c - 1, kb = P.budget / P.c;
   int32_t* out = P.packed + (int64_t)row * P.p_rs;
-  const int32_t* qsl = stage_qsl(P.qsl, P.R, qsl_s);
-  const int r = find_request(qsl, P.R, row);
+
+  // ---- loads that need only the row, issued first: this thread's fast scores (the row is
+  // padded to col_stride) and its share of the Q row.
+  const float* lg = P.logits + (int64_t)row * P.col_stride;
+  const int jb = tid * E;
+  float sc[E];
+#pragma unroll
+  for (int i = 0; i < E; i += 4) {
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (jb + i < P.col_stride) v = *reinterpret_cast<const float4*>(lg + jb + i);
+    sc[i] = v.x;
+    sc[i + 1] = v.y;
+    sc[i + 2] = v.z;
+    sc[i + 3] = v.w;
+  }
+  constexpr int kQPer = (16 * kHeadDim + NT - 1) / NT;
+  float qv[kQPer];
+#pragma unroll
+  for (int k = 0; k < kQPer; ++k) {
+    const int i = tid + k * NT;
+    qv[k] = i < P.Hi * kHeadDim ? load_q_value(P, (int64_t)row * P.Hi * kHeadDim + i) : 0.0f;
+  }
+
+  // ---- the row's request: the thread whose interval [qsl[i], qsl[i+1]) holds the row.
+  bool mine = false;
+  for (int i = tid; i < P.R; i += NT) {
+    if (P.qsl[i] <= row && row < P.qsl[i + 1]) {
+      s_int[0] = i;
+      mine = true;
+    }
+  }
+  for (int i = tid; i < 2 * 256; i += NT) (&hist[0][0])[i] = 0;
+  const int r = __syncthreads_or(mine) ? s_int[0] : -1;
   int p = -1, L = 0, n_req = 0;
   if (r >= 0) {
-    const int q0 = qsl[r], n = qsl[r + 1] - q0;
+    const int q0 = P.qsl[r], n = P.qsl[r + 1] - q0;
     n_req = n;
     L = P.seq_lens[r];
     if (L - n >= 0) p = L - n + (row - q0);
@@ -693,75 +736,83 @@ __global__ __launch_bounds__(NT) void topk_kernel(SelectParams P) {
     for (int col = tid; col <= W; col += NT) out[col] = col < cnt ? col : (col < W ? -1 : cnt);
     return;
   }
-
-  // ---- this thread's scores (vectorised loads; the row is padded to col_stride)
-  const float* lg = P.logits + (int64_t)row * P.col_stride;
-  const int jb = tid * E;
-  float sc[E];
-#pragma unroll
-  for (int i = 0; i < E; i += 4) {
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (jb + i < P.col_stride) v = *reinterpret_cast<const float4*>(lg + jb + i);
-    sc[i] = v.x;
-    sc[i + 1] = v.y;
-    sc[i + 2] = v.z;
-    sc[i + 3] = v.w;
+  // max |k| of the request's 128-key blocks (for the error bound, reduced later).
+  float km = 0.0f;
+  {
+    const int nt = min(P.key_blocks, (min(L / P.c, P.cols) + 127) / 128);
+    for (int t = tid; t < nt; t += NT) km = fmaxf(km, P.kmax[(int64_t)r * P.key_blocks + t]);
   }
-  // Q row (for the band re-scoring and the error bound), float copies of exact values.
-  for (int i = tid; i < P.Hi * kHeadDim; i += NT)
-    qrow[i] = load_q_value(P, (int64_t)row * P.Hi * kHeadDim + i);
+  double qa = 0.0;
+#pragma unroll
+  for (int k = 0; k < kQPer; ++k) {
+    const int i = tid + k * NT;
+    if (i < P.Hi * kHeadDim) {
+      qrow[i] = qv[k];
+      qa += fabs((double)qv[k]);
+    }
+  }
+  const int mask_words = (vis + 31) >> 5;
+  for (int i = tid; i < mask_words; i += NT) sel_mask[i] = 0u;
 
-  // ---- kb-th largest fast score: 4-pass MSB-first radix select on order-preserving keys
+  // ---- kb-th largest fast score: 4-pass MSB-first radix select on order-preserving keys,
+  // histograms double-buffered so that a pass needs two barriers.
   uint32_t prefix = 0, pmask = 0;
   int krem = kb;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 256; i += NT) hist[i] = 0;
-    __syncthreads();
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    int* h = hist[pass & 1];
 #pragma unroll
     for (int i = 0; i < E; ++i) {
       const uint32_t u = fkey(sc[i]);
-      if (jb + i < vis && (u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 0xFFu], 1);
+      if (jb + i < vis && (u & pmask) == prefix) atomicAdd(&h[(u >> shift) & 0xFFu], 1);
+    }
+    if (pass == 3) {  // the error-bound inputs, reduced over the workgroup after this barrier
+      const float kmw = wave_max(km);
+      double qaw = qa;
+#pragma unroll
+      for (int mm = 32; mm >= 1; mm >>= 1) qaw += shfl_xor_f64(qaw, mm);
+      if (lane == 0) {
+        s_flt[w] = kmw;
+        s_dbl[w] = qaw;
+      }
     }
     __syncthreads();
     if (w == 0) {
+      // Lane l owns bins 255-4l-i, i = 0..3 (descending); a prefix sum over the lanes gives
+      // the number of keys in higher bins.
       int c4[4], S = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) { c4[i] = hist[4 * lane + i]; S += c4[i]; }
-      int x = S;  // inclusive suffix sum over lanes
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int y = __shfl_down(x, d, kWave);
-        if (lane + d < 64) x += y;
+      for (int i = 0; i < 4; ++i) {
+        c4[i] = h[255 - 4 * lane - i];
+        S += c4[i];
       }
-      int above = x - S;
+      int above = wave_incl_scan(S) - S;
 #pragma unroll
-      for (int i = 3; i >= 0; --i) {
+      for (int i = 0; i < 4; ++i) {
         if (above < krem && krem <= above + c4[i]) {
-          s_int[0] = 4 * lane + i;
-          s_int[1] = krem - above;
+          s_int[1] = 255 - 4 * lane - i;
+          s_int[2] = krem - above;
         }
         above += c4[i];
       }
+    } else if (pass < 3) {
+      int* hn = hist[(pass + 1) & 1];
+      for (int i = tid - 64; i < 256; i += NT - 64) hn[i] = 0;
     }
     __syncthreads();
-    prefix |= (uint32_t)s_int[0] << shift;
+    prefix |= (uint32_t)s_int[1] << shift;
     pmask |= 0xFFu << shift;
-    krem = s_int[1];
+    krem = s_int[2];
   }
   const double Tk = (double)fval(prefix);
 
   // ---- error bound E of the fast scores for this row
-  float km = 0.0f;
-  const int nt = min(P.key_blocks, (min(L / P.c, P.cols) + 127) / 128);
-  for (int t = tid; t < nt; t += NT) km = fmaxf(km, P.kmax[(int64_t)r * P.key_blocks + t]);
-  double qa = 0.0;
-  for (int i = tid; i < P.Hi * kHeadDim; i += NT) qa += fabs((double)qrow[i]);
-  km = wave_max(km);
-  if (lane == 0) s_dbl[w] = km;
-  __syncthreads();
-  double kappa = 0.0;
-  for (int i = 0; i < NT / 64; ++i) kappa = fmax(kappa, s_dbl[i]);
-  const double A = block_sum<NT>(qa, s_dbl);
+  double kappa = 0.0, A = 0.0;
+  for (int i = 0; i < NT / 64; ++i) {
+    kappa = fmax(kappa, (double)s_flt[i]);
+    A += s_dbl[i];
+  }
   // Bound of the head-folded float32 score (the VALU logits, and the second level below), and
   // of the per-head MFMA score (u = 2^-23 covers any rounding the matrix cores may use).
   const double gam_f = (double)(P.Hi + 130) * 0x1p-24;
@@ -771,29 +822,26 @@ __global__ __launch_bounds__(NT) void topk_kernel(SelectParams P) {
   const double Ebound = mfma_row ? 2.0 * gam_m / (1.0 - gam_m) * kappa * A + 1e-30 : E_f;
   const double hi = Tk + 2.0 * Ebound, lo = Tk - 2.0 * Ebound;
 
-  // ---- classify; collect the band (in LDS when it fits, else in the workspace)
-  const int mask_words = (vis + 31) >> 5;
-  for (int i = tid; i < mask_words; i += NT) sel_mask[i] = 0u;
-  int n_in_local = 0, nb_local = 0;
+  // ---- classify; collect the band (in LDS when it fits, else in the workspace).  The two
+  // counts (each below 2^15) travel packed in one workgroup sum.
+  int packed_cnt = 0;
 #pragma unroll
   for (int i = 0; i < E; ++i) {
     const double s = sc[i];
-    if (jb + i < vis) {
-      n_in_local += s > hi;
-      nb_local += s <= hi && s >= lo;
-    }
+    if (jb + i < vis) packed_cnt += (s > hi) ? (1 << 16) : (s >= lo ? 1 : 0);
   }
-  int need = kb - block_sum<NT>(n_in_local, s_wave);
-  int nb = block_sum<NT>(nb_local, s_wave);
+  packed_cnt = block_sum<NT>(packed_cnt, s_wave);
+  int need = kb - (packed_cnt >> 16);
+  int nb = packed_cnt & 0xFFFF;
   const bool in_lds = nb <= kBandCap;
   int32_t* bidx = in_lds ? band_idx_s : P.band_idx + (int64_t)row * P.col_stride;
   double* bscore = in_lds ? band_score_s : P.band_score + (int64_t)row * P.col_stride;
-  if (tid == 0) s_int[2] = 0;
+  if (tid == 0) s_int[3] = 0;
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < E; ++i) {
     const double s = sc[i];
-    if (jb + i < vis && s <= hi && s >= lo) bidx[atomicAdd(&s_int[2], 1)] = jb + i;
+    if (jb + i < vis && s <= hi && s >= lo) bidx[atomicAdd(&s_int[3], 1)] = jb + i;
   }
   __syncthreads();
   const int32_t* band = bidx;
@@ -806,7 +854,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(SelectParams P) {
     // to the float64 re-scoring.
     for (int d = tid; d < kHeadDim; d += NT) {
       float f = qrow[d];
-      for (int h = 1; h < P.Hi; ++h) f = f + qrow[h * kHeadDim + d];
+      for (int hh = 1; hh < P.Hi; ++hh) f = f + qrow[hh * kHeadDim + d];
       qfold[d] = f;
     }
     __syncthreads();
@@ -869,19 +917,17 @@ __global__ __launch_bounds__(NT) void topk_kernel(SelectParams P) {
   }
   __syncthreads();
 
-  // ---- stable compaction in block order (one block-wide scan) and expansion into tokens
+  // ---- stable compaction in block order (one workgroup-wide scan) and expansion into tokens
+  uint32_t selbits = 0;
   int cnt = 0;
 #pragma unroll
   for (int i = 0; i < E; ++i) {
     const int j = jb + i;
-    cnt += (j < vis) && ((double)sc[i] > hi || ((sel_mask[j >> 5] >> (j & 31)) & 1u));
+    const bool sel = (j < vis) && ((double)sc[i] > hi || ((sel_mask[j >> 5] >> (j & 31)) & 1u));
+    selbits |= (sel ? 1u : 0u) << i;
+    cnt += sel;
   }
-  int incl = cnt;  // inclusive scan within the wave
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(incl, d, kWave);
-    if (lane >= d) incl += y;
-  }
+  const int incl = wave_incl_scan(cnt);
   if (lane == 63) s_wave[w] = incl;
   __syncthreads();
   int pos = incl - cnt, total = 0;
@@ -891,19 +937,16 @@ __global__ __launch_bounds__(NT) void topk_kernel(SelectParams P) {
   }
 #pragma unroll
   for (int i = 0; i < E; ++i) {
-    const int j = jb + i;
-    if ((j < vis) && ((double)sc[i] > hi || ((sel_mask[j >> 5] >> (j & 31)) & 1u))) {
+    if ((selbits >> i) & 1u) {
+      const int j = jb + i;
       if (pos < kb)
         for (int m = 0; m < P.c; ++m) out[pos * P.c + m] = j * P.c + m;
       ++pos;
     }
   }
   const int sel = min(total, kb), count = sel * P.c + tail;
-  for (int col = tid; col <= W; col += NT) {
-    if (col < sel * P.c) continue;
-    if (col < count) out[col] = vis * P.c + (col - sel * P.c);
-    else out[col] = col < W ? -1 : count;
-  }
+  for (int col = sel * P.c + tid; col <= W; col += NT)
+    out[col] = col < count ? vis * P.c + (col - sel * P.c) : (col < W ? -1 : count);
 }
 
 template <int NT, int E>
