@@ -349,21 +349,33 @@ __global__ __launch_bounds__(64) void gqa_partial_kernel(GqaParams P) {
   }
 }
 
-// Grid (T, Hq), one wavefront.  Lane s reads split s's log-sum-exp (all splits at once), the
-// weights are formed in-wave, then lane l merges dims 2l, 2l+1 of every split with independent
-// loads.  splits <= 64.
+// Grid (T, Hq), one wavefront.  Lane s reads split s's log-sum-exp while every lane already
+// loads dims 2l, 2l+1 of all splits' partials (one round trip for both); the weights are formed
+// in-wave, then the partials are combined.  splits <= kMergeMax.
+constexpr int kMergeMax = 64;
 __global__ __launch_bounds__(64) void gqa_merge_kernel(GqaParams P) {
   const int row = blockIdx.x, hq = blockIdx.y, lane = threadIdx.x;
   const int64_t stride = (int64_t)P.T * P.Hq;   // between splits
   const int64_t pi0 = (int64_t)row * P.Hq + hq;
   const float lse = lane < P.splits ? P.part_lse[lane * stride + pi0] : -INFINITY;
-  const float M = wave_max(lse);
+  constexpr int kBatch = 16;
   float o0 = 0.0f, o1 = 0.0f;
+  float2 ov[kBatch];
+#pragma unroll
+  for (int s = 0; s < kBatch; ++s)
+    ov[s] = s < P.splits ? reinterpret_cast<const float2*>(P.part_o + (s * stride + pi0) * kHeadDim)[lane]
+                         : make_float2(0.0f, 0.0f);
+  const float M = wave_max(lse);
   if (M != -INFINITY) {
     const float wgt = lse == -INFINITY ? 0.0f : exp2f(lse - M);
     const float inv = 1.0f / wave_sum(wgt);
-#pragma unroll 8
-    for (int s = 0; s < P.splits; ++s) {
+#pragma unroll
+    for (int s = 0; s < kBatch; ++s) {
+      const float ws = __shfl(wgt, s, kWave);
+      o0 += ws * ov[s].x;
+      o1 += ws * ov[s].y;
+    }
+    for (int s = kBatch; s < P.splits; ++s) {
       const float ws = __shfl(wgt, s, kWave);
       const float2 o = reinterpret_cast<const float2*>(P.part_o + (s * stride + pi0) * kHeadDim)[lane];
       o0 += ws * o.x;
@@ -402,7 +414,7 @@ GqaPlan gqa_plan(const qsa_gqa_args& a) {
     target = base >= 2048 ? 1 : (int)((2048 + base - 1) / base);
   }
   if (target > p.tiles) target = p.tiles;
-  if (target > 64) target = 64;  // the merge reads one split per lane
+  if (target > kMergeMax) target = kMergeMax;  // the merge reads one split per lane
   p.tiles_per_split = (p.tiles + target - 1) / target;
   p.splits = (p.tiles + p.tiles_per_split - 1) / p.tiles_per_split;
   p.ws_bytes = 0;
