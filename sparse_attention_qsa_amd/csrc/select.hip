@@ -57,34 +57,54 @@ __device__ __forceinline__ int64_t key_row(const SelectParams& P, int r, int j) 
 
 // ------------------------------------------------------------------------------ logits
 
-// Loads this lane's 16 dims of the 8 keys it owns in a 256-key tile (keys j0 + w*64 + it*8 + kg,
-// it = 0..7) into raw 32-bit words.  Pages come from the LDS-staged block-table slice; a key
-// whose page is out of range reads the cache's first row and is zeroed.
+// Dims held by lane `part` (0..7) of a key's 8 lanes, as index i = 0..15 of its 16 values: fp8
+// rows are 128 bytes and lane p takes bytes 16p..16p+15 (dims 16p+i); bf16 rows are 256 bytes
+// and lane p takes bytes 16p..16p+15 and 128+16p..128+16p+15 (dims 8p+i and 64+8p+i-8), so each
+// of the two loads covers 128 contiguous bytes of every row.
 template <bool FP8>
-__device__ __forceinline__ void load_key_tile(const SelectParams& P, const int32_t* pages,
-                                              int col0, int ncols, int j0, int vis_max, int w,
-                                              int kg, int part,
-                                              uint32_t (&raw)[8][FP8 ? 4 : 8]) {
+__device__ __forceinline__ int lane_dim(int part, int i) {
+  if (FP8) return part * 16 + i;
+  return i < 8 ? part * 8 + i : 64 + part * 8 + (i - 8);
+}
+
+// Loads this lane's 16 dims of the 8 keys it owns in tile `tile` of the workgroup (keys
+// tile*256 + w*64 + it*8 + kg, it = 0..7) into raw 32-bit words.  `rows` holds the cache row of
+// each of the workgroup's keys (-1: out of range or not visible; such a key reads the cache's
+// first row and is masked when scored).  `okm` bit `it` marks the valid keys.
+template <bool FP8>
+__device__ __forceinline__ void load_key_tile(const SelectParams& P, const int32_t* rows,
+                                              int tile, int w, int kg, int part,
+                                              uint32_t (&raw)[8][FP8 ? 4 : 8], uint32_t& okm) {
   constexpr int kWords = FP8 ? 4 : 8;
-  const char* base = reinterpret_cast<const char*>(P.ckv);
+  const char* base = reinterpret_cast<const char*>(P.ckv) + part * 16;
+  int row[8];
+#pragma unroll
+  for (int it = 0; it < 8; ++it) row[it] = rows[tile * kLogitsKeysPerWG + w * 64 + it * 8 + kg];
+  // The mask is applied when the tile is scored: a select here would consume the loaded words
+  // at once and make the wave wait for them.
+  okm = 0;
 #pragma unroll
   for (int it = 0; it < 8; ++it) {
-    const int j = j0 + w * 64 + it * 8 + kg;
-    const int c = j / P.Pc - col0;
-    const int page = (j < vis_max && c >= 0 && c < ncols) ? pages[c] : -1;
-    const bool ok = page >= 0 && page < P.c_pages;
-    const int64_t off = ok ? ((int64_t)page * P.Pc + (j % P.Pc)) * kHeadDim : 0;
-    const uint4* src = reinterpret_cast<const uint4*>(base + off * (FP8 ? 1 : 2) +
-                                                      part * (FP8 ? 16 : 32));
+    okm |= (uint32_t)(row[it] >= 0) << it;
+    const char* src = base + (int64_t)max(row[it], 0) * (kHeadDim * (FP8 ? 1 : 2));
 #pragma unroll
     for (int v = 0; v < kWords / 4; ++v) {
-      const uint4 x = src[v];
-      raw[it][4 * v] = ok ? x.x : 0u;
-      raw[it][4 * v + 1] = ok ? x.y : 0u;
-      raw[it][4 * v + 2] = ok ? x.z : 0u;
-      raw[it][4 * v + 3] = ok ? x.w : 0u;
+      const uint4 x = *reinterpret_cast<const uint4*>(src + v * 128);
+      raw[it][4 * v] = x.x;
+      raw[it][4 * v + 1] = x.y;
+      raw[it][4 * v + 2] = x.z;
+      raw[it][4 * v + 3] = x.w;
     }
   }
+}
+
+// Sum over the 8 lanes of an aligned half-row (the lanes sharing a key), on DPP: swap adjacent
+// lanes, then lane pairs, then mirror the two quads.  Every lane ends with the 8-lane sum.
+__device__ __forceinline__ float half_row_sum(float d) {
+  d += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(d), 0xB1, 0xF, 0xF, false));
+  d += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(d), 0x4E, 0xF, 0xF, false));
+  d += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(d), 0x141, 0xF, 0xF, false));
+  return d;
 }
 
 // Scores the 8 keys of `raw` against NR folded rows (held per lane as 16 dims each) and writes
@@ -92,18 +112,21 @@ __device__ __forceinline__ void load_key_tile(const SelectParams& P, const int32
 template <bool FP8, int NR>
 __device__ __forceinline__ void score_key_tile(const SelectParams& P,
                                                const uint32_t (&raw)[8][FP8 ? 4 : 8],
-                                               const float (&qf)[NR][16], int nr, int row0,
+                                               uint32_t okm, const float (&qf)[NR][16], int nr,
+                                               int row0,
                                                int j0, int vis_max, int w, int kg, int part,
                                                bool track_kmax, float& kmax) {
 #pragma unroll
   for (int it = 0; it < 8; ++it) {
     const int j = j0 + w * 64 + it * 8 + kg;
     float k[16];
+    const bool ok = (okm >> it) & 1u;
     if (FP8) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(raw[it][i], false);
-        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(raw[it][i], true);
+        const uint32_t word = ok ? raw[it][i] : 0u;
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
         k[4 * i] = lo[0];
         k[4 * i + 1] = lo[1];
         k[4 * i + 2] = hi[0];
@@ -112,8 +135,9 @@ __device__ __forceinline__ void score_key_tile(const SelectParams& P,
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        k[2 * i] = bf16lo(raw[it][i]);
-        k[2 * i + 1] = bf16hi(raw[it][i]);
+        const uint32_t word = ok ? raw[it][i] : 0u;
+        k[2 * i] = bf16lo(word);
+        k[2 * i + 1] = bf16hi(word);
       }
     }
     if (track_kmax) {
@@ -122,87 +146,134 @@ __device__ __forceinline__ void score_key_tile(const SelectParams& P,
     }
 #pragma unroll
     for (int rr = 0; rr < NR; ++rr) {
-      if (rr >= nr) break;  // wave-uniform
       float d = 0.0f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) d = fmaf(qf[rr][i], k[i], d);
-      d += __shfl_xor(d, 1, kWave);
-      d += __shfl_xor(d, 2, kWave);
-      d += __shfl_xor(d, 4, kWave);
-      if (part == rr && j < vis_max) P.logits[(int64_t)(row0 + rr) * P.col_stride + j] = d;
+      d = half_row_sum(d);
+      // Unconditional buffer store: the row's record ends at its visible keys (none for a row
+      // past nr), and lanes other than `part == rr` aim past it, so the hardware drops them.
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          P.logits + (int64_t)(rr < nr ? row0 + rr : row0) * P.col_stride, 0,
+          rr < nr ? vis_max * 4 : 0, 0x00020000);
+      const uint32_t off = part == rr ? (uint32_t)j * 4u : 0xFFFFFFF0u;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(d), rs, off, 0, 0);
     }
   }
 }
 
-// Grid (wg_per_req, R), 256 threads.  Workgroup k of request r scores the request's keys in
-// tiles 4k .. 4k+3 (256 keys each) against every row of the request, NR rows at a time.  Eight
-// lanes share a key (16 dims each), so one wave load reads eight consecutive compressed rows --
-// 2 KiB (bf16) or 1 KiB (fp8) of contiguous cache.  The block-table slice and the head-folded
-// rows are staged in LDS once; the next tile's keys are in flight while a tile is scored.
+// Grid (wg_per_req, R), 256 threads.  Workgroup k of request r scores the request's keys
+// 1024k .. 1024k+1023 (4 tiles of 256) against every row of the request, NR rows at a time.
+// Eight lanes share a key (16 dims each), so one wave load reads eight compressed rows, 128
+// contiguous bytes of each.  The cache row of every key and the head-folded rows are staged in
+// LDS once; two tiles are in flight from the start and each reload is issued before the other
+// buffer's tile is scored.
 template <bool FP8, int NR>
 __global__ __launch_bounds__(256) void logits_valu_kernel(SelectParams P) {
   constexpr int kWords = FP8 ? 4 : 8;
-  constexpr int kMaxCols = kLogitsTilesPerWG * kLogitsKeysPerWG + 2;
-  __shared__ int32_t pages_s[kMaxCols];
+  constexpr int kKeys = kLogitsTilesPerWG * kLogitsKeysPerWG;
+  static_assert(kLogitsTilesPerWG == 4 && kKeys == 4 * 256,
+                "the tile sequence below is written for 4 tiles of 256 keys");
+  __shared__ int32_t rows_s[kKeys];
   __shared__ float qf_s[NR][kHeadDim];
   __shared__ float red[4];
   const int r = blockIdx.y, k = blockIdx.x;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, kg = lane >> 3, part = lane & 7;
+  const int jw = k * kKeys;  // first key of the workgroup
+  // Block-table entries of this thread's keys jw + tid + 256 i: their addresses do not depend
+  // on the request metadata, so they are loaded together with it (one round trip).
+  int col[kKeys / 256], page[kKeys / 256];
+#pragma unroll
+  for (int i = 0; i < kKeys / 256; ++i) {
+    col[i] = (jw + (int)threadIdx.x + 256 * i) / P.Pc;
+    page[i] = P.cbt[(int64_t)r * P.cbt_stride + min(col[i], P.cbt_width - 1)];
+  }
   // Row range of the request, clamped into [0, T): the metadata is device data the host never
   // saw, so it is not trusted to stay inside the buffers.
   const int q0 = max(0, min(P.qsl[r], P.T));
   const int n = max(0, min(P.qsl[r + 1], P.T) - q0), L = P.seq_lens[r];
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, kg = lane >> 3, part = lane & 7;
   // The MFMA kernel, which runs next, starts its work queues from zero.
   if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 8) P.work[threadIdx.x] = 0;
   // Requests with many rows are scored by the MFMA kernel.
   if (n > P.mfma_min_rows) return;  // block-uniform, before any barrier
   const int vis_max = (n > 0 && n <= L) ? min(L / P.c, P.cols) : 0;
-  const int t_lo = k * kLogitsTilesPerWG;
-  const int t_hi = min(t_lo + kLogitsTilesPerWG,
-                       (vis_max + kLogitsKeysPerWG - 1) / kLogitsKeysPerWG);
+  // Barrier without a memory fence (a fence would wait for every load in flight); the LDS
+  // writes before it are complete, and global loads are waited for where their data is used.
+  auto barrier = [] {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
   float kmax = 0.0f;
-  if (t_lo < t_hi) {  // block-uniform
-    // Block-table slice covering keys [t_lo*256, t_hi*256).
-    const int col0 = t_lo * kLogitsKeysPerWG / P.Pc;
-    const int ncols = min((t_hi * kLogitsKeysPerWG - 1) / P.Pc - col0 + 1, kMaxCols);
-    for (int c = threadIdx.x; c < ncols; c += 256) {
-      const int col = col0 + c;
-      pages_s[c] = col < P.cbt_width ? P.cbt[(int64_t)r * P.cbt_stride + col] : -1;
+  if (jw < vis_max) {  // block-uniform
+#pragma unroll
+    for (int i = 0; i < kKeys / 256; ++i) {
+      const int j = jw + threadIdx.x + 256 * i;
+      const bool ok = j < vis_max && col[i] < P.cbt_width && page[i] >= 0 && page[i] < P.c_pages;
+      rows_s[threadIdx.x + 256 * i] = ok ? page[i] * P.Pc + (j - col[i] * P.Pc) : -1;
     }
     for (int rr0 = 0; rr0 < n; rr0 += NR) {
       const int nr = min(NR, n - rr0);
-      __syncthreads();  // pages staged / the previous chunk's readers are done with qf_s
-      for (int e = threadIdx.x; e < nr * kHeadDim; e += 256) {
-        const int rr = e >> 7, d = e & (kHeadDim - 1);
+      // Head-folded Q of the chunk's rows: each of the first nr*128 threads owns one (row, dim)
+      // and loads all its heads at once (clamped to Hi - 1, the extra terms added as zero).
+      constexpr int kSlots = (NR * kHeadDim + 255) / 256;
+      uint32_t v[kSlots][16];  // raw bf16 / e4m3 codes, decoded once the key loads are out
+#pragma unroll
+      for (int sl = 0; sl < kSlots; ++sl) {
+        const int e = threadIdx.x + 256 * sl;
+        const int rr = min(e >> 7, nr - 1), d = e & (kHeadDim - 1);
         const int64_t qb = (int64_t)(q0 + rr0 + rr) * P.Hi * kHeadDim + d;
-        float f = load_q_value(P, qb);
-        for (int h = 1; h < P.Hi; ++h) f = f + load_q_value(P, qb + h * kHeadDim);
-        qf_s[rr][d] = f;
+#pragma unroll
+        for (int h = 0; h < 16; ++h) {
+          const int64_t idx = qb + min(h, P.Hi - 1) * kHeadDim;
+          v[sl][h] = FP8 ? (uint32_t)reinterpret_cast<const uint8_t*>(P.q_idx)[idx]
+                         : (uint32_t)reinterpret_cast<const uint16_t*>(P.q_idx)[idx];
+        }
       }
-      __syncthreads();
+      barrier();  // rows_s written; the previous chunk's readers are done with qf_s
+      // The first two tiles' keys are requested before the wave waits for its Q words.
+      uint32_t a[8][kWords], b[8][kWords], ma, mb;
+      load_key_tile<FP8>(P, rows_s, 0, w, kg, part, a, ma);
+      load_key_tile<FP8>(P, rows_s, 1, w, kg, part, b, mb);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int sl = 0; sl < kSlots; ++sl) {
+        const int e = threadIdx.x + 256 * sl;
+        auto dec = [](uint32_t x) {
+          return FP8 ? e4m3_to_f32_exact((uint8_t)x) : bf16_to_f32((uint16_t)x);
+        };
+        float f = dec(v[sl][0]);
+#pragma unroll
+        for (int h = 1; h < 16; ++h) f = f + (h < P.Hi ? dec(v[sl][h]) : 0.0f);
+        if (e < nr * kHeadDim) qf_s[e >> 7][e & (kHeadDim - 1)] = f;
+      }
+      barrier();
       float qf[NR][16];
 #pragma unroll
       for (int rr = 0; rr < NR; ++rr) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) qf[rr][i] = rr < nr ? qf_s[rr][part * 16 + i] : 0.0f;
+        for (int i = 0; i < 16; ++i)
+          qf[rr][i] = rr < nr ? qf_s[rr][lane_dim<FP8>(part, i)] : 0.0f;
       }
       const bool first = rr0 == 0;
-      uint32_t a[8][kWords], b[8][kWords];
-      load_key_tile<FP8>(P, pages_s, col0, ncols, t_lo * kLogitsKeysPerWG, vis_max, w, kg,
-                         part, a);
-      for (int t = t_lo; t < t_hi; t += 2) {
-        if (t + 1 < t_hi)
-          load_key_tile<FP8>(P, pages_s, col0, ncols, (t + 1) * kLogitsKeysPerWG, vis_max, w,
-                             kg, part, b);
-        score_key_tile<FP8, NR>(P, a, qf, nr, q0 + rr0, t * kLogitsKeysPerWG, vis_max, w, kg,
-                                part, first, kmax);
-        if (t + 2 < t_hi)
-          load_key_tile<FP8>(P, pages_s, col0, ncols, (t + 2) * kLogitsKeysPerWG, vis_max, w,
-                             kg, part, a);
-        if (t + 1 < t_hi)
-          score_key_tile<FP8, NR>(P, b, qf, nr, q0 + rr0, (t + 1) * kLogitsKeysPerWG, vis_max,
-                                  w, kg, part, first, kmax);
-      }
+      const int row0 = q0 + rr0;
+      // Straight-line code: without a loop back-edge the compiler's vmcnt waits name exactly
+      // the tile being scored, and the scheduling barriers keep it from sinking each tile's
+      // loads down to their first use (which it prefers, to shorten register live ranges).
+      __builtin_amdgcn_sched_barrier(0);
+      score_key_tile<FP8, NR>(P, a, ma, qf, nr, row0, jw, vis_max, w, kg, part, first, kmax);
+      __builtin_amdgcn_sched_barrier(0);
+      load_key_tile<FP8>(P, rows_s, 2, w, kg, part, a, ma);
+      __builtin_amdgcn_sched_barrier(0);
+      score_key_tile<FP8, NR>(P, b, mb, qf, nr, row0, jw + 256, vis_max, w, kg, part, first,
+                              kmax);
+      __builtin_amdgcn_sched_barrier(0);
+      load_key_tile<FP8>(P, rows_s, 3, w, kg, part, b, mb);
+      __builtin_amdgcn_sched_barrier(0);
+      score_key_tile<FP8, NR>(P, a, ma, qf, nr, row0, jw + 512, vis_max, w, kg, part, first,
+                              kmax);
+      __builtin_amdgcn_sched_barrier(0);
+      score_key_tile<FP8, NR>(P, b, mb, qf, nr, row0, jw + 768, vis_max, w, kg, part, first,
+                              kmax);
     }
   }
   kmax = wave_max(kmax);
