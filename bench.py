@@ -46,6 +46,11 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--profile-only", action="store_true",
                    help="warm up and run the timed steps only (for rocprofv3)")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only copy MIB MiB device to device 5 times (counter calibration)")
+    p.add_argument("--write-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_DIR"),
+                   help="write profiles/traffic.json from rocprofv3 --pmc FETCH_SIZE and "
+                        "WRITE_SIZE runs of --profile-only and of --copy-calibration")
     return p.parse_args()
 
 
@@ -110,6 +115,82 @@ def traffic_record(call):
     return rec["bytes_per_launch"] if rec.get("source_sha256") == h.hexdigest() else None
 
 
+CALL_KERNELS = {
+    "qsa_compress": ("prep_compress_kernel", "ring_store_kernel"),
+    "qsa_index_logits_topk": ("logits_valu_kernel", "logits_mfma_kernel", "topk_kernel"),
+    "qsa_sparse_gqa": ("gqa_partial_kernel", "gqa_merge_kernel"),
+}
+
+
+def _counter_rows(d):
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        rows += list(csv.DictReader(open(f)))
+    if not rows:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    return rows
+
+
+def write_traffic(fetch_dir, write_dir, cal_dir, cal_mib):
+    """profiles/traffic.json: HBM bytes per launch of each call, from FETCH_SIZE / WRITE_SIZE
+    (KiB per dispatch), each scaled by the factor that maps the same counter on a plain copy of
+    cal_mib MiB to its true size.  A call's launch sums its kernels' per-dispatch averages."""
+    true_bytes = cal_mib * 2**20
+
+    def per_kernel(rows, counter):
+        acc = {}
+        for r in rows:
+            if r["Counter_Name"] != counter:
+                continue
+            key = (r["Kernel_Name"], r.get("Dispatch_Id", ""))
+            acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
+        by_name = {}
+        for (name, _), v in acc.items():
+            by_name.setdefault(name, []).append(v)
+        return {k: sum(v) / len(v) for k, v in by_name.items()}
+
+    cal = {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        pk = per_kernel(_counter_rows(cal_dir), counter)
+        copies = [v for k, v in pk.items() if "qsa::" not in k]
+        if not copies:
+            raise SystemExit("calibration run holds no copy kernel")
+        cal[counter] = true_bytes / (max(copies) * 1024.0)
+    fetch = per_kernel(_counter_rows(fetch_dir), "FETCH_SIZE")
+    write = per_kernel(_counter_rows(write_dir), "WRITE_SIZE")
+    out = {"_note": "HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (KiB "
+                    "per dispatch), scaled by the factor that maps each counter on a plain "
+                    f"{cal_mib} MiB device copy to its true size",
+           "_calibration": cal}
+    for call, kernels in CALL_KERNELS.items():
+        fb = sum(v for k, v in fetch.items() if any(n in k for n in kernels)) * 1024.0
+        wb = sum(v for k, v in write.items() if any(n in k for n in kernels)) * 1024.0
+        h = hashlib.sha256()
+        for f in KERNEL_SOURCES[call]:
+            h.update(open(os.path.join(ROOT, "sparse_attention_qsa_amd", "csrc", f), "rb").read())
+        out[call] = {"fetch_bytes": round(fb * cal["FETCH_SIZE"]),
+                     "write_bytes": round(wb * cal["WRITE_SIZE"]),
+                     "bytes_per_launch": round(fb * cal["FETCH_SIZE"] + wb * cal["WRITE_SIZE"]),
+                     "kernels": sorted(k for k in fetch if any(n in k for n in kernels)),
+                     "source_sha256": h.hexdigest()}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    json.dump(out, open(path, "w"), indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def copy_calibration(mib):
+    """A plain device-to-device copy of mib MiB, 5 times, for counter calibration."""
+    import torch
+    a = torch.ones(mib * 2**20 // 4, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_mib": mib}))
+
+
 def cpu_baseline(host_inputs, wl_meta):
     """The oracle, as it stands, on the whole step of the same workload (host inputs taken
     before any GPU step), single-threaded."""
@@ -128,10 +209,16 @@ def cpu_baseline(host_inputs, wl_meta):
 
 def main():
     args = parse()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic, cal_mib=args.copy_calibration or 1024)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported "
               "(this build has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     import torch
 
     from sparse_attention_qsa_amd.step import QsaStep

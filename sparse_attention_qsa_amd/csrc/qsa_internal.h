@@ -33,8 +33,9 @@ struct TopkLayout {
   size_t total;
 };
 
-constexpr int kLogitsKeysPerWG = 256;  // keys per tile: 4 waves x 64 keys
-constexpr int kLogitsTilesPerWG = 4;   // tiles walked by one logits workgroup
+constexpr int kLogitsThreads = 512;    // VALU logits workgroup: 8 waves
+constexpr int kLogitsKeysPerWG = 512;  // keys per tile: 8 waves x 64 keys
+constexpr int kLogitsTilesPerWG = 2;   // tiles walked by one logits workgroup
 constexpr int kTopkMaxCols = 32768;    // register-resident top-k: 1024 threads x 32 scores
 
 TopkLayout topk_layout(const qsa_topk_args& a);

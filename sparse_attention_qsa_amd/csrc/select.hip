@@ -57,107 +57,129 @@ __device__ __forceinline__ int64_t key_row(const SelectParams& P, int r, int j) 
 
 // ------------------------------------------------------------------------------ logits
 
-// Dims held by lane `part` (0..7) of a key's 8 lanes, as index i = 0..15 of its 16 values: fp8
-// rows are 128 bytes and lane p takes bytes 16p..16p+15 (dims 16p+i); bf16 rows are 256 bytes
-// and lane p takes bytes 16p..16p+15 and 128+16p..128+16p+15 (dims 8p+i and 64+8p+i-8), so each
-// of the two loads covers 128 contiguous bytes of every row.
+// Lane layout of a 64-key wave tile.  A key's row is split over kLanes lanes of 16 bytes: 8 for
+// fp8 (128-byte rows), 16 for bf16 (256-byte rows), so one wave load instruction reads
+// 64 / kLanes consecutive rows -- 1 KiB of contiguous cache -- and a tile takes kLoads
+// instructions.  Lane `x = lane % kLanes` of group `g = lane / kLanes` holds, in load `it`, dims
+// of key `it * (64 / kLanes) + g`: 16x .. 16x+15 (fp8) or 8x .. 8x+7 (bf16).
 template <bool FP8>
-__device__ __forceinline__ int lane_dim(int part, int i) {
-  if (FP8) return part * 16 + i;
-  return i < 8 ? part * 8 + i : 64 + part * 8 + (i - 8);
-}
+struct KeyLanes {
+  static constexpr int kLanes = FP8 ? 8 : 16;
+  static constexpr int kKeysPerLoad = 64 / kLanes;
+  static constexpr int kLoads = 64 / kKeysPerLoad;
+  static constexpr int kDims = FP8 ? 16 : 8;  // dims per lane per key
+};
 
-// Loads this lane's 16 dims of the 8 keys it owns in tile `tile` of the workgroup (keys
-// tile*256 + w*64 + it*8 + kg, it = 0..7) into raw 32-bit words.  `rows` holds the cache row of
-// each of the workgroup's keys (-1: out of range or not visible; such a key reads the cache's
-// first row and is masked when scored).  `okm` bit `it` marks the valid keys.
+// Loads tile `tile` of the workgroup (keys tile*256 + w*64 + 0..63) for this lane.  `rows` holds
+// the cache row of each of the workgroup's keys (-1: out of range or not visible; such a key
+// reads the cache's first row and is masked when scored).  `okm` bit `it` marks load `it` valid.
 template <bool FP8>
 __device__ __forceinline__ void load_key_tile(const SelectParams& P, const int32_t* rows,
-                                              int tile, int w, int kg, int part,
-                                              uint32_t (&raw)[8][FP8 ? 4 : 8], uint32_t& okm) {
-  constexpr int kWords = FP8 ? 4 : 8;
-  const char* base = reinterpret_cast<const char*>(P.ckv) + part * 16;
-  int row[8];
+                                              int tile, int w, int lane,
+                                              uint32_t (&raw)[KeyLanes<FP8>::kLoads][4],
+                                              uint32_t& okm) {
+  using K = KeyLanes<FP8>;
+  const char* base = reinterpret_cast<const char*>(P.ckv) + (lane % K::kLanes) * 16;
+  const int key0 = tile * kLogitsKeysPerWG + w * 64 + lane / K::kLanes;
+  int row[K::kLoads];
 #pragma unroll
-  for (int it = 0; it < 8; ++it) row[it] = rows[tile * kLogitsKeysPerWG + w * 64 + it * 8 + kg];
+  for (int it = 0; it < K::kLoads; ++it) row[it] = rows[key0 + it * K::kKeysPerLoad];
   // The mask is applied when the tile is scored: a select here would consume the loaded words
   // at once and make the wave wait for them.
   okm = 0;
 #pragma unroll
-  for (int it = 0; it < 8; ++it) {
+  for (int it = 0; it < K::kLoads; ++it) {
     okm |= (uint32_t)(row[it] >= 0) << it;
-    const char* src = base + (int64_t)max(row[it], 0) * (kHeadDim * (FP8 ? 1 : 2));
-#pragma unroll
-    for (int v = 0; v < kWords / 4; ++v) {
-      const uint4 x = *reinterpret_cast<const uint4*>(src + v * 128);
-      raw[it][4 * v] = x.x;
-      raw[it][4 * v + 1] = x.y;
-      raw[it][4 * v + 2] = x.z;
-      raw[it][4 * v + 3] = x.w;
-    }
+    const uint4 x = *reinterpret_cast<const uint4*>(
+        base + (int64_t)max(row[it], 0) * (kHeadDim * (FP8 ? 1 : 2)));
+    raw[it][0] = x.x;
+    raw[it][1] = x.y;
+    raw[it][2] = x.z;
+    raw[it][3] = x.w;
   }
 }
 
-// Sum over the 8 lanes of an aligned half-row (the lanes sharing a key), on DPP: swap adjacent
-// lanes, then lane pairs, then mirror the two quads.  Every lane ends with the 8-lane sum.
-__device__ __forceinline__ float half_row_sum(float d) {
-  d += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(d), 0xB1, 0xF, 0xF, false));
-  d += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(d), 0x4E, 0xF, 0xF, false));
-  d += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(d), 0x141, 0xF, 0xF, false));
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the N lanes (8 or 16, aligned) that share a key, on DPP: swap adjacent lanes, then
+// lane pairs, then mirror the quads of each half-row, then (N = 16) the halves of the row.
+// Every lane ends with the N-lane sum.
+template <int N>
+__device__ __forceinline__ float group_sum(float d) {
+  d += dpp_f32<0xB1>(d);   // quad_perm [1,0,3,2]
+  d += dpp_f32<0x4E>(d);   // quad_perm [2,3,0,1]
+  d += dpp_f32<0x141>(d);  // row_half_mirror
+  if (N == 16) d += dpp_f32<0x140>(d);  // row_mirror
   return d;
 }
 
-// Scores the 8 keys of `raw` against NR folded rows (held per lane as 16 dims each) and writes
-// the logits; lanes part == rr write row rr.  Updates the lane's running max |k|.
+// Scores the tile in `raw` against NR folded rows (qf: this lane's dims of each row) and writes
+// the logits.  After the group sums, lane x of group g keeps the sum of load it = x, so every
+// lane ends with one key -- it*(64/kLanes) + g -- and each row is written with one store.
+// Updates the lane's running max |k|.
 template <bool FP8, int NR>
 __device__ __forceinline__ void score_key_tile(const SelectParams& P,
-                                               const uint32_t (&raw)[8][FP8 ? 4 : 8],
+                                               const uint32_t (&raw)[KeyLanes<FP8>::kLoads][4],
                                                uint32_t okm, const float (&qf)[NR][16], int nr,
-                                               int row0,
-                                               int j0, int vis_max, int w, int kg, int part,
+                                               int row0, int j0, int vis_max, int lane,
                                                bool track_kmax, float& kmax) {
+  using K = KeyLanes<FP8>;
+  const int x = lane % K::kLanes, g = lane / K::kLanes;
+  // One-hot weight of load `it` for this lane, as arithmetic: a compare would tie up a scalar
+  // register pair per load.
+  const uint32_t onehot = 1u << x;
+  float res[NR];
 #pragma unroll
-  for (int it = 0; it < 8; ++it) {
-    const int j = j0 + w * 64 + it * 8 + kg;
+  for (int rr = 0; rr < NR; ++rr) res[rr] = 0.0f;
+#pragma unroll
+  for (int it = 0; it < K::kLoads; ++it) {
     float k[16];
     const bool ok = (okm >> it) & 1u;
-    if (FP8) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t word = ok ? raw[it][i] : 0u;
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t word = raw[it][i];
+      if (FP8) {
         const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
         const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
         k[4 * i] = lo[0];
         k[4 * i + 1] = lo[1];
         k[4 * i + 2] = hi[0];
         k[4 * i + 3] = hi[1];
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t word = ok ? raw[it][i] : 0u;
+      } else {
         k[2 * i] = bf16lo(word);
         k[2 * i + 1] = bf16hi(word);
       }
     }
+    // A masked key reads the cache's first row, whatever it holds: its values are dropped by
+    // selects (never by arithmetic, which a NaN there would survive).
     if (track_kmax) {
+      float m = fabsf(k[0]);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) kmax = fmaxf(kmax, fabsf(k[i]));
+      for (int i = 1; i < K::kDims; ++i) m = fmaxf(m, fabsf(k[i]));
+      kmax = fmaxf(kmax, ok ? m : 0.0f);
     }
 #pragma unroll
     for (int rr = 0; rr < NR; ++rr) {
       float d = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) d = fmaf(qf[rr][i], k[i], d);
-      d = half_row_sum(d);
-      // Unconditional buffer store: the row's record ends at its visible keys (none for a row
-      // past nr), and lanes other than `part == rr` aim past it, so the hardware drops them.
-      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-          P.logits + (int64_t)(rr < nr ? row0 + rr : row0) * P.col_stride, 0,
-          rr < nr ? vis_max * 4 : 0, 0x00020000);
-      const uint32_t off = part == rr ? (uint32_t)j * 4u : 0xFFFFFFF0u;
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(d), rs, off, 0, 0);
+      for (int i = 0; i < K::kDims; ++i) d = fmaf(qf[rr][i], k[i], d);
+      d = group_sum<K::kLanes>(ok ? d : 0.0f);
+      res[rr] = fmaf((float)((onehot >> it) & 1u), d, res[rr]);  // exact: one term is d
     }
+  }
+  // Unconditional buffer stores: a row's record ends at its visible keys (none for a row past
+  // nr), so the hardware drops the rest; lanes x >= kLoads hold no key.
+  const int j = j0 + x * K::kKeysPerLoad + g;
+#pragma unroll
+  for (int rr = 0; rr < NR; ++rr) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        P.logits + (int64_t)(rr < nr ? row0 + rr : row0) * P.col_stride, 0,
+        rr < nr ? vis_max * 4 : 0, 0x00020000);
+    const uint32_t off = x < K::kLoads ? (uint32_t)j * 4u : 0xFFFFFFF0u;
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(res[rr]), rs, off, 0, 0);
   }
 }
 
@@ -168,23 +190,24 @@ __device__ __forceinline__ void score_key_tile(const SelectParams& P,
 // LDS once; two tiles are in flight from the start and each reload is issued before the other
 // buffer's tile is scored.
 template <bool FP8, int NR>
-__global__ __launch_bounds__(256) void logits_valu_kernel(SelectParams P) {
-  constexpr int kWords = FP8 ? 4 : 8;
+__global__ __launch_bounds__(kLogitsThreads) __attribute__((amdgpu_waves_per_eu(NR >= 4 ? 2 : 4)))
+void logits_valu_kernel(SelectParams P) {
+  using KL = KeyLanes<FP8>;
+  constexpr int kT = kLogitsThreads, kWaves = kLogitsThreads / 64;
   constexpr int kKeys = kLogitsTilesPerWG * kLogitsKeysPerWG;
-  static_assert(kLogitsTilesPerWG == 4 && kKeys == 4 * 256,
-                "the tile sequence below is written for 4 tiles of 256 keys");
+  static_assert(kLogitsKeysPerWG == kWaves * 64, "a tile is 64 keys per wave");
   __shared__ int32_t rows_s[kKeys];
   __shared__ float qf_s[NR][kHeadDim];
-  __shared__ float red[4];
+  __shared__ float red[kWaves];
   const int r = blockIdx.y, k = blockIdx.x;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, kg = lane >> 3, part = lane & 7;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int jw = k * kKeys;  // first key of the workgroup
-  // Block-table entries of this thread's keys jw + tid + 256 i: their addresses do not depend
+  // Block-table entries of this thread's keys jw + tid + kT i: their addresses do not depend
   // on the request metadata, so they are loaded together with it (one round trip).
-  int col[kKeys / 256], page[kKeys / 256];
+  int col[kKeys / kT], page[kKeys / kT];
 #pragma unroll
-  for (int i = 0; i < kKeys / 256; ++i) {
-    col[i] = (jw + (int)threadIdx.x + 256 * i) / P.Pc;
+  for (int i = 0; i < kKeys / kT; ++i) {
+    col[i] = (jw + (int)threadIdx.x + kT * i) / P.Pc;
     page[i] = P.cbt[(int64_t)r * P.cbt_stride + min(col[i], P.cbt_width - 1)];
   }
   // Row range of the request, clamped into [0, T): the metadata is device data the host never
@@ -206,20 +229,20 @@ __global__ __launch_bounds__(256) void logits_valu_kernel(SelectParams P) {
   float kmax = 0.0f;
   if (jw < vis_max) {  // block-uniform
 #pragma unroll
-    for (int i = 0; i < kKeys / 256; ++i) {
-      const int j = jw + threadIdx.x + 256 * i;
+    for (int i = 0; i < kKeys / kT; ++i) {
+      const int j = jw + threadIdx.x + kT * i;
       const bool ok = j < vis_max && col[i] < P.cbt_width && page[i] >= 0 && page[i] < P.c_pages;
-      rows_s[threadIdx.x + 256 * i] = ok ? page[i] * P.Pc + (j - col[i] * P.Pc) : -1;
+      rows_s[threadIdx.x + kT * i] = ok ? page[i] * P.Pc + (j - col[i] * P.Pc) : -1;
     }
     for (int rr0 = 0; rr0 < n; rr0 += NR) {
       const int nr = min(NR, n - rr0);
       // Head-folded Q of the chunk's rows: each of the first nr*128 threads owns one (row, dim)
       // and loads all its heads at once (clamped to Hi - 1, the extra terms added as zero).
-      constexpr int kSlots = (NR * kHeadDim + 255) / 256;
-      uint32_t v[kSlots][16];  // raw bf16 / e4m3 codes, decoded once the key loads are out
+      constexpr int kSlots = (NR * kHeadDim + kT - 1) / kT;
+      uint32_t v[kSlots][16];  // raw bf16 / e4m3 codes
 #pragma unroll
       for (int sl = 0; sl < kSlots; ++sl) {
-        const int e = threadIdx.x + 256 * sl;
+        const int e = threadIdx.x + kT * sl;
         const int rr = min(e >> 7, nr - 1), d = e & (kHeadDim - 1);
         const int64_t qb = (int64_t)(q0 + rr0 + rr) * P.Hi * kHeadDim + d;
 #pragma unroll
@@ -229,61 +252,55 @@ __global__ __launch_bounds__(256) void logits_valu_kernel(SelectParams P) {
                          : (uint32_t)reinterpret_cast<const uint16_t*>(P.q_idx)[idx];
         }
       }
-      barrier();  // rows_s written; the previous chunk's readers are done with qf_s
-      // The first two tiles' keys are requested before the wave waits for its Q words.
-      uint32_t a[8][kWords], b[8][kWords], ma, mb;
-      load_key_tile<FP8>(P, rows_s, 0, w, kg, part, a, ma);
-      load_key_tile<FP8>(P, rows_s, 1, w, kg, part, b, mb);
-      __builtin_amdgcn_sched_barrier(0);
+      // Q first: issued behind the key burst its words would wait several microseconds in
+      // the memory queues, and every wave needs them before it can score (and reload).
 #pragma unroll
       for (int sl = 0; sl < kSlots; ++sl) {
-        const int e = threadIdx.x + 256 * sl;
         auto dec = [](uint32_t x) {
           return FP8 ? e4m3_to_f32_exact((uint8_t)x) : bf16_to_f32((uint16_t)x);
         };
         float f = dec(v[sl][0]);
 #pragma unroll
         for (int h = 1; h < 16; ++h) f = f + (h < P.Hi ? dec(v[sl][h]) : 0.0f);
-        if (e < nr * kHeadDim) qf_s[e >> 7][e & (kHeadDim - 1)] = f;
+        v[sl][0] = __float_as_uint(f);
       }
-      barrier();
+      if (rr0 > 0) barrier();  // the previous chunk's readers are done with qf_s
+#pragma unroll
+      for (int sl = 0; sl < kSlots; ++sl) {
+        const int e = threadIdx.x + kT * sl;
+        if (e < nr * kHeadDim) qf_s[e >> 7][e & (kHeadDim - 1)] = __uint_as_float(v[sl][0]);
+      }
+      barrier();  // rows_s and qf_s written
       float qf[NR][16];
 #pragma unroll
       for (int rr = 0; rr < NR; ++rr) {
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          qf[rr][i] = rr < nr ? qf_s[rr][lane_dim<FP8>(part, i)] : 0.0f;
+          qf[rr][i] = (rr < nr && i < KL::kDims)
+                          ? qf_s[rr][(lane % KL::kLanes) * KL::kDims + i] : 0.0f;
       }
       const bool first = rr0 == 0;
       const int row0 = q0 + rr0;
-      // Straight-line code: without a loop back-edge the compiler's vmcnt waits name exactly
-      // the tile being scored, and the scheduling barriers keep it from sinking each tile's
-      // loads down to their first use (which it prefers, to shorten register live ranges).
-      __builtin_amdgcn_sched_barrier(0);
-      score_key_tile<FP8, NR>(P, a, ma, qf, nr, row0, jw, vis_max, w, kg, part, first, kmax);
-      __builtin_amdgcn_sched_barrier(0);
-      load_key_tile<FP8>(P, rows_s, 2, w, kg, part, a, ma);
-      __builtin_amdgcn_sched_barrier(0);
-      score_key_tile<FP8, NR>(P, b, mb, qf, nr, row0, jw + 256, vis_max, w, kg, part, first,
-                              kmax);
-      __builtin_amdgcn_sched_barrier(0);
-      load_key_tile<FP8>(P, rows_s, 3, w, kg, part, b, mb);
-      __builtin_amdgcn_sched_barrier(0);
-      score_key_tile<FP8, NR>(P, a, ma, qf, nr, row0, jw + 512, vis_max, w, kg, part, first,
-                              kmax);
-      __builtin_amdgcn_sched_barrier(0);
-      score_key_tile<FP8, NR>(P, b, mb, qf, nr, row0, jw + 768, vis_max, w, kg, part, first,
-                              kmax);
+      // One tile in flight per wave; the other waves of the SIMD (four per SIMD) cover its
+      // latency.  The loop is unrolled, so the compiler's vmcnt waits name exactly the tile.
+      uint32_t a[KL::kLoads][4], ma;
+#pragma unroll
+      for (int t = 0; t < kLogitsTilesPerWG; ++t) {
+        load_key_tile<FP8>(P, rows_s, t, w, lane, a, ma);
+        score_key_tile<FP8, NR>(P, a, ma, qf, nr, row0, jw + t * kLogitsKeysPerWG + w * 64,
+                                vis_max, lane, first, kmax);
+      }
     }
   }
   kmax = wave_max(kmax);
   if (lane == 0) red[w] = kmax;
   __syncthreads();
-  if (threadIdx.x < kLogitsTilesPerWG * kLogitsKeysPerWG / 128) {
-    const int blk = k * (kLogitsTilesPerWG * kLogitsKeysPerWG / 128) + threadIdx.x;
-    if (blk < P.key_blocks)
-      P.kmax[(int64_t)r * P.key_blocks + blk] =
-          fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  if (threadIdx.x < kKeys / 128) {
+    const int blk = k * (kKeys / 128) + threadIdx.x;
+    float m = red[0];
+#pragma unroll
+    for (int i = 1; i < kWaves; ++i) m = fmaxf(m, red[i]);
+    if (blk < P.key_blocks) P.kmax[(int64_t)r * P.key_blocks + blk] = m;
   }
 }
 
@@ -291,11 +308,11 @@ template <bool FP8>
 hipError_t launch_logits(const SelectParams& P, int rows_per_chunk, hipStream_t s) {
   const dim3 grid(P.key_tiles, P.R);
   if (rows_per_chunk <= 1)
-    hipLaunchKernelGGL((logits_valu_kernel<FP8, 1>), grid, dim3(256), 0, s, P);
+    hipLaunchKernelGGL((logits_valu_kernel<FP8, 1>), grid, dim3(kLogitsThreads), 0, s, P);
   else if (rows_per_chunk <= 2)
-    hipLaunchKernelGGL((logits_valu_kernel<FP8, 2>), grid, dim3(256), 0, s, P);
+    hipLaunchKernelGGL((logits_valu_kernel<FP8, 2>), grid, dim3(kLogitsThreads), 0, s, P);
   else
-    hipLaunchKernelGGL((logits_valu_kernel<FP8, 4>), grid, dim3(256), 0, s, P);
+    hipLaunchKernelGGL((logits_valu_kernel<FP8, 4>), grid, dim3(kLogitsThreads), 0, s, P);
   return hipGetLastError();
 }
 
