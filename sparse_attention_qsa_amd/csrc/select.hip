@@ -45,16 +45,6 @@ __device__ __forceinline__ float load_q_value(const SelectParams& P, int64_t idx
   return bf16_to_f32(reinterpret_cast<const uint16_t*>(P.q_idx)[idx]);
 }
 
-// Compressed row j of request r: element offset of its first value, or -1 if its page is
-// out of range (the key then reads as zero).
-__device__ __forceinline__ int64_t key_row(const SelectParams& P, int r, int j) {
-  const int col = j / P.Pc;
-  if (col >= P.cbt_width) return -1;
-  const int page = P.cbt[(int64_t)r * P.cbt_stride + col];
-  if (page < 0 || page >= P.c_pages) return -1;
-  return ((int64_t)page * P.Pc + (j % P.Pc)) * kHeadDim;
-}
-
 // ------------------------------------------------------------------------------ logits
 
 // Lane layout of a 64-key wave tile.  A key's row is split over kLanes lanes of 16 bytes: 8 for
@@ -664,10 +654,16 @@ __device__ __forceinline__ float row_down(float x) {
 }
 
 // Key values of the 16-lane group's lane l: dim pairs i = l, l+16, l+32, l+48 (dims 2i, 2i+1),
-// exact as floats; zero for an out-of-range row (j < 0 or its page outside the cache).
-__device__ __forceinline__ void key_pairs16(const SelectParams& P, int r, int j, int l,
-                                           float (&k)[8]) {
-  const int64_t off = j >= 0 ? key_row(P, r, j) : -1;
+// exact as floats; zero for an out-of-range row (j < 0, a column past cw, or its page outside
+// the cache).  `cbt_row` is the request's block-table row (LDS copy or global), cw its width.
+__device__ __forceinline__ void key_pairs16(const SelectParams& P, const int32_t* cbt_row,
+                                           int cw, int j, int l, float (&k)[8]) {
+  int64_t off = -1;
+  if (j >= 0) {
+    const int col = j / P.Pc;
+    const int page = col < cw ? cbt_row[col] : -1;
+    if (page >= 0 && page < P.c_pages) off = ((int64_t)page * P.Pc + (j - col * P.Pc)) * kHeadDim;
+  }
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int i = l + 16 * q;
@@ -694,10 +690,10 @@ __device__ __forceinline__ void key_pairs16(const SelectParams& P, int r, int j,
 // i < 16, ..., += v_{i+1} for i < 1.  Lane l holds v_l, v_{l+16}, v_{l+32}, v_{l+48}, so the
 // first two halvings are in-lane and the last four take the partner 8, 4, 2, 1 lanes up.
 // The heads are then added in order.  The result is valid in lane l = 0.
-__device__ double canonical_score16(const SelectParams& P, const float* qrow, int r, int j,
-                                    int l) {
+__device__ double canonical_score16(const SelectParams& P, const float* qrow,
+                                    const int32_t* cbt_row, int cw, int j, int l) {
   float k[8];
-  key_pairs16(P, r, j, l, k);
+  key_pairs16(P, cbt_row, cw, j, l, k);
   double s = 0.0;
   for (int h = 0; h < P.Hi; ++h) {
     const float* q = qrow + h * kHeadDim;
@@ -721,9 +717,10 @@ __device__ double canonical_score16(const SelectParams& P, const float* qrow, in
 
 // Head-folded float32 score of compressed row j: (sum_h q_h) . k, the fold held in LDS, by a
 // group of 16 lanes; valid in lane l = 0.  Its error is that of the VALU logits.
-__device__ float folded_score16(const SelectParams& P, const float* qfold, int r, int j, int l) {
+__device__ float folded_score16(const SelectParams& P, const float* qfold,
+                                const int32_t* cbt_row, int cw, int j, int l) {
   float k[8];
-  key_pairs16(P, r, j, l, k);
+  key_pairs16(P, cbt_row, cw, j, l, k);
   float x = 0.0f;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
@@ -752,28 +749,64 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
+// Radix select of the kb-th largest fast score: two passes of 12-bit digits over the top 24
+// bits of the order-preserving key.  The last 8 bits stay unresolved: the threshold is known to
+// lie in the value interval of one 256-key bin, which the band below absorbs.
+constexpr int kRadixBits = 12;
+constexpr int kRadixBins = 1 << kRadixBits;
+// The request's block-table row is copied to LDS when it has at most this many columns.
+constexpr int kTopkCbtCap = 2048;
+
+// float32 thresholds that are conservative for the float64 ones: x > up(t) implies x > t, and
+// x < down(t) implies x < t.
+__device__ __forceinline__ float next_up_f32(float f) {  // f finite
+  if (f == 0.0f) return __uint_as_float(1u);
+  const uint32_t u = __float_as_uint(f);
+  return __uint_as_float(f > 0.0f ? u + 1u : u - 1u);
+}
+__device__ __forceinline__ float round_up_f32(double t) {
+  const float f = (float)t;
+  return (double)f >= t ? f : next_up_f32(f);
+}
+__device__ __forceinline__ float round_down_f32(double t) {
+  const float f = (float)t;
+  return (double)f <= t ? f : -next_up_f32(-f);
+}
+
 // One workgroup of NT threads per row; thread t holds the fast scores of blocks
-// t*E .. t*E+E-1 in registers for the whole selection.
+// t*E .. t*E+E-1 in registers for the whole selection (blocks past the visible range as -inf,
+// which no threshold below admits).
 template <int NT, int E>
 __global__ __launch_bounds__(NT) void topk_kernel(SelectParams P) {
+  static_assert(32 % E == 0 || E == 32, "a thread's blocks share one word of the mask");
+  constexpr int kWaves = NT / 64, kPB = kRadixBins / NT;  // bins per thread in the scans
   extern __shared__ uint32_t sel_mask[];  // [ceil(cols / 32)] band-selected blocks
-  __shared__ int hist[2][256];
-  __shared__ int s_int[4];
-  __shared__ int s_wave[NT / 64];
-  __shared__ double s_dbl[NT / 64];
-  __shared__ float s_flt[NT / 64];
+  __shared__ __attribute__((aligned(16))) int hist[2][kRadixBins];
+  __shared__ int s_int[8];
+  __shared__ int s_wave[kWaves];
+  __shared__ double s_dbl[kWaves];
+  __shared__ float s_flt[kWaves];
   __shared__ float qrow[16 * kHeadDim];
   __shared__ float qfold[kHeadDim];
   __shared__ int32_t band_idx_s[kBandCap];
   __shared__ int32_t band2_idx_s[kBandCap];
   __shared__ double band_score_s[kBandCap];
+  __shared__ int32_t cbt_s[kTopkCbtCap];
 
   const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int W = P.budget + P.c - 1, kb = P.budget / P.c;
   int32_t* out = P.packed + (int64_t)row * P.p_rs;
+  // Barriers: LDS-only ones wait for the wave's LDS operations and nothing else (the fence of
+  // __syncthreads would also wait for every global load in flight, such as the prefetches
+  // below); the full one publishes global writes (bands too large for LDS).
+  auto lds_barrier = [] {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
 
   // ---- loads that need only the row, issued first: this thread's fast scores (the row is
-  // padded to col_stride) and its share of the Q row.
+  // padded to col_stride), its share of the Q row, and the request metadata for the lookup.
   const float* lg = P.logits + (int64_t)row * P.col_stride;
   const int jb = tid * E;
   float sc[E];
@@ -787,29 +820,38 @@ __global__ __launch_bounds__(NT) void topk_kernel(SelectParams P) {
     sc[i + 3] = v.w;
   }
   constexpr int kQPer = (16 * kHeadDim + NT - 1) / NT;
-  float qv[kQPer];
+  uint32_t qv[kQPer];  // raw bf16 / e4m3 codes
 #pragma unroll
   for (int k = 0; k < kQPer; ++k) {
-    const int i = tid + k * NT;
-    qv[k] = i < P.Hi * kHeadDim ? load_q_value(P, (int64_t)row * P.Hi * kHeadDim + i) : 0.0f;
+    const int i = min(tid + k * NT, P.Hi * kHeadDim - 1);
+    const int64_t idx = (int64_t)row * P.Hi * kHeadDim + i;
+    qv[k] = P.fp8 ? (uint32_t)reinterpret_cast<const uint8_t*>(P.q_idx)[idx]
+                  : (uint32_t)reinterpret_cast<const uint16_t*>(P.q_idx)[idx];
   }
-
-  // ---- the row's request: the thread whose interval [qsl[i], qsl[i+1]) holds the row.
+  // The row's request: the thread whose interval [qsl[i], qsl[i+1]) holds the row publishes
+  // the request and its metadata (loaded with the interval, not after it).
   bool mine = false;
   for (int i = tid; i < P.R; i += NT) {
-    if (P.qsl[i] <= row && row < P.qsl[i + 1]) {
+    const int a = P.qsl[i], b = P.qsl[i + 1], Li = P.seq_lens[i];
+    if (a <= row && row < b) {
       s_int[0] = i;
+      s_int[1] = a;
+      s_int[2] = b - a;
+      s_int[3] = Li;
       mine = true;
     }
   }
-  for (int i = tid; i < 2 * 256; i += NT) (&hist[0][0])[i] = 0;
-  const int r = __syncthreads_or(mine) ? s_int[0] : -1;
-  int p = -1, L = 0, n_req = 0;
-  if (r >= 0) {
-    const int q0 = P.qsl[r], n = P.qsl[r + 1] - q0;
-    n_req = n;
-    L = P.seq_lens[r];
-    if (L - n >= 0) p = L - n + (row - q0);
+  {
+    int4* h4 = reinterpret_cast<int4*>(&hist[0][0]);
+    for (int i = tid; i < 2 * kRadixBins / 4; i += NT) h4[i] = make_int4(0, 0, 0, 0);
+  }
+  const int any_mine = __syncthreads_or(mine);
+  int p = -1, L = 0, n_req = 0, r = -1;
+  if (any_mine) {
+    r = s_int[0];
+    n_req = s_int[2];
+    L = s_int[3];
+    if (L - n_req >= 0) p = L - n_req + (row - s_int[1]);
   }
   if (p < 0) {  // inert row: no entries, count 0
     for (int col = tid; col <= W; col += NT) out[col] = col < W ? -1 : 0;
@@ -824,38 +866,52 @@ __global__ __launch_bounds__(NT) void topk_kernel(SelectParams P) {
     for (int col = tid; col <= W; col += NT) out[col] = col < cnt ? col : (col < W ? -1 : cnt);
     return;
   }
-  // max |k| of the request's 128-key blocks (for the error bound, reduced later).
+  // Loads that need the request, in flight during the radix passes: max |k| of its 128-key
+  // blocks (for the error bound) and its block-table row (for the band's key rows).
   float km = 0.0f;
   {
     const int nt = min(P.key_blocks, (min(L / P.c, P.cols) + 127) / 128);
     for (int t = tid; t < nt; t += NT) km = fmaxf(km, P.kmax[(int64_t)r * P.key_blocks + t]);
   }
+  const int cw = min(P.cbt_width, (vis + P.Pc - 1) / P.Pc);
+  const bool cbt_in_lds = cw <= kTopkCbtCap;
+  constexpr int kCbtPer = (kTopkCbtCap + NT - 1) / NT;
+  int cbt_v[kCbtPer];
+#pragma unroll
+  for (int k = 0; k < kCbtPer; ++k) {
+    const int c = tid + k * NT;
+    cbt_v[k] = (cbt_in_lds && c < cw) ? P.cbt[(int64_t)r * P.cbt_stride + c] : -1;
+  }
+#pragma unroll
+  for (int i = 0; i < E; ++i) sc[i] = jb + i < vis ? sc[i] : -__builtin_inff();
   double qa = 0.0;
 #pragma unroll
   for (int k = 0; k < kQPer; ++k) {
     const int i = tid + k * NT;
     if (i < P.Hi * kHeadDim) {
-      qrow[i] = qv[k];
-      qa += fabs((double)qv[k]);
+      const float f = P.fp8 ? e4m3_to_f32_exact(qv[k]) : bf16_to_f32((uint16_t)qv[k]);
+      qrow[i] = f;
+      qa += fabs((double)f);
     }
   }
   const int mask_words = (vis + 31) >> 5;
   for (int i = tid; i < mask_words; i += NT) sel_mask[i] = 0u;
 
-  // ---- kb-th largest fast score: 4-pass MSB-first radix select on order-preserving keys,
-  // histograms double-buffered so that a pass needs two barriers.
+  // ---- radix select.  Thread t reads the counts of bins 4095 - t*kPB - i (i < kPB): lower
+  // threads own higher bins, so a workgroup prefix sum gives the count above each bin.  The
+  // -inf entries land in the lowest bin, below any kb-th largest of the visible blocks.
   uint32_t prefix = 0, pmask = 0;
   int krem = kb;
 #pragma unroll
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    int* h = hist[pass & 1];
+  for (int pass = 0; pass < 2; ++pass) {
+    const int shift = 32 - kRadixBits * (pass + 1);
+    int* h = hist[pass];
 #pragma unroll
     for (int i = 0; i < E; ++i) {
       const uint32_t u = fkey(sc[i]);
-      if (jb + i < vis && (u & pmask) == prefix) atomicAdd(&h[(u >> shift) & 0xFFu], 1);
+      if ((u & pmask) == prefix) atomicAdd(&h[(u >> shift) & (kRadixBins - 1)], 1);
     }
-    if (pass == 3) {  // the error-bound inputs, reduced over the workgroup after this barrier
+    if (pass == 1) {  // the error-bound inputs, reduced over the workgroup below
       const float kmw = wave_max(km);
       double qaw = qa;
 #pragma unroll
@@ -865,39 +921,48 @@ __global__ __launch_bounds__(NT) void topk_kernel(SelectParams P) {
         s_dbl[w] = qaw;
       }
     }
-    __syncthreads();
-    if (w == 0) {
-      // Lane l owns bins 255-4l-i, i = 0..3 (descending); a prefix sum over the lanes gives
-      // the number of keys in higher bins.
-      int c4[4], S = 0;
+    lds_barrier();
+    int c[kPB], S = 0;
+    const int b0 = kRadixBins - (tid + 1) * kPB;  // c[i] = count of bin b0 + kPB - 1 - i
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        c4[i] = h[255 - 4 * lane - i];
-        S += c4[i];
-      }
-      int above = wave_incl_scan(S) - S;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (above < krem && krem <= above + c4[i]) {
-          s_int[1] = 255 - 4 * lane - i;
-          s_int[2] = krem - above;
-        }
-        above += c4[i];
-      }
-    } else if (pass < 3) {
-      int* hn = hist[(pass + 1) & 1];
-      for (int i = tid - 64; i < 256; i += NT - 64) hn[i] = 0;
+    for (int i = 0; i < kPB; ++i) {
+      c[i] = h[b0 + kPB - 1 - i];
+      S += c[i];
     }
-    __syncthreads();
-    prefix |= (uint32_t)s_int[1] << shift;
-    pmask |= 0xFFu << shift;
-    krem = s_int[2];
+    const int incl = wave_incl_scan(S);
+    if (lane == 63) s_wave[w] = incl;
+    lds_barrier();
+    int above = incl - S;
+    for (int i = 0; i < w; ++i) above += s_wave[i];
+    if (above < krem && krem <= above + S) {
+#pragma unroll
+      for (int i = 0; i < kPB; ++i) {
+        if (above < krem && krem <= above + c[i]) {
+          s_int[4] = b0 + kPB - 1 - i;
+          s_int[5] = krem - above;
+        }
+        above += c[i];
+      }
+    }
+    lds_barrier();
+    prefix |= (uint32_t)s_int[4] << shift;
+    pmask |= (uint32_t)(kRadixBins - 1) << shift;
+    krem = s_int[5];
   }
-  const double Tk = (double)fval(prefix);
+  // The kb-th largest fast score lies in [T_lo, T_hi], the values of the keys prefix..prefix|255.
+  const double T_lo = (double)fval(prefix), T_hi = (double)fval(prefix | 0xFFu);
+  if (cbt_in_lds) {
+#pragma unroll
+    for (int k = 0; k < kCbtPer; ++k) {
+      const int c = tid + k * NT;
+      if (c < cw) cbt_s[c] = cbt_v[k];
+    }
+  }
+  const int32_t* cbt_row = cbt_in_lds ? cbt_s : P.cbt + (int64_t)r * P.cbt_stride;
 
   // ---- error bound E of the fast scores for this row
   double kappa = 0.0, A = 0.0;
-  for (int i = 0; i < NT / 64; ++i) {
+  for (int i = 0; i < kWaves; ++i) {
     kappa = fmax(kappa, (double)s_flt[i]);
     A += s_dbl[i];
   }
@@ -908,30 +973,37 @@ __global__ __launch_bounds__(NT) void topk_kernel(SelectParams P) {
   const bool mfma_row = n_req > P.mfma_min_rows;
   const double gam_m = (double)(P.Hi * kHeadDim + 2) * 0x1p-23;
   const double Ebound = mfma_row ? 2.0 * gam_m / (1.0 - gam_m) * kappa * A + 1e-30 : E_f;
-  const double hi = Tk + 2.0 * Ebound, lo = Tk - 2.0 * Ebound;
+  // Certainly kept above hi, certainly dropped below lo; float32 forms widen the band only.
+  const float hi = round_up_f32(T_hi + 2.0 * Ebound), lo = round_down_f32(T_lo - 2.0 * Ebound);
 
-  // ---- classify; collect the band (in LDS when it fits, else in the workspace).  The two
-  // counts (each below 2^15) travel packed in one workgroup sum.
-  int packed_cnt = 0;
+  // ---- classify and collect the band in block order: one workgroup scan of the per-thread
+  // counts (band entries in the low half, certain keeps in the high half of a packed int).
+  uint32_t keepbits = 0, bandbits = 0;
 #pragma unroll
   for (int i = 0; i < E; ++i) {
-    const double s = sc[i];
-    if (jb + i < vis) packed_cnt += (s > hi) ? (1 << 16) : (s >= lo ? 1 : 0);
+    keepbits |= (sc[i] > hi ? 1u : 0u) << i;
+    bandbits |= (sc[i] <= hi && sc[i] >= lo ? 1u : 0u) << i;
   }
-  packed_cnt = block_sum<NT>(packed_cnt, s_wave);
-  int need = kb - (packed_cnt >> 16);
-  int nb = packed_cnt & 0xFFFF;
+  const int my_cnt = __builtin_popcount(bandbits) | (__builtin_popcount(keepbits) << 16);
+  const int cl_incl = wave_incl_scan(my_cnt);
+  if (lane == 63) s_wave[w] = cl_incl;
+  if (tid == 0) s_int[6] = 0;  // the second level's counter, read after later barriers
+  lds_barrier();
+  int cl_off = cl_incl - my_cnt, tot = 0;
+  for (int i = 0; i < kWaves; ++i) {
+    cl_off += i < w ? s_wave[i] : 0;
+    tot += s_wave[i];
+  }
+  int need = kb - (tot >> 16);
+  int nb = tot & 0xFFFF;
   const bool in_lds = nb <= kBandCap;
   int32_t* bidx = in_lds ? band_idx_s : P.band_idx + (int64_t)row * P.col_stride;
-  double* bscore = in_lds ? band_score_s : P.band_score + (int64_t)row * P.col_stride;
-  if (tid == 0) s_int[3] = 0;
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < E; ++i) {
-    const double s = sc[i];
-    if (jb + i < vis && s <= hi && s >= lo) bidx[atomicAdd(&s_int[3], 1)] = jb + i;
+  {
+    int o = cl_off & 0xFFFF;
+    for (uint32_t bits = bandbits; bits; bits &= bits - 1) bidx[o++] = jb + __builtin_ctz(bits);
   }
-  __syncthreads();
+  if (in_lds) lds_barrier(); else __syncthreads();
+  double* bscore = in_lds ? band_score_s : P.band_score + (int64_t)row * P.col_stride;
   const int32_t* band = bidx;
   const int groups = NT / 16;  // 16-lane groups: one band entry each at a time
   const int grp = tid >> 4, l16 = tid & 15;
@@ -945,13 +1017,13 @@ __global__ __launch_bounds__(NT) void topk_kernel(SelectParams P) {
       for (int hh = 1; hh < P.Hi; ++hh) f = f + qrow[hh * kHeadDim + d];
       qfold[d] = f;
     }
-    __syncthreads();
+    lds_barrier();
     for (int b0 = 0; b0 < nb; b0 += groups) {
       const int b = b0 + grp;
-      const float fs = folded_score16(P, qfold, r, b < nb ? bidx[b] : -1, l16);
+      const float fs = folded_score16(P, qfold, cbt_row, cw, b < nb ? bidx[b] : -1, l16);
       if (l16 == 0 && b < nb) bscore[b] = fs;
     }
-    __syncthreads();
+    if (in_lds) lds_barrier(); else __syncthreads();
     // The need-th largest folded score of the band (ranks made unique by position).
     for (int b = tid; b < nb; b += NT) {
       const double sb = bscore[b];
@@ -962,8 +1034,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(SelectParams P) {
       }
       if (rank == need - 1) s_dbl[0] = sb;
     }
-    if (tid == 0) s_int[3] = 0;
-    __syncthreads();
+    lds_barrier();
     const double hi2 = s_dbl[0] + 2.0 * E_f, lo2 = s_dbl[0] - 2.0 * E_f;
     // The band's new list: in LDS with the first, or in the row's logits (no longer needed).
     int32_t* band2 = in_lds ? band2_idx_s
@@ -976,65 +1047,85 @@ __global__ __launch_bounds__(NT) void topk_kernel(SelectParams P) {
         atomicOr(&sel_mask[j >> 5], 1u << (j & 31));
         ++n_in2_local;
       } else if (sb >= lo2) {
-        band2[atomicAdd(&s_int[3], 1)] = j;
+        band2[atomicAdd(&s_int[6], 1)] = j;
       }
     }
-    need -= block_sum<NT>(n_in2_local, s_wave);
-    nb = s_int[3];
+    need -= block_sum<NT>(n_in2_local, s_wave);  // its barriers also publish band2
+    nb = s_int[6];
     band = band2;
   }
 
   // ---- re-score the band in float64, canonical order (16 lanes per entry)
   for (int b0 = 0; b0 < nb; b0 += groups) {
     const int b = b0 + grp;
-    const double s = canonical_score16(P, qrow, r, b < nb ? band[b] : -1, l16);
+    const double s = canonical_score16(P, qrow, cbt_row, cw, b < nb ? band[b] : -1, l16);
     if (l16 == 0 && b < nb) bscore[b] = s;
   }
-  __syncthreads();
+  if (in_lds) lds_barrier(); else __syncthreads();
 
-  // ---- rank the band: keep its `need` best by (score desc, block asc)
-  for (int b = tid; b < nb; b += NT) {
-    const double sb = bscore[b];
-    const int jbb = band[b];
+  // ---- rank the band: keep its `need` best by (score desc, block asc).  A 16-lane group per
+  // entry, each lane comparing against every 16th entry, the counts summed on DPP.
+  for (int b0 = 0; b0 < nb; b0 += groups) {
+    const int b = b0 + grp;
+    const bool live = b < nb;
+    const double sb = live ? bscore[b] : 0.0;
+    const int jbb = live ? band[b] : 0;
     int rank = 0;
-    for (int b2 = 0; b2 < nb; ++b2) {
-      const double s2 = bscore[b2];
-      rank += (s2 > sb) || (s2 == sb && band[b2] < jbb);
+    if (live) {
+      for (int b2 = l16; b2 < nb; b2 += 16) {
+        const double s2 = bscore[b2];
+        rank += (s2 > sb) || (s2 == sb && band[b2] < jbb);
+      }
     }
-    if (rank < need) atomicOr(&sel_mask[jbb >> 5], 1u << (jbb & 31));
+    rank += __builtin_amdgcn_update_dpp(0, rank, 0x108, 0xF, 0xF, false);  // row_shl:8
+    rank += __builtin_amdgcn_update_dpp(0, rank, 0x104, 0xF, 0xF, false);  // row_shl:4
+    rank += __builtin_amdgcn_update_dpp(0, rank, 0x102, 0xF, 0xF, false);  // row_shl:2
+    rank += __builtin_amdgcn_update_dpp(0, rank, 0x101, 0xF, 0xF, false);  // row_shl:1
+    if (live && l16 == 0 && rank < need) atomicOr(&sel_mask[jbb >> 5], 1u << (jbb & 31));
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- stable compaction in block order (one workgroup-wide scan) and expansion into tokens
-  uint32_t selbits = 0;
-  int cnt = 0;
-#pragma unroll
-  for (int i = 0; i < E; ++i) {
-    const int j = jb + i;
-    const bool sel = (j < vis) && ((double)sc[i] > hi || ((sel_mask[j >> 5] >> (j & 31)) & 1u));
-    selbits |= (sel ? 1u : 0u) << i;
-    cnt += sel;
-  }
+  const uint32_t emask = E == 32 ? 0xFFFFFFFFu : ((1u << E) - 1u);
+  const uint32_t selbits =
+      keepbits | (jb < vis ? (sel_mask[jb >> 5] >> (jb & 31)) & emask : 0u);
+  const int cnt = __builtin_popcount(selbits);
   const int incl = wave_incl_scan(cnt);
   if (lane == 63) s_wave[w] = incl;
-  __syncthreads();
+  lds_barrier();
   int pos = incl - cnt, total = 0;
-  for (int i = 0; i < NT / 64; ++i) {
+  for (int i = 0; i < kWaves; ++i) {
     pos += i < w ? s_wave[i] : 0;
     total += s_wave[i];
   }
-#pragma unroll
-  for (int i = 0; i < E; ++i) {
-    if ((selbits >> i) & 1u) {
-      const int j = jb + i;
-      if (pos < kb)
+  const int sel = min(total, kb), count = sel * P.c + tail;
+  // The selected blocks in order go to LDS (the band's score array is free now), and the row
+  // is written with coalesced stores; a list too long for it is expanded in place.
+  constexpr int kListCap = kBandCap * 2;  // int32 entries in band_score_s
+  int32_t* list = reinterpret_cast<int32_t*>(band_score_s);
+  const bool list_in_lds = kb <= kListCap;
+  for (uint32_t bits = selbits; bits; bits &= bits - 1, ++pos) {
+    const int j = jb + __builtin_ctz(bits);
+    if (pos < kb) {
+      if (list_in_lds) {
+        list[pos] = j;
+      } else {
         for (int m = 0; m < P.c; ++m) out[pos * P.c + m] = j * P.c + m;
-      ++pos;
+      }
     }
   }
-  const int sel = min(total, kb), count = sel * P.c + tail;
-  for (int col = sel * P.c + tid; col <= W; col += NT)
-    out[col] = col < count ? vis * P.c + (col - sel * P.c) : (col < W ? -1 : count);
+  if (list_in_lds) {
+    lds_barrier();
+    for (int col = tid; col <= W; col += NT) {
+      const int blk = col / P.c;
+      out[col] = col < sel * P.c ? list[blk] * P.c + (col - blk * P.c)
+                                 : (col < count ? vis * P.c + (col - sel * P.c)
+                                                : (col < W ? -1 : count));
+    }
+  } else {
+    for (int col = sel * P.c + tid; col <= W; col += NT)
+      out[col] = col < count ? vis * P.c + (col - sel * P.c) : (col < W ? -1 : count);
+  }
 }
 
 template <int NT, int E>
