@@ -882,8 +882,12 @@ __global__ __launch_bounds__(NT) void topk_kernel(SelectParams P) {
     const int c = tid + k * NT;
     cbt_v[k] = (cbt_in_lds && c < cw) ? P.cbt[(int64_t)r * P.cbt_stride + c] : -1;
   }
+  uint32_t key[E];  // order-preserving keys of the fast scores
 #pragma unroll
-  for (int i = 0; i < E; ++i) sc[i] = jb + i < vis ? sc[i] : -__builtin_inff();
+  for (int i = 0; i < E; ++i) {
+    sc[i] = jb + i < vis ? sc[i] : -__builtin_inff();
+    key[i] = fkey(sc[i]);
+  }
   double qa = 0.0;
 #pragma unroll
   for (int k = 0; k < kQPer; ++k) {
@@ -908,7 +912,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(SelectParams P) {
     int* h = hist[pass];
 #pragma unroll
     for (int i = 0; i < E; ++i) {
-      const uint32_t u = fkey(sc[i]);
+      const uint32_t u = key[i];
       if ((u & pmask) == prefix) atomicAdd(&h[(u >> shift) & (kRadixBins - 1)], 1);
     }
     if (pass == 1) {  // the error-bound inputs, reduced over the workgroup below
@@ -1116,9 +1120,12 @@ __global__ __launch_bounds__(NT) void topk_kernel(SelectParams P) {
   }
   if (list_in_lds) {
     lds_barrier();
+    // col / c through a float reciprocal, corrected to the exact quotient (col < 2^24).
+    const float rc = 1.0f / (float)P.c;
     for (int col = tid; col <= W; col += NT) {
-      const int blk = col / P.c;
-      out[col] = col < sel * P.c ? list[blk] * P.c + (col - blk * P.c)
+      int blk = (int)((float)col * rc), m = col - blk * P.c;
+      if (m < 0) { --blk; m += P.c; } else if (m >= P.c) { ++blk; m -= P.c; }
+      out[col] = col < sel * P.c ? list[blk] * P.c + m
                                  : (col < count ? vis * P.c + (col - sel * P.c)
                                                 : (col < W ? -1 : count));
     }
