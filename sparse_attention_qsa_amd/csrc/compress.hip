@@ -64,24 +64,46 @@ __device__ __forceinline__ void rmsnorm_pair(float x0f, float x1f, uint32_t wpai
   y1 = bf16_to_f32(f64_to_bf16((x1 * inv) * (1.0 + w1)));
 }
 
-// NeoX rotation of dims 0..63 (pairs (i, i+32)) at per-frequency positions; dims 64..127 pass
-// through.  `posf(f)` gives the (clamped) position of frequency f.
+// cos / sin of the two rotary frequencies of lane l (f0 = 2l mod 32 and f0 + 1), at the
+// (clamped) positions posf(f).  Every lane loads (lanes >= 32 duplicate lanes - 32), so the
+// loads carry no branch and go out as soon as the positions are known.
+struct RopeCS {
+  double c0, s0, c1, s1;
+};
 template <typename PosFn>
-__device__ __forceinline__ void rope_pair(const CompressParams& P, int lane, float& y0,
-                                          float& y1, PosFn posf) {
-  const float p0 = __shfl_xor(y0, 16, kWave);  // partner dims: lane l <-> lane l ^ 16
+__device__ __forceinline__ RopeCS rope_load(const CompressParams& P, int lane, PosFn posf) {
+  const int f0 = (2 * lane) & 31;
+  const int64_t q0 = posf(f0), q1 = posf(f0 + 1);
+  RopeCS cs;
+  cs.c0 = P.cos_sin[q0 * 64 + f0];
+  cs.s0 = P.cos_sin[q0 * 64 + 32 + f0];
+  cs.c1 = P.cos_sin[q1 * 64 + f0 + 1];
+  cs.s1 = P.cos_sin[q1 * 64 + 32 + f0 + 1];
+  return cs;
+}
+
+// NeoX rotation of dims 0..63 (pairs (i, i+32)); dims 64..127 pass through.  Lane l holds dims
+// 2l, 2l+1; its partners are in lane l ^ 16.
+__device__ __forceinline__ void rope_apply(int lane, float& y0, float& y1, const RopeCS& cs) {
+  const float p0 = __shfl_xor(y0, 16, kWave);
   const float p1 = __shfl_xor(y1, 16, kWave);
   if (lane < 32) {
-    const int f0 = (2 * lane) & 31;
-    const int64_t q0 = posf(f0), q1 = posf(f0 + 1);
-    const double c0 = P.cos_sin[q0 * 64 + f0], s0 = P.cos_sin[q0 * 64 + 32 + f0];
-    const double c1 = P.cos_sin[q1 * 64 + f0 + 1], s1 = P.cos_sin[q1 * 64 + 32 + f0 + 1];
     const double sgn = lane < 16 ? -1.0 : 1.0;  // first half: a*cos - b*sin; second: b*cos + a*sin
-    const double r0 = (double)y0 * c0 + sgn * ((double)p0 * s0);
-    const double r1 = (double)y1 * c1 + sgn * ((double)p1 * s1);
+    const double r0 = (double)y0 * cs.c0 + sgn * ((double)p0 * cs.s0);
+    const double r1 = (double)y1 * cs.c1 + sgn * ((double)p1 * cs.s1);
     y0 = bf16_to_f32(f64_to_bf16(r0));
     y1 = bf16_to_f32(f64_to_bf16(r1));
   }
+}
+
+// Positions of a token for the rotation: its three MRoPE axes, or its single position.
+struct TokPos {
+  int64_t t, h, w;
+};
+__device__ __forceinline__ int64_t axis_pos(const CompressParams& P, const TokPos& tp, int f) {
+  if (!P.mrope) return clamp_pos(tp.t, P.max_pos);
+  const int ax = mrope_axis(f, P.sec_h, P.sec_w);
+  return clamp_pos(ax == 0 ? tp.t : (ax == 1 ? tp.h : tp.w), P.max_pos);
 }
 
 __device__ __forceinline__ void store_index_pair(const CompressParams& P, void* base,
@@ -105,85 +127,124 @@ __device__ __forceinline__ void ring_store_row(const CompressParams& P, int row,
   if (P.mrope && lane < 3) P.ring_pos[slot * 3 + lane] = P.pos[(int64_t)row * 3 + lane];
 }
 
+// The request owning `row`, found by the whole wave: lane i tests request base + i, loading its
+// row interval, length and ring page in the same round trip; the owner's values are broadcast.
+struct ReqInfo {
+  int r, q0, n, L, rp;
+};
+__device__ __forceinline__ ReqInfo wave_find_request(const CompressParams& P, int row,
+                                                     int lane) {
+  ReqInfo ri{-1, 0, 0, 0, -1};
+  for (int base = 0; base < P.R; base += kWave) {
+    const int i = min(base + lane, P.R - 1);
+    const int a = P.qsl[i], b = P.qsl[i + 1], Li = P.seq_lens[i], rpi = P.ring_page[i];
+    const uint64_t m = __ballot(base + lane < P.R && a <= row && row < b);
+    if (m) {
+      const int src = (int)__builtin_ctzll(m);
+      ri.r = base + src;
+      ri.q0 = __builtin_amdgcn_readlane(a, src);
+      ri.n = __builtin_amdgcn_readlane(b, src) - ri.q0;
+      ri.L = __builtin_amdgcn_readlane(Li, src);
+      ri.rp = __builtin_amdgcn_readlane(rpi, src);
+      break;
+    }
+  }
+  return ri;
+}
+
 // Waves [0, T*Hi): indexer Q vectors.  Waves [T*Hi, T*Hi + T): the group (if any) completed by
-// row (wave - T*Hi), and -- when fuse_ring -- that row's ring write.
+// row (wave - T*Hi), and -- when fuse_ring -- that row's ring write.  Each wave issues every
+// load its result needs as early as its addresses are known: the rotation's cos / sin go out
+// with (or right after) the positions and land while the norm is computed.
 __global__ __launch_bounds__(256) void prep_compress_kernel(CompressParams P) {
-  __shared__ int32_t qsl_s[kQslCap];
   const int lane = threadIdx.x & 63;
   const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const int64_t nq = (int64_t)P.T * P.Hi;
-  // Blocks holding compress waves stage the row offsets for the request lookups (block-uniform).
-  const int32_t* qsl = P.qsl;
-  if ((int64_t)(blockIdx.x + 1) * (blockDim.x >> 6) > nq) qsl = stage_qsl(P.qsl, P.R, qsl_s);
   if (wave < nq) {
     const int row = (int)(wave / P.Hi), h = (int)(wave % P.Hi);
     const uint32_t u = P.q_proj[(int64_t)row * P.q_rs + h * 64 + lane];
-    float y0, y1;
-    rmsnorm_pair(bf16lo(u), bf16hi(u), reinterpret_cast<const uint32_t*>(P.qw)[lane], P.eps,
-                 y0, y1);
+    const uint32_t wpair = reinterpret_cast<const uint32_t*>(P.qw)[lane];
+    TokPos tp;
     if (P.mrope) {
-      rope_pair(P, lane, y0, y1, [&](int f) {
-        return clamp_pos(P.pos[(int64_t)row * 3 + mrope_axis(f, P.sec_h, P.sec_w)], P.max_pos);
-      });
+      tp = {P.pos[(int64_t)row * 3], P.pos[(int64_t)row * 3 + 1], P.pos[(int64_t)row * 3 + 2]};
     } else {
-      const int64_t q = clamp_pos(P.pos[row], P.max_pos);
-      rope_pair(P, lane, y0, y1, [&](int) { return q; });
+      tp.t = tp.h = tp.w = P.pos[row];
     }
+    const RopeCS cs = rope_load(P, lane, [&](int f) { return axis_pos(P, tp, f); });
+    float y0, y1;
+    rmsnorm_pair(bf16lo(u), bf16hi(u), wpair, P.eps, y0, y1);
+    rope_apply(lane, y0, y1, cs);
     store_index_pair(P, P.q_idx, wave, lane, y0, y1);
     return;
   }
   const int64_t row64 = wave - nq;
   if (row64 >= P.T) return;
   const int row = (int)row64;
-  const int r = find_request(qsl, P.R, row);
-  if (r < 0) return;
-  const int q0 = qsl[r], n = qsl[r + 1] - q0, L = P.seq_lens[r];
-  const int start = L - n;
+  const ReqInfo ri = wave_find_request(P, row, lane);
+  if (ri.r < 0) return;
+  const int r = ri.r, q0 = ri.q0, L = ri.L, rp = ri.rp;
+  const int start = L - ri.n;
   if (start < 0) return;
   const int p = start + (row - q0);
-  const int rp = P.ring_page[r];
   const bool ring_ok = rp >= 0 && rp < P.ring_pages;
 
   if ((p + 1) % P.c == 0) {
     const int g = (p + 1) / P.c - 1;
     const int t0 = g * P.c;
-    double a0 = 0.0, a1 = 0.0;
-    for (int m = 0; m < P.c; ++m) {
-      const int t = t0 + m;
-      uint32_t u = 0;
-      if (t >= start) {
-        u = P.k_proj[(int64_t)(q0 + t - start) * P.k_rs + lane];
-      } else if (ring_ok) {
-        u = P.ring[((int64_t)rp * P.S + (t % P.S)) * 64 + lane];
-      }
-      const double v0 = bf16lo(u), v1 = bf16hi(u);
-      if (m == 0) { a0 = v0; a1 = v1; } else { a0 = a0 + v0; a1 = a1 + v1; }
-    }
-    const float m0 = bf16_to_f32(f64_to_bf16(a0 / (double)P.c));
-    const float m1 = bf16_to_f32(f64_to_bf16(a1 / (double)P.c));
-    float y0, y1;
-    rmsnorm_pair(m0, m1, reinterpret_cast<const uint32_t*>(P.kw)[lane], P.eps, y0, y1);
+    // Everything the group needs, in one round trip: its keys (this step's rows or the ring),
+    // the block-table entry of its compressed row, and its first token's position (1-D: the
+    // token index itself, so the cos / sin loads go out at once).
+    const int col = g / P.Pc;
+    const int page = col < P.cbt_width ? P.cbt[(int64_t)r * P.cbt_stride + col] : -1;
+    TokPos tp;
     if (P.mrope) {
       const bool in_step = t0 >= start;
       const int64_t base = in_step ? (int64_t)(q0 + t0 - start) * 3
-                                   : ((int64_t)rp * P.S + (t0 % P.S)) * 3;
+                                   : ((int64_t)(ring_ok ? rp : 0) * P.S + (t0 % P.S)) * 3;
       const int64_t* src = in_step ? P.pos : P.ring_pos;
       const bool ok = in_step || ring_ok;
-      rope_pair(P, lane, y0, y1, [&](int f) {
-        return ok ? clamp_pos(src[base + mrope_axis(f, P.sec_h, P.sec_w)], P.max_pos)
-                  : (int64_t)0;
-      });
+      tp = {ok ? src[base] : 0, ok ? src[base + 1] : 0, ok ? src[base + 2] : 0};
     } else {
-      const int64_t q = clamp_pos(t0, P.max_pos);
-      rope_pair(P, lane, y0, y1, [&](int) { return q; });
+      tp.t = tp.h = tp.w = t0;
     }
-    const int col = g / P.Pc;
-    if (col < P.cbt_width) {
-      const int page = P.cbt[(int64_t)r * P.cbt_stride + col];
-      if (page >= 0 && page < P.c_pages) {
-        store_index_pair(P, P.ckv, (int64_t)page * P.Pc + (g % P.Pc), lane, y0, y1);
+    const RopeCS cs = rope_load(P, lane, [&](int f) { return axis_pos(P, tp, f); });
+    double a0 = 0.0, a1 = 0.0;
+    for (int m0 = 0; m0 < P.c; m0 += 8) {
+      uint32_t uu[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int t = t0 + m0 + k;
+        uint32_t v = 0;
+        if (m0 + k < P.c) {
+          if (t >= start) {
+            v = P.k_proj[(int64_t)(q0 + t - start) * P.k_rs + lane];
+          } else if (ring_ok) {
+            v = P.ring[((int64_t)rp * P.S + (t % P.S)) * 64 + lane];
+          }
+        }
+        uu[k] = v;
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (m0 + k < P.c) {
+          const double v0 = bf16lo(uu[k]), v1 = bf16hi(uu[k]);
+          if (m0 + k == 0) {
+            a0 = v0;
+            a1 = v1;
+          } else {
+            a0 = a0 + v0;
+            a1 = a1 + v1;
+          }
+        }
       }
     }
+    const float m0f = bf16_to_f32(f64_to_bf16(a0 / (double)P.c));
+    const float m1f = bf16_to_f32(f64_to_bf16(a1 / (double)P.c));
+    float y0, y1;
+    rmsnorm_pair(m0f, m1f, reinterpret_cast<const uint32_t*>(P.kw)[lane], P.eps, y0, y1);
+    rope_apply(lane, y0, y1, cs);
+    if (page >= 0 && page < P.c_pages)
+      store_index_pair(P, P.ckv, (int64_t)page * P.Pc + (g % P.Pc), lane, y0, y1);
   }
   if (P.fuse_ring) ring_store_row(P, row, r, p, L, lane);
 }
