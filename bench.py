@@ -93,7 +93,8 @@ def algorithmic_bytes(wl, packed):
         for row in sel:
             toks.update(row[:row[W]].tolist())
         kv_tokens += len(toks)
-    b_gqa = (kv_tokens * Hkv * 512                          # K and V rows of selected tokens
+    kv_row = 256 if getattr(wl, "kv_dtype", "bf16") == "fp8" else 512   # K + V bytes
+    b_gqa = (kv_tokens * Hkv * kv_row                       # K and V rows of selected tokens
              + T * Hq * 128 * 2 * 3                         # q, gate read; out written
              + T * (W + 1) * 4)                             # packed read
     return {"qsa_compress": b_compress, "qsa_index_logits_topk": b_logits,
@@ -295,7 +296,8 @@ def main():
                    "index_heads": wl0.index_heads, "compress_ratio": wl0.compress_ratio,
                    "budget": wl0.budget, "index_dtype": wl0.index_dtype,
                    "q_heads": wl0.q_heads, "kv_heads": wl0.kv_heads, "head_dim": 128,
-                   "page_size": 16, "input_copies_rotated": len(steps),
+                   "page_size": 16, "kv_dtype": getattr(wl0, "kv_dtype", "bf16"),
+                   "input_copies_rotated": len(steps),
                    "gqa_splits": steps[0].num_splits},
         "hbm_gbps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
         "hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

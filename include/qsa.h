@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 1
+#define QSA_ABI_VERSION 2
 
 typedef enum qsa_status {
   QSA_OK = 0,
@@ -196,6 +196,10 @@ qsa_status qsa_index_logits_topk(const qsa_topk_args* args, void* workspace,
  *     kv_cache + pg*kv_page_stride + h*kv_head_stride + slot*kv_token_stride
  * and holds K in its first head_dim values and V in the next head_dim (the pages' kv_cache
  * [pages, Hkv, P, 2*head_dim], split at head_size after transpose(1, 2)).
+ * FP8 main KV (the FP8 KV reader patch page, e4m3 branch): with kv_dtype FP8_E4M3 the cache
+ * holds OCP e4m3fn codes (one byte per value, strides in bytes) and static per-tensor scales:
+ * K = code * k_scale and V = code * v_scale.  k_scale is applied to the scores and v_scale to
+ * the output, never to the cached values.
  * ------------------------------------------------------------------------------------------ */
 typedef struct qsa_gqa_args {
   int32_t num_tokens;               /* T                                                     */
@@ -206,8 +210,8 @@ typedef struct qsa_gqa_args {
   const uint16_t* q;                /* [T, Hq, 128] bf16                                     */
   int64_t q_row_stride;
   int64_t q_head_stride;            /* must be 128 (a row's heads contiguous)                */
-  const uint16_t* kv_cache;         /* bf16, layout above                                    */
-  int64_t kv_page_stride;           /* strides: multiples of 8 elements                      */
+  const void* kv_cache;             /* bf16 or e4m3fn (kv_dtype), layout above               */
+  int64_t kv_page_stride;           /* strides in elements; multiples of 16 bytes            */
   int64_t kv_head_stride;
   int64_t kv_token_stride;
   int32_t num_pages;
@@ -227,6 +231,9 @@ typedef struct qsa_gqa_args {
   uint16_t* out;                    /* OUT [T, Hq, 128] bf16, fully overwritten              */
   int64_t out_row_stride;
   int64_t out_head_stride;
+  qsa_dtype kv_dtype;               /* BF16 (0) or FP8_E4M3                                  */
+  float k_scale;                    /* FP8_E4M3: K = code * k_scale; 0 -> 1; ignored for bf16 */
+  float v_scale;                    /* FP8_E4M3: V = code * v_scale; 0 -> 1; ignored for bf16 */
 } qsa_gqa_args;
 
 /* Splits the call will use (after the automatic choice and clamping). */

@@ -389,7 +389,7 @@ def index_topk(query_start_loc, seq_lens, q_codes, ckv, c_block_table, compress_
 
 
 def sparse_gqa(q, kv_cache, block_table, token_to_req, packed, gate=None, scale=None,
-               rows=None):
+               rows=None, kv_dtype="bf16", k_scale=1.0, v_scale=1.0):
     """Sparse GQA over the selected tokens of each row, float64 -> [T, Hq, 128].
 
     [ops] qsa_sparse_paged_attention / [fp8kv] _qsa_sparse_paged_gqa_splitk_kernel: Q head
@@ -402,6 +402,9 @@ def sparse_gqa(q, kv_cache, block_table, token_to_req, packed, gate=None, scale=
 
     kv_cache: [pages, Hkv, P, 256] uint16, K in the first 128 values of a token's row and V in
     the last 128 ([qsa] Qwen4ExpQSAImpl.forward splits kv_cache.transpose(1, 2) at head_size).
+    With kv_dtype "fp8" it holds uint8 e4m3fn codes and static per-tensor scales: K = code *
+    k_scale, V = code * v_scale ([fp8kv], e4m3 branch: the kernel folds k_scale into the score
+    scale and v_scale into the epilogue, which is the same attention over these values).
     """
     q = bf16_bits_to_f64(q)
     T, Hq, D = q.shape
@@ -423,11 +426,16 @@ def sparse_gqa(q, kv_cache, block_table, token_to_req, packed, gate=None, scale=
         idx, page = idx[ok], page[ok]
         if len(idx) == 0:
             continue
-        rows_kv = bf16_bits_to_f64(kv_cache[page, :, idx % P, :])   # [n, Hkv, 256]
+        if kv_dtype == "fp8":
+            rows_kv = e4m3_bits_to_f64(kv_cache[page, :, idx % P, :])  # [n, Hkv, 256]
+            ks, vs = float(k_scale), float(v_scale)
+        else:
+            rows_kv = bf16_bits_to_f64(kv_cache[page, :, idx % P, :])
+            ks = vs = 1.0
         for hq in range(Hq):
             kvh = hq // G
-            k = rows_kv[:, kvh, :D]
-            v = rows_kv[:, kvh, D:]
+            k = rows_kv[:, kvh, :D] * ks
+            v = rows_kv[:, kvh, D:] * vs
             z = (k @ q[i, hq]) * scale
             wgt = np.exp(z - z.max())
             out[i, hq] = (wgt @ v) / wgt.sum()

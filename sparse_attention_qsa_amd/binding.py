@@ -74,6 +74,7 @@ class GqaArgs(C.Structure):
         ("gate", _P), ("gate_row_stride", _I64), ("gate_head_stride", _I64),
         ("scale", C.c_float), ("num_splits", _I32),
         ("out", _P), ("out_row_stride", _I64), ("out_head_stride", _I64),
+        ("kv_dtype", _I32), ("k_scale", C.c_float), ("v_scale", C.c_float),
     ]
 
 
@@ -254,10 +255,13 @@ def qsa_index_logits_topk(workspace=None, stream=None, **kw) -> None:
 
 
 def gqa_args(*, q, kv_cache, block_table, token_to_req, packed, out, gate=None, scale=0.0,
-             num_splits=0, num_requests=None, block_table_width=None) -> GqaArgs:
-    """kv_cache: [pages, Hkv, P, 2*head_dim] bf16 (K then V per token row)."""
+             num_splits=0, num_requests=None, block_table_width=None, k_scale=1.0,
+             v_scale=1.0) -> GqaArgs:
+    """kv_cache: [pages, Hkv, P, 2*head_dim] bf16 (K then V per token row), or uint8 e4m3fn
+    codes with K = code * k_scale and V = code * v_scale."""
     _need(q, torch.bfloat16, "q")
-    _need(kv_cache, torch.bfloat16, "kv_cache")
+    _need(kv_cache, torch.uint8 if kv_cache.dtype == torch.uint8 else torch.bfloat16,
+          "kv_cache")
     _need(block_table, torch.int32, "block_table")
     _need(token_to_req, torch.int32, "token_to_req")
     _need(packed, torch.int32, "packed")
@@ -295,6 +299,10 @@ def gqa_args(*, q, kv_cache, block_table, token_to_req, packed, out, gate=None, 
     a.out = _ptr(out)
     a.out_row_stride = out.stride(0)
     a.out_head_stride = out.stride(1)
+    if kv_cache.dtype == torch.uint8:
+        a.kv_dtype = 1
+        a.k_scale = float(k_scale)
+        a.v_scale = float(v_scale)
     return a
 
 

@@ -27,8 +27,9 @@ struct GqaParams {
   int T, R, Hq, Hkv, pages, P, bt_stride, bt_width, W, splits, tiles_per_split;
   const uint16_t* q;
   int64_t q_rs, q_hs;
-  const uint16_t* kv;
-  int64_t kv_ps, kv_hs, kv_ts;
+  const uint8_t* kv;
+  int64_t kv_ps, kv_hs, kv_ts;  // bytes
+  float v_scale;                // output scale: 1 for bf16, the V dequantization scale for fp8
   const int32_t* bt;
   const int32_t* t2r;
   const int32_t* packed;
@@ -65,11 +66,22 @@ __device__ __forceinline__ void lds_dma16(const void* g, void* lds) {
                                    (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
 }
 
-// K and V tiles in LDS: token t's 256-byte row at 256 t, its 16-byte chunk c in slot
-// c ^ (t & 15).  They are filled by LDS-direct loads: load i writes tokens 4i .. 4i+3, lane L
-// landing in token 4i + L/16, slot L%16.
+// K and V tiles in LDS: token t's row (256 bytes bf16, 128 bytes fp8) at t * row, its 16-byte
+// chunk c in slot c ^ (t & 15) (bf16) or c ^ (t & 7) (fp8).  They are filled by LDS-direct
+// loads of 1 KiB: bf16 load i writes tokens 4i .. 4i+3 (lane L: token 4i + L/16, slot L%16),
+// fp8 load i tokens 8i .. 8i+7 (lane L: token 8i + L/8, slot L%8).
 __device__ __forceinline__ uint32_t lds_u32(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// 8-byte LDS read the compiler does not see: it would otherwise guard it with a wait for every
+// LDS-direct load in flight (it cannot tell which ones write the bytes read).  The caller
+// waits (lgkmcnt) before using the result.
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x2_t lds_read_b64_async(uint32_t addr) {
+  u32x2_t v;
+  asm volatile("ds_read_b64 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+  return v;
 }
 
 // Grid (T, Hkv, splits), one wavefront per (row, KV head, split).  Both contractions run on
@@ -86,13 +98,19 @@ __device__ __forceinline__ uint32_t lds_u32(const void* p) {
 //     the 4 x 16 block their 16 eight-byte reads form.
 // K and V are gathered with LDS-direct 16-byte loads, 16 lanes per 256-byte row; the next
 // tile's K is in flight during the softmax and P.V, its V during Q.K and the softmax.
-template <int G>
+// With F8 the rows are e4m3 codes (128 bytes each): the fragments are read as bytes and
+// converted to bf16 (exactly: every e4m3 value is a bf16 value), V's through the transposing
+// byte read ds_read_b64_tr_b8, whose 16-lane groups give lane i byte i % 8 of the reads of
+// lanes i / 8 + 2r, r < 8.  The dequantization scales act on the scores and on the output.
+template <int G, bool F8>
 __global__ __launch_bounds__(64) void gqa_partial_kernel(GqaParams P) {
   static_assert(G <= 16, "the MFMA columns hold at most 16 heads");
+  constexpr int kRow = F8 ? 128 : 256;        // bytes of a token's K (or V) row
+  constexpr int kLoads = kTile * kRow / 1024;  // LDS-direct loads per tile and part
   const int row = blockIdx.x, kvh = blockIdx.y, split = blockIdx.z;
   const int lane = threadIdx.x, l16 = lane & 15, g4 = lane >> 4;
-  __shared__ __attribute__((aligned(16))) uint8_t kt[kTile * 256];
-  __shared__ __attribute__((aligned(16))) uint8_t vt[kTile * 256];
+  __shared__ __attribute__((aligned(16))) uint8_t kt[kTile * kRow];
+  __shared__ __attribute__((aligned(16))) uint8_t vt[kTile * kRow];
   // Resolved cache rows (16-byte offsets) of the chunk's tiles: token 4i + q of tile k at
   // offs[k * 32 + 8q + i], so that lane group q's 8 rows are contiguous; and validity masks.
   __shared__ __attribute__((aligned(16))) uint32_t offs[kChunkTiles * kTile];
@@ -137,16 +155,37 @@ __global__ __launch_bounds__(64) void gqa_partial_kernel(GqaParams P) {
     o[0] = x.x; o[1] = x.y; o[2] = x.z; o[3] = x.w;
     o[4] = y.x; o[5] = y.y; o[6] = y.z; o[7] = y.w;
   };
-  // One tile's K (part 0) or V (part 1) rows into LDS: 8 coalesced LDS-direct loads.
+  // One tile's K (part 0) or V (part 1) rows into LDS: kLoads coalesced LDS-direct loads.
   auto issue_rows = [&](int k, int part, uint8_t* dst) {
-    uint32_t o[8];
-    row_offsets(k, o);
+    if constexpr (F8) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int t = 4 * i + g4;
-      lds_dma16(kvb + (size_t)o[i] * 16 + 256 * part + 16 * (l16 ^ (t & 15)),
-                dst + 1024 * i);
+      for (int i = 0; i < kLoads; ++i) {
+        const int t = 8 * i + (lane >> 3);
+        const uint32_t o = offs[k * kTile + 8 * (t & 3) + (t >> 2)];
+        lds_dma16(kvb + (size_t)o * 16 + kRow * part + 16 * ((lane & 7) ^ (t & 7)),
+                  dst + 1024 * i);
+      }
+    } else {
+      uint32_t o[8];
+      row_offsets(k, o);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int t = 4 * i + g4;
+        lds_dma16(kvb + (size_t)o[i] * 16 + 256 * part + 16 * (l16 ^ (t & 15)),
+                  dst + 1024 * i);
+      }
     }
+  };
+  // Eight e4m3 codes (two words, code j in byte j % 4 of word j / 4) as bf16, exactly.
+  auto e4m3x8_to_bf16 = [](uint32_t w0, uint32_t w1) {
+    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(w0, false);
+    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(w0, true);
+    const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(w1, false);
+    const auto d = __builtin_amdgcn_cvt_pk_f32_fp8(w1, true);
+    bf16x8_t r;
+    r[0] = (__bf16)a[0]; r[1] = (__bf16)a[1]; r[2] = (__bf16)b[0]; r[3] = (__bf16)b[1];
+    r[4] = (__bf16)c[0]; r[5] = (__bf16)c[1]; r[6] = (__bf16)d[0]; r[7] = (__bf16)d[1];
+    return r;
   };
 
   for (int c0 = tile_lo; c0 < tile_end; c0 += kChunkTiles) {
@@ -181,7 +220,7 @@ __global__ __launch_bounds__(64) void gqa_partial_kernel(GqaParams P) {
       const int64_t off = valid ? ((int64_t)page[j] * P.kv_ps + (int64_t)kvh * P.kv_hs +
                                    (int64_t)slot * P.kv_ts) : 0;
       const int e = lane + 64 * j, k = e >> 5, t = e & 31;
-      offs[k * kTile + 8 * (t & 3) + (t >> 2)] = (uint32_t)(off >> 3);
+      offs[k * kTile + 8 * (t & 3) + (t >> 2)] = (uint32_t)(off >> 4);
       const uint64_t vm = __ballot(valid);
       if (lane == 0) {
         vms[2 * j] = (uint32_t)vm;
@@ -202,20 +241,43 @@ __global__ __launch_bounds__(64) void gqa_partial_kernel(GqaParams P) {
         asm volatile("" ::: "memory");  // V loads strictly after the K loads
         issue_rows(0, 1, vt);
       }
-      // The 8 V loads of this tile are the only memory loads issued after its K loads.
-      __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8): this tile's K rows have landed
+      // The kLoads V loads of this tile are the only memory loads issued after its K loads.
+      if constexpr (F8) __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4): K rows have landed
+      else __builtin_amdgcn_s_waitcnt(0x0F78);               // vmcnt(8)
       wave_lds_sync();
 
       // ---- Q.K on the matrix cores: token blocks b = 0, 1 of 16.
       f32x4_t sacc[2];
+      u32x2_t kw[2][4];  // fp8: the K fragments' codes, all read before the first is used
+      if constexpr (F8) {
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb) {
+          const int t = 16 * bb + l16;
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks)  // dims 32 ks + 8 g4 .. +7: chunk 2 ks + g4/2, half
+            kw[bb][ks] = lds_read_b64_async(
+                lds_u32(kt + t * 128 + 16 * ((2 * ks + (g4 >> 1)) ^ (t & 7)) + 8 * (g4 & 1)));
+        }
+        // The wait names every fragment, so nothing that reads them can move above it.
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(kw[0][0]), "+v"(kw[0][1]), "+v"(kw[0][2]), "+v"(kw[0][3]),
+                       "+v"(kw[1][0]), "+v"(kw[1][1]), "+v"(kw[1][2]), "+v"(kw[1][3])
+                     :
+                     : "memory");
+      }
 #pragma unroll
       for (int bb = 0; bb < 2; ++bb) {
         sacc[bb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
         const int t = 16 * bb + l16;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(
-              kt + t * 256 + 16 * ((4 * ks + g4) ^ (t & 15)));
+          bf16x8_t kf;
+          if constexpr (F8) {
+            kf = e4m3x8_to_bf16(kw[bb][ks][0], kw[bb][ks][1]);
+          } else {
+            kf = *reinterpret_cast<const bf16x8_t*>(
+                kt + t * 256 + 16 * ((4 * ks + g4) ^ (t & 15)));
+          }
           sacc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qfr[ks], sacc[bb], 0, 0, 0);
         }
       }
@@ -267,15 +329,20 @@ __global__ __launch_bounds__(64) void gqa_partial_kernel(GqaParams P) {
       }
 
       // This tile's V has landed (only the next tile's K loads may still be in flight).
-      if constexpr (more) __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8)
-      else __builtin_amdgcn_s_waitcnt(0x0F70);                 // vmcnt(0)
+      if constexpr (more) {
+        if constexpr (F8) __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+        else __builtin_amdgcn_s_waitcnt(0x0F78);               // vmcnt(8)
+      } else {
+        __builtin_amdgcn_s_waitcnt(0x0F70);                    // vmcnt(0)
+      }
       // A masked token's V row may hold anything (NaN-poisoned slots included): zero it.
       if (vmask != 0xFFFFFFFFu) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int t = 4 * i + g4;
+        for (int i = 0; i < kLoads; ++i) {
+          const int t = F8 ? 8 * i + (lane >> 3) : 4 * i + g4;
           if (!((vmask >> t) & 1u))
-            *reinterpret_cast<uint4*>(vt + t * 256 + 16 * l16) = make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<uint4*>(vt + t * kRow + 16 * (F8 ? (lane & 7) : l16)) =
+                make_uint4(0, 0, 0, 0);
         }
       }
       wave_lds_sync();
@@ -283,19 +350,36 @@ __global__ __launch_bounds__(64) void gqa_partial_kernel(GqaParams P) {
       // ---- P.V on the matrix cores: dim blocks db of 16.  Transposing reads: lane (g4, l16)
       // supplies the 8 bytes of token 4 g4 + l16/4 (then 16 + that), dims 16 db + 4 (l16 % 4)
       // .. +3, and receives dim 16 db + l16 of the group's 4 tokens.
-      const int tr_t0 = 4 * g4 + (l16 >> 2), tr_t1 = tr_t0 + 16, q4 = l16 & 3;
+      if constexpr (F8) {
+        // Lane (g4, l16) supplies the 8 bytes of token T(l16 / 2), dims 16 db + 8 (l16 & 1)
+        // .. +7, where T(j) is the k-slot j token of group g4 (4 g4 + j, then 16 + 4 g4 + j-4);
+        // it receives dim 16 db + l16 of the group's 8 tokens, in k-slot order.
+        const int jj = l16 >> 1;
+        const int tr = jj < 4 ? 4 * g4 + jj : 16 + 4 * g4 + (jj - 4);
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        const int c = 2 * db + (q4 >> 1), h8 = 8 * (q4 & 1);
-        const uint32_t a0 = lds_u32(vt + tr_t0 * 256 + 16 * (c ^ (tr_t0 & 15)) + h8);
-        const uint32_t a1 = lds_u32(vt + tr_t1 * 256 + 16 * (c ^ (tr_t1 & 15)) + h8);
-        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4_t*)(uintptr_t)a0);
-        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4_t*)(uintptr_t)a1);
-        const bf16x8_t vf = __builtin_bit_cast(
-            bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pfr, acc[db], 0, 0, 0);
+        for (int db = 0; db < 8; ++db) {
+          const uint32_t a = lds_u32(vt + tr * 128 + 16 * (db ^ (tr & 7)) + 8 * (l16 & 1));
+          typedef int i32x2_t __attribute__((ext_vector_type(2)));
+          const i32x2_t w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (__attribute__((address_space(3))) i32x2_t*)(uintptr_t)a);
+          const bf16x8_t vf = e4m3x8_to_bf16((uint32_t)w[0], (uint32_t)w[1]);
+          acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pfr, acc[db], 0, 0, 0);
+        }
+      } else {
+        const int tr_t0 = 4 * g4 + (l16 >> 2), tr_t1 = tr_t0 + 16, q4 = l16 & 3;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+          const int c = 2 * db + (q4 >> 1), h8 = 8 * (q4 & 1);
+          const uint32_t a0 = lds_u32(vt + tr_t0 * 256 + 16 * (c ^ (tr_t0 & 15)) + h8);
+          const uint32_t a1 = lds_u32(vt + tr_t1 * 256 + 16 * (c ^ (tr_t1 & 15)) + h8);
+          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4_t*)(uintptr_t)a0);
+          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4_t*)(uintptr_t)a1);
+          const bf16x8_t vf = __builtin_bit_cast(
+              bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pfr, acc[db], 0, 0, 0);
+        }
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // V reads done: the tile is free
       if constexpr (more) {
@@ -314,7 +398,7 @@ __global__ __launch_bounds__(64) void gqa_partial_kernel(GqaParams P) {
                      __shfl_xor(__shfl_xor(lsum, 16, kWave), 32, kWave);
   if (l16 >= G) return;
   const int hq = kvh * G + l16;
-  const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
+  const float inv = ltot > 0.0f ? P.v_scale / ltot : 0.0f;
   if (P.splits == 1) {
     // Gate and output rows are only 4-byte aligned: dword accesses.
     const uint32_t* gp = P.gate ? reinterpret_cast<const uint32_t*>(
@@ -395,8 +479,13 @@ __global__ __launch_bounds__(64) void gqa_merge_kernel(GqaParams P) {
 }
 
 template <int G>
-hipError_t launch_partial(const GqaParams& P, hipStream_t s) {
-  hipLaunchKernelGGL(gqa_partial_kernel<G>, dim3(P.T, P.Hkv, P.splits), dim3(64), 0, s, P);
+hipError_t launch_partial(const GqaParams& P, bool f8, hipStream_t s) {
+  if (f8)
+    hipLaunchKernelGGL((gqa_partial_kernel<G, true>), dim3(P.T, P.Hkv, P.splits), dim3(64), 0,
+                       s, P);
+  else
+    hipLaunchKernelGGL((gqa_partial_kernel<G, false>), dim3(P.T, P.Hkv, P.splits), dim3(64), 0,
+                       s, P);
   return hipGetLastError();
 }
 
@@ -441,10 +530,12 @@ hipError_t launch_gqa(const qsa_gqa_args& a, const GqaPlan& plan, char* ws, hipS
   P.q = a.q;
   P.q_rs = a.q_row_stride;
   P.q_hs = a.q_head_stride;
-  P.kv = a.kv_cache;
-  P.kv_ps = a.kv_page_stride;
-  P.kv_hs = a.kv_head_stride;
-  P.kv_ts = a.kv_token_stride;
+  const bool f8 = a.kv_dtype == QSA_DTYPE_FP8_E4M3;
+  const int64_t elt = f8 ? 1 : 2;
+  P.kv = reinterpret_cast<const uint8_t*>(a.kv_cache);
+  P.kv_ps = a.kv_page_stride * elt;
+  P.kv_hs = a.kv_head_stride * elt;
+  P.kv_ts = a.kv_token_stride * elt;
   P.bt = a.block_table;
   P.t2r = a.token_to_req;
   P.packed = a.packed;
@@ -453,7 +544,10 @@ hipError_t launch_gqa(const qsa_gqa_args& a, const GqaPlan& plan, char* ws, hipS
   P.g_rs = a.gate_row_stride;
   P.g_hs = a.gate_head_stride;
   const float scale = a.scale > 0.0f ? a.scale : 1.0f / sqrtf((float)a.head_dim);
-  P.scale_log2 = scale * 1.4426950408889634f;
+  // fp8: K = code * k_scale enters every score once, V = code * v_scale the output once.
+  const float k_scale = f8 && a.k_scale > 0.0f ? a.k_scale : 1.0f;
+  P.scale_log2 = scale * k_scale * 1.4426950408889634f;
+  P.v_scale = f8 && a.v_scale > 0.0f ? a.v_scale : 1.0f;
   P.out = a.out;
   P.o_rs = a.out_row_stride;
   P.o_hs = a.out_head_stride;
@@ -464,11 +558,11 @@ hipError_t launch_gqa(const qsa_gqa_args& a, const GqaPlan& plan, char* ws, hipS
   }
   hipError_t e;
   switch (a.num_q_heads / a.num_kv_heads) {
-    case 1: e = launch_partial<1>(P, s); break;
-    case 2: e = launch_partial<2>(P, s); break;
-    case 4: e = launch_partial<4>(P, s); break;
-    case 8: e = launch_partial<8>(P, s); break;
-    case 16: e = launch_partial<16>(P, s); break;
+    case 1: e = launch_partial<1>(P, f8, s); break;
+    case 2: e = launch_partial<2>(P, f8, s); break;
+    case 4: e = launch_partial<4>(P, f8, s); break;
+    case 8: e = launch_partial<8>(P, f8, s); break;
+    case 16: e = launch_partial<16>(P, f8, s); break;
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess || plan.splits == 1) return e;

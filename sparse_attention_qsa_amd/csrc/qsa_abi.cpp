@@ -102,18 +102,24 @@ qsa_status validate_gqa(const qsa_gqa_args* a) {
                   a->block_table_stride >= a->block_table_width,
               kInval);
   QSA_REQUIRE(a->packed_width >= 1 && a->packed_row_stride >= (int64_t)a->packed_width + 1, kInval);
-  QSA_REQUIRE(a->kv_page_stride % 8 == 0 && a->kv_head_stride % 8 == 0 &&
-                  a->kv_token_stride % 8 == 0 && a->kv_token_stride >= 2 * kHeadDim &&
+  QSA_REQUIRE(a->kv_dtype == QSA_DTYPE_BF16 || a->kv_dtype == QSA_DTYPE_FP8_E4M3, kNotSup);
+  QSA_REQUIRE(a->k_scale >= 0.0f && a->v_scale >= 0.0f && a->k_scale < 3.0e38f &&
+                  a->v_scale < 3.0e38f,
+              kInval);
+  // Rows are gathered as 16-byte pieces: every stride is a multiple of 16 bytes.
+  const int64_t elt = a->kv_dtype == QSA_DTYPE_FP8_E4M3 ? 1 : 2;
+  QSA_REQUIRE((a->kv_page_stride * elt) % 16 == 0 && (a->kv_head_stride * elt) % 16 == 0 &&
+                  (a->kv_token_stride * elt) % 16 == 0 && a->kv_token_stride >= 2 * kHeadDim &&
                   a->kv_head_stride >= 0 && a->kv_page_stride >= 0,
               kInval);
-  const int64_t last = (int64_t)(a->num_pages - 1) * a->kv_page_stride +
-                       (int64_t)(a->num_kv_heads - 1) * a->kv_head_stride +
-                       (int64_t)(a->page_size - 1) * a->kv_token_stride + 2 * kHeadDim;
-  QSA_REQUIRE(last < (int64_t(1) << 35), kNotSup);  // 16-byte offsets fit 32 bits
+  const int64_t last = ((int64_t)(a->num_pages - 1) * a->kv_page_stride +
+                        (int64_t)(a->num_kv_heads - 1) * a->kv_head_stride +
+                        (int64_t)(a->page_size - 1) * a->kv_token_stride + 2 * kHeadDim) * elt;
+  QSA_REQUIRE(last < (int64_t(1) << 36), kNotSup);  // 16-byte offsets fit 32 bits
   QSA_REQUIRE(a->q_row_stride % 2 == 0 &&
                   a->q_row_stride >= (int64_t)a->num_q_heads * a->q_head_stride,
               kInval);
-  // The kernels read a row's Q heads through the scalar cache at fixed offsets.
+  // A KV head's query heads are one matrix-core operand, read with 16-byte loads.
   QSA_REQUIRE(a->q_head_stride == kHeadDim, kNotSup);
   QSA_REQUIRE(a->out_row_stride % 2 == 0 && a->out_head_stride % 2 == 0 &&
                   a->out_head_stride >= kHeadDim,

@@ -38,7 +38,8 @@ class QsaStep:
         self.g_args = B.gqa_args(
             q=wl.q, kv_cache=wl.kv_cache, block_table=wl.block_table,
             token_to_req=wl.token_to_req, packed=self.packed, out=self.out,
-            gate=wl.gate if gate else None, num_splits=num_splits)
+            gate=wl.gate if gate else None, num_splits=num_splits,
+            k_scale=getattr(wl, "k_scale", 1.0), v_scale=getattr(wl, "v_scale", 1.0))
         L = B.lib()
         t_ws = int(L.qsa_index_logits_topk_workspace_size(C.byref(self.t_args)))
         # Size the attention workspace for the largest split count, so that a caller may

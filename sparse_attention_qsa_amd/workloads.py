@@ -16,6 +16,8 @@ The five workloads (sizes as the project's benchmark configurations state them):
   spec_verify_mrope   256 requests, lengths log-uniform in [1024, 131072], 4 verify rows
                       each, interleaved MRoPE positions [rows, 3] with section (12, 10, 10),
                       c = 8, budget 4096, fp8 indexer; fragmented page tables.
+  decode_32k_fp8kv    decode_32k with the main KV cache in e4m3fn codes and static scales
+                      (k_scale 0.0167, v_scale 0.0161).
 
 Recipe: activations N(0, 1) float32 rounded to bf16; norm weights N(0, 0.1^2) -> bf16; the
 rotary table cos/sin(pos * 10000^(-2i/64)) in float64 rounded to float32; the indexer
@@ -57,9 +59,16 @@ CONFIGS = {
                               index_heads=8, compress_ratio=8, budget=4096,
                               index_dtype="fp8", q_heads=16, kv_heads=2,
                               mrope_section=(12, 10, 10), pool_factor=1.25),
+    # decode_32k with an fp8 e4m3 main KV cache and static per-tensor scales (the FP8 KV
+    # reader patch page); the scales are arbitrary non-powers of two that keep N(0, 1) values
+    # far inside the e4m3 range.
+    "decode_32k_fp8kv": dict(num_requests=64, lengths=("fixed", 32768), rows=1, index_heads=8,
+                             compress_ratio=4, budget=2048, index_dtype="bf16", q_heads=16,
+                             kv_heads=2, mrope_section=None, pool_factor=1.0,
+                             kv_dtype="fp8", k_scale=0.0167, v_scale=0.0161),
 }
 
-CONFIG_SEEDS = {"tiny_decode": 1001, "decode_32k": 1002, "fp8_decode": 1003,
+CONFIG_SEEDS = {"decode_32k_fp8kv": 1006, "tiny_decode": 1001, "decode_32k": 1002, "fp8_decode": 1003,
                 "chunked_prefill": 1004, "spec_verify_mrope": 1005}
 
 
@@ -97,9 +106,12 @@ class Workload:
     ckv: torch.Tensor                  # [c_pages, Pc, 128] bf16 or uint8 (e4m3fn)
     c_block_table: torch.Tensor        # [R, cw] int32
     q: torch.Tensor                    # [T, Hq, 128] bf16
-    kv_cache: torch.Tensor             # [pages, Hkv, P, 256] bf16
+    kv_cache: torch.Tensor             # [pages, Hkv, P, 256] bf16, or uint8 e4m3fn codes
     block_table: torch.Tensor          # [R, bw] int32
     gate: torch.Tensor                 # [T, Hq, 128] bf16
+    kv_dtype: str = "bf16"             # "bf16" or "fp8" (K = code * k_scale, V = code * v_scale)
+    k_scale: float = 1.0
+    v_scale: float = 1.0
 
     @property
     def output_width(self) -> int:
@@ -253,6 +265,17 @@ def make_workload(name: str, device="cpu", seed: int | None = None, **overrides)
         if rem:
             used[pg[n_full], :rem] = True
     kv = torch.where(used.to(device)[:, None, :, None], kv, torch.full_like(kv, float("nan")))
+    kv_dtype = cfg.get("kv_dtype", "bf16")
+    k_scale = float(cfg.get("k_scale", 1.0))
+    v_scale = float(cfg.get("v_scale", 1.0))
+    if kv_dtype == "fp8":
+        # e4m3fn codes of value / scale (clamped inside the finite range); unused slots keep
+        # the NaN code 0x7F.
+        sc = torch.cat([torch.full((HEAD_DIM,), k_scale), torch.full((HEAD_DIM,), v_scale)])
+        x = kv.float() / sc.to(device)
+        x = torch.where(torch.isnan(x), x, x.clamp(-440.0, 440.0))
+        kv = x.to(torch.float8_e4m3fn).view(torch.uint8)
+        kv = torch.where(used.to(device)[:, None, :, None], kv, torch.full_like(kv, 0x7F))
 
     def dev(a, dtype=None):
         t = torch.from_numpy(np.ascontiguousarray(a))
@@ -275,4 +298,5 @@ def make_workload(name: str, device="cpu", seed: int | None = None, **overrides)
         c_block_table=dev(c_table), q=_normal_bf16((T, Hq, HEAD_DIM), device, seed, 8),
         kv_cache=kv, block_table=dev(table),
         gate=_normal_bf16((T, Hq, HEAD_DIM), device, seed, 9),
+        kv_dtype=kv_dtype, k_scale=k_scale, v_scale=v_scale,
     )

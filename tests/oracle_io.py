@@ -55,5 +55,8 @@ def oracle_step(wl, rows=None, with_attention=True) -> OracleStep:
     out = None
     if with_attention:
         out = oq.sparse_gqa(to_np(wl.q), to_np(wl.kv_cache), to_np(wl.block_table),
-                            to_np(wl.token_to_req), packed, gate=to_np(wl.gate), rows=rows)
+                            to_np(wl.token_to_req), packed, gate=to_np(wl.gate), rows=rows,
+                            kv_dtype=getattr(wl, "kv_dtype", "bf16"),
+                            k_scale=getattr(wl, "k_scale", 1.0),
+                            v_scale=getattr(wl, "v_scale", 1.0))
     return OracleStep(q_codes=q_codes, state_after=after, packed=packed, out=out)

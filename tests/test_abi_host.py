@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(B.EXPORTED)
-    assert lib.qsa_abi_version() == 1
+    assert lib.qsa_abi_version() == 2
     assert lib.qsa_status_string(3) == b"QSA_ERR_WORKSPACE_TOO_SMALL"
 
 
@@ -112,6 +112,14 @@ def test_invalid_calls_are_rejected_before_any_launch():
     assert lib.qsa_sparse_gqa(C.byref(_gqa(packed_row_stride=2051)), None, 0, None) == INVAL
     assert lib.qsa_sparse_gqa(C.byref(_gqa()), None, 0, None) == SMALL      # needs partials
     assert lib.qsa_sparse_gqa(C.byref(_gqa(num_tokens=0)), None, 0, None) == 0
+    # fp8 main KV: a known dtype, finite non-negative scales, 16-byte strides in bytes.
+    assert lib.qsa_sparse_gqa(C.byref(_gqa(kv_dtype=5)), None, 0, None) == NOTSUP
+    assert lib.qsa_sparse_gqa(C.byref(_gqa(kv_dtype=1, k_scale=-1.0)), None, 0, None) == INVAL
+    assert lib.qsa_sparse_gqa(C.byref(_gqa(kv_dtype=1, v_scale=float("nan"))), None, 0,
+                              None) == INVAL
+    assert lib.qsa_sparse_gqa(C.byref(_gqa(kv_dtype=1, kv_token_stride=264)), None, 0,
+                              None) == INVAL
+    assert lib.qsa_sparse_gqa(C.byref(_gqa(kv_dtype=1)), None, 0, None) == SMALL
     assert lib.qsa_index_logits_topk(C.byref(_topk(budget=2047)), None, 0, None) == INVAL
     assert lib.qsa_index_logits_topk(C.byref(_topk(compress_ratio=3)), None, 0, None) == NOTSUP
     assert lib.qsa_index_logits_topk(C.byref(_topk(index_dtype=7)), None, 0, None) == NOTSUP

@@ -75,7 +75,8 @@ def test_selection_is_exact_and_attention_within_tolerance(name):
     assert err <= TOL[wl.index_dtype]
 
 
-@pytest.mark.parametrize("name", ["tiny_decode", "decode_32k", "spec_verify_mrope"])
+@pytest.mark.parametrize("name", ["tiny_decode", "decode_32k", "spec_verify_mrope",
+                                  "decode_32k_fp8kv"])
 def test_attention_alone_on_oracle_indices_and_split_invariance(name):
     wl = workload(name)
     log(f"gqa parity {name}")
@@ -110,6 +111,42 @@ def test_full_size_decode_32k_on_sampled_rows():
     assert np.all(packed[:, W] == 2048)
     assert np.all(np.diff(packed[:, :2048], axis=1) > 0)
     assert np.all(packed[:, 2048:W] == -1)
+
+
+def test_full_size_decode_32k_fp8_kv_on_sampled_rows():
+    """The fp8 main-KV attention at the size bench.py times for it, in that launch
+    configuration, on sampled rows."""
+    wl = workload("decode_32k_fp8kv", num_requests=64, lengths=("fixed", 32768))
+    rows = [1, 30, 62]
+    log(f"full-size decode_32k_fp8kv, sampled rows {rows}")
+    ref = oracle_step(wl, rows=rows)
+    st = run_gpu(wl)
+    assert np.array_equal(to_np(st.packed)[rows], ref.packed[rows])
+    err = max_abs(gpu_out_f64(st)[rows], ref.out[rows])
+    log(f"  max-abs {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
+def test_fp8_kv_scales_act_on_scores_and_output():
+    """Doubling v_scale doubles the output; a k_scale change equals the same change of the
+    softmax scale (both within the float32 / bf16 rounding of the kernel)."""
+    wl = workload("decode_32k_fp8kv")
+    st = run_gpu(wl)
+    base = gpu_out_f64(st)
+    st.g_args.v_scale = 2.0 * wl.v_scale
+    st.gqa()
+    torch.cuda.synchronize()
+    assert max_abs(gpu_out_f64(st), 2.0 * base) <= 2 ** -7 * (np.abs(base).max() + 1.0)
+    st.g_args.v_scale = wl.v_scale
+    st.g_args.k_scale = 1.5 * wl.k_scale
+    st.gqa()
+    torch.cuda.synchronize()
+    a = gpu_out_f64(st)
+    st.g_args.k_scale = wl.k_scale
+    st.g_args.scale = 1.5 * 128 ** -0.5
+    st.gqa()
+    torch.cuda.synchronize()
+    assert max_abs(a, gpu_out_f64(st)) <= 2 ** -6
 
 
 # ----------------------------------------------------------------------------- edge cases

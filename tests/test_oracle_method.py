@@ -338,6 +338,33 @@ def test_sparse_gqa_gate_zero_halves_and_page_permutation_invariance():
     assert np.array_equal(out2, plain)
 
 
+def test_sparse_gqa_fp8_kv_matches_torch_sdpa_on_dequantized_values():
+    """[fp8kv], e4m3 branch: K = code * k_scale, V = code * v_scale.  Pinned against torch's
+    own float8_e4m3fn decoder and scaled_dot_product_attention (float64)."""
+    L, W, Hq, Hkv, P = 100, 120, 8, 2, 16
+    rng = np.random.default_rng(11)
+    pages_needed = (L + P - 1) // P
+    pages = pages_needed + 3
+    perm = rng.permutation(pages)[:pages_needed].astype(np.int32)
+    codes = rng.integers(0, 256, size=(pages, Hkv, P, 256)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x3C          # no NaN codes in the live cache
+    k_scale, v_scale = 0.0317, 0.0453
+    dec = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    K = np.stack([dec[perm[t // P], :, t % P, :128] for t in range(L)]) * k_scale
+    V = np.stack([dec[perm[t // P], :, t % P, 128:] for t in range(L)]) * v_scale
+    q = round_bf16(rng.standard_normal((2, Hq, 128)))
+    packed = np.full((2, W + 1), -1, np.int32)
+    packed[0, :L] = np.arange(L)
+    packed[0, W] = L
+    sel = np.array([2, 30, 31, 77])
+    packed[1, :4] = sel
+    packed[1, W] = 4
+    out = oq.sparse_gqa(f64_to_bf16_bits(q), codes, perm[None, :], np.zeros(2, np.int32), packed,
+                        kv_dtype="fp8", k_scale=k_scale, v_scale=v_scale)
+    assert np.abs(out[0] - _dense_reference(q[0], K, V, 128 ** -0.5)).max() < 1e-12
+    assert np.abs(out[1] - _dense_reference(q[1], K[sel], V[sel], 128 ** -0.5)).max() < 1e-12
+
+
 # ----------------------------------------------------------------------------- end to end
 
 
