@@ -734,8 +734,22 @@ __device__ float folded_score16(const SelectParams& P, const float* qfold,
   return x;
 }
 
-// Band entries kept in LDS; larger bands (adversarial ties) use the workspace.
-constexpr int kBandCap = 1024;
+// Top-k kernel configurations: NT threads holding E scores each; the threshold's radix select
+// takes PASSES passes of RB-bit digits over the top RB*PASSES bits of the order-preserving key
+// (the rest stay unresolved: the threshold lies in one bin's value interval, which the band
+// absorbs); bands of up to BAND entries and block-table rows of up to CBT columns live in LDS.
+// The decode configurations spend LDS on few, fast rows; the prefill one (many rows) keeps its
+// LDS small so that eight rows share a CU.
+template <int NT_, int E_, int RB_, int PASSES_, int BAND_, int CBT_>
+struct TopkCfg {
+  static constexpr int NT = NT_, E = E_, RB = RB_, PASSES = PASSES_, BAND = BAND_, CBT = CBT_;
+};
+using TopkDecode8 = TopkCfg<512, 8, 12, 2, 1024, 2048>;
+using TopkDecode16 = TopkCfg<512, 16, 12, 2, 1024, 2048>;
+using TopkDecode32 = TopkCfg<512, 32, 12, 2, 1024, 2048>;
+using TopkDecode1k = TopkCfg<1024, 32, 12, 2, 1024, 2048>;
+using TopkPrefill = TopkCfg<256, 16, 8, 3, 256, 512>;
+constexpr int kTopkPrefillMinRows = 1024;  // rows in the call from which TopkPrefill is used
 
 // Inclusive prefix sum over the 64 lanes of a wavefront: shifts within rows of 16, then the
 // row totals broadcast to the later rows (DPP, no LDS round trips).
@@ -749,13 +763,6 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
-// Radix select of the kb-th largest fast score: two passes of 12-bit digits over the top 24
-// bits of the order-preserving key.  The last 8 bits stay unresolved: the threshold is known to
-// lie in the value interval of one 256-key bin, which the band below absorbs.
-constexpr int kRadixBits = 12;
-constexpr int kRadixBins = 1 << kRadixBits;
-// The request's block-table row is copied to LDS when it has at most this many columns.
-constexpr int kTopkCbtCap = 2048;
 
 // float32 thresholds that are conservative for the float64 ones: x > up(t) implies x > t, and
 // x < down(t) implies x < t.
@@ -776,9 +783,14 @@ __device__ __forceinline__ float round_down_f32(double t) {
 // One workgroup of NT threads per row; thread t holds the fast scores of blocks
 // t*E .. t*E+E-1 in registers for the whole selection (blocks past the visible range as -inf,
 // which no threshold below admits).
-template <int NT, int E>
-__global__ __launch_bounds__(NT) void topk_kernel(SelectParams P) {
+template <typename C>
+__global__ __launch_bounds__(C::NT) void topk_kernel(SelectParams P) {
+  constexpr int NT = C::NT, E = C::E;
+  constexpr int kRadixBits = C::RB, kRadixBins = 1 << C::RB, kBandCap = C::BAND;
+  constexpr int kTopkCbtCap = C::CBT;
+  constexpr uint32_t kLowMask = (1u << (32 - C::RB * C::PASSES)) - 1u;  // unresolved bits
   static_assert(32 % E == 0 || E == 32, "a thread's blocks share one word of the mask");
+  static_assert(kRadixBins >= NT, "every thread scans at least one bin");
   constexpr int kWaves = NT / 64, kPB = kRadixBins / NT;  // bins per thread in the scans
   extern __shared__ uint32_t sel_mask[];  // [ceil(cols / 32)] band-selected blocks
   __shared__ __attribute__((aligned(16))) int hist[2][kRadixBins];
@@ -901,19 +913,23 @@ __global__ __launch_bounds__(NT) void topk_kernel(SelectParams P) {
   const int mask_words = (vis + 31) >> 5;
   for (int i = tid; i < mask_words; i += NT) sel_mask[i] = 0u;
 
-  // ---- radix select.  Thread t reads the counts of bins 4095 - t*kPB - i (i < kPB): lower
+  // ---- radix select.  Thread t reads the counts of bins (bins-1) - t*kPB - i (i < kPB): lower
   // threads own higher bins, so a workgroup prefix sum gives the count above each bin.  The
   // -inf entries land in the lowest bin, below any kb-th largest of the visible blocks.
+  // Histograms alternate between two buffers; a pass clears the one the next-but-one uses.
   uint32_t prefix = 0, pmask = 0;
   int krem = kb;
 #pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
+  for (int pass = 0; pass < C::PASSES; ++pass) {
     const int shift = 32 - kRadixBits * (pass + 1);
-    int* h = hist[pass];
+    int* h = hist[pass & 1];
 #pragma unroll
     for (int i = 0; i < E; ++i) {
       const uint32_t u = key[i];
       if ((u & pmask) == prefix) atomicAdd(&h[(u >> shift) & (kRadixBins - 1)], 1);
+    }
+    if (pass >= 1 && pass + 1 < C::PASSES) {  // the buffer of pass + 1 was read by pass - 1
+      for (int i = tid; i < kRadixBins; i += NT) hist[(pass + 1) & 1][i] = 0;
     }
     if (pass == 1) {  // the error-bound inputs, reduced over the workgroup below
       const float kmw = wave_max(km);
@@ -954,7 +970,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(SelectParams P) {
     krem = s_int[5];
   }
   // The kb-th largest fast score lies in [T_lo, T_hi], the values of the keys prefix..prefix|255.
-  const double T_lo = (double)fval(prefix), T_hi = (double)fval(prefix | 0xFFu);
+  const double T_lo = (double)fval(prefix), T_hi = (double)fval(prefix | kLowMask);
   if (cbt_in_lds) {
 #pragma unroll
     for (int k = 0; k < kCbtPer; ++k) {
@@ -1135,9 +1151,9 @@ __global__ __launch_bounds__(NT) void topk_kernel(SelectParams P) {
   }
 }
 
-template <int NT, int E>
+template <typename C>
 hipError_t launch_topk_kernel(const SelectParams& P, size_t mask_bytes, hipStream_t s) {
-  hipLaunchKernelGGL((topk_kernel<NT, E>), dim3(P.T), dim3(NT), mask_bytes, s, P);
+  hipLaunchKernelGGL((topk_kernel<C>), dim3(P.T), dim3(C::NT), mask_bytes, s, P);
   return hipGetLastError();
 }
 
@@ -1218,10 +1234,12 @@ hipError_t launch_topk(const qsa_topk_args& a, const TopkLayout& L, char* ws, hi
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const size_t mask_bytes = (size_t)(L.cols + 31) / 32 * sizeof(uint32_t);
-  if (L.cols <= 512 * 8) return launch_topk_kernel<512, 8>(P, mask_bytes, s);
-  if (L.cols <= 512 * 16) return launch_topk_kernel<512, 16>(P, mask_bytes, s);
-  if (L.cols <= 512 * 32) return launch_topk_kernel<512, 32>(P, mask_bytes, s);
-  return launch_topk_kernel<1024, 32>(P, mask_bytes, s);
+  if (P.T >= kTopkPrefillMinRows && L.cols <= TopkPrefill::NT * TopkPrefill::E)
+    return launch_topk_kernel<TopkPrefill>(P, mask_bytes, s);
+  if (L.cols <= 512 * 8) return launch_topk_kernel<TopkDecode8>(P, mask_bytes, s);
+  if (L.cols <= 512 * 16) return launch_topk_kernel<TopkDecode16>(P, mask_bytes, s);
+  if (L.cols <= 512 * 32) return launch_topk_kernel<TopkDecode32>(P, mask_bytes, s);
+  return launch_topk_kernel<TopkDecode1k>(P, mask_bytes, s);
 }
 
 }  // namespace qsa

@@ -12,6 +12,7 @@ import torch
 from oracle import qsa as oq
 from oracle.numerics import bf16_bits_to_f64, e4m3_bits_to_f64
 from sparse_attention_qsa_amd import binding as B
+from sparse_attention_qsa_amd.step import QsaStep
 from tests.gpu_util import (SCALED, TOL, gpu_out_f64, log, max_abs, oracle_step, run_gpu,
                             to_np, workload)
 
@@ -125,6 +126,38 @@ def test_full_size_decode_32k_fp8_kv_on_sampled_rows():
     err = max_abs(gpu_out_f64(st)[rows], ref.out[rows])
     log(f"  max-abs {err:.3e}")
     assert err <= TOL["bf16"]
+
+
+def test_prefill_row_counts_select_exactly():
+    """Calls with many rows take the prefill top-k configuration (three 8-bit radix passes,
+    256 threads): 1280 rows here, every one compared."""
+    wl = workload("chunked_prefill", rows=640)
+    assert wl.num_tokens >= 1024
+    log(f"prefill top-k parity: T={wl.num_tokens}")
+    ref = oracle_step(wl, with_attention=False)
+    st = run_gpu(wl)
+    packed = to_np(st.packed)
+    assert np.array_equal(packed, ref.packed), (
+        f"{int((packed != ref.packed).any(axis=1).sum())} rows differ")
+
+
+def test_full_size_chunked_prefill_on_sampled_rows():
+    """The whole chunked_prefill indexer call (4 x 8192 rows on 8192 cached tokens: MFMA
+    logits, prefill top-k) at full size, on sampled rows."""
+    wl = workload("chunked_prefill", num_requests=4, lengths=("fixed", 16384), rows=8192)
+    rows = [0, 4097, 8191, 8192 + 777, 3 * 8192 + 8191]
+    log(f"full-size chunked_prefill, sampled rows {rows}")
+    ref = oracle_step(wl, rows=rows, with_attention=False)
+    st = QsaStep(wl)
+    st.compress()
+    st.topk()
+    torch.cuda.synchronize()
+    packed = to_np(st.packed)
+    assert np.array_equal(packed[rows], ref.packed[rows])
+    # Every row: the count is kb*c plus the uncompressed tail (p+1) mod c, p = 8192 + i.
+    W, c = wl.output_width, wl.compress_ratio
+    p = 8192 + np.tile(np.arange(8192), 4)
+    assert np.array_equal(packed[:, W], 2048 + (p + 1) % c)
 
 
 def test_fp8_kv_scales_act_on_scores_and_output():
