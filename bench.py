@@ -29,10 +29,11 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
 METRIC = "decode rows/sec + achieved HBM GB/s, QSA indexer+sparse GQA at 32k ctx"
-KERNEL_SOURCES = {
-    "qsa_compress": ["compress.hip"],
-    "qsa_index_logits_topk": ["select.hip"],
-    "qsa_sparse_gqa": ["gqa.hip"],
+KERNEL_SOURCES = {   # the sources of the kernels a traffic record measured (decode workload)
+    "qsa_compress": ["qsa_internal.h", "compress.hip"],
+    "qsa_index_logits_topk": ["qsa_internal.h", "select.h", "select.hip", "logits.hip",
+                              "topk.hip"],
+    "qsa_sparse_gqa": ["qsa_internal.h", "gqa.hip"],
 }
 
 

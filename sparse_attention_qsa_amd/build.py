@@ -17,7 +17,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqsa.so")
 ARCH = "gfx950"
 
-SOURCES = ["qsa_abi.cpp", "compress.hip", "select.hip", "gqa.hip", "diag.hip"]
+SOURCES = ["qsa_abi.cpp", "compress.hip", "select.hip", "logits.hip", "logits_mfma.hip",
+           "topk.hip", "gqa.hip", "diag.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
           "-Wno-unused-function", "-Wno-unused-variable",

@@ -1,0 +1,36 @@
+// Parameter block shared by the qsa_index_logits_topk kernels (indexer logits on the vector
+// units and on the matrix cores, block top-k with expansion) and their launchers.
+#pragma once
+
+#include "qsa_internal.h"
+
+namespace qsa {
+
+struct SelectParams {
+  int T, R, Hi, c, budget, Pc, c_pages, cbt_stride, cbt_width, cols, col_stride, key_tiles;
+  int key_blocks;     // 128-key blocks per request in the kmax array
+  int mfma_min_rows;  // requests with more rows than this are scored by the MFMA kernel
+  bool fp8;
+  const int32_t* qsl;
+  const int32_t* seq_lens;
+  const void* q_idx;
+  const void* ckv;
+  const int32_t* cbt;
+  int32_t* packed;
+  int64_t p_rs;
+  float* logits;
+  float* kmax;  // [R, key_blocks]: an upper bound of max |k| over each block of 128 keys
+  int32_t* band_idx;
+  double* band_score;
+  int* work;  // [8] work counters of the MFMA kernel's queues, zeroed by the VALU kernel
+};
+
+// bf16 requests with more rows than this are scored by the matrix-core logits kernel.
+constexpr int kMfmaMinRows = 16;
+
+// Launchers (each next to its kernels); arguments are validated by the caller.
+hipError_t launch_logits_valu(const SelectParams& P, int rows_per_chunk, hipStream_t s);
+hipError_t launch_logits_mfma(const SelectParams& P, int max_query_len, hipStream_t s);
+hipError_t launch_topk_select(const SelectParams& P, hipStream_t s);
+
+}  // namespace qsa
