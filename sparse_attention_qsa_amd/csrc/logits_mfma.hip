@@ -60,12 +60,54 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
   }
 }
 
+// LDS accesses issued as inline assembly, so that the compiler's own wait insertion (which
+// cannot tell the targets of the LDS-direct loads apart) does not make them wait for every
+// memory operation in flight; each read is waited for before its value is used.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ uint32_t lds_load_u32(const void* p) {
+  uint32_t v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_addr(p))
+               : "memory");
+  return v;
+}
+__device__ __forceinline__ void lds_store_u32(void* p, uint32_t v) {
+  asm volatile("ds_write_b32 %0, %1" ::"v"(lds_addr(p)), "v"(v) : "memory");
+}
+
+// Claims the next work item of a queue (a returning global atomic issued as inline assembly:
+// the compiler would wait for its result at once, and with it for every store in flight).  The
+// result is valid after a vmcnt wait that covers it.
+__device__ __forceinline__ uint32_t claim_async(int* counter) {
+  uint32_t ret;
+  asm volatile("global_atomic_add %0, %1, %2, off sc0"
+               : "=v"(ret)
+               : "v"((uint64_t)(uintptr_t)counter), "v"(1u)
+               : "memory");
+  return ret;
+}
+
+// Largest value over the wavefront (DPP within rows of 16, then the four row results).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return max(max(a, b), max(c, d));
+}
+
 // Persistent workgroups (one per CU; the LDS use allows no more) take work items -- (request,
 // chunk of up to four row blocks, key tile of 256 keys) -- from eight queues, one per XCD:
 // queue x holds the (request, row chunk) pairs x, x+8, ..., each with all its key tiles in
 // order, so that the workgroups of one XCD work on the same rows at once and share their Q in
 // the XCD's L2.  (Workgroup b takes queue b % 8, which is its XCD under round-robin dispatch;
-// any other placement only costs locality.)  An item loads its key tile once and keeps the
+// any other placement only costs locality.)  An item claims the next one when it starts, and
+// loads its key tile once and keeps the
 // key fragments in registers (8 waves, 2 x 4 of 64 rows x 64 keys; per wave 4 x 4
 // accumulators of 16 keys x 16 rows, v_mfma_f32_16x16x32_bf16 with the keys as the A operand
 // so that a lane ends up with 4 consecutive keys of one row).  The Q slabs (128 rows of one
@@ -79,9 +121,9 @@ __global__ __launch_bounds__(512) void logits_mfma_kernel(SelectParams P, int ro
   __shared__ __attribute__((aligned(16))) uint8_t lds[4][kMfmaRows * 256];
   uint8_t* const kl = lds[2];
   uint8_t* const kh = lds[3];
-  __shared__ float red[2][8];
-  __shared__ __attribute__((aligned(4))) uint8_t kok[kMfmaKeys];
-  __shared__ int s_item;
+  __shared__ uint32_t red[2][8];
+  __shared__ __attribute__((aligned(16))) uint8_t kok[kMfmaKeys];
+  __shared__ int s_item[2];
   const int key_tiles = (P.cols + kMfmaKeys - 1) / kMfmaKeys;
   const int row_chunks = (row_blocks + kMfmaRowBlocksPerWG - 1) / kMfmaRowBlocksPerWG;
   const int pairs = P.R * row_chunks;
@@ -89,6 +131,7 @@ __global__ __launch_bounds__(512) void logits_mfma_kernel(SelectParams P, int ro
   const int64_t qlen = (int64_t)((pairs - queue + 7) / 8) * key_tiles;  // items of this queue
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int l16 = lane & 15, l4 = lane >> 4;
   const int wr = w >> 2, wc = w & 3;  // this wave: rows 64wr .. +63, keys 64wc .. +63
   const char* ckv = reinterpret_cast<const char*>(P.ckv);
   const char* qb = reinterpret_cast<const char*>(P.q_idx);
@@ -100,19 +143,25 @@ __global__ __launch_bounds__(512) void logits_mfma_kernel(SelectParams P, int ro
     asm volatile("" ::: "memory");
   };
 
-  for (;;) {
-    if (tid == 0) s_item = atomicAdd(&P.work[queue], 1);
-    barrier();
-    const int64_t item = s_item;
-    barrier();  // every wave has read s_item (and is done with the previous item's LDS)
+  if (tid == 0) s_item[0] = atomicAdd(&P.work[queue], 1);
+  __syncthreads();
+  for (int it = 0;; ++it) {
+    const int64_t item = (int)__builtin_amdgcn_readfirstlane((int)lds_load_u32(&s_item[it & 1]));
     if (item >= qlen) break;  // workgroup-uniform
+    uint32_t next = 0;
+    if (tid == 0) next = claim_async(&P.work[queue]);
     const int g = queue + 8 * (int)(item / key_tiles);
     const int kt = (int)(item % key_tiles);
     const int rc = g % row_chunks, r = g / row_chunks;
 
-    const int q0 = max(0, min(P.qsl[r], P.T));
-    const int n = max(0, min(P.qsl[r + 1], P.T) - q0), L = P.seq_lens[r];
-    if (n <= P.mfma_min_rows || n > L) continue;  // decode request, or inert rows
+    // Request metadata through the scalar cache (vector loads would wait for the stores in
+    // flight).
+    const __attribute__((address_space(4))) int32_t* qsl_c =
+        (const __attribute__((address_space(4))) int32_t*)P.qsl;
+    const __attribute__((address_space(4))) int32_t* sl_c =
+        (const __attribute__((address_space(4))) int32_t*)P.seq_lens;
+    const int q0 = max(0, min(qsl_c[r], P.T));
+    const int n = max(0, min(qsl_c[r + 1], P.T) - q0), L = sl_c[r];
     const int key0 = kt * kMfmaKeys;
     const int vis_max = min(L / P.c, P.cols);
     // Row blocks of this chunk that see at least one key of the tile (visibility grows with
@@ -123,8 +172,17 @@ __global__ __launch_bounds__(512) void logits_mfma_kernel(SelectParams P, int ro
       const int last = min(kMfmaRows, n - rb * kMfmaRows);
       return key0 < min((L - n + rb * kMfmaRows + last) / P.c, P.cols);
     };
-    while (rb_first < rb_end && !sees_tile(rb_first)) ++rb_first;
-    if (rb_first >= rb_end) continue;
+    if (n > P.mfma_min_rows && n <= L) {
+      while (rb_first < rb_end && !sees_tile(rb_first)) ++rb_first;
+    } else {
+      rb_first = rb_end;  // decode request, or inert rows
+    }
+    if (rb_first >= rb_end) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the claim has returned
+      if (tid == 0) lds_store_u32(&s_item[(it + 1) & 1], next);
+      barrier();
+      continue;
+    }
 
     // ---- key tile (keys key0 .. key0+255), 8 loads per wave (wave w: keys 32w .. 32w+31, in
     // kl for w < 4, else kh); the block-table reads come first, all in flight together.  A
@@ -169,48 +227,60 @@ __global__ __launch_bounds__(512) void logits_mfma_kernel(SelectParams P, int ro
     load_q(0, lds[0]);
     if (nslabs > 1) load_q(1, lds[1]);
     wait_vmcnt(nslabs > 1 ? 4 : 0);  // the key tile and slab 0 have landed
+    if (tid == 0) lds_store_u32(&s_item[(it + 1) & 1], next);
     barrier();
 
-    // ---- max |k| over the valid keys of each 128-key half (upper bounds for the top-k).
-    // Consecutive lanes read consecutive dwords; dword d of a half belongs to its key d / 64.
-    {
-      float km[2] = {0.0f, 0.0f};
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const uint32_t* kw = reinterpret_cast<const uint32_t*>(hf ? kh : kl);
-#pragma unroll 8
-        for (int i = 0; i < 16; ++i) {
-          const int d = tid + 512 * i;
-          if (kok[128 * hf + (d >> 6)]) {
-            const uint32_t u = kw[d];
-            km[hf] = fmaxf(km[hf], fmaxf(fabsf(bf16lo(u)), fabsf(bf16hi(u))));
-          }
-        }
-      }
-      km[0] = wave_max(km[0]);
-      km[1] = wave_max(km[1]);
-      if (lane == 0) {
-        red[0][w] = km[0];
-        red[1][w] = km[1];
-      }
-    }
     // ---- this wave's key fragments: keys 64wc + 16kk + lane%16, dims 32ks + 8(lane/16) .. +7
+    // (row 64(wc%2) + 16kk + lane%16 of its half: slot (4ks + lane/16) ^ (lane%16)), and the
+    // validity of those keys.
     bf16x8_t kfr[4][4];
+    uint32_t okk[4];
     {
       const uint8_t* kt_half = wc < 2 ? kl : kh;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
+      for (int ks = 0; ks < 4; ++ks) {
+        const uint32_t a0 = tile_chunk_addr(kt_half, 64 * (wc & 1) + l16, 4 * ks + l4);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          kfr[kk][ks] = tile_chunk(kt_half, 64 * (wc & 1) + 16 * kk + (lane & 15),
-                                   4 * ks + (lane >> 4));
+        for (int kk = 0; kk < 4; ++kk)
+          asm volatile("ds_read_b128 %0, %1" : "=v"(kfr[kk][ks]) : "v"(a0 + 4096u * kk));
       }
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        asm volatile("ds_read_u8 %0, %1"
+                     : "=v"(okk[kk])
+                     : "v"(lds_addr(kok + 64 * wc + 16 * kk + l16)));
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(kfr[0][0]), "+v"(kfr[0][1]), "+v"(kfr[0][2]),
+                   "+v"(kfr[0][3]), "+v"(kfr[1][0]), "+v"(kfr[1][1]), "+v"(kfr[1][2]),
+                   "+v"(kfr[1][3]), "+v"(okk[0]), "+v"(okk[1]), "+v"(okk[2]), "+v"(okk[3]));
+      asm volatile("" : "+v"(kfr[2][0]), "+v"(kfr[2][1]), "+v"(kfr[2][2]), "+v"(kfr[2][3]),
+                   "+v"(kfr[3][0]), "+v"(kfr[3][1]), "+v"(kfr[3][2]), "+v"(kfr[3][3]));
+    }
+    // ---- max |k| over the valid keys of each 128-key half (upper bounds for the top-k's
+    // error band), on the bf16 bit patterns (order-preserving for |k|): per wave, then over
+    // the two waves of each half.
+    {
+      uint32_t mk = 0;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const u32x4_t u = __builtin_bit_cast(u32x4_t, kfr[kk][ks]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t x = u[e] & 0x7FFF7FFFu;
+            m = max(m, max(x & 0xFFFFu, x >> 16));
+          }
+        }
+        mk = okk[kk] ? max(mk, m) : mk;
+      }
+      mk = wave_max_u32(mk);
+      if (lane == 0 && wr == 0) lds_store_u32(&red[wc >> 1][wc & 1], mk);
     }
     barrier();  // red[] complete; the key tile is free for slabs 2 and 3
     if (tid < 2 && 2 * kt + tid < P.key_blocks) {
-      float m = red[tid][0];
-      for (int i = 1; i < 8; ++i) m = fmaxf(m, red[tid][i]);
-      P.kmax[(int64_t)r * P.key_blocks + 2 * kt + tid] = m;
+      const uint32_t m = max(lds_load_u32(&red[tid][0]), lds_load_u32(&red[tid][1]));
+      P.kmax[(int64_t)r * P.key_blocks + 2 * kt + tid] = __uint_as_float(m << 16);
     }
     if (nslabs > 2) load_q(2, lds[2]);
 
