@@ -284,6 +284,81 @@ def compress_step(query_start_loc, seq_lens, k_proj, rope_pos, mrope_section, co
     return CompressState(ring=ring, ring_pos=ring_pos, ckv=ckv)
 
 
+# ----------------------------------------------------------------------------- main prepare
+
+
+def encode_scaled_e4m3(x: np.ndarray, scale: float) -> np.ndarray:
+    """e4m3fn codes of x / scale for a main K/V cache with a static per-tensor scale.
+
+    [fp8kv] the cache bytes are written by reshape_and_cache_flash with the layer's scales,
+    and that writer clamps to +-448 (it never emits the NaN codes).  Reading: the quotient is
+    taken in float32 (correctly rounded), clamped to [-448, 448], then rounded to nearest
+    even on the e4m3fn grid.
+    """
+    q = (np.asarray(x, dtype=np.float64) / float(np.float32(scale))).astype(np.float32)
+    return f64_to_e4m3_bits(np.clip(q.astype(np.float64), -448.0, 448.0))
+
+
+def prepare_main(main_qkv, rope_pos, cos_sin, mrope_section, q_norm_w, k_norm_w, eps,
+                 num_q_heads, num_kv_heads, kv_cache, slot_mapping, kv_dtype="bf16",
+                 k_scale=1.0, v_scale=1.0):
+    """Main-attention prepare: normalised, rotated Q, and the step's K/V in the paged cache.
+
+    [qsa] Qwen4ExpQSAAttention: the q/k/v projection packs a sigmoid output gate next to Q
+    (2*Hq heads of 128), then Hkv K heads and Hkv V heads; q_norm and k_norm are
+    GemmaRMSNorm(head_dim); the fused qsa_prepare launch takes the main qkv, both norm
+    weights, one epsilon, the main cache, the slot mapping and the K/V scales, and returns
+    (query, output_gate); the unfused path writes K/V with reshape_and_cache_flash, which
+    skips rows whose slot is negative.
+
+    Readings: each Q head's 256 values are its q (first 128) then its gate (last 128); Q and
+    K are rotated like the indexer (NeoX on dims 0..63, with the same cos/sin table and the
+    row's rotary position: the fused launch receives one table for both); slot s stores at
+    page s // P, offset s % P; the gate is returned untouched (the attention reads it in
+    place).  The chain is the canonical one of the indexer prep (RMSNorm -> bf16 -> RoPE ->
+    bf16); V is stored as given.
+
+    main_qkv: [T, (2*Hq + 2*Hkv)*128] uint16; kv_cache [pages, Hkv, P, 256] uint16 (bf16) or
+    uint8 (fp8: K and V as encode_scaled_e4m3 with k_scale / v_scale).  Returns (q bits
+    [T, Hq, 128] uint16, a copy of the cache with the step's rows written).
+    """
+    main_qkv = np.asarray(main_qkv)
+    T = main_qkv.shape[0]
+    Hq, Hkv, D = int(num_q_heads), int(num_kv_heads), HEAD_DIM
+    qg = main_qkv[:, :2 * Hq * D].reshape(T, Hq, 2, D)
+    k_bits = main_qkv[:, 2 * Hq * D:(2 * Hq + Hkv) * D].reshape(T, Hkv, D)
+    v_bits = main_qkv[:, (2 * Hq + Hkv) * D:(2 * Hq + 2 * Hkv) * D].reshape(T, Hkv, D)
+    pos = np.asarray(rope_pos, dtype=np.int64)
+
+    def norm_rope(x_bits, w_bits, heads):
+        x = bf16_bits_to_f64(x_bits).reshape(T * heads, D)
+        y = gemma_rmsnorm(x, bf16_bits_to_f64(w_bits), eps)
+        cos, sin = gather_cos_sin(cos_sin, np.repeat(pos, heads, axis=0), mrope_section)
+        return neox_rope(y, cos, sin).reshape(T, heads, D)
+
+    q_out = f64_to_bf16_bits(norm_rope(qg[:, :, 0, :], q_norm_w, Hq)) if T else \
+        np.zeros((0, Hq, D), np.uint16)
+    cache = np.array(kv_cache, copy=True)
+    if T == 0:
+        return q_out, cache
+    k_vals = norm_rope(k_bits, k_norm_w, Hkv)
+    pages, _, P, _ = cache.shape
+    for t in range(T):
+        slot = int(slot_mapping[t])
+        if slot < 0 or slot // P >= pages:
+            continue
+        page, off = slot // P, slot % P
+        for h in range(Hkv):
+            if kv_dtype == "fp8":
+                cache[page, h, off, :D] = encode_scaled_e4m3(k_vals[t, h], k_scale)
+                cache[page, h, off, D:] = encode_scaled_e4m3(bf16_bits_to_f64(v_bits[t, h]),
+                                                             v_scale)
+            else:
+                cache[page, h, off, :D] = f64_to_bf16_bits(k_vals[t, h])
+                cache[page, h, off, D:] = v_bits[t, h]
+    return q_out, cache
+
+
 # ----------------------------------------------------------------------------- A3-A5: select
 
 
