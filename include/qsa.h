@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 2
+#define QSA_ABI_VERSION 3
 
 typedef enum qsa_status {
   QSA_OK = 0,
@@ -86,6 +86,23 @@ typedef enum qsa_dtype { QSA_DTYPE_BF16 = 0, QSA_DTYPE_FP8_E4M3 = 1 } qsa_dtype;
  * Arithmetic is the canonical float64 chain of this project (halving sums over the 128 dims,
  * correctly rounded sqrt and divide, float64 -> float32 -> bf16 rounding, RNE e4m3fn cast that
  * maps overflow to NaN), so q_idx and the cache bytes are reproducible bit for bit.
+ *
+ * Main-attention prepare (optional, in the same launch; skipped when main_qkv is NULL).
+ * Follows the fused qsa_prepare call of QSAIndexer.forward and Qwen4ExpQSAAttention (page
+ * "vllm.models.qwen4_exp.nvidia.qsa": one launch does the indexer prepare, the main Q/K norm,
+ * RoPE and gate split and the main K/V cache write):
+ *   main_qkv row: for each of the Hq query heads its q (128 values) then its output gate (128
+ *   values), then the Hkv K heads, then the Hkv V heads (bf16);
+ *   (4) main Q: per head Gemma RMSNorm with main_q_norm_weight -> bf16 -> NeoX RoPE on dims
+ *       0..63 with the same table and rotary position as the indexer Q -> bf16 -> main_q;
+ *   (5) main K: the same with main_k_norm_weight; K and V (as given) are stored for every row
+ *       whose main_slot_mapping entry s is >= 0 at page s / P, offset s % P of the main cache
+ *       (rows whose page is >= main_num_pages are skipped too).  A bf16 cache receives the bf16
+ *       values; an FP8_E4M3 cache receives e4m3fn(x / scale) with the quotient in float32,
+ *       clamped to +-448 (the cache writer the FP8 KV reader patch page describes saturates).
+ *   The gate is not copied: qsa_sparse_gqa reads it in place (gate = main_qkv + 128, gate
+ *   head stride 256, gate row stride main_qkv_row_stride).
+ * The main cache layout and strides are those of qsa_sparse_gqa's kv_cache.
  * ------------------------------------------------------------------------------------------ */
 typedef struct qsa_compress_args {
   int32_t num_tokens;               /* T: rows of this step                                  */
@@ -127,6 +144,25 @@ typedef struct qsa_compress_args {
   int32_t compress_ratio;           /* c: power of two, 2..64                                */
   qsa_dtype index_dtype;
   void* q_idx;                      /* OUT [T, Hi, 128] in index_dtype, contiguous           */
+  /* main-attention prepare (all ignored when main_qkv is NULL)                              */
+  const uint16_t* main_qkv;         /* [T, (2*Hq + 2*Hkv)*128] bf16, layout above            */
+  int64_t main_qkv_row_stride;      /* in elements, even                                     */
+  int32_t num_q_heads;              /* Hq (1..128)                                           */
+  int32_t num_kv_heads;             /* Hkv (1..64)                                           */
+  const uint16_t* main_q_norm_weight; /* [128] bf16                                          */
+  const uint16_t* main_k_norm_weight; /* [128] bf16                                          */
+  float main_eps;                   /* the main q_norm / k_norm epsilon                      */
+  uint16_t* main_q;                 /* OUT [T, Hq, 128] bf16, contiguous                     */
+  void* main_kv_cache;              /* [pages, Hkv, P, 256] bf16 or e4m3fn, strides below    */
+  int64_t main_kv_page_stride;      /* strides in elements; multiples of 16 bytes            */
+  int64_t main_kv_head_stride;
+  int64_t main_kv_token_stride;     /* >= 256                                                */
+  int32_t main_num_pages;
+  int32_t main_page_size;           /* P >= 1                                                */
+  const int64_t* main_slot_mapping; /* [T] page * P + offset; negative: the row is not stored */
+  qsa_dtype main_kv_dtype;          /* BF16 or FP8_E4M3                                      */
+  float main_k_scale;               /* FP8_E4M3: stored code = e4m3fn(K / k_scale); > 0      */
+  float main_v_scale;               /* FP8_E4M3: stored code = e4m3fn(V / v_scale); > 0      */
 } qsa_compress_args;
 
 qsa_status qsa_compress(const qsa_compress_args* args, void* stream);

@@ -44,6 +44,13 @@ class CompressArgs(C.Structure):
         ("num_index_heads", _I32), ("head_dim", _I32), ("rotary_dim", _I32),
         ("compress_ratio", _I32), ("index_dtype", _I32),
         ("q_idx", _P),
+        ("main_qkv", _P), ("main_qkv_row_stride", _I64), ("num_q_heads", _I32),
+        ("num_kv_heads", _I32), ("main_q_norm_weight", _P), ("main_k_norm_weight", _P),
+        ("main_eps", C.c_float), ("main_q", _P), ("main_kv_cache", _P),
+        ("main_kv_page_stride", _I64), ("main_kv_head_stride", _I64),
+        ("main_kv_token_stride", _I64), ("main_num_pages", _I32), ("main_page_size", _I32),
+        ("main_slot_mapping", _P), ("main_kv_dtype", _I32), ("main_k_scale", C.c_float),
+        ("main_v_scale", C.c_float),
     ]
 
 
@@ -147,7 +154,13 @@ def _need(t: torch.Tensor, dtype, name: str) -> None:
 def compress_args(*, query_start_loc, seq_lens, max_query_len, q_proj, k_proj, positions,
                   cos_sin, q_norm_weight, k_norm_weight, eps, ring, ring_page, ckv,
                   c_block_table, q_idx, num_index_heads, compress_ratio, index_dtype,
-                  ring_pos=None, mrope_section=None, c_block_table_width=None) -> CompressArgs:
+                  ring_pos=None, mrope_section=None, c_block_table_width=None,
+                  main=None) -> CompressArgs:
+    """`main`, if given, adds the main-attention prepare: a dict with main_qkv [T,
+    (2Hq+2Hkv)*128] bf16, num_q_heads, num_kv_heads, main_q_norm_weight, main_k_norm_weight,
+    main_eps, main_q [T, Hq, 128] bf16 (out), main_kv_cache [pages, Hkv, P, 256] (bf16, or uint8
+    e4m3fn codes), main_slot_mapping [T] int64 and, for an fp8 cache, main_k_scale /
+    main_v_scale."""
     _need(q_proj, torch.bfloat16, "q_proj")
     _need(k_proj, torch.bfloat16, "k_proj")
     _need(positions, torch.int64, "positions")
@@ -192,6 +205,33 @@ def compress_args(*, query_start_loc, seq_lens, max_query_len, q_proj, k_proj, p
     a.compress_ratio = int(compress_ratio)
     a.index_dtype = DTYPES[index_dtype]
     a.q_idx = _ptr(q_idx)
+    if main is not None:
+        qkv, cache, slots, mq = (main["main_qkv"], main["main_kv_cache"],
+                                 main["main_slot_mapping"], main["main_q"])
+        _need(qkv, torch.bfloat16, "main_qkv")
+        _need(mq, torch.bfloat16, "main_q")
+        _need(slots, torch.int64, "main_slot_mapping")
+        fp8 = cache.dtype == torch.uint8
+        if not fp8:
+            _need(cache, torch.bfloat16, "main_kv_cache")
+        a.main_qkv = _ptr(qkv)
+        a.main_qkv_row_stride = qkv.stride(0)
+        a.num_q_heads = int(main["num_q_heads"])
+        a.num_kv_heads = int(main["num_kv_heads"])
+        a.main_q_norm_weight = _ptr(main["main_q_norm_weight"])
+        a.main_k_norm_weight = _ptr(main["main_k_norm_weight"])
+        a.main_eps = float(main["main_eps"])
+        a.main_q = _ptr(mq)
+        a.main_kv_cache = _ptr(cache)
+        a.main_kv_page_stride = cache.stride(0)
+        a.main_kv_head_stride = cache.stride(1)
+        a.main_kv_token_stride = cache.stride(2)
+        a.main_num_pages = cache.shape[0]
+        a.main_page_size = cache.shape[2]
+        a.main_slot_mapping = _ptr(slots)
+        a.main_kv_dtype = DTYPES["fp8" if fp8 else "bf16"]
+        a.main_k_scale = float(main.get("main_k_scale", 1.0))
+        a.main_v_scale = float(main.get("main_v_scale", 1.0))
     return a
 
 

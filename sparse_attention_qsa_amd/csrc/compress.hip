@@ -3,7 +3,9 @@
 //
 // Follows QSAIndexer.forward's unfused reference path (page "vllm.models.qwen4_exp.nvidia.qsa")
 // and qsa_compress_groups_with_ratio / qsa_store_cache_rows (page
-// "vllm.models.qwen4_exp.nvidia.ops.qsa").  One wavefront owns one 128-dim vector: lane l holds
+// "vllm.models.qwen4_exp.nvidia.ops.qsa"); optionally, in the same launch, the main-attention
+// prepare of the fused qsa_prepare call (Qwen4ExpQSAAttention: main Q/K norm and RoPE, K/V
+// written to the main cache).  One wavefront owns one 128-dim vector: lane l holds
 // dims 2l and 2l+1, which is also the layout of the canonical halving sum (adjacent pairs first,
 // then the upper half of the lanes onto the lower half), so every value is bit-identical to the
 // float64 chain the oracle defines.  The work is a few MB at most per step: the kernels are
@@ -36,6 +38,19 @@ struct CompressParams {
   void* ckv;
   const int32_t* cbt;
   void* q_idx;
+  // main-attention prepare (main == false: none)
+  bool main, main_fp8;
+  int Hq, Hkv, m_pages, m_P;
+  const uint32_t* mqkv;  // bf16 pairs
+  int64_t m_rs;          // row stride in pairs
+  const uint16_t* mqw;
+  const uint16_t* mkw;
+  double m_eps;
+  uint32_t* mq;  // bf16 pairs [T, Hq, 64]
+  void* mcache;
+  int64_t m_ps, m_hs, m_ts;  // strides in elements
+  const int64_t* slots;
+  float k_scale, v_scale;
 };
 
 // Position axis (0 = T, 1 = H, 2 = W) of rotary frequency f under interleaved MRoPE.
@@ -117,6 +132,14 @@ __device__ __forceinline__ void store_index_pair(const CompressParams& P, void* 
   }
 }
 
+// Main-cache fp8 code of x / scale: the quotient rounded to float32, clamped to +-448 (the
+// saturating writer), then RNE on the e4m3fn grid.
+__device__ __forceinline__ uint32_t scaled_e4m3_sat(float x, float scale) {
+  const float q = (float)((double)x / (double)scale);
+  if (!(q == q)) return f32_to_e4m3(q);
+  return f32_to_e4m3(fminf(fmaxf(q, -448.0f), 448.0f));
+}
+
 __device__ __forceinline__ void ring_store_row(const CompressParams& P, int row, int r, int p,
                                                int L, int lane) {
   if (p < L - P.S) return;
@@ -178,7 +201,57 @@ __global__ __launch_bounds__(256) void prep_compress_kernel(CompressParams P) {
     return;
   }
   const int64_t row64 = wave - nq;
-  if (row64 >= P.T) return;
+  if (row64 >= P.T) {
+    // ---- main-attention prepare: waves [0, T*Hq) of this range normalise and rotate the main
+    // Q heads; waves [T*Hq, T*Hq + T*Hkv) the K heads, stored with their V heads.
+    if (!P.main) return;
+    int64_t mw = row64 - P.T;
+    const int64_t nmq = (int64_t)P.T * P.Hq;
+    const bool is_q = mw < nmq;
+    if (!is_q) {
+      mw -= nmq;
+      if (mw >= (int64_t)P.T * P.Hkv) return;
+    }
+    const int hh = (int)(is_q ? mw % P.Hq : mw % P.Hkv);
+    const int row = (int)(is_q ? mw / P.Hq : mw / P.Hkv);
+    const int64_t rb = (int64_t)row * P.m_rs;
+    // q of head hh: pairs 128*hh .. +63 (its gate follows); K / V heads after the 2*Hq heads.
+    const uint32_t u = P.mqkv[rb + (is_q ? 128 * (int64_t)hh : 64 * ((int64_t)P.Hq * 2 + hh)) +
+                              lane];
+    const uint32_t vu = is_q ? 0u : P.mqkv[rb + 64 * ((int64_t)P.Hq * 2 + P.Hkv + hh) + lane];
+    const int64_t slot = is_q ? 0 : P.slots[row];
+    const uint32_t wpair = reinterpret_cast<const uint32_t*>(is_q ? P.mqw : P.mkw)[lane];
+    TokPos tp;
+    if (P.mrope) {
+      tp = {P.pos[(int64_t)row * 3], P.pos[(int64_t)row * 3 + 1], P.pos[(int64_t)row * 3 + 2]};
+    } else {
+      tp.t = tp.h = tp.w = P.pos[row];
+    }
+    const RopeCS cs = rope_load(P, lane, [&](int f) { return axis_pos(P, tp, f); });
+    float y0, y1;
+    rmsnorm_pair(bf16lo(u), bf16hi(u), wpair, P.m_eps, y0, y1);
+    rope_apply(lane, y0, y1, cs);
+    if (is_q) {
+      P.mq[((int64_t)row * P.Hq + hh) * 64 + lane] =
+          (f32_to_bf16(y0) & 0xFFFFu) | (f32_to_bf16(y1) << 16);
+      return;
+    }
+    if (slot < 0 || slot / P.m_P >= P.m_pages) return;
+    const int64_t base =
+        (slot / P.m_P) * P.m_ps + (int64_t)hh * P.m_hs + (slot % P.m_P) * P.m_ts;  // elements
+    if (P.main_fp8) {
+      uint16_t* c = reinterpret_cast<uint16_t*>(P.mcache);  // byte pairs
+      c[base / 2 + lane] =
+          (uint16_t)(scaled_e4m3_sat(y0, P.k_scale) | (scaled_e4m3_sat(y1, P.k_scale) << 8));
+      c[(base + kHeadDim) / 2 + lane] = (uint16_t)(scaled_e4m3_sat(bf16lo(vu), P.v_scale) |
+                                                   (scaled_e4m3_sat(bf16hi(vu), P.v_scale) << 8));
+    } else {
+      uint32_t* c = reinterpret_cast<uint32_t*>(P.mcache);  // bf16 pairs
+      c[base / 2 + lane] = (f32_to_bf16(y0) & 0xFFFFu) | (f32_to_bf16(y1) << 16);
+      c[(base + kHeadDim) / 2 + lane] = vu;
+    }
+    return;
+  }
   const int row = (int)row64;
   const ReqInfo ri = wave_find_request(P, row, lane);
   if (ri.r < 0) return;
@@ -304,8 +377,30 @@ hipError_t launch_compress(const qsa_compress_args& a, hipStream_t s) {
   P.ckv = a.ckv;
   P.cbt = a.c_block_table;
   P.q_idx = a.q_idx;
+  P.main = a.main_qkv != nullptr;
+  if (P.main) {
+    P.main_fp8 = a.main_kv_dtype == QSA_DTYPE_FP8_E4M3;
+    P.Hq = a.num_q_heads;
+    P.Hkv = a.num_kv_heads;
+    P.m_pages = a.main_num_pages;
+    P.m_P = a.main_page_size;
+    P.mqkv = reinterpret_cast<const uint32_t*>(a.main_qkv);
+    P.m_rs = a.main_qkv_row_stride / 2;
+    P.mqw = a.main_q_norm_weight;
+    P.mkw = a.main_k_norm_weight;
+    P.m_eps = (double)a.main_eps;
+    P.mq = reinterpret_cast<uint32_t*>(a.main_q);
+    P.mcache = a.main_kv_cache;
+    P.m_ps = a.main_kv_page_stride;
+    P.m_hs = a.main_kv_head_stride;
+    P.m_ts = a.main_kv_token_stride;
+    P.slots = a.main_slot_mapping;
+    P.k_scale = a.main_k_scale;
+    P.v_scale = a.main_v_scale;
+  }
 
-  const int64_t waves = (int64_t)P.T * P.Hi + P.T;
+  const int64_t waves = (int64_t)P.T * P.Hi + P.T +
+                        (P.main ? (int64_t)P.T * (P.Hq + P.Hkv) : 0);
   const int64_t blocks = (waves + 3) / 4;
   hipLaunchKernelGGL(prep_compress_kernel, dim3((unsigned)blocks), dim3(256), 0, s, P);
   hipError_t e = hipGetLastError();

@@ -57,6 +57,37 @@ qsa_status validate_compress(const qsa_compress_args* a) {
                   aligned(a->q_norm_weight, 4) && aligned(a->k_norm_weight, 4) &&
                   aligned(a->ckv, 4) && aligned(a->q_idx, 4),
               kInval);
+  if (a->main_qkv) {  // main-attention prepare
+    QSA_REQUIRE(a->num_q_heads >= 1 && a->num_q_heads <= 128 && a->num_kv_heads >= 1 &&
+                    a->num_kv_heads <= 64,
+                kNotSup);
+    QSA_REQUIRE(a->main_kv_dtype == QSA_DTYPE_BF16 || a->main_kv_dtype == QSA_DTYPE_FP8_E4M3,
+                kNotSup);
+    QSA_REQUIRE(a->main_q_norm_weight && a->main_k_norm_weight && a->main_q &&
+                    a->main_kv_cache && a->main_slot_mapping,
+                kInval);
+    QSA_REQUIRE(a->main_qkv_row_stride % 2 == 0 &&
+                    a->main_qkv_row_stride >=
+                        (int64_t)(2 * a->num_q_heads + 2 * a->num_kv_heads) * kHeadDim,
+                kInval);
+    QSA_REQUIRE(a->main_num_pages >= 1 && a->main_page_size >= 1, kInval);
+    const int64_t elt = a->main_kv_dtype == QSA_DTYPE_FP8_E4M3 ? 1 : 2;
+    QSA_REQUIRE((a->main_kv_page_stride * elt) % 16 == 0 &&
+                    (a->main_kv_head_stride * elt) % 16 == 0 &&
+                    (a->main_kv_token_stride * elt) % 16 == 0 &&
+                    a->main_kv_token_stride >= 2 * kHeadDim && a->main_kv_head_stride >= 0 &&
+                    a->main_kv_page_stride >= 0,
+                kInval);
+    if (a->main_kv_dtype == QSA_DTYPE_FP8_E4M3) {
+      QSA_REQUIRE(a->main_k_scale > 0.0f && a->main_v_scale > 0.0f && a->main_k_scale < 3.0e38f &&
+                      a->main_v_scale < 3.0e38f,
+                  kInval);
+    }
+    QSA_REQUIRE(aligned(a->main_qkv, 4) && aligned(a->main_q_norm_weight, 4) &&
+                    aligned(a->main_k_norm_weight, 4) && aligned(a->main_q, 4) &&
+                    aligned(a->main_kv_cache, 16) && aligned(a->main_slot_mapping, 8),
+                kInval);
+  }
   return QSA_OK;
 }
 

@@ -116,23 +116,69 @@ __device__ double canonical_score16(const SelectParams& P, const float* qrow,
   return s;
 }
 
-// Head-folded float32 score of compressed row j: (sum_h q_h) . k, the fold held in LDS, by a
-// group of 16 lanes; valid in lane l = 0.  Its error is that of the VALU logits.
-__device__ float folded_score16(const SelectParams& P, const float* qfold,
-                                const int32_t* cbt_row, int cw, int j, int l) {
-  float k[8];
-  key_pairs16(P, cbt_row, cw, j, l, k);
-  float x = 0.0f;
+// Head-folded float32 scores (sum_h q_h) . k of band entries, by groups of 16 lanes: lane l
+// takes dims 8l .. 8l+7 (one 16-byte bf16 or 8-byte fp8 load), a group handles entries b, b +
+// groups, ... and the loads of kFoldBatch entries are in flight together.  The summation order
+// is free: the error bound of the VALU logits holds for any order.  Writes out[b] (lane 0 of
+// the group); rows out of range (column past cw, page outside the cache) score 0.
+constexpr int kFoldBatch = 4;
+__device__ __forceinline__ void folded_scores16(const SelectParams& P, const float* qfold,
+                                                const int32_t* cbt_row, int cw,
+                                                const int32_t* band, int nb, int groups,
+                                                int grp, int l, double* out) {
+  float qf[8];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int i = l + 16 * t;
-    x += qfold[2 * i] * k[2 * t] + qfold[2 * i + 1] * k[2 * t + 1];
+  for (int d = 0; d < 8; ++d) qf[d] = qfold[8 * l + d];
+  for (int base = 0; base < nb; base += kFoldBatch * groups) {
+    uint4 raw[kFoldBatch];
+#pragma unroll
+    for (int u = 0; u < kFoldBatch; ++u) {
+      const int b = base + u * groups + grp;
+      raw[u] = make_uint4(0u, 0u, 0u, 0u);
+      if (b < nb) {
+        const int j = band[b];
+        const int col = j / P.Pc;
+        const int page = col < cw ? cbt_row[col] : -1;
+        if (page >= 0 && page < P.c_pages) {
+          const int64_t row = (int64_t)page * P.Pc + (j - col * P.Pc);
+          if (P.fp8) {
+            const uint2 v = *reinterpret_cast<const uint2*>(
+                reinterpret_cast<const uint8_t*>(P.ckv) + row * kHeadDim + 8 * l);
+            raw[u].x = v.x;
+            raw[u].y = v.y;
+          } else {
+            raw[u] = *reinterpret_cast<const uint4*>(
+                reinterpret_cast<const uint16_t*>(P.ckv) + row * kHeadDim + 8 * l);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kFoldBatch; ++u) {
+      float k[8];
+      if (P.fp8) {
+#pragma unroll
+        for (int d = 0; d < 8; ++d)
+          k[d] = e4m3_to_f32_exact(((d < 4 ? raw[u].x : raw[u].y) >> (8 * (d & 3))) & 0xFFu);
+      } else {
+        const uint32_t w4[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          k[2 * d] = bf16lo(w4[d]);
+          k[2 * d + 1] = bf16hi(w4[d]);
+        }
+      }
+      float x = 0.0f;
+#pragma unroll
+      for (int d = 0; d < 8; ++d) x += qf[d] * k[d];
+      x = x + row_down<8>(x);
+      x = x + row_down<4>(x);
+      x = x + row_down<2>(x);
+      x = x + row_down<1>(x);
+      const int b = base + u * groups + grp;
+      if (l == 0 && b < nb) out[b] = x;
+    }
   }
-  x = x + row_down<8>(x);
-  x = x + row_down<4>(x);
-  x = x + row_down<2>(x);
-  x = x + row_down<1>(x);
-  return x;
 }
 
 // Top-k kernel configurations: NT threads holding E scores each; the threshold's radix select
@@ -439,11 +485,7 @@ __global__ __launch_bounds__(C::NT) void topk_kernel(SelectParams P) {
       qfold[d] = f;
     }
     lds_barrier();
-    for (int b0 = 0; b0 < nb; b0 += groups) {
-      const int b = b0 + grp;
-      const float fs = folded_score16(P, qfold, cbt_row, cw, b < nb ? bidx[b] : -1, l16);
-      if (l16 == 0 && b < nb) bscore[b] = fs;
-    }
+    folded_scores16(P, qfold, cbt_row, cw, bidx, nb, groups, grp, l16, bscore);
     if (in_lds) lds_barrier(); else __syncthreads();
     // The need-th largest folded score of the band (ranks made unique by position).
     for (int b = tid; b < nb; b += NT) {

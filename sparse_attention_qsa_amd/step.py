@@ -1,6 +1,10 @@
 """One step of the QSA hot path on a workload: qsa_compress -> qsa_index_logits_topk ->
 qsa_sparse_gqa, with outputs and workspaces allocated once and the C argument blocks built
-once, so that repeated steps cost three C calls."""
+once, so that repeated steps cost three C calls.
+
+With `main` (the inputs of the main-attention prepare, see workloads.main_prepare_inputs) the
+compress call also prepares the main Q and writes the step's K/V into the main cache, and the
+attention then runs on that Q with the output gate read in place from the packed projection."""
 
 from __future__ import annotations
 
@@ -12,7 +16,7 @@ from . import binding as B
 
 
 class QsaStep:
-    def __init__(self, wl, num_splits: int = 0, gate: bool = True):
+    def __init__(self, wl, num_splits: int = 0, gate: bool = True, main: dict | None = None):
         dev = wl.q.device
         T = wl.num_tokens
         idx_dtype = torch.uint8 if wl.index_dtype == "fp8" else torch.bfloat16
@@ -27,7 +31,12 @@ class QsaStep:
             k_norm_weight=wl.k_norm_w, eps=wl.eps, ring=wl.ring, ring_page=wl.ring_page,
             ckv=wl.ckv, c_block_table=wl.c_block_table, q_idx=self.q_idx,
             num_index_heads=wl.index_heads, compress_ratio=wl.compress_ratio,
-            index_dtype=wl.index_dtype, ring_pos=wl.ring_pos, mrope_section=wl.mrope_section)
+            index_dtype=wl.index_dtype, ring_pos=wl.ring_pos, mrope_section=wl.mrope_section,
+            main=main)
+        q, g = wl.q, wl.gate
+        if main is not None:
+            q = main["main_q"]
+            g = main["main_qkv"][:, :2 * wl.q_heads * 128].view(T, wl.q_heads, 256)[:, :, 128:]
         self.t_args = B.topk_args(
             query_start_loc=wl.query_start_loc, seq_lens=wl.seq_lens, q_idx=self.q_idx,
             ckv=wl.ckv, c_block_table=wl.c_block_table, packed=self.packed,
@@ -36,9 +45,9 @@ class QsaStep:
             max_seq_len=wl.max_seq_len, num_decode_requests=wl.num_decode_requests,
             decode_query_len=wl.decode_query_len)
         self.g_args = B.gqa_args(
-            q=wl.q, kv_cache=wl.kv_cache, block_table=wl.block_table,
+            q=q, kv_cache=wl.kv_cache, block_table=wl.block_table,
             token_to_req=wl.token_to_req, packed=self.packed, out=self.out,
-            gate=wl.gate if gate else None, num_splits=num_splits,
+            gate=g if gate else None, num_splits=num_splits,
             k_scale=getattr(wl, "k_scale", 1.0), v_scale=getattr(wl, "v_scale", 1.0))
         L = B.lib()
         t_ws = int(L.qsa_index_logits_topk_workspace_size(C.byref(self.t_args)))

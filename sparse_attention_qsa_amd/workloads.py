@@ -300,3 +300,35 @@ def make_workload(name: str, device="cpu", seed: int | None = None, **overrides)
         gate=_normal_bf16((T, Hq, HEAD_DIM), device, seed, 9),
         kv_dtype=kv_dtype, k_scale=k_scale, v_scale=v_scale,
     )
+
+
+def main_prepare_inputs(wl: Workload, seed: int | None = None) -> dict:
+    """Inputs of the main-attention prepare for a workload's rows (the keyword block of the
+    binding's `main` argument): the packed main projection [T, (2Hq + 2Hkv)*128] ~ N(0, 1)
+    (per Q head its q then its gate, then the K and V heads), norm weights ~ N(0, 0.1^2), and
+    the slot of each row's token in the workload's main cache (page from its block table,
+    offset p % P).  Draws numbers only; the output buffer main_q is allocated here."""
+    seed = CONFIG_SEEDS.get(wl.name, 1000) if seed is None else seed
+    device = wl.q_proj.device
+    T, Hq, Hkv = wl.num_tokens, wl.q_heads, wl.kv_heads
+    P = wl.kv_cache.shape[2]
+    qsl = wl.query_start_loc.cpu().numpy().astype(np.int64)
+    table = wl.block_table.cpu().numpy().astype(np.int64)
+    slots = np.empty(T, dtype=np.int64)
+    for r in range(wl.num_requests):
+        n = qsl[r + 1] - qsl[r]
+        p = np.arange(wl.seq_lens_host[r] - n, wl.seq_lens_host[r])
+        slots[qsl[r]:qsl[r + 1]] = table[r, p // P] * P + p % P
+    out = dict(
+        main_qkv=_normal_bf16((T, (2 * Hq + 2 * Hkv) * HEAD_DIM), device, seed, 10),
+        num_q_heads=Hq, num_kv_heads=Hkv,
+        main_q_norm_weight=_normal_bf16((HEAD_DIM,), device, seed, 11, std=0.1),
+        main_k_norm_weight=_normal_bf16((HEAD_DIM,), device, seed, 12, std=0.1),
+        main_eps=1e-6,
+        main_q=torch.empty((T, Hq, HEAD_DIM), dtype=torch.bfloat16, device=device),
+        main_kv_cache=wl.kv_cache,
+        main_slot_mapping=torch.from_numpy(slots).to(device),
+    )
+    if wl.kv_dtype == "fp8":
+        out.update(main_k_scale=wl.k_scale, main_v_scale=wl.v_scale)
+    return out

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(B.EXPORTED)
-    assert lib.qsa_abi_version() == 2
+    assert lib.qsa_abi_version() == 3
     assert lib.qsa_status_string(3) == b"QSA_ERR_WORKSPACE_TOO_SMALL"
 
 
@@ -133,3 +133,45 @@ def test_invalid_calls_are_rejected_before_any_launch():
     c.head_dim, c.rotary_dim, c.num_index_heads, c.compress_ratio = 128, 64, 8, 4
     assert lib.qsa_compress(C.byref(c), None) == INVAL       # NULL tensors
     assert lib.qsa_compress(None, None) == INVAL
+
+
+def _compress(**over):
+    a = B.CompressArgs(num_tokens=64, num_requests=64, query_start_loc=FAKE, seq_lens=FAKE,
+                       max_query_len=1, q_proj=FAKE, q_proj_row_stride=8 * 128, k_proj=FAKE,
+                       k_proj_row_stride=128, positions=FAKE, cos_sin=FAKE, max_position=40000,
+                       q_norm_weight=FAKE, k_norm_weight=FAKE, eps=1e-6, ring=FAKE,
+                       ring_page=FAKE, ring_pages=64, ring_size=16, ckv=FAKE,
+                       c_block_table=FAKE, c_block_table_stride=512, c_block_table_width=512,
+                       c_page_size=16, c_pages=32768, num_index_heads=8, head_dim=128,
+                       rotary_dim=64, compress_ratio=4, index_dtype=0, q_idx=FAKE,
+                       main_qkv=FAKE, main_qkv_row_stride=(2 * 16 + 2 * 2) * 128,
+                       num_q_heads=16, num_kv_heads=2, main_q_norm_weight=FAKE,
+                       main_k_norm_weight=FAKE, main_eps=1e-6, main_q=FAKE,
+                       main_kv_cache=FAKE, main_kv_page_stride=2 * 16 * 256,
+                       main_kv_head_stride=16 * 256, main_kv_token_stride=256,
+                       main_num_pages=8192, main_page_size=16, main_slot_mapping=FAKE,
+                       main_kv_dtype=0, main_k_scale=1.0, main_v_scale=1.0)
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_invalid_main_prepare_arguments_are_rejected_before_any_launch():
+    lib = B.lib()
+    INVAL, NOTSUP = 1, 2
+    call = lambda **o: lib.qsa_compress(C.byref(_compress(**o)), None)  # noqa: E731
+    assert call(num_q_heads=0) == NOTSUP
+    assert call(num_kv_heads=65) == NOTSUP
+    assert call(main_kv_dtype=5) == NOTSUP
+    assert call(main_q=None) == INVAL
+    assert call(main_slot_mapping=None) == INVAL
+    assert call(main_qkv_row_stride=(2 * 16 + 2 * 2) * 128 - 2) == INVAL
+    assert call(main_qkv_row_stride=(2 * 16 + 2 * 2) * 128 + 1) == INVAL
+    assert call(main_kv_token_stride=200) == INVAL
+    assert call(main_kv_token_stride=260) == INVAL           # 520 bytes: not a 16-byte multiple
+    assert call(main_page_size=0) == INVAL
+    assert call(main_kv_dtype=1, main_k_scale=0.0) == INVAL
+    assert call(main_kv_dtype=1, main_v_scale=float("nan")) == INVAL
+    assert call(main_kv_dtype=1, main_kv_token_stride=264) == INVAL
+    assert call(main_slot_mapping=FAKE + 4) == INVAL
+    assert call(main_kv_cache=FAKE + 8) == INVAL
