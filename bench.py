@@ -45,6 +45,10 @@ def parse():
     p.add_argument("--workload", default="decode_32k")
     p.add_argument("--rotate", type=int, default=4, help="input copies cycled through")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--main-prepare", action="store_true",
+                   help="also run the main-attention prepare inside qsa_compress (the attention "
+                        "then uses the prepared Q and reads the gate in place) and report its "
+                        "marginal cost")
     p.add_argument("--profile-only", action="store_true",
                    help="warm up and run the timed steps only (for rocprofv3)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -229,7 +233,7 @@ def main():
     import torch
 
     from sparse_attention_qsa_amd.step import QsaStep
-    from sparse_attention_qsa_amd.workloads import make_workload
+    from sparse_attention_qsa_amd.workloads import main_prepare_inputs, make_workload
 
     dev = "cuda:0"
     wl0 = make_workload(args.workload, device=dev)
@@ -240,7 +244,8 @@ def main():
             if isinstance(v, torch.Tensor):
                 setattr(host, k, v.cpu())
     wls = [wl0] + [clone_workload(wl0) for _ in range(max(0, args.rotate - 1))]
-    steps = [QsaStep(w) for w in wls]
+    mains = [main_prepare_inputs(w) if args.main_prepare else None for w in wls]
+    steps = [QsaStep(w, main=m) for w, m in zip(wls, mains)]
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
@@ -277,6 +282,30 @@ def main():
         torch.cuda.synchronize()
         per_call[call] = sum(a.elapsed_time(b) for a, b in evs) / len(evs) * 1e3   # us
 
+    main_leg = None
+    if args.main_prepare:
+        # The prepare's marginal cost: the same compress call without it.
+        plain = [QsaStep(w) for w in wls]
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(evs):
+            a.record(stream)
+            plain[i % len(plain)].compress(stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        us_plain = sum(a.elapsed_time(b) for a, b in evs) / len(evs) * 1e3
+        elt = 1 if wl0.kv_dtype == "fp8" else 2
+        Hq, Hkv, T = wl0.q_heads, wl0.kv_heads, wl0.num_tokens
+        mbytes = T * (Hq * 128 * 2 + 2 * Hkv * 128 * 2          # q heads, K, V read
+                      + Hq * 128 * 2 + 2 * Hkv * 128 * elt + 8)  # main Q, cache rows written
+        marg = per_call["qsa_compress"] - us_plain
+        main_leg = {"us_compress_with_main": round(per_call["qsa_compress"], 2),
+                    "us_compress_without": round(us_plain, 2), "us_marginal": round(marg, 2),
+                    "algorithmic_bytes": int(mbytes),
+                    "gbps_over_call": round(mbytes / (per_call["qsa_compress"] * 1e-6) / 1e9, 1)}
+        del plain
+
     alg, kv_tokens = algorithmic_bytes(wl0, steps[0].packed)
     step_bytes = sum(alg.values())
     rows_per_s = wl0.num_tokens / (ms_step * 1e-3)
@@ -304,6 +333,7 @@ def main():
                    "q_heads": wl0.q_heads, "kv_heads": wl0.kv_heads, "head_dim": 128,
                    "page_size": 16, "kv_dtype": getattr(wl0, "kv_dtype", "bf16"),
                    "input_copies_rotated": len(steps),
+                   "main_prepare": bool(args.main_prepare),
                    "gqa_splits": steps[0].num_splits},
         "hbm_gbps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
         "hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -314,6 +344,8 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
     }
+    if main_leg is not None:
+        out["main_prepare"] = main_leg
     if host is not None:
         del steps, wls
         torch.cuda.empty_cache()

@@ -175,80 +175,213 @@ __device__ __forceinline__ ReqInfo wave_find_request(const CompressParams& P, in
   return ri;
 }
 
-// Waves [0, T*Hi): indexer Q vectors.  Waves [T*Hi, T*Hi + T): the group (if any) completed by
+// ---- vectors on 16-lane rows.  Row r = lane / 16 of a wave holds one 128-dim vector; its lane
+// l = lane % 16 holds the dim pairs (2i, 2i+1) for i = l, l+16, l+32, l+48 (index k of the
+// pair arrays below is i = l + 16k).  The canonical halving sum is then in-lane for its
+// strides 32 and 16 (in pairs) and a DPP shift within the row for 8, 4, 2, 1, and the rotation
+// partners (d, d+32), d < 32, sit in the same lane: no cross-row data movement at all.
+
+// Value of lane l + N of the same 16-lane row (DPP row_shl); past the row's end: 0 (only lane
+// 0's result is used).
+template <int N>
+__device__ __forceinline__ double row_down_f64(double x) {
+  const uint64_t u = (uint64_t)__double_as_longlong(x);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, 0x100 + N, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), 0x100 + N, 0xF, 0xF,
+                                             false);
+  return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+
+// Lane 16r's double, for every lane of row r.
+__device__ __forceinline__ double row_broadcast_f64(double x, int lane) {
+  const uint64_t u = (uint64_t)__double_as_longlong(x);
+  const int lo = (int)(uint32_t)u, hi = (int)(uint32_t)(u >> 32);
+  const int r = lane >> 4;
+  int blo = __builtin_amdgcn_readlane(lo, 0), bhi = __builtin_amdgcn_readlane(hi, 0);
+  const int lo1 = __builtin_amdgcn_readlane(lo, 16), hi1 = __builtin_amdgcn_readlane(hi, 16);
+  const int lo2 = __builtin_amdgcn_readlane(lo, 32), hi2 = __builtin_amdgcn_readlane(hi, 32);
+  const int lo3 = __builtin_amdgcn_readlane(lo, 48), hi3 = __builtin_amdgcn_readlane(hi, 48);
+  blo = r == 1 ? lo1 : (r == 2 ? lo2 : (r == 3 ? lo3 : blo));
+  bhi = r == 1 ? hi1 : (r == 2 ? hi2 : (r == 3 ? hi3 : bhi));
+  return __longlong_as_double((long long)(((uint64_t)(uint32_t)bhi << 32) | (uint32_t)blo));
+}
+
+// Gemma RMSNorm of a row vector (x: this lane's 8 values, pair k in x[2k], x[2k+1]) with the
+// weight pairs wp[k], rounded float64 -> float32 -> bf16 (values returned as floats).
+__device__ __forceinline__ void rmsnorm_row(const float (&x)[8], const uint32_t (&wp)[4],
+                                            double eps, int lane, float (&y)[8]) {
+  double v[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    v[k] = (double)x[2 * k] * (double)x[2 * k] + (double)x[2 * k + 1] * (double)x[2 * k + 1];
+  double t = (v[0] + v[2]) + (v[1] + v[3]);
+  t = t + row_down_f64<8>(t);
+  t = t + row_down_f64<4>(t);
+  t = t + row_down_f64<2>(t);
+  t = t + row_down_f64<1>(t);
+  t = row_broadcast_f64(t, lane);
+  const double var = t / 128.0 + eps;
+  const double inv = 1.0 / sqrt(var);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const double w0 = bf16lo(wp[k]), w1 = bf16hi(wp[k]);
+    y[2 * k] = bf16_to_f32(f64_to_bf16(((double)x[2 * k] * inv) * (1.0 + w0)));
+    y[2 * k + 1] = bf16_to_f32(f64_to_bf16(((double)x[2 * k + 1] * inv) * (1.0 + w1)));
+  }
+}
+
+// cos / sin of frequencies 2l and 2l+1 (the rotations of dims 2l, 2l+1 with 2l+32, 2l+33).
+template <typename PosFn>
+__device__ __forceinline__ RopeCS rope_load_row(const CompressParams& P, int l, PosFn posf) {
+  const int f0 = 2 * l;
+  const int64_t q0 = posf(f0), q1 = posf(f0 + 1);
+  RopeCS cs;
+  cs.c0 = P.cos_sin[q0 * 64 + f0];
+  cs.s0 = P.cos_sin[q0 * 64 + 32 + f0];
+  cs.c1 = P.cos_sin[q1 * 64 + f0 + 1];
+  cs.s1 = P.cos_sin[q1 * 64 + 32 + f0 + 1];
+  return cs;
+}
+
+// NeoX rotation in-lane: pair 0 (dims 2l, 2l+1) with pair 1 (dims 2l+32, 2l+33).
+__device__ __forceinline__ void rope_row(float (&y)[8], const RopeCS& cs) {
+  const double a0 = y[0], a1 = y[1], b0 = y[2], b1 = y[3];
+  y[0] = bf16_to_f32(f64_to_bf16(a0 * cs.c0 - b0 * cs.s0));
+  y[2] = bf16_to_f32(f64_to_bf16(b0 * cs.c0 + a0 * cs.s0));
+  y[1] = bf16_to_f32(f64_to_bf16(a1 * cs.c1 - b1 * cs.s1));
+  y[3] = bf16_to_f32(f64_to_bf16(b1 * cs.c1 + a1 * cs.s1));
+}
+
+__device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
+  return (f32_to_bf16(a) & 0xFFFFu) | (f32_to_bf16(b) << 16);
+}
+
+// The rotary positions of `row`.
+__device__ __forceinline__ TokPos row_pos(const CompressParams& P, int row) {
+  TokPos tp;
+  if (P.mrope) {
+    tp = {P.pos[(int64_t)row * 3], P.pos[(int64_t)row * 3 + 1], P.pos[(int64_t)row * 3 + 2]};
+  } else {
+    tp.t = tp.h = tp.w = P.pos[row];
+  }
+  return tp;
+}
+
+// One Q-type vector per 16-lane row: RMSNorm (weights wt) -> RoPE at the row's positions.
+// Loads are clamped to vector n-1 for rows past the end (their results are not stored).
+template <typename SrcFn>
+__device__ __forceinline__ void norm_rope_row(const CompressParams& P, int64_t v, int64_t n,
+                                              int heads, const uint16_t* wt, double eps,
+                                              int lane, SrcFn src, float (&y)[8], int& row) {
+  const int l = lane & 15;
+  const int64_t vc = v < n ? v : n - 1;
+  row = (int)(vc / heads);
+  const uint32_t* s = src(row, (int)(vc % heads));
+  uint32_t u[4], wp[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    u[k] = s[l + 16 * k];
+    wp[k] = reinterpret_cast<const uint32_t*>(wt)[l + 16 * k];
+  }
+  const TokPos tp = row_pos(P, row);
+  const RopeCS cs = rope_load_row(P, l, [&](int f) { return axis_pos(P, tp, f); });
+  float x[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    x[2 * k] = bf16lo(u[k]);
+    x[2 * k + 1] = bf16hi(u[k]);
+  }
+  rmsnorm_row(x, wp, eps, lane, y);
+  rope_row(y, cs);
+}
+
+// Waves [0, ceil(T*Hi/4)): indexer Q vectors, four per wave.  Waves [T*Hi, T*Hi + T): the group (if any) completed by
 // row (wave - T*Hi), and -- when fuse_ring -- that row's ring write.  Each wave issues every
 // load its result needs as early as its addresses are known: the rotation's cos / sin go out
 // with (or right after) the positions and land while the norm is computed.
 __global__ __launch_bounds__(256) void prep_compress_kernel(CompressParams P) {
-  const int lane = threadIdx.x & 63;
+  const int lane = threadIdx.x & 63, l = lane & 15;
   const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-  const int64_t nq = (int64_t)P.T * P.Hi;
-  if (wave < nq) {
-    const int row = (int)(wave / P.Hi), h = (int)(wave % P.Hi);
-    const uint32_t u = P.q_proj[(int64_t)row * P.q_rs + h * 64 + lane];
-    const uint32_t wpair = reinterpret_cast<const uint32_t*>(P.qw)[lane];
-    TokPos tp;
-    if (P.mrope) {
-      tp = {P.pos[(int64_t)row * 3], P.pos[(int64_t)row * 3 + 1], P.pos[(int64_t)row * 3 + 2]};
-    } else {
-      tp.t = tp.h = tp.w = P.pos[row];
+  const int64_t nq = (int64_t)P.T * P.Hi, nqw = (nq + 3) / 4;
+  if (wave < nqw) {
+    const int64_t v = 4 * wave + (lane >> 4);
+    float y[8];
+    int row;
+    norm_rope_row(P, v, nq, P.Hi, P.qw, P.eps, lane,
+                  [&](int rw, int h) { return P.q_proj + (int64_t)rw * P.q_rs + h * 64; }, y,
+                  row);
+    if (v < nq) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if (P.fp8) {
+          reinterpret_cast<uint16_t*>(P.q_idx)[v * 64 + l + 16 * k] =
+              (uint16_t)(f32_to_e4m3(y[2 * k]) | (f32_to_e4m3(y[2 * k + 1]) << 8));
+        } else {
+          reinterpret_cast<uint32_t*>(P.q_idx)[v * 64 + l + 16 * k] =
+              bf16_pair(y[2 * k], y[2 * k + 1]);
+        }
+      }
     }
-    const RopeCS cs = rope_load(P, lane, [&](int f) { return axis_pos(P, tp, f); });
-    float y0, y1;
-    rmsnorm_pair(bf16lo(u), bf16hi(u), wpair, P.eps, y0, y1);
-    rope_apply(lane, y0, y1, cs);
-    store_index_pair(P, P.q_idx, wave, lane, y0, y1);
     return;
   }
-  const int64_t row64 = wave - nq;
+  const int64_t row64 = wave - nqw;
   if (row64 >= P.T) {
-    // ---- main-attention prepare: waves [0, T*Hq) of this range normalise and rotate the main
-    // Q heads; waves [T*Hq, T*Hq + T*Hkv) the K heads, stored with their V heads.
+    // ---- main-attention prepare: waves [0, ceil(T*Hq/4)) of this range normalise and rotate
+    // the main Q heads, the next ceil(T*Hkv/4) the K heads, stored with their V heads; four
+    // vectors per wave.
     if (!P.main) return;
     int64_t mw = row64 - P.T;
-    const int64_t nmq = (int64_t)P.T * P.Hq;
-    const bool is_q = mw < nmq;
-    if (!is_q) {
-      mw -= nmq;
-      if (mw >= (int64_t)P.T * P.Hkv) return;
-    }
-    const int hh = (int)(is_q ? mw % P.Hq : mw % P.Hkv);
-    const int row = (int)(is_q ? mw / P.Hq : mw / P.Hkv);
-    const int64_t rb = (int64_t)row * P.m_rs;
-    // q of head hh: pairs 128*hh .. +63 (its gate follows); K / V heads after the 2*Hq heads.
-    const uint32_t u = P.mqkv[rb + (is_q ? 128 * (int64_t)hh : 64 * ((int64_t)P.Hq * 2 + hh)) +
-                              lane];
-    const uint32_t vu = is_q ? 0u : P.mqkv[rb + 64 * ((int64_t)P.Hq * 2 + P.Hkv + hh) + lane];
-    const int64_t slot = is_q ? 0 : P.slots[row];
-    const uint32_t wpair = reinterpret_cast<const uint32_t*>(is_q ? P.mqw : P.mkw)[lane];
-    TokPos tp;
-    if (P.mrope) {
-      tp = {P.pos[(int64_t)row * 3], P.pos[(int64_t)row * 3 + 1], P.pos[(int64_t)row * 3 + 2]};
-    } else {
-      tp.t = tp.h = tp.w = P.pos[row];
-    }
-    const RopeCS cs = rope_load(P, lane, [&](int f) { return axis_pos(P, tp, f); });
-    float y0, y1;
-    rmsnorm_pair(bf16lo(u), bf16hi(u), wpair, P.m_eps, y0, y1);
-    rope_apply(lane, y0, y1, cs);
-    if (is_q) {
-      P.mq[((int64_t)row * P.Hq + hh) * 64 + lane] =
-          (f32_to_bf16(y0) & 0xFFFFu) | (f32_to_bf16(y1) << 16);
+    const int64_t nmq = (int64_t)P.T * P.Hq, nmqw = (nmq + 3) / 4;
+    const int64_t nkv = (int64_t)P.T * P.Hkv;
+    float y[8];
+    int row;
+    if (mw < nmqw) {
+      const int64_t v = 4 * mw + (lane >> 4);
+      // q of head h: pairs 128h .. 128h+63 of the row (its gate follows).
+      norm_rope_row(P, v, nmq, P.Hq, P.mqw, P.m_eps, lane,
+                    [&](int rw, int h) { return P.mqkv + (int64_t)rw * P.m_rs + 128 * h; }, y,
+                    row);
+      if (v < nmq) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) P.mq[v * 64 + l + 16 * k] = bf16_pair(y[2 * k], y[2 * k + 1]);
+      }
       return;
     }
-    if (slot < 0 || slot / P.m_P >= P.m_pages) return;
+    mw -= nmqw;
+    if (mw >= (nkv + 3) / 4) return;
+    const int64_t v = 4 * mw + (lane >> 4);
+    const int64_t vc = v < nkv ? v : nkv - 1;
+    const int hh = (int)(vc % P.Hkv);
+    // K head hh: pairs 64 (2Hq + hh) ..; its V head: 64 (2Hq + Hkv + hh) ..
+    uint32_t vu[4];
+    {
+      const uint32_t* vs = P.mqkv + (int64_t)(vc / P.Hkv) * P.m_rs + 64 * ((int64_t)P.Hq * 2 + P.Hkv + hh);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) vu[k] = vs[l + 16 * k];
+    }
+    const int64_t slot = P.slots[vc / P.Hkv];
+    norm_rope_row(P, v, nkv, P.Hkv, P.mkw, P.m_eps, lane,
+                  [&](int rw, int h) {
+                    return P.mqkv + (int64_t)rw * P.m_rs + 64 * ((int64_t)P.Hq * 2 + h);
+                  },
+                  y, row);
+    if (v >= nkv || slot < 0 || slot / P.m_P >= P.m_pages) return;
     const int64_t base =
         (slot / P.m_P) * P.m_ps + (int64_t)hh * P.m_hs + (slot % P.m_P) * P.m_ts;  // elements
-    if (P.main_fp8) {
-      uint16_t* c = reinterpret_cast<uint16_t*>(P.mcache);  // byte pairs
-      c[base / 2 + lane] =
-          (uint16_t)(scaled_e4m3_sat(y0, P.k_scale) | (scaled_e4m3_sat(y1, P.k_scale) << 8));
-      c[(base + kHeadDim) / 2 + lane] = (uint16_t)(scaled_e4m3_sat(bf16lo(vu), P.v_scale) |
-                                                   (scaled_e4m3_sat(bf16hi(vu), P.v_scale) << 8));
-    } else {
-      uint32_t* c = reinterpret_cast<uint32_t*>(P.mcache);  // bf16 pairs
-      c[base / 2 + lane] = (f32_to_bf16(y0) & 0xFFFFu) | (f32_to_bf16(y1) << 16);
-      c[(base + kHeadDim) / 2 + lane] = vu;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int64_t e = base + 2 * (l + 16 * k);  // element of dim pair l + 16k
+      if (P.main_fp8) {
+        uint16_t* c = reinterpret_cast<uint16_t*>(P.mcache);  // byte pairs
+        c[e / 2] = (uint16_t)(scaled_e4m3_sat(y[2 * k], P.k_scale) |
+                              (scaled_e4m3_sat(y[2 * k + 1], P.k_scale) << 8));
+        c[(e + kHeadDim) / 2] = (uint16_t)(scaled_e4m3_sat(bf16lo(vu[k]), P.v_scale) |
+                                           (scaled_e4m3_sat(bf16hi(vu[k]), P.v_scale) << 8));
+      } else {
+        uint32_t* c = reinterpret_cast<uint32_t*>(P.mcache);  // bf16 pairs
+        c[e / 2] = bf16_pair(y[2 * k], y[2 * k + 1]);
+        c[(e + kHeadDim) / 2] = vu[k];
+      }
     }
     return;
   }
@@ -399,8 +532,9 @@ hipError_t launch_compress(const qsa_compress_args& a, hipStream_t s) {
     P.v_scale = a.main_v_scale;
   }
 
-  const int64_t waves = (int64_t)P.T * P.Hi + P.T +
-                        (P.main ? (int64_t)P.T * (P.Hq + P.Hkv) : 0);
+  const int64_t waves = ((int64_t)P.T * P.Hi + 3) / 4 + P.T +
+                        (P.main ? ((int64_t)P.T * P.Hq + 3) / 4 + ((int64_t)P.T * P.Hkv + 3) / 4
+                                : 0);
   const int64_t blocks = (waves + 3) / 4;
   hipLaunchKernelGGL(prep_compress_kernel, dim3((unsigned)blocks), dim3(256), 0, s, P);
   hipError_t e = hipGetLastError();
