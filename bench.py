@@ -106,14 +106,15 @@ def algorithmic_bytes(wl, packed):
             "qsa_sparse_gqa": b_gqa}, int(np.int64(kv_tokens))
 
 
-def traffic_record(call):
+def traffic_record(call, workload):
     """Per-launch HBM bytes measured by rocprofv3 counters for `call`, if the committed record
-    was taken on the current kernel sources (else None)."""
+    was taken on this workload and on the current kernel sources (else None)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
-    rec = json.load(open(path)).get(call)
-    if not rec:
+    table = json.load(open(path))
+    rec = table.get(call)
+    if not rec or table.get("_workload") != workload:
         return None
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[call]:
@@ -139,7 +140,7 @@ def _counter_rows(d):
     return rows
 
 
-def write_traffic(fetch_dir, write_dir, cal_dir, cal_mib):
+def write_traffic(fetch_dir, write_dir, cal_dir, cal_mib, workload):
     """profiles/traffic.json: HBM bytes per launch of each call, from FETCH_SIZE / WRITE_SIZE
     (KiB per dispatch), each scaled by the factor that maps the same counter on a plain copy of
     cal_mib MiB to its true size.  A call's launch sums its kernels' per-dispatch averages."""
@@ -169,7 +170,7 @@ def write_traffic(fetch_dir, write_dir, cal_dir, cal_mib):
     out = {"_note": "HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (KiB "
                     "per dispatch), scaled by the factor that maps each counter on a plain "
                     f"{cal_mib} MiB device copy to its true size",
-           "_calibration": cal}
+           "_calibration": cal, "_workload": workload}
     for call, kernels in CALL_KERNELS.items():
         fb = sum(v for k, v in fetch.items() if any(n in k for n in kernels)) * 1024.0
         wb = sum(v for k, v in write.items() if any(n in k for n in kernels)) * 1024.0
@@ -221,7 +222,8 @@ def cpu_baseline(host_inputs, wl_meta, min_seconds=10.0):
 def main():
     args = parse()
     if args.write_traffic:
-        write_traffic(*args.write_traffic, cal_mib=args.copy_calibration or 1024)
+        write_traffic(*args.write_traffic, cal_mib=args.copy_calibration or 1024,
+                      workload=args.workload)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported "
@@ -311,7 +313,7 @@ def main():
     rows_per_s = wl0.num_tokens / (ms_step * 1e-3)
     dom = max(per_call, key=per_call.get)
     achieved = alg[dom] / (per_call[dom] * 1e-6) / 1e9
-    traffic = traffic_record(dom)
+    traffic = traffic_record(dom, wl0.name)
 
     out = {
         "metric": METRIC,
