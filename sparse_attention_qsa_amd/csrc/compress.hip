@@ -5,11 +5,11 @@
 // and qsa_compress_groups_with_ratio / qsa_store_cache_rows (page
 // "vllm.models.qwen4_exp.nvidia.ops.qsa"); optionally, in the same launch, the main-attention
 // prepare of the fused qsa_prepare call (Qwen4ExpQSAAttention: main Q/K norm and RoPE, K/V
-// written to the main cache).  One wavefront owns one 128-dim vector: lane l holds
-// dims 2l and 2l+1, which is also the layout of the canonical halving sum (adjacent pairs first,
-// then the upper half of the lanes onto the lower half), so every value is bit-identical to the
-// float64 chain the oracle defines.  The work is a few MB at most per step: the kernels are
-// latency-bound and kept simple.
+// written to the main cache).  Both vector layouts follow the canonical float64 chain the
+// oracle defines (halving sums, rotation pairs), so every value is bit-identical to it: a
+// pooled group owns a wavefront (lane l holds dims 2l and 2l+1; the halving sum folds the upper
+// half of the lanes onto the lower half), and the Q and K vectors, which are many at prefill
+// sizes, take a 16-lane row each (no cross-lane traffic beyond DPP shifts).
 #include "qsa_internal.h"
 
 #pragma clang fp contract(off)
@@ -444,8 +444,9 @@ __global__ __launch_bounds__(256) void prep_compress_kernel(CompressParams P) {
         }
       }
     }
-    const float m0f = bf16_to_f32(f64_to_bf16(a0 / (double)P.c));
-    const float m1f = bf16_to_f32(f64_to_bf16(a1 / (double)P.c));
+    const double inv_c = 1.0 / (double)P.c;  // c is a power of two: exact, as is the product
+    const float m0f = bf16_to_f32(f64_to_bf16(a0 * inv_c));
+    const float m1f = bf16_to_f32(f64_to_bf16(a1 * inv_c));
     float y0, y1;
     rmsnorm_pair(m0f, m1f, reinterpret_cast<const uint32_t*>(P.kw)[lane], P.eps, y0, y1);
     rope_apply(lane, y0, y1, cs);
