@@ -9,8 +9,9 @@ the inputs are rotated step by step so that a step never finds its ~270 MB worki
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
-Prints one JSON line: rows/s for the whole step, the step's algorithmic HBM GB/s, per-call
-times, the roofline of the dominant call, and the CPU oracle timed on the host beside it.
+Prints one JSON line: rows/s for the whole step, the step's algorithmic HBM GB/s, per-call and
+per-kernel times (each kernel alone, through the library call that launches only it), the
+roofline of the dominant kernel, and the CPU oracle timed on the host beside it.
 """
 
 from __future__ import annotations
@@ -29,11 +30,14 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
 METRIC = "decode rows/sec + achieved HBM GB/s, QSA indexer+sparse GQA at 32k ctx"
-KERNEL_SOURCES = {   # the sources of the kernels a traffic record measured (decode workload)
-    "qsa_compress": ["qsa_internal.h", "compress.hip"],
-    "qsa_index_logits_topk": ["qsa_internal.h", "select.h", "select.hip", "logits.hip",
-                              "topk.hip"],
-    "qsa_sparse_gqa": ["qsa_internal.h", "gqa.hip"],
+# The kernels timed one by one (each through the call that launches only it), with the sources
+# they are built from (a traffic record applies only while these are unchanged).
+KERNELS = {
+    "prep_compress_kernel": ("compress", ["qsa_internal.h", "compress.hip"]),
+    "logits_valu_kernel": ("logits", ["qsa_internal.h", "select.h", "select.hip", "logits.hip"]),
+    "topk_kernel": ("block_topk", ["qsa_internal.h", "select.h", "select.hip", "topk.hip"]),
+    "gqa_partial_kernel": ("gqa_partial", ["qsa_internal.h", "gqa.hip"]),
+    "gqa_merge_kernel": ("gqa_merge", ["qsa_internal.h", "gqa.hip"]),
 }
 
 
@@ -102,31 +106,32 @@ def algorithmic_bytes(wl, packed):
     b_gqa = (kv_tokens * Hkv * kv_row                       # K and V rows of selected tokens
              + T * Hq * 128 * 2 * 3                         # q, gate read; out written
              + T * (W + 1) * 4)                             # packed read
-    return {"qsa_compress": b_compress, "qsa_index_logits_topk": b_logits,
-            "qsa_sparse_gqa": b_gqa}, int(np.int64(kv_tokens))
+    per_call = {"qsa_compress": b_compress, "qsa_index_logits_topk": b_logits,
+                "qsa_sparse_gqa": b_gqa}
+    b_packed = T * (W + 1) * 4
+    b_qgo = T * Hq * 128 * 2
+    per_kernel = {"prep_compress_kernel": b_compress,
+                  "logits_valu_kernel": b_logits - b_packed,      # keys + q_idx (logits: scratch)
+                  "topk_kernel": b_packed,                        # packed rows written
+                  "gqa_partial_kernel": b_gqa - 2 * b_qgo,        # K/V, q, packed
+                  "gqa_merge_kernel": 2 * b_qgo}                  # gate read, out written
+    return per_call, per_kernel, int(np.int64(kv_tokens))
 
 
-def traffic_record(call, workload):
-    """Per-launch HBM bytes measured by rocprofv3 counters for `call`, if the committed record
+def traffic_record(kernel, workload):
+    """Per-launch HBM bytes measured by rocprofv3 counters for `kernel`, if the committed record
     was taken on this workload and on the current kernel sources (else None)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     table = json.load(open(path))
-    rec = table.get(call)
+    rec = table.get(kernel)
     if not rec or table.get("_workload") != workload:
         return None
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES[call]:
+    for f in KERNELS[kernel][1]:
         h.update(open(os.path.join(ROOT, "sparse_attention_qsa_amd", "csrc", f), "rb").read())
     return rec["bytes_per_launch"] if rec.get("source_sha256") == h.hexdigest() else None
-
-
-CALL_KERNELS = {
-    "qsa_compress": ("prep_compress_kernel", "ring_store_kernel"),
-    "qsa_index_logits_topk": ("logits_valu_kernel", "logits_mfma_kernel", "topk_kernel"),
-    "qsa_sparse_gqa": ("gqa_partial_kernel", "gqa_merge_kernel"),
-}
 
 
 def _counter_rows(d):
@@ -171,17 +176,19 @@ def write_traffic(fetch_dir, write_dir, cal_dir, cal_mib, workload):
                     "per dispatch), scaled by the factor that maps each counter on a plain "
                     f"{cal_mib} MiB device copy to its true size",
            "_calibration": cal, "_workload": workload}
-    for call, kernels in CALL_KERNELS.items():
-        fb = sum(v for k, v in fetch.items() if any(n in k for n in kernels)) * 1024.0
-        wb = sum(v for k, v in write.items() if any(n in k for n in kernels)) * 1024.0
+    for kernel, (_, sources) in KERNELS.items():
+        names = sorted(k for k in fetch if kernel in k)
+        if not names:
+            continue
+        fb = sum(fetch[k] for k in names) * 1024.0
+        wb = sum(write.get(k, 0.0) for k in names) * 1024.0
         h = hashlib.sha256()
-        for f in KERNEL_SOURCES[call]:
+        for f in sources:
             h.update(open(os.path.join(ROOT, "sparse_attention_qsa_amd", "csrc", f), "rb").read())
-        out[call] = {"fetch_bytes": round(fb * cal["FETCH_SIZE"]),
-                     "write_bytes": round(wb * cal["WRITE_SIZE"]),
-                     "bytes_per_launch": round(fb * cal["FETCH_SIZE"] + wb * cal["WRITE_SIZE"]),
-                     "kernels": sorted(k for k in fetch if any(n in k for n in kernels)),
-                     "source_sha256": h.hexdigest()}
+        out[kernel] = {"fetch_bytes": round(fb * cal["FETCH_SIZE"]),
+                       "write_bytes": round(wb * cal["WRITE_SIZE"]),
+                       "bytes_per_launch": round(fb * cal["FETCH_SIZE"] + wb * cal["WRITE_SIZE"]),
+                       "kernels": names, "source_sha256": h.hexdigest()}
     path = os.path.join(ROOT, "profiles", "traffic.json")
     json.dump(out, open(path, "w"), indent=1)
     print(json.dumps(out, indent=1))
@@ -284,6 +291,23 @@ def main():
         torch.cuda.synchronize()
         per_call[call] = sum(a.elapsed_time(b) for a, b in evs) / len(evs) * 1e3   # us
 
+    # ---- per-kernel times: each kernel alone, through the call that launches only it (the
+    # decode workloads run the VALU logits kernel only; prefill ones add the matrix-core one).
+    # Launched back to back between two events (rotating the input copies), as in the step, so
+    # that the average is the kernel's launch duration rather than launch latency plus kernel.
+    def timed(fn_name):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for i in range(args.steps):
+            getattr(steps[i % len(steps)], fn_name)(stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps * 1e3   # us
+    per_kernel = {k: timed(fn) for k, (fn, _) in KERNELS.items()}
+    if steps[0].num_splits == 1:
+        per_kernel.pop("gqa_merge_kernel")           # not launched with one split
+
     main_leg = None
     if args.main_prepare:
         # The prepare's marginal cost: the same compress call without it.
@@ -308,11 +332,11 @@ def main():
                     "gbps_over_call": round(mbytes / (per_call["qsa_compress"] * 1e-6) / 1e9, 1)}
         del plain
 
-    alg, kv_tokens = algorithmic_bytes(wl0, steps[0].packed)
+    alg, alg_k, kv_tokens = algorithmic_bytes(wl0, steps[0].packed)
     step_bytes = sum(alg.values())
     rows_per_s = wl0.num_tokens / (ms_step * 1e-3)
-    dom = max(per_call, key=per_call.get)
-    achieved = alg[dom] / (per_call[dom] * 1e-6) / 1e9
+    dom = max(per_kernel, key=per_kernel.get)      # the dominant kernel
+    achieved = alg_k[dom] / (per_kernel[dom] * 1e-6) / 1e9
     traffic = traffic_record(dom, wl0.name)
 
     out = {
@@ -342,6 +366,8 @@ def main():
         "step_algorithmic_bytes": int(step_bytes),
         "per_call_us": {k: round(v, 2) for k, v in per_call.items()},
         "per_call_algorithmic_bytes": {k: int(v) for k, v in alg.items()},
+        "per_kernel_us": {k: round(v, 2) for k, v in per_kernel.items()},
+        "per_kernel_algorithmic_bytes": {k: int(alg_k[k]) for k in per_kernel},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},

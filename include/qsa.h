@@ -216,6 +216,17 @@ size_t qsa_index_logits_topk_workspace_size(const qsa_topk_args* args);
 qsa_status qsa_index_logits_topk(const qsa_topk_args* args, void* workspace,
                                  size_t workspace_bytes, void* stream);
 
+/* The two kernels of qsa_index_logits_topk as separate calls, for a caller that times them
+ * one by one: qsa_index_logits runs the scoring (fast float32 logits and per-block key bounds
+ * into the workspace), qsa_block_topk the selection and expansion from that workspace.  Run in
+ * this order on one stream, with the same arguments and the same, otherwise untouched,
+ * workspace, they have exactly the effect of qsa_index_logits_topk.  The workspace contents
+ * in between are private to the library. */
+qsa_status qsa_index_logits(const qsa_topk_args* args, void* workspace, size_t workspace_bytes,
+                            void* stream);
+qsa_status qsa_block_topk(const qsa_topk_args* args, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
 /* ------------------------------------------------------------------------------------------
  * qsa_sparse_gqa
  *
@@ -277,6 +288,16 @@ int32_t qsa_sparse_gqa_num_splits(const qsa_gqa_args* args);
 size_t qsa_sparse_gqa_workspace_size(const qsa_gqa_args* args);
 qsa_status qsa_sparse_gqa(const qsa_gqa_args* args, void* workspace, size_t workspace_bytes,
                           void* stream);
+
+/* The two kernels of qsa_sparse_gqa as separate calls (for per-kernel timing):
+ * qsa_sparse_gqa_partial computes the split partials (with one split: the gated output itself),
+ * qsa_sparse_gqa_merge merges them into the output (a no-op with one split).  In this order on
+ * one stream, with the same arguments and workspace, they have exactly the effect of
+ * qsa_sparse_gqa. */
+qsa_status qsa_sparse_gqa_partial(const qsa_gqa_args* args, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+qsa_status qsa_sparse_gqa_merge(const qsa_gqa_args* args, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * Diagnostics: the device arithmetic the bit-exact parts of the path rest on, exposed so a test

@@ -19,7 +19,9 @@ DTYPES = {"bf16": 0, "fp8": 1}
 
 EXPORTED = (
     "qsa_compress", "qsa_index_logits_topk", "qsa_index_logits_topk_workspace_size",
+    "qsa_index_logits", "qsa_block_topk",
     "qsa_sparse_gqa", "qsa_sparse_gqa_workspace_size", "qsa_sparse_gqa_num_splits",
+    "qsa_sparse_gqa_partial", "qsa_sparse_gqa_merge",
     "qsa_diag_e4m3_decode", "qsa_diag_fp64_sqrt_div", "qsa_status_string", "qsa_abi_version",
 )
 
@@ -100,14 +102,16 @@ def lib() -> C.CDLL:
         h.qsa_compress.restype = C.c_int
         h.qsa_index_logits_topk_workspace_size.argtypes = [C.POINTER(TopkArgs)]
         h.qsa_index_logits_topk_workspace_size.restype = C.c_size_t
-        h.qsa_index_logits_topk.argtypes = [C.POINTER(TopkArgs), _P, C.c_size_t, _P]
-        h.qsa_index_logits_topk.restype = C.c_int
+        for f in ("qsa_index_logits_topk", "qsa_index_logits", "qsa_block_topk"):
+            getattr(h, f).argtypes = [C.POINTER(TopkArgs), _P, C.c_size_t, _P]
+            getattr(h, f).restype = C.c_int
         h.qsa_sparse_gqa_workspace_size.argtypes = [C.POINTER(GqaArgs)]
         h.qsa_sparse_gqa_workspace_size.restype = C.c_size_t
         h.qsa_sparse_gqa_num_splits.argtypes = [C.POINTER(GqaArgs)]
         h.qsa_sparse_gqa_num_splits.restype = _I32
-        h.qsa_sparse_gqa.argtypes = [C.POINTER(GqaArgs), _P, C.c_size_t, _P]
-        h.qsa_sparse_gqa.restype = C.c_int
+        for f in ("qsa_sparse_gqa", "qsa_sparse_gqa_partial", "qsa_sparse_gqa_merge"):
+            getattr(h, f).argtypes = [C.POINTER(GqaArgs), _P, C.c_size_t, _P]
+            getattr(h, f).restype = C.c_int
         h.qsa_diag_e4m3_decode.argtypes = [_P, _P]
         h.qsa_diag_e4m3_decode.restype = C.c_int
         h.qsa_diag_fp64_sqrt_div.argtypes = [_P, _P, _I64, _P]

@@ -514,7 +514,8 @@ GqaPlan gqa_plan(const qsa_gqa_args& a) {
   return p;
 }
 
-hipError_t launch_gqa(const qsa_gqa_args& a, const GqaPlan& plan, char* ws, hipStream_t s) {
+hipError_t launch_gqa(const qsa_gqa_args& a, const GqaPlan& plan, char* ws, hipStream_t s,
+                      Phase phase) {
   GqaParams P{};
   P.T = a.num_tokens;
   P.R = a.num_requests;
@@ -556,7 +557,12 @@ hipError_t launch_gqa(const qsa_gqa_args& a, const GqaPlan& plan, char* ws, hipS
     P.part_o = reinterpret_cast<float*>(ws);
     P.part_lse = reinterpret_cast<float*>(ws + (n * kHeadDim * sizeof(float) + 255) / 256 * 256);
   }
-  hipError_t e;
+  hipError_t e = hipSuccess;
+  if (phase == Phase::kSecond) {  // the merge alone (nothing to merge with one split)
+    if (plan.splits == 1) return hipSuccess;
+    hipLaunchKernelGGL(gqa_merge_kernel, dim3(P.T, P.Hq), dim3(64), 0, s, P);
+    return hipGetLastError();
+  }
   switch (a.num_q_heads / a.num_kv_heads) {
     case 1: e = launch_partial<1>(P, f8, s); break;
     case 2: e = launch_partial<2>(P, f8, s); break;
@@ -565,7 +571,7 @@ hipError_t launch_gqa(const qsa_gqa_args& a, const GqaPlan& plan, char* ws, hipS
     case 16: e = launch_partial<16>(P, f8, s); break;
     default: return hipErrorInvalidValue;
   }
-  if (e != hipSuccess || plan.splits == 1) return e;
+  if (e != hipSuccess || plan.splits == 1 || phase == Phase::kFirst) return e;
   hipLaunchKernelGGL(gqa_merge_kernel, dim3(P.T, P.Hq), dim3(64), 0, s, P);
   return hipGetLastError();
 }

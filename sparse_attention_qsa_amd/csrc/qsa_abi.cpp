@@ -169,6 +169,32 @@ qsa_status validate_gqa(const qsa_gqa_args* a) {
 
 qsa_status from_hip(hipError_t e) { return e == hipSuccess ? QSA_OK : QSA_ERR_HIP; }
 
+qsa_status run_topk(const qsa_topk_args* a, void* ws, size_t ws_bytes, void* stream,
+                    qsa::Phase phase) {
+  if (a == nullptr || a->num_tokens < 0) return kInval;
+  if (a->num_tokens == 0) return QSA_OK;  // nothing else is examined
+  if (qsa_status s = validate_topk(a)) return s;
+  const qsa::TopkLayout L = qsa::topk_layout(*a);
+  if (ws == nullptr || ws_bytes < L.total) return QSA_ERR_WORKSPACE_TOO_SMALL;
+  if (!aligned(ws, 256)) return kInval;
+  return from_hip(qsa::launch_topk(*a, L, static_cast<char*>(ws),
+                                   reinterpret_cast<hipStream_t>(stream), phase));
+}
+
+qsa_status run_gqa(const qsa_gqa_args* a, void* ws, size_t ws_bytes, void* stream,
+                   qsa::Phase phase) {
+  if (a == nullptr || a->num_tokens < 0) return kInval;
+  if (a->num_tokens == 0) return QSA_OK;  // nothing else is examined
+  if (qsa_status s = validate_gqa(a)) return s;
+  const qsa::GqaPlan plan = qsa::gqa_plan(*a);
+  if (plan.ws_bytes > 0) {
+    if (ws == nullptr || ws_bytes < plan.ws_bytes) return QSA_ERR_WORKSPACE_TOO_SMALL;
+    if (!aligned(ws, 256)) return kInval;
+  }
+  return from_hip(qsa::launch_gqa(*a, plan, static_cast<char*>(ws),
+                                  reinterpret_cast<hipStream_t>(stream), phase));
+}
+
 }  // namespace
 
 extern "C" {
@@ -200,14 +226,15 @@ size_t qsa_index_logits_topk_workspace_size(const qsa_topk_args* a) {
 
 qsa_status qsa_index_logits_topk(const qsa_topk_args* a, void* ws, size_t ws_bytes,
                                  void* stream) {
-  if (a == nullptr || a->num_tokens < 0) return kInval;
-  if (a->num_tokens == 0) return QSA_OK;  // nothing else is examined
-  if (qsa_status s = validate_topk(a)) return s;
-  const qsa::TopkLayout L = qsa::topk_layout(*a);
-  if (ws == nullptr || ws_bytes < L.total) return QSA_ERR_WORKSPACE_TOO_SMALL;
-  if (!aligned(ws, 256)) return kInval;
-  return from_hip(qsa::launch_topk(*a, L, static_cast<char*>(ws),
-                                   reinterpret_cast<hipStream_t>(stream)));
+  return run_topk(a, ws, ws_bytes, stream, qsa::Phase::kAll);
+}
+
+qsa_status qsa_index_logits(const qsa_topk_args* a, void* ws, size_t ws_bytes, void* stream) {
+  return run_topk(a, ws, ws_bytes, stream, qsa::Phase::kFirst);
+}
+
+qsa_status qsa_block_topk(const qsa_topk_args* a, void* ws, size_t ws_bytes, void* stream) {
+  return run_topk(a, ws, ws_bytes, stream, qsa::Phase::kSecond);
 }
 
 int32_t qsa_sparse_gqa_num_splits(const qsa_gqa_args* a) {
@@ -221,16 +248,16 @@ size_t qsa_sparse_gqa_workspace_size(const qsa_gqa_args* a) {
 }
 
 qsa_status qsa_sparse_gqa(const qsa_gqa_args* a, void* ws, size_t ws_bytes, void* stream) {
-  if (a == nullptr || a->num_tokens < 0) return kInval;
-  if (a->num_tokens == 0) return QSA_OK;  // nothing else is examined
-  if (qsa_status s = validate_gqa(a)) return s;
-  const qsa::GqaPlan plan = qsa::gqa_plan(*a);
-  if (plan.ws_bytes > 0) {
-    if (ws == nullptr || ws_bytes < plan.ws_bytes) return QSA_ERR_WORKSPACE_TOO_SMALL;
-    if (!aligned(ws, 256)) return kInval;
-  }
-  return from_hip(qsa::launch_gqa(*a, plan, static_cast<char*>(ws),
-                                  reinterpret_cast<hipStream_t>(stream)));
+  return run_gqa(a, ws, ws_bytes, stream, qsa::Phase::kAll);
+}
+
+qsa_status qsa_sparse_gqa_partial(const qsa_gqa_args* a, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  return run_gqa(a, ws, ws_bytes, stream, qsa::Phase::kFirst);
+}
+
+qsa_status qsa_sparse_gqa_merge(const qsa_gqa_args* a, void* ws, size_t ws_bytes, void* stream) {
+  return run_gqa(a, ws, ws_bytes, stream, qsa::Phase::kSecond);
 }
 
 qsa_status qsa_diag_e4m3_decode(float* out, void* stream) {

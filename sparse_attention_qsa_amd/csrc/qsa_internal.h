@@ -49,10 +49,15 @@ struct GqaPlan {
 
 GqaPlan gqa_plan(const qsa_gqa_args& a);
 
-// Launchers (defined next to their kernels).  They assume validated arguments.
+// Launchers (defined next to their kernels).  They assume validated arguments.  A two-kernel
+// call runs both phases, or only its first (logits; attention partials) or second (top-k;
+// split merge) kernel.
+enum class Phase { kAll, kFirst, kSecond };
 hipError_t launch_compress(const qsa_compress_args& a, hipStream_t s);
-hipError_t launch_topk(const qsa_topk_args& a, const TopkLayout& L, char* ws, hipStream_t s);
-hipError_t launch_gqa(const qsa_gqa_args& a, const GqaPlan& plan, char* ws, hipStream_t s);
+hipError_t launch_topk(const qsa_topk_args& a, const TopkLayout& L, char* ws, hipStream_t s,
+                       Phase phase = Phase::kAll);
+hipError_t launch_gqa(const qsa_gqa_args& a, const GqaPlan& plan, char* ws, hipStream_t s,
+                      Phase phase = Phase::kAll);
 hipError_t launch_diag_e4m3(float* out, hipStream_t s);
 hipError_t launch_diag_fp64(const double* in, double* out, int64_t n, hipStream_t s);
 

@@ -25,7 +25,8 @@ TopkLayout topk_layout(const qsa_topk_args& a) {
   return L;
 }
 
-hipError_t launch_topk(const qsa_topk_args& a, const TopkLayout& L, char* ws, hipStream_t s) {
+hipError_t launch_topk(const qsa_topk_args& a, const TopkLayout& L, char* ws, hipStream_t s,
+                       Phase phase) {
   SelectParams P{};
   P.T = a.num_tokens;
   P.R = a.num_requests;
@@ -58,10 +59,12 @@ hipError_t launch_topk(const qsa_topk_args& a, const TopkLayout& L, char* ws, hi
   // (and every fp8 request) by the VALU kernel; each kernel skips the other's requests.
   const bool mfma = !P.fp8 && a.max_query_len > kMfmaMinRows;
   P.mfma_min_rows = P.fp8 ? INT32_MAX : kMfmaMinRows;
+  if (phase == Phase::kSecond) return launch_topk_select(P, s);
   const int rows_per_chunk = mfma ? kMfmaMinRows : a.max_query_len;
   hipError_t e = launch_logits_valu(P, rows_per_chunk, s);
   if (e != hipSuccess) return e;
   if (mfma && (e = launch_logits_mfma(P, a.max_query_len, s)) != hipSuccess) return e;
+  if (phase == Phase::kFirst) return hipSuccess;
   return launch_topk_select(P, s);
 }
 

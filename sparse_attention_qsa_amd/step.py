@@ -72,6 +72,26 @@ class QsaStep:
         B._check(B.lib().qsa_sparse_gqa(C.byref(self.g_args), self.g_ws.data_ptr(),
                                         self.g_ws.numel(), B._stream(stream)), "qsa_sparse_gqa")
 
+    # The single kernels of the two-kernel calls (for per-kernel timing).
+    def logits(self, stream=None):
+        B._check(B.lib().qsa_index_logits(C.byref(self.t_args), self.t_ws.data_ptr(),
+                                          self.t_ws.numel(), B._stream(stream)),
+                 "qsa_index_logits")
+
+    def block_topk(self, stream=None):
+        B._check(B.lib().qsa_block_topk(C.byref(self.t_args), self.t_ws.data_ptr(),
+                                        self.t_ws.numel(), B._stream(stream)), "qsa_block_topk")
+
+    def gqa_partial(self, stream=None):
+        B._check(B.lib().qsa_sparse_gqa_partial(C.byref(self.g_args), self.g_ws.data_ptr(),
+                                                self.g_ws.numel(), B._stream(stream)),
+                 "qsa_sparse_gqa_partial")
+
+    def gqa_merge(self, stream=None):
+        B._check(B.lib().qsa_sparse_gqa_merge(C.byref(self.g_args), self.g_ws.data_ptr(),
+                                              self.g_ws.numel(), B._stream(stream)),
+                 "qsa_sparse_gqa_merge")
+
     def run(self, stream=None):
         self.compress(stream)
         self.topk(stream)

@@ -126,6 +126,15 @@ def test_invalid_calls_are_rejected_before_any_launch():
     assert lib.qsa_index_logits_topk(C.byref(_topk()), None, 0, None) == SMALL
     assert lib.qsa_index_logits_topk(C.byref(_topk(num_tokens=0)), None, 0, None) == 0
     assert lib.qsa_index_logits_topk_workspace_size(C.byref(_topk(head_dim=64))) == 0
+    # The single-kernel halves validate exactly as the calls they split.
+    assert lib.qsa_index_logits(C.byref(_topk(budget=2047)), None, 0, None) == INVAL
+    assert lib.qsa_block_topk(C.byref(_topk(compress_ratio=3)), None, 0, None) == NOTSUP
+    assert lib.qsa_block_topk(C.byref(_topk()), None, 0, None) == SMALL
+    assert lib.qsa_index_logits(C.byref(_topk(num_tokens=0)), None, 0, None) == 0
+    assert lib.qsa_sparse_gqa_partial(C.byref(_gqa(head_dim=64)), None, 0, None) == NOTSUP
+    assert lib.qsa_sparse_gqa_merge(C.byref(_gqa(q=None)), None, 0, None) == INVAL
+    assert lib.qsa_sparse_gqa_merge(C.byref(_gqa()), None, 0, None) == SMALL
+    assert lib.qsa_sparse_gqa_partial(C.byref(_gqa(num_tokens=0)), None, 0, None) == 0
     c = B.CompressArgs()
     assert lib.qsa_compress(C.byref(c), None) == 0           # zero rows: a no-op
     c.num_tokens, c.num_requests = 1, 1

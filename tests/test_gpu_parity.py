@@ -232,3 +232,24 @@ def test_zero_rows_is_a_no_op():
     assert B.lib().qsa_sparse_gqa(B.C.byref(a), None, 0, None) == 0
     torch.cuda.synchronize()
     assert torch.equal(before, st.out)
+
+
+@pytest.mark.parametrize("name", ["decode_32k", "chunked_prefill", "fp8_decode"])
+def test_single_kernel_calls_equal_the_combined_calls(name):
+    """qsa_index_logits + qsa_block_topk and qsa_sparse_gqa_partial + qsa_sparse_gqa_merge
+    (the per-kernel calls the benchmark times) give the combined calls' results bit for bit."""
+    wl = workload(name)
+    twin = workload(name)
+    log(f"single-kernel calls {name}: T={wl.num_tokens}")
+    a = QsaStep(wl)
+    a.run()
+    b = QsaStep(twin)
+    b.compress()
+    b.logits()
+    b.block_topk()
+    b.gqa_partial()
+    b.gqa_merge()
+    torch.cuda.synchronize()
+    assert a.num_splits == b.num_splits
+    assert np.array_equal(to_np(a.packed), to_np(b.packed))
+    assert np.array_equal(to_np(a.out), to_np(b.out))
