@@ -362,19 +362,25 @@ def prepare_main(main_qkv, rope_pos, cos_sin, mrope_section, q_norm_w, k_norm_w,
 # ----------------------------------------------------------------------------- A3-A5: select
 
 
-def index_scores(q_vals: np.ndarray, keys: np.ndarray) -> np.ndarray:
-    """Indexer score of one row against compressed keys [n, 128]: the plain sum over the
-    indexer heads of the per-head dot products, float64.
+def index_scores(q_vals: np.ndarray, keys: np.ndarray, agg: str = "sum") -> np.ndarray:
+    """Indexer score of one row against compressed keys [n, 128]: the sum over the indexer
+    heads of the per-head dot products, float64.
 
     [qsa] QSAIndexer is "weight-free selection"; the decode logits buffer holds one float32
     per (token, compressed column) ([qsa] Qwen4ExpQSAAttention._run_qsa sizes it as
     tokens x columns x 4 bytes), so heads are reduced inside the logits.  Reading: no per-head
-    weights, no activation.  Canonical order: each head's 128 products by `halving_sum`,
-    then the heads added in order 0, 1, ..., Hi-1.
+    weights, no activation (agg "sum").  The aggregation switch agg "relu" takes max(0, .) of
+    each head's product before the sum -- the ReLU-sum of other sparse indexers, kept as an
+    alternative should the plain reading prove wrong.  Canonical order: each head's 128
+    products by `halving_sum`, then the heads added in order 0, 1, ..., Hi-1.
     """
+    if agg not in ("sum", "relu"):
+        raise ValueError(f"unknown aggregation {agg!r}")
     s = None
     for h in range(q_vals.shape[0]):
         t = halving_sum(keys * q_vals[h][None, :])
+        if agg == "relu":
+            t = np.maximum(t, 0.0)
         s = t if s is None else s + t
     return s
 
@@ -423,14 +429,14 @@ def compressed_keys_of_request(ckv_vals: np.ndarray, c_block_table_row: np.ndarr
 
 
 def index_topk(query_start_loc, seq_lens, q_codes, ckv, c_block_table, compress_ratio,
-               budget, idx_dtype, rows=None):
+               budget, idx_dtype, rows=None, agg="sum"):
     """Packed selection buffer [T, W + 1] int32 for every row (or only `rows`; the others
     stay -1 with count 0, like the inert rows of [qsa] QSAIndexer.forward).
 
     Row at position p sees vis = floor((p + 1) / c) completed blocks (reading: a row sees the
     group it completes; W = budget + c - 1 then leaves room for the c - 1 tail tokens).  If
     vis <= budget / c every visible block is taken, otherwise the budget / c best by
-    `index_scores`.
+    `index_scores` (with aggregation `agg`).
     """
     c = int(compress_ratio)
     kb = budget // c
@@ -454,7 +460,7 @@ def index_topk(query_start_loc, seq_lens, q_codes, ckv, c_block_table, compress_
             if r not in key_cache:
                 key_cache = {r: compressed_keys_of_request(
                     ckv_vals, c_block_table[r], int(seq_lens[r]) // c)}
-            s = index_scores(q_vals[i], key_cache[r][:vis])
+            s = index_scores(q_vals[i], key_cache[r][:vis], agg)
             blocks = select_blocks(s, kb)
         packed[i] = expand_row(blocks, p, c, budget)
     return packed

@@ -404,3 +404,39 @@ def test_tiny_decode_selection_invariants_and_no_poison_read():
         assert np.all(st.packed[i, cnt:W] == -1)
     assert np.all(np.isfinite(st.out))
     assert np.all(np.isfinite(bf16_bits_to_f64(st.q_codes)))
+
+
+# ----------------------------------------------------------------------------- ReLU-sum switch
+
+
+def test_relu_sum_scores_brute_force_and_special_cases():
+    """agg "relu": sum over heads of max(0, q_h . k), against a plain float loop on small
+    integers (exact); equal to the plain sum when every head's product is positive; 0 when
+    every head's product is negative; never below the plain sum."""
+    q = RNG.integers(-3, 4, size=(4, 128)).astype(np.float64)
+    k = RNG.integers(-3, 4, size=(50, 128)).astype(np.float64)
+    got = oq.index_scores(q, k, "relu")
+    want = np.array([sum(max(0.0, float(np.dot(q[h], k[j]))) for h in range(4))
+                     for j in range(50)])
+    assert np.array_equal(got, want)
+    assert np.all(got >= oq.index_scores(q, k))
+    pos = np.abs(q)
+    kp = np.abs(k) + 1.0
+    assert np.array_equal(oq.index_scores(pos, kp, "relu"), oq.index_scores(pos, kp))
+    assert np.all(oq.index_scores(pos, -kp, "relu") == 0.0)
+    with pytest.raises(ValueError):
+        oq.index_scores(q, k, "softmax")
+
+
+def test_relu_sum_selection_differs_from_plain_sum_where_heads_disagree():
+    """A block whose heads cancel (one strongly positive, one strongly negative) ranks low under
+    the plain sum and high under ReLU-sum: the switch changes the selection."""
+    q = np.zeros((2, 128))
+    q[0, 0], q[1, 1] = 1.0, 1.0
+    keys = np.zeros((4, 128))
+    keys[0, 0], keys[0, 1] = 10.0, -10.0   # heads: +10, -10 -> sum 0, relu 10
+    keys[1, 0], keys[1, 1] = 3.0, 0.0      # sum 3, relu 3
+    keys[2, 0], keys[2, 1] = 2.0, 2.0      # sum 4, relu 4
+    keys[3, 0], keys[3, 1] = -1.0, -1.0    # sum -2, relu 0
+    assert list(oq.select_blocks(oq.index_scores(q, keys), 2)) == [1, 2]
+    assert list(oq.select_blocks(oq.index_scores(q, keys, "relu"), 2)) == [0, 2]
