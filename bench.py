@@ -49,6 +49,8 @@ def parse():
     p.add_argument("--workload", default="decode_32k")
     p.add_argument("--rotate", type=int, default=4, help="input copies cycled through")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--index-agg", choices=("sum", "relu"), default="sum",
+                   help="head aggregation of the indexer score (relu: the ReLU-sum switch)")
     p.add_argument("--main-prepare", action="store_true",
                    help="also run the main-attention prepare inside qsa_compress (the attention "
                         "then uses the prepared Q and reads the gate in place) and report its "
@@ -205,7 +207,7 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_mib": mib}))
 
 
-def cpu_baseline(host_inputs, wl_meta, min_seconds=10.0):
+def cpu_baseline(host_inputs, wl_meta, agg="sum", min_seconds=10.0):
     """The oracle, as it stands, on the whole step of the same workload (host inputs taken
     before any GPU step), single-threaded, repeated until at least min_seconds have passed."""
     from threadpoolctl import threadpool_limits
@@ -215,7 +217,7 @@ def cpu_baseline(host_inputs, wl_meta, min_seconds=10.0):
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
         while True:
-            oracle_step(host_inputs)
+            oracle_step(host_inputs, agg=agg)
             reps += 1
             dt = time.perf_counter() - t0
             if dt >= min_seconds:
@@ -254,7 +256,7 @@ def main():
                 setattr(host, k, v.cpu())
     wls = [wl0] + [clone_workload(wl0) for _ in range(max(0, args.rotate - 1))]
     mains = [main_prepare_inputs(w) if args.main_prepare else None for w in wls]
-    steps = [QsaStep(w, main=m) for w, m in zip(wls, mains)]
+    steps = [QsaStep(w, main=m, index_agg=args.index_agg) for w, m in zip(wls, mains)]
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
@@ -311,7 +313,7 @@ def main():
     main_leg = None
     if args.main_prepare:
         # The prepare's marginal cost: the same compress call without it.
-        plain = [QsaStep(w) for w in wls]
+        plain = [QsaStep(w, index_agg=args.index_agg) for w in wls]
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.steps)]
         torch.cuda.synchronize()
@@ -359,7 +361,7 @@ def main():
                    "q_heads": wl0.q_heads, "kv_heads": wl0.kv_heads, "head_dim": 128,
                    "page_size": 16, "kv_dtype": getattr(wl0, "kv_dtype", "bf16"),
                    "input_copies_rotated": len(steps),
-                   "main_prepare": bool(args.main_prepare),
+                   "main_prepare": bool(args.main_prepare), "index_agg": args.index_agg,
                    "gqa_splits": steps[0].num_splits},
         "hbm_gbps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
         "hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -377,7 +379,7 @@ def main():
     if host is not None:
         del steps, wls
         torch.cuda.empty_cache()
-        out["cpu_baseline"] = cpu_baseline(host, wl0)
+        out["cpu_baseline"] = cpu_baseline(host, wl0, args.index_agg)
     print(json.dumps(out))
 
 

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 3
+#define QSA_ABI_VERSION 4
 
 typedef enum qsa_status {
   QSA_OK = 0,
@@ -66,6 +66,11 @@ typedef enum qsa_status {
 /* Indexer storage type: bf16, or OCP e4m3fn "without scales" (page
  * "vllm.models.qwen4_exp.nvidia.qsa", QSAIndexer.__init__, the indexer_kv_dtype branch). */
 typedef enum qsa_dtype { QSA_DTYPE_BF16 = 0, QSA_DTYPE_FP8_E4M3 = 1 } qsa_dtype;
+
+/* Head aggregation of the indexer score: the plain sum over heads (the reading of the pages'
+ * weight-free selection), or the sum of max(0, .) of each head's product (an alternative kept
+ * in case that reading is wrong). */
+typedef enum qsa_agg { QSA_AGG_SUM = 0, QSA_AGG_RELU_SUM = 1 } qsa_agg;
 
 /* ------------------------------------------------------------------------------------------
  * qsa_compress
@@ -210,6 +215,9 @@ typedef struct qsa_topk_args {
   qsa_dtype index_dtype;
   int32_t* packed;                  /* OUT [T, B + c] int32 (W + 1 columns), row stride below */
   int64_t packed_row_stride;
+  qsa_agg index_agg;                /* SUM (0), or RELU_SUM: score = sum_h max(0, q_h . k),
+                                       heads in order; RELU_SUM needs Hi <= 8 and is scored
+                                       by the vector-unit kernel for every request          */
 } qsa_topk_args;
 
 size_t qsa_index_logits_topk_workspace_size(const qsa_topk_args* args);

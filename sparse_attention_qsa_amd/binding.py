@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqsa.so")
 
 QSA_OK = 0
 DTYPES = {"bf16": 0, "fp8": 1}
+AGGS = {"sum": 0, "relu": 1}   # head aggregation of the indexer score
 
 EXPORTED = (
     "qsa_compress", "qsa_index_logits_topk", "qsa_index_logits_topk_workspace_size",
@@ -66,7 +67,7 @@ class TopkArgs(C.Structure):
         ("c_block_table_width", _I32), ("c_page_size", _I32), ("c_pages", _I32),
         ("num_index_heads", _I32), ("head_dim", _I32), ("compress_ratio", _I32),
         ("budget", _I32), ("index_dtype", _I32),
-        ("packed", _P), ("packed_row_stride", _I64),
+        ("packed", _P), ("packed_row_stride", _I64), ("index_agg", _I32),
     ]
 
 
@@ -249,7 +250,8 @@ def qsa_compress(stream=None, **kw) -> None:
 
 def topk_args(*, query_start_loc, seq_lens, q_idx, ckv, c_block_table, packed, num_index_heads,
               compress_ratio, budget, index_dtype, max_query_len, max_seq_len,
-              num_decode_requests=0, decode_query_len=0, c_block_table_width=None) -> TopkArgs:
+              num_decode_requests=0, decode_query_len=0, c_block_table_width=None,
+              index_agg="sum") -> TopkArgs:
     _need(query_start_loc, torch.int32, "query_start_loc")
     _need(seq_lens, torch.int32, "seq_lens")
     _need(c_block_table, torch.int32, "c_block_table")
@@ -278,6 +280,7 @@ def topk_args(*, query_start_loc, seq_lens, q_idx, ckv, c_block_table, packed, n
     a.index_dtype = DTYPES[index_dtype]
     a.packed = _ptr(packed)
     a.packed_row_stride = packed.stride(0)
+    a.index_agg = AGGS[index_agg]
     return a
 
 

@@ -69,8 +69,9 @@ __device__ __forceinline__ float group_sum(float d) {
 // Scores the tile in `raw` against NR folded rows (qf: this lane's dims of each row) and writes
 // the logits.  After the group sums, lane x of group g keeps the sum of load it = x, so every
 // lane ends with one key -- it*(64/kLanes) + g -- and each row is written with one store.
-// Updates the lane's running max |k|.
-template <bool FP8, int NR>
+// Updates the lane's running max |k|.  RELU: the NR "rows" are the heads of one row, and its
+// logit is the sum over heads of max(0, head product).
+template <bool FP8, int NR, bool RELU = false>
 __device__ __forceinline__ void score_key_tile(const SelectParams& P,
                                                const uint32_t (&raw)[KeyLanes<FP8>::kLoads][4],
                                                uint32_t okm, const float (&qf)[NR][16], int nr,
@@ -123,6 +124,16 @@ __device__ __forceinline__ void score_key_tile(const SelectParams& P,
   // Unconditional buffer stores: a row's record ends at its visible keys (none for a row past
   // nr), so the hardware drops the rest; lanes x >= kLoads hold no key.
   const int j = j0 + x * K::kKeysPerLoad + g;
+  if (RELU) {
+    float sum = fmaxf(res[0], 0.0f);
+#pragma unroll
+    for (int rr = 1; rr < NR; ++rr) sum = sum + fmaxf(res[rr], 0.0f);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        P.logits + (int64_t)row0 * P.col_stride, 0, vis_max * 4, 0x00020000);
+    const uint32_t off = x < K::kLoads ? (uint32_t)j * 4u : 0xFFFFFFF0u;
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sum), rs, off, 0, 0);
+    return;
+  }
 #pragma unroll
   for (int rr = 0; rr < NR; ++rr) {
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -139,7 +150,8 @@ __device__ __forceinline__ void score_key_tile(const SelectParams& P,
 // contiguous bytes of each.  The cache row of every key and the head-folded rows are staged in
 // LDS once; two tiles are in flight from the start and each reload is issued before the other
 // buffer's tile is scored.
-template <bool FP8, int NR>
+// RELU: one row at a time, its NR = 8 heads held unfolded as the scorer's rows.
+template <bool FP8, int NR, bool RELU = false>
 __global__ __launch_bounds__(kLogitsThreads) __attribute__((amdgpu_waves_per_eu(NR >= 4 ? 2 : 4)))
 void logits_valu_kernel(SelectParams P) {
   using KL = KeyLanes<FP8>;
@@ -184,8 +196,8 @@ void logits_valu_kernel(SelectParams P) {
       const bool ok = j < vis_max && col[i] < P.cbt_width && page[i] >= 0 && page[i] < P.c_pages;
       rows_s[threadIdx.x + kT * i] = ok ? page[i] * P.Pc + (j - col[i] * P.Pc) : -1;
     }
-    for (int rr0 = 0; rr0 < n; rr0 += NR) {
-      const int nr = min(NR, n - rr0);
+    for (int rr0 = 0; rr0 < n; rr0 += (RELU ? 1 : NR)) {
+      const int nr = RELU ? NR : min(NR, n - rr0);
       // Head-folded Q of the chunk's rows: each of the first nr*128 threads owns one (row, dim)
       // and loads all its heads at once (clamped to Hi - 1, the extra terms added as zero).
       constexpr int kSlots = (NR * kHeadDim + kT - 1) / kT;
@@ -194,10 +206,11 @@ void logits_valu_kernel(SelectParams P) {
       for (int sl = 0; sl < kSlots; ++sl) {
         const int e = threadIdx.x + kT * sl;
         const int rr = min(e >> 7, nr - 1), d = e & (kHeadDim - 1);
-        const int64_t qb = (int64_t)(q0 + rr0 + rr) * P.Hi * kHeadDim + d;
+        const int64_t qb = (int64_t)(q0 + rr0 + (RELU ? 0 : rr)) * P.Hi * kHeadDim + d;
 #pragma unroll
-        for (int h = 0; h < 16; ++h) {
-          const int64_t idx = qb + min(h, P.Hi - 1) * kHeadDim;
+        for (int h = 0; h < (RELU ? 1 : 16); ++h) {
+          // RELU: slot e holds head rr of the one row (clamped to Hi - 1, zeroed below).
+          const int64_t idx = qb + min(RELU ? rr : h, P.Hi - 1) * kHeadDim;
           v[sl][h] = FP8 ? (uint32_t)reinterpret_cast<const uint8_t*>(P.q_idx)[idx]
                          : (uint32_t)reinterpret_cast<const uint16_t*>(P.q_idx)[idx];
         }
@@ -210,8 +223,12 @@ void logits_valu_kernel(SelectParams P) {
           return FP8 ? e4m3_to_f32_exact((uint8_t)x) : bf16_to_f32((uint16_t)x);
         };
         float f = dec(v[sl][0]);
+        if (RELU) {
+          if (((int)threadIdx.x + kT * sl) >> 7 >= P.Hi) f = 0.0f;  // a head past Hi
+        } else {
 #pragma unroll
-        for (int h = 1; h < 16; ++h) f = f + (h < P.Hi ? dec(v[sl][h]) : 0.0f);
+          for (int h = 1; h < 16; ++h) f = f + (h < P.Hi ? dec(v[sl][h]) : 0.0f);
+        }
         v[sl][0] = __float_as_uint(f);
       }
       if (rr0 > 0) barrier();  // the previous chunk's readers are done with qf_s
@@ -237,8 +254,9 @@ void logits_valu_kernel(SelectParams P) {
 #pragma unroll
       for (int t = 0; t < kLogitsTilesPerWG; ++t) {
         load_key_tile<FP8>(P, rows_s, t, w, lane, a, ma);
-        score_key_tile<FP8, NR>(P, a, ma, qf, nr, row0, jw + t * kLogitsKeysPerWG + w * 64,
-                                vis_max, lane, first, kmax);
+        score_key_tile<FP8, NR, RELU>(P, a, ma, qf, nr, row0,
+                                      jw + t * kLogitsKeysPerWG + w * 64, vis_max, lane, first,
+                                      kmax);
       }
     }
   }
@@ -267,6 +285,16 @@ hipError_t launch_logits(const SelectParams& P, int rows_per_chunk, hipStream_t 
 }
 
 }  // namespace
+
+hipError_t launch_logits_valu_relu(const SelectParams& P, hipStream_t s) {
+  const dim3 grid(P.key_tiles, P.R);
+  if (P.fp8)
+    hipLaunchKernelGGL((logits_valu_kernel<true, 8, true>), grid, dim3(kLogitsThreads), 0, s, P);
+  else
+    hipLaunchKernelGGL((logits_valu_kernel<false, 8, true>), grid, dim3(kLogitsThreads), 0, s,
+                       P);
+  return hipGetLastError();
+}
 
 hipError_t launch_logits_valu(const SelectParams& P, int rows_per_chunk, hipStream_t s) {
   return P.fp8 ? launch_logits<true>(P, rows_per_chunk, s)

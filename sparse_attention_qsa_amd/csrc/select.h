@@ -11,6 +11,7 @@ struct SelectParams {
   int key_blocks;     // 128-key blocks per request in the kmax array
   int mfma_min_rows;  // requests with more rows than this are scored by the MFMA kernel
   bool fp8;
+  bool relu;          // ReLU-sum aggregation (every request on the vector-unit kernel)
   const int32_t* qsl;
   const int32_t* seq_lens;
   const void* q_idx;
@@ -30,6 +31,7 @@ constexpr int kMfmaMinRows = 16;
 
 // Launchers (each next to its kernels); arguments are validated by the caller.
 hipError_t launch_logits_valu(const SelectParams& P, int rows_per_chunk, hipStream_t s);
+hipError_t launch_logits_valu_relu(const SelectParams& P, hipStream_t s);
 hipError_t launch_logits_mfma(const SelectParams& P, int max_query_len, hipStream_t s);
 hipError_t launch_topk_select(const SelectParams& P, hipStream_t s);
 

@@ -42,6 +42,7 @@ hipError_t launch_topk(const qsa_topk_args& a, const TopkLayout& L, char* ws, hi
   P.key_tiles = L.key_tiles;
   P.key_blocks = L.key_blocks;
   P.fp8 = a.index_dtype == QSA_DTYPE_FP8_E4M3;
+  P.relu = a.index_agg == QSA_AGG_RELU_SUM;
   P.qsl = a.query_start_loc;
   P.seq_lens = a.seq_lens;
   P.q_idx = a.q_idx;
@@ -57,11 +58,13 @@ hipError_t launch_topk(const qsa_topk_args& a, const TopkLayout& L, char* ws, hi
 
   // bf16 requests with more than kMfmaMinRows rows are scored on the matrix cores, the others
   // (and every fp8 request) by the VALU kernel; each kernel skips the other's requests.
-  const bool mfma = !P.fp8 && a.max_query_len > kMfmaMinRows;
-  P.mfma_min_rows = P.fp8 ? INT32_MAX : kMfmaMinRows;
+  // (The matrix-core kernel sums the heads in its accumulator: ReLU-sum requests stay on the
+  // vector units.)
+  const bool mfma = !P.fp8 && !P.relu && a.max_query_len > kMfmaMinRows;
+  P.mfma_min_rows = (P.fp8 || P.relu) ? INT32_MAX : kMfmaMinRows;
   if (phase == Phase::kSecond) return launch_topk_select(P, s);
   const int rows_per_chunk = mfma ? kMfmaMinRows : a.max_query_len;
-  hipError_t e = launch_logits_valu(P, rows_per_chunk, s);
+  hipError_t e = P.relu ? launch_logits_valu_relu(P, s) : launch_logits_valu(P, rows_per_chunk, s);
   if (e != hipSuccess) return e;
   if (mfma && (e = launch_logits_mfma(P, a.max_query_len, s)) != hipSuccess) return e;
   if (phase == Phase::kFirst) return hipSuccess;

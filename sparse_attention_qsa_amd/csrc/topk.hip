@@ -90,7 +90,8 @@ __device__ __forceinline__ void key_pairs16(const SelectParams& P, const int32_t
 // by halving: pairs (2i, 2i+1) give v_i; then v_i += v_{i+32} for i < 32, += v_{i+16} for
 // i < 16, ..., += v_{i+1} for i < 1.  Lane l holds v_l, v_{l+16}, v_{l+32}, v_{l+48}, so the
 // first two halvings are in-lane and the last four take the partner 8, 4, 2, 1 lanes up.
-// The heads are then added in order.  The result is valid in lane l = 0.
+// The heads are then added in order (ReLU-sum: each head's sum clamped at 0 first).  The result
+// is valid in lane l = 0.
 __device__ double canonical_score16(const SelectParams& P, const float* qrow,
                                     const int32_t* cbt_row, int cw, int j, int l) {
   float k[8];
@@ -111,6 +112,7 @@ __device__ double canonical_score16(const SelectParams& P, const float* qrow,
     x = x + row_down<4>(x);
     x = x + row_down<2>(x);
     x = x + row_down<1>(x);
+    if (P.relu) x = x > 0.0 ? x : 0.0;  // ReLU-sum: max(0, head product)
     s = (h == 0) ? x : s + x;
   }
   return s;

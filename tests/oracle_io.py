@@ -40,7 +40,7 @@ def oracle_compress(wl, requests=None):
     return q_codes, after
 
 
-def oracle_step(wl, rows=None, with_attention=True) -> OracleStep:
+def oracle_step(wl, rows=None, with_attention=True, agg="sum") -> OracleStep:
     """The whole path on the CPU: prep + compress, logits + top-k + expand, sparse GQA.
     `rows` restricts selection and attention to a subset of rows (their requests are
     compressed; the other rows stay inert)."""
@@ -51,7 +51,7 @@ def oracle_step(wl, rows=None, with_attention=True) -> OracleStep:
     q_codes, after = oracle_compress(wl, requests)
     packed = oq.index_topk(to_np(wl.query_start_loc), to_np(wl.seq_lens), q_codes, after.ckv,
                            to_np(wl.c_block_table), wl.compress_ratio, wl.budget,
-                           wl.index_dtype, rows=rows)
+                           wl.index_dtype, rows=rows, agg=agg)
     out = None
     if with_attention:
         out = oq.sparse_gqa(to_np(wl.q), to_np(wl.kv_cache), to_np(wl.block_table),

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(B.EXPORTED)
-    assert lib.qsa_abi_version() == 3
+    assert lib.qsa_abi_version() == 4
     assert lib.qsa_status_string(3) == b"QSA_ERR_WORKSPACE_TOO_SMALL"
 
 
@@ -123,6 +123,10 @@ def test_invalid_calls_are_rejected_before_any_launch():
     assert lib.qsa_index_logits_topk(C.byref(_topk(budget=2047)), None, 0, None) == INVAL
     assert lib.qsa_index_logits_topk(C.byref(_topk(compress_ratio=3)), None, 0, None) == NOTSUP
     assert lib.qsa_index_logits_topk(C.byref(_topk(index_dtype=7)), None, 0, None) == NOTSUP
+    assert lib.qsa_index_logits_topk(C.byref(_topk(index_agg=2)), None, 0, None) == NOTSUP
+    assert lib.qsa_index_logits_topk(C.byref(_topk(index_agg=1, num_index_heads=9)), None, 0,
+                                     None) == NOTSUP
+    assert lib.qsa_index_logits_topk(C.byref(_topk(index_agg=1)), None, 0, None) == SMALL
     assert lib.qsa_index_logits_topk(C.byref(_topk()), None, 0, None) == SMALL
     assert lib.qsa_index_logits_topk(C.byref(_topk(num_tokens=0)), None, 0, None) == 0
     assert lib.qsa_index_logits_topk_workspace_size(C.byref(_topk(head_dim=64))) == 0

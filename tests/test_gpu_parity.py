@@ -15,6 +15,7 @@ from sparse_attention_qsa_amd import binding as B
 from sparse_attention_qsa_amd.step import QsaStep
 from tests.gpu_util import (SCALED, TOL, gpu_out_f64, log, max_abs, oracle_step, run_gpu,
                             to_np, workload)
+from tests.oracle_io import oracle_compress
 
 pytestmark = pytest.mark.gpu
 
@@ -253,3 +254,23 @@ def test_single_kernel_calls_equal_the_combined_calls(name):
     assert a.num_splits == b.num_splits
     assert np.array_equal(to_np(a.packed), to_np(b.packed))
     assert np.array_equal(to_np(a.out), to_np(b.out))
+
+
+
+@pytest.mark.parametrize("name", ["tiny_decode", "decode_32k", "fp8_decode", "chunked_prefill"])
+def test_relu_sum_selection_is_exact(name):
+    """The ReLU-sum aggregation switch: the selection equals the oracle's on the same workload
+    (bit for bit), and differs from the plain-sum selection somewhere."""
+    wl = workload(name)
+    log(f"relu-sum selection {name}: T={wl.num_tokens}")
+    q_codes, after = oracle_compress(wl)
+    args = (to_np(wl.query_start_loc), to_np(wl.seq_lens), q_codes, after.ckv,
+            to_np(wl.c_block_table), wl.compress_ratio, wl.budget, wl.index_dtype)
+    ref = oq.index_topk(*args, agg="relu")
+    st = QsaStep(wl, index_agg="relu")
+    st.compress()
+    st.topk()
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(st.packed), ref)
+    if name != "tiny_decode":
+        assert not np.array_equal(ref, oq.index_topk(*args, agg="sum"))
