@@ -274,3 +274,59 @@ def test_relu_sum_selection_is_exact(name):
     assert np.array_equal(to_np(st.packed), ref)
     if name != "tiny_decode":
         assert not np.array_equal(ref, oq.index_topk(*args, agg="sum"))
+
+
+def _advance(wl, seed):
+    """The next decode step of `wl` (one row per request): each request one token longer, its
+    row at the next position with fresh projections; the caches are shared with `wl`."""
+    import copy
+    nxt = copy.copy(wl)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    nxt.seq_lens_host = wl.seq_lens_host + wl.rows_host
+    nxt.seq_lens = wl.seq_lens + torch.from_numpy(wl.rows_host).to(torch.int32).cuda()
+    nxt.max_seq_len = int(nxt.seq_lens_host.max())
+    nxt.positions = wl.positions + 1
+    for name in ("q_proj", "k_proj", "q", "gate"):
+        t = getattr(wl, name)
+        setattr(nxt, name, torch.randn(t.shape, generator=g, device="cuda").to(t.dtype))
+    return nxt
+
+
+def test_speculative_step_reuses_selection_and_rollback_rewrites_the_caches():
+    """Later speculative steps reuse step 0's selection (the pages' skip_topk: the caches are
+    still updated, the top-k is skipped, the attention reads the step-0 packed rows); a rejected
+    token is rolled back by running the next step at the same position again, which leaves the
+    caches exactly as if the rejected token had never been written (the ring is wider than a
+    group, so no slot a pooled group needs is overwritten)."""
+    wl = workload("decode_32k")
+    log(f"speculative reuse and rollback: R={wl.num_requests}")
+    st0 = QsaStep(wl)
+    st0.run()
+    torch.cuda.synchronize()
+    packed0 = st0.packed.clone()
+    pre = (wl.ring.clone(), wl.ckv.clone())            # caches after step 0
+    # Step 1 (a speculative token X): compress, no top-k, attention on the step-0 rows.
+    x = _advance(wl, 11)
+    q_codes, after = oracle_compress(x)                 # oracle from the post-step-0 caches
+    st1 = QsaStep(x)
+    st1.compress()
+    st1.packed.copy_(packed0)
+    st1.gqa()
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(wl.ckv).view(np.uint8), after.ckv.view(np.uint8))
+    assert np.array_equal(to_np(wl.ring), after.ring)
+    ref = oq.sparse_gqa(to_np(x.q), to_np(x.kv_cache), to_np(x.block_table),
+                        to_np(x.token_to_req), to_np(packed0), gate=to_np(x.gate))
+    assert max_abs(gpu_out_f64(st1), ref) <= TOL[wl.index_dtype]
+    # Rollback: token X rejected, the step runs again at the same position with token Y.
+    y = _advance(wl, 12)
+    QsaStep(y).compress()
+    torch.cuda.synchronize()
+    after_xy = (wl.ring.clone(), wl.ckv.clone())
+    wl.ring.copy_(pre[0])
+    wl.ckv.copy_(pre[1])
+    QsaStep(y).compress()                               # Y alone, from the step-0 caches
+    torch.cuda.synchronize()
+    assert torch.equal(after_xy[0], wl.ring)
+    assert torch.equal(after_xy[1].view(torch.uint8), wl.ckv.view(torch.uint8))
