@@ -178,8 +178,9 @@ void logits_valu_kernel(SelectParams P) {
   const int n = max(0, min(P.qsl[r + 1], P.T) - q0), L = P.seq_lens[r];
   // The MFMA kernel, which runs next, starts its work queues from zero.
   if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 8) P.work[threadIdx.x] = 0;
-  // Requests with many rows are scored by the MFMA kernel.
-  if (n > P.mfma_min_rows) return;  // block-uniform, before any barrier
+  // Requests with many rows are scored by the MFMA kernel; for them this kernel only takes the
+  // per-block bound of max |k| the top-k needs (one pass over their keys).
+  const bool kmax_only = n > P.mfma_min_rows;  // block-uniform
   const int vis_max = (n > 0 && n <= L) ? min(L / P.c, P.cols) : 0;
   // Barrier without a memory fence (a fence would wait for every load in flight); the LDS
   // writes before it are complete, and global loads are waited for where their data is used.
@@ -196,7 +197,32 @@ void logits_valu_kernel(SelectParams P) {
       const bool ok = j < vis_max && col[i] < P.cbt_width && page[i] >= 0 && page[i] < P.c_pages;
       rows_s[threadIdx.x + kT * i] = ok ? page[i] * P.Pc + (j - col[i] * P.Pc) : -1;
     }
-    for (int rr0 = 0; rr0 < n; rr0 += (RELU ? 1 : NR)) {
+    if (kmax_only) {
+      barrier();  // rows_s written
+#pragma unroll
+      for (int t = 0; t < kLogitsTilesPerWG; ++t) {
+        uint32_t a[KL::kLoads][4], ma;
+        load_key_tile<FP8>(P, rows_s, t, w, lane, a, ma);
+#pragma unroll
+        for (int it = 0; it < KL::kLoads; ++it) {
+          float m = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t word = a[it][i];
+            if (FP8) {
+              const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
+              const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
+              m = fmaxf(m, fmaxf(fmaxf(fabsf(lo[0]), fabsf(lo[1])),
+                                 fmaxf(fabsf(hi[0]), fabsf(hi[1]))));
+            } else {
+              m = fmaxf(m, fmaxf(fabsf(bf16lo(word)), fabsf(bf16hi(word))));
+            }
+          }
+          kmax = fmaxf(kmax, ((ma >> it) & 1u) ? m : 0.0f);  // masked keys dropped by a select
+        }
+      }
+    }
+    for (int rr0 = 0; rr0 < (kmax_only ? 0 : n); rr0 += (RELU ? 1 : NR)) {
       const int nr = RELU ? NR : min(NR, n - rr0);
       // Head-folded Q of the chunk's rows: each of the first nr*128 threads owns one (row, dim)
       // and loads all its heads at once (clamped to Hi - 1, the extra terms added as zero).

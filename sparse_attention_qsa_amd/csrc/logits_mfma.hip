@@ -7,65 +7,50 @@
 
 namespace qsa {
 namespace {
-// Requests with many rows (chunked prefill) are scored per head on the matrix cores: for a
-// tile of 128 rows x 256 keys, S = sum_h Q_h K^T, the head sum taken in the fp32 accumulator
-// (bf16 products are exact in fp32).  The fp32 result differs from the canonical float64
-// score by at most gamma_{Hi*128} kappa A with u = 2^-23 (any summation order, faithful
-// rounding); the top-k's band covers that.
+// Requests with many rows (chunked prefill) are scored per head on the matrix cores:
+// S = sum_h Q_h K^T with the head sum taken in the fp32 accumulator (bf16 products are exact in
+// fp32).  The fp32 result differs from the canonical float64 score by at most
+// gamma_{Hi*128} kappa A with u = 2^-23 (any summation order, faithful rounding); the top-k's
+// band covers that.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kMfmaRows = 128;        // rows per row block
-constexpr int kMfmaKeys = 256;        // keys per workgroup (its key tile)
-constexpr int kMfmaRowBlocksPerWG = 4;
+constexpr int kMfmaRows = 128;         // rows per row block: 8 waves x 16 rows
+constexpr int kMfmaKeys = 256;         // keys per tile
+constexpr int kMfmaTilesPerItem = 8;   // key tiles per work item
 
 __device__ __forceinline__ void lds_dma16(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
                                    (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
 }
 
-// Tiles in LDS hold rows of 256 bytes; row t's 16-byte chunk c sits in slot c ^ (t & 15), so
-// that 16 lanes reading chunk c of 16 consecutive rows hit 16 different slots.  They are
-// filled by LDS-direct loads: a load writes 4 rows (1 KiB), lane L landing in row L/16, slot
+// Key tiles in LDS hold rows of 256 bytes; key t's 16-byte chunk c sits in slot c ^ (t & 15),
+// so that 16 lanes reading chunk c of 16 consecutive keys hit 16 different slots.  They are
+// filled by LDS-direct loads: a load writes 4 keys (1 KiB), lane L landing in key L/16, slot
 // L%16.
-__device__ __forceinline__ const bf16x8_t& tile_chunk(const uint8_t* buf, int t, int c) {
-  return *reinterpret_cast<const bf16x8_t*>(buf + t * 256 + 16 * (c ^ (t & 15)));
-}
-__device__ __forceinline__ uint32_t tile_chunk_addr(const uint8_t* buf, int t, int c) {
-  const __attribute__((address_space(3))) uint8_t* p =
-      (const __attribute__((address_space(3))) uint8_t*)(buf + t * 256 + 16 * (c ^ (t & 15)));
-  return (uint32_t)(uintptr_t)p;
-}
-// 16-byte LDS read at addr + OFF issued as inline assembly; the caller waits (lgkmcnt)
-// before use.
-template <int OFF>
-__device__ __forceinline__ bf16x8_t lds_read16_off(uint32_t addr) {
-  static_assert(OFF >= 0 && OFF < 65536, "ds_read offset field is 16 bits");
-  bf16x8_t v;
-  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
-  return v;
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// Waits until at most n VMEM operations of this wave are outstanding (n from the small set of
-// counts the MFMA kernel uses; any other count waits for all).
+// Waits until at most n VMEM operations of this wave are outstanding, n rounded down to a
+// multiple of 4 (at most 60): rounding down only makes the wait stricter.
 __device__ __forceinline__ void wait_vmcnt(int n) {
-  switch (n) {
-    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
-    case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
-    case 16: __builtin_amdgcn_s_waitcnt(0x4F70); break;
-    case 20: __builtin_amdgcn_s_waitcnt(0x4F74); break;
-    case 24: __builtin_amdgcn_s_waitcnt(0x4F78); break;
-    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+#define QSA_VMCNT(i)                                                                 \
+  case i:                                                                            \
+    __builtin_amdgcn_s_waitcnt(((4 * i) & 15) | (((4 * i) >> 4) << 14) | 0x0F70); \
+    break;
+  switch (n < 0 ? 0 : (n >= 60 ? 15 : n >> 2)) {
+    QSA_VMCNT(0) QSA_VMCNT(1) QSA_VMCNT(2) QSA_VMCNT(3) QSA_VMCNT(4) QSA_VMCNT(5)
+    QSA_VMCNT(6) QSA_VMCNT(7) QSA_VMCNT(8) QSA_VMCNT(9) QSA_VMCNT(10) QSA_VMCNT(11)
+    QSA_VMCNT(12) QSA_VMCNT(13) QSA_VMCNT(14) QSA_VMCNT(15)
   }
+#undef QSA_VMCNT
 }
 
 // LDS accesses issued as inline assembly, so that the compiler's own wait insertion (which
 // cannot tell the targets of the LDS-direct loads apart) does not make them wait for every
 // memory operation in flight; each read is waited for before its value is used.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
 __device__ __forceinline__ uint32_t lds_load_u32(const void* p) {
   uint32_t v;
   asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_addr(p))
@@ -76,8 +61,8 @@ __device__ __forceinline__ void lds_store_u32(void* p, uint32_t v) {
   asm volatile("ds_write_b32 %0, %1" ::"v"(lds_addr(p)), "v"(v) : "memory");
 }
 
-// Claims the next work item of a queue (a returning global atomic issued as inline assembly:
-// the compiler would wait for its result at once, and with it for every store in flight).  The
+// Claims the next work item (a returning global atomic issued as inline assembly: the
+// compiler would wait for its result at once, and with it for every store in flight).  The
 // result is valid after a vmcnt wait that covers it.
 __device__ __forceinline__ uint32_t claim_async(int* counter) {
   uint32_t ret;
@@ -88,295 +73,205 @@ __device__ __forceinline__ uint32_t claim_async(int* counter) {
   return ret;
 }
 
-// Largest value over the wavefront (DPP within rows of 16, then the four row results).
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
-  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
-  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
-  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
-  const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
-  return max(max(a, b), max(c, d));
-}
-
-// Persistent workgroups (one per CU; the LDS use allows no more) take work items -- (request,
-// chunk of up to four row blocks, key tile of 256 keys) -- from eight queues, one per XCD:
-// queue x holds the (request, row chunk) pairs x, x+8, ..., each with all its key tiles in
-// order, so that the workgroups of one XCD work on the same rows at once and share their Q in
-// the XCD's L2.  (Workgroup b takes queue b % 8, which is its XCD under round-robin dispatch;
-// any other placement only costs locality.)  An item claims the next one when it starts, and
-// loads its key tile once and keeps the
-// key fragments in registers (8 waves, 2 x 4 of 64 rows x 64 keys; per wave 4 x 4
-// accumulators of 16 keys x 16 rows, v_mfma_f32_16x16x32_bf16 with the keys as the A operand
-// so that a lane ends up with 4 consecutive keys of one row).  The Q slabs (128 rows of one
-// head) of its row blocks then stream through four 32 KiB LDS buffers (two of them the key
-// tile's), three slabs in flight while one is multiplied.  Stores are unconditional buffer
-// stores (out-of-range lanes are dropped by the buffer's bounds), so that every wave issues a
-// known number of memory operations and the waits for the slabs are exact.
+// Persistent workgroups (one per CU; the LDS use allows no more) take work items from one
+// queue.  An item is (request, row block of 128 rows, up to eight consecutive 256-key tiles
+// the block sees); the items of every row block's first eight tiles come first, the later
+// tiles of the longest rows next, so that the big items are claimed first.  The next item is
+// claimed when an item starts.
+//
+// The item's Q stays in registers: wave w holds rows 16w .. 16w+15 of the block, all heads
+// (up to kMfmaMaxHeads) and all 128 dims, as the B operand of v_mfma_f32_16x16x32_bf16.  Key
+// tiles (64 KiB) stream through two LDS buffers, loaded LDS-direct one tile ahead, so a tile
+// costs one barrier.  A wave multiplies a tile four 16-key groups at a time -- 4 x 4 k-steps x
+// Hi heads of MFMAs into four accumulators, the A operand (16 keys x 32 dims) read from LDS --
+// and stores each group's 16 rows x 16 keys as soon as it is final: the logits leave a store
+// per 128 MFMAs instead of in bursts, so that they do not stall the key loads behind them.
+// Stores are buffer stores whose range ends at the block's last row; keys a row does not see
+// go to an out-of-range offset and are dropped.
 __global__ __launch_bounds__(512) void logits_mfma_kernel(SelectParams P, int row_blocks) {
-  // Four 32 KiB buffers: 0 and 1 hold Q slabs; 2 and 3 hold the key tile (keys 0..127,
-  // 128..255) and afterwards two more Q slabs.  Slab sl lives in buffer sl % 4.
-  __shared__ __attribute__((aligned(16))) uint8_t lds[4][kMfmaRows * 256];
-  uint8_t* const kl = lds[2];
-  uint8_t* const kh = lds[3];
-  __shared__ uint32_t red[2][8];
-  __shared__ __attribute__((aligned(16))) uint8_t kok[kMfmaKeys];
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][kMfmaKeys * 256];
+  __shared__ __attribute__((aligned(16))) uint8_t kok[2][kMfmaKeys];
   __shared__ int s_item[2];
   const int key_tiles = (P.cols + kMfmaKeys - 1) / kMfmaKeys;
-  const int row_chunks = (row_blocks + kMfmaRowBlocksPerWG - 1) / kMfmaRowBlocksPerWG;
-  const int pairs = P.R * row_chunks;
-  const int queue = blockIdx.x & 7;
-  const int64_t qlen = (int64_t)((pairs - queue + 7) / 8) * key_tiles;  // items of this queue
+  const int chunks = (key_tiles + kMfmaTilesPerItem - 1) / kMfmaTilesPerItem;
+  const int per_chunk = P.R * row_blocks;
+  const int64_t qlen = (int64_t)per_chunk * chunks;
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int l16 = lane & 15, l4 = lane >> 4;
-  const int wr = w >> 2, wc = w & 3;  // this wave: rows 64wr .. +63, keys 64wc .. +63
+  const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, l4 = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const char* ckv = reinterpret_cast<const char*>(P.ckv);
   const char* qb = reinterpret_cast<const char*>(P.q_idx);
-  // Barrier without a memory fence (a fence would wait for every load in flight); LDS reads
-  // are complete before it, and the loads into LDS are waited for explicitly.
+  const __attribute__((address_space(4))) int32_t* qsl_c =
+      (const __attribute__((address_space(4))) int32_t*)P.qsl;
+  const __attribute__((address_space(4))) int32_t* sl_c =
+      (const __attribute__((address_space(4))) int32_t*)P.seq_lens;
+  // Barrier without a memory fence (a fence would wait for every load in flight); LDS
+  // operations are complete before it, and the loads into LDS are waited for explicitly.
   auto barrier = [] {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
+  // This lane's A-operand address in buffer b for k-step ks: key l16 of the group (the group
+  // is an offset of 4 KiB), chunk 4ks + l4.
+  uint32_t kaddr[2][4];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      kaddr[b][ks] = lds_addr(kbuf[b] + l16 * 256 + 16 * ((4 * ks + l4) ^ l16));
+  }
 
-  if (tid == 0) s_item[0] = atomicAdd(&P.work[queue], 1);
+  if (tid == 0) s_item[0] = atomicAdd(&P.work[0], 1);
   __syncthreads();
   for (int it = 0;; ++it) {
     const int64_t item = (int)__builtin_amdgcn_readfirstlane((int)lds_load_u32(&s_item[it & 1]));
     if (item >= qlen) break;  // workgroup-uniform
     uint32_t next = 0;
-    if (tid == 0) next = claim_async(&P.work[queue]);
-    const int g = queue + 8 * (int)(item / key_tiles);
-    const int kt = (int)(item % key_tiles);
-    const int rc = g % row_chunks, r = g / row_chunks;
-
-    // Request metadata through the scalar cache (vector loads would wait for the stores in
-    // flight).
-    const __attribute__((address_space(4))) int32_t* qsl_c =
-        (const __attribute__((address_space(4))) int32_t*)P.qsl;
-    const __attribute__((address_space(4))) int32_t* sl_c =
-        (const __attribute__((address_space(4))) int32_t*)P.seq_lens;
+    if (tid == 0) next = claim_async(&P.work[0]);
+    const int chunk = (int)(item / per_chunk), jj = (int)(item % per_chunk);
+    const int r = jj % P.R;
+    const int rb = chunk == 0 ? jj / P.R : row_blocks - 1 - jj / P.R;
     const int q0 = max(0, min(qsl_c[r], P.T));
     const int n = max(0, min(qsl_c[r + 1], P.T) - q0), L = sl_c[r];
-    const int key0 = kt * kMfmaKeys;
-    const int vis_max = min(L / P.c, P.cols);
-    // Row blocks of this chunk that see at least one key of the tile (visibility grows with
-    // the row, so they are a suffix of the chunk).
-    const int rb_end = min((rc + 1) * kMfmaRowBlocksPerWG, (n + kMfmaRows - 1) / kMfmaRows);
-    int rb_first = rc * kMfmaRowBlocksPerWG;
-    auto sees_tile = [&](int rb) {
-      const int last = min(kMfmaRows, n - rb * kMfmaRows);
-      return key0 < min((L - n + rb * kMfmaRows + last) / P.c, P.cols);
-    };
-    if (n > P.mfma_min_rows && n <= L) {
-      while (rb_first < rb_end && !sees_tile(rb_first)) ++rb_first;
-    } else {
-      rb_first = rb_end;  // decode request, or inert rows
+    int t0 = 0, t1 = 0, nrows = 0, pbase = 0;
+    if (n > P.mfma_min_rows && n <= L && rb * kMfmaRows < n) {
+      nrows = min(kMfmaRows, n - rb * kMfmaRows);
+      pbase = L - n + rb * kMfmaRows;  // position of the block's first row
+      const int vis_hi = min((pbase + nrows) / P.c, P.cols);
+      t0 = chunk * kMfmaTilesPerItem;
+      t1 = min(t0 + kMfmaTilesPerItem, (vis_hi + kMfmaKeys - 1) / kMfmaKeys);
     }
-    if (rb_first >= rb_end) {
+    if (t0 >= t1) {  // decode request, inert rows, or no tile of this chunk is seen
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the claim has returned
       if (tid == 0) lds_store_u32(&s_item[(it + 1) & 1], next);
       barrier();
       continue;
     }
+    const int vis_max = min(L / P.c, P.cols);
+    barrier();  // every wave is done with the previous item's buffers
+    // This lane's row of the block and the keys it sees.
+    const int trow = 16 * w + l16;
+    const int vis_t = trow < nrows ? min((pbase + trow + 1) / P.c, P.cols) : 0;
 
-    // ---- key tile (keys key0 .. key0+255), 8 loads per wave (wave w: keys 32w .. 32w+31, in
-    // kl for w < 4, else kh); the block-table reads come first, all in flight together.  A
-    // key that is not visible or whose page is outside the cache loads the cache's first row
-    // and is masked afterwards.
-    {
+    // ---- key tile kt into buffer b: 8 LDS-direct loads per wave (wave w: keys 32w .. 32w+31);
+    // a key that is not visible or whose page is outside the cache loads the cache's first
+    // row and is flagged (its logits are written as zero).
+    auto load_tile = [&](int kt, int b) __attribute__((always_inline)) {
       int page[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const int jk = key0 + 32 * w + 4 * i + (lane >> 4);
+        const int jk = kt * kMfmaKeys + 32 * w + 4 * i + l4;
         const int col = jk < vis_max ? min(jk / P.Pc, P.cbt_width - 1) : 0;
         page[i] = P.cbt[(int64_t)r * P.cbt_stride + col];
       }
       asm volatile("" : "+v"(page[0]), "+v"(page[1]), "+v"(page[2]), "+v"(page[3]),
                    "+v"(page[4]), "+v"(page[5]), "+v"(page[6]), "+v"(page[7]));
-      uint8_t* const kdst = w < 4 ? kl : kh;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const int j = 32 * w + 4 * i + (lane >> 4), jk = key0 + j;
+        const int j = 32 * w + 4 * i + l4, jk = kt * kMfmaKeys + j;
         const bool ok = jk < vis_max && jk / P.Pc < P.cbt_width && page[i] >= 0 &&
                         page[i] < P.c_pages;
         const int64_t off = ok ? ((int64_t)page[i] * P.Pc + jk % P.Pc) * kHeadDim * 2 : 0;
-        lds_dma16(ckv + off + 16 * ((lane & 15) ^ (j & 15)),
-                  kdst + ((32 * w + 4 * i) & 127) * 256);
-        if ((lane & 15) == 0) kok[j] = ok;
-      }
-    }
-    // ---- Q slab sl: head sl % Hi of row block rb_first + sl / Hi (rows past the request
-    // repeat its last row), 4 loads per wave.
-    const int nslabs = (rb_end - rb_first) * P.Hi;
-    auto load_q = [&](int sl, uint8_t* dst) {
-      const int rb = rb_first + sl / P.Hi, h = sl % P.Hi;
-      const int last = min(kMfmaRows, n - rb * kMfmaRows) - 1;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 16 * w + 4 * i + (lane >> 4);
-        const int64_t grow = q0 + rb * kMfmaRows + min(t, last);
-        lds_dma16(qb + ((grow * P.Hi + h) * kHeadDim) * 2 + 16 * ((lane & 15) ^ (t & 15)),
-                  dst + (16 * w + 4 * i) * 256);
+        lds_dma16(ckv + off + 16 * (l16 ^ (j & 15)), kbuf[b] + (32 * w + 4 * i) * 256);
+        if (l16 == 0) kok[b][j] = ok;
       }
     };
-    load_q(0, lds[0]);
-    if (nslabs > 1) load_q(1, lds[1]);
-    wait_vmcnt(nslabs > 1 ? 4 : 0);  // the key tile and slab 0 have landed
-    if (tid == 0) lds_store_u32(&s_item[(it + 1) & 1], next);
-    barrier();
+    load_tile(t0, t0 & 1);
 
-    // ---- this wave's key fragments: keys 64wc + 16kk + lane%16, dims 32ks + 8(lane/16) .. +7
-    // (row 64(wc%2) + 16kk + lane%16 of its half: slot (4ks + lane/16) ^ (lane%16)), and the
-    // validity of those keys.
-    bf16x8_t kfr[4][4];
-    uint32_t okk[4];
+    // ---- Q of this wave's rows (rows past the request repeat its last row), all heads; heads
+    // past Hi are zero (their products add exact zeros).
+    bf16x8_t qf[kMfmaMaxHeads][4];
     {
-      const uint8_t* kt_half = wc < 2 ? kl : kh;
+      const int t = min(trow, nrows - 1);
+      const char* qrow = qb + (int64_t)(q0 + rb * kMfmaRows + t) * P.Hi * kHeadDim * 2;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const uint32_t a0 = tile_chunk_addr(kt_half, 64 * (wc & 1) + l16, 4 * ks + l4);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          asm volatile("ds_read_b128 %0, %1" : "=v"(kfr[kk][ks]) : "v"(a0 + 4096u * kk));
-      }
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        asm volatile("ds_read_u8 %0, %1"
-                     : "=v"(okk[kk])
-                     : "v"(lds_addr(kok + 64 * wc + 16 * kk + l16)));
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(kfr[0][0]), "+v"(kfr[0][1]), "+v"(kfr[0][2]),
-                   "+v"(kfr[0][3]), "+v"(kfr[1][0]), "+v"(kfr[1][1]), "+v"(kfr[1][2]),
-                   "+v"(kfr[1][3]), "+v"(okk[0]), "+v"(okk[1]), "+v"(okk[2]), "+v"(okk[3]));
-      asm volatile("" : "+v"(kfr[2][0]), "+v"(kfr[2][1]), "+v"(kfr[2][2]), "+v"(kfr[2][3]),
-                   "+v"(kfr[3][0]), "+v"(kfr[3][1]), "+v"(kfr[3][2]), "+v"(kfr[3][3]));
-    }
-    // ---- max |k| over the valid keys of each 128-key half (upper bounds for the top-k's
-    // error band), on the bf16 bit patterns (order-preserving for |k|): per wave, then over
-    // the two waves of each half.
-    {
-      uint32_t mk = 0;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        uint32_t m = 0;
+      for (int h = 0; h < kMfmaMaxHeads; ++h) {
+        const int hh = min(h, P.Hi - 1);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          const u32x4_t u = __builtin_bit_cast(u32x4_t, kfr[kk][ks]);
+          const u32x4_t u = *reinterpret_cast<const u32x4_t*>(
+              qrow + (int64_t)(hh * kHeadDim + 32 * ks + 8 * l4) * 2);
+          qf[h][ks] = __builtin_bit_cast(bf16x8_t, h < P.Hi ? u : u32x4_t{0u, 0u, 0u, 0u});
+        }
+      }
+    }
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        P.logits + (int64_t)(q0 + rb * kMfmaRows) * P.col_stride, 0,
+        nrows * P.col_stride * 4, 0x00020000);
+
+    // Stores this wave issued while multiplying the previous tile (after this tile's loads,
+    // which were issued at the start of that step): they may stay in flight.
+    int st_prev = 0;
+    for (int kt = t0; kt < t1; ++kt) {
+      const int b = kt & 1;
+      // Tile kt has landed once only the stores issued after its loads are outstanding.
+      wait_vmcnt(st_prev);
+      if (kt == t0 && tid == 0) lds_store_u32(&s_item[(it + 1) & 1], next);
+      barrier();  // tile kt visible; every wave is done with tile kt-1 (buffer b ^ 1)
+      if (kt + 1 < t1) load_tile(kt + 1, b ^ 1);
+      int st = 0;
+      // Groups of four 16-key blocks; the A fragments of the next k-step are read while the
+      // current one is multiplied.
+      bf16x8_t kf[2][4];
+      auto read_kf = [&](int kg0, int ks, bf16x8_t (&dst)[4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          asm volatile("ds_read_b128 %0, %1"
+                       : "=v"(dst[q])
+                       : "v"(kaddr[b][ks] + 4096u * (kg0 + q)));
+      };
+      read_kf(0, 0, kf[0]);
+#pragma unroll
+      for (int kg0 = 0; kg0 < 16; kg0 += 4) {
+        f32x4_t acc[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[q] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          bf16x8_t(&cur)[4] = kf[ks & 1];
+          asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(cur[0]), "+v"(cur[1]), "+v"(cur[2]),
+                       "+v"(cur[3]));
+          if (ks < 3) {
+            read_kf(kg0, ks + 1, kf[(ks + 1) & 1]);
+          } else if (kg0 + 4 < 16) {
+            read_kf(kg0 + 4, 0, kf[(ks + 1) & 1]);
+          }
+#pragma unroll
+          for (int h = 0; h < kMfmaMaxHeads; ++h) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur[q], qf[h][ks], acc[q], 0, 0, 0);
+          }
+        }
+        // Groups kg0 .. kg0+3 are final: element e of group kg is key 16kg + 4(lane/16) + e
+        // of row trow.  A group of 4 keys is written when its first key is visible to the row
+        // (the rest lies inside the row's stride, past its visible keys, where the top-k does
+        // not read); keys that were not loaded are written as zero.
+        uint32_t okm[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          asm volatile("ds_read_b32 %0, %1"
+                       : "=v"(okm[q])
+                       : "v"(lds_addr(&kok[b][16 * (kg0 + q) + 4 * l4])));
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(okm[0]), "+v"(okm[1]), "+v"(okm[2]),
+                     "+v"(okm[3]), "+v"(kf[0][0]), "+v"(kf[0][1]), "+v"(kf[0][2]),
+                     "+v"(kf[0][3]));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          f32x4_t v = acc[q];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const uint32_t x = u[e] & 0x7FFF7FFFu;
-            m = max(m, max(x & 0xFFFFu, x >> 16));
+            if (!((okm[q] >> (8 * e)) & 0xFFu)) v[e] = 0.0f;
           }
-        }
-        mk = okk[kk] ? max(mk, m) : mk;
-      }
-      mk = wave_max_u32(mk);
-      if (lane == 0 && wr == 0) lds_store_u32(&red[wc >> 1][wc & 1], mk);
-    }
-    barrier();  // red[] complete; the key tile is free for slabs 2 and 3
-    if (tid < 2 && 2 * kt + tid < P.key_blocks) {
-      const uint32_t m = max(lds_load_u32(&red[tid][0]), lds_load_u32(&red[tid][1]));
-      P.kmax[(int64_t)r * P.key_blocks + 2 * kt + tid] = __uint_as_float(m << 16);
-    }
-    if (nslabs > 2) load_q(2, lds[2]);
-
-    f32x4_t acc[4][4];
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-#pragma unroll
-      for (int b = 0; b < 4; ++b) acc[a][b] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    }
-    // Bit k of `stored`: the iteration k+1 back wrote its row block (16 stores per wave).
-    uint32_t stored = 0;
-    // Per-lane LDS addresses of this wave's Q fragments in buffers 0/1 and 2/3 for each K step
-    // (row 64wr + lane%16, chunk 4ks + lane/16); the buffer and the row block go in the
-    // instruction's offset.
-    uint32_t qaddr[2][4];
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        qaddr[hb][ks] = tile_chunk_addr(lds[2 * hb], 64 * wr + (lane & 15), 4 * ks + (lane >> 4));
-    }
-    // One slab: wait for it, load slab sl+3 into the buffer slab sl-1 used, multiply, and
-    // write the row block when its last head is done.
-    auto step = [&](int sl, auto buf_tag) {
-      constexpr int kBuf = decltype(buf_tag)::value;
-      uint8_t* const next = lds[(kBuf + 3) & 3];
-      // Memory operations this wave issued after slab sl's loads: the loads of slabs sl+1
-      // and sl+2 (4 each), and the stores of iterations max(0, sl-3) .. sl-1.
-      const int dmas = 4 * (min(nslabs - 1, sl + 2) - sl);
-      int after = dmas + 16 * __builtin_popcount(stored & 7u);
-      if (after > 24) after = dmas;  // fewer than issued: a stricter wait
-      wait_vmcnt(after);
-      barrier();  // slab sl visible to all waves; slab sl-1's buffer is free
-      if (sl + 3 < nslabs) load_q(sl + 3, next);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        // The slab reads are issued as inline assembly, which the compiler's own wait
-        // insertion does not track: it would otherwise wait for every load into LDS in
-        // flight (including the next slabs') before reading this one, which the wait above
-        // already guarantees has landed.
-        bf16x8_t qfr[4];
-        const uint32_t qa = qaddr[kBuf >> 1][ks];
-        qfr[0] = lds_read16_off<(kBuf & 1) * kMfmaRows * 256 + 0 * 4096>(qa);
-        qfr[1] = lds_read16_off<(kBuf & 1) * kMfmaRows * 256 + 1 * 4096>(qa);
-        qfr[2] = lds_read16_off<(kBuf & 1) * kMfmaRows * 256 + 2 * 4096>(qa);
-        qfr[3] = lds_read16_off<(kBuf & 1) * kMfmaRows * 256 + 3 * 4096>(qa);
-        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(qfr[0]), "+v"(qfr[1]), "+v"(qfr[2]),
-                     "+v"(qfr[3]));
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk)
-            acc[rr][kk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfr[kk][ks], qfr[rr],
-                                                                  acc[rr][kk], 0, 0, 0);
+          const int j = kt * kMfmaKeys + 16 * (kg0 + q) + 4 * l4;
+          const uint32_t off =
+              j < vis_t ? (uint32_t)(trow * P.col_stride + j) * 4u : 0xFFFFFFF0u;
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), rs, off, 0, 0);
+          ++st;
         }
       }
-      const bool last_head = sl % P.Hi == P.Hi - 1;
-      stored = (stored << 1) | (last_head ? 1u : 0u);
-      if (last_head) {
-        // ---- row block done.  Accumulator element e of block (rr, kk) is key 64wc + 16kk +
-        // 4(lane/16) + e of row 64wr + 16rr + lane%16.  A group of 4 keys is written when its
-        // first key is visible to the row (the rest of the group lies inside the row's stride
-        // and past its visible keys, which the top-k does not read).
-        const int rb = rb_first + sl / P.Hi;
-        const int nrows = min(kMfmaRows, n - rb * kMfmaRows);
-        const int pbase = L - n + rb * kMfmaRows;
-        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-            P.logits + (int64_t)(q0 + rb * kMfmaRows) * P.col_stride, 0,
-            nrows * P.col_stride * 4, 0x00020000);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int t = 64 * wr + 16 * rr + (lane & 15);
-          const int vis = t < nrows ? min((pbase + t + 1) / P.c, P.cols) : 0;
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk) {
-            const int j = 64 * wc + 16 * kk + 4 * (lane >> 4);
-            const uint32_t okm = *reinterpret_cast<const uint32_t*>(kok + j);
-            f32x4_t v = acc[rr][kk];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              if (!((okm >> (8 * e)) & 0xFFu)) v[e] = 0.0f;
-            }
-            const uint32_t off = key0 + j < vis ? (uint32_t)(t * P.col_stride + key0 + j) * 4u
-                                                : 0xFFFFFFF0u;
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), rs, off, 0,
-                                                   0);
-            acc[rr][kk] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-          }
-        }
-      }
-    };
-    for (int sl = 0; sl < nslabs; sl += 4) {
-      step(sl, std::integral_constant<int, 0>{});
-      if (sl + 1 < nslabs) step(sl + 1, std::integral_constant<int, 1>{});
-      if (sl + 2 < nslabs) step(sl + 2, std::integral_constant<int, 2>{});
-      if (sl + 3 < nslabs) step(sl + 3, std::integral_constant<int, 3>{});
+      st_prev = st;
     }
   }
 }
@@ -384,7 +279,7 @@ __global__ __launch_bounds__(512) void logits_mfma_kernel(SelectParams P, int ro
 }  // namespace
 
 hipError_t launch_logits_mfma(const SelectParams& P, int max_query_len, hipStream_t s) {
-  // One persistent workgroup per CU (a multiple of 8, one set of queues per XCD).
+  // One persistent workgroup per CU.
   static int cus[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
@@ -396,7 +291,7 @@ hipError_t launch_logits_mfma(const SelectParams& P, int max_query_len, hipStrea
     cus[dev] = n;
   }
   const int row_blocks = (max_query_len + kMfmaRows - 1) / kMfmaRows;
-  const unsigned grid = (unsigned)((cus[dev] + 7) / 8 * 8);
+  const unsigned grid = (unsigned)cus[dev];
   hipLaunchKernelGGL(logits_mfma_kernel, dim3(grid), dim3(512), 0, s, P, row_blocks);
   return hipGetLastError();
 }

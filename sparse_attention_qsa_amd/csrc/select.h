@@ -28,6 +28,8 @@ struct SelectParams {
 
 // bf16 requests with more rows than this are scored by the matrix-core logits kernel.
 constexpr int kMfmaMinRows = 16;
+// ... and at most this many indexer heads (their Q is held in registers).
+constexpr int kMfmaMaxHeads = 8;
 
 // Launchers (each next to its kernels); arguments are validated by the caller.
 hipError_t launch_logits_valu(const SelectParams& P, int rows_per_chunk, hipStream_t s);

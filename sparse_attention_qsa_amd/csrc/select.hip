@@ -60,8 +60,9 @@ hipError_t launch_topk(const qsa_topk_args& a, const TopkLayout& L, char* ws, hi
   // (and every fp8 request) by the VALU kernel; each kernel skips the other's requests.
   // (The matrix-core kernel sums the heads in its accumulator: ReLU-sum requests stay on the
   // vector units.)
-  const bool mfma = !P.fp8 && !P.relu && a.max_query_len > kMfmaMinRows;
-  P.mfma_min_rows = (P.fp8 || P.relu) ? INT32_MAX : kMfmaMinRows;
+  const bool mfma_ok = !P.fp8 && !P.relu && P.Hi <= kMfmaMaxHeads;
+  const bool mfma = mfma_ok && a.max_query_len > kMfmaMinRows;
+  P.mfma_min_rows = mfma_ok ? kMfmaMinRows : INT32_MAX;
   if (phase == Phase::kSecond) return launch_topk_select(P, s);
   const int rows_per_chunk = mfma ? kMfmaMinRows : a.max_query_len;
   hipError_t e = P.relu ? launch_logits_valu_relu(P, s) : launch_logits_valu(P, rows_per_chunk, s);
