@@ -34,7 +34,8 @@ METRIC = "decode rows/sec + achieved HBM GB/s, QSA indexer+sparse GQA at 32k ctx
 # they are built from (a traffic record applies only while these are unchanged).
 KERNELS = {
     "prep_compress_kernel": ("compress", ["qsa_internal.h", "compress.hip"]),
-    "logits_valu_kernel": ("logits", ["qsa_internal.h", "select.h", "select.hip", "logits.hip"]),
+    "logits_valu_kernel": ("logits", ["qsa_internal.h", "select.h", "select.hip", "logits_tile.h",
+                                      "logits.hip", "logits_list.hip"]),
     "topk_kernel": ("block_topk", ["qsa_internal.h", "select.h", "select.hip", "topk.hip"]),
     "gqa_partial_kernel": ("gqa_partial", ["qsa_internal.h", "gqa.hip"]),
     "gqa_merge_kernel": ("gqa_merge", ["qsa_internal.h", "gqa.hip"]),

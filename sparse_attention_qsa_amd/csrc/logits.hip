@@ -3,146 +3,14 @@
 // (sum_h q[h]) . k, written to the logits workspace together with the per-128-key bound of
 // max |k| that the top-k's error band needs.  Follows the scoring step of QSAIndexer.forward
 // (page "vllm.models.qwen4_exp.nvidia.qsa").
-#include "select.h"
+// This file holds the one-item-per-workgroup kernel and the launchers; the persistent variant
+// for grids that do not fit the chip in one round is in logits_list.hip (a translation unit of
+// its own: beside it, the compiler schedules this kernel's loads differently).
+#include "logits_tile.h"
 
 namespace qsa {
 namespace {
-// Lane layout of a 64-key wave tile.  A key's row is split over kLanes lanes of 16 bytes: 8 for
-// fp8 (128-byte rows), 16 for bf16 (256-byte rows), so one wave load instruction reads
-// 64 / kLanes consecutive rows -- 1 KiB of contiguous cache -- and a tile takes kLoads
-// instructions.  Lane `x = lane % kLanes` of group `g = lane / kLanes` holds, in load `it`, dims
-// of key `it * (64 / kLanes) + g`: 16x .. 16x+15 (fp8) or 8x .. 8x+7 (bf16).
-template <bool FP8>
-struct KeyLanes {
-  static constexpr int kLanes = FP8 ? 8 : 16;
-  static constexpr int kKeysPerLoad = 64 / kLanes;
-  static constexpr int kLoads = 64 / kKeysPerLoad;
-  static constexpr int kDims = FP8 ? 16 : 8;  // dims per lane per key
-};
-
-// Loads tile `tile` of the workgroup (keys tile*256 + w*64 + 0..63) for this lane.  `rows` holds
-// the cache row of each of the workgroup's keys (-1: out of range or not visible; such a key
-// reads the cache's first row and is masked when scored).  `okm` bit `it` marks load `it` valid.
-template <bool FP8>
-__device__ __forceinline__ void load_key_tile(const SelectParams& P, const int32_t* rows,
-                                              int tile, int w, int lane,
-                                              uint32_t (&raw)[KeyLanes<FP8>::kLoads][4],
-                                              uint32_t& okm) {
-  using K = KeyLanes<FP8>;
-  const char* base = reinterpret_cast<const char*>(P.ckv) + (lane % K::kLanes) * 16;
-  const int key0 = tile * kLogitsKeysPerWG + w * 64 + lane / K::kLanes;
-  int row[K::kLoads];
-#pragma unroll
-  for (int it = 0; it < K::kLoads; ++it) row[it] = rows[key0 + it * K::kKeysPerLoad];
-  // The mask is applied when the tile is scored: a select here would consume the loaded words
-  // at once and make the wave wait for them.
-  okm = 0;
-#pragma unroll
-  for (int it = 0; it < K::kLoads; ++it) {
-    okm |= (uint32_t)(row[it] >= 0) << it;
-    const uint4 x = *reinterpret_cast<const uint4*>(
-        base + (int64_t)max(row[it], 0) * (kHeadDim * (FP8 ? 1 : 2)));
-    raw[it][0] = x.x;
-    raw[it][1] = x.y;
-    raw[it][2] = x.z;
-    raw[it][3] = x.w;
-  }
-}
-
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-
-// Sum over the N lanes (8 or 16, aligned) that share a key, on DPP: swap adjacent lanes, then
-// lane pairs, then mirror the quads of each half-row, then (N = 16) the halves of the row.
-// Every lane ends with the N-lane sum.
-template <int N>
-__device__ __forceinline__ float group_sum(float d) {
-  d += dpp_f32<0xB1>(d);   // quad_perm [1,0,3,2]
-  d += dpp_f32<0x4E>(d);   // quad_perm [2,3,0,1]
-  d += dpp_f32<0x141>(d);  // row_half_mirror
-  if (N == 16) d += dpp_f32<0x140>(d);  // row_mirror
-  return d;
-}
-
-// Scores the tile in `raw` against NR folded rows (qf: this lane's dims of each row) and writes
-// the logits.  After the group sums, lane x of group g keeps the sum of load it = x, so every
-// lane ends with one key -- it*(64/kLanes) + g -- and each row is written with one store.
-// Updates the lane's running max |k|.  RELU: the NR "rows" are the heads of one row, and its
-// logit is the sum over heads of max(0, head product).
-template <bool FP8, int NR, bool RELU = false>
-__device__ __forceinline__ void score_key_tile(const SelectParams& P,
-                                               const uint32_t (&raw)[KeyLanes<FP8>::kLoads][4],
-                                               uint32_t okm, const float (&qf)[NR][16], int nr,
-                                               int row0, int j0, int vis_max, int lane,
-                                               bool track_kmax, float& kmax) {
-  using K = KeyLanes<FP8>;
-  const int x = lane % K::kLanes, g = lane / K::kLanes;
-  // One-hot weight of load `it` for this lane, as arithmetic: a compare would tie up a scalar
-  // register pair per load.
-  const uint32_t onehot = 1u << x;
-  float res[NR];
-#pragma unroll
-  for (int rr = 0; rr < NR; ++rr) res[rr] = 0.0f;
-#pragma unroll
-  for (int it = 0; it < K::kLoads; ++it) {
-    float k[16];
-    const bool ok = (okm >> it) & 1u;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t word = raw[it][i];
-      if (FP8) {
-        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
-        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
-        k[4 * i] = lo[0];
-        k[4 * i + 1] = lo[1];
-        k[4 * i + 2] = hi[0];
-        k[4 * i + 3] = hi[1];
-      } else {
-        k[2 * i] = bf16lo(word);
-        k[2 * i + 1] = bf16hi(word);
-      }
-    }
-    // A masked key reads the cache's first row, whatever it holds: its values are dropped by
-    // selects (never by arithmetic, which a NaN there would survive).
-    if (track_kmax) {
-      float m = fabsf(k[0]);
-#pragma unroll
-      for (int i = 1; i < K::kDims; ++i) m = fmaxf(m, fabsf(k[i]));
-      kmax = fmaxf(kmax, ok ? m : 0.0f);
-    }
-#pragma unroll
-    for (int rr = 0; rr < NR; ++rr) {
-      float d = 0.0f;
-#pragma unroll
-      for (int i = 0; i < K::kDims; ++i) d = fmaf(qf[rr][i], k[i], d);
-      d = group_sum<K::kLanes>(ok ? d : 0.0f);
-      res[rr] = fmaf((float)((onehot >> it) & 1u), d, res[rr]);  // exact: one term is d
-    }
-  }
-  // Unconditional buffer stores: a row's record ends at its visible keys (none for a row past
-  // nr), so the hardware drops the rest; lanes x >= kLoads hold no key.
-  const int j = j0 + x * K::kKeysPerLoad + g;
-  if (RELU) {
-    float sum = fmaxf(res[0], 0.0f);
-#pragma unroll
-    for (int rr = 1; rr < NR; ++rr) sum = sum + fmaxf(res[rr], 0.0f);
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        P.logits + (int64_t)row0 * P.col_stride, 0, vis_max * 4, 0x00020000);
-    const uint32_t off = x < K::kLoads ? (uint32_t)j * 4u : 0xFFFFFFF0u;
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sum), rs, off, 0, 0);
-    return;
-  }
-#pragma unroll
-  for (int rr = 0; rr < NR; ++rr) {
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        P.logits + (int64_t)(rr < nr ? row0 + rr : row0) * P.col_stride, 0,
-        rr < nr ? vis_max * 4 : 0, 0x00020000);
-    const uint32_t off = x < K::kLoads ? (uint32_t)j * 4u : 0xFFFFFFF0u;
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(res[rr]), rs, off, 0, 0);
-  }
-}
+using namespace logits_tile;
 
 // Grid (wg_per_req, R), 256 threads.  Workgroup k of request r scores the request's keys
 // 1024k .. 1024k+1023 (4 tiles of 256) against every row of the request, NR rows at a time.
@@ -151,7 +19,9 @@ __device__ __forceinline__ void score_key_tile(const SelectParams& P,
 // LDS once; two tiles are in flight from the start and each reload is issued before the other
 // buffer's tile is scored.
 // RELU: one row at a time, its NR = 8 heads held unfolded as the scorer's rows.
-template <bool FP8, int NR, bool RELU = false>
+// KMAX: the call also has matrix-core requests, for which this kernel only takes the per-block
+// bound of max |k| (a separate instance, so that the decode instances carry no such branch).
+template <bool FP8, int NR, bool RELU = false, bool KMAX = false>
 __global__ __launch_bounds__(kLogitsThreads) __attribute__((amdgpu_waves_per_eu(NR >= 4 ? 2 : 4)))
 void logits_valu_kernel(SelectParams P) {
   using KL = KeyLanes<FP8>;
@@ -178,9 +48,9 @@ void logits_valu_kernel(SelectParams P) {
   const int n = max(0, min(P.qsl[r + 1], P.T) - q0), L = P.seq_lens[r];
   // The MFMA kernel, which runs next, starts its work queues from zero.
   if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 8) P.work[threadIdx.x] = 0;
-  // Requests with many rows are scored by the MFMA kernel; for them this kernel only takes the
-  // per-block bound of max |k| the top-k needs (one pass over their keys).
-  const bool kmax_only = n > P.mfma_min_rows;  // block-uniform
+  // Requests with many rows are scored by the MFMA kernel; for them the KMAX instance only takes
+  // the per-block bound of max |k| the top-k needs (one pass over their keys).
+  if (!KMAX && n > P.mfma_min_rows) return;  // block-uniform, before any barrier
   const int vis_max = (n > 0 && n <= L) ? min(L / P.c, P.cols) : 0;
   // Barrier without a memory fence (a fence would wait for every load in flight); the LDS
   // writes before it are complete, and global loads are waited for where their data is used.
@@ -197,32 +67,36 @@ void logits_valu_kernel(SelectParams P) {
       const bool ok = j < vis_max && col[i] < P.cbt_width && page[i] >= 0 && page[i] < P.c_pages;
       rows_s[threadIdx.x + kT * i] = ok ? page[i] * P.Pc + (j - col[i] * P.Pc) : -1;
     }
-    if (kmax_only) {
-      barrier();  // rows_s written
-#pragma unroll
-      for (int t = 0; t < kLogitsTilesPerWG; ++t) {
-        uint32_t a[KL::kLoads][4], ma;
-        load_key_tile<FP8>(P, rows_s, t, w, lane, a, ma);
-#pragma unroll
-        for (int it = 0; it < KL::kLoads; ++it) {
-          float m = 0.0f;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint32_t word = a[it][i];
-            if (FP8) {
-              const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
-              const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
-              m = fmaxf(m, fmaxf(fmaxf(fabsf(lo[0]), fabsf(lo[1])),
-                                 fmaxf(fabsf(hi[0]), fabsf(hi[1]))));
-            } else {
-              m = fmaxf(m, fmaxf(fabsf(bf16lo(word)), fabsf(bf16hi(word))));
+    if constexpr (KMAX) {
+      if (n > P.mfma_min_rows) {  // block-uniform
+        barrier();  // rows_s written
+        #pragma unroll
+        for (int t = 0; t < kLogitsTilesPerWG; ++t) {
+          uint32_t a[KL::kLoads][4], ma;
+          load_key_tile<FP8>(P, rows_s, t, w, lane, a, ma);
+          #pragma unroll
+          for (int it = 0; it < KL::kLoads; ++it) {
+            float m = 0.0f;
+            #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const uint32_t word = a[it][i];
+              if (FP8) {
+                const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
+                const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
+                m = fmaxf(m, fmaxf(fmaxf(fabsf(lo[0]), fabsf(lo[1])),
+                                   fmaxf(fabsf(hi[0]), fabsf(hi[1]))));
+              } else {
+                m = fmaxf(m, fmaxf(fabsf(bf16lo(word)), fabsf(bf16hi(word))));
+              }
             }
+            kmax = fmaxf(kmax, ((ma >> it) & 1u) ? m : 0.0f);  // masked keys dropped by a select
           }
-          kmax = fmaxf(kmax, ((ma >> it) & 1u) ? m : 0.0f);  // masked keys dropped by a select
         }
       }
     }
-    for (int rr0 = 0; rr0 < (kmax_only ? 0 : n); rr0 += (RELU ? 1 : NR)) {
+    // (KMAX: the rows of a matrix-core request are not scored here.)
+    const int n_scored = KMAX ? (n > P.mfma_min_rows ? 0 : n) : n;
+    for (int rr0 = 0; rr0 < n_scored; rr0 += (RELU ? 1 : NR)) {
       const int nr = RELU ? NR : min(NR, n - rr0);
       // Head-folded Q of the chunk's rows: each of the first nr*128 threads owns one (row, dim)
       // and loads all its heads at once (clamped to Hi - 1, the extra terms added as zero).
@@ -298,33 +172,41 @@ void logits_valu_kernel(SelectParams P) {
   }
 }
 
+// Workgroups the chip holds at once: two per CU with up to two rows per chunk (four waves per
+// SIMD), one with four or more.
+constexpr int kCUs = 256;
+
+template <bool FP8, int NR, bool RELU, bool KMAX>
+hipError_t launch_valu(const SelectParams& P, hipStream_t s) {
+  const int per_cu = NR >= 4 ? 1 : 2;
+  const int64_t dense = (int64_t)P.R * P.key_tiles, resident = (int64_t)kCUs * per_cu;
+  if (dense <= resident || P.R > kLogitsListReqs) {
+    hipLaunchKernelGGL((logits_valu_kernel<FP8, NR, RELU, KMAX>), dim3(P.key_tiles, P.R),
+                       dim3(kLogitsThreads), 0, s, P);
+    return hipGetLastError();
+  }
+  return launch_logits_list(P, NR, RELU, KMAX, (unsigned)resident, s);
+}
+
 template <bool FP8>
-hipError_t launch_logits(const SelectParams& P, int rows_per_chunk, hipStream_t s) {
-  const dim3 grid(P.key_tiles, P.R);
-  if (rows_per_chunk <= 1)
-    hipLaunchKernelGGL((logits_valu_kernel<FP8, 1>), grid, dim3(kLogitsThreads), 0, s, P);
-  else if (rows_per_chunk <= 2)
-    hipLaunchKernelGGL((logits_valu_kernel<FP8, 2>), grid, dim3(kLogitsThreads), 0, s, P);
-  else
-    hipLaunchKernelGGL((logits_valu_kernel<FP8, 4>), grid, dim3(kLogitsThreads), 0, s, P);
-  return hipGetLastError();
+hipError_t launch_logits(const SelectParams& P, int rows_per_chunk, bool mfma, hipStream_t s) {
+  if (mfma && !FP8)  // the matrix-core kernel scores the requests of more than 16 rows
+    return launch_valu<FP8, 4, false, true>(P, s);
+  if (rows_per_chunk <= 1) return launch_valu<FP8, 1, false, false>(P, s);
+  if (rows_per_chunk <= 2) return launch_valu<FP8, 2, false, false>(P, s);
+  return launch_valu<FP8, 4, false, false>(P, s);
 }
 
 }  // namespace
 
 hipError_t launch_logits_valu_relu(const SelectParams& P, hipStream_t s) {
-  const dim3 grid(P.key_tiles, P.R);
-  if (P.fp8)
-    hipLaunchKernelGGL((logits_valu_kernel<true, 8, true>), grid, dim3(kLogitsThreads), 0, s, P);
-  else
-    hipLaunchKernelGGL((logits_valu_kernel<false, 8, true>), grid, dim3(kLogitsThreads), 0, s,
-                       P);
-  return hipGetLastError();
+  return P.fp8 ? launch_valu<true, 8, true, false>(P, s) : launch_valu<false, 8, true, false>(P, s);
 }
 
-hipError_t launch_logits_valu(const SelectParams& P, int rows_per_chunk, hipStream_t s) {
-  return P.fp8 ? launch_logits<true>(P, rows_per_chunk, s)
-               : launch_logits<false>(P, rows_per_chunk, s);
+hipError_t launch_logits_valu(const SelectParams& P, int rows_per_chunk, bool mfma,
+                              hipStream_t s) {
+  return P.fp8 ? launch_logits<true>(P, rows_per_chunk, mfma, s)
+               : launch_logits<false>(P, rows_per_chunk, mfma, s);
 }
 
 }  // namespace qsa

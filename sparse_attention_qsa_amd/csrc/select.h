@@ -32,8 +32,15 @@ constexpr int kMfmaMinRows = 16;
 constexpr int kMfmaMaxHeads = 8;
 
 // Launchers (each next to its kernels); arguments are validated by the caller.
-hipError_t launch_logits_valu(const SelectParams& P, int rows_per_chunk, hipStream_t s);
+// mfma: the call has requests scored on the matrix cores (rows_per_chunk is then 16).
+hipError_t launch_logits_valu(const SelectParams& P, int rows_per_chunk, bool mfma,
+                              hipStream_t s);
 hipError_t launch_logits_valu_relu(const SelectParams& P, hipStream_t s);
+// The persistent variant (logits_list.hip): `grid` workgroups walk the call's work list of
+// (request, 1024-key item) pairs; at most kLogitsListReqs requests.
+constexpr int kLogitsListReqs = 1024;
+hipError_t launch_logits_list(const SelectParams& P, int nr, bool relu, bool kmax, unsigned grid,
+                              hipStream_t s);
 hipError_t launch_logits_mfma(const SelectParams& P, int max_query_len, hipStream_t s);
 hipError_t launch_topk_select(const SelectParams& P, hipStream_t s);
 

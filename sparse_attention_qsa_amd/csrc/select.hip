@@ -65,7 +65,8 @@ hipError_t launch_topk(const qsa_topk_args& a, const TopkLayout& L, char* ws, hi
   P.mfma_min_rows = mfma_ok ? kMfmaMinRows : INT32_MAX;
   if (phase == Phase::kSecond) return launch_topk_select(P, s);
   const int rows_per_chunk = mfma ? kMfmaMinRows : a.max_query_len;
-  hipError_t e = P.relu ? launch_logits_valu_relu(P, s) : launch_logits_valu(P, rows_per_chunk, s);
+  hipError_t e = P.relu ? launch_logits_valu_relu(P, s)
+                        : launch_logits_valu(P, rows_per_chunk, mfma, s);
   if (e != hipSuccess) return e;
   if (mfma && (e = launch_logits_mfma(P, a.max_query_len, s)) != hipSuccess) return e;
   if (phase == Phase::kFirst) return hipSuccess;

@@ -129,6 +129,82 @@ def test_full_size_decode_32k_fp8_kv_on_sampled_rows():
     assert err <= TOL["bf16"]
 
 
+def test_full_size_fp8_decode_on_sampled_rows():
+    """The fp8-indexer decode workload at the size bench.py times (128 requests of 4096..65536
+    tokens), in that launch configuration: its logits grid does not fit the chip in one round,
+    so the persistent work-list kernel scores it."""
+    wl = workload("fp8_decode", num_requests=128, lengths=("uniform", 4096, 65536))
+    L = wl.seq_lens_host
+    rows = sorted({0, 63, 127, int(np.argmax(L)), int(np.argmin(L))})
+    log(f"full-size fp8_decode, sampled rows {rows}")
+    ref = oracle_step(wl, rows=rows)
+    st = run_gpu(wl)
+    packed = to_np(st.packed)
+    assert np.array_equal(packed[rows], ref.packed[rows])
+    err = max_abs(gpu_out_f64(st)[rows], ref.out[rows])
+    log(f"  max-abs {err:.3e}")
+    assert err <= TOL["fp8"]
+    # Every row (one per request, p = L - 1, at least 512 visible blocks): kb*c plus the tail.
+    W, c = wl.output_width, wl.compress_ratio
+    assert np.array_equal(packed[:, W], 2048 + L % c)
+    for i in range(wl.num_tokens):
+        n = packed[i, W]
+        assert np.all(np.diff(packed[i, :n]) > 0) and packed[i, 0] >= 0
+        assert packed[i, n - 1] <= L[i] - 1 and np.all(packed[i, n:W] == -1)
+
+
+def test_full_size_spec_verify_on_sampled_rows():
+    """The speculative-verify workload at the size bench.py times (256 requests of 1024..131072
+    tokens, 4 MRoPE rows each, fp8 indexer), on rows of the longest, the shortest and a few
+    other requests."""
+    wl = workload("spec_verify_mrope", num_requests=256, lengths=("loguniform", 1024, 131072))
+    L = wl.seq_lens_host
+    reqs = sorted({0, 100, 255, int(np.argmax(L)), int(np.argmin(L))})
+    rows = [4 * r + i for r in reqs for i in (0, 3)]
+    log(f"full-size spec_verify_mrope, requests {reqs}")
+    ref = oracle_step(wl, rows=rows)
+    st = run_gpu(wl)
+    packed = to_np(st.packed)
+    assert np.array_equal(packed[rows], ref.packed[rows])
+    err = max_abs(gpu_out_f64(st)[rows], ref.out[rows])
+    log(f"  max-abs {err:.3e}")
+    assert err <= TOL["fp8"]
+
+
+@pytest.mark.parametrize("case", ["bf16_1row", "bf16_3rows", "relu"])
+def test_work_list_kernel_on_many_short_requests(case):
+    """Batches whose one-item-per-workgroup logits grid would not fit the chip in one round are
+    scored by the persistent work-list kernel: many requests of uneven length, each compared
+    row by row (bf16 indexer with one and three rows per request, and the ReLU-sum switch)."""
+    rows = 3 if case == "bf16_3rows" else 1
+    R = 300 if rows == 3 else 600
+    wl = workload("decode_32k", num_requests=R, lengths=("uniform", 2100, 6000), rows=rows)
+    agg = "relu" if case == "relu" else "sum"
+    log(f"work-list logits {case}: R={R} T={wl.num_tokens}")
+    ref = oracle_step(wl, with_attention=False, agg=agg)
+    st = QsaStep(wl, index_agg=agg)
+    st.compress()
+    st.topk()
+    torch.cuda.synchronize()
+    packed = to_np(st.packed)
+    assert np.array_equal(packed, ref.packed), (
+        f"{int((packed != ref.packed).any(axis=1).sum())} rows differ")
+
+
+def test_work_list_kernel_with_matrix_core_requests():
+    """Many prefill requests (17 rows each, scored on the matrix cores) in a call whose max |k|
+    pass needs the work-list kernel; sampled rows compared."""
+    wl = workload("chunked_prefill", num_requests=270, lengths=("uniform", 2100, 4000), rows=17)
+    rows = [0, 16, 17 * 100 + 5, 17 * 269 + 16]
+    log(f"work-list max|k| pass with MFMA requests: T={wl.num_tokens}")
+    ref = oracle_step(wl, rows=rows, with_attention=False)
+    st = QsaStep(wl)
+    st.compress()
+    st.topk()
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(st.packed)[rows], ref.packed[rows])
+
+
 def test_prefill_row_counts_select_exactly():
     """Calls with many rows take the prefill top-k configuration (three 8-bit radix passes,
     256 threads): 1280 rows here, every one compared."""
