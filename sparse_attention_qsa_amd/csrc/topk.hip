@@ -198,6 +198,8 @@ using TopkDecode16 = TopkCfg<512, 16, 12, 2, 1024, 2048>;
 using TopkDecode32 = TopkCfg<512, 32, 12, 2, 1024, 2048>;
 using TopkDecode1k = TopkCfg<1024, 32, 12, 2, 1024, 2048>;
 using TopkPrefill = TopkCfg<256, 16, 8, 3, 256, 512>;
+// Scores loaded before the request lookup (the rest once the visible range is known).
+constexpr int kTopkPrefetchCols = 8192;
 constexpr int kTopkPrefillMinRows = 1024;  // rows in the call from which TopkPrefill is used
 
 // Inclusive prefix sum over the 64 lanes of a wavefront: shifts within rows of 16, then the
@@ -268,13 +270,16 @@ __global__ __launch_bounds__(C::NT) void topk_kernel(SelectParams P) {
 
   // ---- loads that need only the row, issued first: this thread's fast scores (the row is
   // padded to col_stride), its share of the Q row, and the request metadata for the lookup.
+  // Scores past kTopkPrefetchCols are loaded once the row's visible range is known (a short
+  // request of a call with long ones would otherwise read a long row it does not use).
   const float* lg = P.logits + (int64_t)row * P.col_stride;
   const int jb = tid * E;
+  const int pf_end = min(P.col_stride, kTopkPrefetchCols);
   float sc[E];
 #pragma unroll
   for (int i = 0; i < E; i += 4) {
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (jb + i < P.col_stride) v = *reinterpret_cast<const float4*>(lg + jb + i);
+    if (jb + i < pf_end) v = *reinterpret_cast<const float4*>(lg + jb + i);
     sc[i] = v.x;
     sc[i + 1] = v.y;
     sc[i + 2] = v.z;
@@ -343,6 +348,16 @@ __global__ __launch_bounds__(C::NT) void topk_kernel(SelectParams P) {
     const int c = tid + k * NT;
     cbt_v[k] = (cbt_in_lds && c < cw) ? P.cbt[(int64_t)r * P.cbt_stride + c] : -1;
   }
+#pragma unroll
+  for (int i = 0; i < E; i += 4) {  // the rest of the visible scores
+    if (jb + i >= pf_end && jb + i < vis) {
+      const float4 v = *reinterpret_cast<const float4*>(lg + jb + i);
+      sc[i] = v.x;
+      sc[i + 1] = v.y;
+      sc[i + 2] = v.z;
+      sc[i + 3] = v.w;
+    }
+  }
   uint32_t key[E];  // order-preserving keys of the fast scores
 #pragma unroll
   for (int i = 0; i < E; ++i) {
@@ -363,8 +378,9 @@ __global__ __launch_bounds__(C::NT) void topk_kernel(SelectParams P) {
   for (int i = tid; i < mask_words; i += NT) sel_mask[i] = 0u;
 
   // ---- radix select.  Thread t reads the counts of bins (bins-1) - t*kPB - i (i < kPB): lower
-  // threads own higher bins, so a workgroup prefix sum gives the count above each bin.  The
-  // -inf entries land in the lowest bin, below any kb-th largest of the visible blocks.
+  // threads own higher bins, so a workgroup prefix sum gives the count above each bin.  Only
+  // visible blocks are counted (the -inf entries of a short row would all add to one bin, and
+  // its LDS atomics would serialise).
   // Histograms alternate between two buffers; a pass clears the one the next-but-one uses.
   uint32_t prefix = 0, pmask = 0;
   int krem = kb;
@@ -375,7 +391,8 @@ __global__ __launch_bounds__(C::NT) void topk_kernel(SelectParams P) {
 #pragma unroll
     for (int i = 0; i < E; ++i) {
       const uint32_t u = key[i];
-      if ((u & pmask) == prefix) atomicAdd(&h[(u >> shift) & (kRadixBins - 1)], 1);
+      if (jb + i < vis && (u & pmask) == prefix)
+        atomicAdd(&h[(u >> shift) & (kRadixBins - 1)], 1);
     }
     if (pass >= 1 && pass + 1 < C::PASSES) {  // the buffer of pass + 1 was read by pass - 1
       for (int i = tid; i < kRadixBins; i += NT) hist[(pass + 1) & 1][i] = 0;
