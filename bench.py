@@ -29,6 +29,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix cores, 2.5 PFLOP/s
+MFMA_MIN_ROWS = 16      # bf16 requests with more rows are scored on the matrix cores
 METRIC = "decode rows/sec + achieved HBM GB/s, QSA indexer+sparse GQA at 32k ctx"
 # The kernels timed one by one (each through the call that launches only it), with the sources
 # they are built from (a traffic record applies only while these are unchanged).
@@ -119,6 +121,19 @@ def algorithmic_bytes(wl, packed):
                   "gqa_partial_kernel": b_gqa - 2 * b_qgo,        # K/V, q, packed
                   "gqa_merge_kernel": 2 * b_qgo}                  # gate read, out written
     return per_call, per_kernel, int(np.int64(kv_tokens))
+
+
+def mfma_logits_flop(wl, index_agg):
+    """Causal-visible indexer logits FLOP of the requests the matrix-core kernel scores: every
+    (row, visible block) pair costs 2 * Hi * 128 (the per-head contraction it executes)."""
+    if wl.index_dtype != "bf16" or index_agg != "sum" or wl.index_heads > 8:
+        return 0
+    c, flop = wl.compress_ratio, 0
+    for L, n in zip(wl.seq_lens_host.tolist(), wl.rows_host.tolist()):
+        if n > MFMA_MIN_ROWS and n <= L:
+            p = range(L - n, L)
+            flop += sum((x + 1) // c for x in p) * 2 * wl.index_heads * 128
+    return int(flop)
 
 
 def traffic_record(kernel, workload):
@@ -336,6 +351,7 @@ def main():
         del plain
 
     alg, alg_k, kv_tokens = algorithmic_bytes(wl0, steps[0].packed)
+    mfma_flop = mfma_logits_flop(wl0, args.index_agg)
     step_bytes = sum(alg.values())
     rows_per_s = wl0.num_tokens / (ms_step * 1e-3)
     dom = max(per_kernel, key=per_kernel.get)      # the dominant kernel
@@ -375,6 +391,17 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
     }
+    if mfma_flop:
+        # The logits call of a workload with matrix-core requests: logits_valu_kernel only takes
+        # max |k| of their keys, logits_mfma_kernel scores them.  Timed together (one call), so
+        # the rate is a lower bound of the matrix-core kernel's own.
+        us = per_kernel["logits_valu_kernel"]
+        tf = mfma_flop / (us * 1e-6) / 1e12
+        out["mfma_logits"] = {"bound": "mfma", "kernels": ["logits_valu_kernel (max |k| pass)",
+                                                           "logits_mfma_kernel"],
+                              "us": round(us, 2), "flop": mfma_flop,
+                              "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                              "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
     if main_leg is not None:
         out["main_prepare"] = main_leg
     if host is not None:
