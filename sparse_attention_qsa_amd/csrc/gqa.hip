@@ -84,7 +84,7 @@ __device__ __forceinline__ u32x2_t lds_read_b64_async(uint32_t addr) {
   return v;
 }
 
-// Grid (T, Hkv, splits), one wavefront per (row, KV head, split).  Both contractions run on
+// One wavefront per (row, KV head, split), ordered by XCD (below).  Both contractions run on
 // the matrix cores (v_mfma_f32_16x16x32_bf16), with the G query heads of the KV head padded
 // to the 16 columns of the instruction:
 //   * Q.K: S^T (tokens x heads) = K (tokens x dims) . Q^T; K fragments are read from the LDS
@@ -107,7 +107,17 @@ __global__ __launch_bounds__(64) void gqa_partial_kernel(GqaParams P) {
   static_assert(G <= 16, "the MFMA columns hold at most 16 heads");
   constexpr int kRow = F8 ? 128 : 256;        // bytes of a token's K (or V) row
   constexpr int kLoads = kTile * kRow / 1024;  // LDS-direct loads per tile and part
-  const int row = blockIdx.x, kvh = blockIdx.y, split = blockIdx.z;
+  // Workgroup b runs on XCD b mod 8 (round-robin dispatch).  The work order (KV head, row,
+  // split) is cut into 8 contiguous chunks, chunk x for XCD x, so that the workgroups one XCD
+  // runs at a time share a request: rows of one request (prefill) or the verify rows of one
+  // request find the K/V rows they have in common in that XCD's L2.
+  const uint32_t total = (uint32_t)P.T * (uint32_t)(P.Hkv * P.splits);
+  const uint32_t chunk = (total + 7u) >> 3;
+  const uint32_t wi = (blockIdx.x & 7u) * chunk + (blockIdx.x >> 3);
+  if (wi >= total) return;  // the grid is 8 * chunk >= total
+  const int split = (int)(wi % (uint32_t)P.splits);
+  const uint32_t rk = wi / (uint32_t)P.splits;
+  const int row = (int)(rk % (uint32_t)P.T), kvh = (int)(rk / (uint32_t)P.T);
   const int lane = threadIdx.x, l16 = lane & 15, g4 = lane >> 4;
   __shared__ __attribute__((aligned(16))) uint8_t kt[kTile * kRow];
   __shared__ __attribute__((aligned(16))) uint8_t vt[kTile * kRow];
@@ -480,12 +490,14 @@ __global__ __launch_bounds__(64) void gqa_merge_kernel(GqaParams P) {
 
 template <int G>
 hipError_t launch_partial(const GqaParams& P, bool f8, hipStream_t s) {
+  // A 1-D grid of 8 * ceil(T * Hkv * splits / 8) workgroups, mapped onto the work by XCD.
+  const uint64_t total = (uint64_t)P.T * P.Hkv * P.splits;
+  if (total > 0xFFFFFFF0ull) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((total + 7) / 8 * 8));
   if (f8)
-    hipLaunchKernelGGL((gqa_partial_kernel<G, true>), dim3(P.T, P.Hkv, P.splits), dim3(64), 0,
-                       s, P);
+    hipLaunchKernelGGL((gqa_partial_kernel<G, true>), grid, dim3(64), 0, s, P);
   else
-    hipLaunchKernelGGL((gqa_partial_kernel<G, false>), dim3(P.T, P.Hkv, P.splits), dim3(64), 0,
-                       s, P);
+    hipLaunchKernelGGL((gqa_partial_kernel<G, false>), grid, dim3(64), 0, s, P);
   return hipGetLastError();
 }
 
