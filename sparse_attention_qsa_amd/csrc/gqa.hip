@@ -509,10 +509,13 @@ GqaPlan gqa_plan(const qsa_gqa_args& a) {
   if (p.tiles < 1) p.tiles = 1;
   int target = a.num_splits;
   if (target <= 0) {
-    // Aim for about 2048 workgroups (8 per CU, what the registers allow) so that the gathers
-    // keep HBM busy in one wave of workgroups.
+    // Workgroups to aim for, measured on the decode workloads: with bf16 K/V about 768 (three
+    // per CU), each split then gathering ~11 tiles of 16 KiB, so that its two dependent
+    // round trips before the first gather are amortised; with fp8 K/V (half the bytes per
+    // token) about 2048.  More waves than that queue behind the HBM without adding bandwidth.
     const int64_t base = (int64_t)a.num_tokens * a.num_kv_heads;
-    target = base >= 2048 ? 1 : (int)((2048 + base - 1) / base);
+    const int64_t want = a.kv_dtype == QSA_DTYPE_FP8_E4M3 ? 2048 : 768;
+    target = base >= want ? 1 : (int)((want + base - 1) / base);
   }
   if (target > p.tiles) target = p.tiles;
   if (target > kMergeMax) target = kMergeMax;  // the merge reads one split per lane

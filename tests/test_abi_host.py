@@ -88,9 +88,14 @@ def _topk(**over):
 def test_split_plan_and_workspace_sizes():
     lib = B.lib()
     a = _gqa()
-    # 65 tiles of 32 tokens; 128 (row, KV head) units -> 16 splits wanted -> 5 tiles each.
-    assert lib.qsa_sparse_gqa_num_splits(C.byref(a)) == 13
-    assert lib.qsa_sparse_gqa_workspace_size(C.byref(a)) >= 13 * 64 * 16 * 128 * 4
+    # 65 tiles of 32 tokens; 128 (row, KV head) units -> 768 / 128 = 6 splits wanted -> 11
+    # tiles each -> 6 splits.
+    assert lib.qsa_sparse_gqa_num_splits(C.byref(a)) == 6
+    assert lib.qsa_sparse_gqa_workspace_size(C.byref(a)) >= 6 * 64 * 16 * 128 * 4
+    # fp8 K/V: 2048 / 128 = 16 splits wanted -> 5 tiles each -> 13 splits.
+    f8 = _gqa(kv_dtype=1, kv_page_stride=2 * 16 * 256, kv_head_stride=16 * 256,
+              kv_token_stride=256)
+    assert lib.qsa_sparse_gqa_num_splits(C.byref(f8)) == 13
     one = _gqa(num_splits=1)
     assert lib.qsa_sparse_gqa_num_splits(C.byref(one)) == 1
     assert lib.qsa_sparse_gqa_workspace_size(C.byref(one)) == 0
