@@ -48,6 +48,11 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 #undef QSA_VMCNT
 }
 
+// Two float32 values rounded to nearest even as bf16, packed low then high.
+__device__ __forceinline__ uint32_t bf16_pack_rne(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
 // LDS accesses issued as inline assembly, so that the compiler's own wait insertion (which
 // cannot tell the targets of the LDS-direct loads apart) does not make them wait for every
 // memory operation in flight; each read is waited for before its value is used.
@@ -87,7 +92,9 @@ __device__ __forceinline__ uint32_t claim_async(int* counter) {
 // and stores each group's 16 rows x 16 keys as soon as it is final: the logits leave a store
 // per 128 MFMAs instead of in bursts, so that they do not stall the key loads behind them.
 // Stores are buffer stores whose range ends at the block's last row; keys a row does not see
-// go to an out-of-range offset and are dropped.
+// go to an out-of-range offset and are dropped.  The logits leave as bf16 (rounded to nearest
+// even; the row keeps its float32-sized stride): half the bytes of float32, and the top-k's
+// band absorbs the rounding (at most 2^-8 of the stored value).
 __global__ __launch_bounds__(512) void logits_mfma_kernel(SelectParams P, int row_blocks) {
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][kMfmaKeys * 256];
   __shared__ __attribute__((aligned(16))) uint8_t kok[2][kMfmaKeys];
@@ -266,8 +273,10 @@ __global__ __launch_bounds__(512) void logits_mfma_kernel(SelectParams P, int ro
           }
           const int j = kt * kMfmaKeys + 16 * (kg0 + q) + 4 * l4;
           const uint32_t off =
-              j < vis_t ? (uint32_t)(trow * P.col_stride + j) * 4u : 0xFFFFFFF0u;
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), rs, off, 0, 0);
+              j < vis_t ? (uint32_t)(trow * P.col_stride * 4 + j * 2) : 0xFFFFFFF0u;
+          typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+          const u32x2_t pk = {bf16_pack_rne(v[0], v[1]), bf16_pack_rne(v[2], v[3])};
+          __builtin_amdgcn_raw_buffer_store_b64(pk, rs, off, 0, 0);
           ++st;
         }
       }

@@ -186,20 +186,21 @@ __device__ __forceinline__ void folded_scores16(const SelectParams& P, const flo
 // Top-k kernel configurations: NT threads holding E scores each; the threshold's radix select
 // takes PASSES passes of RB-bit digits over the top RB*PASSES bits of the order-preserving key
 // (the rest stay unresolved: the threshold lies in one bin's value interval, which the band
-// absorbs); bands of up to BAND entries and block-table rows of up to CBT columns live in LDS.
-// The decode configurations spend LDS on few, fast rows; the prefill one (many rows) keeps its
-// LDS small so that eight rows share a CU.
-template <int NT_, int E_, int RB_, int PASSES_, int BAND_, int CBT_>
+// absorbs; a bf16 row is resolved after its 16 bits); bands of up to BAND entries and
+// block-table rows of up to CBT columns live in LDS; the first PF scores of a row are loaded
+// before the request lookup (the rest once the visible range is known).  The decode
+// configurations spend LDS on few, fast rows; the prefill one (many rows, eight sharing a CU)
+// keeps its LDS small and loads after the lookup, when the row's width and type are known.
+template <int NT_, int E_, int RB_, int PASSES_, int BAND_, int CBT_, int PF_>
 struct TopkCfg {
   static constexpr int NT = NT_, E = E_, RB = RB_, PASSES = PASSES_, BAND = BAND_, CBT = CBT_;
+  static constexpr int PF = PF_;
 };
-using TopkDecode8 = TopkCfg<512, 8, 12, 2, 1024, 2048>;
-using TopkDecode16 = TopkCfg<512, 16, 12, 2, 1024, 2048>;
-using TopkDecode32 = TopkCfg<512, 32, 12, 2, 1024, 2048>;
-using TopkDecode1k = TopkCfg<1024, 32, 12, 2, 1024, 2048>;
-using TopkPrefill = TopkCfg<256, 16, 8, 3, 256, 512>;
-// Scores loaded before the request lookup (the rest once the visible range is known).
-constexpr int kTopkPrefetchCols = 8192;
+using TopkDecode8 = TopkCfg<512, 8, 12, 2, 1024, 2048, 8192>;
+using TopkDecode16 = TopkCfg<512, 16, 12, 2, 1024, 2048, 8192>;
+using TopkDecode32 = TopkCfg<512, 32, 12, 2, 1024, 2048, 8192>;
+using TopkDecode1k = TopkCfg<1024, 32, 12, 2, 1024, 2048, 8192>;
+using TopkPrefill = TopkCfg<256, 16, 8, 3, 256, 512, 0>;
 constexpr int kTopkPrefillMinRows = 1024;  // rows in the call from which TopkPrefill is used
 
 // Inclusive prefix sum over the 64 lanes of a wavefront: shifts within rows of 16, then the
@@ -270,11 +271,11 @@ __global__ __launch_bounds__(C::NT) void topk_kernel(SelectParams P) {
 
   // ---- loads that need only the row, issued first: this thread's fast scores (the row is
   // padded to col_stride), its share of the Q row, and the request metadata for the lookup.
-  // Scores past kTopkPrefetchCols are loaded once the row's visible range is known (a short
-  // request of a call with long ones would otherwise read a long row it does not use).
+  // Scores past C::PF are loaded once the row's visible range is known (a short request of a
+  // call with long ones would otherwise read a long row it does not use).
   const float* lg = P.logits + (int64_t)row * P.col_stride;
   const int jb = tid * E;
-  const int pf_end = min(P.col_stride, kTopkPrefetchCols);
+  const int pf_end = min(P.col_stride, C::PF);
   float sc[E];
 #pragma unroll
   for (int i = 0; i < E; i += 4) {
@@ -348,14 +349,32 @@ __global__ __launch_bounds__(C::NT) void topk_kernel(SelectParams P) {
     const int c = tid + k * NT;
     cbt_v[k] = (cbt_in_lds && c < cw) ? P.cbt[(int64_t)r * P.cbt_stride + c] : -1;
   }
+  // Rows scored on the matrix cores hold bf16 logits (in the row's float32-sized stride).
+  const bool bf16_row = n_req > P.mfma_min_rows;  // block-uniform
+  if (bf16_row) {
+    static_assert(E % 8 == 0, "a thread's bf16 scores are whole 16-byte words");
+    const uint16_t* lb = reinterpret_cast<const uint16_t*>(lg);
 #pragma unroll
-  for (int i = 0; i < E; i += 4) {  // the rest of the visible scores
-    if (jb + i >= pf_end && jb + i < vis) {
-      const float4 v = *reinterpret_cast<const float4*>(lg + jb + i);
-      sc[i] = v.x;
-      sc[i + 1] = v.y;
-      sc[i + 2] = v.z;
-      sc[i + 3] = v.w;
+    for (int i = 0; i < E; i += 8) {
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (jb + i < vis) v = *reinterpret_cast<const uint4*>(lb + jb + i);
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        sc[i + 2 * k] = bf16lo(w4[k]);
+        sc[i + 2 * k + 1] = bf16hi(w4[k]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < E; i += 4) {  // the rest of the visible scores
+      if (jb + i >= pf_end && jb + i < vis) {
+        const float4 v = *reinterpret_cast<const float4*>(lg + jb + i);
+        sc[i] = v.x;
+        sc[i + 1] = v.y;
+        sc[i + 2] = v.z;
+        sc[i + 3] = v.w;
+      }
     }
   }
   uint32_t key[E];  // order-preserving keys of the fast scores
@@ -382,11 +401,16 @@ __global__ __launch_bounds__(C::NT) void topk_kernel(SelectParams P) {
   // visible blocks are counted (the -inf entries of a short row would all add to one bin, and
   // its LDS atomics would serialise).
   // Histograms alternate between two buffers; a pass clears the one the next-but-one uses.
-  uint32_t prefix = 0, pmask = 0;
+  uint32_t prefix = 0, pmask = 0, lowmask = kLowMask;
   int krem = kb;
 #pragma unroll
   for (int pass = 0; pass < C::PASSES; ++pass) {
     const int shift = 32 - kRadixBits * (pass + 1);
+    // A bf16 value's key has 16 significant bits: once they are resolved, stop (block-uniform).
+    if (bf16_row && shift + kRadixBits <= 16) {
+      lowmask = (1u << (shift + kRadixBits)) - 1u;
+      break;
+    }
     int* h = hist[pass & 1];
 #pragma unroll
     for (int i = 0; i < E; ++i) {
@@ -435,8 +459,8 @@ __global__ __launch_bounds__(C::NT) void topk_kernel(SelectParams P) {
     pmask |= (uint32_t)(kRadixBins - 1) << shift;
     krem = s_int[5];
   }
-  // The kb-th largest fast score lies in [T_lo, T_hi], the values of the keys prefix..prefix|255.
-  const double T_lo = (double)fval(prefix), T_hi = (double)fval(prefix | kLowMask);
+  // The kb-th largest fast score lies in [T_lo, T_hi], the values of the keys with this prefix.
+  const double T_lo = (double)fval(prefix), T_hi = (double)fval(prefix | lowmask);
   if (cbt_in_lds) {
 #pragma unroll
     for (int k = 0; k < kCbtPer; ++k) {
@@ -456,11 +480,29 @@ __global__ __launch_bounds__(C::NT) void topk_kernel(SelectParams P) {
   // of the per-head MFMA score (u = 2^-23 covers any rounding the matrix cores may use).
   const double gam_f = (double)(P.Hi + 130) * 0x1p-24;
   const double E_f = 2.0 * gam_f / (1.0 - gam_f) * kappa * A + 1e-30;
-  const bool mfma_row = n_req > P.mfma_min_rows;
+  const bool mfma_row = bf16_row;
   const double gam_m = (double)(P.Hi * kHeadDim + 2) * 0x1p-23;
   const double Ebound = mfma_row ? 2.0 * gam_m / (1.0 - gam_m) * kappa * A + 1e-30 : E_f;
   // Certainly kept above hi, certainly dropped below lo; float32 forms widen the band only.
-  const float hi = round_up_f32(T_hi + 2.0 * Ebound), lo = round_down_f32(T_lo - 2.0 * Ebound);
+  // A score b stands for canonical scores in [b - d(b), b + d(b)] with d(b) = Ebound (float32
+  // rows) or Ebound + r |b| (bf16 rows: rounding to nearest moves a value by at most 2^-8 of
+  // the result; r adds a margin).  Both ends increase with b, so the kb-th largest canonical
+  // score lies in [T_lo - d(T_lo), T_hi + d(T_hi)]; a block is certainly kept if b - d(b)
+  // exceeds the upper end and certainly dropped if b + d(b) is below the lower end.  hi and lo
+  // solve those two conditions for b.
+  float hi, lo;
+  if (bf16_row) {
+    const double rr = 0x1p-8 * (1.0 + 0x1p-20);
+    const double x = T_hi + rr * fabs(T_hi) + 2.0 * Ebound;   // b - r|b| must exceed x
+    const double y = T_lo - rr * fabs(T_lo) - 2.0 * Ebound;   // b + r|b| must reach y
+    const double bh = x >= 0.0 ? x / (1.0 - rr) : x / (1.0 + rr);
+    const double bl = y >= 0.0 ? y / (1.0 + rr) : y / (1.0 - rr);
+    hi = round_up_f32(bh + fabs(bh) * 0x1p-40 + 1e-30);
+    lo = round_down_f32(bl - fabs(bl) * 0x1p-40 - 1e-30);
+  } else {
+    hi = round_up_f32(T_hi + 2.0 * Ebound);
+    lo = round_down_f32(T_lo - 2.0 * Ebound);
+  }
 
   // ---- classify and collect the band in block order: one workgroup scan of the per-thread
   // counts (band entries in the low half, certain keeps in the high half of a packed int).
