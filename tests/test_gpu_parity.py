@@ -281,6 +281,23 @@ def test_exact_ties_go_to_the_lower_block():
     assert np.array_equal(to_np(st.packed), ref.packed)
 
 
+def test_exact_ties_on_matrix_core_rows():
+    """Rows scored on the matrix cores (stored as bf16, certified with the rounding bound):
+    every compressed row of the pre-state is the same key, so the visible blocks tie exactly
+    and the lower block index decides; one call takes the decode top-k configuration (fewer
+    than 1024 rows), the other the prefill one."""
+    for rows in (100, 600):
+        wl = workload("chunked_prefill", num_requests=2, lengths=("fixed", 3000), rows=rows)
+        row = wl.ckv[wl.c_block_table[0, 0], 0].clone()
+        wl.ckv[:] = row
+        log(f"matrix-core ties: T={wl.num_tokens}")
+        ref = oracle_step(wl, with_attention=False)
+        st = run_gpu(wl)
+        packed = to_np(st.packed)
+        assert np.array_equal(packed, ref.packed), (
+            f"{int((packed != ref.packed).any(axis=1).sum())} rows differ")
+
+
 def test_inert_rows_invalid_entries_and_empty_requests():
     wl = workload("tiny_decode")
     ref = oracle_step(wl)
