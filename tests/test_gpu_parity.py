@@ -219,8 +219,8 @@ def test_prefill_row_counts_select_exactly():
 
 
 def test_full_size_chunked_prefill_on_sampled_rows():
-    """The whole chunked_prefill indexer call (4 x 8192 rows on 8192 cached tokens: MFMA
-    logits, prefill top-k) at full size, on sampled rows."""
+    """The whole chunked_prefill step (4 x 8192 rows on 8192 cached tokens: MFMA logits,
+    prefill top-k, attention) at full size, on sampled rows."""
     wl = workload("chunked_prefill", num_requests=4, lengths=("fixed", 16384), rows=8192)
     rows = [0, 4097, 8191, 8192 + 777, 3 * 8192 + 8191]
     log(f"full-size chunked_prefill, sampled rows {rows}")
@@ -235,6 +235,15 @@ def test_full_size_chunked_prefill_on_sampled_rows():
     W, c = wl.output_width, wl.compress_ratio
     p = 8192 + np.tile(np.arange(8192), 4)
     assert np.array_equal(packed[:, W], 2048 + (p + 1) % c)
+    # The attention over the 32,768 rows (one split each, the launch bench.py times), on the
+    # sampled rows, from the oracle's own selection.
+    st.gqa()
+    torch.cuda.synchronize()
+    ref_out = oq.sparse_gqa(to_np(wl.q), to_np(wl.kv_cache), to_np(wl.block_table),
+                            to_np(wl.token_to_req), ref.packed, gate=to_np(wl.gate), rows=rows)
+    err = max_abs(gpu_out_f64(st)[rows], ref_out[rows])
+    log(f"  attention max-abs {err:.3e}")
+    assert err <= TOL["bf16"]
 
 
 def test_fp8_kv_scales_act_on_scores_and_output():
