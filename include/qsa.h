@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 4
+#define QSA_ABI_VERSION 5
 
 typedef enum qsa_status {
   QSA_OK = 0,
@@ -218,11 +218,22 @@ typedef struct qsa_topk_args {
   qsa_agg index_agg;                /* SUM (0), or RELU_SUM: score = sum_h max(0, q_h . k),
                                        heads in order; RELU_SUM needs Hi <= 8 and is scored
                                        by the vector-unit kernel for every request          */
+  int64_t max_logits_bytes;         /* 0: no cap.  Else the rows are scored and selected in
+                                       windows of consecutive rows whose logits fit this many
+                                       bytes (4 per compressed column, rounded to 64), each
+                                       window reusing the workspace: see below              */
 } qsa_topk_args;
 
 size_t qsa_index_logits_topk_workspace_size(const qsa_topk_args* args);
 qsa_status qsa_index_logits_topk(const qsa_topk_args* args, void* workspace,
                                  size_t workspace_bytes, void* stream);
+
+/* Logits memory cap (the pages bound the prefill logits buffer by a size in MB): with
+ * max_logits_bytes > 0 the call runs window by window over rows [w*n, (w+1)*n), n =
+ * max(1, max_logits_bytes / (4 * ceil(max_seq_len / c / 64) * 64)), and the workspace query
+ * sizes everything per-row (logits, band spill) for n rows instead of T.  The result is the
+ * same packed buffer, bit for bit.  A row window is also the unit of the split calls below:
+ * they return QSA_ERR_NOT_SUPPORTED when the cap makes more than one window. */
 
 /* The two kernels of qsa_index_logits_topk as separate calls, for a caller that times them
  * one by one: qsa_index_logits runs the scoring (fast float32 logits and per-block key bounds

@@ -68,6 +68,7 @@ class TopkArgs(C.Structure):
         ("num_index_heads", _I32), ("head_dim", _I32), ("compress_ratio", _I32),
         ("budget", _I32), ("index_dtype", _I32),
         ("packed", _P), ("packed_row_stride", _I64), ("index_agg", _I32),
+        ("max_logits_bytes", _I64),
     ]
 
 
@@ -251,7 +252,7 @@ def qsa_compress(stream=None, **kw) -> None:
 def topk_args(*, query_start_loc, seq_lens, q_idx, ckv, c_block_table, packed, num_index_heads,
               compress_ratio, budget, index_dtype, max_query_len, max_seq_len,
               num_decode_requests=0, decode_query_len=0, c_block_table_width=None,
-              index_agg="sum") -> TopkArgs:
+              index_agg="sum", max_logits_bytes=0) -> TopkArgs:
     _need(query_start_loc, torch.int32, "query_start_loc")
     _need(seq_lens, torch.int32, "seq_lens")
     _need(c_block_table, torch.int32, "c_block_table")
@@ -281,6 +282,7 @@ def topk_args(*, query_start_loc, seq_lens, q_idx, ckv, c_block_table, packed, n
     a.packed = _ptr(packed)
     a.packed_row_stride = packed.stride(0)
     a.index_agg = AGGS[index_agg]
+    a.max_logits_bytes = int(max_logits_bytes)
     return a
 
 

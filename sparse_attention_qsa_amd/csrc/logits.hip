@@ -21,7 +21,9 @@ using namespace logits_tile;
 // RELU: one row at a time, its NR = 8 heads held unfolded as the scorer's rows.
 // KMAX: the call also has matrix-core requests, for which this kernel only takes the per-block
 // bound of max |k| (a separate instance, so that the decode instances carry no such branch).
-template <bool FP8, int NR, bool RELU = false, bool KMAX = false>
+// WIN: the call runs in row windows (a logits memory cap): only the rows in [row_lo, row_hi)
+// are scored, into logits rows relative to row_lo.
+template <bool FP8, int NR, bool RELU = false, bool KMAX = false, bool WIN = false>
 __global__ __launch_bounds__(kLogitsThreads) __attribute__((amdgpu_waves_per_eu(NR >= 4 ? 2 : 4)))
 void logits_valu_kernel(SelectParams P) {
   using KL = KeyLanes<FP8>;
@@ -52,6 +54,10 @@ void logits_valu_kernel(SelectParams P) {
   // the per-block bound of max |k| the top-k needs (one pass over their keys).
   if (!KMAX && n > P.mfma_min_rows) return;  // block-uniform, before any barrier
   const int vis_max = (n > 0 && n <= L) ? min(L / P.c, P.cols) : 0;
+  // The request's rows in this window: [rb, re) of its n.
+  const int rb = WIN ? min(max(P.row_lo - q0, 0), n) : 0;
+  const int re = WIN ? min(max(P.row_hi - q0, 0), n) : n;
+  if (WIN && rb >= re) return;  // block-uniform, before any barrier
   // Barrier without a memory fence (a fence would wait for every load in flight); the LDS
   // writes before it are complete, and global loads are waited for where their data is used.
   auto barrier = [] {
@@ -70,14 +76,14 @@ void logits_valu_kernel(SelectParams P) {
     if constexpr (KMAX) {
       if (n > P.mfma_min_rows) {  // block-uniform
         barrier();  // rows_s written
-        #pragma unroll
+#pragma unroll
         for (int t = 0; t < kLogitsTilesPerWG; ++t) {
           uint32_t a[KL::kLoads][4], ma;
           load_key_tile<FP8>(P, rows_s, t, w, lane, a, ma);
-          #pragma unroll
+#pragma unroll
           for (int it = 0; it < KL::kLoads; ++it) {
             float m = 0.0f;
-            #pragma unroll
+#pragma unroll
             for (int i = 0; i < 4; ++i) {
               const uint32_t word = a[it][i];
               if (FP8) {
@@ -95,9 +101,9 @@ void logits_valu_kernel(SelectParams P) {
       }
     }
     // (KMAX: the rows of a matrix-core request are not scored here.)
-    const int n_scored = KMAX ? (n > P.mfma_min_rows ? 0 : n) : n;
-    for (int rr0 = 0; rr0 < n_scored; rr0 += (RELU ? 1 : NR)) {
-      const int nr = RELU ? NR : min(NR, n - rr0);
+    const int n_scored = KMAX ? (n > P.mfma_min_rows ? rb : re) : re;
+    for (int rr0 = rb; rr0 < n_scored; rr0 += (RELU ? 1 : NR)) {
+      const int nr = RELU ? NR : min(NR, re - rr0);
       // Head-folded Q of the chunk's rows: each of the first nr*128 threads owns one (row, dim)
       // and loads all its heads at once (clamped to Hi - 1, the extra terms added as zero).
       constexpr int kSlots = (NR * kHeadDim + kT - 1) / kT;
@@ -131,7 +137,7 @@ void logits_valu_kernel(SelectParams P) {
         }
         v[sl][0] = __float_as_uint(f);
       }
-      if (rr0 > 0) barrier();  // the previous chunk's readers are done with qf_s
+      if (rr0 > rb) barrier();  // the previous chunk's readers are done with qf_s
 #pragma unroll
       for (int sl = 0; sl < kSlots; ++sl) {
         const int e = threadIdx.x + kT * sl;
@@ -146,8 +152,8 @@ void logits_valu_kernel(SelectParams P) {
           qf[rr][i] = (rr < nr && i < KL::kDims)
                           ? qf_s[rr][(lane % KL::kLanes) * KL::kDims + i] : 0.0f;
       }
-      const bool first = rr0 == 0;
-      const int row0 = q0 + rr0;
+      const bool first = rr0 == rb;
+      const int row0 = q0 + rr0 - (WIN ? P.row_lo : 0);  // logits row (window-relative)
       // One tile in flight per wave; the other waves of the SIMD (four per SIMD) cover its
       // latency.  The loop is unrolled, so the compiler's vmcnt waits name exactly the tile.
       uint32_t a[KL::kLoads][4], ma;
@@ -181,8 +187,11 @@ hipError_t launch_valu(const SelectParams& P, hipStream_t s) {
   const int per_cu = NR >= 4 ? 1 : 2;
   const int64_t dense = (int64_t)P.R * P.key_tiles, resident = (int64_t)kCUs * per_cu;
   if (dense <= resident || P.R > kLogitsListReqs) {
-    hipLaunchKernelGGL((logits_valu_kernel<FP8, NR, RELU, KMAX>), dim3(P.key_tiles, P.R),
-                       dim3(kLogitsThreads), 0, s, P);
+    const dim3 grid(P.key_tiles, P.R), block(kLogitsThreads);
+    if (P.row_lo > 0 || P.row_hi < P.T)  // row windows
+      hipLaunchKernelGGL((logits_valu_kernel<FP8, NR, RELU, KMAX, true>), grid, block, 0, s, P);
+    else
+      hipLaunchKernelGGL((logits_valu_kernel<FP8, NR, RELU, KMAX>), grid, block, 0, s, P);
     return hipGetLastError();
   }
   return launch_logits_list(P, NR, RELU, KMAX, (unsigned)resident, s);

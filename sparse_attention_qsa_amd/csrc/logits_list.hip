@@ -60,14 +60,14 @@ void logits_valu_list_kernel(SelectParams P) {
     // Block-table entries of this thread's keys jw + tid + kT i: their addresses do not depend
     // on the request metadata, so they are loaded together with it (one round trip).
     int col[kKeys / kT], page[kKeys / kT];
-    #pragma unroll
+#pragma unroll
     for (int i = 0; i < kKeys / kT; ++i) {
       col[i] = (jw + (int)threadIdx.x + kT * i) / P.Pc;
       page[i] = P.cbt[(int64_t)r * P.cbt_stride + min(col[i], P.cbt_width - 1)];
     }
     const int q0 = req_q0[r], n = req_n[r], vis_max = req_vis[r];
-    // The MFMA kernel, which runs next, starts its work queues from zero.
-    if (blockIdx.x == 0 && threadIdx.x < 8) P.work[threadIdx.x] = 0;
+    // The request's rows in this launch's window (all of them without a logits cap).
+    const int rb = min(max(P.row_lo - q0, 0), n), re = min(max(P.row_hi - q0, 0), n);
     // Requests with many rows are scored by the MFMA kernel (none in a call without one); for
     // them this kernel only takes the per-block bound of max |k| the top-k needs (one pass over
     // their keys).
@@ -75,7 +75,7 @@ void logits_valu_list_kernel(SelectParams P) {
     const bool kmax_only = KMAX && n > P.mfma_min_rows;  // block-uniform
     float kmax = 0.0f;
     if (jw < vis_max) {  // block-uniform
-      #pragma unroll
+#pragma unroll
       for (int i = 0; i < kKeys / kT; ++i) {
         const int j = jw + threadIdx.x + kT * i;
         const bool ok = j < vis_max && col[i] < P.cbt_width && page[i] >= 0 && page[i] < P.c_pages;
@@ -83,14 +83,14 @@ void logits_valu_list_kernel(SelectParams P) {
       }
       if (kmax_only) {
         barrier();  // rows_s written
-        #pragma unroll
+#pragma unroll
         for (int t = 0; t < kLogitsTilesPerWG; ++t) {
           uint32_t a[KL::kLoads][4], ma;
           load_key_tile<FP8>(P, rows_s, t, w, lane, a, ma);
-          #pragma unroll
+#pragma unroll
           for (int it = 0; it < KL::kLoads; ++it) {
             float m = 0.0f;
-            #pragma unroll
+#pragma unroll
             for (int i = 0; i < 4; ++i) {
               const uint32_t word = a[it][i];
               if (FP8) {
@@ -106,18 +106,18 @@ void logits_valu_list_kernel(SelectParams P) {
           }
         }
       }
-      for (int rr0 = 0; rr0 < (kmax_only ? 0 : n); rr0 += (RELU ? 1 : NR)) {
-        const int nr = RELU ? NR : min(NR, n - rr0);
+      for (int rr0 = rb; rr0 < (kmax_only ? rb : re); rr0 += (RELU ? 1 : NR)) {
+        const int nr = RELU ? NR : min(NR, re - rr0);
         // Head-folded Q of the chunk's rows: each of the first nr*128 threads owns one (row, dim)
         // and loads all its heads at once (clamped to Hi - 1, the extra terms added as zero).
         constexpr int kSlots = (NR * kHeadDim + kT - 1) / kT;
         uint32_t v[kSlots][16];  // raw bf16 / e4m3 codes
-        #pragma unroll
+#pragma unroll
         for (int sl = 0; sl < kSlots; ++sl) {
           const int e = threadIdx.x + kT * sl;
           const int rr = min(e >> 7, nr - 1), d = e & (kHeadDim - 1);
           const int64_t qb = (int64_t)(q0 + rr0 + (RELU ? 0 : rr)) * P.Hi * kHeadDim + d;
-          #pragma unroll
+#pragma unroll
           for (int h = 0; h < (RELU ? 1 : 16); ++h) {
             // RELU: slot e holds head rr of the one row (clamped to Hi - 1, zeroed below).
             const int64_t idx = qb + min(RELU ? rr : h, P.Hi - 1) * kHeadDim;
@@ -127,7 +127,7 @@ void logits_valu_list_kernel(SelectParams P) {
         }
         // Q first: issued behind the key burst its words would wait several microseconds in
         // the memory queues, and every wave needs them before it can score (and reload).
-        #pragma unroll
+#pragma unroll
         for (int sl = 0; sl < kSlots; ++sl) {
           auto dec = [](uint32_t x) {
             return FP8 ? e4m3_to_f32_exact((uint8_t)x) : bf16_to_f32((uint16_t)x);
@@ -136,32 +136,32 @@ void logits_valu_list_kernel(SelectParams P) {
           if (RELU) {
             if (((int)threadIdx.x + kT * sl) >> 7 >= P.Hi) f = 0.0f;  // a head past Hi
           } else {
-            #pragma unroll
+#pragma unroll
             for (int h = 1; h < 16; ++h) f = f + (h < P.Hi ? dec(v[sl][h]) : 0.0f);
           }
           v[sl][0] = __float_as_uint(f);
         }
-        if (rr0 > 0) barrier();  // the previous chunk's readers are done with qf_s
-        #pragma unroll
+        if (rr0 > rb) barrier();  // the previous chunk's readers are done with qf_s
+#pragma unroll
         for (int sl = 0; sl < kSlots; ++sl) {
           const int e = threadIdx.x + kT * sl;
           if (e < nr * kHeadDim) qf_s[e >> 7][e & (kHeadDim - 1)] = __uint_as_float(v[sl][0]);
         }
         barrier();  // rows_s and qf_s written
         float qf[NR][16];
-        #pragma unroll
+#pragma unroll
         for (int rr = 0; rr < NR; ++rr) {
-          #pragma unroll
+#pragma unroll
           for (int i = 0; i < 16; ++i)
             qf[rr][i] = (rr < nr && i < KL::kDims)
                             ? qf_s[rr][(lane % KL::kLanes) * KL::kDims + i] : 0.0f;
         }
-        const bool first = rr0 == 0;
-        const int row0 = q0 + rr0;
+        const bool first = rr0 == rb;
+        const int row0 = q0 + rr0 - P.row_lo;  // logits row (window-relative)
         // One tile in flight per wave; the other waves of the SIMD (four per SIMD) cover its
         // latency.  The loop is unrolled, so the compiler's vmcnt waits name exactly the tile.
         uint32_t a[KL::kLoads][4], ma;
-        #pragma unroll
+#pragma unroll
         for (int t = 0; t < kLogitsTilesPerWG; ++t) {
           load_key_tile<FP8>(P, rows_s, t, w, lane, a, ma);
           score_key_tile<FP8, NR, RELU>(P, a, ma, qf, nr, row0,
@@ -178,24 +178,28 @@ void logits_valu_list_kernel(SelectParams P) {
     if (threadIdx.x < kKeys / 128) {
       const int blk = k * (kKeys / 128) + threadIdx.x;
       float m = red[0];
-      #pragma unroll
+#pragma unroll
       for (int i = 1; i < kWaves; ++i) m = fmaxf(m, red[i]);
       if (blk < P.key_blocks) P.kmax[(int64_t)r * P.key_blocks + blk] = m;
     }
   };
 
+  // The MFMA kernel, which runs next, starts its work queues from zero.
+  if (blockIdx.x == 0 && threadIdx.x < 8) P.work[threadIdx.x] = 0;
   {
     // Thread t counts the items of requests t*per .. t*per+per-1; a workgroup scan of the
     // counts (in-wave, then the wave totals) gives every request's end.
     constexpr int kPerMax = kLogitsListReqs / kT;
     const int per = (P.R + kT - 1) / kT, i0 = threadIdx.x * per;
     int cnt[kPerMax];
-    #pragma unroll
+#pragma unroll
     for (int u = 0; u < kPerMax; ++u) {
       cnt[u] = 0;
       if (u < per && i0 + u < P.R) {
         int q0, n, vm;
         req_range(i0 + u, q0, n, vm);
+        // No items for a request without rows in this launch's window.
+        if (P.row_hi <= q0 || q0 + n <= P.row_lo) vm = 0;
         cnt[u] = (vm + kKeys - 1) / kKeys;
         req_q0[i0 + u] = q0;
         req_n[i0 + u] = n;
@@ -203,10 +207,10 @@ void logits_valu_list_kernel(SelectParams P) {
       }
     }
     int sum = 0;
-    #pragma unroll
+#pragma unroll
     for (int u = 0; u < kPerMax; ++u) sum += cnt[u];
     int incl = sum;
-    #pragma unroll
+#pragma unroll
     for (int m = 1; m < 64; m <<= 1) {
       const int v = __shfl_up(incl, m, 64);
       if (lane >= m) incl += v;
@@ -214,12 +218,12 @@ void logits_valu_list_kernel(SelectParams P) {
     if (lane == 63) s_tot[w] = incl;
     barrier();
     int run = incl - sum, total = 0;
-    #pragma unroll
+#pragma unroll
     for (int i = 0; i < kWaves; ++i) {
       run += i < w ? s_tot[i] : 0;
       total += s_tot[i];
     }
-    #pragma unroll
+#pragma unroll
     for (int u = 0; u < kPerMax; ++u) {
       run += cnt[u];
       if (u < per && i0 + u < P.R) item_end[i0 + u] = run;

@@ -141,11 +141,18 @@ __global__ __launch_bounds__(512) void logits_mfma_kernel(SelectParams P, int ro
     const int rb = chunk == 0 ? jj / P.R : row_blocks - 1 - jj / P.R;
     const int q0 = max(0, min(qsl_c[r], P.T));
     const int n = max(0, min(qsl_c[r + 1], P.T) - q0), L = sl_c[r];
-    int t0 = 0, t1 = 0, nrows = 0, pbase = 0;
+    int t0 = 0, t1 = 0, nrows = 0, pbase = 0, wlo = 0, whi = 0;
     if (n > P.mfma_min_rows && n <= L && rb * kMfmaRows < n) {
       nrows = min(kMfmaRows, n - rb * kMfmaRows);
       pbase = L - n + rb * kMfmaRows;  // position of the block's first row
-      const int vis_hi = min((pbase + nrows) / P.c, P.cols);
+      // The block's rows in this launch's window: [wlo, whi) of its nrows.
+      const int blk0 = q0 + rb * kMfmaRows;
+      wlo = min(max(P.row_lo - blk0, 0), nrows);
+      whi = min(max(P.row_hi - blk0, 0), nrows);
+      if (wlo >= whi) nrows = 0;
+    }
+    if (nrows > 0) {
+      const int vis_hi = min((pbase + whi) / P.c, P.cols);
       t0 = chunk * kMfmaTilesPerItem;
       t1 = min(t0 + kMfmaTilesPerItem, (vis_hi + kMfmaKeys - 1) / kMfmaKeys);
     }
@@ -159,7 +166,7 @@ __global__ __launch_bounds__(512) void logits_mfma_kernel(SelectParams P, int ro
     barrier();  // every wave is done with the previous item's buffers
     // This lane's row of the block and the keys it sees.
     const int trow = 16 * w + l16;
-    const int vis_t = trow < nrows ? min((pbase + trow + 1) / P.c, P.cols) : 0;
+    const int vis_t = trow >= wlo && trow < whi ? min((pbase + trow + 1) / P.c, P.cols) : 0;
 
     // ---- key tile kt into buffer b: 8 LDS-direct loads per wave (wave w: keys 32w .. 32w+31);
     // a key that is not visible or whose page is outside the cache loads the cache's first
@@ -203,9 +210,11 @@ __global__ __launch_bounds__(512) void logits_mfma_kernel(SelectParams P, int ro
         }
       }
     }
+    // Logits rows are relative to the window: the record starts at the block's first row in
+    // it and ends at its last.
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        P.logits + (int64_t)(q0 + rb * kMfmaRows) * P.col_stride, 0,
-        nrows * P.col_stride * 4, 0x00020000);
+        P.logits + (int64_t)(q0 + rb * kMfmaRows + wlo - P.row_lo) * P.col_stride, 0,
+        (whi - wlo) * P.col_stride * 4, 0x00020000);
 
     // Stores this wave issued while multiplying the previous tile (after this tile's loads,
     // which were issued at the start of that step): they may stay in flight.
@@ -273,7 +282,7 @@ __global__ __launch_bounds__(512) void logits_mfma_kernel(SelectParams P, int ro
           }
           const int j = kt * kMfmaKeys + 16 * (kg0 + q) + 4 * l4;
           const uint32_t off =
-              j < vis_t ? (uint32_t)(trow * P.col_stride * 4 + j * 2) : 0xFFFFFFF0u;
+              j < vis_t ? (uint32_t)((trow - wlo) * P.col_stride * 4 + j * 2) : 0xFFFFFFF0u;
           typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
           const u32x2_t pk = {bf16_pack_rne(v[0], v[1]), bf16_pack_rne(v[2], v[3])};
           __builtin_amdgcn_raw_buffer_store_b64(pk, rs, off, 0, 0);

@@ -31,12 +31,12 @@ __device__ __forceinline__ void load_key_tile(const SelectParams& P, const int32
   const char* base = reinterpret_cast<const char*>(P.ckv) + (lane % K::kLanes) * 16;
   const int key0 = tile * kLogitsKeysPerWG + w * 64 + lane / K::kLanes;
   int row[K::kLoads];
-  #pragma unroll
+#pragma unroll
   for (int it = 0; it < K::kLoads; ++it) row[it] = rows[key0 + it * K::kKeysPerLoad];
   // The mask is applied when the tile is scored: a select here would consume the loaded words
   // at once and make the wave wait for them.
   okm = 0;
-  #pragma unroll
+#pragma unroll
   for (int it = 0; it < K::kLoads; ++it) {
     okm |= (uint32_t)(row[it] >= 0) << it;
     const uint4 x = *reinterpret_cast<const uint4*>(
@@ -82,13 +82,13 @@ __device__ __forceinline__ void score_key_tile(const SelectParams& P,
   // register pair per load.
   const uint32_t onehot = 1u << x;
   float res[NR];
-  #pragma unroll
+#pragma unroll
   for (int rr = 0; rr < NR; ++rr) res[rr] = 0.0f;
-  #pragma unroll
+#pragma unroll
   for (int it = 0; it < K::kLoads; ++it) {
     float k[16];
     const bool ok = (okm >> it) & 1u;
-    #pragma unroll
+#pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t word = raw[it][i];
       if (FP8) {
@@ -107,14 +107,14 @@ __device__ __forceinline__ void score_key_tile(const SelectParams& P,
     // selects (never by arithmetic, which a NaN there would survive).
     if (track_kmax) {
       float m = fabsf(k[0]);
-      #pragma unroll
+#pragma unroll
       for (int i = 1; i < K::kDims; ++i) m = fmaxf(m, fabsf(k[i]));
       kmax = fmaxf(kmax, ok ? m : 0.0f);
     }
-    #pragma unroll
+#pragma unroll
     for (int rr = 0; rr < NR; ++rr) {
       float d = 0.0f;
-      #pragma unroll
+#pragma unroll
       for (int i = 0; i < K::kDims; ++i) d = fmaf(qf[rr][i], k[i], d);
       d = group_sum<K::kLanes>(ok ? d : 0.0f);
       res[rr] = fmaf((float)((onehot >> it) & 1u), d, res[rr]);  // exact: one term is d
@@ -125,7 +125,7 @@ __device__ __forceinline__ void score_key_tile(const SelectParams& P,
   const int j = j0 + x * K::kKeysPerLoad + g;
   if (RELU) {
     float sum = fmaxf(res[0], 0.0f);
-    #pragma unroll
+#pragma unroll
     for (int rr = 1; rr < NR; ++rr) sum = sum + fmaxf(res[rr], 0.0f);
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         P.logits + (int64_t)row0 * P.col_stride, 0, vis_max * 4, 0x00020000);
@@ -133,7 +133,7 @@ __device__ __forceinline__ void score_key_tile(const SelectParams& P,
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sum), rs, off, 0, 0);
     return;
   }
-  #pragma unroll
+#pragma unroll
   for (int rr = 0; rr < NR; ++rr) {
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         P.logits + (int64_t)(rr < nr ? row0 + rr : row0) * P.col_stride, 0,

@@ -117,6 +117,7 @@ qsa_status validate_topk(const qsa_topk_args* a) {
   QSA_REQUIRE(a->index_agg == QSA_AGG_SUM || a->index_agg == QSA_AGG_RELU_SUM, kNotSup);
   // ReLU-sum keeps every head's Q in registers (eight at most).
   QSA_REQUIRE(a->index_agg == QSA_AGG_SUM || a->num_index_heads <= 8, kNotSup);
+  QSA_REQUIRE(a->max_logits_bytes >= 0, kInval);
   return QSA_OK;
 }
 
@@ -180,6 +181,8 @@ qsa_status run_topk(const qsa_topk_args* a, void* ws, size_t ws_bytes, void* str
   const qsa::TopkLayout L = qsa::topk_layout(*a);
   if (ws == nullptr || ws_bytes < L.total) return QSA_ERR_WORKSPACE_TOO_SMALL;
   if (!aligned(ws, 256)) return kInval;
+  // The split calls hand the workspace over between them: one window only.
+  if (phase != qsa::Phase::kAll && L.rows < a->num_tokens) return kNotSup;
   return from_hip(qsa::launch_topk(*a, L, static_cast<char*>(ws),
                                    reinterpret_cast<hipStream_t>(stream), phase));
 }

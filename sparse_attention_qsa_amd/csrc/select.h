@@ -10,6 +10,8 @@ struct SelectParams {
   int T, R, Hi, c, budget, Pc, c_pages, cbt_stride, cbt_width, cols, col_stride, key_tiles;
   int key_blocks;     // 128-key blocks per request in the kmax array
   int mfma_min_rows;  // requests with more rows than this are scored by the MFMA kernel
+  int row_lo, row_hi;  // the rows of this launch (a window under a logits memory cap); the
+                       // per-row workspace arrays are indexed by row - row_lo
   bool fp8;
   bool relu;          // ReLU-sum aggregation (every request on the vector-unit kernel)
   const int32_t* qsl;

@@ -13,13 +13,20 @@ TopkLayout topk_layout(const qsa_topk_args& a) {
   L.col_stride = (L.cols + 63) / 64 * 64;
   L.key_tiles = (L.cols + kLogitsTilesPerWG * kLogitsKeysPerWG - 1) /
                 (kLogitsTilesPerWG * kLogitsKeysPerWG);
+  // Rows per window: all of them, or as many as the logits cap allows (at least one).
+  int64_t rows = T;
+  if (a.max_logits_bytes > 0) {
+    rows = a.max_logits_bytes / ((int64_t)L.col_stride * (int64_t)sizeof(float));
+    rows = rows < 1 ? 1 : (rows > T ? T : rows);
+  }
+  L.rows = (int32_t)rows;
   auto align = [](size_t x) { return (x + 255) / 256 * 256; };
   size_t off = 0;
-  L.off_logits = off;     off = align(off + (size_t)T * L.col_stride * sizeof(float));
+  L.off_logits = off;     off = align(off + (size_t)rows * L.col_stride * sizeof(float));
   L.key_blocks = (L.cols + 127) / 128;
   L.off_kmax = off;       off = align(off + (size_t)R * L.key_blocks * sizeof(float));
-  L.off_band_idx = off;   off = align(off + (size_t)T * L.col_stride * sizeof(int32_t));
-  L.off_band_score = off; off = align(off + (size_t)T * L.col_stride * sizeof(double));
+  L.off_band_idx = off;   off = align(off + (size_t)rows * L.col_stride * sizeof(int32_t));
+  L.off_band_score = off; off = align(off + (size_t)rows * L.col_stride * sizeof(double));
   L.off_work = off;       off = align(off + 8 * sizeof(int));
   L.total = off;
   return L;
@@ -55,6 +62,8 @@ hipError_t launch_topk(const qsa_topk_args& a, const TopkLayout& L, char* ws, hi
   P.band_idx = reinterpret_cast<int32_t*>(ws + L.off_band_idx);
   P.band_score = reinterpret_cast<double*>(ws + L.off_band_score);
   P.work = reinterpret_cast<int*>(ws + L.off_work);
+  P.row_lo = 0;
+  P.row_hi = P.T;
 
   // bf16 requests with more than kMfmaMinRows rows are scored on the matrix cores, the others
   // (and every fp8 request) by the VALU kernel; each kernel skips the other's requests.
@@ -65,12 +74,19 @@ hipError_t launch_topk(const qsa_topk_args& a, const TopkLayout& L, char* ws, hi
   P.mfma_min_rows = mfma_ok ? kMfmaMinRows : INT32_MAX;
   if (phase == Phase::kSecond) return launch_topk_select(P, s);
   const int rows_per_chunk = mfma ? kMfmaMinRows : a.max_query_len;
-  hipError_t e = P.relu ? launch_logits_valu_relu(P, s)
-                        : launch_logits_valu(P, rows_per_chunk, mfma, s);
-  if (e != hipSuccess) return e;
-  if (mfma && (e = launch_logits_mfma(P, a.max_query_len, s)) != hipSuccess) return e;
-  if (phase == Phase::kFirst) return hipSuccess;
-  return launch_topk_select(P, s);
+  // Window by window (one window without a logits cap; the split calls take one only): the
+  // logits of the window's rows, then their selection, reusing the workspace.
+  for (int lo = 0; lo < P.T; lo += L.rows) {
+    P.row_lo = lo;
+    P.row_hi = lo + L.rows < P.T ? lo + L.rows : P.T;
+    hipError_t e = P.relu ? launch_logits_valu_relu(P, s)
+                          : launch_logits_valu(P, rows_per_chunk, mfma, s);
+    if (e != hipSuccess) return e;
+    if (mfma && (e = launch_logits_mfma(P, a.max_query_len, s)) != hipSuccess) return e;
+    if (phase == Phase::kFirst) return hipSuccess;
+    if ((e = launch_topk_select(P, s)) != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace qsa

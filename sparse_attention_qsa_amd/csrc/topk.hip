@@ -257,7 +257,10 @@ __global__ __launch_bounds__(C::NT) void topk_kernel(SelectParams P) {
   __shared__ double band_score_s[kBandCap];
   __shared__ int32_t cbt_s[kTopkCbtCap];
 
-  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // The call's rows run in windows (one without a logits cap); the per-row workspace arrays
+  // hold the window's rows.
+  const int row = P.row_lo + blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t wrow = blockIdx.x;  // row - row_lo
   const int W = P.budget + P.c - 1, kb = P.budget / P.c;
   int32_t* out = P.packed + (int64_t)row * P.p_rs;
   // Barriers: LDS-only ones wait for the wave's LDS operations and nothing else (the fence of
@@ -273,7 +276,7 @@ __global__ __launch_bounds__(C::NT) void topk_kernel(SelectParams P) {
   // padded to col_stride), its share of the Q row, and the request metadata for the lookup.
   // Scores past C::PF are loaded once the row's visible range is known (a short request of a
   // call with long ones would otherwise read a long row it does not use).
-  const float* lg = P.logits + (int64_t)row * P.col_stride;
+  const float* lg = P.logits + wrow * P.col_stride;
   const int jb = tid * E;
   const int pf_end = min(P.col_stride, C::PF);
   float sc[E];
@@ -525,13 +528,13 @@ __global__ __launch_bounds__(C::NT) void topk_kernel(SelectParams P) {
   int need = kb - (tot >> 16);
   int nb = tot & 0xFFFF;
   const bool in_lds = nb <= kBandCap;
-  int32_t* bidx = in_lds ? band_idx_s : P.band_idx + (int64_t)row * P.col_stride;
+  int32_t* bidx = in_lds ? band_idx_s : P.band_idx + wrow * P.col_stride;
   {
     int o = cl_off & 0xFFFF;
     for (uint32_t bits = bandbits; bits; bits &= bits - 1) bidx[o++] = jb + __builtin_ctz(bits);
   }
   if (in_lds) lds_barrier(); else __syncthreads();
-  double* bscore = in_lds ? band_score_s : P.band_score + (int64_t)row * P.col_stride;
+  double* bscore = in_lds ? band_score_s : P.band_score + wrow * P.col_stride;
   const int32_t* band = bidx;
   const int groups = NT / 16;  // 16-lane groups: one band entry each at a time
   const int grp = tid >> 4, l16 = tid & 15;
@@ -562,7 +565,7 @@ __global__ __launch_bounds__(C::NT) void topk_kernel(SelectParams P) {
     const double hi2 = s_dbl[0] + 2.0 * E_f, lo2 = s_dbl[0] - 2.0 * E_f;
     // The band's new list: in LDS with the first, or in the row's logits (no longer needed).
     int32_t* band2 = in_lds ? band2_idx_s
-                            : reinterpret_cast<int32_t*>(P.logits + (int64_t)row * P.col_stride);
+                            : reinterpret_cast<int32_t*>(P.logits + wrow * P.col_stride);
     int n_in2_local = 0;
     for (int b = tid; b < nb; b += NT) {
       const double sb = bscore[b];
@@ -657,7 +660,8 @@ __global__ __launch_bounds__(C::NT) void topk_kernel(SelectParams P) {
 
 template <typename C>
 hipError_t launch_topk_kernel(const SelectParams& P, size_t mask_bytes, hipStream_t s) {
-  hipLaunchKernelGGL((topk_kernel<C>), dim3(P.T), dim3(C::NT), mask_bytes, s, P);
+  hipLaunchKernelGGL((topk_kernel<C>), dim3(P.row_hi - P.row_lo), dim3(C::NT), mask_bytes, s,
+                     P);
   return hipGetLastError();
 }
 
@@ -665,7 +669,7 @@ hipError_t launch_topk_kernel(const SelectParams& P, size_t mask_bytes, hipStrea
 
 hipError_t launch_topk_select(const SelectParams& P, hipStream_t s) {
   const size_t mask_bytes = (size_t)(P.cols + 31) / 32 * sizeof(uint32_t);
-  if (P.T >= kTopkPrefillMinRows && P.cols <= TopkPrefill::NT * TopkPrefill::E)
+  if (P.row_hi - P.row_lo >= kTopkPrefillMinRows && P.cols <= TopkPrefill::NT * TopkPrefill::E)
     return launch_topk_kernel<TopkPrefill>(P, mask_bytes, s);
   if (P.cols <= 512 * 8) return launch_topk_kernel<TopkDecode8>(P, mask_bytes, s);
   if (P.cols <= 512 * 16) return launch_topk_kernel<TopkDecode16>(P, mask_bytes, s);

@@ -17,7 +17,7 @@ from . import binding as B
 
 class QsaStep:
     def __init__(self, wl, num_splits: int = 0, gate: bool = True, main: dict | None = None,
-                 index_agg: str = "sum"):
+                 index_agg: str = "sum", max_logits_bytes: int = 0):
         dev = wl.q.device
         T = wl.num_tokens
         idx_dtype = torch.uint8 if wl.index_dtype == "fp8" else torch.bfloat16
@@ -44,7 +44,8 @@ class QsaStep:
             num_index_heads=wl.index_heads, compress_ratio=wl.compress_ratio,
             budget=wl.budget, index_dtype=wl.index_dtype, max_query_len=wl.max_query_len,
             max_seq_len=wl.max_seq_len, num_decode_requests=wl.num_decode_requests,
-            decode_query_len=wl.decode_query_len, index_agg=index_agg)
+            decode_query_len=wl.decode_query_len, index_agg=index_agg,
+            max_logits_bytes=max_logits_bytes)
         self.g_args = B.gqa_args(
             q=q, kv_cache=wl.kv_cache, block_table=wl.block_table,
             token_to_req=wl.token_to_req, packed=self.packed, out=self.out,

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(B.EXPORTED)
-    assert lib.qsa_abi_version() == 4
+    assert lib.qsa_abi_version() == 5
     assert lib.qsa_status_string(3) == b"QSA_ERR_WORKSPACE_TOO_SMALL"
 
 
@@ -104,11 +104,25 @@ def test_split_plan_and_workspace_sizes():
     t = _topk()
     ws = lib.qsa_index_logits_topk_workspace_size(C.byref(t))
     assert ws >= 64 * 8192 * (4 + 4 + 8)    # logits + band index + band score per column
+    # A logits cap of 10 rows' logits: the per-row arrays are sized for 10 rows, not 64.
+    capped = _topk(max_logits_bytes=10 * 8192 * 4)
+    wc = lib.qsa_index_logits_topk_workspace_size(C.byref(capped))
+    assert 10 * 8192 * 16 <= wc < 11 * 8192 * 16 + 64 * 64 * 4 + 4096
+    # A cap below one row still runs one row per window.
+    tiny = _topk(max_logits_bytes=1)
+    assert lib.qsa_index_logits_topk_workspace_size(C.byref(tiny)) >= 8192 * 16
+    assert lib.qsa_index_logits_topk_workspace_size(C.byref(_topk(max_logits_bytes=-1))) == 0
 
 
 def test_invalid_calls_are_rejected_before_any_launch():
     lib = B.lib()
     INVAL, NOTSUP, SMALL = 1, 2, 3
+    # The split top-k calls hand the workspace over between them: not under a multi-window cap.
+    capped = _topk(max_logits_bytes=10 * 8192 * 4)
+    ws = lib.qsa_index_logits_topk_workspace_size(C.byref(capped))
+    assert lib.qsa_index_logits(C.byref(capped), FAKE, ws, None) == NOTSUP
+    assert lib.qsa_block_topk(C.byref(capped), FAKE, ws, None) == NOTSUP
+    assert lib.qsa_index_logits_topk(C.byref(_topk(max_logits_bytes=-5)), FAKE, ws, None) == INVAL
     assert lib.qsa_sparse_gqa(C.byref(_gqa(head_dim=64)), None, 0, None) == NOTSUP
     assert lib.qsa_sparse_gqa(C.byref(_gqa(num_q_heads=12)), None, 0, None) == NOTSUP
     assert lib.qsa_sparse_gqa(C.byref(_gqa(page_size=8)), None, 0, None) == NOTSUP

@@ -205,6 +205,52 @@ def test_work_list_kernel_with_matrix_core_requests():
     assert np.array_equal(to_np(st.packed)[rows], ref.packed[rows])
 
 
+def _cap_for_rows(wl, rows: int) -> int:
+    """A logits cap (bytes) that makes windows of `rows` rows."""
+    cols = max(1, wl.max_seq_len // wl.compress_ratio)
+    return rows * ((cols + 63) // 64 * 64) * 4
+
+
+@pytest.mark.parametrize("name,rows,kw", [
+    ("chunked_prefill", 100, {}),                  # windows cut 128-row matrix-core blocks
+    ("chunked_prefill", 1100, dict(rows=640)),     # a window of 1100 rows: prefill top-k
+    ("decode_32k", 2, {}),
+    ("spec_verify_mrope", 7, {}),                  # windows cut a request's verify rows
+    ("fp8_decode", 3, {}),
+    ("decode_32k", 150, dict(num_requests=600, lengths=("uniform", 2100, 6000))),  # work list
+])
+def test_logits_cap_runs_in_windows_with_the_same_selection(name, rows, kw):
+    """With a logits memory cap the call scores and selects window by window, reusing a
+    workspace sized for one window; the packed rows equal the oracle's, bit for bit."""
+    wl = workload(name, **kw)
+    cap = _cap_for_rows(wl, rows)
+    log(f"logits cap {name}: T={wl.num_tokens}, windows of {rows} rows")
+    ref = oracle_step(wl, with_attention=False)
+    st = QsaStep(wl, max_logits_bytes=cap)
+    full = B.lib().qsa_index_logits_topk_workspace_size(
+        B.C.byref(QsaStep(workload(name, **kw)).t_args))
+    assert st.t_ws.numel() < full or rows >= wl.num_tokens
+    st.compress()
+    st.topk()
+    torch.cuda.synchronize()
+    packed = to_np(st.packed)
+    assert np.array_equal(packed, ref.packed), (
+        f"{int((packed != ref.packed).any(axis=1).sum())} rows differ")
+
+
+def test_logits_cap_with_relu_sum():
+    wl = workload("decode_32k", num_requests=40, lengths=("uniform", 2100, 6000), rows=3)
+    q_codes, after = oracle_compress(wl)
+    ref = oq.index_topk(to_np(wl.query_start_loc), to_np(wl.seq_lens), q_codes, after.ckv,
+                        to_np(wl.c_block_table), wl.compress_ratio, wl.budget, wl.index_dtype,
+                        agg="relu")
+    st = QsaStep(wl, index_agg="relu", max_logits_bytes=_cap_for_rows(wl, 10))
+    st.compress()
+    st.topk()
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(st.packed), ref)
+
+
 def test_prefill_row_counts_select_exactly():
     """Calls with many rows take the prefill top-k configuration (three 8-bit radix passes,
     256 threads): 1280 rows here, every one compared."""
