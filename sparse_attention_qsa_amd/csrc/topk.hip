@@ -191,16 +191,17 @@ __device__ __forceinline__ void folded_scores16(const SelectParams& P, const flo
 // before the request lookup (the rest once the visible range is known).  The decode
 // configurations spend LDS on few, fast rows; the prefill one (many rows, eight sharing a CU)
 // keeps its LDS small and loads after the lookup, when the row's width and type are known.
-template <int NT_, int E_, int RB_, int PASSES_, int BAND_, int CBT_, int PF_>
+template <int NT_, int E_, int RB_, int PASSES_, int BAND_, int CBT_, int PF_, int WPE_ = 1>
 struct TopkCfg {
   static constexpr int NT = NT_, E = E_, RB = RB_, PASSES = PASSES_, BAND = BAND_, CBT = CBT_;
   static constexpr int PF = PF_;
+  static constexpr int WPE = WPE_;  // waves per SIMD the registers must allow (1: no bound)
 };
 using TopkDecode8 = TopkCfg<512, 8, 12, 2, 1024, 2048, 8192>;
 using TopkDecode16 = TopkCfg<512, 16, 12, 2, 1024, 2048, 8192>;
 using TopkDecode32 = TopkCfg<512, 32, 12, 2, 1024, 2048, 8192>;
 using TopkDecode1k = TopkCfg<1024, 32, 12, 2, 1024, 2048, 8192>;
-using TopkPrefill = TopkCfg<256, 16, 8, 3, 256, 512, 0>;
+using TopkPrefill = TopkCfg<256, 16, 8, 3, 256, 512, 0, 8>;
 constexpr int kTopkPrefillMinRows = 1024;  // rows in the call from which TopkPrefill is used
 
 // Inclusive prefix sum over the 64 lanes of a wavefront: shifts within rows of 16, then the
@@ -236,7 +237,8 @@ __device__ __forceinline__ float round_down_f32(double t) {
 // t*E .. t*E+E-1 in registers for the whole selection (blocks past the visible range as -inf,
 // which no threshold below admits).
 template <typename C>
-__global__ __launch_bounds__(C::NT) void topk_kernel(SelectParams P) {
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
+void topk_kernel(SelectParams P) {
   constexpr int NT = C::NT, E = C::E;
   constexpr int kRadixBits = C::RB, kRadixBins = 1 << C::RB, kBandCap = C::BAND;
   constexpr int kTopkCbtCap = C::CBT;
