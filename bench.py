@@ -29,7 +29,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
-MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix cores, 2.5 PFLOP/s
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}   # MI355X dense matrix cores per dtype
 MFMA_MIN_ROWS = 16      # bf16 requests with more rows are scored on the matrix cores
 METRIC = "decode rows/sec + achieved HBM GB/s, QSA indexer+sparse GQA at 32k ctx"
 # The kernels timed one by one (each through the call that launches only it), with the sources
@@ -129,7 +129,7 @@ def algorithmic_bytes(wl, packed):
 def mfma_logits_flop(wl, index_agg):
     """Causal-visible indexer logits FLOP of the requests the matrix-core kernel scores: every
     (row, visible block) pair costs 2 * Hi * 128 (the per-head contraction it executes)."""
-    if wl.index_dtype != "bf16" or index_agg != "sum" or wl.index_heads > 8:
+    if index_agg != "sum" or wl.index_heads > 8:
         return 0
     c, flop = wl.compress_ratio, 0
     for L, n in zip(wl.seq_lens_host.tolist(), wl.rows_host.tolist()):
@@ -420,11 +420,13 @@ def main():
         # the rate is a lower bound of the matrix-core kernel's own.
         us = per_kernel["logits_valu_kernel+logits_mfma_kernel"]
         tf = mfma_flop / (us * 1e-6) / 1e12
-        out["mfma_logits"] = {"bound": "mfma", "kernels": ["logits_valu_kernel (max |k| pass)",
-                                                           "logits_mfma_kernel"],
+        peak = MFMA_PEAK_TFLOPS[wl0.index_dtype]
+        out["mfma_logits"] = {"bound": "mfma", "dtype": wl0.index_dtype,
+                              "kernels": ["logits_valu_kernel (max |k| pass)",
+                                          "logits_mfma_kernel"],
                               "us": round(us, 2), "flop": mfma_flop,
-                              "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
-                              "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+                              "achieved": round(tf, 1), "peak": peak,
+                              "unit": "TFLOP/s", "frac": round(tf / peak, 4)}
     if main_leg is not None:
         out["main_prepare"] = main_leg
     if host is not None:

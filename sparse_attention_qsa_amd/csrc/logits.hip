@@ -199,7 +199,7 @@ hipError_t launch_valu(const SelectParams& P, hipStream_t s) {
 
 template <bool FP8>
 hipError_t launch_logits(const SelectParams& P, int rows_per_chunk, bool mfma, hipStream_t s) {
-  if (mfma && !FP8)  // the matrix-core kernel scores the requests of more than 16 rows
+  if (mfma)  // the matrix-core kernel scores the requests of more than 16 rows
     return launch_valu<FP8, 4, false, true>(P, s);
   if (rows_per_chunk <= 1) return launch_valu<FP8, 1, false, false>(P, s);
   if (rows_per_chunk <= 2) return launch_valu<FP8, 2, false, false>(P, s);

@@ -251,8 +251,11 @@ hipError_t launch_logits_list(const SelectParams& P, int nr, bool relu, bool kma
       hipLaunchKernelGGL((logits_valu_list_kernel<true, 8, true>), g, b, 0, s, P);
     else
       hipLaunchKernelGGL((logits_valu_list_kernel<false, 8, true>), g, b, 0, s, P);
-  } else if (kmax) {  // matrix-core requests in the call: bf16 only
-    hipLaunchKernelGGL((logits_valu_list_kernel<false, 4, false, true>), g, b, 0, s, P);
+  } else if (kmax) {  // matrix-core requests in the call
+    if (P.fp8)
+      hipLaunchKernelGGL((logits_valu_list_kernel<true, 4, false, true>), g, b, 0, s, P);
+    else
+      hipLaunchKernelGGL((logits_valu_list_kernel<false, 4, false, true>), g, b, 0, s, P);
   } else if (P.fp8) {
     if (nr <= 1) hipLaunchKernelGGL((logits_valu_list_kernel<true, 1>), g, b, 0, s, P);
     else if (nr <= 2) hipLaunchKernelGGL((logits_valu_list_kernel<true, 2>), g, b, 0, s, P);

@@ -95,8 +95,15 @@ __device__ __forceinline__ uint32_t claim_async(int* counter) {
 // go to an out-of-range offset and are dropped.  The logits leave as bf16 (rounded to nearest
 // even; the row keeps its float32-sized stride): half the bytes of float32, and the top-k's
 // band absorbs the rounding (at most 2^-8 of the stored value).
+// F8: e4m3 indexer (128-byte key rows, 8 codes per operand register pair): the products of two
+// e4m3 values are exact in fp32, so the accumulated score has the bf16 instance's error bound.
+template <bool F8>
 __global__ __launch_bounds__(512) void logits_mfma_kernel(SelectParams P, int row_blocks) {
-  __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][kMfmaKeys * 256];
+  using frag_t = std::conditional_t<F8, long, bf16x8_t>;  // 8 values of one operand row
+  constexpr int kRowB = F8 ? 128 : 256;       // bytes of a key row
+  constexpr int kChunks = kRowB / 16;         // its 16-byte chunks
+  constexpr int kKeysPerLoad = 1024 / kRowB;  // keys one LDS-direct load instruction fills
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][kMfmaKeys * kRowB];
   __shared__ __attribute__((aligned(16))) uint8_t kok[2][kMfmaKeys];
   __shared__ int s_item[2];
   const int key_tiles = (P.cols + kMfmaKeys - 1) / kMfmaKeys;
@@ -121,12 +128,15 @@ __global__ __launch_bounds__(512) void logits_mfma_kernel(SelectParams P, int ro
   };
   // This lane's A-operand address in buffer b for k-step ks: key l16 of the group (the group
   // is an offset of 4 KiB), chunk 4ks + l4.
+  // (fp8: the 8 codes of dims 32ks + 8 l4 are half of chunk 2ks + l4/2.)
   uint32_t kaddr[2][4];
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-      kaddr[b][ks] = lds_addr(kbuf[b] + l16 * 256 + 16 * ((4 * ks + l4) ^ l16));
+      kaddr[b][ks] = F8 ? lds_addr(kbuf[b] + l16 * kRowB + 16 * ((2 * ks + (l4 >> 1)) ^ (l16 & 7)) +
+                                   8 * (l4 & 1))
+                        : lds_addr(kbuf[b] + l16 * kRowB + 16 * ((4 * ks + l4) ^ l16));
   }
 
   if (tid == 0) s_item[0] = atomicAdd(&P.work[0], 1);
@@ -168,45 +178,58 @@ __global__ __launch_bounds__(512) void logits_mfma_kernel(SelectParams P, int ro
     const int trow = 16 * w + l16;
     const int vis_t = trow >= wlo && trow < whi ? min((pbase + trow + 1) / P.c, P.cols) : 0;
 
-    // ---- key tile kt into buffer b: 8 LDS-direct loads per wave (wave w: keys 32w .. 32w+31);
+    // ---- key tile kt into buffer b: LDS-direct loads of 1 KiB, 32 / kKeysPerLoad per wave
+    // (wave w: keys 32w .. 32w+31; a load's lane L lands in key L / kChunks, slot L % kChunks);
     // a key that is not visible or whose page is outside the cache loads the cache's first
     // row and is flagged (its logits are written as zero).
     auto load_tile = [&](int kt, int b) __attribute__((always_inline)) {
-      int page[8];
+      constexpr int kL = 32 / kKeysPerLoad;
+      const int kin = lane / kChunks, slot = lane % kChunks;
+      int page[kL];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int jk = kt * kMfmaKeys + 32 * w + 4 * i + l4;
+      for (int i = 0; i < kL; ++i) {
+        const int jk = kt * kMfmaKeys + 32 * w + kKeysPerLoad * i + kin;
         const int col = jk < vis_max ? min(jk / P.Pc, P.cbt_width - 1) : 0;
         page[i] = P.cbt[(int64_t)r * P.cbt_stride + col];
       }
-      asm volatile("" : "+v"(page[0]), "+v"(page[1]), "+v"(page[2]), "+v"(page[3]),
-                   "+v"(page[4]), "+v"(page[5]), "+v"(page[6]), "+v"(page[7]));
+      if constexpr (kL == 8)
+        asm volatile("" : "+v"(page[0]), "+v"(page[1]), "+v"(page[2]), "+v"(page[3]),
+                     "+v"(page[4]), "+v"(page[5]), "+v"(page[6]), "+v"(page[7]));
+      else
+        asm volatile("" : "+v"(page[0]), "+v"(page[1]), "+v"(page[2]), "+v"(page[3]));
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int j = 32 * w + 4 * i + l4, jk = kt * kMfmaKeys + j;
+      for (int i = 0; i < kL; ++i) {
+        const int j = 32 * w + kKeysPerLoad * i + kin, jk = kt * kMfmaKeys + j;
         const bool ok = jk < vis_max && jk / P.Pc < P.cbt_width && page[i] >= 0 &&
                         page[i] < P.c_pages;
-        const int64_t off = ok ? ((int64_t)page[i] * P.Pc + jk % P.Pc) * kHeadDim * 2 : 0;
-        lds_dma16(ckv + off + 16 * (l16 ^ (j & 15)), kbuf[b] + (32 * w + 4 * i) * 256);
-        if (l16 == 0) kok[b][j] = ok;
+        const int64_t off = ok ? ((int64_t)page[i] * P.Pc + jk % P.Pc) * kRowB : 0;
+        lds_dma16(ckv + off + 16 * (slot ^ (j & (kChunks - 1))),
+                  kbuf[b] + (32 * w + kKeysPerLoad * i) * kRowB);
+        if (slot == 0) kok[b][j] = ok;
       }
     };
     load_tile(t0, t0 & 1);
 
     // ---- Q of this wave's rows (rows past the request repeat its last row), all heads; heads
     // past Hi are zero (their products add exact zeros).
-    bf16x8_t qf[kMfmaMaxHeads][4];
+    frag_t qf[kMfmaMaxHeads][4];
     {
       const int t = min(trow, nrows - 1);
-      const char* qrow = qb + (int64_t)(q0 + rb * kMfmaRows + t) * P.Hi * kHeadDim * 2;
+      const char* qrow = qb + (int64_t)(q0 + rb * kMfmaRows + t) * P.Hi * kHeadDim * (F8 ? 1 : 2);
 #pragma unroll
       for (int h = 0; h < kMfmaMaxHeads; ++h) {
         const int hh = min(h, P.Hi - 1);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          const u32x4_t u = *reinterpret_cast<const u32x4_t*>(
-              qrow + (int64_t)(hh * kHeadDim + 32 * ks + 8 * l4) * 2);
-          qf[h][ks] = __builtin_bit_cast(bf16x8_t, h < P.Hi ? u : u32x4_t{0u, 0u, 0u, 0u});
+          if constexpr (F8) {
+            const long u = *reinterpret_cast<const long*>(
+                qrow + (int64_t)(hh * kHeadDim + 32 * ks + 8 * l4));
+            qf[h][ks] = h < P.Hi ? u : 0l;
+          } else {
+            const u32x4_t u = *reinterpret_cast<const u32x4_t*>(
+                qrow + (int64_t)(hh * kHeadDim + 32 * ks + 8 * l4) * 2);
+            qf[h][ks] = __builtin_bit_cast(bf16x8_t, h < P.Hi ? u : u32x4_t{0u, 0u, 0u, 0u});
+          }
         }
       }
     }
@@ -229,13 +252,19 @@ __global__ __launch_bounds__(512) void logits_mfma_kernel(SelectParams P, int ro
       int st = 0;
       // Groups of four 16-key blocks; the A fragments of the next k-step are read while the
       // current one is multiplied.
-      bf16x8_t kf[2][4];
-      auto read_kf = [&](int kg0, int ks, bf16x8_t (&dst)[4]) __attribute__((always_inline)) {
+      frag_t kf[2][4];
+      auto read_kf = [&](int kg0, int ks, frag_t (&dst)[4]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          asm volatile("ds_read_b128 %0, %1"
-                       : "=v"(dst[q])
-                       : "v"(kaddr[b][ks] + 4096u * (kg0 + q)));
+        for (int q = 0; q < 4; ++q) {
+          if constexpr (F8)
+            asm volatile("ds_read_b64 %0, %1"
+                         : "=v"(dst[q])
+                         : "v"(kaddr[b][ks] + (uint32_t)(16 * kRowB) * (kg0 + q)));
+          else
+            asm volatile("ds_read_b128 %0, %1"
+                         : "=v"(dst[q])
+                         : "v"(kaddr[b][ks] + (uint32_t)(16 * kRowB) * (kg0 + q)));
+        }
       };
       read_kf(0, 0, kf[0]);
 #pragma unroll
@@ -245,7 +274,7 @@ __global__ __launch_bounds__(512) void logits_mfma_kernel(SelectParams P, int ro
         for (int q = 0; q < 4; ++q) acc[q] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          bf16x8_t(&cur)[4] = kf[ks & 1];
+          frag_t(&cur)[4] = kf[ks & 1];
           asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(cur[0]), "+v"(cur[1]), "+v"(cur[2]),
                        "+v"(cur[3]));
           if (ks < 3) {
@@ -257,7 +286,12 @@ __global__ __launch_bounds__(512) void logits_mfma_kernel(SelectParams P, int ro
           for (int h = 0; h < kMfmaMaxHeads; ++h) {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-              acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur[q], qf[h][ks], acc[q], 0, 0, 0);
+              if constexpr (F8)
+                acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(cur[q], qf[h][ks], acc[q], 0,
+                                                                   0, 0);
+              else
+                acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur[q], qf[h][ks], acc[q], 0, 0,
+                                                                 0);
           }
         }
         // Groups kg0 .. kg0+3 are final: element e of group kg is key 16kg + 4(lane/16) + e
@@ -310,7 +344,10 @@ hipError_t launch_logits_mfma(const SelectParams& P, int max_query_len, hipStrea
   }
   const int row_blocks = (max_query_len + kMfmaRows - 1) / kMfmaRows;
   const unsigned grid = (unsigned)cus[dev];
-  hipLaunchKernelGGL(logits_mfma_kernel, dim3(grid), dim3(512), 0, s, P, row_blocks);
+  if (P.fp8)
+    hipLaunchKernelGGL(logits_mfma_kernel<true>, dim3(grid), dim3(512), 0, s, P, row_blocks);
+  else
+    hipLaunchKernelGGL(logits_mfma_kernel<false>, dim3(grid), dim3(512), 0, s, P, row_blocks);
   return hipGetLastError();
 }
 

@@ -28,7 +28,7 @@ struct SelectParams {
   int* work;  // [8] work counters of the MFMA kernel's queues, zeroed by the VALU kernel
 };
 
-// bf16 requests with more rows than this are scored by the matrix-core logits kernel.
+// Requests with more rows than this are scored by the matrix-core logits kernel.
 constexpr int kMfmaMinRows = 16;
 // ... and at most this many indexer heads (their Q is held in registers).
 constexpr int kMfmaMaxHeads = 8;

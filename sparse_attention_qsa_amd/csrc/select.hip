@@ -65,11 +65,11 @@ hipError_t launch_topk(const qsa_topk_args& a, const TopkLayout& L, char* ws, hi
   P.row_lo = 0;
   P.row_hi = P.T;
 
-  // bf16 requests with more than kMfmaMinRows rows are scored on the matrix cores, the others
-  // (and every fp8 request) by the VALU kernel; each kernel skips the other's requests.
-  // (The matrix-core kernel sums the heads in its accumulator: ReLU-sum requests stay on the
-  // vector units.)
-  const bool mfma_ok = !P.fp8 && !P.relu && P.Hi <= kMfmaMaxHeads;
+  // Requests with more than kMfmaMinRows rows are scored on the matrix cores (bf16 or e4m3
+  // operands), the others by the VALU kernel; each kernel skips the other's requests.  (The
+  // matrix-core kernel sums the heads in its accumulator: ReLU-sum requests stay on the vector
+  // units.)
+  const bool mfma_ok = !P.relu && P.Hi <= kMfmaMaxHeads;
   const bool mfma = mfma_ok && a.max_query_len > kMfmaMinRows;
   P.mfma_min_rows = mfma_ok ? kMfmaMinRows : INT32_MAX;
   if (phase == Phase::kSecond) return launch_topk_select(P, s);

@@ -66,10 +66,15 @@ CONFIGS = {
                              compress_ratio=4, budget=2048, index_dtype="bf16", q_heads=16,
                              kv_heads=2, mrope_section=None, pool_factor=1.0,
                              kv_dtype="fp8", k_scale=0.0167, v_scale=0.0161),
+    # chunked_prefill with the fp8 e4m3 indexer (its logits on the fp8 matrix cores).
+    "chunked_prefill_fp8": dict(num_requests=4, lengths=("fixed", 16384), rows=8192,
+                                index_heads=8, compress_ratio=4, budget=2048,
+                                index_dtype="fp8", q_heads=16, kv_heads=2, mrope_section=None,
+                                pool_factor=1.0),
 }
 
 CONFIG_SEEDS = {"decode_32k_fp8kv": 1006, "tiny_decode": 1001, "decode_32k": 1002, "fp8_decode": 1003,
-                "chunked_prefill": 1004, "spec_verify_mrope": 1005}
+                "chunked_prefill": 1004, "spec_verify_mrope": 1005, "chunked_prefill_fp8": 1007}
 
 
 @dataclasses.dataclass

@@ -21,6 +21,7 @@ SCALED = {
     "chunked_prefill": dict(num_requests=2, lengths=("uniform", 3000, 4100), rows=384),
     "spec_verify_mrope": dict(num_requests=10, lengths=("loguniform", 1024, 24000)),
     "decode_32k_fp8kv": dict(num_requests=6, lengths=("uniform", 3000, 9000)),
+    "chunked_prefill_fp8": dict(num_requests=2, lengths=("uniform", 3000, 4100), rows=384),
 }
 
 TOL = {"bf16": 2e-2, "fp8": 6e-2}

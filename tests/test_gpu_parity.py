@@ -292,6 +292,21 @@ def test_full_size_chunked_prefill_on_sampled_rows():
     assert err <= TOL["bf16"]
 
 
+def test_full_size_chunked_prefill_fp8_indexer_on_sampled_rows():
+    """The fp8-indexer prefill (e4m3 logits on the matrix cores) at full size, sampled rows,
+    selection and attention."""
+    wl = workload("chunked_prefill_fp8", num_requests=4, lengths=("fixed", 16384), rows=8192)
+    rows = [3, 4096 + 5, 8192 + 8191, 2 * 8192 + 128, 3 * 8192 + 4000]
+    log(f"full-size chunked_prefill_fp8, sampled rows {rows}")
+    ref = oracle_step(wl, rows=rows)
+    st = run_gpu(wl)
+    packed = to_np(st.packed)
+    assert np.array_equal(packed[rows], ref.packed[rows])
+    err = max_abs(gpu_out_f64(st)[rows], ref.out[rows])
+    log(f"  max-abs {err:.3e}")
+    assert err <= TOL["fp8"]
+
+
 def test_fp8_kv_scales_act_on_scores_and_output():
     """Doubling v_scale doubles the output; a k_scale change equals the same change of the
     softmax scale (both within the float32 / bf16 rounding of the kernel)."""
@@ -351,6 +366,15 @@ def test_exact_ties_on_matrix_core_rows():
         packed = to_np(st.packed)
         assert np.array_equal(packed, ref.packed), (
             f"{int((packed != ref.packed).any(axis=1).sum())} rows differ")
+
+
+def test_exact_ties_on_fp8_matrix_core_rows():
+    wl = workload("chunked_prefill_fp8", num_requests=2, lengths=("fixed", 3000), rows=100)
+    row = wl.ckv[wl.c_block_table[0, 0], 0].clone()
+    wl.ckv[:] = row
+    ref = oracle_step(wl, with_attention=False)
+    st = run_gpu(wl)
+    assert np.array_equal(to_np(st.packed), ref.packed)
 
 
 def test_inert_rows_invalid_entries_and_empty_requests():
