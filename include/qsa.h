@@ -216,8 +216,8 @@ typedef struct qsa_topk_args {
   int32_t* packed;                  /* OUT [T, B + c] int32 (W + 1 columns), row stride below */
   int64_t packed_row_stride;
   qsa_agg index_agg;                /* SUM (0), or RELU_SUM: score = sum_h max(0, q_h . k),
-                                       heads in order; RELU_SUM needs Hi <= 8 and is scored
-                                       by the vector-unit kernel for every request          */
+                                       heads in order; RELU_SUM scores every request on the
+                                       matrix cores, one head per operand column            */
   int64_t max_logits_bytes;         /* 0: no cap.  Else the rows are scored and selected in
                                        windows of consecutive rows whose logits fit this many
                                        bytes (4 per compressed column, rounded to 64), each

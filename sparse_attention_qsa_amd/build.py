@@ -17,7 +17,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqsa.so")
 ARCH = "gfx950"
 
-SOURCES = ["qsa_abi.cpp", "compress.hip", "select.hip", "logits.hip", "logits_list.hip", "logits_mfma.hip",
+SOURCES = ["qsa_abi.cpp", "compress.hip", "select.hip", "logits.hip", "logits_list.hip", "logits_mfma.hip", "logits_relu.hip",
            "topk.hip", "gqa.hip", "diag.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",

@@ -208,10 +208,6 @@ hipError_t launch_logits(const SelectParams& P, int rows_per_chunk, bool mfma, h
 
 }  // namespace
 
-hipError_t launch_logits_valu_relu(const SelectParams& P, hipStream_t s) {
-  return P.fp8 ? launch_valu<true, 8, true, false>(P, s) : launch_valu<false, 8, true, false>(P, s);
-}
-
 hipError_t launch_logits_valu(const SelectParams& P, int rows_per_chunk, bool mfma,
                               hipStream_t s) {
   return P.fp8 ? launch_logits<true>(P, rows_per_chunk, mfma, s)

@@ -13,8 +13,8 @@ using namespace logits_tile;
 // trip) into LDS as the prefix sums of the requests' item counts, with the requests' row ranges
 // and visible keys beside it, then takes items blockIdx.x, blockIdx.x + gridDim.x, ...
 // Persistent variant of logits_valu_kernel for grids that do not fit the chip in one round
-// (long, uneven requests): workgroups of 512 threads (8 waves).  Item k of request r is the request's keys 1024k ..
-// 1024k+1023 (2 tiles of 512; a wave scores 64 keys per tile), scored against every row of the
+// (long, uneven requests): workgroups of 512 threads (8 waves).  Item k of request r is the
+// request's keys 1024k .. 1024k+1023 (2 tiles of 512; a wave scores 64 keys per tile), scored against every row of the
 // request, NR rows at a time.  A key's row is split over 16 lanes (bf16) or 8 lanes (fp8) of 16
 // bytes, so every load instruction reads 1 KiB of contiguous cache.  The cache row of every key
 // and the head-folded rows are staged in LDS once per item; the block table and the request
@@ -35,7 +35,7 @@ void logits_valu_list_kernel(SelectParams P) {
   __shared__ int32_t rows_s[kKeys];
   __shared__ float qf_s[NR][kHeadDim];
   __shared__ float red[kWaves];
-  __shared__ int32_t item_end[kLogitsListReqs];  // inclusive prefix sums of the requests' item counts
+  __shared__ int32_t item_end[kLogitsListReqs];  // inclusive prefix sums of the item counts
   __shared__ int32_t req_q0[kLogitsListReqs], req_n[kLogitsListReqs], req_vis[kLogitsListReqs];
   __shared__ int32_t s_tot[kWaves];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -246,12 +246,7 @@ void logits_valu_list_kernel(SelectParams P) {
 hipError_t launch_logits_list(const SelectParams& P, int nr, bool relu, bool kmax, unsigned grid,
                               hipStream_t s) {
   const dim3 g(grid), b(kLogitsThreads);
-  if (relu) {
-    if (P.fp8)
-      hipLaunchKernelGGL((logits_valu_list_kernel<true, 8, true>), g, b, 0, s, P);
-    else
-      hipLaunchKernelGGL((logits_valu_list_kernel<false, 8, true>), g, b, 0, s, P);
-  } else if (kmax) {  // matrix-core requests in the call
+  if (kmax) {  // matrix-core requests in the call
     if (P.fp8)
       hipLaunchKernelGGL((logits_valu_list_kernel<true, 4, false, true>), g, b, 0, s, P);
     else

@@ -115,8 +115,6 @@ qsa_status validate_topk(const qsa_topk_args* a) {
   // A row's fast scores are held in the registers of one workgroup.
   QSA_REQUIRE(a->max_seq_len / a->compress_ratio <= qsa::kTopkMaxCols, kNotSup);
   QSA_REQUIRE(a->index_agg == QSA_AGG_SUM || a->index_agg == QSA_AGG_RELU_SUM, kNotSup);
-  // ReLU-sum keeps every head's Q in registers (eight at most).
-  QSA_REQUIRE(a->index_agg == QSA_AGG_SUM || a->num_index_heads <= 8, kNotSup);
   QSA_REQUIRE(a->max_logits_bytes >= 0, kInval);
   return QSA_OK;
 }

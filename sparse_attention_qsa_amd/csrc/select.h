@@ -13,7 +13,7 @@ struct SelectParams {
   int row_lo, row_hi;  // the rows of this launch (a window under a logits memory cap); the
                        // per-row workspace arrays are indexed by row - row_lo
   bool fp8;
-  bool relu;          // ReLU-sum aggregation (every request on the vector-unit kernel)
+  bool relu;          // ReLU-sum aggregation (every request on the ReLU matrix-core kernel)
   const int32_t* qsl;
   const int32_t* seq_lens;
   const void* q_idx;
@@ -37,7 +37,9 @@ constexpr int kMfmaMaxHeads = 8;
 // mfma: the call has requests scored on the matrix cores (rows_per_chunk is then 16).
 hipError_t launch_logits_valu(const SelectParams& P, int rows_per_chunk, bool mfma,
                               hipStream_t s);
-hipError_t launch_logits_valu_relu(const SelectParams& P, hipStream_t s);
+// ReLU-sum logits on the matrix cores (logits_relu.hip): every head's product a column of one
+// contraction; the top-k bounds these scores with u = 2^-23.
+hipError_t launch_logits_relu_mfma(const SelectParams& P, hipStream_t s);
 // The persistent variant (logits_list.hip): `grid` workgroups walk the call's work list of
 // (request, 1024-key item) pairs; at most kLogitsListReqs requests.
 constexpr int kLogitsListReqs = 1024;

@@ -79,7 +79,7 @@ hipError_t launch_topk(const qsa_topk_args& a, const TopkLayout& L, char* ws, hi
   for (int lo = 0; lo < P.T; lo += L.rows) {
     P.row_lo = lo;
     P.row_hi = lo + L.rows < P.T ? lo + L.rows : P.T;
-    hipError_t e = P.relu ? launch_logits_valu_relu(P, s)
+    hipError_t e = P.relu ? launch_logits_relu_mfma(P, s)
                           : launch_logits_valu(P, rows_per_chunk, mfma, s);
     if (e != hipSuccess) return e;
     if (mfma && (e = launch_logits_mfma(P, a.max_query_len, s)) != hipSuccess) return e;

@@ -483,7 +483,8 @@ void topk_kernel(SelectParams P) {
   }
   // Bound of the head-folded float32 score (the VALU logits, and the second level below), and
   // of the per-head MFMA score (u = 2^-23 covers any rounding the matrix cores may use).
-  const double gam_f = (double)(P.Hi + 130) * 0x1p-24;
+  // (ReLU-sum scores come from the matrix cores: u = 2^-23, any order.)
+  const double gam_f = (double)(P.Hi + 130) * (P.relu ? 0x1p-23 : 0x1p-24);
   const double E_f = 2.0 * gam_f / (1.0 - gam_f) * kappa * A + 1e-30;
   const bool mfma_row = bf16_row;
   const double gam_m = (double)(P.Hi * kHeadDim + 2) * 0x1p-23;

@@ -123,6 +123,11 @@ def test_invalid_calls_are_rejected_before_any_launch():
     assert lib.qsa_index_logits(C.byref(capped), FAKE, ws, None) == NOTSUP
     assert lib.qsa_block_topk(C.byref(capped), FAKE, ws, None) == NOTSUP
     assert lib.qsa_index_logits_topk(C.byref(_topk(max_logits_bytes=-5)), FAKE, ws, None) == INVAL
+    # ReLU-sum takes up to 16 heads (one per matrix-core operand column), like the plain sum.
+    assert lib.qsa_index_logits_topk_workspace_size(C.byref(_topk(index_agg=1,
+                                                                    num_index_heads=16))) > 0
+    assert lib.qsa_index_logits_topk_workspace_size(C.byref(_topk(index_agg=1,
+                                                                    num_index_heads=17))) == 0
     assert lib.qsa_sparse_gqa(C.byref(_gqa(head_dim=64)), None, 0, None) == NOTSUP
     assert lib.qsa_sparse_gqa(C.byref(_gqa(num_q_heads=12)), None, 0, None) == NOTSUP
     assert lib.qsa_sparse_gqa(C.byref(_gqa(page_size=8)), None, 0, None) == NOTSUP
@@ -143,7 +148,8 @@ def test_invalid_calls_are_rejected_before_any_launch():
     assert lib.qsa_index_logits_topk(C.byref(_topk(compress_ratio=3)), None, 0, None) == NOTSUP
     assert lib.qsa_index_logits_topk(C.byref(_topk(index_dtype=7)), None, 0, None) == NOTSUP
     assert lib.qsa_index_logits_topk(C.byref(_topk(index_agg=2)), None, 0, None) == NOTSUP
-    assert lib.qsa_index_logits_topk(C.byref(_topk(index_agg=1, num_index_heads=9)), None, 0,
+    # ReLU-sum with more than 16 heads: as for the plain sum.
+    assert lib.qsa_index_logits_topk(C.byref(_topk(index_agg=1, num_index_heads=17)), None, 0,
                                      None) == NOTSUP
     assert lib.qsa_index_logits_topk(C.byref(_topk(index_agg=1)), None, 0, None) == SMALL
     assert lib.qsa_index_logits_topk(C.byref(_topk()), None, 0, None) == SMALL

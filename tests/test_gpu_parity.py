@@ -448,6 +448,20 @@ def test_relu_sum_selection_is_exact(name):
         assert not np.array_equal(ref, oq.index_topk(*args, agg="sum"))
 
 
+def test_relu_sum_with_sixteen_heads():
+    """ReLU-sum with 16 indexer heads (every operand column of the matrix-core kernel a head)."""
+    wl = workload("decode_32k", index_heads=16)
+    q_codes, after = oracle_compress(wl)
+    ref = oq.index_topk(to_np(wl.query_start_loc), to_np(wl.seq_lens), q_codes, after.ckv,
+                        to_np(wl.c_block_table), wl.compress_ratio, wl.budget, wl.index_dtype,
+                        agg="relu")
+    st = QsaStep(wl, index_agg="relu")
+    st.compress()
+    st.topk()
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(st.packed), ref)
+
+
 def _advance(wl, seed):
     """The next decode step of `wl` (one row per request): each request one token longer, its
     row at the next position with fresh projections; the caches are shared with `wl`."""
