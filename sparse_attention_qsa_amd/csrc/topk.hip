@@ -72,8 +72,10 @@ __device__ __forceinline__ void key_pairs16(const SelectParams& P, const int32_t
     if (off >= 0) {
       if (P.fp8) {
         const uint32_t u = reinterpret_cast<const uint16_t*>(P.ckv)[off / 2 + i];
-        k0 = e4m3_to_f32_exact(u & 0xFFu);
-        k1 = e4m3_to_f32_exact(u >> 8);
+        // The hardware converter (OCP e4m3fn on gfx950) equals the definition on every code.
+        const auto f = __builtin_amdgcn_cvt_pk_f32_fp8(u, false);
+        k0 = f[0];
+        k1 = f[1];
       } else {
         const uint32_t u = reinterpret_cast<const uint32_t*>(P.ckv)[off / 2 + i];
         k0 = bf16lo(u);
@@ -159,9 +161,12 @@ __device__ __forceinline__ void folded_scores16(const SelectParams& P, const flo
     for (int u = 0; u < kFoldBatch; ++u) {
       float k[8];
       if (P.fp8) {
-#pragma unroll
-        for (int d = 0; d < 8; ++d)
-          k[d] = e4m3_to_f32_exact(((d < 4 ? raw[u].x : raw[u].y) >> (8 * (d & 3))) & 0xFFu);
+        const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(raw[u].x, false);
+        const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(raw[u].x, true);
+        const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(raw[u].y, false);
+        const auto d = __builtin_amdgcn_cvt_pk_f32_fp8(raw[u].y, true);
+        k[0] = a[0]; k[1] = a[1]; k[2] = b[0]; k[3] = b[1];
+        k[4] = c[0]; k[5] = c[1]; k[6] = d[0]; k[7] = d[1];
       } else {
         const uint32_t w4[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
 #pragma unroll
