@@ -61,6 +61,8 @@ def parse():
                    help="also run the main-attention prepare inside qsa_compress (the attention "
                         "then uses the prepared Q and reads the gate in place) and report its "
                         "marginal cost")
+    p.add_argument("--graph", action="store_true",
+                   help="also time the step captured in one HIP graph per input copy")
     p.add_argument("--profile-only", action="store_true",
                    help="warm up and run the timed steps only (for rocprofv3)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -341,6 +343,31 @@ def main():
     if steps[0].num_splits == 1:
         per_kernel.pop("gqa_merge_kernel")           # not launched with one split
 
+    graph_leg = None
+    if args.graph:
+        # The same K steps, each a replay of that input copy's captured step (no host launch
+        # work between the kernels).  Reported beside the eager figure, not in its place.
+        graphs = []
+        for st in steps:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                st.run()
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for i in range(args.warmup):
+            graphs[i % len(graphs)].replay()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for i in range(args.steps):
+            graphs[i % len(graphs)].replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms_g = a.elapsed_time(b) / args.steps
+        graph_leg = {"ms_per_step": round(ms_g, 4),
+                     "rows_per_s": round(wl0.num_tokens / (ms_g * 1e-3), 1)}
+        del graphs
+
     main_leg = None
     if args.main_prepare:
         # The prepare's marginal cost: the same compress call without it.
@@ -429,6 +456,8 @@ def main():
                               "unit": "TFLOP/s", "frac": round(tf / peak, 4)}
     if main_leg is not None:
         out["main_prepare"] = main_leg
+    if graph_leg is not None:
+        out["graph_replay"] = graph_leg
     if host is not None:
         del steps, wls
         torch.cuda.empty_cache()

@@ -516,3 +516,38 @@ def test_speculative_step_reuses_selection_and_rollback_rewrites_the_caches():
     torch.cuda.synchronize()
     assert torch.equal(after_xy[0], wl.ring)
     assert torch.equal(after_xy[1].view(torch.uint8), wl.ckv.view(torch.uint8))
+
+
+@pytest.mark.parametrize("name", ["decode_32k", "spec_verify_mrope", "chunked_prefill"])
+def test_step_captured_in_a_graph_replays_the_eager_results(name):
+    """The three calls make no host synchronisation, allocation or memset, so a caller can
+    capture a whole step in a HIP graph (decode loops in serving engines do).  Every replay,
+    with eager work on the same buffers in between, gives the eager step's results bit for
+    bit (this also covers the work-list kernel, which clears its own counter on the device)."""
+    wl = workload(name)
+    log(f"graph replay {name}: T={wl.num_tokens}")
+    st = QsaStep(wl)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        st.run(side)                       # eager, on a side stream, before the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    ref_packed, ref_out = st.packed.clone(), st.out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st.run()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        st.packed.fill_(-7)                # eager work between the replays
+        st.out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        log(f"  replay {rep}")
+        assert torch.equal(st.packed, ref_packed)
+        assert torch.equal(st.out.view(torch.int16), ref_out.view(torch.int16))
+        st.run()                           # an eager step between replays too
+        torch.cuda.synchronize()
+        assert torch.equal(st.packed, ref_packed)
+    del g
