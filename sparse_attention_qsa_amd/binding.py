@@ -154,6 +154,27 @@ def _need(t: torch.Tensor, dtype, name: str) -> None:
         raise ValueError(f"{name} must be contiguous in its last dimension")
 
 
+def _shape(t: torch.Tensor, shape: tuple, name: str) -> None:
+    """Exact shape check; a None entry matches any extent."""
+    if t.dim() != len(shape) or any(w is not None and int(g) != w
+                                    for g, w in zip(t.shape, shape)):
+        raise ValueError(f"{name} must have shape {shape}, got {tuple(t.shape)}")
+
+
+def _index_codes(t: torch.Tensor, index_dtype: str, name: str) -> None:
+    """Indexer storage: bf16 values, or e4m3fn codes held as uint8."""
+    if index_dtype not in DTYPES:
+        raise ValueError(f"index_dtype must be one of {sorted(DTYPES)}, got {index_dtype!r}")
+    _need(t, torch.bfloat16 if index_dtype == "bf16" else torch.uint8, name)
+
+
+def _q_idx(q_idx: torch.Tensor, T: int, heads: int, index_dtype: str) -> None:
+    _index_codes(q_idx, index_dtype, "q_idx")
+    _shape(q_idx, (T, heads, 128), "q_idx")
+    if not q_idx.is_contiguous():
+        raise ValueError("q_idx must be contiguous")
+
+
 # ------------------------------------------------------------------------------ qsa_compress
 
 
@@ -176,8 +197,24 @@ def compress_args(*, query_start_loc, seq_lens, max_query_len, q_proj, k_proj, p
     _need(seq_lens, torch.int32, "seq_lens")
     _need(ring_page, torch.int32, "ring_page")
     _need(c_block_table, torch.int32, "c_block_table")
+    T = q_proj.shape[0]
+    mrope = bool(mrope_section) and any(mrope_section)
+    _shape(k_proj, (T, None), "k_proj")
+    _shape(positions, (T, 3) if mrope else (T,), "positions")
+    for w, name in ((q_norm_weight, "q_norm_weight"), (k_norm_weight, "k_norm_weight")):
+        _need(w, torch.bfloat16, name)
+        _shape(w, (128,), name)
+    _shape(ring, (None, None, 128), "ring")
+    if mrope:
+        if ring_pos is None:
+            raise ValueError("ring_pos is required with mrope_section")
+        _need(ring_pos, torch.int64, "ring_pos")
+        _shape(ring_pos, (ring.shape[0], ring.shape[1], 3), "ring_pos")
+    _index_codes(ckv, index_dtype, "ckv")
+    _shape(ckv, (None, None, 128), "ckv")
+    _q_idx(q_idx, T, int(num_index_heads), index_dtype)
     a = CompressArgs()
-    a.num_tokens = q_proj.shape[0]
+    a.num_tokens = T
     a.num_requests = seq_lens.shape[0]
     a.query_start_loc = _ptr(query_start_loc)
     a.seq_lens = _ptr(seq_lens)
@@ -257,8 +294,13 @@ def topk_args(*, query_start_loc, seq_lens, q_idx, ckv, c_block_table, packed, n
     _need(seq_lens, torch.int32, "seq_lens")
     _need(c_block_table, torch.int32, "c_block_table")
     _need(packed, torch.int32, "packed")
+    T = q_idx.shape[0]
+    _q_idx(q_idx, T, int(num_index_heads), index_dtype)
+    _index_codes(ckv, index_dtype, "ckv")
+    _shape(ckv, (None, None, 128), "ckv")
+    _shape(packed, (T, int(budget) + int(compress_ratio) - 1 + 1), "packed")
     a = TopkArgs()
-    a.num_tokens = q_idx.shape[0]
+    a.num_tokens = T
     a.num_requests = seq_lens.shape[0]
     a.query_start_loc = _ptr(query_start_loc)
     a.seq_lens = _ptr(seq_lens)
@@ -315,6 +357,14 @@ def gqa_args(*, q, kv_cache, block_table, token_to_req, packed, out, gate=None, 
     _need(token_to_req, torch.int32, "token_to_req")
     _need(packed, torch.int32, "packed")
     _need(out, torch.bfloat16, "out")
+    T = q.shape[0]
+    _shape(q, (T, None, 128), "q")
+    _shape(kv_cache, (None, None, None, 256), "kv_cache")
+    _shape(token_to_req, (T,), "token_to_req")
+    _shape(packed, (T, None), "packed")
+    _shape(out, tuple(q.shape), "out")
+    if gate is not None:
+        _shape(gate, tuple(q.shape), "gate")
     a = GqaArgs()
     a.num_tokens = q.shape[0]
     a.num_requests = block_table.shape[0] if num_requests is None else int(num_requests)

@@ -7,9 +7,10 @@
 // Error bound: every product of two bf16 (or two e4m3) values is exact in float32; a head's 128
 // products are accumulated in an order the matrix core does not specify, so with faithful
 // rounding (u = 2^-23) the head's score is within gamma_130 of its exact value times
-// sum_d |q_hd k_d|; max(0, .) does not increase the distance, and the eight in-order float32
-// head additions add gamma_8.  The top-k bounds the whole score by gamma_{Hi+130} (u = 2^-23)
-// kappa A.
+// sum_d |q_hd k_d|; max(0, .) does not increase the distance, and the head sum is a DPP tree
+// over the 16 head lanes: any one head's value meets at most min(Hi - 1, 4) roundings (adding a
+// zero column past Hi is exact), which adds at most gamma_{Hi-1}.  The top-k bounds the whole
+// score by gamma_{Hi+130} (u = 2^-23) kappa A.
 #include "logits_tile.h"
 
 namespace qsa {

@@ -65,10 +65,11 @@ hipError_t launch_topk(const qsa_topk_args& a, const TopkLayout& L, char* ws, hi
   P.row_lo = 0;
   P.row_hi = P.T;
 
-  // Requests with more than kMfmaMinRows rows are scored on the matrix cores (bf16 or e4m3
-  // operands), the others by the VALU kernel; each kernel skips the other's requests.  (The
-  // matrix-core kernel sums the heads in its accumulator: ReLU-sum requests stay on the vector
-  // units.)
+  // Plain sum: requests with more than kMfmaMinRows rows are scored by the per-head matrix-core
+  // contraction (bf16 or e4m3 operands), the others by the VALU kernel; each kernel skips the
+  // other's requests.  ReLU-sum: every request goes to logits_relu_mfma_kernel, which clamps
+  // each head's product before the head sum (the per-head contraction keeps the heads summed
+  // in its accumulator, so it cannot clamp them).
   const bool mfma_ok = !P.relu && P.Hi <= kMfmaMaxHeads;
   const bool mfma = mfma_ok && a.max_query_len > kMfmaMinRows;
   P.mfma_min_rows = mfma_ok ? kMfmaMinRows : INT32_MAX;

@@ -9,6 +9,7 @@ import subprocess
 import tempfile
 
 import pytest
+import torch
 
 from sparse_attention_qsa_amd import binding as B
 
@@ -213,3 +214,55 @@ def test_invalid_main_prepare_arguments_are_rejected_before_any_launch():
     assert call(main_kv_dtype=1, main_kv_token_stride=264) == INVAL
     assert call(main_slot_mapping=FAKE + 4) == INVAL
     assert call(main_kv_cache=FAKE + 8) == INVAL
+
+
+def test_binding_rejects_tensors_that_do_not_match_the_call():
+    """The Python binding refuses, before any C call, tensors whose dtype or shape does not fit
+    the sizes it derives the argument blocks from (an e4m3 q_idx with a bf16 indexer would
+    make the kernels read and write past the buffers)."""
+    from sparse_attention_qsa_amd.workloads import make_workload
+    wl = make_workload("tiny_decode", device="cpu")
+    T, Hi = wl.num_tokens, wl.index_heads
+    q_idx = torch.empty((T, Hi, 128), dtype=torch.bfloat16)
+    packed = torch.empty((T, wl.output_width + 1), dtype=torch.int32)
+    out = torch.empty((T, wl.q_heads, 128), dtype=torch.bfloat16)
+    comp = dict(query_start_loc=wl.query_start_loc, seq_lens=wl.seq_lens,
+                max_query_len=wl.max_query_len, q_proj=wl.q_proj, k_proj=wl.k_proj,
+                positions=wl.positions, cos_sin=wl.cos_sin, q_norm_weight=wl.q_norm_w,
+                k_norm_weight=wl.k_norm_w, eps=wl.eps, ring=wl.ring, ring_page=wl.ring_page,
+                ckv=wl.ckv, c_block_table=wl.c_block_table, q_idx=q_idx, num_index_heads=Hi,
+                compress_ratio=wl.compress_ratio, index_dtype="bf16")
+    B.compress_args(**comp)                                           # the good call builds
+    bad = [
+        dict(q_idx=q_idx.view(torch.uint8)[..., :128]),               # e4m3 buffer, bf16 call
+        dict(q_idx=torch.empty((T, Hi - 1, 128), dtype=torch.bfloat16)),
+        dict(ckv=wl.ckv.view(torch.uint8)),                           # cache dtype mismatch
+        dict(index_dtype="fp8"),                                      # q_idx and ckv are bf16
+        dict(k_proj=wl.k_proj[:T - 1]),
+        dict(positions=torch.stack([wl.positions] * 3, 1)),           # triples without MRoPE
+        dict(mrope_section=(12, 10, 10)),                             # 1-D positions, no ring_pos
+        dict(q_norm_weight=wl.q_norm_w.float()),
+        dict(k_norm_weight=wl.k_norm_w[:64]),
+    ]
+    for over in bad:
+        with pytest.raises(ValueError):
+            B.compress_args(**{**comp, **over})
+    sel = dict(query_start_loc=wl.query_start_loc, seq_lens=wl.seq_lens, q_idx=q_idx,
+               ckv=wl.ckv, c_block_table=wl.c_block_table, packed=packed,
+               num_index_heads=Hi, compress_ratio=wl.compress_ratio, budget=wl.budget,
+               index_dtype="bf16", max_query_len=wl.max_query_len,
+               max_seq_len=wl.max_seq_len)
+    B.topk_args(**sel)
+    for over in (dict(index_dtype="fp8"), dict(num_index_heads=Hi + 1),
+                 dict(packed=packed[:, :-1]), dict(budget=wl.budget * 2),
+                 dict(ckv=wl.ckv.view(torch.uint8))):
+        with pytest.raises(ValueError):
+            B.topk_args(**{**sel, **over})
+    att = dict(q=wl.q, kv_cache=wl.kv_cache, block_table=wl.block_table,
+               token_to_req=wl.token_to_req, packed=packed, out=out, gate=wl.gate)
+    B.gqa_args(**att)
+    for over in (dict(out=out[:, :1]), dict(token_to_req=wl.token_to_req[:1]),
+                 dict(packed=packed[:1]), dict(gate=wl.gate[:, :, :64]),
+                 dict(kv_cache=wl.kv_cache[..., :128])):
+        with pytest.raises(ValueError):
+            B.gqa_args(**{**att, **over})

@@ -35,11 +35,34 @@ def ulp_diff_bf16(a, b):
 def test_halving_sum_is_exact_on_integers_and_has_the_stated_order():
     x = RNG.integers(-1000, 1000, size=(50, 128)).astype(np.float64)
     assert np.array_equal(oq.halving_sum(x), x.sum(axis=1))
-    # Order pin: big terms at dims 0 and 64 cancel only if they meet early.
+
+
+def test_halving_sum_order_pins_pairs_first_then_upper_half_onto_lower_half():
+    """Values where the order decides the float64 result.  Each case is worked by hand from
+    the stated order (adjacent pairs, then strides 32, 16, ..., 1); a sequential sum and a
+    tree that keeps adding adjacent partials give a different answer on one of them."""
+    # Case 1: dims 2 and 3 cancel inside their pair, so the 1 at dim 1 survives.
+    #   halving: pair(0,1) = 1, pair(2,3) = 0 -> 1.   sequential: (1 + 2^60) - 2^60 = 0.
     v = np.zeros(128)
-    v[0], v[1], v[64] = 2.0 ** 60, 1.0, -(2.0 ** 60)
-    # pairs: (0,1) -> 2^60 (1 is lost); the halvings then bring dim 64's pair onto it -> 0.
-    assert oq.halving_sum(v[None])[0] == 0.0
+    v[1], v[2], v[3] = 1.0, 2.0 ** 60, -(2.0 ** 60)
+    assert oq.halving_sum(v[None])[0] == 1.0
+    assert np.cumsum(v)[-1] == 0.0                   # the order the pin rules out
+    # Case 2: pair(0,1) = 2^60, pair(2,3) = 1, pair(64,65) = -2^60.  The stride-32 fold adds
+    # pair 32 (dims 64, 65) onto pair 0 first -> 0, and pair 1 keeps its 1 -> 1.  A tree of
+    # adjacent partials adds pair 1 onto pair 0 first and loses the 1 -> 0.
+    v = np.zeros(128)
+    v[0], v[2], v[64] = 2.0 ** 60, 1.0, -(2.0 ** 60)
+    assert oq.halving_sum(v[None])[0] == 1.0
+    t = v[0::2] + v[1::2]
+    while len(t) > 1:
+        t = t[0::2] + t[1::2]
+    assert t[0] == 0.0                               # the adjacent tree the pin rules out
+    # Case 3: the same with the big pair at stride 16 (pair 16 = dims 32, 33): the stride-32
+    # fold leaves pair 16 alone and the stride-16 fold brings it onto pair 0.  2^60 + 1 at
+    # pair 0 would swallow the 1 if pair 1 were added before pair 16.
+    v = np.zeros(128)
+    v[0], v[2], v[32] = 2.0 ** 60, 1.0, -(2.0 ** 60)
+    assert oq.halving_sum(v[None])[0] == 1.0
 
 
 # ----------------------------------------------------------------------------- RMSNorm
@@ -202,6 +225,59 @@ def test_compress_of_identical_group_members_is_that_key_normalised_and_rotated(
     assert np.array_equal(got, expect)
 
 
+def _groups_with_exact_distinct_means(n_groups, c, scale, rng):
+    """Raw keys [n_groups * c, 128]: every member is an integer times `scale`, the members of
+    a group are distinct and none is parallel to the group's mean, and each dim's sum is a
+    multiple of c, so the mean is an integer times `scale` (exact in bf16)."""
+    raw = np.empty((n_groups * c, 128))
+    means = np.empty((n_groups, 128))
+    for g in range(n_groups):
+        members = rng.integers(-40, 41, size=(c - 1, 128))
+        # The mean is the integer `target`; the last member makes the sum c * target.
+        target = members.sum(axis=0) // c + rng.integers(-3, 4, size=128)
+        last = c * target - members.sum(axis=0)
+        grp = np.vstack([members, last[None, :]]).astype(np.float64)
+        for m in grp:   # no member may point the same way as the mean
+            assert abs(m @ target) < 0.999 * np.linalg.norm(m) * np.linalg.norm(target)
+        raw[g * c:(g + 1) * c] = grp * scale
+        means[g] = target * scale
+    return raw, means
+
+
+@pytest.mark.parametrize("c,chunks", [(4, [40]), (4, [9, 1, 13, 17]), (8, [40]),
+                                      (8, [3, 30, 7])])
+def test_compress_pools_the_mean_of_distinct_members(c, chunks):
+    """[ops] qsa_compress_groups_with_ratio pools each completed group; the reading is the mean.
+    With distinct integer members (scaled by 2^-14, so that RMSNorm's epsilon is not negligible)
+    the expected row is written out here without compress_step: mean -> Gemma RMSNorm ->
+    NeoX RoPE at the position of the group's first token.  Taking any one member, the sum, or
+    another rotary position gives a different row."""
+    rng = np.random.default_rng(2024 + c)
+    L = 40
+    raw, means = _groups_with_exact_distinct_means(L // c, c, 2.0 ** -14, rng)
+    assert np.array_equal(round_bf16(raw), raw) and np.array_equal(round_bf16(means), means)
+    st = _one_request_compress(raw, chunks, c)
+    w = bf16_bits_to_f64(_one_request_compress.w)
+    tab = rotary_table(L + 256).numpy().astype(np.float64)
+    table = np.arange(64)[::-1]
+    for g in range(L // c):
+        m = means[g]
+        # Gemma RMSNorm, written out: every square and the sum are exact here.
+        inv = 1.0 / np.sqrt(np.sum(m * m) / 128.0 + float(np.float32(1e-6)))
+        y = round_bf16((m * inv) * (1.0 + w))
+        cos, sin = tab[g * c, :32], tab[g * c, 32:]
+        a, b = y[:32], y[32:64]
+        expect = y.copy()
+        expect[:32] = round_bf16(a * cos - b * sin)
+        expect[32:64] = round_bf16(b * cos + a * sin)
+        got = bf16_bits_to_f64(st.ckv[table[g // 16], g % 16])
+        assert np.array_equal(got, expect), g
+        # The plausible wrong poolings differ from it.
+        for wrong in (raw[g * c], raw[g * c + c - 1], c * m):
+            inv_w = 1.0 / np.sqrt(np.sum(wrong * wrong) / 128.0 + float(np.float32(1e-6)))
+            assert not np.array_equal(round_bf16((wrong * inv_w) * (1.0 + w)), y)
+
+
 # ----------------------------------------------------------------------------- scores / select
 
 
@@ -230,6 +306,90 @@ def test_select_matches_brute_force_sort_with_ties():
 
 def test_select_all_tied_takes_lowest_indices():
     assert np.array_equal(oq.select_blocks(np.zeros(100), 7), np.arange(7))
+
+
+def _small_integer_index_case(idx_dtype, seed):
+    """A batch for index_topk with small-integer queries and keys (every score is an exact
+    integer, with many ties): 4 requests of 1, 3, 2 and 5 rows, compressed pages of 8 rows laid
+    out by a seeded permutation, unused rows poisoned with NaN."""
+    rng = np.random.default_rng(seed)
+    c, budget, Pc, Hi = 4, 32, 8, 3
+    lens = np.array([70, 37, 9, 130])
+    nrows = np.array([1, 3, 2, 5])
+    qsl = np.concatenate([[0], np.cumsum(nrows)])
+    ncols = (lens // c + Pc - 1) // Pc
+    pages = int(ncols.sum()) + 5
+    perm = rng.permutation(pages)
+    table = np.full((4, int(ncols.max())), -1, np.int64)
+    k = 0
+    for r in range(4):
+        table[r, :ncols[r]] = perm[k:k + ncols[r]]
+        k += ncols[r]
+    key_int = rng.integers(-3, 4, size=(pages, Pc, 128))
+    q_int = rng.integers(-3, 4, size=(int(qsl[-1]), Hi, 128))
+    if idx_dtype == "bf16":
+        enc = lambda v: torch.from_numpy(v.astype(np.float32)).to(torch.bfloat16).view(
+            torch.int16).numpy().view(np.uint16)
+        nan = np.uint16(0x7FC0)
+    else:
+        enc = lambda v: torch.from_numpy(v.astype(np.float32)).to(torch.float8_e4m3fn).view(
+            torch.uint8).numpy()
+        nan = np.uint8(0x7F)
+    ckv = enc(key_int)
+    used = np.zeros((pages, Pc), bool)
+    for r in range(4):
+        for j in range(lens[r] // c):
+            used[table[r, j // Pc], j % Pc] = True
+    ckv[~used] = nan
+    return dict(c=c, budget=budget, lens=lens, qsl=qsl, table=table.astype(np.int32),
+                key_int=key_int, q_int=q_int, ckv=ckv, q_codes=enc(q_int))
+
+
+def _brute_force_packed(case):
+    """Packed rows written out directly: dense keys gathered from the pages, integer scores,
+    a full sort by (score descending, block ascending), then the blocks' tokens and the tail."""
+    c, budget = case["c"], case["budget"]
+    kb, W = budget // c, budget + c - 1
+    qsl, lens = case["qsl"], case["lens"]
+    out = np.full((int(qsl[-1]), W + 1), -1, np.int64)
+    for r in range(len(lens)):
+        n = qsl[r + 1] - qsl[r]
+        for i in range(n):
+            row = qsl[r] + i
+            p = lens[r] - n + i
+            vis = (p + 1) // c
+            j = np.arange(vis)
+            keys = case["key_int"][case["table"][r, j // 8], j % 8]          # [vis, 128]
+            score = (keys.astype(np.int64) @ case["q_int"][row].T.astype(np.int64)).sum(1)
+            order = sorted(range(vis), key=lambda b: (-score[b], b))
+            chosen = sorted(order[:kb])
+            toks = [t for b in chosen for t in range(b * c, b * c + c)]
+            toks += list(range(vis * c, p + 1))
+            out[row, :len(toks)] = toks
+            out[row, W] = len(toks)
+    return out
+
+
+@pytest.mark.parametrize("idx_dtype,seed", [("bf16", 1), ("bf16", 2), ("fp8", 3)])
+def test_index_topk_matches_brute_force_and_ignores_page_placement(idx_dtype, seed):
+    """[qsa] QSAIndexer.forward: each row scores its own indexer Q against its request's
+    compressed keys read through the compressed block table, keeps the budget / c best
+    blocks and expands them.  Checked against a brute force written here (no oracle code),
+    then the same batch with every compressed page moved and the table renumbered."""
+    case = _small_integer_index_case(idx_dtype, seed)
+    got = oq.index_topk(case["qsl"], case["lens"], case["q_codes"], case["ckv"],
+                        case["table"], case["c"], case["budget"], idx_dtype)
+    want = _brute_force_packed(case)
+    assert np.array_equal(got, want)
+    # Some rows really choose (vis > kb) and meet exact ties at the threshold.
+    assert (got[:, -1] >= case["budget"]).sum() >= 6
+    perm = np.random.default_rng(seed + 100).permutation(case["ckv"].shape[0])
+    moved = np.empty_like(case["ckv"])
+    moved[perm] = case["ckv"]
+    table2 = np.where(case["table"] >= 0, perm[case["table"]], -1).astype(np.int32)
+    again = oq.index_topk(case["qsl"], case["lens"], case["q_codes"], moved, table2, case["c"],
+                          case["budget"], idx_dtype)
+    assert np.array_equal(again, got)
 
 
 # ----------------------------------------------------------------------------- expand
