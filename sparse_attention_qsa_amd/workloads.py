@@ -124,11 +124,16 @@ class Workload:
 
     @property
     def num_decode_requests(self) -> int:
-        """Leading requests whose rows form a uniform decode batch (all of them when every
-        request has the same small row count)."""
-        if len(set(self.rows_host.tolist())) == 1 and self.rows_host[0] <= DECODE_MAX_ROWS:
-            return self.num_requests
-        return 0
+        """Leading requests whose rows form a uniform decode batch: the run of requests at the
+        front with the first request's row count, when that count is small (all of them for a
+        uniform decode batch; none when the batch starts with a prefill request)."""
+        n0 = int(self.rows_host[0])
+        if n0 > DECODE_MAX_ROWS:
+            return 0
+        k = 0
+        while k < self.num_requests and int(self.rows_host[k]) == n0:
+            k += 1
+        return k
 
     @property
     def decode_query_len(self) -> int:
@@ -189,21 +194,32 @@ def _page_table(needed: np.ndarray, pool_factor: float, rng):
 
 def make_workload(name: str, device="cpu", seed: int | None = None, **overrides) -> Workload:
     """Build the named workload.  `overrides` replace entries of its configuration (e.g.
-    num_requests=4, lengths=("fixed", 600), rows=3) for scaled-down parity cases."""
+    num_requests=4, lengths=("fixed", 600), rows=3) for scaled-down parity cases.  `rows` may
+    also be a sequence (rows of each request: decode requests first, then prefill requests, as
+    one mixed batch), and page_size, c_page_size and ring_size replace the main page (16), the
+    compressed page (16) and the raw-key ring width (16)."""
     cfg = dict(CONFIGS[name])
     cfg.update(overrides)
     seed = CONFIG_SEEDS.get(name, 1000) if seed is None else seed
     rng = np.random.default_rng(seed)
     R = int(cfg["num_requests"])
     lens = _lengths(cfg["lengths"], R, rng)
-    rows = np.minimum(np.full(R, int(cfg["rows"]), dtype=np.int64), lens)
+    if np.ndim(cfg["rows"]) == 0:
+        rows = np.full(R, int(cfg["rows"]), dtype=np.int64)
+    else:
+        rows = np.asarray(cfg["rows"], dtype=np.int64)
+        if rows.shape != (R,):
+            raise ValueError("rows must give one count per request")
+    rows = np.minimum(rows, lens)
     T = int(rows.sum())
     c = int(cfg["compress_ratio"])
     Hi = int(cfg["index_heads"])
     Hq, Hkv = int(cfg["q_heads"]), int(cfg["kv_heads"])
     mrope = cfg["mrope_section"]
     idt = cfg["index_dtype"]
-    S, Pc, P = RING_SIZE, C_PAGE_SIZE, PAGE_SIZE
+    S = int(cfg.get("ring_size", RING_SIZE))
+    Pc = int(cfg.get("c_page_size", C_PAGE_SIZE))
+    P = int(cfg.get("page_size", PAGE_SIZE))
 
     qsl = np.zeros(R + 1, dtype=np.int64)
     qsl[1:] = np.cumsum(rows)
