@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 5
+#define QSA_ABI_VERSION 6
 
 typedef enum qsa_status {
   QSA_OK = 0,
@@ -317,6 +317,25 @@ qsa_status qsa_sparse_gqa_partial(const qsa_gqa_args* args, void* workspace,
                                   size_t workspace_bytes, void* stream);
 qsa_status qsa_sparse_gqa_merge(const qsa_gqa_args* args, void* workspace,
                                 size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * qsa_sparse_gqa_noalloc: qsa_sparse_gqa for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments, kernels and results as qsa_sparse_gqa with a workspace; the split partials go to a
+ * static device array of qsa_sparse_gqa_noalloc_scratch_bytes() bytes (40 MiB) that the library
+ * holds on every GPU it runs on until the process ends.  The call allocates and frees nothing.
+ * Limits and behaviour:
+ *   - a call whose partials need more than that (qsa_sparse_gqa_workspace_size of the same
+ *     arguments) returns QSA_ERR_WORKSPACE_TOO_SMALL before any launch; every automatic split
+ *     plan fits (its partials stay below 34 MB for any T, Hq, Hkv), a forced num_splits may not;
+ *   - every call on one GPU shares that GPU's array: calls that overlap in time on one GPU (two
+ *     streams, two threads) race and give undefined results.  Serialise them on one stream.
+ *     Nothing needs clearing between calls: each call writes every partial it reads.
+ *   - the first call on a device looks up the array's device address (hipGetSymbolAddress);
+ *     a failure there returns QSA_ERR_HIP.
+ * ------------------------------------------------------------------------------------------ */
+qsa_status qsa_sparse_gqa_noalloc(const qsa_gqa_args* args, void* stream);
+size_t qsa_sparse_gqa_noalloc_scratch_bytes(void);
 
 /* ------------------------------------------------------------------------------------------
  * Diagnostics: the device arithmetic the bit-exact parts of the path rest on, exposed so a test

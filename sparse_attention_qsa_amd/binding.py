@@ -23,6 +23,7 @@ EXPORTED = (
     "qsa_index_logits", "qsa_block_topk",
     "qsa_sparse_gqa", "qsa_sparse_gqa_workspace_size", "qsa_sparse_gqa_num_splits",
     "qsa_sparse_gqa_partial", "qsa_sparse_gqa_merge",
+    "qsa_sparse_gqa_noalloc", "qsa_sparse_gqa_noalloc_scratch_bytes",
     "qsa_diag_e4m3_decode", "qsa_diag_fp64_sqrt_div", "qsa_status_string", "qsa_abi_version",
 )
 
@@ -114,6 +115,10 @@ def lib() -> C.CDLL:
         for f in ("qsa_sparse_gqa", "qsa_sparse_gqa_partial", "qsa_sparse_gqa_merge"):
             getattr(h, f).argtypes = [C.POINTER(GqaArgs), _P, C.c_size_t, _P]
             getattr(h, f).restype = C.c_int
+        h.qsa_sparse_gqa_noalloc.argtypes = [C.POINTER(GqaArgs), _P]
+        h.qsa_sparse_gqa_noalloc.restype = C.c_int
+        h.qsa_sparse_gqa_noalloc_scratch_bytes.argtypes = []
+        h.qsa_sparse_gqa_noalloc_scratch_bytes.restype = C.c_size_t
         h.qsa_diag_e4m3_decode.argtypes = [_P, _P]
         h.qsa_diag_e4m3_decode.restype = C.c_int
         h.qsa_diag_fp64_sqrt_div.argtypes = [_P, _P, _I64, _P]
@@ -423,6 +428,13 @@ def qsa_sparse_gqa(workspace=None, stream=None, **kw) -> None:
     nbytes = 0 if workspace is None else workspace.numel()
     _check(lib().qsa_sparse_gqa(C.byref(a), _ptr(workspace), nbytes, _stream(stream)),
            "qsa_sparse_gqa")
+
+
+def qsa_sparse_gqa_noalloc(stream=None, **kw) -> None:
+    """qsa_sparse_gqa without a workspace: the split partials live in the library's static
+    per-GPU scratch (calls that overlap on one GPU race; serialise them on one stream)."""
+    a = gqa_args(**kw)
+    _check(lib().qsa_sparse_gqa_noalloc(C.byref(a), _stream(stream)), "qsa_sparse_gqa_noalloc")
 
 
 # ------------------------------------------------------------------------------ diagnostics

@@ -15,6 +15,7 @@
 // of a KV head, and P.V) run on the matrix cores, which leaves the wave's VALU time to the
 // softmax (measured: the dot2 form of these contractions kept the SIMDs busy while the
 // gathers waited on them).
+#include <mutex>
 #include <type_traits>
 
 #include "qsa_internal.h"
@@ -502,6 +503,32 @@ hipError_t launch_partial(const GqaParams& P, bool f8, hipStream_t s) {
 }
 
 }  // namespace
+
+// Scratch of the allocation-free attention call: the split partials live in this array instead
+// of a caller workspace.  Every GPU the library runs on holds its own copy until the process
+// ends.  Host code never uses the array's name as an address: the device address of each
+// GPU's copy is looked up once with hipGetSymbolAddress and kept per device.
+static __device__ __align__(256) uint8_t scratch[kGqaScratchBytes];
+
+hipError_t gqa_scratch(char** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* per_device[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (per_device[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    per_device[dev] = p;
+  }
+  *ptr = static_cast<char*>(per_device[dev]);
+  return hipSuccess;
+}
 
 GqaPlan gqa_plan(const qsa_gqa_args& a) {
   GqaPlan p{};

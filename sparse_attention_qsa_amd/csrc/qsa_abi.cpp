@@ -264,6 +264,22 @@ qsa_status qsa_sparse_gqa_merge(const qsa_gqa_args* a, void* ws, size_t ws_bytes
   return run_gqa(a, ws, ws_bytes, stream, qsa::Phase::kSecond);
 }
 
+qsa_status qsa_sparse_gqa_noalloc(const qsa_gqa_args* a, void* stream) {
+  if (a == nullptr || a->num_tokens < 0) return kInval;
+  if (a->num_tokens == 0) return QSA_OK;  // nothing else is examined
+  if (qsa_status s = validate_gqa(a)) return s;
+  const qsa::GqaPlan plan = qsa::gqa_plan(*a);
+  if (plan.ws_bytes > qsa::kGqaScratchBytes) return QSA_ERR_WORKSPACE_TOO_SMALL;
+  char* ws = nullptr;
+  if (plan.ws_bytes > 0) {
+    if (qsa_status s = from_hip(qsa::gqa_scratch(&ws))) return s;
+  }
+  return from_hip(qsa::launch_gqa(*a, plan, ws, reinterpret_cast<hipStream_t>(stream),
+                                  qsa::Phase::kAll));
+}
+
+size_t qsa_sparse_gqa_noalloc_scratch_bytes(void) { return qsa::kGqaScratchBytes; }
+
 qsa_status qsa_diag_e4m3_decode(float* out, void* stream) {
   if (out == nullptr || !aligned(out, 4)) return kInval;
   return from_hip(qsa::launch_diag_e4m3(out, reinterpret_cast<hipStream_t>(stream)));

@@ -59,6 +59,10 @@ hipError_t launch_topk(const qsa_topk_args& a, const TopkLayout& L, char* ws, hi
                        Phase phase = Phase::kAll);
 hipError_t launch_gqa(const qsa_gqa_args& a, const GqaPlan& plan, char* ws, hipStream_t s,
                       Phase phase = Phase::kAll);
+// The allocation-free attention call's static scratch (gqa.hip): its size, and the device
+// address of the current device's copy (looked up on the first call on each device).
+constexpr size_t kGqaScratchBytes = size_t(40) << 20;
+hipError_t gqa_scratch(char** ptr);
 hipError_t launch_diag_e4m3(float* out, hipStream_t s);
 hipError_t launch_diag_fp64(const double* in, double* out, int64_t n, hipStream_t s);
 

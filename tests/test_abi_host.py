@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(B.EXPORTED)
-    assert lib.qsa_abi_version() == 5
+    assert lib.qsa_abi_version() == 6
     assert lib.qsa_status_string(3) == b"QSA_ERR_WORKSPACE_TOO_SMALL"
 
 
@@ -266,3 +266,32 @@ def test_binding_rejects_tensors_that_do_not_match_the_call():
                  dict(kv_cache=wl.kv_cache[..., :128])):
         with pytest.raises(ValueError):
             B.gqa_args(**{**att, **over})
+
+
+def test_no_alloc_attention_rejects_before_any_launch():
+    """qsa_sparse_gqa_noalloc validates like qsa_sparse_gqa, and refuses a plan whose partials
+    exceed its static scratch (here 64 forced splits of 1024 rows x 16 heads) before touching a
+    device."""
+    lib = B.lib()
+    INVAL, NOTSUP, SMALL = 1, 2, 3
+    limit = lib.qsa_sparse_gqa_noalloc_scratch_bytes()
+    assert limit == 40 << 20
+    assert lib.qsa_sparse_gqa_noalloc(None, None) == INVAL
+    assert lib.qsa_sparse_gqa_noalloc(C.byref(_gqa(num_tokens=0)), None) == 0
+    assert lib.qsa_sparse_gqa_noalloc(C.byref(_gqa(head_dim=64)), None) == NOTSUP
+    assert lib.qsa_sparse_gqa_noalloc(C.byref(_gqa(q=None)), None) == INVAL
+    big = _gqa(num_tokens=1024, num_splits=64)
+    assert lib.qsa_sparse_gqa_workspace_size(C.byref(big)) > limit
+    assert lib.qsa_sparse_gqa_noalloc(C.byref(big), None) == SMALL
+    # Every automatic split plan fits the scratch, whatever the rows, heads and K/V dtype.
+    for T in (1, 2, 3, 5, 17, 64, 100, 255, 383, 767, 1023, 2047, 4096, 65536):
+        for hkv in (1, 2, 4, 8):
+            for G in (1, 2, 4, 8, 16):
+                for kv_dtype in (0, 1):
+                    a = _gqa(num_tokens=T, num_kv_heads=hkv, num_q_heads=hkv * G,
+                             q_row_stride=hkv * G * 128, out_row_stride=hkv * G * 128,
+                             kv_head_stride=16 * 256, kv_page_stride=hkv * 16 * 256,
+                             num_pages=1024, kv_dtype=kv_dtype)
+                    need = lib.qsa_sparse_gqa_workspace_size(C.byref(a))
+                    assert 0 < need or lib.qsa_sparse_gqa_num_splits(C.byref(a)) == 1
+                    assert need <= limit, (T, hkv, G, kv_dtype, need)
