@@ -96,11 +96,12 @@ def algorithmic_bytes(wl, packed):
     c = wl.compress_ratio
     lens = wl.seq_lens_host
     rows = wl.rows_host
+    S = int(wl.ring.shape[1])
     groups = int(sum(L // c - (L - n) // c for L, n in zip(lens, rows)))
     b_compress = (T * Hi * 128 * 2 + T * 128 * 2          # q_proj, k_proj
                   + T * Hi * 128 * elt                     # q_idx written
                   + groups * 128 * elt                     # compressed rows written
-                  + int(sum(min(16, n) for n in rows)) * 128 * 2)   # ring rows written
+                  + int(sum(min(S, n) for n in rows)) * 128 * 2)    # ring rows written
     b_logits = (int(sum(L // c for L in lens)) * 128 * elt  # every visible compressed key
                 + T * Hi * 128 * elt + T * (W + 1) * 4)    # q_idx read, packed written
     pk = packed.cpu().numpy()
@@ -131,7 +132,7 @@ def algorithmic_bytes(wl, packed):
 def mfma_logits_flop(wl, index_agg):
     """Causal-visible indexer logits FLOP of the requests the matrix-core kernel scores: every
     (row, visible block) pair costs 2 * Hi * 128 (the per-head contraction it executes)."""
-    if index_agg != "sum" or wl.index_heads > 8:
+    if index_agg != "sum" or wl.index_heads > 16:
         return 0
     c, flop = wl.compress_ratio, 0
     for L, n in zip(wl.seq_lens_host.tolist(), wl.rows_host.tolist()):
@@ -228,9 +229,42 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_mib": mib}))
 
 
-def cpu_baseline(host_inputs, wl_meta, agg="sum", min_seconds=10.0):
+_WORKER_WL = None
+
+
+def _oracle_rows(args):
+    """One task of the all-cores leg: the whole step restricted to a slice of the rows, on the
+    worker's own host copy of the workload (built on its first task from the same generator;
+    the worker was forked before the parent touched the GPU)."""
+    global _WORKER_WL
+    name, rows, agg = args
+    from threadpoolctl import threadpool_limits
+
+    from sparse_attention_qsa_amd.workloads import make_workload
+    from tests.oracle_io import oracle_step
+    with threadpool_limits(limits=1):
+        if _WORKER_WL is None or _WORKER_WL.name != name:
+            _WORKER_WL = make_workload(name, device="cpu")
+        if rows is None:        # warm-up task: hold the worker so that every worker gets one
+            time.sleep(1.0)
+            return 0
+        oracle_step(_WORKER_WL, rows=rows, agg=agg)
+    return len(rows)
+
+
+def oracle_pool():
+    """Worker processes for the all-cores oracle leg, one per host core (at most 16), forked
+    before anything in this process initialises the GPU."""
+    import multiprocessing as mp
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    cores = max(1, min(int(cores or 1), 16))
+    return mp.get_context("fork").Pool(cores), cores
+
+
+def cpu_baseline(host_inputs, wl_meta, agg="sum", min_seconds=10.0, pool=None):
     """The oracle, as it stands, on the whole step of the same workload (host inputs taken
-    before any GPU step), single-threaded, repeated until at least min_seconds have passed."""
+    before any GPU step): single-threaded, repeated until at least min_seconds have passed;
+    then, with `pool`, the same step's rows dealt out to one process per host core."""
     from threadpoolctl import threadpool_limits
 
     from tests.oracle_io import oracle_step
@@ -243,10 +277,78 @@ def cpu_baseline(host_inputs, wl_meta, agg="sum", min_seconds=10.0):
             dt = time.perf_counter() - t0
             if dt >= min_seconds:
                 break
-    return {"value": round(reps * wl_meta.num_tokens / dt, 3), "unit": "rows/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"the whole step ({wl_meta.num_tokens} rows of {wl_meta.name}) {reps} times, "
-                      f"{dt:.2f} s wall on one host core"}
+    out = {"value": round(reps * wl_meta.num_tokens / dt, 3), "unit": "rows/s", "cores": 1,
+           "kind": "oracle",
+           "sample": f"the whole step ({wl_meta.num_tokens} rows of {wl_meta.name}) {reps} times, "
+                     f"{dt:.2f} s wall on one host core"}
+    if pool is None:
+        return out
+    pool, cores = pool
+    T = wl_meta.num_tokens
+    cores = min(cores, T)
+    slices = [list(range(T))[i::cores] for i in range(cores)]
+    # Every worker builds its host copy first (not timed).
+    pool.map(_oracle_rows, [(wl_meta.name, None, agg)] * (2 * cores), chunksize=1)
+    t0 = time.perf_counter()
+    done, passes = 0, 0
+    while True:
+        done += sum(pool.map(_oracle_rows, [(wl_meta.name, sl, agg) for sl in slices],
+                             chunksize=1))
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds / 2:
+            break
+    out["all_cores"] = {"value": round(done / dt, 3), "unit": "rows/s", "cores": cores,
+                        "hardware_concurrency": os.cpu_count(),
+                        "sample": f"the whole step's {T} rows dealt to {cores} processes "
+                                  f"(each holds a host copy of the workload drawn with the same "
+                                  f"recipe and compresses the requests of its rows), {passes} "
+                                  f"passes, {dt:.2f} s wall"}
+    return out
+
+
+def measured_ceilings():
+    """Practical HBM ceilings on this device, measured with torch: a 1 GiB device copy (read +
+    write) and a gather of 2 KiB rows at random positions of a 1 GiB table (the access of the
+    attention's K/V gather: 4 consecutive tokens x 512 B), each cold (a fresh 1 GiB buffer is
+    written in between so the Infinity Cache holds nothing useful)."""
+    import torch
+    n = 2**30
+    a = torch.empty(n // 2, dtype=torch.bfloat16, device="cuda:0").normal_()
+    b = torch.empty_like(a)
+    flush = torch.empty(n // 4, dtype=torch.float32, device="cuda:0")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def timed(fn):
+        best = None
+        for _ in range(5):
+            flush.fill_(1.0)
+            torch.cuda.synchronize()
+            ev[0].record()
+            fn()
+            ev[1].record()
+            torch.cuda.synchronize()
+            t = ev[0].elapsed_time(ev[1]) * 1e-3
+            best = t if best is None else min(best, t)
+        return best
+    t_copy = timed(lambda: b.copy_(a))
+    rows = a.view(-1, 1024)                       # 2 KiB rows
+    idx = torch.randint(0, rows.shape[0], (rows.shape[0] // 8,), device="cuda:0")
+    out = torch.empty((idx.numel(), 1024), dtype=torch.bfloat16, device="cuda:0")
+    t_gather = timed(lambda: torch.index_select(rows, 0, idx, out=out))
+    gbytes = idx.numel() * 2048 * 2               # rows read + written
+    res = {"copy_gbps": round(2 * n / t_copy / 1e9, 1),
+           "gather_2k_gbps": round(gbytes / t_gather / 1e9, 1)}
+    del a, b, flush, rows, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def path_dtype(wl):
+    """Arithmetic types of the path: the indexer's, then the attention's K/V."""
+    idx = "e4m3" if wl.index_dtype == "fp8" else "bf16"
+    kv = "e4m3" if getattr(wl, "kv_dtype", "bf16") == "fp8" else "bf16"
+    return idx if idx == kv else f"{idx} indexer, {kv} attention"
 
 
 def main():
@@ -262,6 +364,9 @@ def main():
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return
+    pool = None
+    if not args.no_cpu_baseline and not args.profile_only:
+        pool = oracle_pool()                # forked before this process touches the GPU
     import torch
 
     from sparse_attention_qsa_amd.step import QsaStep
@@ -299,6 +404,21 @@ def main():
     if args.profile_only:
         print(json.dumps({"profile_only": True, "ms_per_step": ms_step}))
         return
+
+    # ---- per-step distribution: the same K steps again, an event pair around each
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        steps[i % len(steps)].run(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    import numpy as np
+    per_step_us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+    step_dist = {"median": round(float(np.median(per_step_us)), 2),
+                 "p10": round(float(np.percentile(per_step_us, 10)), 2),
+                 "p90": round(float(np.percentile(per_step_us, 90)), 2)}
 
     # ---- per-call times (HIP events on the launch stream around each call)
     per_call = {}
@@ -401,6 +521,7 @@ def main():
         per_kernel = {both if k == "logits_valu_kernel" else k: v for k, v in per_kernel.items()}
         alg_k[both] = alg_k.pop("logits_valu_kernel")
     step_bytes = sum(alg.values())
+    ceilings = measured_ceilings()
     rows_per_s = wl0.num_tokens / (ms_step * 1e-3)
     dom = max(per_kernel, key=per_kernel.get)      # the dominant kernel
     achieved = alg_k[dom] / (per_kernel[dom] * 1e-6) / 1e9
@@ -417,14 +538,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": path_dtype(wl0),
         "data": "synthetic",
         "config": {"workload": wl0.name, "requests": wl0.num_requests,
                    "context": int(wl0.max_seq_len), "rows_per_request": int(wl0.rows_host[0]),
                    "index_heads": wl0.index_heads, "compress_ratio": wl0.compress_ratio,
                    "budget": wl0.budget, "index_dtype": wl0.index_dtype,
                    "q_heads": wl0.q_heads, "kv_heads": wl0.kv_heads, "head_dim": 128,
-                   "page_size": 16, "kv_dtype": getattr(wl0, "kv_dtype", "bf16"),
+                   "page_size": int(wl0.kv_cache.shape[2]), "kv_dtype": getattr(wl0, "kv_dtype", "bf16"),
                    "input_copies_rotated": len(steps),
                    "main_prepare": bool(args.main_prepare), "index_agg": args.index_agg,
                    "max_logits_mb": args.max_logits_mb,
@@ -432,6 +553,10 @@ def main():
                    "gqa_splits": steps[0].num_splits},
         "hbm_gbps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
         "hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "step_us": step_dist,
+        "measured_ceilings": ceilings,
+        "hbm_frac_of_copy_ceiling": round(step_bytes / (ms_step * 1e-3) / 1e9
+                                          / ceilings["copy_gbps"], 4),
         "step_algorithmic_bytes": int(step_bytes),
         "per_call_us": {k: round(v, 2) for k, v in per_call.items()},
         "per_call_algorithmic_bytes": {k: int(v) for k, v in alg.items()},
@@ -439,7 +564,8 @@ def main():
         "per_kernel_algorithmic_bytes": {k: int(alg_k[k]) for k in per_kernel},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "frac_of_gather_ceiling": round(achieved / ceilings["gather_2k_gbps"], 4)},
     }
     if mfma_flop and "logits_valu_kernel+logits_mfma_kernel" in per_kernel:
         # The logits call of a workload with matrix-core requests: logits_valu_kernel only takes
@@ -461,7 +587,10 @@ def main():
     if host is not None:
         del steps, wls
         torch.cuda.empty_cache()
-        out["cpu_baseline"] = cpu_baseline(host, wl0, args.index_agg)
+        out["cpu_baseline"] = cpu_baseline(host, wl0, args.index_agg, pool=pool)
+    if pool is not None:
+        pool[0].close()
+        pool[0].join()
     print(json.dumps(out))
 
 

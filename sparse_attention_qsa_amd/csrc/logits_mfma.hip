@@ -7,11 +7,15 @@
 
 namespace qsa {
 namespace {
-// Requests with many rows (chunked prefill) are scored per head on the matrix cores:
-// S = sum_h Q_h K^T with the head sum taken in the fp32 accumulator (bf16 products are exact in
-// fp32).  The fp32 result differs from the canonical float64 score by at most
-// gamma_{Hi*128} kappa A with u = 2^-23 (any summation order, faithful rounding); the top-k's
-// band covers that.
+// Requests with many rows (chunked prefill) are scored on the matrix cores with the heads
+// folded into Q: f = sum_h q_h (float32, heads in order), split into two bf16 terms
+// hi = bf16(f), lo = bf16(f - hi) (|f - hi - lo| <= 2^-16 |f|), and S = (hi + lo) . k as one
+// contraction of length 256 (bf16 products are exact in fp32).  Against the exact score
+// sum_h q_h . k the result is off by at most C kappa A with
+// C = gamma_{Hi-1} + (2^-16 + gamma'_{258} (1 + 2^-6)) (1 + gamma_{Hi-1})
+// (gamma with u = 2^-24 for the fold, gamma' with u = 2^-23 for the matrix-core sums, whose
+// order and rounding are not specified); the top-k's band covers that.  One contraction instead
+// of one per head: a quarter of the matrix-core work of the per-head form, and a tighter bound.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -48,9 +52,12 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 #undef QSA_VMCNT
 }
 
-// Two float32 values rounded to nearest even as bf16, packed low then high.
+// Two float32 values rounded to nearest even as bf16, packed low then high (one
+// v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t bf16_pack_rne(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // LDS accesses issued as inline assembly, so that the compiler's own wait insertion (which
@@ -64,6 +71,16 @@ __device__ __forceinline__ uint32_t lds_load_u32(const void* p) {
 }
 __device__ __forceinline__ void lds_store_u32(void* p, uint32_t v) {
   asm volatile("ds_write_b32 %0, %1" ::"v"(lds_addr(p)), "v"(v) : "memory");
+}
+// Four LDS words at a, b, c, d (byte addresses), one wait.
+template <int N>
+__device__ __forceinline__ void lds_load_u32x4(uint32_t a, uint32_t b, uint32_t c, uint32_t d,
+                                               int (&o)[N], int k) {
+  asm volatile("ds_read_b32 %0, %4\n\tds_read_b32 %1, %5\n\tds_read_b32 %2, %6\n\t"
+               "ds_read_b32 %3, %7\n\ts_waitcnt lgkmcnt(0)"
+               : "=v"(o[k]), "=v"(o[k + 1]), "=v"(o[k + 2]), "=v"(o[k + 3])
+               : "v"(a), "v"(b), "v"(c), "v"(d)
+               : "memory");
 }
 
 // Claims the next work item (a returning global atomic issued as inline assembly: the
@@ -84,19 +101,20 @@ __device__ __forceinline__ uint32_t claim_async(int* counter) {
 // tiles of the longest rows next, so that the big items are claimed first.  The next item is
 // claimed when an item starts.
 //
-// The item's Q stays in registers: wave w holds rows 16w .. 16w+15 of the block, all heads
-// (up to kMfmaMaxHeads) and all 128 dims, as the B operand of v_mfma_f32_16x16x32_bf16.  Key
-// tiles (64 KiB) stream through two LDS buffers, loaded LDS-direct one tile ahead, so a tile
-// costs one barrier.  A wave multiplies a tile four 16-key groups at a time -- 4 x 4 k-steps x
-// Hi heads of MFMAs into four accumulators, the A operand (16 keys x 32 dims) read from LDS --
+// The item's folded Q stays in registers: wave w holds rows 16w .. 16w+15 of the block, the hi
+// and lo terms of all 128 dims, as the B operand of v_mfma_f32_16x16x32_bf16.  Key tiles
+// (64 KiB) stream through two LDS buffers, loaded LDS-direct one tile ahead, so a tile costs
+// one barrier.  A wave multiplies a tile four 16-key groups at a time -- 4 x 4 k-steps x 2
+// terms of MFMAs into four accumulators, the A operand (16 keys x 32 dims) read from LDS --
 // and stores each group's 16 rows x 16 keys as soon as it is final: the logits leave a store
 // per 128 MFMAs instead of in bursts, so that they do not stall the key loads behind them.
 // Stores are buffer stores whose range ends at the block's last row; keys a row does not see
 // go to an out-of-range offset and are dropped.  The logits leave as bf16 (rounded to nearest
 // even; the row keeps its float32-sized stride): half the bytes of float32, and the top-k's
 // band absorbs the rounding (at most 2^-8 of the stored value).
-// F8: e4m3 indexer (128-byte key rows, 8 codes per operand register pair): the products of two
-// e4m3 values are exact in fp32, so the accumulated score has the bf16 instance's error bound.
+// F8: e4m3 indexer (128-byte key rows): the key codes are converted to bf16 as the fragments are
+// read (exact: every e4m3 value is a bf16 value), Q is folded from its codes (exact in fp32),
+// and the contraction and its bound are those of the bf16 instance.
 template <bool F8>
 __global__ __launch_bounds__(512) void logits_mfma_kernel(SelectParams P, int row_blocks) {
   using frag_t = std::conditional_t<F8, long, bf16x8_t>;  // 8 values of one operand row
@@ -105,6 +123,10 @@ __global__ __launch_bounds__(512) void logits_mfma_kernel(SelectParams P, int ro
   constexpr int kKeysPerLoad = 1024 / kRowB;  // keys one LDS-direct load instruction fills
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][kMfmaKeys * kRowB];
   __shared__ __attribute__((aligned(16))) uint8_t kok[2][kMfmaKeys];
+  // The item's compressed-block-table entries (columns col0 ..), read once per item, so that a
+  // tile's loads need no global round trip (whose wait would also drain the logit stores).
+  constexpr int kPgCap = kMfmaTilesPerItem * kMfmaKeys + 1;
+  __shared__ int32_t pg_s[kPgCap];
   __shared__ int s_item[2];
   const int key_tiles = (P.cols + kMfmaKeys - 1) / kMfmaKeys;
   const int chunks = (key_tiles + kMfmaTilesPerItem - 1) / kMfmaTilesPerItem;
@@ -174,6 +196,15 @@ __global__ __launch_bounds__(512) void logits_mfma_kernel(SelectParams P, int ro
     }
     const int vis_max = min(L / P.c, P.cols);
     barrier();  // every wave is done with the previous item's buffers
+    // Block-table columns of the item's visible keys [t0 * 256, min(t1 * 256, vis_max)).
+    const int col0 = (t0 * kMfmaKeys) / P.Pc;
+    {
+      const int kend = min(t1 * kMfmaKeys, vis_max);
+      const int ncol = kend > t0 * kMfmaKeys ? (kend - 1) / P.Pc - col0 + 1 : 0;
+      for (int c = tid; c < ncol; c += 512)
+        pg_s[c] = P.cbt[(int64_t)r * P.cbt_stride + min(col0 + c, P.cbt_width - 1)];
+    }
+    barrier();  // the item's pages are in LDS
     // This lane's row of the block and the keys it sees.
     const int trow = 16 * w + l16;
     const int vis_t = trow >= wlo && trow < whi ? min((pbase + trow + 1) / P.c, P.cols) : 0;
@@ -186,17 +217,16 @@ __global__ __launch_bounds__(512) void logits_mfma_kernel(SelectParams P, int ro
       constexpr int kL = 32 / kKeysPerLoad;
       const int kin = lane / kChunks, slot = lane % kChunks;
       int page[kL];
+      uint32_t pa[kL];
 #pragma unroll
       for (int i = 0; i < kL; ++i) {
         const int jk = kt * kMfmaKeys + 32 * w + kKeysPerLoad * i + kin;
-        const int col = jk < vis_max ? min(jk / P.Pc, P.cbt_width - 1) : 0;
-        page[i] = P.cbt[(int64_t)r * P.cbt_stride + col];
+        // Visible keys have their column in pg_s; the others are masked below.
+        const int ci = jk < vis_max ? jk / P.Pc - col0 : 0;
+        pa[i] = lds_addr(&pg_s[ci]);
       }
-      if constexpr (kL == 8)
-        asm volatile("" : "+v"(page[0]), "+v"(page[1]), "+v"(page[2]), "+v"(page[3]),
-                     "+v"(page[4]), "+v"(page[5]), "+v"(page[6]), "+v"(page[7]));
-      else
-        asm volatile("" : "+v"(page[0]), "+v"(page[1]), "+v"(page[2]), "+v"(page[3]));
+#pragma unroll
+      for (int i = 0; i < kL; i += 4) lds_load_u32x4(pa[i], pa[i + 1], pa[i + 2], pa[i + 3], page, i);
 #pragma unroll
       for (int i = 0; i < kL; ++i) {
         const int j = 32 * w + kKeysPerLoad * i + kin, jk = kt * kMfmaKeys + j;
@@ -210,26 +240,45 @@ __global__ __launch_bounds__(512) void logits_mfma_kernel(SelectParams P, int ro
     };
     load_tile(t0, t0 & 1);
 
-    // ---- Q of this wave's rows (rows past the request repeat its last row), all heads; heads
-    // past Hi are zero (their products add exact zeros).
-    frag_t qf[kMfmaMaxHeads][4];
+    // ---- folded Q of this wave's rows (rows past the request repeat its last row): lane
+    // (l16, l4) holds dims 32 ks + 8 l4 .. +7 of row l16 for each k-step ks, as hi and lo bf16
+    // terms of f = sum_h q_h (float32, heads in order 0 .. Hi-1).
+    bf16x8_t qhi[4], qlo[4];
     {
       const int t = min(trow, nrows - 1);
       const char* qrow = qb + (int64_t)(q0 + rb * kMfmaRows + t) * P.Hi * kHeadDim * (F8 ? 1 : 2);
 #pragma unroll
-      for (int h = 0; h < kMfmaMaxHeads; ++h) {
-        const int hh = min(h, P.Hi - 1);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
+      for (int ks = 0; ks < 4; ++ks) {
+        float f[8];
+        for (int h = 0; h < P.Hi; ++h) {
+          float x[8];
           if constexpr (F8) {
-            const long u = *reinterpret_cast<const long*>(
-                qrow + (int64_t)(hh * kHeadDim + 32 * ks + 8 * l4));
-            qf[h][ks] = h < P.Hi ? u : 0l;
+            const uint2 u = *reinterpret_cast<const uint2*>(
+                qrow + (int64_t)(h * kHeadDim + 32 * ks + 8 * l4));
+            const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(u.x, false);
+            const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(u.x, true);
+            const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(u.y, false);
+            const auto d = __builtin_amdgcn_cvt_pk_f32_fp8(u.y, true);
+            x[0] = a[0]; x[1] = a[1]; x[2] = b[0]; x[3] = b[1];
+            x[4] = c[0]; x[5] = c[1]; x[6] = d[0]; x[7] = d[1];
           } else {
-            const u32x4_t u = *reinterpret_cast<const u32x4_t*>(
-                qrow + (int64_t)(hh * kHeadDim + 32 * ks + 8 * l4) * 2);
-            qf[h][ks] = __builtin_bit_cast(bf16x8_t, h < P.Hi ? u : u32x4_t{0u, 0u, 0u, 0u});
+            const uint4 u = *reinterpret_cast<const uint4*>(
+                qrow + (int64_t)(h * kHeadDim + 32 * ks + 8 * l4) * 2);
+            const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              x[2 * e] = __uint_as_float(w4[e] << 16);
+              x[2 * e + 1] = __uint_as_float(w4[e] & 0xFFFF0000u);
+            }
           }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) f[e] = h == 0 ? x[e] : f[e] + x[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const __bf16 hv = (__bf16)f[e];
+          qhi[ks][e] = hv;
+          qlo[ks][e] = (__bf16)(f[e] - (float)hv);  // f - hi is exact in float32
         }
       }
     }
@@ -253,6 +302,22 @@ __global__ __launch_bounds__(512) void logits_mfma_kernel(SelectParams P, int ro
       // Groups of four 16-key blocks; the A fragments of the next k-step are read while the
       // current one is multiplied.
       frag_t kf[2][4];
+      // Eight e4m3 codes (one 64-bit fragment) as bf16, exactly.
+      auto to_bf16 = [](frag_t v) __attribute__((always_inline)) {
+        if constexpr (F8) {
+          const uint32_t w0 = (uint32_t)(uint64_t)v, w1 = (uint32_t)((uint64_t)v >> 32);
+          const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(w0, false);
+          const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(w0, true);
+          const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(w1, false);
+          const auto d = __builtin_amdgcn_cvt_pk_f32_fp8(w1, true);
+          bf16x8_t r;
+          r[0] = (__bf16)a[0]; r[1] = (__bf16)a[1]; r[2] = (__bf16)b[0]; r[3] = (__bf16)b[1];
+          r[4] = (__bf16)c[0]; r[5] = (__bf16)c[1]; r[6] = (__bf16)d[0]; r[7] = (__bf16)d[1];
+          return r;
+        } else {
+          return v;
+        }
+      };
       auto read_kf = [&](int kg0, int ks, frag_t (&dst)[4]) __attribute__((always_inline)) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -282,17 +347,15 @@ __global__ __launch_bounds__(512) void logits_mfma_kernel(SelectParams P, int ro
           } else if (kg0 + 4 < 16) {
             read_kf(kg0 + 4, 0, kf[(ks + 1) & 1]);
           }
+          bf16x8_t ka[4];
 #pragma unroll
-          for (int h = 0; h < kMfmaMaxHeads; ++h) {
+          for (int q = 0; q < 4; ++q) ka[q] = to_bf16(cur[q]);
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-              if constexpr (F8)
-                acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(cur[q], qf[h][ks], acc[q], 0,
-                                                                   0, 0);
-              else
-                acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur[q], qf[h][ks], acc[q], 0, 0,
-                                                                 0);
-          }
+          for (int q = 0; q < 4; ++q)
+            acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[q], qhi[ks], acc[q], 0, 0, 0);
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[q], qlo[ks], acc[q], 0, 0, 0);
         }
         // Groups kg0 .. kg0+3 are final: element e of group kg is key 16kg + 4(lane/16) + e
         // of row trow.  A group of 4 keys is written when its first key is visible to the row

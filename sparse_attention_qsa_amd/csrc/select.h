@@ -30,8 +30,8 @@ struct SelectParams {
 
 // Requests with more rows than this are scored by the matrix-core logits kernel.
 constexpr int kMfmaMinRows = 16;
-// ... and at most this many indexer heads (their Q is held in registers).
-constexpr int kMfmaMaxHeads = 8;
+// ... and at most this many indexer heads (they are folded into one Q in registers).
+constexpr int kMfmaMaxHeads = 16;
 
 // Launchers (each next to its kernels); arguments are validated by the caller.
 // mfma: the call has requests scored on the matrix cores (rows_per_chunk is then 16).

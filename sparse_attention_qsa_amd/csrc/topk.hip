@@ -487,13 +487,17 @@ void topk_kernel(SelectParams P) {
     A += s_dbl[i];
   }
   // Bound of the head-folded float32 score (the VALU logits, and the second level below), and
-  // of the per-head MFMA score (u = 2^-23 covers any rounding the matrix cores may use).
+  // of the matrix-core score: Q folded in float32 (heads in order), split into bf16 terms
+  // hi + lo with |f - hi - lo| <= 2^-16 |f| and |hi| + |lo| <= (1 + 2^-6) |f|, and 2 x 128
+  // exact products summed by the matrix cores in an unspecified order (u = 2^-23).
   // (ReLU-sum scores come from the matrix cores: u = 2^-23, any order.)
   const double gam_f = (double)(P.Hi + 130) * (P.relu ? 0x1p-23 : 0x1p-24);
   const double E_f = 2.0 * gam_f / (1.0 - gam_f) * kappa * A + 1e-30;
   const bool mfma_row = bf16_row;
-  const double gam_m = (double)(P.Hi * kHeadDim + 2) * 0x1p-23;
-  const double Ebound = mfma_row ? 2.0 * gam_m / (1.0 - gam_m) * kappa * A + 1e-30 : E_f;
+  const double g_fold = (double)(P.Hi - 1) * 0x1p-24 / (1.0 - (double)(P.Hi - 1) * 0x1p-24);
+  const double g_acc = (double)(2 * kHeadDim + 2) * 0x1p-23 / (1.0 - (double)(2 * kHeadDim + 2) * 0x1p-23);
+  const double gam_m = g_fold + (0x1p-16 + g_acc * (1.0 + 0x1p-6)) * (1.0 + g_fold);
+  const double Ebound = mfma_row ? 2.0 * gam_m * (1.0 + 0x1p-20) * kappa * A + 1e-30 : E_f;
   // Certainly kept above hi, certainly dropped below lo; float32 forms widen the band only.
   // A score b stands for canonical scores in [b - d(b), b + d(b)] with d(b) = Ebound (float32
   // rows) or Ebound + r |b| (bf16 rows: rounding to nearest moves a value by at most 2^-8 of
