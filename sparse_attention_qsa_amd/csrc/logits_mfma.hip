@@ -8,14 +8,18 @@
 namespace qsa {
 namespace {
 // Requests with many rows (chunked prefill) are scored on the matrix cores with the heads
-// folded into Q: f = sum_h q_h (float32, heads in order), split into two bf16 terms
-// hi = bf16(f), lo = bf16(f - hi) (|f - hi - lo| <= 2^-16 |f|), and S = (hi + lo) . k as one
-// contraction of length 256 (bf16 products are exact in fp32).  Against the exact score
-// sum_h q_h . k the result is off by at most C kappa A with
-// C = gamma_{Hi-1} + (2^-16 + gamma'_{258} (1 + 2^-6)) (1 + gamma_{Hi-1})
-// (gamma with u = 2^-24 for the fold, gamma' with u = 2^-23 for the matrix-core sums, whose
-// order and rounding are not specified); the top-k's band covers that.  One contraction instead
-// of one per head: a quarter of the matrix-core work of the per-head form, and a tighter bound.
+// folded into Q: f = sum_h q_h (float32, heads in order), split into three bf16 terms
+// hi = bf16(f), mid = bf16(f - hi), lo = bf16(f - hi - mid) (each difference exact in float32;
+// |f - hi - mid - lo| <= 2^-24 |f|), and S = (hi + mid + lo) . k (bf16 products are exact in
+// fp32).  The hi products of each 32-dim k-step are summed in an accumulator of their own (32
+// terms), the mid and lo products of all dims in one more (their size is 2^-8 of hi's), and the
+// five partial sums are added on the vector unit.  Against the exact score sum_h q_h . k the
+// result is off by at most C kappa A with
+// C = g_fold + (2^-24 + g'_34 (1 + 2^-7) + g'_258 2^-7 + g_4 (1 + 2^-6)) (1 + g_fold)
+// (g with u = 2^-24: the fold over Hi-1 additions and the final 4; g' with u = 2^-23: the
+// matrix-core sums, whose order and rounding are not specified); the top-k's band covers that.
+// One contraction of length 384 instead of one of length 128 per head: fewer matrix-core
+// operations than the per-head form and a bound below the vector-unit logits' own.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -101,11 +105,12 @@ __device__ __forceinline__ uint32_t claim_async(int* counter) {
 // tiles of the longest rows next, so that the big items are claimed first.  The next item is
 // claimed when an item starts.
 //
-// The item's folded Q stays in registers: wave w holds rows 16w .. 16w+15 of the block, the hi
-// and lo terms of all 128 dims, as the B operand of v_mfma_f32_16x16x32_bf16.  Key tiles
+// The item's folded Q stays in registers: wave w holds rows 16w .. 16w+15 of the block, the
+// three terms of all 128 dims, as the B operand of v_mfma_f32_16x16x32_bf16.  Key tiles
 // (64 KiB) stream through two LDS buffers, loaded LDS-direct one tile ahead, so a tile costs
-// one barrier.  A wave multiplies a tile four 16-key groups at a time -- 4 x 4 k-steps x 2
-// terms of MFMAs into four accumulators, the A operand (16 keys x 32 dims) read from LDS --
+// one barrier.  A wave multiplies a tile four 16-key groups at a time -- 4 x 4 k-steps x 3
+// terms of MFMAs into five accumulators per group, the A operand (16 keys x 32 dims) read
+// from LDS --
 // and stores each group's 16 rows x 16 keys as soon as it is final: the logits leave a store
 // per 128 MFMAs instead of in bursts, so that they do not stall the key loads behind them.
 // Stores are buffer stores whose range ends at the block's last row; keys a row does not see
@@ -127,6 +132,11 @@ __global__ __launch_bounds__(512) void logits_mfma_kernel(SelectParams P, int ro
   // tile's loads need no global round trip (whose wait would also drain the logit stores).
   constexpr int kPgCap = kMfmaTilesPerItem * kMfmaKeys + 1;
   __shared__ int32_t pg_s[kPgCap];
+  // Per wave, one batch of logits (16 rows x 64 keys, bf16) on its way out: the batch is
+  // written here as the matrix-core layout has it (4 keys of one row per lane) and read back
+  // as 16-byte row pieces, so that a store instruction writes 8 whole 128-byte row segments
+  // instead of 16 rows x 32 bytes.  16-byte chunk c of row r sits in slot c ^ (r & 7).
+  __shared__ __attribute__((aligned(16))) uint8_t stg[kMfmaRows / 16][16 * 128];
   __shared__ int s_item[2];
   const int key_tiles = (P.cols + kMfmaKeys - 1) / kMfmaKeys;
   const int chunks = (key_tiles + kMfmaTilesPerItem - 1) / kMfmaTilesPerItem;
@@ -206,8 +216,17 @@ __global__ __launch_bounds__(512) void logits_mfma_kernel(SelectParams P, int ro
     }
     barrier();  // the item's pages are in LDS
     // This lane's row of the block and the keys it sees.
-    const int trow = 16 * w + l16;
-    const int vis_t = trow >= wlo && trow < whi ? min((pbase + trow + 1) / P.c, P.cols) : 0;
+    const int trow = 16 * w + l16;  // the row of this lane's matrix-core results
+    // The rows this lane stores from the staging buffer: 16 w + (lane / 8) + 8 s, s < 2, keys
+    // 8 (lane % 8) .. +7 of each batch; their visible limits and offsets in the window.
+    int vis_s[2], roff_s[2];
+#pragma unroll
+    for (int sr = 0; sr < 2; ++sr) {
+      const int br = 16 * w + (lane >> 3) + 8 * sr;
+      vis_s[sr] = br >= wlo && br < whi ? min((pbase + br + 1) / P.c, P.cols) : 0;
+      roff_s[sr] = (br - wlo) * P.col_stride * 4;
+    }
+    const uint32_t stg_base = lds_addr(stg[w]);
 
     // ---- key tile kt into buffer b: LDS-direct loads of 1 KiB, 32 / kKeysPerLoad per wave
     // (wave w: keys 32w .. 32w+31; a load's lane L lands in key L / kChunks, slot L % kChunks);
@@ -241,44 +260,73 @@ __global__ __launch_bounds__(512) void logits_mfma_kernel(SelectParams P, int ro
     load_tile(t0, t0 & 1);
 
     // ---- folded Q of this wave's rows (rows past the request repeat its last row): lane
-    // (l16, l4) holds dims 32 ks + 8 l4 .. +7 of row l16 for each k-step ks, as hi and lo bf16
-    // terms of f = sum_h q_h (float32, heads in order 0 .. Hi-1).
-    bf16x8_t qhi[4], qlo[4];
+    // (l16, l4) holds dims 32 ks + 8 l4 .. +7 of row l16 for each k-step ks, as the hi, mid and
+    // lo bf16 terms of f = sum_h q_h (float32, heads in order 0 .. Hi-1).
+    bf16x8_t qhi[4], qmid[4], qlo[4];
     {
       const int t = min(trow, nrows - 1);
       const char* qrow = qb + (int64_t)(q0 + rb * kMfmaRows + t) * P.Hi * kHeadDim * (F8 ? 1 : 2);
+      float f[4][8];  // +0 plus the heads in order (a zero's sign changes no score)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        float f[8];
-        for (int h = 0; h < P.Hi; ++h) {
-          float x[8];
-          if constexpr (F8) {
-            const uint2 u = *reinterpret_cast<const uint2*>(
-                qrow + (int64_t)(h * kHeadDim + 32 * ks + 8 * l4));
-            const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(u.x, false);
-            const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(u.x, true);
-            const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(u.y, false);
-            const auto d = __builtin_amdgcn_cvt_pk_f32_fp8(u.y, true);
-            x[0] = a[0]; x[1] = a[1]; x[2] = b[0]; x[3] = b[1];
-            x[4] = c[0]; x[5] = c[1]; x[6] = d[0]; x[7] = d[1];
-          } else {
-            const uint4 u = *reinterpret_cast<const uint4*>(
-                qrow + (int64_t)(h * kHeadDim + 32 * ks + 8 * l4) * 2);
-            const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              x[2 * e] = __uint_as_float(w4[e] << 16);
-              x[2 * e + 1] = __uint_as_float(w4[e] & 0xFFFF0000u);
+        for (int e = 0; e < 8; ++e) f[ks][e] = 0.0f;
+      }
+      // Four heads at a time: their loads for all four k-steps are in flight together.
+      for (int hb = 0; hb < P.Hi; hb += 4) {  // workgroup-uniform
+        uint4 raw[4][4];
+#pragma unroll
+        for (int hh = 0; hh < 4; ++hh) {
+          const int h = min(hb + hh, P.Hi - 1);
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            if constexpr (F8) {
+              const uint2 u = *reinterpret_cast<const uint2*>(
+                  qrow + (int64_t)(h * kHeadDim + 32 * ks + 8 * l4));
+              raw[hh][ks] = make_uint4(u.x, u.y, 0u, 0u);
+            } else {
+              raw[hh][ks] = *reinterpret_cast<const uint4*>(
+                  qrow + (int64_t)(h * kHeadDim + 32 * ks + 8 * l4) * 2);
             }
           }
-#pragma unroll
-          for (int e = 0; e < 8; ++e) f[e] = h == 0 ? x[e] : f[e] + x[e];
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const __bf16 hv = (__bf16)f[e];
+        for (int hh = 0; hh < 4; ++hh) {
+          const bool use = hb + hh < P.Hi;  // workgroup-uniform
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            float x[8];
+            if constexpr (F8) {
+              const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(raw[hh][ks].x, false);
+              const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(raw[hh][ks].x, true);
+              const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(raw[hh][ks].y, false);
+              const auto d = __builtin_amdgcn_cvt_pk_f32_fp8(raw[hh][ks].y, true);
+              x[0] = a[0]; x[1] = a[1]; x[2] = b[0]; x[3] = b[1];
+              x[4] = c[0]; x[5] = c[1]; x[6] = d[0]; x[7] = d[1];
+            } else {
+              const uint32_t w4[4] = {raw[hh][ks].x, raw[hh][ks].y, raw[hh][ks].z,
+                                      raw[hh][ks].w};
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                x[2 * e] = __uint_as_float(w4[e] << 16);
+                x[2 * e + 1] = __uint_as_float(w4[e] & 0xFFFF0000u);
+              }
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f[ks][e] = f[ks][e] + (use ? x[e] : 0.0f);
+          }
+        }
+      }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {  // each difference below is exact in float32
+          const __bf16 hv = (__bf16)f[ks][e];
+          const float r1 = f[ks][e] - (float)hv;
+          const __bf16 mv = (__bf16)r1;
           qhi[ks][e] = hv;
-          qlo[ks][e] = (__bf16)(f[e] - (float)hv);  // f - hi is exact in float32
+          qmid[ks][e] = mv;
+          qlo[ks][e] = (__bf16)(r1 - (float)mv);
         }
       }
     }
@@ -334,9 +382,11 @@ __global__ __launch_bounds__(512) void logits_mfma_kernel(SelectParams P, int ro
       read_kf(0, 0, kf[0]);
 #pragma unroll
       for (int kg0 = 0; kg0 < 16; kg0 += 4) {
-        f32x4_t acc[4];
+        // ah: the hi products of k-step ks (32 terms each); al: every mid and lo product.
+        f32x4_t ah[4][4], al[4];
+        const f32x4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[q] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int q = 0; q < 4; ++q) al[q] = zero;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
           frag_t(&cur)[4] = kf[ks & 1];
@@ -352,15 +402,20 @@ __global__ __launch_bounds__(512) void logits_mfma_kernel(SelectParams P, int ro
           for (int q = 0; q < 4; ++q) ka[q] = to_bf16(cur[q]);
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[q], qhi[ks], acc[q], 0, 0, 0);
+            ah[q][ks] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[q], qhi[ks], zero, 0, 0, 0);
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[q], qlo[ks], acc[q], 0, 0, 0);
+            al[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[q], qmid[ks], al[q], 0, 0, 0);
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            al[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[q], qlo[ks], al[q], 0, 0, 0);
         }
+        f32x4_t acc[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          acc[q] = ((ah[q][0] + ah[q][1]) + (ah[q][2] + ah[q][3])) + al[q];
         // Groups kg0 .. kg0+3 are final: element e of group kg is key 16kg + 4(lane/16) + e
-        // of row trow.  A group of 4 keys is written when its first key is visible to the row
-        // (the rest lies inside the row's stride, past its visible keys, where the top-k does
-        // not read); keys that were not loaded are written as zero.
+        // of row trow; keys that were not loaded are written as zero.
         uint32_t okm[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q)
@@ -370,6 +425,7 @@ __global__ __launch_bounds__(512) void logits_mfma_kernel(SelectParams P, int ro
         asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(okm[0]), "+v"(okm[1]), "+v"(okm[2]),
                      "+v"(okm[3]), "+v"(kf[0][0]), "+v"(kf[0][1]), "+v"(kf[0][2]),
                      "+v"(kf[0][3]));
+        typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           f32x4_t v = acc[q];
@@ -377,12 +433,28 @@ __global__ __launch_bounds__(512) void logits_mfma_kernel(SelectParams P, int ro
           for (int e = 0; e < 4; ++e) {
             if (!((okm[q] >> (8 * e)) & 0xFFu)) v[e] = 0.0f;
           }
-          const int j = kt * kMfmaKeys + 16 * (kg0 + q) + 4 * l4;
-          const uint32_t off =
-              j < vis_t ? (uint32_t)((trow - wlo) * P.col_stride * 4 + j * 2) : 0xFFFFFFF0u;
-          typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+          // Keys 16 q + 4 l4 .. +3 of row l16: bytes 32 q + 8 l4 of its 128-byte batch row.
           const u32x2_t pk = {bf16_pack_rne(v[0], v[1]), bf16_pack_rne(v[2], v[3])};
-          __builtin_amdgcn_raw_buffer_store_b64(pk, rs, off, 0, 0);
+          const uint32_t a = stg_base + l16 * 128 + 16 * ((2 * q + (l4 >> 1)) ^ (l16 & 7)) +
+                             8 * (l4 & 1);
+          asm volatile("ds_write_b64 %0, %1" ::"v"(a), "v"(pk) : "memory");
+        }
+        u32x4_t piece[2];
+#pragma unroll
+        for (int sr = 0; sr < 2; ++sr) {
+          const int r16 = (lane >> 3) + 8 * sr, c = lane & 7;
+          asm volatile("ds_read_b128 %0, %1"
+                       : "=v"(piece[sr])
+                       : "v"(stg_base + r16 * 128 + 16 * (c ^ (r16 & 7))));
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(piece[0]), "+v"(piece[1]));
+        // A row piece of 8 keys is written when its first key is visible to the row (the rest
+        // lies inside the row's stride, past its visible keys, where the top-k does not read).
+#pragma unroll
+        for (int sr = 0; sr < 2; ++sr) {
+          const int j = kt * kMfmaKeys + 16 * kg0 + 8 * (lane & 7);
+          const uint32_t off = j < vis_s[sr] ? (uint32_t)(roff_s[sr] + j * 2) : 0xFFFFFFF0u;
+          __builtin_amdgcn_raw_buffer_store_b128(piece[sr], rs, off, 0, 0);
           ++st;
         }
       }

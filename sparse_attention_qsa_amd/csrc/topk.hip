@@ -488,15 +488,18 @@ void topk_kernel(SelectParams P) {
   }
   // Bound of the head-folded float32 score (the VALU logits, and the second level below), and
   // of the matrix-core score: Q folded in float32 (heads in order), split into bf16 terms
-  // hi + lo with |f - hi - lo| <= 2^-16 |f| and |hi| + |lo| <= (1 + 2^-6) |f|, and 2 x 128
-  // exact products summed by the matrix cores in an unspecified order (u = 2^-23).
-  // (ReLU-sum scores come from the matrix cores: u = 2^-23, any order.)
+  // hi + mid + lo (residual <= 2^-24 |f|; |hi| <= (1 + 2^-8) |f|, |mid| + |lo| <= 2^-7 |f|);
+  // per k-step the 32 exact hi products summed by the matrix cores, all mid and lo products in
+  // one more sum (any order and rounding: u = 2^-23), and the five partial sums added on the
+  // vector unit (u = 2^-24).  (ReLU-sum scores come from the matrix cores: u = 2^-23.)
   const double gam_f = (double)(P.Hi + 130) * (P.relu ? 0x1p-23 : 0x1p-24);
   const double E_f = 2.0 * gam_f / (1.0 - gam_f) * kappa * A + 1e-30;
   const bool mfma_row = bf16_row;
-  const double g_fold = (double)(P.Hi - 1) * 0x1p-24 / (1.0 - (double)(P.Hi - 1) * 0x1p-24);
-  const double g_acc = (double)(2 * kHeadDim + 2) * 0x1p-23 / (1.0 - (double)(2 * kHeadDim + 2) * 0x1p-23);
-  const double gam_m = g_fold + (0x1p-16 + g_acc * (1.0 + 0x1p-6)) * (1.0 + g_fold);
+  auto gam = [](double n, double u) { return n * u / (1.0 - n * u); };
+  const double g_fold = gam(P.Hi - 1, 0x1p-24);
+  const double gam_m = g_fold + (0x1p-24 + gam(34, 0x1p-23) * (1.0 + 0x1p-7) +
+                                 gam(2 * kHeadDim + 2, 0x1p-23) * 0x1p-7 +
+                                 gam(4, 0x1p-24) * (1.0 + 0x1p-6)) * (1.0 + g_fold);
   const double Ebound = mfma_row ? 2.0 * gam_m * (1.0 + 0x1p-20) * kappa * A + 1e-30 : E_f;
   // Certainly kept above hi, certainly dropped below lo; float32 forms widen the band only.
   // A score b stands for canonical scores in [b - d(b), b + d(b)] with d(b) = Ebound (float32
@@ -551,7 +554,8 @@ void topk_kernel(SelectParams P) {
   const int groups = NT / 16;  // 16-lane groups: one band entry each at a time
   const int grp = tid >> 4, l16 = tid & 15;
 
-  if (mfma_row && need > 0) {
+  // The second level narrows the band only where its bound is the tighter one.
+  if (mfma_row && need > 0 && E_f < Ebound) {
     // ---- second level: the band's head-folded float32 scores (error <= E_f) select within
     // the band exactly as the first level selected within the row; the rest of the band goes
     // to the float64 re-scoring.
