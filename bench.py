@@ -61,6 +61,9 @@ def parse():
                    help="also run the main-attention prepare inside qsa_compress (the attention "
                         "then uses the prepared Q and reads the gate in place) and report its "
                         "marginal cost")
+    p.add_argument("--row-tiles", action="store_true",
+                   help="qsa_sparse_gqa's opt-in row-tiled prefill attention (32-row tiles of "
+                        "one request share each loaded K/V window)")
     p.add_argument("--graph", action="store_true",
                    help="also time the step captured in one HIP graph per input copy")
     p.add_argument("--profile-only", action="store_true",
@@ -385,6 +388,8 @@ def main():
     cap = int(args.max_logits_mb * 2**20)
     steps = [QsaStep(w, main=m, index_agg=args.index_agg, max_logits_bytes=cap)
              for w, m in zip(wls, mains)]
+    for st in steps:
+        st.g_args.row_tiles = 1 if args.row_tiles else 0
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
@@ -548,7 +553,7 @@ def main():
                    "page_size": int(wl0.kv_cache.shape[2]), "kv_dtype": getattr(wl0, "kv_dtype", "bf16"),
                    "input_copies_rotated": len(steps),
                    "main_prepare": bool(args.main_prepare), "index_agg": args.index_agg,
-                   "max_logits_mb": args.max_logits_mb,
+                   "max_logits_mb": args.max_logits_mb, "row_tiles": bool(args.row_tiles),
                    "topk_workspace_mb": round(steps[0].t_ws.numel() / 2**20, 1),
                    "gqa_splits": steps[0].num_splits},
         "hbm_gbps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),

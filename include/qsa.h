@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 6
+#define QSA_ABI_VERSION 7
 
 typedef enum qsa_status {
   QSA_OK = 0,
@@ -300,6 +300,12 @@ typedef struct qsa_gqa_args {
   qsa_dtype kv_dtype;               /* BF16 (0) or FP8_E4M3                                  */
   float k_scale;                    /* FP8_E4M3: K = code * k_scale; 0 -> 1; ignored for bf16 */
   float v_scale;                    /* FP8_E4M3: V = code * v_scale; 0 -> 1; ignored for bf16 */
+  int32_t row_tiles;                /* 1: row-tiled prefill attention where it applies (bf16
+                                       K/V, Hq = 8 Hkv, one split, T >= 2048): 32-row tiles of
+                                       one request share each loaded K/V window, every
+                                       (row, token) pair a row did not select masked; pays off
+                                       when nearby rows select overlapping tokens.  0: off.
+                                       Results equal the per-row path within rounding.      */
 } qsa_gqa_args;
 
 /* Splits the call will use (after the automatic choice and clamping). */

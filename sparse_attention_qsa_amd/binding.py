@@ -87,6 +87,7 @@ class GqaArgs(C.Structure):
         ("scale", C.c_float), ("num_splits", _I32),
         ("out", _P), ("out_row_stride", _I64), ("out_head_stride", _I64),
         ("kv_dtype", _I32), ("k_scale", C.c_float), ("v_scale", C.c_float),
+        ("row_tiles", _I32),
     ]
 
 
@@ -352,7 +353,7 @@ def qsa_index_logits_topk(workspace=None, stream=None, **kw) -> None:
 
 def gqa_args(*, q, kv_cache, block_table, token_to_req, packed, out, gate=None, scale=0.0,
              num_splits=0, num_requests=None, block_table_width=None, k_scale=1.0,
-             v_scale=1.0) -> GqaArgs:
+             v_scale=1.0, row_tiles=False) -> GqaArgs:
     """kv_cache: [pages, Hkv, P, 2*head_dim] bf16 (K then V per token row), or uint8 e4m3fn
     codes with K = code * k_scale and V = code * v_scale."""
     _need(q, torch.bfloat16, "q")
@@ -403,6 +404,7 @@ def gqa_args(*, q, kv_cache, block_table, token_to_req, packed, out, gate=None, 
     a.out = _ptr(out)
     a.out_row_stride = out.stride(0)
     a.out_head_stride = out.stride(1)
+    a.row_tiles = 1 if row_tiles else 0
     if kv_cache.dtype == torch.uint8:
         a.kv_dtype = 1
         a.k_scale = float(k_scale)

@@ -42,6 +42,9 @@ struct GqaParams {
   int64_t o_rs, o_hs;
   float* part_o;    // [splits, T, Hq, 128]
   float* part_lse;  // [splits, T, Hq]
+  // Row tiles (prefill): flags [Hkv, T / kRT], set to 1 for each (tile, KV head) whose outputs
+  // the row-tiled kernel wrote (the per-row kernel then skips those rows); NULL: none.
+  int32_t* rt_flags;
 };
 
 
@@ -61,6 +64,7 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kTile = 32;        // selected tokens per tile (one MFMA K step of P.V)
 constexpr int kChunkTiles = 8;   // tiles whose cache rows are resolved together
+constexpr int kRT = 32;          // rows per tile of the row-tiled (prefill) kernel
 
 __device__ __forceinline__ void lds_dma16(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
@@ -119,6 +123,10 @@ __global__ __launch_bounds__(64) void gqa_partial_kernel(GqaParams P) {
   const int split = (int)(wi % (uint32_t)P.splits);
   const uint32_t rk = wi / (uint32_t)P.splits;
   const int row = (int)(rk % (uint32_t)P.T), kvh = (int)(rk / (uint32_t)P.T);
+  if (P.rt_flags != nullptr) {  // rows the row-tiled kernel already wrote
+    const int ntiles = P.T / kRT;
+    if (row / kRT < ntiles && P.rt_flags[(int64_t)kvh * ntiles + row / kRT] != 0) return;
+  }
   const int lane = threadIdx.x, l16 = lane & 15, g4 = lane >> 4;
   __shared__ __attribute__((aligned(16))) uint8_t kt[kTile * kRow];
   __shared__ __attribute__((aligned(16))) uint8_t vt[kTile * kRow];
@@ -444,6 +452,350 @@ __global__ __launch_bounds__(64) void gqa_partial_kernel(GqaParams P) {
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Row-tiled attention for long prefill chunks (bf16 K/V, G = 8; opt-in: row_tiles = 1).
+// Workgroup (tile, KV head)
+// takes the kRT = 32 rows tile * 32 .. +31 when they all belong to one request.  Every row's
+// selection is a set of that request's tokens, and nearby rows together select most of them,
+// so instead of gathering each row's tokens on its own the workgroup walks the request's
+// 32-token windows that any of its rows selected, in ascending order, loads each window's K
+// and V once into LDS, and scores it against all 32 x 8 queries, each (row, token) pair the row
+// did not select masked out of the softmax.  A window is a contiguous run of tokens (whole
+// 16-token pages), so its K/V rows come in 8 KiB contiguous blocks.
+//   * Row masks: a bit per (row, token) over a span of kRTSpan tokens in LDS (64 KiB), built
+//     from the rows' packed entries (negative entries, entries past the count or the block
+//     table are left out, as in the per-row kernel); a row that lists a token twice would need
+//     it counted twice, so such a tile is left to the per-row kernel (flag 0).
+//   * Waves: wave w holds rows 4w .. 4w+3 as two MFMA column blocks (2 rows x 8 heads each),
+//     their Q^T fragments in registers; K fragments and (transposed) V fragments of a window are
+//     read once and serve both blocks.  Three window buffers keep two windows in flight.
+//   * Softmax per query as in the per-row kernel (base 2, P rounded to bf16).  V elements of
+//     tokens that no row selected (slots past the request, unwritten slots, pages outside the
+//     cache) are zeroed in the fragments: P is 0 there, but 0 x NaN would not be.
+// The flag [kvh][tile] says whether this kernel wrote the tile's outputs; the per-row kernel
+// runs after it and takes the rows of every tile it did not.
+constexpr int kRTSpan = 16384;               // tokens whose row masks are held at a time
+constexpr int kRTWords = kRTSpan / 32;
+constexpr int kRTBt = kRTSpan / 16 + 2;      // block-table entries of a span (pages >= 16)
+constexpr int kRTMinRows = 2048;             // calls with at least this many rows use it
+
+template <int G>
+__global__ __launch_bounds__(512) void gqa_rowtile_kernel(GqaParams P) {
+  static_assert(G == 8, "a column block is two rows of eight heads");
+  __shared__ uint32_t bits[kRT][kRTWords];                                  // 64 KiB
+  __shared__ __attribute__((aligned(16))) uint8_t kvt[3][2][kTile * 256];  // 48 KiB
+  __shared__ int32_t bt_s[kRTBt];
+  __shared__ __attribute__((aligned(4))) uint16_t wlist[kRTWords];  // active windows, ascending
+  __shared__ uint32_t wany[kRTWords];     // per active window: tokens some row selected
+  __shared__ int s_cnt[kRT];
+  __shared__ int s_int[8];
+  __shared__ int s_wsum[8];
+
+  const int tile = blockIdx.x, kvh = blockIdx.y;
+  const int ntiles = P.T / kRT;
+  const int row0 = tile * kRT;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, g4 = lane >> 4;
+  int32_t* flag = P.rt_flags + (int64_t)kvh * ntiles + tile;
+
+  // ---- the tile's request (all 32 rows must share it) and the rows' counts
+  if (tid < kRT) {
+    const int row = row0 + tid;
+    s_cnt[tid] = min(max(P.packed[(int64_t)row * P.p_rs + P.W], 0), P.W);
+    if (tid == 0) s_int[0] = P.t2r[row];
+  }
+  __syncthreads();
+  {
+    const int r0 = s_int[0];
+    int bad = 0;
+    if (tid < kRT) bad = (P.t2r[row0 + tid] != r0) || r0 < 0 || r0 >= P.R;
+    if (__syncthreads_or(bad)) {
+      if (tid == 0) *flag = 0;
+      return;
+    }
+  }
+  const int r = s_int[0];
+  const int32_t* btr = P.bt + (int64_t)r * P.bt_stride;
+  const int64_t tok_lim = (int64_t)P.bt_width * P.P;  // entries at or past this are masked
+  const char* kvb = reinterpret_cast<const char*>(P.kv);
+
+  // ---- Q^T fragments of the wave's two column blocks: column l16 is row 4w + 2i + l16/8,
+  // head kvh * 8 + l16 % 8; dims 32 ks + 8 g4 .. +7.
+  bf16x8_t qfr[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = row0 + 4 * w + 2 * i + (l16 >> 3);
+    const uint4* qrow = reinterpret_cast<const uint4*>(
+        P.q + (int64_t)row * P.q_rs + (int64_t)(kvh * G + (l16 & 7)) * P.q_hs);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qfr[i][ks] = __builtin_bit_cast(bf16x8_t, qrow[4 * ks + g4]);
+  }
+  float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.0f, 0.0f};
+  f32x4_t acc[2][8];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int db = 0; db < 8; ++db) acc[i][db] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // The row of this thread's entry scan: 16 threads per row.
+  const int srow = tid >> 4, ssub = tid & 15;
+  const int32_t* sent = P.packed + (int64_t)(row0 + srow) * P.p_rs;
+  const int scnt = s_cnt[srow];
+
+  for (int64_t s0 = 0;; s0 += kRTSpan) {
+    // ---- row masks of span [s0, s0 + kRTSpan): clear, then set a bit per entry
+    for (int i = tid; i < kRT * kRTWords; i += 512) (&bits[0][0])[i] = 0u;
+    if (tid == 0) { s_int[1] = 0; s_int[2] = 0; s_int[3] = 0; }
+    __syncthreads();
+    int more = 0, dup = 0;
+    for (int e0 = 0; e0 < scnt; e0 += 128) {  // eight entries per thread in flight
+      int x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int e = e0 + ssub + 16 * j;
+        x[j] = e < scnt ? sent[e] : -1;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (x[j] < 0 || (int64_t)x[j] >= tok_lim || (int64_t)x[j] < s0) continue;
+        if ((int64_t)x[j] >= s0 + kRTSpan) { more = 1; continue; }
+        const int o = (int)((int64_t)x[j] - s0);
+        const uint32_t bit = 1u << (o & 31);
+        const uint32_t old = atomicOr(&bits[srow][o >> 5], bit);
+        dup |= (old & bit) != 0u;
+      }
+    }
+    if (more) s_int[2] = 1;
+    if (dup) s_int[3] = 1;
+    __syncthreads();
+    if (s_int[3]) {  // a row lists a token twice: leave the tile to the per-row kernel
+      if (tid == 0) *flag = 0;
+      return;
+    }
+    const bool more_spans = s_int[2] != 0;
+    // ---- active windows (ascending, by a workgroup scan) and the span's block-table slice
+    {
+      const int wi = tid;  // kRTWords == 512 words: one per thread
+      uint32_t any = 0u;
+#pragma unroll 8
+      for (int rr = 0; rr < kRT; ++rr) any |= bits[rr][wi];
+      const int act = any != 0u;
+      const uint64_t bal = __ballot(act);
+      const int before = __builtin_popcountll(bal & ((1ull << lane) - 1ull));
+      if (lane == 0) s_wsum[w] = __builtin_popcountll(bal);
+      __syncthreads();
+      int off = before;
+      for (int i = 0; i < w; ++i) off += s_wsum[i];
+      if (act) {
+        wlist[off] = (uint16_t)wi;
+        wany[off] = any;
+      }
+      if (tid == 511) s_int[4] = off + act;
+    }
+    const int col0 = (int)(s0 / P.P);
+    for (int c = tid; c < kRTBt; c += 512) {
+      const int col = col0 + c;
+      bt_s[c] = col < P.bt_width ? btr[col] : -1;
+    }
+    __syncthreads();
+    const int nwin = s_int[4];
+
+    // Loads of window list entry k into buffer k % 3: wave w fetches tokens 4w .. 4w+3 (K,
+    // then V), 16 lanes per 256-byte row, chunk c into slot c ^ (t & 15).  A token whose page is
+    // not in the cache loads the cache's first row (masked below).
+    // LDS words read with inline assembly inside the window loop: a plain read would make the
+    // compiler wait for every LDS-direct load in flight (two windows' worth).
+    auto lds_word = [](const void* p) {
+      uint32_t v;
+      asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_u32(p))
+                   : "memory");
+      return v;
+    };
+    auto win_of = [&](int k) {
+      const uint32_t v = lds_word(&wlist[k & ~1]);  // two 16-bit entries per word
+      return (int)((k & 1) ? (v >> 16) : (v & 0xFFFFu));
+    };
+    auto issue = [&](int k) {
+      const int t = 4 * w + g4;
+      const int64_t tok = s0 + (int64_t)win_of(k) * 32 + t;
+      const int c = (int)(tok / P.P) - col0;
+      const int page = (int)lds_word(&bt_s[c]);
+      const bool ok = tok < tok_lim && page >= 0 && page < P.pages;
+      const int64_t off = ok ? ((int64_t)page * P.kv_ps + (int64_t)kvh * P.kv_hs +
+                                (int64_t)(tok - (int64_t)(tok / P.P) * P.P) * P.kv_ts) : 0;
+      uint8_t* dst = kvt[k % 3][0] + 1024 * w;
+      const char* src = kvb + off + 16 * (l16 ^ (t & 15));
+      lds_dma16(src, dst);
+      lds_dma16(src + 256, dst + kTile * 256);
+    };
+    if (nwin > 0) issue(0);
+    if (nwin > 1) issue(1);
+    for (int k = 0; k < nwin; ++k) {
+      // Window k's two loads have landed once only window k+1's may be in flight.
+      if (k + 1 < nwin) __builtin_amdgcn_s_waitcnt(0x0F72);  // vmcnt(2)
+      else __builtin_amdgcn_s_waitcnt(0x0F70);                // vmcnt(0)
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();  // window k visible; window k-1's buffer is free
+      asm volatile("" ::: "memory");
+      if (k + 2 < nwin) issue(k + 2);
+      const uint8_t* kt = kvt[k % 3][0];
+      const uint8_t* vt = kvt[k % 3][1];
+      const int wi = win_of(k);
+      // Tokens of the window with a page in the cache (lane l < 32: token l), and the row masks
+      // of this lane's two query columns.
+      uint32_t valid;
+      {
+        const int64_t tok = s0 + (int64_t)wi * 32 + (lane & 31);
+        const int page = (int)lds_word(&bt_s[(int)(tok / P.P) - col0]);
+        valid = (uint32_t)__ballot(tok < tok_lim && page >= 0 && page < P.pages);
+      }
+      uint32_t rm[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) rm[i] = lds_word(&bits[4 * w + 2 * i + (l16 >> 3)][wi]) & valid;
+      const uint32_t anyv = lds_word(&wany[k]) & valid;
+
+      // ---- fragments: K (token blocks bb = 0, 1 of 16, k-steps ks) and, read behind them,
+      // V^T through the transposing read (lane (g4, l16) receives dim 16 db + l16 of tokens
+      // 4 g4 + j, then 16 + 4 g4 + j, j < 4).
+      bf16x8_t kf[2][4];
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb) {
+        const int t = 16 * bb + l16;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          asm volatile("ds_read_b128 %0, %1" : "=v"(kf[bb][ks])
+                       : "v"(lds_u32(kt + t * 256 + 16 * ((4 * ks + g4) ^ (t & 15)))));
+      }
+      i16x4_t vlo[8], vhi[8];
+      {
+        const int tr_t0 = 4 * g4 + (l16 >> 2), tr_t1 = tr_t0 + 16, q4 = l16 & 3;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+          const int cc = 2 * db + (q4 >> 1), h8 = 8 * (q4 & 1);
+          asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(vlo[db])
+                       : "v"(lds_u32(vt + tr_t0 * 256 + 16 * (cc ^ (tr_t0 & 15)) + h8)));
+          asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(vhi[db])
+                       : "v"(lds_u32(vt + tr_t1 * 256 + 16 * (cc ^ (tr_t1 & 15)) + h8)));
+        }
+      }
+      // The K fragments first (the V reads, issued later, complete in order behind them).
+      asm volatile("s_waitcnt lgkmcnt(8)" : "+v"(kf[0][0]), "+v"(kf[0][1]), "+v"(kf[0][2]),
+                   "+v"(kf[0][3]), "+v"(kf[1][0]), "+v"(kf[1][1]), "+v"(kf[1][2]),
+                   "+v"(kf[1][3]));
+
+      // ---- S^T = K . Q^T for both column blocks
+      f32x4_t sacc[2][2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb) {
+          sacc[i][bb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks)
+            sacc[i][bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[bb][ks], qfr[i][ks],
+                                                                   sacc[i][bb], 0, 0, 0);
+        }
+      // ---- online softmax per query column; P rounded to bf16
+      bf16x8_t pfr[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        float z[8];
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int t = 16 * bb + 4 * g4 + e;
+            z[4 * bb + e] = ((rm[i] >> t) & 1u) ? sacc[i][bb][e] * P.scale_log2 : -INFINITY;
+          }
+        float tmax = z[0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) tmax = fmaxf(tmax, z[j]);
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+        const float mn = fmaxf(m[i], tmax);
+        float alpha = 1.0f, psum = 0.0f;
+        if (mn != -INFINITY) {
+          alpha = __builtin_amdgcn_exp2f(m[i] - mn);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            pfr[i][j] = (__bf16)__builtin_amdgcn_exp2f(z[j] - mn);
+            psum += (float)pfr[i][j];
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) pfr[i][j] = (__bf16)0.0f;
+        }
+        m[i] = mn;
+        lsum[i] = lsum[i] * alpha + psum;
+        if (__ballot(alpha != 1.0f) != 0ull) {
+#pragma unroll
+          for (int db = 0; db < 8; ++db) acc[i][db] *= alpha;
+        }
+      }
+      // ---- O^T += V^T . P^T for both blocks; V elements of unselected tokens zeroed.  Lane
+      // (g4, l16) receives dim 16 db + l16 of tokens 4 g4 + j (lo) and 16 + 4 g4 + j (hi).
+      const uint32_t zlo = anyv >> (4 * g4), zhi = anyv >> (16 + 4 * g4);
+      const uint32_t mlo0 = ((zlo & 1u) ? 0xFFFFu : 0u) | ((zlo & 2u) ? 0xFFFF0000u : 0u);
+      const uint32_t mlo1 = ((zlo & 4u) ? 0xFFFFu : 0u) | ((zlo & 8u) ? 0xFFFF0000u : 0u);
+      const uint32_t mhi0 = ((zhi & 1u) ? 0xFFFFu : 0u) | ((zhi & 2u) ? 0xFFFF0000u : 0u);
+      const uint32_t mhi1 = ((zhi & 4u) ? 0xFFFFu : 0u) | ((zhi & 8u) ? 0xFFFF0000u : 0u);
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(vlo[0]), "+v"(vlo[1]), "+v"(vlo[2]),
+                   "+v"(vlo[3]), "+v"(vlo[4]), "+v"(vlo[5]), "+v"(vlo[6]), "+v"(vlo[7]),
+                   "+v"(vhi[0]), "+v"(vhi[1]), "+v"(vhi[2]), "+v"(vhi[3]), "+v"(vhi[4]),
+                   "+v"(vhi[5]), "+v"(vhi[6]), "+v"(vhi[7]));
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        typedef uint32_t u32x4v_t __attribute__((ext_vector_type(4)));
+        u32x4v_t u = __builtin_bit_cast(
+            u32x4v_t, __builtin_shufflevector(vlo[db], vhi[db], 0, 1, 2, 3, 4, 5, 6, 7));
+        u[0] &= mlo0;
+        u[1] &= mlo1;
+        u[2] &= mhi0;
+        u[3] &= mhi1;
+        const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, u);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          acc[i][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pfr[i], acc[i][db], 0, 0, 0);
+      }
+    }
+    if (!more_spans) break;
+    __syncthreads();  // every wave is done with the span's masks and windows
+  }
+
+  // ---- epilogue: lane (g4, l16) of block i holds dims 16 db + 4 g4 + e of row
+  // 4w + 2i + l16 / 8, head l16 % 8.
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const float ltot = lsum[i] + __shfl_xor(lsum[i], 16, kWave) +
+                       __shfl_xor(lsum[i], 32, kWave) +
+                       __shfl_xor(__shfl_xor(lsum[i], 16, kWave), 32, kWave);
+    const int row = row0 + 4 * w + 2 * i + (l16 >> 3);
+    const int hq = kvh * G + (l16 & 7);
+    const float inv = ltot > 0.0f ? P.v_scale / ltot : 0.0f;
+    const uint32_t* gp = P.gate ? reinterpret_cast<const uint32_t*>(
+                                      P.gate + (int64_t)row * P.g_rs + (int64_t)hq * P.g_hs)
+                                : nullptr;
+    uint32_t* op =
+        reinterpret_cast<uint32_t*>(P.out + (int64_t)row * P.o_rs + (int64_t)hq * P.o_hs);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      float o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = acc[i][db][e] * inv;
+      const int d0 = 16 * db + 4 * g4;
+      if (gp) {
+        const uint32_t g01 = gp[d0 / 2], g23 = gp[d0 / 2 + 1];
+        o[0] *= sigmoidf(bf16lo(g01));
+        o[1] *= sigmoidf(bf16hi(g01));
+        o[2] *= sigmoidf(bf16lo(g23));
+        o[3] *= sigmoidf(bf16hi(g23));
+      }
+      op[d0 / 2] = (f32_to_bf16(o[0]) & 0xFFFFu) | (f32_to_bf16(o[1]) << 16);
+      op[d0 / 2 + 1] = (f32_to_bf16(o[2]) & 0xFFFFu) | (f32_to_bf16(o[3]) << 16);
+    }
+  }
+  if (tid == 0) *flag = 1;
+}
+
 // Grid (T, Hq), one wavefront.  Lane s reads split s's log-sum-exp while every lane already
 // loads dims 2l, 2l+1 of all splits' partials (one round trip for both); the weights are formed
 // in-wave, then the partials are combined.  splits <= kMergeMax.
@@ -553,6 +905,15 @@ GqaPlan gqa_plan(const qsa_gqa_args& a) {
     const size_t n = (size_t)p.splits * a.num_tokens * a.num_q_heads;
     p.ws_bytes = (n * kHeadDim * sizeof(float) + 255) / 256 * 256 + n * sizeof(float);
   }
+  // Row tiles for large prefill calls (bf16 K/V, eight query heads per KV head, one split):
+  // a flag per (KV head, tile) after everything else.
+  p.row_tiles = 0;
+  if (a.row_tiles == 1 && a.kv_dtype == QSA_DTYPE_BF16 && a.num_q_heads == 8 * a.num_kv_heads &&
+      p.splits == 1 && a.num_tokens >= kRTMinRows) {
+    p.row_tiles = a.num_tokens / kRT;
+    p.ws_bytes = (p.ws_bytes + 255) / 256 * 256 +
+                 (size_t)p.row_tiles * a.num_kv_heads * sizeof(int32_t);
+  }
   return p;
 }
 
@@ -594,16 +955,25 @@ hipError_t launch_gqa(const qsa_gqa_args& a, const GqaPlan& plan, char* ws, hipS
   P.out = a.out;
   P.o_rs = a.out_row_stride;
   P.o_hs = a.out_head_stride;
+  size_t used = 0;
   if (plan.splits > 1) {
     const size_t n = (size_t)plan.splits * a.num_tokens * a.num_q_heads;
     P.part_o = reinterpret_cast<float*>(ws);
     P.part_lse = reinterpret_cast<float*>(ws + (n * kHeadDim * sizeof(float) + 255) / 256 * 256);
+    used = (n * kHeadDim * sizeof(float) + 255) / 256 * 256 + n * sizeof(float);
   }
+  P.rt_flags = plan.row_tiles > 0
+                   ? reinterpret_cast<int32_t*>(ws + (used + 255) / 256 * 256)
+                   : nullptr;
   hipError_t e = hipSuccess;
   if (phase == Phase::kSecond) {  // the merge alone (nothing to merge with one split)
     if (plan.splits == 1) return hipSuccess;
     hipLaunchKernelGGL(gqa_merge_kernel, dim3(P.T, P.Hq), dim3(64), 0, s, P);
     return hipGetLastError();
+  }
+  if (plan.row_tiles > 0) {  // every flag is written: 1 where the tile's outputs are done
+    hipLaunchKernelGGL(gqa_rowtile_kernel<8>, dim3(plan.row_tiles, P.Hkv), dim3(512), 0, s, P);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   switch (a.num_q_heads / a.num_kv_heads) {
     case 1: e = launch_partial<1>(P, f8, s); break;

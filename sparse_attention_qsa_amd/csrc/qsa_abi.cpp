@@ -166,6 +166,7 @@ qsa_status validate_gqa(const qsa_gqa_args* a) {
                   aligned(a->packed, 4),
               kInval);
   QSA_REQUIRE(a->num_kv_heads <= 65535 && a->scale >= 0.0f, kInval);
+  QSA_REQUIRE(a->row_tiles == 0 || a->row_tiles == 1, kInval);
   return QSA_OK;
 }
 

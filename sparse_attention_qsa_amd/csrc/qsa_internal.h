@@ -45,7 +45,8 @@ struct GqaPlan {
   int32_t tiles;        // ceil(W / 32)
   int32_t splits;       // workgroups per (row, KV head)
   int32_t tiles_per_split;
-  size_t ws_bytes;      // partial outputs + lse when splits > 1
+  size_t ws_bytes;      // partial outputs + lse when splits > 1, row-tile flags
+  int32_t row_tiles;    // tiles of the row-tiled prefill kernel (0: not used)
 };
 
 GqaPlan gqa_plan(const qsa_gqa_args& a);

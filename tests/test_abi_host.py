@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(B.EXPORTED)
-    assert lib.qsa_abi_version() == 6
+    assert lib.qsa_abi_version() == 7
     assert lib.qsa_status_string(3) == b"QSA_ERR_WORKSPACE_TOO_SMALL"
 
 

@@ -551,3 +551,43 @@ def test_step_captured_in_a_graph_replays_the_eager_results(name):
         torch.cuda.synchronize()
         assert torch.equal(st.packed, ref_packed)
     del g
+
+
+def test_row_tiled_prefill_attention_every_row_and_adversarial_entries():
+    """With row_tiles set, calls of 2048+ rows with 8 query heads per KV head take the
+    row-tiled kernel for every 32-row tile of one request (the tile that straddles the two requests, and the rows past the
+    last full tile, go to the per-row kernel).  Every row is compared with the oracle, with the
+    top-k's selection and then with rows holding a duplicated entry (its tile falls back to the
+    per-row kernel, which counts the token twice as the oracle does), negative entries and
+    entries past the block table."""
+    wl = workload("chunked_prefill", num_requests=2, rows=1100, lengths=("fixed", 3300))
+    assert wl.num_tokens >= 2048
+    log(f"row-tiled attention: T={wl.num_tokens}")
+    ref = oracle_step(wl)
+    st = run_gpu(wl)
+    assert np.array_equal(to_np(st.packed), ref.packed)
+    per_row = gpu_out_f64(st)
+    st.g_args.row_tiles = 1
+    st.gqa()
+    torch.cuda.synchronize()
+    err = max_abs(gpu_out_f64(st), ref.out)
+    log(f"  max-abs (selection) {err:.3e}; against the per-row path {max_abs(gpu_out_f64(st), per_row):.3e}")
+    assert max_abs(gpu_out_f64(st), per_row) <= 2 ** -6
+    assert err <= TOL["bf16"]
+    W = wl.output_width
+    adv = ref.packed.copy()
+    r_dup, r_neg, r_big = 5, 40, 1500
+    c = adv[r_dup, W]
+    adv[r_dup, c] = adv[r_dup, 7]            # token listed twice
+    adv[r_dup, W] = c + 1
+    adv[r_neg, 3] = -1
+    adv[r_neg, 10] = -77
+    adv[r_big, 0] = 10 ** 7                  # past the block table
+    st.packed.copy_(torch.from_numpy(adv).cuda())
+    st.gqa()
+    torch.cuda.synchronize()
+    want = oq.sparse_gqa(to_np(wl.q), to_np(wl.kv_cache), to_np(wl.block_table),
+                         to_np(wl.token_to_req), adv, gate=to_np(wl.gate))
+    err = max_abs(gpu_out_f64(st), want)
+    log(f"  max-abs (adversarial entries) {err:.3e}")
+    assert err <= TOL["bf16"]
