@@ -133,16 +133,17 @@ def algorithmic_bytes(wl, packed):
 
 
 def mfma_logits_flop(wl, index_agg):
-    """Causal-visible indexer logits FLOP of the requests the matrix-core kernel scores: every
-    (row, visible block) pair costs 2 * Hi * 128 (the per-head contraction it executes)."""
+    """Causal-visible indexer logits of the requests the matrix-core kernel scores, as
+    (executed, per_head) FLOP: the kernel folds the heads into Q and runs one contraction of 3 x
+    128 (three bf16 terms of the folded Q) per (row, visible block), 2 * 384 FLOP; the per-head
+    form (one contraction of 128 per head) would be 2 * Hi * 128."""
     if index_agg != "sum" or wl.index_heads > 16:
-        return 0
-    c, flop = wl.compress_ratio, 0
+        return 0, 0
+    c, pairs = wl.compress_ratio, 0
     for L, n in zip(wl.seq_lens_host.tolist(), wl.rows_host.tolist()):
         if n > MFMA_MIN_ROWS and n <= L:
-            p = range(L - n, L)
-            flop += sum((x + 1) // c for x in p) * 2 * wl.index_heads * 128
-    return int(flop)
+            pairs += sum((x + 1) // c for x in range(L - n, L))
+    return int(pairs * 2 * 3 * 128), int(pairs * 2 * wl.index_heads * 128)
 
 
 def traffic_record(kernel, workload):
@@ -311,15 +312,21 @@ def cpu_baseline(host_inputs, wl_meta, agg="sum", min_seconds=10.0, pool=None):
 
 
 def measured_ceilings():
-    """Practical HBM ceilings on this device, measured with torch: a 1 GiB device copy (read +
-    write) and a gather of 2 KiB rows at random positions of a 1 GiB table (the access of the
-    attention's K/V gather: 4 consecutive tokens x 512 B), each cold (a fresh 1 GiB buffer is
-    written in between so the Infinity Cache holds nothing useful)."""
+    """Practical HBM read ceilings on this device, measured with the library's own probe
+    (qsa_diag_read_bandwidth) on 2 GiB, cold (a fresh 1 GiB buffer is written in between, so
+    the Infinity Cache holds nothing useful): a streaming read in 4 KiB chunks (the compressed
+    keys' page-sized runs), and a gather of 2 KiB chunks at random positions (a selected block's
+    4 tokens x 512 B of K/V), plus a device copy for reference."""
     import torch
-    n = 2**30
+
+    from sparse_attention_qsa_amd import binding as B
+    n = 2 * 2**30
     a = torch.empty(n // 2, dtype=torch.bfloat16, device="cuda:0").normal_()
-    b = torch.empty_like(a)
-    flush = torch.empty(n // 4, dtype=torch.float32, device="cuda:0")
+    b = torch.empty(n // 4, dtype=torch.bfloat16, device="cuda:0")
+    flush = torch.empty(2**30 // 4, dtype=torch.float32, device="cuda:0")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    idx = torch.randint(0, n // 2048, (n // 2048 // 4,), dtype=torch.int32, device="cuda:0")
+    stream = torch.cuda.current_stream()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
 
     def timed(fn):
@@ -327,22 +334,21 @@ def measured_ceilings():
         for _ in range(5):
             flush.fill_(1.0)
             torch.cuda.synchronize()
-            ev[0].record()
+            ev[0].record(stream)
             fn()
-            ev[1].record()
+            ev[1].record(stream)
             torch.cuda.synchronize()
             t = ev[0].elapsed_time(ev[1]) * 1e-3
             best = t if best is None else min(best, t)
         return best
-    t_copy = timed(lambda: b.copy_(a))
-    rows = a.view(-1, 1024)                       # 2 KiB rows
-    idx = torch.randint(0, rows.shape[0], (rows.shape[0] // 8,), device="cuda:0")
-    out = torch.empty((idx.numel(), 1024), dtype=torch.bfloat16, device="cuda:0")
-    t_gather = timed(lambda: torch.index_select(rows, 0, idx, out=out))
-    gbytes = idx.numel() * 2048 * 2               # rows read + written
-    res = {"copy_gbps": round(2 * n / t_copy / 1e9, 1),
-           "gather_2k_gbps": round(gbytes / t_gather / 1e9, 1)}
-    del a, b, flush, rows, out
+    t_read = timed(lambda: B.qsa_diag_read_bandwidth(a, 4096, sink, stream=stream))
+    t_gather = timed(lambda: B.qsa_diag_read_bandwidth(a, 2048, sink, chunk_index=idx,
+                                                       stream=stream))
+    t_copy = timed(lambda: b.copy_(a[:n // 4]))
+    res = {"stream_read_gbps": round(n / t_read / 1e9, 1),
+           "gather_2k_gbps": round(idx.numel() * 2048 / t_gather / 1e9, 1),
+           "copy_gbps": round(2 * (n // 2) / t_copy / 1e9, 1)}
+    del a, b, flush, idx
     torch.cuda.empty_cache()
     return res
 
@@ -518,7 +524,7 @@ def main():
         del plain
 
     alg, alg_k, kv_tokens = algorithmic_bytes(wl0, steps[0].packed)
-    mfma_flop = mfma_logits_flop(wl0, args.index_agg)
+    mfma_flop, mfma_flop_per_head = mfma_logits_flop(wl0, args.index_agg)
     if mfma_flop:
         # The logits call also launches the matrix-core kernel: name the entry for both (the
         # roofline of the pair is reported against the matrix cores in mfma_logits below).
@@ -560,8 +566,8 @@ def main():
         "hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "step_us": step_dist,
         "measured_ceilings": ceilings,
-        "hbm_frac_of_copy_ceiling": round(step_bytes / (ms_step * 1e-3) / 1e9
-                                          / ceilings["copy_gbps"], 4),
+        "hbm_frac_of_read_ceiling": round(step_bytes / (ms_step * 1e-3) / 1e9
+                                          / ceilings["stream_read_gbps"], 4),
         "step_algorithmic_bytes": int(step_bytes),
         "per_call_us": {k: round(v, 2) for k, v in per_call.items()},
         "per_call_algorithmic_bytes": {k: int(v) for k, v in alg.items()},
@@ -578,13 +584,18 @@ def main():
         # the rate is a lower bound of the matrix-core kernel's own.
         us = per_kernel["logits_valu_kernel+logits_mfma_kernel"]
         tf = mfma_flop / (us * 1e-6) / 1e12
-        peak = MFMA_PEAK_TFLOPS[wl0.index_dtype]
-        out["mfma_logits"] = {"bound": "mfma", "dtype": wl0.index_dtype,
+        peak = MFMA_PEAK_TFLOPS["bf16"]      # both indexer dtypes run bf16 contractions
+        tf_h = mfma_flop_per_head / (us * 1e-6) / 1e12
+        out["mfma_logits"] = {"bound": "mfma", "dtype": "bf16",
                               "kernels": ["logits_valu_kernel (max |k| pass)",
                                           "logits_mfma_kernel"],
                               "us": round(us, 2), "flop": mfma_flop,
                               "achieved": round(tf, 1), "peak": peak,
-                              "unit": "TFLOP/s", "frac": round(tf / peak, 4)}
+                              "unit": "TFLOP/s", "frac": round(tf / peak, 4),
+                              "per_head_equivalent": {
+                                  "flop": mfma_flop_per_head,
+                                  "floor_us_at_peak": round(mfma_flop_per_head / peak / 1e6, 2),
+                                  "tflops": round(tf_h, 1), "frac": round(tf_h / peak, 4)}}
     if main_leg is not None:
         out["main_prepare"] = main_leg
     if graph_leg is not None:

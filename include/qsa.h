@@ -357,6 +357,16 @@ size_t qsa_sparse_gqa_noalloc_scratch_bytes(void);
 qsa_status qsa_diag_e4m3_decode(float* out, void* stream);
 qsa_status qsa_diag_fp64_sqrt_div(const double* in, double* out, int64_t n, void* stream);
 
+/* qsa_diag_read_bandwidth: a read-bandwidth probe with the access patterns of the path's HBM
+ * kernels, for measuring practical ceilings.  Reads n_chunks chunks of chunk_bytes (1024, 2048,
+ * 3072 or 4096) from src (device, 16-byte aligned): chunk i at i * chunk_bytes (a streaming read)
+ * or, with chunk_index (device int32 [n_chunks]) not NULL, at chunk_index[i] * chunk_bytes (a
+ * gather; the caller keeps every chunk inside its buffer).  16 bytes per lane, eight chunks per
+ * wavefront in flight; the XOR of everything read is folded into *sink (device) so that no load
+ * is dead.  Writes nothing else. */
+qsa_status qsa_diag_read_bandwidth(const void* src, const int32_t* chunk_index, int64_t n_chunks,
+                                   int32_t chunk_bytes, uint32_t* sink, void* stream);
+
 /* ------------------------------------------------------------------------------------------ */
 const char* qsa_status_string(qsa_status status);
 int32_t qsa_abi_version(void);

@@ -24,7 +24,8 @@ EXPORTED = (
     "qsa_sparse_gqa", "qsa_sparse_gqa_workspace_size", "qsa_sparse_gqa_num_splits",
     "qsa_sparse_gqa_partial", "qsa_sparse_gqa_merge",
     "qsa_sparse_gqa_noalloc", "qsa_sparse_gqa_noalloc_scratch_bytes",
-    "qsa_diag_e4m3_decode", "qsa_diag_fp64_sqrt_div", "qsa_status_string", "qsa_abi_version",
+    "qsa_diag_e4m3_decode", "qsa_diag_fp64_sqrt_div", "qsa_diag_read_bandwidth",
+    "qsa_status_string", "qsa_abi_version",
 )
 
 _P = C.c_void_p
@@ -124,6 +125,8 @@ def lib() -> C.CDLL:
         h.qsa_diag_e4m3_decode.restype = C.c_int
         h.qsa_diag_fp64_sqrt_div.argtypes = [_P, _P, _I64, _P]
         h.qsa_diag_fp64_sqrt_div.restype = C.c_int
+        h.qsa_diag_read_bandwidth.argtypes = [_P, _P, _I64, _I32, _P, _P]
+        h.qsa_diag_read_bandwidth.restype = C.c_int
         h.qsa_status_string.argtypes = [C.c_int]
         h.qsa_status_string.restype = C.c_char_p
         h.qsa_abi_version.argtypes = []
@@ -454,3 +457,17 @@ def qsa_diag_fp64_sqrt_div(x: torch.Tensor) -> torch.Tensor:
     _check(lib().qsa_diag_fp64_sqrt_div(_ptr(x), _ptr(out), x.numel(), _stream(None)),
            "qsa_diag_fp64_sqrt_div")
     return out
+
+
+def qsa_diag_read_bandwidth(src: torch.Tensor, chunk_bytes: int, sink: torch.Tensor,
+                            chunk_index: torch.Tensor | None = None, stream=None) -> None:
+    """Read-bandwidth probe over `src` (a streaming read of every chunk, or a gather of the
+    chunks listed in `chunk_index`); see qsa.h."""
+    _need(sink, torch.int32, "sink")
+    if chunk_index is not None:
+        _need(chunk_index, torch.int32, "chunk_index")
+        n = chunk_index.numel()
+    else:
+        n = src.numel() * src.element_size() // int(chunk_bytes)
+    _check(lib().qsa_diag_read_bandwidth(_ptr(src), _ptr(chunk_index), n, int(chunk_bytes),
+                                         _ptr(sink), _stream(stream)), "qsa_diag_read_bandwidth")

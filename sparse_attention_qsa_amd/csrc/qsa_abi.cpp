@@ -286,6 +286,16 @@ qsa_status qsa_diag_e4m3_decode(float* out, void* stream) {
   return from_hip(qsa::launch_diag_e4m3(out, reinterpret_cast<hipStream_t>(stream)));
 }
 
+qsa_status qsa_diag_read_bandwidth(const void* src, const int32_t* chunk_index, int64_t n_chunks,
+                                   int32_t chunk_bytes, uint32_t* sink, void* stream) {
+  if (src == nullptr || sink == nullptr || n_chunks < 0 || !aligned(src, 16) ||
+      !aligned(sink, 4) || chunk_bytes < 1024 || chunk_bytes > 4096 || chunk_bytes % 1024 != 0)
+    return kInval;
+  if (n_chunks == 0) return QSA_OK;
+  return from_hip(qsa::launch_diag_read(src, chunk_index, n_chunks, chunk_bytes, sink,
+                                        reinterpret_cast<hipStream_t>(stream)));
+}
+
 qsa_status qsa_diag_fp64_sqrt_div(const double* in, double* out, int64_t n, void* stream) {
   if (in == nullptr || out == nullptr || n < 0 || !aligned(in, 8) || !aligned(out, 8))
     return kInval;

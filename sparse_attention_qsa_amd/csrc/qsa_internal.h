@@ -66,6 +66,8 @@ constexpr size_t kGqaScratchBytes = size_t(40) << 20;
 hipError_t gqa_scratch(char** ptr);
 hipError_t launch_diag_e4m3(float* out, hipStream_t s);
 hipError_t launch_diag_fp64(const double* in, double* out, int64_t n, hipStream_t s);
+hipError_t launch_diag_read(const void* src, const int32_t* idx, int64_t n, int32_t chunk_bytes,
+                            uint32_t* sink, hipStream_t s);
 
 // ------------------------------------------------------------------------------ device helpers
 

@@ -295,3 +295,15 @@ def test_no_alloc_attention_rejects_before_any_launch():
                     need = lib.qsa_sparse_gqa_workspace_size(C.byref(a))
                     assert 0 < need or lib.qsa_sparse_gqa_num_splits(C.byref(a)) == 1
                     assert need <= limit, (T, hkv, G, kv_dtype, need)
+
+
+def test_read_bandwidth_probe_rejects_bad_arguments():
+    lib = B.lib()
+    INVAL = 1
+    assert lib.qsa_diag_read_bandwidth(None, None, 4, 2048, FAKE, None) == INVAL
+    assert lib.qsa_diag_read_bandwidth(FAKE, None, 4, 2048, None, None) == INVAL
+    assert lib.qsa_diag_read_bandwidth(FAKE, None, 4, 1000, FAKE, None) == INVAL
+    assert lib.qsa_diag_read_bandwidth(FAKE, None, 4, 8192, FAKE, None) == INVAL
+    assert lib.qsa_diag_read_bandwidth(FAKE + 8, None, 4, 2048, FAKE, None) == INVAL
+    assert lib.qsa_diag_read_bandwidth(FAKE, None, -1, 2048, FAKE, None) == INVAL
+    assert lib.qsa_diag_read_bandwidth(FAKE, None, 0, 2048, FAKE, None) == 0
