@@ -25,10 +25,12 @@ __global__ void diag_fp64_kernel(const double* in, double* out, int64_t n) {
   out[3 * i + 2] = 1.0 / r;
 }
 
-// Read-bandwidth probe: wave v reads chunks v, v + waves, ... of chunk_bytes each (chunk i at
+// Read-bandwidth probe: wave v reads list entries 8v .. 8v+7, then 8(v + waves) .. +7, ... (so a
+// streaming read walks contiguous 8-chunk runs), each a chunk of chunk_bytes (entry i at
 // i * chunk_bytes, or at idx[i] * chunk_bytes with an index list), 16 bytes per lane, the loads
-// of eight chunks in flight together, and folds everything it read into one word with XOR
-// (atomically into sink[0]) so that no load is dead.
+// of the eight chunks in flight together (the next run's indices are loaded beside them), and
+// folds everything it read into one word with XOR (atomically into sink[0]) so that no load is
+// dead.
 __global__ __launch_bounds__(256) void diag_read_kernel(const uint4* src, const int32_t* idx,
                                                        int64_t n, int32_t chunk_bytes,
                                                        uint32_t* sink) {
@@ -37,12 +39,24 @@ __global__ __launch_bounds__(256) void diag_read_kernel(const uint4* src, const 
   const int64_t v = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
   const int per = chunk_bytes / 1024;  // 1 KiB loads per chunk
   uint32_t acc = 0u;
-  for (int64_t c0 = v; c0 < n; c0 += 8 * waves) {
+  int64_t cur[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int64_t c = 8 * v + u;
+    cur[u] = c < n ? (idx ? (int64_t)idx[c] : c) : -1;
+  }
+  for (int64_t c0 = 8 * v; c0 < n; c0 += 8 * waves) {
     uint4 x[8][4];
+    int64_t nxt[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int64_t c = c0 + u * waves;
-      const int64_t base = c < n ? (idx ? (int64_t)idx[c] : c) * (chunk_bytes / 16) : 0;
+      const int64_t c = c0 + 8 * waves + u;
+      nxt[u] = c < n ? (idx ? (int64_t)idx[c] : c) : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t c = c0 + u;
+      const int64_t base = cur[u] >= 0 ? cur[u] * (chunk_bytes / 16) : 0;
 #pragma unroll
       for (int k = 0; k < 4; ++k)
         x[u][k] = (c < n && k < per) ? src[base + 64 * k + lane] : make_uint4(0u, 0u, 0u, 0u);
@@ -51,6 +65,8 @@ __global__ __launch_bounds__(256) void diag_read_kernel(const uint4* src, const 
     for (int u = 0; u < 8; ++u)
 #pragma unroll
       for (int k = 0; k < 4; ++k) acc ^= x[u][k].x ^ x[u][k].y ^ x[u][k].z ^ x[u][k].w;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) cur[u] = nxt[u];
   }
   for (int m = 32; m >= 1; m >>= 1) acc ^= __shfl_xor(acc, m, kWave);
   if (lane == 0) atomicXor(sink, acc);
