@@ -12,6 +12,8 @@
 // score, a block with fast score > T + 2E is certainly kept, one below T - 2E certainly dropped,
 // and only the band in between is re-scored in float64 in the canonical order and ranked by
 // (score desc, block asc).
+#include <type_traits>
+
 #include "select.h"
 
 namespace qsa {
@@ -39,19 +41,18 @@ __device__ __forceinline__ T block_sum(T v, T* scratch) {
 }
 
 // Value of lane l + N of the same row of 16 lanes (DPP row_shl); lanes past the row's end get
-// zero.  Only the lanes whose partner exists use the result.
+// zero (bound_ctrl, so no old value has to be set up).  Only the lanes whose partner exists
+// use the result.
 template <int N>
 __device__ __forceinline__ double row_down(double x) {
   const uint64_t u = (uint64_t)__double_as_longlong(x);
-  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, 0x100 + N, 0xF, 0xF, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), 0x100 + N, 0xF, 0xF,
-                                             false);
+  const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)u, 0x100 + N, 0xF, 0xF, true);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(u >> 32), 0x100 + N, 0xF, 0xF, true);
   return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
 }
 template <int N>
 __device__ __forceinline__ float row_down(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x100 + N, 0xF, 0xF,
-                                                    false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x100 + N, 0xF, 0xF, true));
 }
 
 // Key values of the 16-lane group's lane l: dim pairs i = l, l+16, l+32, l+48 (dims 2i, 2i+1),
@@ -87,34 +88,48 @@ __device__ __forceinline__ void key_pairs16(const SelectParams& P, const int32_t
   }
 }
 
-// Canonical float64 score of compressed row j against the row's Q (held in LDS as floats),
-// computed by a group of 16 lanes (l = lane % 16).  Per head the 128 exact products are summed
-// by halving: pairs (2i, 2i+1) give v_i; then v_i += v_{i+32} for i < 32, += v_{i+16} for
-// i < 16, ..., += v_{i+1} for i < 1.  Lane l holds v_l, v_{l+16}, v_{l+32}, v_{l+48}, so the
-// first two halvings are in-lane and the last four take the partner 8, 4, 2, 1 lanes up.
-// The heads are then added in order (ReLU-sum: each head's sum clamped at 0 first).  The result
-// is valid in lane l = 0.
+// Canonical float64 score of compressed row j against the row's Q, computed by a group of 16
+// lanes (l = lane % 16).  Per head the 128 exact products are summed by halving: pairs
+// (2i, 2i+1) give v_i; then v_i += v_{i+32} for i < 32, += v_{i+16} for i < 16, ..., += v_{i+1}
+// for i < 1.  Lane l holds v_l, v_{l+16}, v_{l+32}, v_{l+48}, so the first two halvings are
+// in-lane and the last four take the partner 8, 4, 2, 1 lanes up.  The heads are then added in
+// order (RELU, the ReLU-sum: each head's sum clamped at 0 first).  Q is read from LDS as
+// float64 (Q64: the row's heads fit) or as float32 converted here; both hold the same values.
+// The result is valid in lane l = 0.
+template <bool Q64, bool RELU>
 __device__ double canonical_score16(const SelectParams& P, const float* qrow,
                                     const int32_t* cbt_row, int cw, int j, int l) {
   float k[8];
   key_pairs16(P, cbt_row, cw, j, l, k);
+  double kd[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) kd[t] = (double)k[t];
   double s = 0.0;
   for (int h = 0; h < P.Hi; ++h) {
-    const float* q = qrow + h * kHeadDim;
     double v[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int i = l + 16 * t;
-      const double p0 = (double)q[2 * i] * (double)k[2 * t];          // exact
-      const double p1 = (double)q[2 * i + 1] * (double)k[2 * t + 1];  // exact
-      v[t] = p0 + p1;
+      double q0, q1;
+      if constexpr (Q64) {
+        const double2 qq =
+            *reinterpret_cast<const double2*>(reinterpret_cast<const double*>(qrow) +
+                                              h * kHeadDim + 2 * i);
+        q0 = qq.x;
+        q1 = qq.y;
+      } else {
+        const float2 qq = *reinterpret_cast<const float2*>(qrow + h * kHeadDim + 2 * i);
+        q0 = (double)qq.x;
+        q1 = (double)qq.y;
+      }
+      v[t] = fma(q0, kd[2 * t], q1 * kd[2 * t + 1]);  // both products exact: p0 + p1 rounded
     }
     double x = (v[0] + v[2]) + (v[1] + v[3]);
     x = x + row_down<8>(x);
     x = x + row_down<4>(x);
     x = x + row_down<2>(x);
     x = x + row_down<1>(x);
-    if (P.relu) x = x > 0.0 ? x : 0.0;  // ReLU-sum: max(0, head product)
+    if constexpr (RELU) x = x > 0.0 ? x : 0.0;  // ReLU-sum: max(0, head product)
     s = (h == 0) ? x : s + x;
   }
   return s;
@@ -257,7 +272,8 @@ void topk_kernel(SelectParams P) {
   __shared__ int s_wave[kWaves];
   __shared__ double s_dbl[kWaves];
   __shared__ float s_flt[kWaves];
-  __shared__ float qrow[16 * kHeadDim];
+  // The row's Q: as float64 when its heads fit (Hi <= 8), else as float32.
+  __shared__ __attribute__((aligned(16))) float qrow[16 * kHeadDim];
   __shared__ float qfold[kHeadDim];
   __shared__ int32_t band_idx_s[kBandCap];
   __shared__ int32_t band2_idx_s[kBandCap];
@@ -394,12 +410,14 @@ void topk_kernel(SelectParams P) {
     key[i] = fkey(sc[i]);
   }
   double qa = 0.0;
+  const bool q64 = P.Hi <= 8;
 #pragma unroll
   for (int k = 0; k < kQPer; ++k) {
     const int i = tid + k * NT;
     if (i < P.Hi * kHeadDim) {
       const float f = P.fp8 ? e4m3_to_f32_exact(qv[k]) : bf16_to_f32((uint16_t)qv[k]);
-      qrow[i] = f;
+      if (q64) reinterpret_cast<double*>(qrow)[i] = (double)f;
+      else qrow[i] = f;
       qa += fabs((double)f);
     }
   }
@@ -560,8 +578,11 @@ void topk_kernel(SelectParams P) {
     // the band exactly as the first level selected within the row; the rest of the band goes
     // to the float64 re-scoring.
     for (int d = tid; d < kHeadDim; d += NT) {
-      float f = qrow[d];
-      for (int hh = 1; hh < P.Hi; ++hh) f = f + qrow[hh * kHeadDim + d];
+      auto qat = [&](int i) {
+        return q64 ? (float)reinterpret_cast<const double*>(qrow)[i] : qrow[i];
+      };
+      float f = qat(d);
+      for (int hh = 1; hh < P.Hi; ++hh) f = f + qat(hh * kHeadDim + d);
       qfold[d] = f;
     }
     lds_barrier();
@@ -598,17 +619,31 @@ void topk_kernel(SelectParams P) {
     band = band2;
   }
 
-  // ---- re-score the band in float64, canonical order (16 lanes per entry)
-  for (int b0 = 0; b0 < nb; b0 += groups) {
-    const int b = b0 + grp;
-    const double s = canonical_score16(P, qrow, cbt_row, cw, b < nb ? band[b] : -1, l16);
-    if (l16 == 0 && b < nb) bscore[b] = s;
+  // ---- re-score the band in float64, canonical order (16 lanes per entry; a wave whose four
+  // groups hold no entry of the round skips it)
+  auto rescore = [&](auto q64_tag, auto relu_tag) {
+    constexpr bool kQ64 = decltype(q64_tag)::value, kRelu = decltype(relu_tag)::value;
+    for (int b0 = 0; b0 < nb; b0 += groups) {
+      if (b0 + 4 * w >= nb) break;  // wave-uniform: later rounds start further on
+      const int b = b0 + grp;
+      const double s = canonical_score16<kQ64, kRelu>(P, qrow, cbt_row, cw,
+                                                      b < nb ? band[b] : -1, l16);
+      if (l16 == 0 && b < nb) bscore[b] = s;
+    }
+  };
+  if (q64) {
+    if (P.relu) rescore(std::true_type{}, std::true_type{});
+    else rescore(std::true_type{}, std::false_type{});
+  } else {
+    if (P.relu) rescore(std::false_type{}, std::true_type{});
+    else rescore(std::false_type{}, std::false_type{});
   }
   if (in_lds) lds_barrier(); else __syncthreads();
 
   // ---- rank the band: keep its `need` best by (score desc, block asc).  A 16-lane group per
   // entry, each lane comparing against every 16th entry, the counts summed on DPP.
   for (int b0 = 0; b0 < nb; b0 += groups) {
+    if (b0 + 4 * w >= nb) break;  // wave-uniform, as in the re-scoring
     const int b = b0 + grp;
     const bool live = b < nb;
     const double sb = live ? bscore[b] : 0.0;
