@@ -14,6 +14,10 @@ struct SelectParams {
                        // per-row workspace arrays are indexed by row - row_lo
   bool fp8;
   bool relu;          // ReLU-sum aggregation (every request on the ReLU matrix-core kernel)
+  // Factors F of the fast scores' error bounds E = F * kappa * A (kappa = max |k| over the
+  // request's keys, A = sum |q|): the head-folded float32 score of the vector-unit logits, and
+  // the matrix-core score.  They depend on Hi and the aggregation only (set by the host).
+  double e_fold, e_mfma;
   const int32_t* qsl;
   const int32_t* seq_lens;
   const void* q_idx;
@@ -47,5 +51,7 @@ hipError_t launch_logits_list(const SelectParams& P, int nr, bool relu, bool kma
                               hipStream_t s);
 hipError_t launch_logits_mfma(const SelectParams& P, int max_query_len, hipStream_t s);
 hipError_t launch_topk_select(const SelectParams& P, hipStream_t s);
+// The error-bound factors of SelectParams (topk.hip).
+void topk_bound_factors(int Hi, bool relu, double& e_fold, double& e_mfma);
 
 }  // namespace qsa

@@ -50,6 +50,7 @@ hipError_t launch_topk(const qsa_topk_args& a, const TopkLayout& L, char* ws, hi
   P.key_blocks = L.key_blocks;
   P.fp8 = a.index_dtype == QSA_DTYPE_FP8_E4M3;
   P.relu = a.index_agg == QSA_AGG_RELU_SUM;
+  topk_bound_factors(P.Hi, P.relu, P.e_fold, P.e_mfma);
   P.qsl = a.query_start_loc;
   P.seq_lens = a.seq_lens;
   P.q_idx = a.q_idx;

@@ -377,38 +377,6 @@ void topk_kernel(SelectParams P) {
   }
   // Rows scored on the matrix cores hold bf16 logits (in the row's float32-sized stride).
   const bool bf16_row = n_req > P.mfma_min_rows;  // block-uniform
-  if (bf16_row) {
-    static_assert(E % 8 == 0, "a thread's bf16 scores are whole 16-byte words");
-    const uint16_t* lb = reinterpret_cast<const uint16_t*>(lg);
-#pragma unroll
-    for (int i = 0; i < E; i += 8) {
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (jb + i < vis) v = *reinterpret_cast<const uint4*>(lb + jb + i);
-      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        sc[i + 2 * k] = bf16lo(w4[k]);
-        sc[i + 2 * k + 1] = bf16hi(w4[k]);
-      }
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < E; i += 4) {  // the rest of the visible scores
-      if (jb + i >= pf_end && jb + i < vis) {
-        const float4 v = *reinterpret_cast<const float4*>(lg + jb + i);
-        sc[i] = v.x;
-        sc[i + 1] = v.y;
-        sc[i + 2] = v.z;
-        sc[i + 3] = v.w;
-      }
-    }
-  }
-  uint32_t key[E];  // order-preserving keys of the fast scores
-#pragma unroll
-  for (int i = 0; i < E; ++i) {
-    sc[i] = jb + i < vis ? sc[i] : -__builtin_inff();
-    key[i] = fkey(sc[i]);
-  }
   double qa = 0.0;
   const bool q64 = P.Hi <= 8;
 #pragma unroll
@@ -424,101 +392,37 @@ void topk_kernel(SelectParams P) {
   const int mask_words = (vis + 31) >> 5;
   for (int i = tid; i < mask_words; i += NT) sel_mask[i] = 0u;
 
-  // ---- radix select.  Thread t reads the counts of bins (bins-1) - t*kPB - i (i < kPB): lower
-  // threads own higher bins, so a workgroup prefix sum gives the count above each bin.  Only
-  // visible blocks are counted (the -inf entries of a short row would all add to one bin, and
-  // its LDS atomics would serialise).
-  // Histograms alternate between two buffers; a pass clears the one the next-but-one uses.
-  uint32_t prefix = 0, pmask = 0, lowmask = kLowMask;
-  int krem = kb;
+  // Shared steps of both row types.  The error-bound inputs are reduced per wave during the
+  // last radix pass (published by that pass's barrier).
+  auto publish_bound_inputs = [&] {
+    const float kmw = wave_max(km);
+    double qaw = qa;
 #pragma unroll
-  for (int pass = 0; pass < C::PASSES; ++pass) {
-    const int shift = 32 - kRadixBits * (pass + 1);
-    // A bf16 value's key has 16 significant bits: once they are resolved, stop (block-uniform).
-    if (bf16_row && shift + kRadixBits <= 16) {
-      lowmask = (1u << (shift + kRadixBits)) - 1u;
-      break;
+    for (int mm = 32; mm >= 1; mm >>= 1) qaw += shfl_xor_f64(qaw, mm);
+    if (lane == 0) {
+      s_flt[w] = kmw;
+      s_dbl[w] = qaw;
     }
-    int* h = hist[pass & 1];
+  };
+  double E_f = 0.0, Ebound = 0.0;
+  auto bounds = [&] {
+    if (cbt_in_lds) {
 #pragma unroll
-    for (int i = 0; i < E; ++i) {
-      const uint32_t u = key[i];
-      if (jb + i < vis && (u & pmask) == prefix)
-        atomicAdd(&h[(u >> shift) & (kRadixBins - 1)], 1);
-    }
-    if (pass >= 1 && pass + 1 < C::PASSES) {  // the buffer of pass + 1 was read by pass - 1
-      for (int i = tid; i < kRadixBins; i += NT) hist[(pass + 1) & 1][i] = 0;
-    }
-    if (pass == 1) {  // the error-bound inputs, reduced over the workgroup below
-      const float kmw = wave_max(km);
-      double qaw = qa;
-#pragma unroll
-      for (int mm = 32; mm >= 1; mm >>= 1) qaw += shfl_xor_f64(qaw, mm);
-      if (lane == 0) {
-        s_flt[w] = kmw;
-        s_dbl[w] = qaw;
+      for (int k = 0; k < kCbtPer; ++k) {
+        const int c = tid + k * NT;
+        if (c < cw) cbt_s[c] = cbt_v[k];
       }
     }
-    lds_barrier();
-    int c[kPB], S = 0;
-    const int b0 = kRadixBins - (tid + 1) * kPB;  // c[i] = count of bin b0 + kPB - 1 - i
-#pragma unroll
-    for (int i = 0; i < kPB; ++i) {
-      c[i] = h[b0 + kPB - 1 - i];
-      S += c[i];
+    double kappa = 0.0, A = 0.0;
+    for (int i = 0; i < kWaves; ++i) {
+      kappa = fmax(kappa, (double)s_flt[i]);
+      A += s_dbl[i];
     }
-    const int incl = wave_incl_scan(S);
-    if (lane == 63) s_wave[w] = incl;
-    lds_barrier();
-    int above = incl - S;
-    for (int i = 0; i < w; ++i) above += s_wave[i];
-    if (above < krem && krem <= above + S) {
-#pragma unroll
-      for (int i = 0; i < kPB; ++i) {
-        if (above < krem && krem <= above + c[i]) {
-          s_int[4] = b0 + kPB - 1 - i;
-          s_int[5] = krem - above;
-        }
-        above += c[i];
-      }
-    }
-    lds_barrier();
-    prefix |= (uint32_t)s_int[4] << shift;
-    pmask |= (uint32_t)(kRadixBins - 1) << shift;
-    krem = s_int[5];
-  }
-  // The kb-th largest fast score lies in [T_lo, T_hi], the values of the keys with this prefix.
-  const double T_lo = (double)fval(prefix), T_hi = (double)fval(prefix | lowmask);
-  if (cbt_in_lds) {
-#pragma unroll
-    for (int k = 0; k < kCbtPer; ++k) {
-      const int c = tid + k * NT;
-      if (c < cw) cbt_s[c] = cbt_v[k];
-    }
-  }
-  const int32_t* cbt_row = cbt_in_lds ? cbt_s : P.cbt + (int64_t)r * P.cbt_stride;
-
-  // ---- error bound E of the fast scores for this row
-  double kappa = 0.0, A = 0.0;
-  for (int i = 0; i < kWaves; ++i) {
-    kappa = fmax(kappa, (double)s_flt[i]);
-    A += s_dbl[i];
-  }
-  // Bound of the head-folded float32 score (the VALU logits, and the second level below), and
-  // of the matrix-core score: Q folded in float32 (heads in order), split into bf16 terms
-  // hi + mid + lo (residual <= 2^-24 |f|; |hi| <= (1 + 2^-8) |f|, |mid| + |lo| <= 2^-7 |f|);
-  // per k-step the 32 exact hi products summed by the matrix cores, all mid and lo products in
-  // one more sum (any order and rounding: u = 2^-23), and the five partial sums added on the
-  // vector unit (u = 2^-24).  (ReLU-sum scores come from the matrix cores: u = 2^-23.)
-  const double gam_f = (double)(P.Hi + 130) * (P.relu ? 0x1p-23 : 0x1p-24);
-  const double E_f = 2.0 * gam_f / (1.0 - gam_f) * kappa * A + 1e-30;
-  const bool mfma_row = bf16_row;
-  auto gam = [](double n, double u) { return n * u / (1.0 - n * u); };
-  const double g_fold = gam(P.Hi - 1, 0x1p-24);
-  const double gam_m = g_fold + (0x1p-24 + gam(34, 0x1p-23) * (1.0 + 0x1p-7) +
-                                 gam(2 * kHeadDim + 2, 0x1p-23) * 0x1p-7 +
-                                 gam(4, 0x1p-24) * (1.0 + 0x1p-6)) * (1.0 + g_fold);
-  const double Ebound = mfma_row ? 2.0 * gam_m * (1.0 + 0x1p-20) * kappa * A + 1e-30 : E_f;
+    // Bounds of the head-folded float32 score (the VALU logits, and the second level below)
+    // and of the matrix-core score (topk_bound_factors).
+    E_f = P.e_fold * kappa * A + 1e-30;
+    Ebound = bf16_row ? P.e_mfma * kappa * A + 1e-30 : E_f;
+  };
   // Certainly kept above hi, certainly dropped below lo; float32 forms widen the band only.
   // A score b stands for canonical scores in [b - d(b), b + d(b)] with d(b) = Ebound (float32
   // rows) or Ebound + r |b| (bf16 rows: rounding to nearest moves a value by at most 2^-8 of
@@ -526,28 +430,169 @@ void topk_kernel(SelectParams P) {
   // score lies in [T_lo - d(T_lo), T_hi + d(T_hi)]; a block is certainly kept if b - d(b)
   // exceeds the upper end and certainly dropped if b + d(b) is below the lower end.  hi and lo
   // solve those two conditions for b.
-  float hi, lo;
+  uint32_t keepbits = 0, bandbits = 0;
   if (bf16_row) {
+    // ---- bf16 rows: the 16-bit order-preserving keys of a pair of scores share a word (score
+    // 2m in the low half, 2m + 1 in the high half), and two passes of 8-bit digits resolve the
+    // kb-th largest key exactly, so the threshold is one bf16 value T.
+    static_assert(E % 8 == 0, "a thread's bf16 scores are whole 16-byte words");
+    constexpr int E2 = E / 2;
+    uint32_t rw[E2], kp[E2];
+    const uint16_t* lb = reinterpret_cast<const uint16_t*>(lg);
+#pragma unroll
+    for (int i = 0; i < E; i += 8) {
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (jb + i < vis) v = *reinterpret_cast<const uint4*>(lb + jb + i);
+      rw[i / 2] = v.x;
+      rw[i / 2 + 1] = v.y;
+      rw[i / 2 + 2] = v.z;
+      rw[i / 2 + 3] = v.w;
+    }
+    const int nv = min(max(vis - jb, 0), E);  // this thread's visible scores: i < nv
+    // Per half: sign clear -> b | 0x8000, sign set -> ~b (as fkey on float32).
+#pragma unroll
+    for (int m = 0; m < E2; ++m) {
+      const uint32_t sgn = (rw[m] >> 15) & 0x00010001u;
+      kp[m] = rw[m] ^ 0x80008000u ^ (sgn * 0x7FFFu);
+    }
+    // One 256-bin pass: thread t < 256 owns bin 255 - t, a workgroup prefix sum gives the count
+    // above each bin; returns the bin holding the krem-th largest and the rank within it.
+    auto scan256 = [&](const int* h, int& kr) {
+      const int S = tid < 256 ? h[255 - tid] : 0;
+      const int incl = wave_incl_scan(S);
+      if (lane == 63) s_wave[w] = incl;
+      lds_barrier();
+      int above = incl - S;
+      for (int i = 0; i < w; ++i) above += s_wave[i];
+      if (above < kr && kr <= above + S) {
+        s_int[4] = 255 - tid;
+        s_int[5] = kr - above;
+      }
+      lds_barrier();
+      kr = s_int[5];
+      return s_int[4];
+    };
+    int krem = kb;
+#pragma unroll
+    for (int m = 0; m < E2; ++m) {
+      if (2 * m < nv) atomicAdd(&hist[0][(kp[m] >> 8) & 0xFFu], 1);
+      if (2 * m + 1 < nv) atomicAdd(&hist[0][kp[m] >> 24], 1);
+    }
+    lds_barrier();
+    const uint32_t d0 = (uint32_t)scan256(hist[0], krem);
+#pragma unroll
+    for (int m = 0; m < E2; ++m) {
+      if (2 * m < nv && ((kp[m] >> 8) & 0xFFu) == d0) atomicAdd(&hist[1][kp[m] & 0xFFu], 1);
+      if (2 * m + 1 < nv && (kp[m] >> 24) == d0) atomicAdd(&hist[1][(kp[m] >> 16) & 0xFFu], 1);
+    }
+    publish_bound_inputs();
+    lds_barrier();
+    const uint32_t key16 = (d0 << 8) | (uint32_t)scan256(hist[1], krem);
+    const uint32_t tb = (key16 & 0x8000u) ? (key16 ^ 0x8000u) : (key16 ^ 0xFFFFu);
+    const double T = (double)__uint_as_float(tb << 16);  // the kb-th largest fast score
+    bounds();
     const double rr = 0x1p-8 * (1.0 + 0x1p-20);
-    const double x = T_hi + rr * fabs(T_hi) + 2.0 * Ebound;   // b - r|b| must exceed x
-    const double y = T_lo - rr * fabs(T_lo) - 2.0 * Ebound;   // b + r|b| must reach y
+    const double x = T + rr * fabs(T) + 2.0 * Ebound;   // b - r|b| must exceed x
+    const double y = T - rr * fabs(T) - 2.0 * Ebound;   // b + r|b| must reach y
     const double bh = x >= 0.0 ? x / (1.0 - rr) : x / (1.0 + rr);
     const double bl = y >= 0.0 ? y / (1.0 + rr) : y / (1.0 - rr);
-    hi = round_up_f32(bh + fabs(bh) * 0x1p-40 + 1e-30);
-    lo = round_down_f32(bl - fabs(bl) * 0x1p-40 - 1e-30);
-  } else {
-    hi = round_up_f32(T_hi + 2.0 * Ebound);
-    lo = round_down_f32(T_lo - 2.0 * Ebound);
-  }
-
-  // ---- classify and collect the band in block order: one workgroup scan of the per-thread
-  // counts (band entries in the low half, certain keeps in the high half of a packed int).
-  uint32_t keepbits = 0, bandbits = 0;
+    const float hi = round_up_f32(bh + fabs(bh) * 0x1p-40 + 1e-30);
+    const float lo = round_down_f32(bl - fabs(bl) * 0x1p-40 - 1e-30);
+    // ---- classify (invisible scores are neither kept nor in the band)
 #pragma unroll
-  for (int i = 0; i < E; ++i) {
-    keepbits |= (sc[i] > hi ? 1u : 0u) << i;
-    bandbits |= (sc[i] <= hi && sc[i] >= lo ? 1u : 0u) << i;
+    for (int m = 0; m < E2; ++m) {
+      const float f0 = __uint_as_float(rw[m] << 16), f1 = __uint_as_float(rw[m] & 0xFFFF0000u);
+      const bool v0 = 2 * m < nv, v1 = 2 * m + 1 < nv;
+      keepbits |= (v0 && f0 > hi ? 1u : 0u) << (2 * m);
+      keepbits |= (v1 && f1 > hi ? 1u : 0u) << (2 * m + 1);
+      bandbits |= (v0 && f0 <= hi && f0 >= lo ? 1u : 0u) << (2 * m);
+      bandbits |= (v1 && f1 <= hi && f1 >= lo ? 1u : 0u) << (2 * m + 1);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < E; i += 4) {  // the rest of the visible scores
+      if (jb + i >= pf_end && jb + i < vis) {
+        const float4 v = *reinterpret_cast<const float4*>(lg + jb + i);
+        sc[i] = v.x;
+        sc[i + 1] = v.y;
+        sc[i + 2] = v.z;
+        sc[i + 3] = v.w;
+      }
+    }
+    uint32_t key[E];  // order-preserving keys of the fast scores
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      sc[i] = jb + i < vis ? sc[i] : -__builtin_inff();
+      key[i] = fkey(sc[i]);
+    }
+
+    // ---- radix select.  Thread t reads the counts of bins (bins-1) - t*kPB - i (i < kPB):
+    // lower threads own higher bins, so a workgroup prefix sum gives the count above each bin.
+    // Only visible blocks are counted (the -inf entries of a short row would all add to one
+    // bin, and its LDS atomics would serialise).  Histograms alternate between two buffers; a
+    // pass clears the one the next-but-one uses.
+    uint32_t prefix = 0, pmask = 0;
+    int krem = kb;
+#pragma unroll
+    for (int pass = 0; pass < C::PASSES; ++pass) {
+      const int shift = 32 - kRadixBits * (pass + 1);
+      int* h = hist[pass & 1];
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        const uint32_t u = key[i];
+        if (jb + i < vis && (u & pmask) == prefix)
+          atomicAdd(&h[(u >> shift) & (kRadixBins - 1)], 1);
+      }
+      if (pass >= 1 && pass + 1 < C::PASSES) {  // the buffer of pass + 1 was read by pass - 1
+        for (int i = tid; i < kRadixBins; i += NT) hist[(pass + 1) & 1][i] = 0;
+      }
+      if (pass == C::PASSES - 1) publish_bound_inputs();
+      lds_barrier();
+      int c[kPB], S = 0;
+      const int b0 = kRadixBins - (tid + 1) * kPB;  // c[i] = count of bin b0 + kPB - 1 - i
+#pragma unroll
+      for (int i = 0; i < kPB; ++i) {
+        c[i] = h[b0 + kPB - 1 - i];
+        S += c[i];
+      }
+      const int incl = wave_incl_scan(S);
+      if (lane == 63) s_wave[w] = incl;
+      lds_barrier();
+      int above = incl - S;
+      for (int i = 0; i < w; ++i) above += s_wave[i];
+      if (above < krem && krem <= above + S) {
+#pragma unroll
+        for (int i = 0; i < kPB; ++i) {
+          if (above < krem && krem <= above + c[i]) {
+            s_int[4] = b0 + kPB - 1 - i;
+            s_int[5] = krem - above;
+          }
+          above += c[i];
+        }
+      }
+      lds_barrier();
+      prefix |= (uint32_t)s_int[4] << shift;
+      pmask |= (uint32_t)(kRadixBins - 1) << shift;
+      krem = s_int[5];
+    }
+    // The kb-th largest fast score lies in [T_lo, T_hi], the values of the keys with this
+    // prefix.
+    const double T_lo = (double)fval(prefix), T_hi = (double)fval(prefix | kLowMask);
+    bounds();
+    const float hi = round_up_f32(T_hi + 2.0 * Ebound);
+    const float lo = round_down_f32(T_lo - 2.0 * Ebound);
+    // ---- classify
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      keepbits |= (sc[i] > hi ? 1u : 0u) << i;
+      bandbits |= (sc[i] <= hi && sc[i] >= lo ? 1u : 0u) << i;
+    }
   }
+  const bool mfma_row = bf16_row;
+  const int32_t* cbt_row = cbt_in_lds ? cbt_s : P.cbt + (int64_t)r * P.cbt_stride;
+
+  // ---- collect the band in block order: one workgroup scan of the per-thread counts (band
+  // entries in the low half, certain keeps in the high half of a packed int).
   const int my_cnt = __builtin_popcount(bandbits) | (__builtin_popcount(keepbits) << 16);
   const int cl_incl = wave_incl_scan(my_cnt);
   if (lane == 63) s_wave[w] = cl_incl;
@@ -694,15 +739,14 @@ void topk_kernel(SelectParams P) {
   }
   if (list_in_lds) {
     lds_barrier();
-    // col / c through a float reciprocal, corrected to the exact quotient (col < 2^24).
-    const float rc = 1.0f / (float)P.c;
-    for (int col = tid; col <= W; col += NT) {
-      int blk = (int)((float)col * rc), m = col - blk * P.c;
-      if (m < 0) { --blk; m += P.c; } else if (m >= P.c) { ++blk; m -= P.c; }
-      out[col] = col < sel * P.c ? list[blk] * P.c + m
-                                 : (col < count ? vis * P.c + (col - sel * P.c)
-                                                : (col < W ? -1 : count));
+    // Block b's c tokens by thread b (mod NT), then the tail, the padding and the count.
+    for (int b = tid; b < sel; b += NT) {
+      const int t0 = list[b] * P.c;
+      int32_t* o = out + b * P.c;
+      for (int m = 0; m < P.c; ++m) o[m] = t0 + m;
     }
+    for (int col = sel * P.c + tid; col <= W; col += NT)
+      out[col] = col < count ? vis * P.c + (col - sel * P.c) : (col < W ? -1 : count);
   } else {
     for (int col = sel * P.c + tid; col <= W; col += NT)
       out[col] = col < count ? vis * P.c + (col - sel * P.c) : (col < W ? -1 : count);
@@ -717,6 +761,26 @@ hipError_t launch_topk_kernel(const SelectParams& P, size_t mask_bytes, hipStrea
 }
 
 }  // namespace
+
+// Error-bound factors of the fast scores, E = F * kappa * A, with gamma_n = n u / (1 - n u):
+//  * the head-folded float32 score (the VALU logits): Hi - 1 folding additions and a 128-term
+//    dot product, u = 2^-24 (ReLU-sum scores come from the matrix cores: u = 2^-23), F twice
+//    gamma_{Hi+130} / (1 - gamma_{Hi+130});
+//  * the matrix-core score: Q folded in float32 (heads in order, gamma_{Hi-1}), split into bf16
+//    terms hi + mid + lo (residual <= 2^-24 |f|; |hi| <= (1 + 2^-8) |f|, |mid| + |lo| <=
+//    2^-7 |f|); per k-step the 32 exact hi products summed by the matrix cores, all mid and lo
+//    products in one more sum (any order and rounding: u = 2^-23), and the five partial sums
+//    added on the vector unit (u = 2^-24); F twice that, widened by 2^-20.
+void topk_bound_factors(int Hi, bool relu, double& e_fold, double& e_mfma) {
+  auto gam = [](double n, double u) { return n * u / (1.0 - n * u); };
+  const double gam_f = (double)(Hi + 130) * (relu ? 0x1p-23 : 0x1p-24);
+  e_fold = 2.0 * gam_f / (1.0 - gam_f);
+  const double g_fold = gam(Hi - 1, 0x1p-24);
+  const double gam_m = g_fold + (0x1p-24 + gam(34, 0x1p-23) * (1.0 + 0x1p-7) +
+                                 gam(2 * kHeadDim + 2, 0x1p-23) * 0x1p-7 +
+                                 gam(4, 0x1p-24) * (1.0 + 0x1p-6)) * (1.0 + g_fold);
+  e_mfma = 2.0 * gam_m * (1.0 + 0x1p-20);
+}
 
 hipError_t launch_topk_select(const SelectParams& P, hipStream_t s) {
   const size_t mask_bytes = (size_t)(P.cols + 31) / 32 * sizeof(uint32_t);
