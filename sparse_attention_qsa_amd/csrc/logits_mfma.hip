@@ -80,9 +80,11 @@ __device__ __forceinline__ void lds_store_u32(void* p, uint32_t v) {
 template <int N>
 __device__ __forceinline__ void lds_load_u32x4(uint32_t a, uint32_t b, uint32_t c, uint32_t d,
                                                int (&o)[N], int k) {
+  // Early-clobber outputs: a read's destination must not be the address register of a read
+  // issued after it, whose address the returning data could otherwise overwrite.
   asm volatile("ds_read_b32 %0, %4\n\tds_read_b32 %1, %5\n\tds_read_b32 %2, %6\n\t"
                "ds_read_b32 %3, %7\n\ts_waitcnt lgkmcnt(0)"
-               : "=v"(o[k]), "=v"(o[k + 1]), "=v"(o[k + 2]), "=v"(o[k + 3])
+               : "=&v"(o[k]), "=&v"(o[k + 1]), "=&v"(o[k + 2]), "=&v"(o[k + 3])
                : "v"(a), "v"(b), "v"(c), "v"(d)
                : "memory");
 }
