@@ -236,7 +236,8 @@ qsa_status qsa_index_logits_topk(const qsa_topk_args* args, void* workspace,
  * they return QSA_ERR_NOT_SUPPORTED when the cap makes more than one window. */
 
 /* The two kernels of qsa_index_logits_topk as separate calls, for a caller that times them
- * one by one: qsa_index_logits runs the scoring (fast float32 logits and per-block key bounds
+ * one by one: qsa_index_logits runs the scoring (fast logits, float32 or, for matrix-core
+ * rows, scaled fp16, and per-block key bounds
  * into the workspace), qsa_block_topk the selection and expansion from that workspace.  Run in
  * this order on one stream, with the same arguments and the same, otherwise untouched,
  * workspace, they have exactly the effect of qsa_index_logits_topk.  The workspace contents

@@ -56,11 +56,11 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 #undef QSA_VMCNT
 }
 
-// Two float32 values rounded to nearest even as bf16, packed low then high (one
-// v_cvt_pk_bf16_f32).
-__device__ __forceinline__ uint32_t bf16_pack_rne(float lo, float hi) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+// Two float32 values rounded to nearest even as fp16, packed low then high (one
+// v_cvt_pk_f16_f32).
+__device__ __forceinline__ uint32_t f16_pack_rne(float lo, float hi) {
+  typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+  const f16x2_t v = {(_Float16)lo, (_Float16)hi};
   return __builtin_bit_cast(uint32_t, v);
 }
 
@@ -116,9 +116,10 @@ __device__ __forceinline__ uint32_t claim_async(int* counter) {
 // and stores each group's 16 rows x 16 keys as soon as it is final: the logits leave a store
 // per 128 MFMAs instead of in bursts, so that they do not stall the key loads behind them.
 // Stores are buffer stores whose range ends at the block's last row; keys a row does not see
-// go to an out-of-range offset and are dropped.  The logits leave as bf16 (rounded to nearest
-// even; the row keeps its float32-sized stride): half the bytes of float32, and the top-k's
-// band absorbs the rounding (at most 2^-8 of the stored value).
+// go to an out-of-range offset and are dropped.  The logits leave as fp16, scaled by a power
+// of two per row that keeps them in range (rounded to nearest even; the row keeps its
+// float32-sized stride): half the bytes of float32, and the top-k's band absorbs the rounding
+// (at most 2^-11 of the stored value, or half the smallest subnormal step).
 // F8: e4m3 indexer (128-byte key rows): the key codes are converted to bf16 as the fragments are
 // read (exact: every e4m3 value is a bf16 value), Q is folded from its codes (exact in fp32),
 // and the contraction and its bound are those of the bf16 instance.
@@ -134,7 +135,7 @@ __global__ __launch_bounds__(512) void logits_mfma_kernel(SelectParams P, int ro
   // tile's loads need no global round trip (whose wait would also drain the logit stores).
   constexpr int kPgCap = kMfmaTilesPerItem * kMfmaKeys + 1;
   __shared__ int32_t pg_s[kPgCap];
-  // Per wave, one batch of logits (16 rows x 64 keys, bf16) on its way out: the batch is
+  // Per wave, one batch of logits (16 rows x 64 keys, fp16) on its way out: the batch is
   // written here as the matrix-core layout has it (4 keys of one row per lane) and read back
   // as 16-byte row pieces, so that a store instruction writes 8 whole 128-byte row segments
   // instead of 16 rows x 32 bytes.  16-byte chunk c of row r sits in slot c ^ (r & 7).
@@ -265,8 +266,20 @@ __global__ __launch_bounds__(512) void logits_mfma_kernel(SelectParams P, int ro
     // (l16, l4) holds dims 32 ks + 8 l4 .. +7 of row l16 for each k-step ks, as the hi, mid and
     // lo bf16 terms of f = sum_h q_h (float32, heads in order 0 .. Hi-1).
     bf16x8_t qhi[4], qmid[4], qlo[4];
+    // The row's logits are stored as fp16 scaled by 2^-erow: every score satisfies
+    // |s| <= kappa * A (kappa = max |k| over the request's keys, from the per-block bounds the
+    // vector-unit kernel wrote before this one; A = sum |q| of the row, its heads unfolded), and
+    // erow makes kappa * A * 2^-erow < 2^15, inside the fp16 range with room to spare.
+    int erow = 0;
+    float km = 0.0f;  // this lane's share of kappa, loaded with Q (one round trip)
+    {
+      const int nkb = min(P.key_blocks, (min(L / P.c, P.cols) + 127) / 128);
+      for (int bk = lane; bk < nkb; bk += 64)
+        km = fmaxf(km, P.kmax[(int64_t)r * P.key_blocks + bk]);
+    }
     {
       const int t = min(trow, nrows - 1);
+      float qabs = 0.0f;  // sum |q| over this lane's dims of the row, all heads
       const char* qrow = qb + (int64_t)(q0 + rb * kMfmaRows + t) * P.Hi * kHeadDim * (F8 ? 1 : 2);
       float f[4][8];  // +0 plus the heads in order (a zero's sign changes no score)
 #pragma unroll
@@ -315,10 +328,24 @@ __global__ __launch_bounds__(512) void logits_mfma_kernel(SelectParams P, int ro
               }
             }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) f[ks][e] = f[ks][e] + (use ? x[e] : 0.0f);
+            for (int e = 0; e < 8; ++e) {
+              f[ks][e] = f[ks][e] + (use ? x[e] : 0.0f);
+              qabs = qabs + (use ? fabsf(x[e]) : 0.0f);
+            }
           }
         }
       }
+      // The row's A: its four lanes' sums (float32 sums of at most 512 terms, widened by 2^-6
+      // so that they bound the exact sum), then the exponent.
+      qabs = qabs + __shfl_xor(qabs, 16, 64);
+      qabs = qabs + __shfl_xor(qabs, 32, 64);
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) km = fmaxf(km, __shfl_xor(km, m, 64));
+      const float bound = km * qabs * (1.0f + 0x1p-6f);
+      if (!(bound < 0x1p126f)) erow = 127;  // huge or not finite: scaled to nothing
+      else erow = max(0, __builtin_amdgcn_frexp_expf(bound) - 15);
+      const int grow = q0 + rb * kMfmaRows + trow;  // the call row of this lane's results
+      if (l4 == 0 && trow >= wlo && trow < whi) P.lexp[grow - P.row_lo] = erow;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
@@ -436,7 +463,10 @@ __global__ __launch_bounds__(512) void logits_mfma_kernel(SelectParams P, int ro
             if (!((okm[q] >> (8 * e)) & 0xFFu)) v[e] = 0.0f;
           }
           // Keys 16 q + 4 l4 .. +3 of row l16: bytes 32 q + 8 l4 of its 128-byte batch row.
-          const u32x2_t pk = {bf16_pack_rne(v[0], v[1]), bf16_pack_rne(v[2], v[3])};
+          const u32x2_t pk = {f16_pack_rne(__builtin_amdgcn_ldexpf(v[0], -erow),
+                                           __builtin_amdgcn_ldexpf(v[1], -erow)),
+                              f16_pack_rne(__builtin_amdgcn_ldexpf(v[2], -erow),
+                                           __builtin_amdgcn_ldexpf(v[3], -erow))};
           const uint32_t a = stg_base + l16 * 128 + 16 * ((2 * q + (l4 >> 1)) ^ (l16 & 7)) +
                              8 * (l4 & 1);
           asm volatile("ds_write_b64 %0, %1" ::"v"(a), "v"(pk) : "memory");

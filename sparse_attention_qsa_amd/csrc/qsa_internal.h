@@ -26,11 +26,12 @@ struct TopkLayout {
   int32_t key_tiles;      // VALU logits workgroups per request (kLogitsTilesPerWG tiles each)
   int32_t key_blocks;     // blocks of 128 keys per request
   int32_t rows;           // rows per window (T without a logits cap): the per-row arrays' rows
-  size_t off_logits;      // float  [rows, col_stride] (bf16 rows use the first half)
+  size_t off_logits;      // float  [rows, col_stride] (matrix-core rows: fp16 in the first half)
   size_t off_kmax;        // float  [R, key_blocks]: upper bound of max |k| per block of 128 keys
   size_t off_band_idx;    // int32  [rows, col_stride]
   size_t off_band_score;  // double [rows, col_stride]
   size_t off_work;        // int [8]: work counters of the MFMA kernel
+  size_t off_lexp;        // int32  [rows]: scale exponent of each matrix-core row's logits
   size_t total;
 };
 

@@ -30,6 +30,9 @@ struct SelectParams {
   int32_t* band_idx;
   double* band_score;
   int* work;  // [8] work counters of the MFMA kernel's queues, zeroed by the VALU kernel
+  // [window rows]: a matrix-core row's logits are stored as fp16 values h, the score being
+  // h * 2^lexp[row] (lexp >= 0 keeps every score of the row inside the fp16 range).
+  int32_t* lexp;
 };
 
 // Requests with more rows than this are scored by the matrix-core logits kernel.

@@ -28,6 +28,7 @@ TopkLayout topk_layout(const qsa_topk_args& a) {
   L.off_band_idx = off;   off = align(off + (size_t)rows * L.col_stride * sizeof(int32_t));
   L.off_band_score = off; off = align(off + (size_t)rows * L.col_stride * sizeof(double));
   L.off_work = off;       off = align(off + 8 * sizeof(int));
+  L.off_lexp = off;       off = align(off + (size_t)rows * sizeof(int32_t));
   L.total = off;
   return L;
 }
@@ -63,6 +64,7 @@ hipError_t launch_topk(const qsa_topk_args& a, const TopkLayout& L, char* ws, hi
   P.band_idx = reinterpret_cast<int32_t*>(ws + L.off_band_idx);
   P.band_score = reinterpret_cast<double*>(ws + L.off_band_score);
   P.work = reinterpret_cast<int*>(ws + L.off_work);
+  P.lexp = reinterpret_cast<int32_t*>(ws + L.off_lexp);
   P.row_lo = 0;
   P.row_hi = P.T;
 

@@ -204,10 +204,11 @@ __device__ __forceinline__ void folded_scores16(const SelectParams& P, const flo
 }
 
 // Top-k kernel configurations: NT threads holding E scores each; the threshold's radix select
-// takes PASSES passes of RB-bit digits over the top RB*PASSES bits of the order-preserving key
-// (the rest stay unresolved: the threshold lies in one bin's value interval, which the band
-// absorbs; a bf16 row is resolved after its 16 bits); bands of up to BAND entries and
-// block-table rows of up to CBT columns live in LDS; the first PF scores of a row are loaded
+// over a float32 row takes PASSES passes of RB-bit digits over the top RB*PASSES bits of the
+// order-preserving key (the rest stay unresolved: the threshold lies in one bin's value
+// interval, which the band absorbs; a matrix-core row, fp16, is resolved exactly in two 8-bit
+// passes of its own); bands of up to BAND entries and block-table rows of up to CBT columns
+// live in LDS; the first PF scores of a row are loaded
 // before the request lookup (the rest once the visible range is known).  The decode
 // configurations spend LDS on few, fast rows; the prefill one (many rows, eight sharing a CU)
 // keeps its LDS small and loads after the lookup, when the row's width and type are known.
@@ -375,8 +376,9 @@ void topk_kernel(SelectParams P) {
     const int c = tid + k * NT;
     cbt_v[k] = (cbt_in_lds && c < cw) ? P.cbt[(int64_t)r * P.cbt_stride + c] : -1;
   }
-  // Rows scored on the matrix cores hold bf16 logits (in the row's float32-sized stride).
-  const bool bf16_row = n_req > P.mfma_min_rows;  // block-uniform
+  // Rows scored on the matrix cores hold fp16 logits scaled by 2^-lexp (in the row's
+  // float32-sized stride).
+  const bool f16_row = n_req > P.mfma_min_rows;  // block-uniform
   double qa = 0.0;
   const bool q64 = P.Hi <= 8;
 #pragma unroll
@@ -421,23 +423,26 @@ void topk_kernel(SelectParams P) {
     // Bounds of the head-folded float32 score (the VALU logits, and the second level below)
     // and of the matrix-core score (topk_bound_factors).
     E_f = P.e_fold * kappa * A + 1e-30;
-    Ebound = bf16_row ? P.e_mfma * kappa * A + 1e-30 : E_f;
+    Ebound = f16_row ? P.e_mfma * kappa * A + 1e-30 : E_f;
   };
   // Certainly kept above hi, certainly dropped below lo; float32 forms widen the band only.
   // A score b stands for canonical scores in [b - d(b), b + d(b)] with d(b) = Ebound (float32
-  // rows) or Ebound + r |b| (bf16 rows: rounding to nearest moves a value by at most 2^-8 of
-  // the result; r adds a margin).  Both ends increase with b, so the kb-th largest canonical
+  // rows) or, in the scaled units of a matrix-core row, Ebound 2^-erow + 2^-14 + r |b|
+  // (rounding to nearest fp16 moves a value by at most 2^-11 of the result; r adds a margin).
+  // Both ends increase with b, so the kb-th largest canonical
   // score lies in [T_lo - d(T_lo), T_hi + d(T_hi)]; a block is certainly kept if b - d(b)
   // exceeds the upper end and certainly dropped if b + d(b) is below the lower end.  hi and lo
   // solve those two conditions for b.
   uint32_t keepbits = 0, bandbits = 0;
-  if (bf16_row) {
-    // ---- bf16 rows: the 16-bit order-preserving keys of a pair of scores share a word (score
-    // 2m in the low half, 2m + 1 in the high half), and two passes of 8-bit digits resolve the
-    // kb-th largest key exactly, so the threshold is one bf16 value T.
-    static_assert(E % 8 == 0, "a thread's bf16 scores are whole 16-byte words");
+  if (f16_row) {
+    // ---- matrix-core rows: the row's scores are fp16 values h (score h * 2^erow), worked on
+    // in these scaled units.  The 16-bit order-preserving keys of a pair of scores share a word
+    // (score 2m in the low half, 2m + 1 in the high half), and two passes of 8-bit digits
+    // resolve the kb-th largest key exactly, so the threshold is one fp16 value T.
+    static_assert(E % 8 == 0, "a thread's fp16 scores are whole 16-byte words");
     constexpr int E2 = E / 2;
     uint32_t rw[E2], kp[E2];
+    const int erow = P.lexp[wrow];
     const uint16_t* lb = reinterpret_cast<const uint16_t*>(lg);
 #pragma unroll
     for (int i = 0; i < E; i += 8) {
@@ -489,11 +494,18 @@ void topk_kernel(SelectParams P) {
     lds_barrier();
     const uint32_t key16 = (d0 << 8) | (uint32_t)scan256(hist[1], krem);
     const uint32_t tb = (key16 & 0x8000u) ? (key16 ^ 0x8000u) : (key16 ^ 0xFFFFu);
-    const double T = (double)__uint_as_float(tb << 16);  // the kb-th largest fast score
+    auto f16f = [](uint32_t bits) {
+      return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+    };
+    const double T = (double)f16f(tb);  // the kb-th largest fast score, scaled
     bounds();
-    const double rr = 0x1p-8 * (1.0 + 0x1p-20);
-    const double x = T + rr * fabs(T) + 2.0 * Ebound;   // b - r|b| must exceed x
-    const double y = T - rr * fabs(T) - 2.0 * Ebound;   // b + r|b| must reach y
+    // A stored value h stands for fast scores within 2^-11 |h| of it (rounding to nearest; a
+    // subnormal one within 2^-14, however the conversions treat subnormals), and the fast
+    // score for canonical scores within Ebound, which is 2^-erow of it in these units.
+    const double rr = 0x1p-11 * (1.0 + 0x1p-20);
+    const double Es = __builtin_amdgcn_ldexp(Ebound, -erow) + 0x1p-14;
+    const double x = T + rr * fabs(T) + 2.0 * Es;   // b - r|b| must exceed x
+    const double y = T - rr * fabs(T) - 2.0 * Es;   // b + r|b| must reach y
     const double bh = x >= 0.0 ? x / (1.0 - rr) : x / (1.0 + rr);
     const double bl = y >= 0.0 ? y / (1.0 + rr) : y / (1.0 - rr);
     const float hi = round_up_f32(bh + fabs(bh) * 0x1p-40 + 1e-30);
@@ -501,7 +513,7 @@ void topk_kernel(SelectParams P) {
     // ---- classify (invisible scores are neither kept nor in the band)
 #pragma unroll
     for (int m = 0; m < E2; ++m) {
-      const float f0 = __uint_as_float(rw[m] << 16), f1 = __uint_as_float(rw[m] & 0xFFFF0000u);
+      const float f0 = f16f(rw[m] & 0xFFFFu), f1 = f16f(rw[m] >> 16);
       const bool v0 = 2 * m < nv, v1 = 2 * m + 1 < nv;
       keepbits |= (v0 && f0 > hi ? 1u : 0u) << (2 * m);
       keepbits |= (v1 && f1 > hi ? 1u : 0u) << (2 * m + 1);
@@ -588,7 +600,7 @@ void topk_kernel(SelectParams P) {
       bandbits |= (sc[i] <= hi && sc[i] >= lo ? 1u : 0u) << i;
     }
   }
-  const bool mfma_row = bf16_row;
+  const bool mfma_row = f16_row;
   const int32_t* cbt_row = cbt_in_lds ? cbt_s : P.cbt + (int64_t)r * P.cbt_stride;
 
   // ---- collect the band in block order: one workgroup scan of the per-thread counts (band

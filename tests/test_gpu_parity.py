@@ -352,7 +352,7 @@ def test_exact_ties_go_to_the_lower_block():
 
 
 def test_exact_ties_on_matrix_core_rows():
-    """Rows scored on the matrix cores (stored as bf16, certified with the rounding bound):
+    """Rows scored on the matrix cores (stored as fp16, certified with the rounding bound):
     every compressed row of the pre-state is the same key, so the visible blocks tie exactly
     and the lower block index decides; one call takes the decode top-k configuration (fewer
     than 1024 rows), the other the prefill one."""
@@ -375,6 +375,24 @@ def test_exact_ties_on_fp8_matrix_core_rows():
     ref = oracle_step(wl, with_attention=False)
     st = run_gpu(wl)
     assert np.array_equal(to_np(st.packed), ref.packed)
+
+
+@pytest.mark.parametrize("w", [1023.0, 65535.0])
+def test_matrix_core_rows_with_scaled_fp16_logits(w):
+    """Matrix-core logits are stored as fp16 scaled by 2^-e per row (e from kappa * A).
+    Indexer norm weights of w make the scores far exceed the fp16 range (|q . k| ~ 1e4 .. 1e9;
+    e = 7 and more), and the selection must still be the oracle's, in the decode (fewer than
+    1024 rows) and the prefill top-k configurations."""
+    for rows in (100, 600):
+        wl = workload("chunked_prefill", num_requests=2, lengths=("fixed", 3000), rows=rows)
+        wl.q_norm_w.fill_(w)
+        wl.k_norm_w.fill_(w)
+        log(f"scaled fp16 logits: w={w} T={wl.num_tokens}")
+        ref = oracle_step(wl, with_attention=False)
+        st = run_gpu(wl)
+        packed = to_np(st.packed)
+        assert np.array_equal(packed, ref.packed), (
+            f"{int((packed != ref.packed).any(axis=1).sum())} rows differ")
 
 
 def test_inert_rows_invalid_entries_and_empty_requests():
