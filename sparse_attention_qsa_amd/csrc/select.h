@@ -8,6 +8,7 @@ namespace qsa {
 
 struct SelectParams {
   int T, R, Hi, c, budget, Pc, c_pages, cbt_stride, cbt_width, cols, col_stride, key_tiles;
+  int c_log2;         // log2(c) (c is a power of two)
   int key_blocks;     // 128-key blocks per request in the kmax array
   int mfma_min_rows;  // requests with more rows than this are scored by the MFMA kernel
   int row_lo, row_hi;  // the rows of this launch (a window under a logits memory cap); the

@@ -40,6 +40,7 @@ hipError_t launch_topk(const qsa_topk_args& a, const TopkLayout& L, char* ws, hi
   P.R = a.num_requests;
   P.Hi = a.num_index_heads;
   P.c = a.compress_ratio;
+  P.c_log2 = __builtin_ctz((unsigned)a.compress_ratio);
   P.budget = a.budget;
   P.Pc = a.c_page_size;
   P.c_pages = a.c_pages;

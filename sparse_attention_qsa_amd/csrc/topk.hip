@@ -339,13 +339,15 @@ void topk_kernel(SelectParams P) {
     int4* h4 = reinterpret_cast<int4*>(&hist[0][0]);
     for (int i = tid; i < 2 * kRadixBins / 4; i += NT) h4[i] = make_int4(0, 0, 0, 0);
   }
-  const int any_mine = __syncthreads_or(mine);
+  // The request's values are the same for every thread: read into scalar registers, so that
+  // the arithmetic on them below runs on the scalar unit.
+  const int any_mine = __builtin_amdgcn_readfirstlane(__syncthreads_or(mine));
   int p = -1, L = 0, n_req = 0, r = -1;
   if (any_mine) {
-    r = s_int[0];
-    n_req = s_int[2];
-    L = s_int[3];
-    if (L - n_req >= 0) p = L - n_req + (row - s_int[1]);
+    r = __builtin_amdgcn_readfirstlane(s_int[0]);
+    n_req = __builtin_amdgcn_readfirstlane(s_int[2]);
+    L = __builtin_amdgcn_readfirstlane(s_int[3]);
+    if (L - n_req >= 0) p = L - n_req + (row - __builtin_amdgcn_readfirstlane(s_int[1]));
   }
   if (p < 0) {  // inert row: no entries, count 0
     for (int col = tid; col <= W; col += NT) out[col] = col < W ? -1 : 0;
@@ -353,7 +355,7 @@ void topk_kernel(SelectParams P) {
   }
   // seq_lens beyond the max_seq_len the workspace was sized for would overrun the logits
   // row: such rows are clamped (their selection is then undefined but stays in bounds).
-  const int vis = min((p + 1) / P.c, P.cols);
+  const int vis = min((p + 1) >> P.c_log2, P.cols);  // c is a power of two
   const int tail = min(p + 1 - vis * P.c, P.c - 1);
   if (vis <= kb) {  // every visible block: tokens 0..vis*c+tail-1
     const int cnt = vis * P.c + tail;
@@ -364,7 +366,7 @@ void topk_kernel(SelectParams P) {
   // blocks (for the error bound) and its block-table row (for the band's key rows).
   float km = 0.0f;
   {
-    const int nt = min(P.key_blocks, (min(L / P.c, P.cols) + 127) / 128);
+    const int nt = min(P.key_blocks, (min(L >> P.c_log2, P.cols) + 127) / 128);
     for (int t = tid; t < nt; t += NT) km = fmaxf(km, P.kmax[(int64_t)r * P.key_blocks + t]);
   }
   const int cw = min(P.cbt_width, (vis + P.Pc - 1) / P.Pc);
@@ -474,8 +476,8 @@ void topk_kernel(SelectParams P) {
         s_int[5] = kr - above;
       }
       lds_barrier();
-      kr = s_int[5];
-      return s_int[4];
+      kr = __builtin_amdgcn_readfirstlane(s_int[5]);
+      return __builtin_amdgcn_readfirstlane(s_int[4]);
     };
     int krem = kb;
 #pragma unroll
@@ -502,12 +504,15 @@ void topk_kernel(SelectParams P) {
     // A stored value h stands for fast scores within 2^-11 |h| of it (rounding to nearest; a
     // subnormal one within 2^-14, however the conversions treat subnormals), and the fast
     // score for canonical scores within Ebound, which is 2^-erow of it in these units.
-    const double rr = 0x1p-11 * (1.0 + 0x1p-20);
+    constexpr double rr = 0x1p-11 * (1.0 + 0x1p-20);
+    // x / (1 -+ rr) as products with the rounded reciprocals (within 2^-52 of the quotients,
+    // far inside the 2^-40 widening below).
+    constexpr double kInvLo = 1.0 / (1.0 - rr), kInvHi = 1.0 / (1.0 + rr);
     const double Es = __builtin_amdgcn_ldexp(Ebound, -erow) + 0x1p-14;
     const double x = T + rr * fabs(T) + 2.0 * Es;   // b - r|b| must exceed x
     const double y = T - rr * fabs(T) - 2.0 * Es;   // b + r|b| must reach y
-    const double bh = x >= 0.0 ? x / (1.0 - rr) : x / (1.0 + rr);
-    const double bl = y >= 0.0 ? y / (1.0 + rr) : y / (1.0 - rr);
+    const double bh = x * (x >= 0.0 ? kInvLo : kInvHi);
+    const double bl = y * (y >= 0.0 ? kInvHi : kInvLo);
     const float hi = round_up_f32(bh + fabs(bh) * 0x1p-40 + 1e-30);
     const float lo = round_down_f32(bl - fabs(bl) * 0x1p-40 - 1e-30);
     // ---- classify (invisible scores are neither kept nor in the band)
@@ -583,9 +588,9 @@ void topk_kernel(SelectParams P) {
         }
       }
       lds_barrier();
-      prefix |= (uint32_t)s_int[4] << shift;
+      prefix |= (uint32_t)__builtin_amdgcn_readfirstlane(s_int[4]) << shift;
       pmask |= (uint32_t)(kRadixBins - 1) << shift;
-      krem = s_int[5];
+      krem = __builtin_amdgcn_readfirstlane(s_int[5]);
     }
     // The kb-th largest fast score lies in [T_lo, T_hi], the values of the keys with this
     // prefix.
@@ -615,6 +620,7 @@ void topk_kernel(SelectParams P) {
     cl_off += i < w ? s_wave[i] : 0;
     tot += s_wave[i];
   }
+  tot = __builtin_amdgcn_readfirstlane(tot);  // the same in every thread
   int need = kb - (tot >> 16);
   int nb = tot & 0xFFFF;
   const bool in_lds = nb <= kBandCap;
@@ -672,7 +678,7 @@ void topk_kernel(SelectParams P) {
       }
     }
     need -= block_sum<NT>(n_in2_local, s_wave);  // its barriers also publish band2
-    nb = s_int[6];
+    nb = __builtin_amdgcn_readfirstlane(s_int[6]);
     band = band2;
   }
 
@@ -733,7 +739,7 @@ void topk_kernel(SelectParams P) {
     pos += i < w ? s_wave[i] : 0;
     total += s_wave[i];
   }
-  const int sel = min(total, kb), count = sel * P.c + tail;
+  const int sel = min(__builtin_amdgcn_readfirstlane(total), kb), count = sel * P.c + tail;
   // The selected blocks in order go to LDS (the band's score array is free now), and the row
   // is written with coalesced stores; a list too long for it is expanded in place.
   constexpr int kListCap = kBandCap * 2;  // int32 entries in band_score_s
@@ -752,10 +758,20 @@ void topk_kernel(SelectParams P) {
   if (list_in_lds) {
     lds_barrier();
     // Block b's c tokens by thread b (mod NT), then the tail, the padding and the count.
-    for (int b = tid; b < sel; b += NT) {
-      const int t0 = list[b] * P.c;
-      int32_t* o = out + b * P.c;
-      for (int m = 0; m < P.c; ++m) o[m] = t0 + m;
+    // With c a multiple of 4 on a 16-byte aligned row a block is c / 4 16-byte stores.
+    if ((P.c & 3) == 0 && ((uintptr_t)out & 15u) == 0) {  // block-uniform
+      for (int b = tid; b < sel; b += NT) {
+        const int t0 = list[b] * P.c;
+        int4* o = reinterpret_cast<int4*>(out + b * P.c);
+        for (int q = 0; q < (P.c >> 2); ++q)
+          o[q] = make_int4(t0 + 4 * q, t0 + 4 * q + 1, t0 + 4 * q + 2, t0 + 4 * q + 3);
+      }
+    } else {
+      for (int b = tid; b < sel; b += NT) {
+        const int t0 = list[b] * P.c;
+        int32_t* o = out + b * P.c;
+        for (int m = 0; m < P.c; ++m) o[m] = t0 + m;
+      }
     }
     for (int col = sel * P.c + tid; col <= W; col += NT)
       out[col] = col < count ? vis * P.c + (col - sel * P.c) : (col < W ? -1 : count);
