@@ -703,8 +703,62 @@ void topk_kernel(SelectParams P) {
   }
   if (in_lds) lds_barrier(); else __syncthreads();
 
-  // ---- rank the band: keep its `need` best by (score desc, block asc).  A 16-lane group per
-  // entry, each lane comparing against every 16th entry, the counts summed on DPP.
+  // ---- rank the band: keep its `need` best by (score desc, block asc).
+  constexpr int kRankRadixMin = 256;
+  if (need > 0 && nb > kRankRadixMin) {  // block-uniform
+    // A large band (many exact ties, e.g. an all-zero cache): the need-th best entry by a radix
+    // select over the 96-bit key (order-preserving float64 score, then the complemented block
+    // index), eight bits per pass; then every entry at or above it is kept.  A score of -0 is
+    // keyed as +0: equal scores tie whatever their sign.
+    auto dkey = [](double x) {
+      const uint64_t u = (uint64_t)__double_as_longlong(x == 0.0 ? 0.0 : x);
+      return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+    };
+    uint64_t pre_hi = 0, msk_hi = 0;
+    uint32_t pre_lo = 0, msk_lo = 0;
+    int kr = need;
+    int* h = hist[0];
+    for (int pass = 0; pass < 12; ++pass) {
+      for (int i = tid; i < 256; i += NT) h[i] = 0;
+      lds_barrier();
+      const int sh = pass < 8 ? 56 - 8 * pass : 24 - 8 * (pass - 8);
+      for (int b = tid; b < nb; b += NT) {
+        const uint64_t kh = dkey(bscore[b]);
+        const uint32_t kl = ~(uint32_t)band[b];
+        if ((kh & msk_hi) == pre_hi && (kl & msk_lo) == pre_lo)
+          atomicAdd(&h[pass < 8 ? (uint32_t)(kh >> sh) & 0xFFu : (kl >> sh) & 0xFFu], 1);
+      }
+      lds_barrier();
+      const int S = tid < 256 ? h[255 - tid] : 0;  // thread t owns bin 255 - t
+      const int incl = wave_incl_scan(S);
+      if (lane == 63) s_wave[w] = incl;
+      lds_barrier();
+      int above = incl - S;
+      for (int i = 0; i < w; ++i) above += s_wave[i];
+      if (above < kr && kr <= above + S) {
+        s_int[4] = 255 - tid;
+        s_int[5] = kr - above;
+      }
+      lds_barrier();
+      const uint32_t d = (uint32_t)__builtin_amdgcn_readfirstlane(s_int[4]);
+      kr = __builtin_amdgcn_readfirstlane(s_int[5]);
+      if (pass < 8) {
+        pre_hi |= (uint64_t)d << sh;
+        msk_hi |= 0xFFull << sh;
+      } else {
+        pre_lo |= d << sh;
+        msk_lo |= 0xFFu << sh;
+      }
+    }
+    for (int b = tid; b < nb; b += NT) {
+      const uint64_t kh = dkey(bscore[b]);
+      const int j = band[b];
+      if (kh > pre_hi || (kh == pre_hi && ~(uint32_t)j >= pre_lo))
+        atomicOr(&sel_mask[j >> 5], 1u << (j & 31));
+    }
+  } else {
+  // A 16-lane group per entry, each lane comparing against every 16th entry, the counts
+  // summed on DPP.
   for (int b0 = 0; b0 < nb; b0 += groups) {
     if (b0 + 4 * w >= nb) break;  // wave-uniform, as in the re-scoring
     const int b = b0 + grp;
@@ -723,6 +777,7 @@ void topk_kernel(SelectParams P) {
     rank += __builtin_amdgcn_update_dpp(0, rank, 0x102, 0xF, 0xF, false);  // row_shl:2
     rank += __builtin_amdgcn_update_dpp(0, rank, 0x101, 0xF, 0xF, false);  // row_shl:1
     if (live && l16 == 0 && rank < need) atomicOr(&sel_mask[jbb >> 5], 1u << (jbb & 31));
+  }
   }
   lds_barrier();
 

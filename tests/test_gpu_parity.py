@@ -351,6 +351,25 @@ def test_exact_ties_go_to_the_lower_block():
     assert np.array_equal(to_np(st.packed), ref.packed)
 
 
+@pytest.mark.parametrize("base,kw", [
+    ("decode_32k", dict(num_requests=3, lengths=("fixed", 5000))),
+    ("chunked_prefill", dict(num_requests=2, lengths=("fixed", 3000), rows=600)),
+])
+def test_all_zero_keys_tie_whatever_the_sign_of_zero(base, kw):
+    """An all-zero compressed cache (the step's own groups aside): the canonical scores of
+    the visible blocks are +0 or -0 (a product with a negative query element is -0), which
+    tie exactly, so the lower blocks win.  The band is every visible block, which the top-k
+    ranks by a radix select over (score, block) rather than by pairwise comparison."""
+    wl = workload(base, **kw)
+    wl.ckv.zero_()
+    log(f"all-zero keys: {base} T={wl.num_tokens}")
+    ref = oracle_step(wl, with_attention=False)
+    st = run_gpu(wl)
+    packed = to_np(st.packed)
+    assert np.array_equal(packed, ref.packed), (
+        f"{int((packed != ref.packed).any(axis=1).sum())} rows differ")
+
+
 def test_exact_ties_on_matrix_core_rows():
     """Rows scored on the matrix cores (stored as fp16, certified with the rounding bound):
     every compressed row of the pre-state is the same key, so the visible blocks tie exactly
