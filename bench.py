@@ -621,8 +621,10 @@ def main():
         if windows and fn in ("logits", "block_topk"):
             continue    # the split top-k calls take one window only (the combined call is timed)
         per_kernel[k] = timed(fn)
-    if steps[0].num_splits == 1:
-        per_kernel.pop("gqa_merge_kernel")           # not launched with one split
+    # The merge kernel runs only with several splits that are not merged in the workgroup.
+    merge_kernel = B.lib().qsa_sparse_gqa_merge_kernel(ctypes.byref(steps[0].g_args)) == 1
+    if not merge_kernel:
+        per_kernel.pop("gqa_merge_kernel")
 
     graph_leg = None
     if args.graph:
@@ -674,6 +676,8 @@ def main():
         del plain
 
     alg, alg_k, kv_tokens = algorithmic_bytes(wl0, steps[0].packed)
+    if not merge_kernel:   # the attention kernel also reads the gate and writes the output
+        alg_k["gqa_partial_kernel"] += alg_k.pop("gqa_merge_kernel")
     mfma_flop, mfma_flop_per_head = mfma_logits_flop(wl0, args.index_agg)
     if mfma_flop:
         # The logits call also launches the matrix-core kernel: name the entry for both (the
@@ -711,7 +715,8 @@ def main():
                    "main_prepare": bool(args.main_prepare), "index_agg": args.index_agg,
                    "max_logits_mb": args.max_logits_mb, "row_tiles": bool(args.row_tiles),
                    "topk_workspace_mb": round(steps[0].t_ws.numel() / 2**20, 1),
-                   "gqa_splits": steps[0].num_splits},
+                   "gqa_splits": steps[0].num_splits,
+                   "gqa_merge_kernel": merge_kernel},
         "hbm_gbps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
         "hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "step_us": step_dist,

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 7
+#define QSA_ABI_VERSION 8
 
 typedef enum qsa_status {
   QSA_OK = 0,
@@ -256,9 +256,12 @@ qsa_status qsa_block_topk(const qsa_topk_args* args, void* workspace, size_t wor
  * packed buffer, where count is its column W; entry t maps to page block_table[req, t / P],
  * slot t % P.  Negative entries, entries whose page column or page is out of range are
  * masked.  Softmax scale = `scale` (0: head_dim^-0.5); a row with no valid entry yields 0.
- * The selection is split across `num_splits` workgroups per (row, KV head) whose float32
- * partials are merged by log-sum-exp; the sigmoid of `gate` (if not NULL) multiplies the
- * merged output; the result is written as bf16.
+ * The selection is split into `num_splits` parts per (row, KV head) whose float32 partials are
+ * merged by log-sum-exp; the sigmoid of `gate` (if not NULL) multiplies the merged output; the
+ * result is written as bf16.  With bf16 K/V and 2..8 splits (forced, or chosen automatically
+ * for 128..256 (row, KV head) pairs) the parts are the waves of one workgroup and are merged in
+ * it; otherwise each part is a workgroup and a second kernel merges their partials, which then
+ * take workspace.
  * KV cache layout: token row of KV head h on page pg starts at
  *     kv_cache + pg*kv_page_stride + h*kv_head_stride + slot*kv_token_stride
  * and holds K in its first head_dim values and V in the next head_dim (the pages' kv_cache
@@ -311,13 +314,18 @@ typedef struct qsa_gqa_args {
 
 /* Splits the call will use (after the automatic choice and clamping). */
 int32_t qsa_sparse_gqa_num_splits(const qsa_gqa_args* args);
+/* 1 if the call runs the separate merge kernel (so that qsa_sparse_gqa_merge below has work), 0
+ * if not (one split, or splits merged inside the attention workgroup), -1 for invalid
+ * arguments. */
+int32_t qsa_sparse_gqa_merge_kernel(const qsa_gqa_args* args);
 size_t qsa_sparse_gqa_workspace_size(const qsa_gqa_args* args);
 qsa_status qsa_sparse_gqa(const qsa_gqa_args* args, void* workspace, size_t workspace_bytes,
                           void* stream);
 
 /* The two kernels of qsa_sparse_gqa as separate calls (for per-kernel timing):
- * qsa_sparse_gqa_partial computes the split partials (with one split: the gated output itself),
- * qsa_sparse_gqa_merge merges them into the output (a no-op with one split).  In this order on
+ * qsa_sparse_gqa_partial computes the split partials (with one split, or splits merged in the
+ * workgroup: the gated output itself), qsa_sparse_gqa_merge merges them into the output (a
+ * no-op when qsa_sparse_gqa_merge_kernel is 0).  In this order on
  * one stream, with the same arguments and workspace, they have exactly the effect of
  * qsa_sparse_gqa. */
 qsa_status qsa_sparse_gqa_partial(const qsa_gqa_args* args, void* workspace,

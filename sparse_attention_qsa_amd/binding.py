@@ -22,6 +22,7 @@ EXPORTED = (
     "qsa_compress", "qsa_index_logits_topk", "qsa_index_logits_topk_workspace_size",
     "qsa_index_logits", "qsa_block_topk",
     "qsa_sparse_gqa", "qsa_sparse_gqa_workspace_size", "qsa_sparse_gqa_num_splits",
+    "qsa_sparse_gqa_merge_kernel",
     "qsa_sparse_gqa_partial", "qsa_sparse_gqa_merge",
     "qsa_sparse_gqa_noalloc", "qsa_sparse_gqa_noalloc_scratch_bytes",
     "qsa_diag_e4m3_decode", "qsa_diag_fp64_sqrt_div", "qsa_diag_read_bandwidth",
@@ -114,6 +115,8 @@ def lib() -> C.CDLL:
         h.qsa_sparse_gqa_workspace_size.restype = C.c_size_t
         h.qsa_sparse_gqa_num_splits.argtypes = [C.POINTER(GqaArgs)]
         h.qsa_sparse_gqa_num_splits.restype = _I32
+        h.qsa_sparse_gqa_merge_kernel.argtypes = [C.POINTER(GqaArgs)]
+        h.qsa_sparse_gqa_merge_kernel.restype = _I32
         for f in ("qsa_sparse_gqa", "qsa_sparse_gqa_partial", "qsa_sparse_gqa_merge"):
             getattr(h, f).argtypes = [C.POINTER(GqaArgs), _P, C.c_size_t, _P]
             getattr(h, f).restype = C.c_int

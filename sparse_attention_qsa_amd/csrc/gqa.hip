@@ -64,6 +64,7 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kTile = 32;        // selected tokens per tile (one MFMA K step of P.V)
 constexpr int kChunkTiles = 8;   // tiles whose cache rows are resolved together
+constexpr int kMergeWaves = 8;   // splits merged inside one workgroup (bf16 K/V)
 constexpr int kRT = 32;          // rows per tile of the row-tiled (prefill) kernel
 
 __device__ __forceinline__ void lds_dma16(const void* g, void* lds) {
@@ -89,6 +90,63 @@ __device__ __forceinline__ u32x2_t lds_read_b64_async(uint32_t addr) {
   return v;
 }
 
+// The in-workgroup merge of gqa_partial_kernel<G, F8, NW > 1>.  Wave w leaves its split's
+// normalised partial (G heads x 128 dims, float32, at po + w * po_stride) and its log-sum-exp in
+// LDS; then wave w merges heads w, w + NW, ...: lane l takes dims 2l, 2l+1 of all NW partials,
+// weights them by exp2(lse - max lse) (a split without tokens has lse -inf and weight 0), and
+// writes the gated bf16 output -- the merge kernel's arithmetic, the weights summed in split
+// order.  po must not be in use by any wave when this is called (every tile is done).
+template <int G, int NW>
+__device__ __forceinline__ void merge_in_workgroup(const GqaParams& P, int row, int kvh, int wv,
+                                                   int lane, float m, float ltot,
+                                                   const f32x4_t (&acc)[8], float* po,
+                                                   int po_stride) {
+  static_assert(G * kHeadDim * 4 <= 2 * kTile * 256, "a partial fits the wave's K/V buffers");
+  __shared__ float lse_s[NW][16];
+  const int l16 = lane & 15, g4 = lane >> 4;
+  if (l16 < G) {
+    const float inv = ltot > 0.0f ? P.v_scale / ltot : 0.0f;
+    float* mine = po + wv * po_stride + l16 * kHeadDim;
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+      *reinterpret_cast<float4*>(mine + 16 * db + 4 * g4) =
+          make_float4(acc[db][0] * inv, acc[db][1] * inv, acc[db][2] * inv, acc[db][3] * inv);
+    if (g4 == 0) lse_s[wv][l16] = ltot > 0.0f ? m + log2f(ltot) : -INFINITY;
+  }
+  __syncthreads();  // no global loads are in flight here
+  for (int h = wv; h < G; h += NW) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, lse_s[w][h]);
+    float o0 = 0.0f, o1 = 0.0f;
+    const int hq = kvh * G + h;
+    if (M != -INFINITY) {
+      float wsum = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float ls = lse_s[w][h];
+        const float wgt = ls == -INFINITY ? 0.0f : exp2f(ls - M);
+        const float2 o =
+            *reinterpret_cast<const float2*>(po + w * po_stride + h * kHeadDim + 2 * lane);
+        wsum += wgt;
+        o0 += wgt * o.x;
+        o1 += wgt * o.y;
+      }
+      const float inv = 1.0f / wsum;
+      o0 *= inv;
+      o1 *= inv;
+      if (P.gate) {
+        const uint32_t gp = reinterpret_cast<const uint32_t*>(
+            P.gate + (int64_t)row * P.g_rs + (int64_t)hq * P.g_hs)[lane];
+        o0 *= sigmoidf(bf16lo(gp));
+        o1 *= sigmoidf(bf16hi(gp));
+      }
+    }
+    reinterpret_cast<uint32_t*>(P.out + (int64_t)row * P.o_rs + (int64_t)hq * P.o_hs)[lane] =
+        (f32_to_bf16(o0) & 0xFFFFu) | (f32_to_bf16(o1) << 16);
+  }
+}
+
 // One wavefront per (row, KV head, split), ordered by XCD (below).  Both contractions run on
 // the matrix cores (v_mfma_f32_16x16x32_bf16), with the G query heads of the KV head padded
 // to the 16 columns of the instruction:
@@ -107,33 +165,45 @@ __device__ __forceinline__ u32x2_t lds_read_b64_async(uint32_t addr) {
 // converted to bf16 (exactly: every e4m3 value is a bf16 value), V's through the transposing
 // byte read ds_read_b64_tr_b8, whose 16-lane groups give lane i byte i % 8 of the reads of
 // lanes i / 8 + 2r, r < 8.  The dequantization scales act on the scores and on the output.
-template <int G, bool F8>
-__global__ __launch_bounds__(64) void gqa_partial_kernel(GqaParams P) {
+//
+// NW > 1 (bf16 K/V): a workgroup of NW waves takes one (row, KV head), wave w its split w (the
+// plan has at most NW splits); the waves' partials are merged in LDS by the workgroup, with the
+// merge kernel's arithmetic, and no merge kernel runs.
+template <int G, bool F8, int NW = 1>
+__global__ __launch_bounds__(64 * NW) void gqa_partial_kernel(GqaParams P) {
   static_assert(G <= 16, "the MFMA columns hold at most 16 heads");
+  static_assert(NW == 1 || !F8, "in-workgroup merging is built for bf16 K/V");
   constexpr int kRow = F8 ? 128 : 256;        // bytes of a token's K (or V) row
   constexpr int kLoads = kTile * kRow / 1024;  // LDS-direct loads per tile and part
   // Workgroup b runs on XCD b mod 8 (round-robin dispatch).  The work order (KV head, row,
-  // split) is cut into 8 contiguous chunks, chunk x for XCD x, so that the workgroups one XCD
-  // runs at a time share a request: rows of one request (prefill) or the verify rows of one
-  // request find the K/V rows they have in common in that XCD's L2.
-  const uint32_t total = (uint32_t)P.T * (uint32_t)(P.Hkv * P.splits);
+  // split) -- (KV head, row) with NW > 1 -- is cut into 8 contiguous chunks, chunk x for XCD x,
+  // so that the workgroups one XCD runs at a time share a request: rows of one request
+  // (prefill) or the verify rows of one request find the K/V rows they have in common in that
+  // XCD's L2.
+  const uint32_t total = (uint32_t)P.T * (uint32_t)(P.Hkv * (NW > 1 ? 1 : P.splits));
   const uint32_t chunk = (total + 7u) >> 3;
   const uint32_t wi = (blockIdx.x & 7u) * chunk + (blockIdx.x >> 3);
-  if (wi >= total) return;  // the grid is 8 * chunk >= total
-  const int split = (int)(wi % (uint32_t)P.splits);
-  const uint32_t rk = wi / (uint32_t)P.splits;
+  if (wi >= total) return;  // the grid is 8 * chunk >= total (workgroup-uniform)
+  const int wv = NW > 1 ? (int)(threadIdx.x >> 6) : 0;  // this wave's buffers
+  const int split = NW > 1 ? wv : (int)(wi % (uint32_t)P.splits);
+  const uint32_t rk = NW > 1 ? wi : wi / (uint32_t)P.splits;
   const int row = (int)(rk % (uint32_t)P.T), kvh = (int)(rk / (uint32_t)P.T);
   if (P.rt_flags != nullptr) {  // rows the row-tiled kernel already wrote
     const int ntiles = P.T / kRT;
     if (row / kRT < ntiles && P.rt_flags[(int64_t)kvh * ntiles + row / kRT] != 0) return;
   }
-  const int lane = threadIdx.x, l16 = lane & 15, g4 = lane >> 4;
-  __shared__ __attribute__((aligned(16))) uint8_t kt[kTile * kRow];
-  __shared__ __attribute__((aligned(16))) uint8_t vt[kTile * kRow];
-  // Resolved cache rows (16-byte offsets) of the chunk's tiles: token 4i + q of tile k at
-  // offs[k * 32 + 8q + i], so that lane group q's 8 rows are contiguous; and validity masks.
-  __shared__ __attribute__((aligned(16))) uint32_t offs[kChunkTiles * kTile];
-  __shared__ uint32_t vms[kChunkTiles];
+  const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
+  // Per wave: the K and V tiles (kt, vt: one buffer, so that the merge can reuse it for the
+  // wave's partial), the resolved cache rows (16-byte offsets) of the chunk's tiles -- token
+  // 4i + q of tile k at offs[k * 32 + 8q + i], so that lane group q's 8 rows are contiguous --
+  // and the tiles' validity masks.
+  __shared__ __attribute__((aligned(16))) uint8_t kv_s[NW][2 * kTile * kRow];
+  __shared__ __attribute__((aligned(16))) uint32_t offs_s[NW][kChunkTiles * kTile];
+  __shared__ uint32_t vms_s[NW][kChunkTiles];
+  uint8_t* const kt = kv_s[wv];
+  uint8_t* const vt = kv_s[wv] + kTile * kRow;
+  uint32_t* const offs = offs_s[wv];
+  uint32_t* const vms = vms_s[wv];
 
   // The split's tile range comes from the packed width, so that its first index loads need
   // not wait for the count: the count, the request and the first chunk's entries are read in
@@ -415,6 +485,11 @@ __global__ __launch_bounds__(64) void gqa_partial_kernel(GqaParams P) {
   // ---- epilogue: lanes with l16 < G hold head l16, dims 16 db + 4 g4 + e.
   const float ltot = lsum + __shfl_xor(lsum, 16, kWave) + __shfl_xor(lsum, 32, kWave) +
                      __shfl_xor(__shfl_xor(lsum, 16, kWave), 32, kWave);
+  if constexpr (NW > 1) {
+    merge_in_workgroup<G, NW>(P, row, kvh, wv, lane, m, ltot, acc,
+                              reinterpret_cast<float*>(kv_s), 2 * kTile * kRow / 4);
+    return;
+  }
   if (l16 >= G) return;
   const int hq = kvh * G + l16;
   const float inv = ltot > 0.0f ? P.v_scale / ltot : 0.0f;
@@ -842,11 +917,17 @@ __global__ __launch_bounds__(64) void gqa_merge_kernel(GqaParams P) {
 }
 
 template <int G>
-hipError_t launch_partial(const GqaParams& P, bool f8, hipStream_t s) {
-  // A 1-D grid of 8 * ceil(T * Hkv * splits / 8) workgroups, mapped onto the work by XCD.
-  const uint64_t total = (uint64_t)P.T * P.Hkv * P.splits;
+hipError_t launch_partial(const GqaParams& P, bool f8, bool in_wg, hipStream_t s) {
+  // A 1-D grid of 8 * ceil(T * Hkv * splits / 8) workgroups (in-workgroup merge: 8 *
+  // ceil(T * Hkv / 8) workgroups of kMergeWaves waves), mapped onto the work by XCD.
+  const uint64_t total = (uint64_t)P.T * P.Hkv * (in_wg ? 1 : P.splits);
   if (total > 0xFFFFFFF0ull) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((total + 7) / 8 * 8));
+  if (in_wg) {
+    hipLaunchKernelGGL((gqa_partial_kernel<G, false, kMergeWaves>), grid, dim3(64 * kMergeWaves),
+                       0, s, P);
+    return hipGetLastError();
+  }
   if (f8)
     hipLaunchKernelGGL((gqa_partial_kernel<G, true>), grid, dim3(64), 0, s, P);
   else
@@ -887,21 +968,32 @@ GqaPlan gqa_plan(const qsa_gqa_args& a) {
   p.tiles = (a.packed_width + kTile - 1) / kTile;
   if (p.tiles < 1) p.tiles = 1;
   int target = a.num_splits;
+  const bool bf16 = a.kv_dtype != QSA_DTYPE_FP8_E4M3;
+  const int64_t units = (int64_t)a.num_tokens * a.num_kv_heads;  // (row, KV head) pairs
+  bool in_wg = bf16 && target > 1 && target <= kMergeWaves;      // forced: 2..8 splits
   if (target <= 0) {
     // Workgroups to aim for, measured on the decode workloads: with bf16 K/V about 768 (three
     // per CU), each split then gathering ~11 tiles of 16 KiB, so that its two dependent
     // round trips before the first gather are amortised; with fp8 K/V (half the bytes per
     // token) about 2048.  More waves than that queue behind the HBM without adding bandwidth.
-    const int64_t base = (int64_t)a.num_tokens * a.num_kv_heads;
-    const int64_t want = a.kv_dtype == QSA_DTYPE_FP8_E4M3 ? 2048 : 768;
-    target = base >= want ? 1 : (int)((want + base - 1) / base);
+    const int64_t want = bf16 ? 768 : 2048;
+    target = units >= want ? 1 : (int)((want + units - 1) / units);
+    // bf16 K/V with 128..256 units: one workgroup of 8 waves per unit, one split per wave,
+    // merged in the workgroup (no partials in memory, no merge kernel).  Measured against the
+    // split-K plan above on decode batches of 32k-token requests: 128 units 35.9 -> 35.5 us,
+    // 192 units 49.5 -> 43.2 us, 256 units (fp8 indexer) 59.5 -> 56.2 us; with fewer units
+    // the chip is too empty (64 units: 20.2 -> 28.6 us), with more the workgroups (one per CU:
+    // their K/V buffers take 137 KiB of LDS) no longer fit in one round (320 units: 72 -> 84).
+    in_wg = bf16 && units >= 128 && units <= 256 && target > 1;
+    if (in_wg) target = kMergeWaves;
   }
   if (target > p.tiles) target = p.tiles;
   if (target > kMergeMax) target = kMergeMax;  // the merge reads one split per lane
   p.tiles_per_split = (p.tiles + target - 1) / target;
   p.splits = (p.tiles + p.tiles_per_split - 1) / p.tiles_per_split;
+  p.merge_in_wg = in_wg && p.splits > 1;
   p.ws_bytes = 0;
-  if (p.splits > 1) {
+  if (p.splits > 1 && !p.merge_in_wg) {
     const size_t n = (size_t)p.splits * a.num_tokens * a.num_q_heads;
     p.ws_bytes = (n * kHeadDim * sizeof(float) + 255) / 256 * 256 + n * sizeof(float);
   }
@@ -956,7 +1048,7 @@ hipError_t launch_gqa(const qsa_gqa_args& a, const GqaPlan& plan, char* ws, hipS
   P.o_rs = a.out_row_stride;
   P.o_hs = a.out_head_stride;
   size_t used = 0;
-  if (plan.splits > 1) {
+  if (plan.splits > 1 && !plan.merge_in_wg) {
     const size_t n = (size_t)plan.splits * a.num_tokens * a.num_q_heads;
     P.part_o = reinterpret_cast<float*>(ws);
     P.part_lse = reinterpret_cast<float*>(ws + (n * kHeadDim * sizeof(float) + 255) / 256 * 256);
@@ -967,7 +1059,7 @@ hipError_t launch_gqa(const qsa_gqa_args& a, const GqaPlan& plan, char* ws, hipS
                    : nullptr;
   hipError_t e = hipSuccess;
   if (phase == Phase::kSecond) {  // the merge alone (nothing to merge with one split)
-    if (plan.splits == 1) return hipSuccess;
+    if (plan.splits == 1 || plan.merge_in_wg) return hipSuccess;
     hipLaunchKernelGGL(gqa_merge_kernel, dim3(P.T, P.Hq), dim3(64), 0, s, P);
     return hipGetLastError();
   }
@@ -976,14 +1068,14 @@ hipError_t launch_gqa(const qsa_gqa_args& a, const GqaPlan& plan, char* ws, hipS
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   switch (a.num_q_heads / a.num_kv_heads) {
-    case 1: e = launch_partial<1>(P, f8, s); break;
-    case 2: e = launch_partial<2>(P, f8, s); break;
-    case 4: e = launch_partial<4>(P, f8, s); break;
-    case 8: e = launch_partial<8>(P, f8, s); break;
-    case 16: e = launch_partial<16>(P, f8, s); break;
+    case 1: e = launch_partial<1>(P, f8, plan.merge_in_wg, s); break;
+    case 2: e = launch_partial<2>(P, f8, plan.merge_in_wg, s); break;
+    case 4: e = launch_partial<4>(P, f8, plan.merge_in_wg, s); break;
+    case 8: e = launch_partial<8>(P, f8, plan.merge_in_wg, s); break;
+    case 16: e = launch_partial<16>(P, f8, plan.merge_in_wg, s); break;
     default: return hipErrorInvalidValue;
   }
-  if (e != hipSuccess || plan.splits == 1 || phase == Phase::kFirst) return e;
+  if (e != hipSuccess || plan.splits == 1 || plan.merge_in_wg || phase == Phase::kFirst) return e;
   hipLaunchKernelGGL(gqa_merge_kernel, dim3(P.T, P.Hq), dim3(64), 0, s, P);
   return hipGetLastError();
 }

@@ -247,6 +247,12 @@ int32_t qsa_sparse_gqa_num_splits(const qsa_gqa_args* a) {
   return qsa::gqa_plan(*a).splits;
 }
 
+int32_t qsa_sparse_gqa_merge_kernel(const qsa_gqa_args* a) {
+  if (validate_gqa(a) != QSA_OK) return -1;
+  const qsa::GqaPlan p = qsa::gqa_plan(*a);
+  return p.splits > 1 && !p.merge_in_wg ? 1 : 0;
+}
+
 size_t qsa_sparse_gqa_workspace_size(const qsa_gqa_args* a) {
   if (validate_gqa(a) != QSA_OK) return 0;
   return qsa::gqa_plan(*a).ws_bytes;

@@ -44,9 +44,10 @@ TopkLayout topk_layout(const qsa_topk_args& a);
 
 struct GqaPlan {
   int32_t tiles;        // ceil(W / 32)
-  int32_t splits;       // workgroups per (row, KV head)
+  int32_t splits;       // parts per (row, KV head): workgroups, or waves of one workgroup
   int32_t tiles_per_split;
-  size_t ws_bytes;      // partial outputs + lse when splits > 1, row-tile flags
+  bool merge_in_wg;     // the splits are the waves of one workgroup and merged there
+  size_t ws_bytes;      // partial outputs + lse when a merge kernel runs, row-tile flags
   int32_t row_tiles;    // tiles of the row-tiled prefill kernel (0: not used)
 };
 

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(B.EXPORTED)
-    assert lib.qsa_abi_version() == 7
+    assert lib.qsa_abi_version() == 8
     assert lib.qsa_status_string(3) == b"QSA_ERR_WORKSPACE_TOO_SMALL"
 
 
@@ -89,17 +89,32 @@ def _topk(**over):
 def test_split_plan_and_workspace_sizes():
     lib = B.lib()
     a = _gqa()
-    # 65 tiles of 32 tokens; 128 (row, KV head) units -> 768 / 128 = 6 splits wanted -> 11
-    # tiles each -> 6 splits.
-    assert lib.qsa_sparse_gqa_num_splits(C.byref(a)) == 6
-    assert lib.qsa_sparse_gqa_workspace_size(C.byref(a)) >= 6 * 64 * 16 * 128 * 4
+    # 65 tiles of 32 tokens; 128 (row, KV head) units of bf16 K/V: one workgroup of 8 waves per
+    # unit, 8 splits of 9 tiles merged in the workgroup (no partials, no merge kernel).
+    assert lib.qsa_sparse_gqa_num_splits(C.byref(a)) == 8
+    assert lib.qsa_sparse_gqa_merge_kernel(C.byref(a)) == 0
+    assert lib.qsa_sparse_gqa_workspace_size(C.byref(a)) == 0
+    # 64 units: 768 / 64 = 12 splits wanted -> 6 tiles each -> 11 splits, merged by the merge
+    # kernel from partials in the workspace.
+    half = _gqa(num_tokens=32)
+    assert lib.qsa_sparse_gqa_num_splits(C.byref(half)) == 11
+    assert lib.qsa_sparse_gqa_merge_kernel(C.byref(half)) == 1
+    assert lib.qsa_sparse_gqa_workspace_size(C.byref(half)) >= 11 * 32 * 16 * 128 * 4
+    # 384 units: 2 splits, two kernels; a forced 4 splits are merged in the workgroup.
+    assert lib.qsa_sparse_gqa_num_splits(C.byref(_gqa(num_tokens=192))) == 2
+    assert lib.qsa_sparse_gqa_merge_kernel(C.byref(_gqa(num_tokens=192))) == 1
+    assert lib.qsa_sparse_gqa_merge_kernel(C.byref(_gqa(num_tokens=192, num_splits=4))) == 0
+    assert lib.qsa_sparse_gqa_merge_kernel(C.byref(_gqa(num_splits=9))) == 1
+    assert lib.qsa_sparse_gqa_merge_kernel(C.byref(_gqa(head_dim=64))) == -1
     # fp8 K/V: 2048 / 128 = 16 splits wanted -> 5 tiles each -> 13 splits.
     f8 = _gqa(kv_dtype=1, kv_page_stride=2 * 16 * 256, kv_head_stride=16 * 256,
               kv_token_stride=256)
     assert lib.qsa_sparse_gqa_num_splits(C.byref(f8)) == 13
+    assert lib.qsa_sparse_gqa_merge_kernel(C.byref(f8)) == 1
     one = _gqa(num_splits=1)
     assert lib.qsa_sparse_gqa_num_splits(C.byref(one)) == 1
     assert lib.qsa_sparse_gqa_workspace_size(C.byref(one)) == 0
+    assert lib.qsa_sparse_gqa_merge_kernel(C.byref(one)) == 0
     big = _gqa(num_tokens=4096)
     assert lib.qsa_sparse_gqa_num_splits(C.byref(big)) == 1
     t = _topk()
@@ -135,7 +150,7 @@ def test_invalid_calls_are_rejected_before_any_launch():
     assert lib.qsa_sparse_gqa(C.byref(_gqa(q=None)), None, 0, None) == INVAL
     assert lib.qsa_sparse_gqa(C.byref(_gqa(kv_token_stride=100)), None, 0, None) == INVAL
     assert lib.qsa_sparse_gqa(C.byref(_gqa(packed_row_stride=2051)), None, 0, None) == INVAL
-    assert lib.qsa_sparse_gqa(C.byref(_gqa()), None, 0, None) == SMALL      # needs partials
+    assert lib.qsa_sparse_gqa(C.byref(_gqa(num_tokens=32)), None, 0, None) == SMALL  # partials
     assert lib.qsa_sparse_gqa(C.byref(_gqa(num_tokens=0)), None, 0, None) == 0
     # fp8 main KV: a known dtype, finite non-negative scales, 16-byte strides in bytes.
     assert lib.qsa_sparse_gqa(C.byref(_gqa(kv_dtype=5)), None, 0, None) == NOTSUP
@@ -163,7 +178,7 @@ def test_invalid_calls_are_rejected_before_any_launch():
     assert lib.qsa_index_logits(C.byref(_topk(num_tokens=0)), None, 0, None) == 0
     assert lib.qsa_sparse_gqa_partial(C.byref(_gqa(head_dim=64)), None, 0, None) == NOTSUP
     assert lib.qsa_sparse_gqa_merge(C.byref(_gqa(q=None)), None, 0, None) == INVAL
-    assert lib.qsa_sparse_gqa_merge(C.byref(_gqa()), None, 0, None) == SMALL
+    assert lib.qsa_sparse_gqa_merge(C.byref(_gqa(num_tokens=32)), None, 0, None) == SMALL
     assert lib.qsa_sparse_gqa_partial(C.byref(_gqa(num_tokens=0)), None, 0, None) == 0
     c = B.CompressArgs()
     assert lib.qsa_compress(C.byref(c), None) == 0           # zero rows: a no-op
@@ -293,7 +308,7 @@ def test_no_alloc_attention_rejects_before_any_launch():
                              kv_head_stride=16 * 256, kv_page_stride=hkv * 16 * 256,
                              num_pages=1024, kv_dtype=kv_dtype)
                     need = lib.qsa_sparse_gqa_workspace_size(C.byref(a))
-                    assert 0 < need or lib.qsa_sparse_gqa_num_splits(C.byref(a)) == 1
+                    assert (0 < need) == (lib.qsa_sparse_gqa_merge_kernel(C.byref(a)) == 1)
                     assert need <= limit, (T, hkv, G, kv_dtype, need)
 
 
