@@ -415,10 +415,14 @@ def test_matrix_core_rows_with_scaled_fp16_logits(w):
             f"{int((packed != ref.packed).any(axis=1).sum())} rows differ")
 
 
-def test_inert_rows_invalid_entries_and_empty_requests():
+@pytest.mark.parametrize("splits", [0, 4, 1000])
+def test_inert_rows_invalid_entries_and_empty_requests(splits):
+    """A row with count 0, a negative entry and an entry past the block table, with the
+    automatic plan, four splits merged in the workgroup and the most splits (merge kernel)."""
     wl = workload("tiny_decode")
     ref = oracle_step(wl)
     st = run_gpu(wl)
+    st.g_args.num_splits = splits
     W = wl.output_width
     packed = ref.packed.copy()
     packed[0, W] = 0                              # count 0 -> zero output
@@ -445,16 +449,18 @@ def test_zero_rows_is_a_no_op():
     assert torch.equal(before, st.out)
 
 
-@pytest.mark.parametrize("name", ["decode_32k", "chunked_prefill", "fp8_decode"])
-def test_single_kernel_calls_equal_the_combined_calls(name):
+@pytest.mark.parametrize("name,splits", [("decode_32k", 0), ("decode_32k", 4),
+                                         ("chunked_prefill", 0), ("fp8_decode", 0)])
+def test_single_kernel_calls_equal_the_combined_calls(name, splits):
     """qsa_index_logits + qsa_block_topk and qsa_sparse_gqa_partial + qsa_sparse_gqa_merge
-    (the per-kernel calls the benchmark times) give the combined calls' results bit for bit."""
+    (the per-kernel calls the benchmark times) give the combined calls' results bit for bit;
+    with splits merged in the workgroup the merge call has nothing to do."""
     wl = workload(name)
     twin = workload(name)
-    log(f"single-kernel calls {name}: T={wl.num_tokens}")
-    a = QsaStep(wl)
+    log(f"single-kernel calls {name}: T={wl.num_tokens}, num_splits={splits}")
+    a = QsaStep(wl, num_splits=splits)
     a.run()
-    b = QsaStep(twin)
+    b = QsaStep(twin, num_splits=splits)
     b.compress()
     b.logits()
     b.block_topk()
