@@ -395,6 +395,21 @@ def test_index_topk_matches_brute_force_and_ignores_page_placement(idx_dtype, se
 # ----------------------------------------------------------------------------- expand
 
 
+def test_compressed_keys_outside_the_cache_read_as_zero():
+    """A visible block whose page is negative, past the cache, or past the block table's
+    columns scores as an all-zero key (the oracle's reading; the GPU logits mask such keys
+    the same way)."""
+    ckv_vals = RNG.standard_normal((4, 16, 128)) + 5.0          # no zero anywhere
+    row = np.array([2, 7, -1, 0], np.int32)                      # page 7 of 4 pages, then -1
+    keys = oq.compressed_keys_of_request(ckv_vals, row, 64)
+    assert np.array_equal(keys[:16], ckv_vals[2])
+    assert np.all(keys[16:48] == 0.0)
+    assert np.array_equal(keys[48:64], ckv_vals[0])
+    short = oq.compressed_keys_of_request(ckv_vals, row[:2], 48)  # column 2 past the table
+    assert np.array_equal(short[:16], ckv_vals[2])
+    assert np.all(short[16:48] == 0.0)
+
+
 def test_expand_closed_form_and_golden_tiny_decode_counts():
     with open(os.path.join(GOLDEN, "tiny_decode_counts.json")) as f:
         gold = json.load(f)
@@ -462,7 +477,7 @@ def test_sparse_gqa_masks_invalid_entries_and_empty_rows():
     L, W = 100, 40
     kv, bt, q, K, V = _tiny_attention_case(L)
     sel = np.array([3, 17, 40, 41, 99])
-    packed = np.full((3, W + 1), -1, np.int32)
+    packed = np.full((4, W + 1), -1, np.int32)
     # row 0: the selection; row 1: same with -1 and out-of-table entries mixed in;
     # row 2: count 0.
     packed[0, :5] = sel
@@ -470,12 +485,18 @@ def test_sparse_gqa_masks_invalid_entries_and_empty_rows():
     packed[1, :9] = [3, -1, 17, 40, 5000, 41, -7, 99, -1]
     packed[1, W] = 9
     packed[2, W] = 0
+    # row 3: row 0 with a count past W, which reads as W (the count column itself, 47 here,
+    # would otherwise be taken for a token).
+    packed[3] = packed[0]
+    packed[3, W] = W + 7
     kvb = f64_to_bf16_bits(kv)
-    out = oq.sparse_gqa(f64_to_bf16_bits(q[[0, 0, 0]]), kvb, bt, np.zeros(3, np.int32), packed)
+    out = oq.sparse_gqa(f64_to_bf16_bits(q[[0, 0, 0, 0]]), kvb, bt, np.zeros(4, np.int32),
+                        packed)
     ref = _dense_reference(q[0], K[sel], V[sel], 128 ** -0.5)
     assert np.abs(out[0] - ref).max() < 1e-12
     assert np.abs(out[1] - ref).max() < 1e-12
     assert np.all(out[2] == 0.0)
+    assert np.abs(out[3] - ref).max() < 1e-12
 
 
 def test_sparse_gqa_gate_zero_halves_and_page_permutation_invariance():
