@@ -278,6 +278,63 @@ def test_compress_pools_the_mean_of_distinct_members(c, chunks):
             assert not np.array_equal(round_bf16((wrong * inv_w) * (1.0 + w)), y)
 
 
+def _torch_norm_rope(x, w, pos_tab_rows):
+    """bf16 rows x [..., 128] -> torch rms_norm (float64, weight 1 + w, the float32 epsilon)
+    -> bf16 -> rotate-half RoPE of dims 0..63 with the given cos | sin rows -> bf16."""
+    y = F.rms_norm(torch.from_numpy(x), (128,), weight=torch.from_numpy(1.0 + w),
+                   eps=float(np.float32(1e-6)))
+    y = torch.from_numpy(round_bf16(y.numpy()))
+    cs = torch.from_numpy(np.array(pos_tab_rows, dtype=np.float64))
+    cos, sin = cs[..., :32], cs[..., 32:]
+    a, b = y[..., :32], y[..., 32:64]
+    out = y.clone()
+    out[..., :32] = a * cos - b * sin
+    out[..., 32:64] = b * cos + a * sin
+    return round_bf16(out.numpy())
+
+
+def test_prepare_index_q_normalises_then_rotates_every_head_at_the_row_position():
+    """Indexer Q prep ([qsa] QSAIndexer.forward, unfused path): each head of a row through
+    Gemma RMSNorm (here torch's rms_norm in float64), bf16, RoPE at the row's position, bf16.
+    Only the last bit of a near-tie may differ from torch's summation order; skipping the
+    norm, rotating at another position or mixing heads changes most values."""
+    T, Hi = 8, 4
+    x = rand_bf16((T, Hi, 128))
+    w = rand_bf16(128, std=0.1)
+    pos = RNG.integers(0, 900, size=T)
+    tab = rotary_table(1024).numpy()
+    codes, vals = oq.prepare_index_q(f64_to_bf16_bits(x.reshape(T, Hi * 128)), pos, tab, None,
+                                     f64_to_bf16_bits(w), 1e-6, Hi, "bf16")
+    rows = tab.astype(np.float64)[pos][:, None, :]               # [T, 1, 64]
+    ref = _torch_norm_rope(x, w, np.broadcast_to(rows, (T, Hi, 64)))
+    d = ulp_diff_bf16(vals, ref)
+    assert d.max() <= 1 and (d == 0).mean() > 0.995
+    shifted = _torch_norm_rope(x, w, np.broadcast_to(tab.astype(np.float64)[pos + 1][:, None, :],
+                                                     (T, Hi, 64)))
+    assert (ulp_diff_bf16(vals, shifted) == 0).mean() < 0.9
+
+
+def test_compress_rounds_the_pooled_mean_to_bf16_before_the_norm():
+    """[ops] qsa_compress_groups_with_ratio returns the pooled row in bf16; the norm and the
+    rotation then work on that row.  Random members make the mean rarely a bf16 value, so the
+    rounding shows: the row matches mean -> bf16 -> norm -> RoPE (torch's rms_norm, as above)
+    and not the chain that skips the first rounding."""
+    c, L = 4, 128
+    raw = rand_bf16((L, 128))
+    st = _one_request_compress(raw, [L], c)
+    w = bf16_bits_to_f64(_one_request_compress.w)
+    tab = rotary_table(L + 256).numpy().astype(np.float64)
+    mean = raw.reshape(L // c, c, 128).sum(axis=1) / c
+    rows = tab[np.arange(0, L, c)]
+    ref = _torch_norm_rope(round_bf16(mean), w, rows)
+    unrounded = _torch_norm_rope(mean, w, rows)
+    table = np.arange(64)[::-1]
+    got = np.stack([bf16_bits_to_f64(st.ckv[table[g // 16], g % 16]) for g in range(L // c)])
+    d = ulp_diff_bf16(got, ref)
+    assert d.max() <= 1 and (d == 0).mean() > 0.995
+    assert (ulp_diff_bf16(got, unrounded) == 0).mean() < 0.95
+
+
 # ----------------------------------------------------------------------------- scores / select
 
 
