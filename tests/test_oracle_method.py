@@ -314,6 +314,22 @@ def test_prepare_index_q_normalises_then_rotates_every_head_at_the_row_position(
     assert (ulp_diff_bf16(vals, shifted) == 0).mean() < 0.9
 
 
+def test_fp8_indexer_codes_are_the_bf16_prep_cast_to_e4m3():
+    """With the e4m3 indexer the prepared bf16 Q is cast to e4m3fn ([qsa] QSAIndexer.forward:
+    `.to(self.indexer_dtype)`): the codes equal torch's float8_e4m3fn cast of the bf16
+    values, and decode back to those e4m3 values."""
+    T, Hi = 8, 8
+    x = rand_bf16((T, Hi * 128))
+    w = f64_to_bf16_bits(rand_bf16(128, std=0.1))
+    pos = RNG.integers(0, 900, size=T)
+    tab = rotary_table(1024).numpy()
+    _, v16 = oq.prepare_index_q(f64_to_bf16_bits(x), pos, tab, None, w, 1e-6, Hi, "bf16")
+    c8, v8 = oq.prepare_index_q(f64_to_bf16_bits(x), pos, tab, None, w, 1e-6, Hi, "fp8")
+    ref = torch.from_numpy(v16.astype(np.float32)).to(torch.float8_e4m3fn)
+    assert np.array_equal(c8, ref.view(torch.uint8).numpy())
+    assert np.array_equal(v8, ref.to(torch.float64).numpy())
+
+
 def test_compress_rounds_the_pooled_mean_to_bf16_before_the_norm():
     """[ops] qsa_compress_groups_with_ratio returns the pooled row in bf16; the norm and the
     rotation then work on that row.  Random members make the mean rarely a bf16 value, so the
