@@ -161,6 +161,10 @@ def test_invalid_calls_are_rejected_before_any_launch():
                               None) == INVAL
     assert lib.qsa_sparse_gqa(C.byref(_gqa(kv_dtype=1)), None, 0, None) == SMALL
     assert lib.qsa_index_logits_topk(C.byref(_topk(budget=2047)), None, 0, None) == INVAL
+    # The top-k holds a row's scores in registers: at most 32,768 compressed columns.
+    assert lib.qsa_index_logits_topk_workspace_size(C.byref(_topk(max_seq_len=4 * 32768))) > 0
+    assert lib.qsa_index_logits_topk(C.byref(_topk(max_seq_len=4 * 32768 + 4)), None, 0,
+                                     None) == NOTSUP
     assert lib.qsa_index_logits_topk(C.byref(_topk(compress_ratio=3)), None, 0, None) == NOTSUP
     assert lib.qsa_index_logits_topk(C.byref(_topk(index_dtype=7)), None, 0, None) == NOTSUP
     assert lib.qsa_index_logits_topk(C.byref(_topk(index_agg=2)), None, 0, None) == NOTSUP

@@ -26,6 +26,10 @@ CASES = {
     # 1,102 rows in the call: the prefill configuration of the top-k next to decode rows.
     "mixed_topk_prefill": ("decode_32k", dict(num_requests=3, rows=(1, 1, 1100),
                                               lengths=("fixed", 2200))),
+    # Contexts up to the largest the top-k holds in registers (32,768 compressed columns): the
+    # 1,024-thread configuration, beyond the 16,384 columns of the workloads' own shapes.
+    "long_context": ("decode_32k", dict(num_requests=3, lengths=("uniform", 70000, 131072))),
+    "max_context": ("decode_32k", dict(num_requests=2, lengths=("fixed", 131072))),
     # GQA group sizes ([ops] qsa_sparse_paged_attention pads the group to a power of two).
     "G1": ("decode_32k", dict(q_heads=2, kv_heads=2)),
     "G2": ("decode_32k", dict(q_heads=4, kv_heads=2)),
