@@ -37,6 +37,8 @@ CASES = {
     "G16": ("chunked_prefill", dict(q_heads=16, kv_heads=1, rows=96)),
     "G16_fp8kv": ("decode_32k_fp8kv", dict(q_heads=16, kv_heads=1)),
     "G1_fp8kv": ("decode_32k_fp8kv", dict(q_heads=4, kv_heads=4)),
+    "G2_fp8kv": ("decode_32k_fp8kv", dict(q_heads=4, kv_heads=2)),
+    "G4_fp8kv": ("decode_32k_fp8kv", dict(q_heads=8, kv_heads=2)),
     # Compress ratios: any power of two > 1 ([indexer] _supports_fused_pre_indexer); the ring
     # is at least one group wide.
     "c2": ("decode_32k", dict(compress_ratio=2, rows=3)),

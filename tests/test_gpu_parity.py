@@ -172,14 +172,16 @@ def test_full_size_spec_verify_on_sampled_rows():
     assert err <= TOL["fp8"]
 
 
-@pytest.mark.parametrize("case", ["bf16_1row", "bf16_3rows", "relu"])
+@pytest.mark.parametrize("case", ["bf16_1row", "bf16_2rows", "bf16_3rows", "fp8_2rows", "relu"])
 def test_work_list_kernel_on_many_short_requests(case):
     """Batches whose one-item-per-workgroup logits grid would not fit the chip in one round are
     scored by the persistent work-list kernel: many requests of uneven length, each compared
-    row by row (bf16 indexer with one and three rows per request, and the ReLU-sum switch)."""
-    rows = 3 if case == "bf16_3rows" else 1
+    row by row (bf16 indexer with one, two and three rows per request, e4m3 with two, and the
+    ReLU-sum switch)."""
+    rows = {"bf16_2rows": 2, "bf16_3rows": 3, "fp8_2rows": 2}.get(case, 1)
     R = 300 if rows == 3 else 600
-    wl = workload("decode_32k", num_requests=R, lengths=("uniform", 2100, 6000), rows=rows)
+    base = "fp8_decode" if case.startswith("fp8") else "decode_32k"
+    wl = workload(base, num_requests=R, lengths=("uniform", 2100, 6000), rows=rows)
     agg = "relu" if case == "relu" else "sum"
     log(f"work-list logits {case}: R={R} T={wl.num_tokens}")
     ref = oracle_step(wl, with_attention=False, agg=agg)
@@ -192,10 +194,11 @@ def test_work_list_kernel_on_many_short_requests(case):
         f"{int((packed != ref.packed).any(axis=1).sum())} rows differ")
 
 
-def test_work_list_kernel_with_matrix_core_requests():
+@pytest.mark.parametrize("name", ["chunked_prefill", "chunked_prefill_fp8"])
+def test_work_list_kernel_with_matrix_core_requests(name):
     """Many prefill requests (17 rows each, scored on the matrix cores) in a call whose max |k|
-    pass needs the work-list kernel; sampled rows compared."""
-    wl = workload("chunked_prefill", num_requests=270, lengths=("uniform", 2100, 4000), rows=17)
+    pass needs the work-list kernel, bf16 and e4m3 indexer; sampled rows compared."""
+    wl = workload(name, num_requests=270, lengths=("uniform", 2100, 4000), rows=17)
     rows = [0, 16, 17 * 100 + 5, 17 * 269 + 16]
     log(f"work-list max|k| pass with MFMA requests: T={wl.num_tokens}")
     ref = oracle_step(wl, rows=rows, with_attention=False)
@@ -219,6 +222,10 @@ def _cap_for_rows(wl, rows: int) -> int:
     ("spec_verify_mrope", 7, {}),                  # windows cut a request's verify rows
     ("fp8_decode", 3, {}),
     ("decode_32k", 150, dict(num_requests=600, lengths=("uniform", 2100, 6000))),  # work list
+    ("decode_32k", 3, dict(rows=2)),               # two and three rows per request, windowed
+    ("decode_32k", 4, dict(rows=3)),
+    ("fp8_decode", 3, dict(rows=2)),
+    ("chunked_prefill_fp8", 100, {}),              # e4m3 max |k| pass in windows
 ])
 def test_logits_cap_runs_in_windows_with_the_same_selection(name, rows, kw):
     """With a logits memory cap the call scores and selects window by window, reusing a
@@ -635,3 +642,26 @@ def test_row_tiled_prefill_attention_every_row_and_adversarial_entries():
     err = max_abs(gpu_out_f64(st), want)
     log(f"  max-abs (adversarial entries) {err:.3e}")
     assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("chunk_bytes", [1024, 2048, 3072, 4096])
+def test_read_bandwidth_probe_reads_every_chunk_once(chunk_bytes):
+    """The bench's read probe folds the XOR of every 32-bit word it reads into one word: a
+    streaming read gives the XOR of the whole buffer, a gather the XOR of the listed chunks
+    (a chunk listed twice cancels out)."""
+    g = torch.Generator().manual_seed(chunk_bytes)
+    n_chunks = 3001
+    words = torch.randint(-2 ** 31, 2 ** 31 - 1, (n_chunks * chunk_bytes // 4,), generator=g,
+                          dtype=torch.int64).to(torch.int32)
+    src = words.cuda()
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    B.qsa_diag_read_bandwidth(src, chunk_bytes, sink)
+    torch.cuda.synchronize()
+    per_chunk = np.bitwise_xor.reduce(words.numpy().view(np.uint32).reshape(n_chunks, -1), axis=1)
+    assert int(sink.cpu().numpy().view(np.uint32)[0]) == int(np.bitwise_xor.reduce(per_chunk))
+    idx = torch.randint(0, n_chunks, (5000,), generator=g, dtype=torch.int32)
+    sink.zero_()
+    B.qsa_diag_read_bandwidth(src, chunk_bytes, sink, chunk_index=idx.cuda())
+    torch.cuda.synchronize()
+    expect = np.bitwise_xor.reduce(per_chunk[idx.numpy()])
+    assert int(sink.cpu().numpy().view(np.uint32)[0]) == int(expect)
