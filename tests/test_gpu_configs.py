@@ -28,6 +28,9 @@ CASES = {
                                               lengths=("fixed", 2200))),
     # Contexts up to the largest the top-k holds in registers (32,768 compressed columns): the
     # 1,024-thread configuration, beyond the 16,384 columns of the workloads' own shapes.
+    # Two rows per request (speculative decoding with one draft token): the two-row instance
+    # of the vector-unit logits.
+    "two_rows": ("decode_32k", dict(rows=2)),
     "long_context": ("decode_32k", dict(num_requests=3, lengths=("uniform", 70000, 131072))),
     "max_context": ("decode_32k", dict(num_requests=2, lengths=("fixed", 131072))),
     # GQA group sizes ([ops] qsa_sparse_paged_attention pads the group to a power of two).
