@@ -207,7 +207,7 @@ typedef struct qsa_topk_args {
   int32_t c_block_table_stride;
   int32_t c_block_table_width;
   int32_t c_page_size;
-  int32_t c_pages;
+  int32_t c_pages;                  /* c_pages * c_page_size < 2^31 (else NOT_SUPPORTED)     */
   int32_t num_index_heads;          /* Hi (1..16)                                            */
   int32_t head_dim;                 /* must be 128                                           */
   int32_t compress_ratio;           /* c (power of two)                                      */

@@ -2,6 +2,9 @@
 // before any HIP call, so an invalid call has no side effect (and needs no GPU).
 #include <hip/hip_runtime.h>
 
+#include <climits>
+#include <cstdint>
+
 #include "qsa_internal.h"
 
 namespace {
@@ -112,6 +115,8 @@ qsa_status validate_topk(const qsa_topk_args* a) {
                   a->c_block_table_stride >= a->c_block_table_width,
               kInval);
   QSA_REQUIRE(aligned(a->ckv, 16) && aligned(a->q_idx, 4) && aligned(a->packed, 4), kInval);
+  // Compressed cache rows are numbered in 32 bits (2^31 rows would be 512 GiB of bf16 keys).
+  QSA_REQUIRE((int64_t)a->c_pages * a->c_page_size <= INT32_MAX, kNotSup);
   // A row's fast scores are held in the registers of one workgroup.
   QSA_REQUIRE(a->max_seq_len / a->compress_ratio <= qsa::kTopkMaxCols, kNotSup);
   QSA_REQUIRE(a->index_agg == QSA_AGG_SUM || a->index_agg == QSA_AGG_RELU_SUM, kNotSup);

@@ -161,6 +161,9 @@ def test_invalid_calls_are_rejected_before_any_launch():
                               None) == INVAL
     assert lib.qsa_sparse_gqa(C.byref(_gqa(kv_dtype=1)), None, 0, None) == SMALL
     assert lib.qsa_index_logits_topk(C.byref(_topk(budget=2047)), None, 0, None) == INVAL
+    # Compressed cache rows are numbered in 32 bits.
+    assert lib.qsa_index_logits_topk(C.byref(_topk(c_pages=1 << 27, c_page_size=16)), None, 0,
+                                     None) == NOTSUP
     # The top-k holds a row's scores in registers: at most 32,768 compressed columns.
     assert lib.qsa_index_logits_topk_workspace_size(C.byref(_topk(max_seq_len=4 * 32768))) > 0
     assert lib.qsa_index_logits_topk(C.byref(_topk(max_seq_len=4 * 32768 + 4)), None, 0,
