@@ -12,23 +12,32 @@ namespace qsa {
 namespace {
 using namespace logits_tile;
 
-// Grid (wg_per_req, R), 256 threads.  Workgroup k of request r scores the request's keys
-// 1024k .. 1024k+1023 (4 tiles of 256) against every row of the request, NR rows at a time.
-// Eight lanes share a key (16 dims each), so one wave load reads eight compressed rows, 128
-// contiguous bytes of each.  The cache row of every key and the head-folded rows are staged in
-// LDS once; two tiles are in flight from the start and each reload is issued before the other
-// buffer's tile is scored.
+// Grid (workgroups per request, R), 512 threads (8 waves).  Workgroup k of request r scores the
+// request's keys 1024k .. 1024k+1023 (2 tiles of 512; a wave takes 64 keys of each) against
+// every row of the request, NR rows at a time.  A key's row is split over 16 lanes (bf16) or 8
+// lanes (e4m3) of 16 bytes, so one wave load reads 1 KiB of contiguous cache (the lane layout is
+// in logits_tile.h).  The cache row of every key and the head-folded rows are staged in LDS
+// once; each wave keeps one tile in flight, the other waves of its SIMD covering the latency.
 // RELU: one row at a time, its NR = 8 heads held unfolded as the scorer's rows.
 // KMAX: the call also has matrix-core requests, for which this kernel only takes the per-block
 // bound of max |k| (a separate instance, so that the decode instances carry no such branch).
 // WIN: the call runs in row windows (a logits memory cap): only the rows in [row_lo, row_hi)
 // are scored, into logits rows relative to row_lo.
-template <bool FP8, int NR, bool RELU = false, bool KMAX = false, bool WIN = false>
-__global__ __launch_bounds__(kLogitsThreads) __attribute__((amdgpu_waves_per_eu(NR >= 4 ? 2 : 4)))
+// WIDE (one-row requests, no cap, batches that fill the chip): a workgroup scores 2048 keys as
+// 4 tiles, two in flight per wave (the next tile's loads go out before a tile is scored), at 2
+// waves per SIMD: the same bytes in flight as 4 waves with one tile each, with the per-workgroup
+// round trips for the block table, the metadata and Q paid once per 2048 keys instead of 1024.
+// On decode_32k: 30.6 -> 29.6 us; with 8 tiles (half the workgroups) it took 35.5 us.
+template <bool FP8, int NR, bool RELU = false, bool KMAX = false, bool WIN = false,
+          bool WIDE = false>
+__global__ __launch_bounds__(kLogitsThreads)
+__attribute__((amdgpu_waves_per_eu((NR >= 4 || WIDE) ? 2 : 4)))
 void logits_valu_kernel(SelectParams P) {
+  static_assert(!WIDE || (NR == 1 && !RELU && !KMAX && !WIN), "the wide instance is for decode");
   using KL = KeyLanes<FP8>;
   constexpr int kT = kLogitsThreads, kWaves = kLogitsThreads / 64;
-  constexpr int kKeys = kLogitsTilesPerWG * kLogitsKeysPerWG;
+  constexpr int kTiles = WIDE ? 2 * kLogitsTilesPerWG : kLogitsTilesPerWG;
+  constexpr int kKeys = kTiles * kLogitsKeysPerWG;
   static_assert(kLogitsKeysPerWG == kWaves * 64, "a tile is 64 keys per wave");
   __shared__ int32_t rows_s[kKeys];
   __shared__ float qf_s[NR][kHeadDim];
@@ -77,7 +86,7 @@ void logits_valu_kernel(SelectParams P) {
       if (n > P.mfma_min_rows) {  // block-uniform
         barrier();  // rows_s written
 #pragma unroll
-        for (int t = 0; t < kLogitsTilesPerWG; ++t) {
+        for (int t = 0; t < kTiles; ++t) {
           uint32_t a[KL::kLoads][4], ma;
           load_key_tile<FP8>(P, rows_s, t, w, lane, a, ma);
 #pragma unroll
@@ -154,15 +163,28 @@ void logits_valu_kernel(SelectParams P) {
       }
       const bool first = rr0 == rb;
       const int row0 = q0 + rr0 - (WIN ? P.row_lo : 0);  // logits row (window-relative)
-      // One tile in flight per wave; the other waves of the SIMD (four per SIMD) cover its
-      // latency.  The loop is unrolled, so the compiler's vmcnt waits name exactly the tile.
-      uint32_t a[KL::kLoads][4], ma;
+      // One tile in flight per wave (WIDE: two); the other waves of the SIMD cover its
+      // latency.  The loops are unrolled, so the compiler's vmcnt waits name exactly the tile.
+      if constexpr (WIDE) {
+        uint32_t a[2][KL::kLoads][4], ma[2];
+        load_key_tile<FP8>(P, rows_s, 0, w, lane, a[0], ma[0]);
 #pragma unroll
-      for (int t = 0; t < kLogitsTilesPerWG; ++t) {
-        load_key_tile<FP8>(P, rows_s, t, w, lane, a, ma);
-        score_key_tile<FP8, NR, RELU>(P, a, ma, qf, nr, row0,
-                                      jw + t * kLogitsKeysPerWG + w * 64, vis_max, lane, first,
-                                      kmax);
+        for (int t = 0; t < kTiles; ++t) {
+          if (t + 1 < kTiles)
+            load_key_tile<FP8>(P, rows_s, t + 1, w, lane, a[(t + 1) & 1], ma[(t + 1) & 1]);
+          score_key_tile<FP8, NR, RELU>(P, a[t & 1], ma[t & 1], qf, nr, row0,
+                                        jw + t * kLogitsKeysPerWG + w * 64, vis_max, lane,
+                                        first, kmax);
+        }
+      } else {
+        uint32_t a[KL::kLoads][4], ma;
+#pragma unroll
+        for (int t = 0; t < kTiles; ++t) {
+          load_key_tile<FP8>(P, rows_s, t, w, lane, a, ma);
+          score_key_tile<FP8, NR, RELU>(P, a, ma, qf, nr, row0,
+                                        jw + t * kLogitsKeysPerWG + w * 64, vis_max, lane,
+                                        first, kmax);
+        }
       }
     }
   }
@@ -188,7 +210,19 @@ hipError_t launch_valu(const SelectParams& P, hipStream_t s) {
   const int64_t dense = (int64_t)P.R * P.key_tiles, resident = (int64_t)kCUs * per_cu;
   if (dense <= resident || P.R > kLogitsListReqs) {
     const dim3 grid(P.key_tiles, P.R), block(kLogitsThreads);
-    if (P.row_lo > 0 || P.row_hi < P.T)  // row windows
+    const bool windows = P.row_lo > 0 || P.row_hi < P.T;
+    if constexpr (NR == 1 && !RELU && !KMAX) {
+      // One-row requests filling the chip with 2048-key workgroups (one per CU): the wide
+      // instance.  Smaller batches keep 1024-key workgroups, which spread over more CUs.
+      const int wide_tiles = (P.cols + 2 * kLogitsTilesPerWG * kLogitsKeysPerWG - 1) /
+                             (2 * kLogitsTilesPerWG * kLogitsKeysPerWG);
+      if (!windows && (int64_t)P.R * wide_tiles >= kCUs) {
+        hipLaunchKernelGGL((logits_valu_kernel<FP8, 1, false, false, false, true>),
+                           dim3(wide_tiles, P.R), block, 0, s, P);
+        return hipGetLastError();
+      }
+    }
+    if (windows)
       hipLaunchKernelGGL((logits_valu_kernel<FP8, NR, RELU, KMAX, true>), grid, block, 0, s, P);
     else
       hipLaunchKernelGGL((logits_valu_kernel<FP8, NR, RELU, KMAX>), grid, block, 0, s, P);

@@ -32,6 +32,10 @@ CASES = {
     # of the vector-unit logits.
     "two_rows": ("decode_32k", dict(rows=2)),
     "long_context": ("decode_32k", dict(num_requests=3, lengths=("uniform", 70000, 131072))),
+    # One-row batches that fill the chip with 2048-key logits workgroups (the wide instance of
+    # the vector-unit logits), bf16 and e4m3 indexer.
+    "wide_bf16": ("decode_32k", dict(num_requests=256, compress_ratio=2, lengths=("fixed", 4096))),
+    "wide_fp8": ("fp8_decode", dict(num_requests=256, compress_ratio=2, lengths=("fixed", 4096))),
     "max_context": ("decode_32k", dict(num_requests=2, lengths=("fixed", 131072))),
     # GQA group sizes ([ops] qsa_sparse_paged_attention pads the group to a power of two).
     "G1": ("decode_32k", dict(q_heads=2, kv_heads=2)),
