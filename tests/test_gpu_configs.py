@@ -36,6 +36,7 @@ CASES = {
     # the vector-unit logits), bf16 and e4m3 indexer.
     "wide_bf16": ("decode_32k", dict(num_requests=256, compress_ratio=2, lengths=("fixed", 4096))),
     "wide_fp8": ("fp8_decode", dict(num_requests=256, compress_ratio=2, lengths=("fixed", 4096))),
+    "wide_ragged": ("decode_32k", dict(num_requests=128, lengths=("uniform", 10000, 14000))),
     "max_context": ("decode_32k", dict(num_requests=2, lengths=("fixed", 131072))),
     # GQA group sizes ([ops] qsa_sparse_paged_attention pads the group to a power of two).
     "G1": ("decode_32k", dict(q_heads=2, kv_heads=2)),
