@@ -8,7 +8,9 @@
 // rounded to bf16, and each split emits float32 (o, lse) partials merged afterwards; with one
 // split the kernel writes the gated bf16 output directly.
 //
-// MI355X layout: one wavefront per (row, KV head, split), tiles of 32 selected tokens.  The
+// MI355X layout: one wavefront per (row, KV head, split), tiles of 32 selected tokens; with
+// bf16 K/V and at most 8 splits the splits of a (row, KV head) are the waves of one workgroup,
+// which merges them in LDS (no partials in memory, no merge kernel).  The
 // split's entries are resolved to cache rows up front (index and block-table loads all in
 // flight together) and kept in LDS; K and V rows are gathered straight into LDS with
 // coalesced 16-byte LDS-direct loads, a tile ahead; both contractions (Q.K over the G heads
