@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 8
+#define QSA_ABI_VERSION 9
 
 typedef enum qsa_status {
   QSA_OK = 0,
@@ -246,6 +246,37 @@ qsa_status qsa_index_logits(const qsa_topk_args* args, void* workspace, size_t w
                             void* stream);
 qsa_status qsa_block_topk(const qsa_topk_args* args, void* workspace, size_t workspace_bytes,
                           void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * qsa_compress_index_logits_topk
+ *
+ * qsa_compress(compress_args) followed by qsa_index_logits_topk(topk_args, workspace) on one
+ * stream, as one call: the same outputs, bit for bit (q_idx, the compressed cache, the ring,
+ * the packed rows; workspace: qsa_index_logits_topk_workspace_size(topk_args)).  Both argument
+ * blocks are validated before anything runs; an invalid one leaves every buffer untouched.
+ * Follows QSAIndexer.forward (page "vllm.models.qwen4_exp.nvidia.qsa"), whose decode path runs
+ * the indexer prepare and then the paged selection on the same requests.
+ *
+ * When the step is a batch of one-row requests (num_tokens == num_requests, max_query_len 1
+ * in both blocks, the rows' offsets starting at 0) large enough for the wide vector-unit
+ * scoring layout, with no main-attention prepare, plain-sum aggregation, no logits window, and
+ * both blocks naming the same requests, q_idx, compressed cache and block table, the scoring
+ * kernel does the indexer prepare itself and the compress launch is saved
+ * (qsa_compress_index_logits_topk_fused returns 1; 0 when the two calls run back to back, -1
+ * for invalid arguments).  In that case no request's visible compressed rows may lie in a page
+ * that another request's step writes (a group this step completes).
+ * qsa_compress_index_logits runs the first part only (the prepare and the scoring), for a
+ * caller that times qsa_block_topk separately: followed by qsa_block_topk(topk_args) with the
+ * same workspace it has exactly the effect of qsa_compress_index_logits_topk.
+ * ------------------------------------------------------------------------------------------ */
+qsa_status qsa_compress_index_logits_topk(const qsa_compress_args* compress_args,
+                                          const qsa_topk_args* topk_args, void* workspace,
+                                          size_t workspace_bytes, void* stream);
+qsa_status qsa_compress_index_logits(const qsa_compress_args* compress_args,
+                                     const qsa_topk_args* topk_args, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+int32_t qsa_compress_index_logits_topk_fused(const qsa_compress_args* compress_args,
+                                             const qsa_topk_args* topk_args);
 
 /* ------------------------------------------------------------------------------------------
  * qsa_sparse_gqa

@@ -21,6 +21,8 @@ AGGS = {"sum": 0, "relu": 1}   # head aggregation of the indexer score
 EXPORTED = (
     "qsa_compress", "qsa_index_logits_topk", "qsa_index_logits_topk_workspace_size",
     "qsa_index_logits", "qsa_block_topk",
+    "qsa_compress_index_logits_topk", "qsa_compress_index_logits",
+    "qsa_compress_index_logits_topk_fused",
     "qsa_sparse_gqa", "qsa_sparse_gqa_workspace_size", "qsa_sparse_gqa_num_splits",
     "qsa_sparse_gqa_merge_kernel",
     "qsa_sparse_gqa_partial", "qsa_sparse_gqa_merge",
@@ -111,6 +113,13 @@ def lib() -> C.CDLL:
         for f in ("qsa_index_logits_topk", "qsa_index_logits", "qsa_block_topk"):
             getattr(h, f).argtypes = [C.POINTER(TopkArgs), _P, C.c_size_t, _P]
             getattr(h, f).restype = C.c_int
+        for f in ("qsa_compress_index_logits_topk", "qsa_compress_index_logits"):
+            getattr(h, f).argtypes = [C.POINTER(CompressArgs), C.POINTER(TopkArgs), _P,
+                                      C.c_size_t, _P]
+            getattr(h, f).restype = C.c_int
+        h.qsa_compress_index_logits_topk_fused.argtypes = [C.POINTER(CompressArgs),
+                                                           C.POINTER(TopkArgs)]
+        h.qsa_compress_index_logits_topk_fused.restype = _I32
         h.qsa_sparse_gqa_workspace_size.argtypes = [C.POINTER(GqaArgs)]
         h.qsa_sparse_gqa_workspace_size.restype = C.c_size_t
         h.qsa_sparse_gqa_num_splits.argtypes = [C.POINTER(GqaArgs)]
@@ -352,6 +361,25 @@ def qsa_index_logits_topk(workspace=None, stream=None, **kw) -> None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=kw["packed"].device)
     _check(lib().qsa_index_logits_topk(C.byref(a), _ptr(workspace), workspace.numel(),
                                        _stream(stream)), "qsa_index_logits_topk")
+
+
+def qsa_compress_index_logits_topk(compress, topk, workspace=None, stream=None) -> None:
+    """qsa_compress(**compress) then qsa_index_logits_topk(**topk) as one call (one launch fewer
+    for a batch of one-row decode requests)."""
+    ca, ta = compress_args(**compress), topk_args(**topk)
+    need = int(lib().qsa_index_logits_topk_workspace_size(C.byref(ta)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=topk["packed"].device)
+    _check(lib().qsa_compress_index_logits_topk(C.byref(ca), C.byref(ta), _ptr(workspace),
+                                                workspace.numel(), _stream(stream)),
+           "qsa_compress_index_logits_topk")
+
+
+def qsa_compress_index_logits_topk_fused(compress, topk) -> int:
+    """1 when qsa_compress_index_logits_topk runs as one scoring launch, 0 when as the two
+    calls, -1 for invalid arguments."""
+    ca, ta = compress_args(**compress), topk_args(**topk)
+    return int(lib().qsa_compress_index_logits_topk_fused(C.byref(ca), C.byref(ta)))
 
 
 # ------------------------------------------------------------------------------ qsa_sparse_gqa

@@ -18,7 +18,7 @@ LIB = os.path.join(PKG, "libqsa.so")
 ARCH = "gfx950"
 
 SOURCES = ["qsa_abi.cpp", "compress.hip", "select.hip", "logits.hip", "logits_list.hip", "logits_mfma.hip", "logits_relu.hip",
-           "topk.hip", "gqa.hip", "diag.hip"]
+           "topk.hip", "gqa.hip", "prep_logits.hip", "diag.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
           "-Wno-unused-function", "-Wno-unused-variable",

@@ -204,21 +204,37 @@ void logits_valu_kernel(SelectParams P) {
 // SIMD), one with four or more.
 constexpr int kCUs = 256;
 
+// Workgroups per request of the wide instance (2048 keys each).
+int wide_tiles(const SelectParams& P) {
+  return (P.cols + 2 * kLogitsTilesPerWG * kLogitsKeysPerWG - 1) /
+         (2 * kLogitsTilesPerWG * kLogitsKeysPerWG);
+}
+
+// The one-item-per-workgroup grid (rather than the persistent work list) for NR rows per chunk.
+bool valu_grid(const SelectParams& P, int nr) {
+  const int per_cu = nr >= 4 ? 1 : 2;
+  const int64_t dense = (int64_t)P.R * P.key_tiles, resident = (int64_t)kCUs * per_cu;
+  return dense <= resident || P.R > kLogitsListReqs;
+}
+
+// One-row requests filling the chip with 2048-key workgroups (one per CU): the wide instance.
+// Smaller batches keep 1024-key workgroups, which spread over more CUs.
+bool wide_applies(const SelectParams& P) {
+  const bool windows = P.row_lo > 0 || P.row_hi < P.T;
+  return valu_grid(P, 1) && !windows && (int64_t)P.R * wide_tiles(P) >= kCUs;
+}
+
 template <bool FP8, int NR, bool RELU, bool KMAX>
 hipError_t launch_valu(const SelectParams& P, hipStream_t s) {
   const int per_cu = NR >= 4 ? 1 : 2;
-  const int64_t dense = (int64_t)P.R * P.key_tiles, resident = (int64_t)kCUs * per_cu;
-  if (dense <= resident || P.R > kLogitsListReqs) {
+  const int64_t resident = (int64_t)kCUs * per_cu;
+  if (valu_grid(P, NR)) {
     const dim3 grid(P.key_tiles, P.R), block(kLogitsThreads);
     const bool windows = P.row_lo > 0 || P.row_hi < P.T;
     if constexpr (NR == 1 && !RELU && !KMAX) {
-      // One-row requests filling the chip with 2048-key workgroups (one per CU): the wide
-      // instance.  Smaller batches keep 1024-key workgroups, which spread over more CUs.
-      const int wide_tiles = (P.cols + 2 * kLogitsTilesPerWG * kLogitsKeysPerWG - 1) /
-                             (2 * kLogitsTilesPerWG * kLogitsKeysPerWG);
-      if (!windows && (int64_t)P.R * wide_tiles >= kCUs) {
+      if (wide_applies(P)) {
         hipLaunchKernelGGL((logits_valu_kernel<FP8, 1, false, false, false, true>),
-                           dim3(wide_tiles, P.R), block, 0, s, P);
+                           dim3(wide_tiles(P), P.R), block, 0, s, P);
         return hipGetLastError();
       }
     }
@@ -241,6 +257,10 @@ hipError_t launch_logits(const SelectParams& P, int rows_per_chunk, bool mfma, h
 }
 
 }  // namespace
+
+bool logits_wide(const SelectParams& P, int rows_per_chunk, bool mfma) {
+  return !mfma && !P.relu && rows_per_chunk <= 1 && wide_applies(P);
+}
 
 hipError_t launch_logits_valu(const SelectParams& P, int rows_per_chunk, bool mfma,
                               hipStream_t s) {

@@ -247,6 +247,55 @@ qsa_status qsa_block_topk(const qsa_topk_args* a, void* ws, size_t ws_bytes, voi
   return run_topk(a, ws, ws_bytes, stream, qsa::Phase::kSecond);
 }
 
+}  // extern "C"
+
+namespace {
+
+// qsa_compress + qsa_index_logits_topk as one call: validated as the two calls are, fused when
+// prep_logits_fusable says so, else the two calls back to back.
+qsa_status run_prep_topk(const qsa_compress_args* c, const qsa_topk_args* t, void* ws,
+                         size_t ws_bytes, void* stream, qsa::Phase phase) {
+  if (c == nullptr || t == nullptr || c->num_tokens < 0 || t->num_tokens < 0) return kInval;
+  if (c->num_tokens > 0) {
+    if (qsa_status s = validate_compress(c)) return s;
+  }
+  if (t->num_tokens > 0) {
+    if (qsa_status s = validate_topk(t)) return s;
+    const qsa::TopkLayout L = qsa::topk_layout(*t);
+    if (ws == nullptr || ws_bytes < L.total) return QSA_ERR_WORKSPACE_TOO_SMALL;
+    if (!aligned(ws, 256)) return kInval;
+    if (phase != qsa::Phase::kAll && L.rows < t->num_tokens) return kNotSup;
+    if (c->num_tokens > 0 && qsa::prep_logits_fusable(*c, *t))
+      return from_hip(qsa::launch_prep_logits_topk(*c, *t, L, static_cast<char*>(ws),
+                                                   reinterpret_cast<hipStream_t>(stream),
+                                                   phase));
+  }
+  if (qsa_status s = qsa_compress(c, stream)) return s;
+  return run_topk(t, ws, ws_bytes, stream, phase);
+}
+
+}  // namespace
+
+extern "C" {
+
+qsa_status qsa_compress_index_logits_topk(const qsa_compress_args* c, const qsa_topk_args* t,
+                                          void* ws, size_t ws_bytes, void* stream) {
+  return run_prep_topk(c, t, ws, ws_bytes, stream, qsa::Phase::kAll);
+}
+
+qsa_status qsa_compress_index_logits(const qsa_compress_args* c, const qsa_topk_args* t,
+                                     void* ws, size_t ws_bytes, void* stream) {
+  return run_prep_topk(c, t, ws, ws_bytes, stream, qsa::Phase::kFirst);
+}
+
+int32_t qsa_compress_index_logits_topk_fused(const qsa_compress_args* c,
+                                             const qsa_topk_args* t) {
+  if (c == nullptr || t == nullptr || c->num_tokens < 0 || t->num_tokens < 0) return -1;
+  if (c->num_tokens > 0 && validate_compress(c) != QSA_OK) return -1;
+  if (t->num_tokens > 0 && validate_topk(t) != QSA_OK) return -1;
+  return c->num_tokens > 0 && t->num_tokens > 0 && qsa::prep_logits_fusable(*c, *t) ? 1 : 0;
+}
+
 int32_t qsa_sparse_gqa_num_splits(const qsa_gqa_args* a) {
   if (validate_gqa(a) != QSA_OK) return 0;
   return qsa::gqa_plan(*a).splits;

@@ -62,6 +62,13 @@ hipError_t launch_topk(const qsa_topk_args& a, const TopkLayout& L, char* ws, hi
                        Phase phase = Phase::kAll);
 hipError_t launch_gqa(const qsa_gqa_args& a, const GqaPlan& plan, char* ws, hipStream_t s,
                       Phase phase = Phase::kAll);
+// qsa_compress and qsa_index_logits_topk in one scoring launch (prep_logits.hip): whether a
+// pair of calls qualifies (one-row requests on the wide vector-unit layout, the two calls
+// describing the same requests and caches), and the fused launch (kFirst: without the top-k).
+bool prep_logits_fusable(const qsa_compress_args& c, const qsa_topk_args& t);
+hipError_t launch_prep_logits_topk(const qsa_compress_args& c, const qsa_topk_args& t,
+                                   const TopkLayout& L, char* ws, hipStream_t s,
+                                   Phase phase = Phase::kAll);
 // The allocation-free attention call's static scratch (gqa.hip): its size, and the device
 // address of the current device's copy (looked up on the first call on each device).
 constexpr size_t kGqaScratchBytes = size_t(40) << 20;

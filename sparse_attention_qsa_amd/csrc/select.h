@@ -36,6 +36,10 @@ struct SelectParams {
   int32_t* lexp;
 };
 
+// The parameter block of a qsa_index_logits_topk call over workspace `ws` (no workspace
+// pointers when ws is null: for plans made before a workspace exists).
+SelectParams select_params(const qsa_topk_args& a, const TopkLayout& L, char* ws);
+
 // Requests with more rows than this are scored by the matrix-core logits kernel.
 constexpr int kMfmaMinRows = 16;
 // ... and at most this many indexer heads (they are folded into one Q in registers).
@@ -45,6 +49,9 @@ constexpr int kMfmaMaxHeads = 16;
 // mfma: the call has requests scored on the matrix cores (rows_per_chunk is then 16).
 hipError_t launch_logits_valu(const SelectParams& P, int rows_per_chunk, bool mfma,
                               hipStream_t s);
+// Whether launch_logits_valu runs the wide instance (one-row requests filling the chip with
+// 2048-key workgroups), the layout the fused decode prepare + logits kernel shares.
+bool logits_wide(const SelectParams& P, int rows_per_chunk, bool mfma);
 // ReLU-sum logits on the matrix cores (logits_relu.hip): every head's product a column of one
 // contraction; the top-k bounds these scores with u = 2^-23.
 hipError_t launch_logits_relu_mfma(const SelectParams& P, hipStream_t s);

@@ -33,8 +33,7 @@ TopkLayout topk_layout(const qsa_topk_args& a) {
   return L;
 }
 
-hipError_t launch_topk(const qsa_topk_args& a, const TopkLayout& L, char* ws, hipStream_t s,
-                       Phase phase) {
+SelectParams select_params(const qsa_topk_args& a, const TopkLayout& L, char* ws) {
   SelectParams P{};
   P.T = a.num_tokens;
   P.R = a.num_requests;
@@ -60,23 +59,30 @@ hipError_t launch_topk(const qsa_topk_args& a, const TopkLayout& L, char* ws, hi
   P.cbt = a.c_block_table;
   P.packed = a.packed;
   P.p_rs = a.packed_row_stride;
-  P.logits = reinterpret_cast<float*>(ws + L.off_logits);
-  P.kmax = reinterpret_cast<float*>(ws + L.off_kmax);
-  P.band_idx = reinterpret_cast<int32_t*>(ws + L.off_band_idx);
-  P.band_score = reinterpret_cast<double*>(ws + L.off_band_score);
-  P.work = reinterpret_cast<int*>(ws + L.off_work);
-  P.lexp = reinterpret_cast<int32_t*>(ws + L.off_lexp);
+  if (ws != nullptr) {
+    P.logits = reinterpret_cast<float*>(ws + L.off_logits);
+    P.kmax = reinterpret_cast<float*>(ws + L.off_kmax);
+    P.band_idx = reinterpret_cast<int32_t*>(ws + L.off_band_idx);
+    P.band_score = reinterpret_cast<double*>(ws + L.off_band_score);
+    P.work = reinterpret_cast<int*>(ws + L.off_work);
+    P.lexp = reinterpret_cast<int32_t*>(ws + L.off_lexp);
+  }
   P.row_lo = 0;
   P.row_hi = P.T;
+  const bool mfma_ok = !P.relu && P.Hi <= kMfmaMaxHeads;
+  P.mfma_min_rows = mfma_ok ? kMfmaMinRows : INT32_MAX;
+  return P;
+}
 
+hipError_t launch_topk(const qsa_topk_args& a, const TopkLayout& L, char* ws, hipStream_t s,
+                       Phase phase) {
+  SelectParams P = select_params(a, L, ws);
   // Plain sum: requests with more than kMfmaMinRows rows are scored by the per-head matrix-core
   // contraction (bf16 or e4m3 operands), the others by the VALU kernel; each kernel skips the
   // other's requests.  ReLU-sum: every request goes to logits_relu_mfma_kernel, which clamps
   // each head's product before the head sum (the per-head contraction keeps the heads summed
   // in its accumulator, so it cannot clamp them).
-  const bool mfma_ok = !P.relu && P.Hi <= kMfmaMaxHeads;
-  const bool mfma = mfma_ok && a.max_query_len > kMfmaMinRows;
-  P.mfma_min_rows = mfma_ok ? kMfmaMinRows : INT32_MAX;
+  const bool mfma = P.mfma_min_rows == kMfmaMinRows && a.max_query_len > kMfmaMinRows;
   if (phase == Phase::kSecond) return launch_topk_select(P, s);
   const int rows_per_chunk = mfma ? kMfmaMinRows : a.max_query_len;
   // Window by window (one window without a logits cap; the split calls take one only): the

@@ -74,6 +74,23 @@ class QsaStep:
         B._check(B.lib().qsa_sparse_gqa(C.byref(self.g_args), self.g_ws.data_ptr(),
                                         self.g_ws.numel(), B._stream(stream)), "qsa_sparse_gqa")
 
+    # qsa_compress + qsa_index_logits_topk as one call (one scoring launch for a batch of
+    # one-row requests); `fused` says whether this step's calls qualify.
+    @property
+    def fused(self) -> bool:
+        return int(B.lib().qsa_compress_index_logits_topk_fused(
+            C.byref(self.c_args), C.byref(self.t_args))) == 1
+
+    def prep_topk(self, stream=None):
+        B._check(B.lib().qsa_compress_index_logits_topk(
+            C.byref(self.c_args), C.byref(self.t_args), self.t_ws.data_ptr(), self.t_ws.numel(),
+            B._stream(stream)), "qsa_compress_index_logits_topk")
+
+    def prep_logits(self, stream=None):
+        B._check(B.lib().qsa_compress_index_logits(
+            C.byref(self.c_args), C.byref(self.t_args), self.t_ws.data_ptr(), self.t_ws.numel(),
+            B._stream(stream)), "qsa_compress_index_logits")
+
     # The single kernels of the two-kernel calls (for per-kernel timing).
     def logits(self, stream=None):
         B._check(B.lib().qsa_index_logits(C.byref(self.t_args), self.t_ws.data_ptr(),
@@ -94,8 +111,13 @@ class QsaStep:
                                               self.g_ws.numel(), B._stream(stream)),
                  "qsa_sparse_gqa_merge")
 
-    def run(self, stream=None):
-        self.compress(stream)
-        self.topk(stream)
+    def run(self, stream=None, combined=False):
+        """One step: the three calls, or (combined) qsa_compress_index_logits_topk and the
+        attention."""
+        if combined:
+            self.prep_topk(stream)
+        else:
+            self.compress(stream)
+            self.topk(stream)
         self.gqa(stream)
         return self.out

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(B.EXPORTED)
-    assert lib.qsa_abi_version() == 8
+    assert lib.qsa_abi_version() == 9
     assert lib.qsa_status_string(3) == b"QSA_ERR_WORKSPACE_TOO_SMALL"
 
 
@@ -215,6 +215,38 @@ def _compress(**over):
     for k, v in over.items():
         setattr(a, k, v)
     return a
+
+
+def test_combined_prepare_and_selection_plan_and_invalid_calls():
+    """qsa_compress_index_logits_topk fuses the indexer prepare into the scoring launch only for
+    one-row batches on the wide scoring layout whose two argument blocks describe the same
+    requests and caches; anything invalid is rejected before any launch (no GPU here)."""
+    lib = B.lib()
+    INVAL, NOTSUP, SMALL = 1, 2, 3
+    fused = lambda c, t: lib.qsa_compress_index_logits_topk_fused(C.byref(c), C.byref(t))  # noqa
+    c, t = _compress(main_qkv=None), _topk()     # 64 one-row requests of 32k tokens
+    assert fused(c, t) == 1
+    many = dict(num_tokens=256, num_requests=256)
+    assert fused(_compress(main_qkv=None, **many),
+                 _topk(num_decode_requests=256, max_seq_len=8192, **many)) == 1
+    assert fused(_compress(), t) == 0                            # main-attention prepare
+    assert fused(c, _topk(index_agg=1)) == 0                     # ReLU-sum
+    assert fused(c, _topk(max_logits_bytes=8192 * 4)) == 0       # logits windows
+    assert fused(_compress(main_qkv=None, max_query_len=2), _topk(max_query_len=2)) == 0
+    assert fused(c, _topk(q_idx=FAKE + 256)) == 0                # the blocks disagree
+    assert fused(c, _topk(c_block_table_width=256)) == 0
+    assert fused(c, _topk(max_seq_len=8192)) == 0                # 64 workgroups: too few
+    half = dict(num_tokens=32, num_requests=32)
+    assert fused(_compress(main_qkv=None, **half), _topk(num_decode_requests=32, **half)) == 0
+    assert fused(_compress(main_qkv=None, head_dim=64), t) == -1
+    assert fused(c, _topk(budget=3)) == -1
+    call = lambda c, t, n=1 << 40, f=lib.qsa_compress_index_logits_topk: f(  # noqa: E731
+        C.byref(c) if c is not None else None, C.byref(t), FAKE, n, None)
+    assert call(_compress(main_qkv=None, head_dim=64), t) == NOTSUP
+    assert call(c, _topk(budget=3)) == INVAL
+    assert call(None, t) == INVAL
+    assert call(c, t, 16) == SMALL
+    assert call(c, _topk(max_logits_bytes=8192 * 4), f=lib.qsa_compress_index_logits) == NOTSUP
 
 
 def test_invalid_main_prepare_arguments_are_rejected_before_any_launch():
