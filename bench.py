@@ -1,13 +1,15 @@
 """Benchmark of the QSA hot path on one MI355X.
 
-A step is one pass of the whole path -- qsa_compress, qsa_index_logits_topk, qsa_sparse_gqa --
-over one batch of the decode_32k workload: 64 requests at 32768 tokens of context, one query
+A step is one pass of the whole path -- qsa_compress and qsa_index_logits_topk (as the one call
+qsa_compress_index_logits_topk, a single scoring launch for a one-row batch such as this), then
+qsa_sparse_gqa -- over one batch of the decode_32k workload: 64 requests at 32768 tokens of context, one query
 row each; indexer 8 heads, compress ratio 4, budget 2048, bf16; attention 16 Q / 2 KV heads,
 head_dim 128, page 16.  Inputs are seeded synthetic tensors resident in HBM.  Several copies of
 the inputs are rotated step by step so that a step never finds its ~270 MB working set in the
 256 MB Infinity Cache.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                    [--separate-calls]
 
 Prints one JSON line: rows/s for the whole step, the step's algorithmic HBM GB/s, per-call and
 per-kernel times (each kernel alone, through the library call that launches only it), the
@@ -35,7 +37,9 @@ METRIC = "decode rows/sec + achieved HBM GB/s, QSA indexer+sparse GQA at 32k ctx
 # The kernels timed one by one (each through the call that launches only it), with the sources
 # they are built from (a traffic record applies only while these are unchanged).
 KERNELS = {
-    "prep_compress_kernel": ("compress", ["qsa_internal.h", "compress.hip"]),
+    "prep_compress_kernel": ("compress", ["qsa_internal.h", "prep_ops.h", "compress.hip"]),
+    "prep_logits_kernel": ("prep_logits", ["qsa_internal.h", "prep_ops.h", "select.h",
+                                           "logits_tile.h", "prep_logits.hip"]),
     "logits_valu_kernel": ("logits", ["qsa_internal.h", "select.h", "select.hip", "logits_tile.h",
                                       "logits.hip", "logits_list.hip", "logits_mfma.hip"]),
     "topk_kernel": ("block_topk", ["qsa_internal.h", "select.h", "select.hip", "topk.hip"]),
@@ -45,6 +49,7 @@ KERNELS = {
 # The device kernels each of those calls launches (counter records group them per call).
 CALL_KERNELS = {
     "prep_compress_kernel": ("prep_compress_kernel", "ring_store_kernel"),
+    "prep_logits_kernel": ("prep_logits_kernel",),
     "logits_valu_kernel": ("logits_valu_kernel", "logits_valu_list_kernel", "logits_mfma_kernel"),
     "topk_kernel": ("topk_kernel",),
     "gqa_partial_kernel": ("gqa_partial_kernel", "gqa_rowtile_kernel"),
@@ -73,6 +78,9 @@ def parse():
     p.add_argument("--row-tiles", action="store_true",
                    help="qsa_sparse_gqa's opt-in row-tiled prefill attention (32-row tiles of "
                         "one request share each loaded K/V window)")
+    p.add_argument("--separate-calls", action="store_true",
+                   help="run qsa_compress and qsa_index_logits_topk as two calls even when the "
+                        "batch qualifies for the combined call (its fused scoring launch)")
     p.add_argument("--graph", action="store_true",
                    help="also time the step captured in one HIP graph per input copy")
     p.add_argument("--profile-only", action="store_true",
@@ -102,12 +110,13 @@ def clone_workload(wl):
     return c
 
 
-def algorithmic_bytes(wl, packed):
+def algorithmic_bytes(wl, packed, combined=False):
     """Bytes each call must move at minimum (read + write), from the workload's shapes and the
     selection it produced.  Compressed keys count once per request (every visible key, read
     once); K/V count once per selected token per KV head (the union of a request's rows'
     selections; one row per request here); partials, logits scratch and re-reads are not
-    algorithmic."""
+    algorithmic.  `combined`: the step's first two calls are one (qsa_compress_index_logits_topk,
+    whose scoring kernel computes q_idx instead of reading it; the top-k reads it)."""
     import numpy as np
     T, Hi, Hq, Hkv = wl.num_tokens, wl.index_heads, wl.q_heads, wl.kv_heads
     elt = 1 if wl.index_dtype == "fp8" else 2
@@ -145,6 +154,15 @@ def algorithmic_bytes(wl, packed):
                   "topk_kernel": b_packed,                        # packed rows written
                   "gqa_partial_kernel": b_gqa - 2 * b_qgo,        # K/V, q, packed
                   "gqa_merge_kernel": 2 * b_qgo}                  # gate read, out written
+    if combined:
+        b_qidx = T * Hi * 128 * elt
+        per_call = {"qsa_compress_index_logits_topk": b_compress + b_logits,
+                    "qsa_sparse_gqa": b_gqa}
+        per_kernel.pop("prep_compress_kernel")
+        per_kernel.pop("logits_valu_kernel")
+        per_kernel = {"prep_logits_kernel": b_compress + b_logits - b_packed - b_qidx,
+                      "topk_kernel": b_packed + b_qidx, **{
+                          k: v for k, v in per_kernel.items() if k.startswith("gqa")}}
     return per_call, per_kernel, int(np.int64(kv_tokens))
 
 
@@ -548,9 +566,11 @@ def main():
         st.g_args.row_tiles = 1 if args.row_tiles else 0
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
+    # The combined prepare + selection call when the batch qualifies for its fused launch.
+    combined = steps[0].fused and not args.separate_calls
 
     for i in range(args.warmup):
-        steps[i % len(steps)].run(stream)
+        steps[i % len(steps)].run(stream, combined=combined)
     torch.cuda.synchronize()
 
     # ---- the timed region: exactly K steps
@@ -558,7 +578,7 @@ def main():
     torch.cuda.synchronize()
     ev0.record(stream)
     for i in range(args.steps):
-        steps[i % len(steps)].run(stream)
+        steps[i % len(steps)].run(stream, combined=combined)
     ev1.record(stream)
     torch.cuda.synchronize()
     ms_step = ev0.elapsed_time(ev1) / args.steps
@@ -572,7 +592,7 @@ def main():
     torch.cuda.synchronize()
     for i, (a, b) in enumerate(evs):
         a.record(stream)
-        steps[i % len(steps)].run(stream)
+        steps[i % len(steps)].run(stream, combined=combined)
         b.record(stream)
     torch.cuda.synchronize()
     import numpy as np
@@ -583,9 +603,11 @@ def main():
 
     # ---- per-call times (HIP events on the launch stream around each call)
     per_call = {}
-    for call in ("qsa_compress", "qsa_index_logits_topk", "qsa_sparse_gqa"):
-        fn = {"qsa_compress": "compress", "qsa_index_logits_topk": "topk",
-              "qsa_sparse_gqa": "gqa"}[call]
+    call_fns = ({"qsa_compress_index_logits_topk": "prep_topk", "qsa_sparse_gqa": "gqa"}
+                if combined else
+                {"qsa_compress": "compress", "qsa_index_logits_topk": "topk",
+                 "qsa_sparse_gqa": "gqa"})
+    for call, fn in call_fns.items():
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.steps)]
         torch.cuda.synchronize()
@@ -617,7 +639,11 @@ def main():
     windows = steps[0].t_ws.numel() < B.lib().qsa_index_logits_topk_workspace_size(
         ctypes.byref(uncapped))
     per_kernel = {}
+    skip = ({"prep_compress_kernel", "logits_valu_kernel"} if combined
+            else {"prep_logits_kernel"})
     for k, (fn, _) in KERNELS.items():
+        if k in skip:
+            continue    # the other form of the step's first two calls
         if windows and fn in ("logits", "block_topk"):
             continue    # the split top-k calls take one window only (the combined call is timed)
         per_kernel[k] = timed(fn)
@@ -634,7 +660,7 @@ def main():
         for st in steps:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                st.run()
+                st.run(combined=combined)
             graphs.append(g)
         torch.cuda.synchronize()
         for i in range(args.warmup):
@@ -675,7 +701,7 @@ def main():
                     "gbps_over_call": round(mbytes / (per_call["qsa_compress"] * 1e-6) / 1e9, 1)}
         del plain
 
-    alg, alg_k, kv_tokens = algorithmic_bytes(wl0, steps[0].packed)
+    alg, alg_k, kv_tokens = algorithmic_bytes(wl0, steps[0].packed, combined)
     if not merge_kernel:   # the attention kernel also reads the gate and writes the output
         alg_k["gqa_partial_kernel"] += alg_k.pop("gqa_merge_kernel")
     mfma_flop, mfma_flop_per_head = mfma_logits_flop(wl0, args.index_agg)
@@ -715,6 +741,7 @@ def main():
                    "main_prepare": bool(args.main_prepare), "index_agg": args.index_agg,
                    "max_logits_mb": args.max_logits_mb, "row_tiles": bool(args.row_tiles),
                    "topk_workspace_mb": round(steps[0].t_ws.numel() / 2**20, 1),
+                   "combined_prepare_call": combined,
                    "gqa_splits": steps[0].num_splits,
                    "gqa_merge_kernel": merge_kernel},
         "hbm_gbps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),

@@ -60,6 +60,25 @@ def test_algorithmic_bytes_count_each_selected_token_once_per_request():
             == per_call["qsa_sparse_gqa"])
 
 
+def test_combined_call_moves_the_bytes_of_the_two_calls_it_replaces():
+    wl = make_workload("decode_32k", num_requests=3, lengths=("fixed", 96), rows=1)
+    pk = _packed(wl, [[0, 1], [4], [8, 9, 10]])
+    sep, sep_k, _ = bench.algorithmic_bytes(wl, pk)
+    comb, comb_k, _ = bench.algorithmic_bytes(wl, pk, combined=True)
+    assert set(comb) == {"qsa_compress_index_logits_topk", "qsa_sparse_gqa"}
+    assert (comb["qsa_compress_index_logits_topk"]
+            == sep["qsa_compress"] + sep["qsa_index_logits_topk"])
+    assert comb["qsa_sparse_gqa"] == sep["qsa_sparse_gqa"]
+    # The fused scoring kernel computes q_idx instead of reading it; the top-k reads it.
+    q_idx = wl.num_tokens * wl.index_heads * 128 * 2
+    assert comb_k["prep_logits_kernel"] == (sep_k["prep_compress_kernel"]
+                                            + sep_k["logits_valu_kernel"] - q_idx)
+    assert comb_k["topk_kernel"] == sep_k["topk_kernel"] + q_idx
+    assert sum(comb_k.values()) == sum(comb.values())
+    assert set(comb_k) == {"prep_logits_kernel", "topk_kernel", "gqa_partial_kernel",
+                           "gqa_merge_kernel"}
+
+
 def test_algorithmic_bytes_use_one_byte_codes_for_fp8():
     wl8 = make_workload("decode_32k_fp8kv", num_requests=2, lengths=("fixed", 64), rows=1)
     picks = [[1, 2, 3], [4]]
