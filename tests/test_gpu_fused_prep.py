@@ -134,3 +134,39 @@ def test_combined_call_runs_the_two_calls_when_not_fused(name):
     sb.prep_topk()
     torch.cuda.synchronize()
     _assert_same_state(wa, sa, wb, sb)
+
+
+def test_combined_step_captured_in_a_graph_replays_the_eager_results():
+    """The fused launch makes no host synchronisation, allocation or memset either: a step with
+    the combined call, captured in a HIP graph, replays the eager results bit for bit, with
+    eager work on the same buffers in between."""
+    name, kw = FUSED["bf16"]
+    wl = make_workload(name, device="cuda", **kw)
+    st = QsaStep(wl)
+    assert st.fused
+    log(f"graph replay of the combined step: R={wl.num_requests}")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        st.run(side, combined=True)        # eager, on a side stream, before the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (st.packed, st.out, st.q_idx, wl.ckv, wl.ring)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st.run(combined=True)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        st.packed.fill_(-7)                # eager work between the replays
+        st.out.fill_(float("nan"))
+        st.q_idx.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        log(f"  replay {rep}")
+        for a, b in zip((st.packed, st.out, st.q_idx, wl.ckv, wl.ring), ref):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+        st.run(combined=True)              # an eager step between replays too
+        torch.cuda.synchronize()
+        assert torch.equal(st.packed, ref[0])
+    del g
