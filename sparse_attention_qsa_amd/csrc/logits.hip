@@ -200,9 +200,8 @@ void logits_valu_kernel(SelectParams P) {
   }
 }
 
-// Workgroups the chip holds at once: two per CU with up to two rows per chunk (four waves per
-// SIMD), one with four or more.
-constexpr int kCUs = 256;
+// Workgroups the chip holds at once (kCUs, qsa_internal.h): two per CU with up to two rows per
+// chunk (four waves per SIMD), one with four or more.
 
 // Workgroups per request of the wide instance (2048 keys each).
 int wide_tiles(const SelectParams& P) {

@@ -6,7 +6,8 @@
 // reference path and the scoring of qsa_select_paged_decode.
 //
 // Grid (workgroups per request, R), 512 threads: workgroup k of request r scores keys
-// 2048k .. 2048k+2047 of the request, as logits.hip's wide instance does.  Before scoring, it
+// 2048k .. 2048k+2047 of the request, as logits.hip's wide instance does (or 1024k .. 1024k+1023
+// for batches whose 1024-key workgroups fit the chip at one per CU).  Before scoring, it
 // computes the row's indexer Q itself (waves 0 .. ceil(Hi/4)-1, one head per 16-lane row, the
 // same float64 chain as qsa_compress) into LDS, instead of loading qsa_compress's output; the
 // workgroup that holds the key the step completes pools that group (wave 7) and substitutes its
@@ -22,12 +23,15 @@ namespace qsa {
 namespace {
 using namespace logits_tile;
 
-template <bool FP8>
+// TILES: 512-key tiles per workgroup, 4 (the wide layout) or 2 (1024-key workgroups, for
+// batches whose workgroups fit the chip at one per CU).
+template <bool FP8, int TILES>
 __global__ __launch_bounds__(kLogitsThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void prep_logits_kernel(SelectParams P, CompressParams C) {
   using KL = KeyLanes<FP8>;
   constexpr int kT = kLogitsThreads, kWaves = kLogitsThreads / 64;
-  constexpr int kTiles = 2 * kLogitsTilesPerWG;
+  constexpr int kTiles = TILES;
+  static_assert(TILES == 2 || TILES == 4, "two tiles are loaded before the prepare");
   constexpr int kKeys = kTiles * kLogitsKeysPerWG;
   static_assert(kLogitsKeysPerWG == kWaves * 64, "a tile is 64 keys per wave");
   __shared__ int32_t rows_s[kKeys];
@@ -277,6 +281,17 @@ void prep_logits_kernel(SelectParams P, CompressParams C) {
 
 }  // namespace
 
+namespace {
+// The fused kernel's tiles per workgroup for a call: 4 where the plain scoring would use the
+// wide layout, 2 where the call's 1024-key workgroups fit the chip at one per CU, else 0 (the
+// two calls run instead).
+int prep_logits_tiles(const SelectParams& P) {
+  if (logits_wide(P, 1, false)) return 4;
+  if ((int64_t)P.R * P.key_tiles <= kCUs && P.row_lo == 0 && P.row_hi == P.T) return 2;
+  return 0;
+}
+}  // namespace
+
 bool prep_logits_fusable(const qsa_compress_args& c, const qsa_topk_args& t) {
   // One row per request (row r is request r's: the rows' offsets start at 0 and no request
   // has more than one row), no main-attention prepare, plain-sum aggregation, one window, and
@@ -296,20 +311,24 @@ bool prep_logits_fusable(const qsa_compress_args& c, const qsa_topk_args& t) {
   if ((int64_t)c.max_query_len + c.compress_ratio - 2 >= c.ring_size) return false;
   const TopkLayout L = topk_layout(t);
   if (L.rows != t.num_tokens) return false;
-  return logits_wide(select_params(t, L, nullptr), 1, false);
+  return prep_logits_tiles(select_params(t, L, nullptr)) != 0;
 }
 
 hipError_t launch_prep_logits_topk(const qsa_compress_args& c, const qsa_topk_args& t,
                                    const TopkLayout& L, char* ws, hipStream_t s, Phase phase) {
   const SelectParams P = select_params(t, L, ws);
   const CompressParams C = compress_params(c);
-  const int tiles = (P.cols + 2 * kLogitsTilesPerWG * kLogitsKeysPerWG - 1) /
-                    (2 * kLogitsTilesPerWG * kLogitsKeysPerWG);
-  const dim3 grid(tiles, P.R), block(kLogitsThreads);
-  if (P.fp8)
-    hipLaunchKernelGGL(prep_logits_kernel<true>, grid, block, 0, s, P, C);
+  const int tiles = prep_logits_tiles(P);
+  const int keys = tiles * kLogitsKeysPerWG;
+  const dim3 grid((P.cols + keys - 1) / keys, P.R), block(kLogitsThreads);
+  if (tiles == 4 && P.fp8)
+    hipLaunchKernelGGL((prep_logits_kernel<true, 4>), grid, block, 0, s, P, C);
+  else if (tiles == 4)
+    hipLaunchKernelGGL((prep_logits_kernel<false, 4>), grid, block, 0, s, P, C);
+  else if (P.fp8)
+    hipLaunchKernelGGL((prep_logits_kernel<true, 2>), grid, block, 0, s, P, C);
   else
-    hipLaunchKernelGGL(prep_logits_kernel<false>, grid, block, 0, s, P, C);
+    hipLaunchKernelGGL((prep_logits_kernel<false, 2>), grid, block, 0, s, P, C);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || phase == Phase::kFirst) return e;
   return launch_topk_select(P, s);

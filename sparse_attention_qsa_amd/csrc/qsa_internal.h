@@ -35,6 +35,7 @@ struct TopkLayout {
   size_t total;
 };
 
+constexpr int kCUs = 256;              // compute units of an MI355X
 constexpr int kLogitsThreads = 512;    // VALU logits workgroup: 8 waves
 constexpr int kLogitsKeysPerWG = 512;  // keys per tile: 8 waves x 64 keys
 constexpr int kLogitsTilesPerWG = 2;   // tiles walked by one logits workgroup

@@ -235,9 +235,14 @@ def test_combined_prepare_and_selection_plan_and_invalid_calls():
     assert fused(_compress(main_qkv=None, max_query_len=2), _topk(max_query_len=2)) == 0
     assert fused(c, _topk(q_idx=FAKE + 256)) == 0                # the blocks disagree
     assert fused(c, _topk(c_block_table_width=256)) == 0
-    assert fused(c, _topk(max_seq_len=8192)) == 0                # 64 workgroups: too few
+    # 1024-key workgroups at one per CU: 64 x 2 and 32 x 8 fit the chip, 100 x 4 does not (and
+    # its 2048-key workgroups would not fill it).
+    assert fused(c, _topk(max_seq_len=8192)) == 1
     half = dict(num_tokens=32, num_requests=32)
-    assert fused(_compress(main_qkv=None, **half), _topk(num_decode_requests=32, **half)) == 0
+    assert fused(_compress(main_qkv=None, **half), _topk(num_decode_requests=32, **half)) == 1
+    odd = dict(num_tokens=100, num_requests=100)
+    assert fused(_compress(main_qkv=None, **odd),
+                 _topk(num_decode_requests=100, max_seq_len=16384, **odd)) == 0
     assert fused(_compress(main_qkv=None, head_dim=64), t) == -1
     assert fused(c, _topk(budget=3)) == -1
     call = lambda c, t, n=1 << 40, f=lib.qsa_compress_index_logits_topk: f(  # noqa: E731

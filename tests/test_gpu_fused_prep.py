@@ -15,8 +15,11 @@ from tests.gpu_util import SCALED, log, oracle_step, to_np
 pytestmark = pytest.mark.gpu
 
 # One-row batches the combined call fuses: 256 requests of at most 2,048 compressed keys (one
-# 2048-key workgroup each), or 64 of 8,192 (four each, the decode_32k step itself).
+# 2048-key workgroup each), 64 of 8,192 (four each, the decode_32k step itself), and batches
+# whose 1024-key workgroups fit the chip at one per CU (the small cases).
 FUSED = {
+    "bf16_small": ("decode_32k", dict(num_requests=64, lengths=("uniform", 5000, 8192))),
+    "fp8_small": ("fp8_decode", dict(num_requests=32, lengths=("uniform", 4096, 32768))),
     "bf16": ("decode_32k", dict(num_requests=256, lengths=("fixed", 8192))),
     # Lengths that are not multiples of c: some rows complete no group.
     "bf16_ragged": ("decode_32k", dict(num_requests=256, lengths=("uniform", 5000, 8192))),
@@ -57,7 +60,8 @@ def test_fused_prepare_equals_the_two_calls(case):
     _assert_same_state(wa, sa, wb, sb)
 
 
-@pytest.mark.parametrize("case", ["bf16", "bf16_ragged", "fp8_indexer", "mrope"])
+@pytest.mark.parametrize("case", ["bf16", "bf16_ragged", "fp8_indexer", "mrope", "bf16_small",
+                                  "fp8_small"])
 def test_fused_prepare_matches_the_oracle(case):
     name, kw = FUSED[case]
     wl = make_workload(name, device="cuda", **kw)
@@ -123,10 +127,11 @@ def test_split_prepare_then_block_topk_equals_the_combined_call():
     _assert_same_state(wa, sa, wb, sb)
 
 
-@pytest.mark.parametrize("name", ["decode_32k", "spec_verify_mrope", "chunked_prefill",
-                                  "fp8_decode"])
-def test_combined_call_runs_the_two_calls_when_not_fused(name):
-    (wa, sa), (wb, sb) = _pair(name, **SCALED[name])
+@pytest.mark.parametrize("name, kw", [("decode_32k", dict(rows=2)), ("spec_verify_mrope", {}),
+                                      ("chunked_prefill", {}),
+                                      ("decode_32k", dict(num_requests=300))])
+def test_combined_call_runs_the_two_calls_when_not_fused(name, kw):
+    (wa, sa), (wb, sb) = _pair(name, **{**SCALED[name], **kw})
     log(f"combined call, unfused {name}")
     assert not sb.fused
     sa.compress()
