@@ -1,9 +1,9 @@
-// Fused decode prepare + indexer logits: for a batch of one-row requests that fills the chip
-// with the wide vector-unit layout, one launch does the work of qsa_compress (the indexer Q
-// prep, the pooling of the group the step completes, the raw-key ring write) and of the wide
-// logits kernel (logits.hip), so the step has one launch and one dependency fewer.  Follows
-// QSAIndexer.forward (page "vllm.models.qwen4_exp.nvidia.qsa"): the prepare of its unfused
-// reference path and the scoring of qsa_select_paged_decode.
+// Fused decode prepare + indexer logits: for a batch of one-row requests whose scoring
+// workgroups fit the chip in one round, one launch does the work of qsa_compress (the indexer Q
+// prep, the pooling of the group the step completes, the raw-key ring write) and of the
+// vector-unit logits kernel (logits.hip), so the step has one launch and one dependency fewer.
+// Follows QSAIndexer.forward (page "vllm.models.qwen4_exp.nvidia.qsa"): the prepare of its
+// unfused reference path and the scoring of qsa_select_paged_decode.
 //
 // Grid (workgroups per request, R), 512 threads: workgroup k of request r scores keys
 // 2048k .. 2048k+2047 of the request, as logits.hip's wide instance does (or 1024k .. 1024k+1023
