@@ -67,6 +67,9 @@ void logits_valu_kernel(SelectParams P) {
   const int rb = WIN ? min(max(P.row_lo - q0, 0), n) : 0;
   const int re = WIN ? min(max(P.row_hi - q0, 0), n) : n;
   if (WIN && rb >= re) return;  // block-uniform, before any barrier
+  // A matrix-core request that began in an earlier window has its max |k| from that window's
+  // launch (the bound depends on the keys only), and none of its rows are scored here.
+  if (KMAX && WIN && n > P.mfma_min_rows && rb > 0) return;  // block-uniform
   // Barrier without a memory fence (a fence would wait for every load in flight); the LDS
   // writes before it are complete, and global loads are waited for where their data is used.
   auto barrier = [] {

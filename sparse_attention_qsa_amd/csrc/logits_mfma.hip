@@ -26,7 +26,7 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kMfmaRows = 128;         // rows per row block: 8 waves x 16 rows
 constexpr int kMfmaKeys = 256;         // keys per tile
-constexpr int kMfmaTilesPerItem = 8;   // key tiles per work item
+constexpr int kMfmaTilesPerItem = 8;   // key tiles per work item (at most)
 
 __device__ __forceinline__ void lds_dma16(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
@@ -102,8 +102,8 @@ __device__ __forceinline__ uint32_t claim_async(int* counter) {
 }
 
 // Persistent workgroups (one per CU; the LDS use allows no more) take work items from one
-// queue.  An item is (request, row block of 128 rows, up to eight consecutive 256-key tiles
-// the block sees); the items of every row block's first eight tiles come first, the later
+// queue.  An item is (request, row block of 128 rows, up to `tpi` <= 8 consecutive 256-key
+// tiles the block sees); the items of every row block's first tiles come first, the later
 // tiles of the longest rows next, so that the big items are claimed first.  The next item is
 // claimed when an item starts.
 //
@@ -124,7 +124,8 @@ __device__ __forceinline__ uint32_t claim_async(int* counter) {
 // read (exact: every e4m3 value is a bf16 value), Q is folded from its codes (exact in fp32),
 // and the contraction and its bound are those of the bf16 instance.
 template <bool F8>
-__global__ __launch_bounds__(512) void logits_mfma_kernel(SelectParams P, int row_blocks) {
+__global__ __launch_bounds__(512) void logits_mfma_kernel(SelectParams P, int row_blocks,
+                                                          int tpi) {
   using frag_t = std::conditional_t<F8, long, bf16x8_t>;  // 8 values of one operand row
   constexpr int kRowB = F8 ? 128 : 256;       // bytes of a key row
   constexpr int kChunks = kRowB / 16;         // its 16-byte chunks
@@ -142,7 +143,7 @@ __global__ __launch_bounds__(512) void logits_mfma_kernel(SelectParams P, int ro
   __shared__ __attribute__((aligned(16))) uint8_t stg[kMfmaRows / 16][16 * 128];
   __shared__ int s_item[2];
   const int key_tiles = (P.cols + kMfmaKeys - 1) / kMfmaKeys;
-  const int chunks = (key_tiles + kMfmaTilesPerItem - 1) / kMfmaTilesPerItem;
+  const int chunks = (key_tiles + tpi - 1) / tpi;
   const int per_chunk = P.R * row_blocks;
   const int64_t qlen = (int64_t)per_chunk * chunks;
 
@@ -198,8 +199,8 @@ __global__ __launch_bounds__(512) void logits_mfma_kernel(SelectParams P, int ro
     }
     if (nrows > 0) {
       const int vis_hi = min((pbase + whi) / P.c, P.cols);
-      t0 = chunk * kMfmaTilesPerItem;
-      t1 = min(t0 + kMfmaTilesPerItem, (vis_hi + kMfmaKeys - 1) / kMfmaKeys);
+      t0 = chunk * tpi;
+      t1 = min(t0 + tpi, (vis_hi + kMfmaKeys - 1) / kMfmaKeys);
     }
     if (t0 >= t1) {  // decode request, inert rows, or no tile of this chunk is seen
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the claim has returned
@@ -497,6 +498,18 @@ __global__ __launch_bounds__(512) void logits_mfma_kernel(SelectParams P, int ro
 
 }  // namespace
 
+// Tiles per item: eight (an item's setup, its claim and its block-table and Q round trips,
+// costs about as much as two tiles), halved while the launch's rows would make fewer items
+// than there are workgroups (a short call, or one window of a call under a logits cap), so
+// that the work still spreads over the chip.
+static int mfma_tiles_per_item(const SelectParams& P, unsigned workgroups) {
+  const int64_t blocks = ((int64_t)(P.row_hi - P.row_lo) + kMfmaRows - 1) / kMfmaRows;
+  const int key_tiles = (P.cols + kMfmaKeys - 1) / kMfmaKeys;
+  int tpi = kMfmaTilesPerItem;
+  while (tpi > 1 && blocks * ((key_tiles + tpi - 1) / tpi) < (int64_t)workgroups) tpi /= 2;
+  return tpi;
+}
+
 hipError_t launch_logits_mfma(const SelectParams& P, int max_query_len, hipStream_t s) {
   // One persistent workgroup per CU.
   static int cus[64] = {0};
@@ -511,10 +524,13 @@ hipError_t launch_logits_mfma(const SelectParams& P, int max_query_len, hipStrea
   }
   const int row_blocks = (max_query_len + kMfmaRows - 1) / kMfmaRows;
   const unsigned grid = (unsigned)cus[dev];
+  const int tpi = mfma_tiles_per_item(P, grid);
   if (P.fp8)
-    hipLaunchKernelGGL(logits_mfma_kernel<true>, dim3(grid), dim3(512), 0, s, P, row_blocks);
+    hipLaunchKernelGGL(logits_mfma_kernel<true>, dim3(grid), dim3(512), 0, s, P, row_blocks,
+                       tpi);
   else
-    hipLaunchKernelGGL(logits_mfma_kernel<false>, dim3(grid), dim3(512), 0, s, P, row_blocks);
+    hipLaunchKernelGGL(logits_mfma_kernel<false>, dim3(grid), dim3(512), 0, s, P, row_blocks,
+                       tpi);
   return hipGetLastError();
 }
 
