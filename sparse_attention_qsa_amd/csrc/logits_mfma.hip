@@ -142,12 +142,29 @@ __global__ __launch_bounds__(512) void logits_mfma_kernel(SelectParams P, int ro
   // instead of 16 rows x 32 bytes.  16-byte chunk c of row r sits in slot c ^ (r & 7).
   __shared__ __attribute__((aligned(16))) uint8_t stg[kMfmaRows / 16][16 * 128];
   __shared__ int s_item[2];
+  const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, l4 = lane >> 4;
   const int key_tiles = (P.cols + kMfmaKeys - 1) / kMfmaKeys;
   const int chunks = (key_tiles + tpi - 1) / tpi;
-  const int per_chunk = P.R * row_blocks;
+  // The queue covers the requests whose rows meet this launch's rows [row_lo, row_hi): r_lo ..
+  // r_lo + nreq - 1 (the requests' rows are consecutive and in order), and per request at
+  // most bw row blocks from rb_first (the first request's block holding row_lo, else 0).  A
+  // call that is one window covers every request and row block.
+  const bool windowed = P.row_lo > 0 || P.row_hi < P.T;
+  int r_lo = 0, nreq = P.R, bw = row_blocks;
+  if (windowed) {  // block-uniform
+    int before = 0, started = 0;
+    for (int b0 = 0; b0 < P.R; b0 += 512) {
+      const int i = b0 + tid;
+      before += __syncthreads_count(i < P.R && P.qsl[i + 1] <= P.row_lo);
+      started += __syncthreads_count(i < P.R && P.qsl[i] < P.row_hi);
+    }
+    r_lo = before;
+    nreq = max(started - before, 0);
+    bw = min(row_blocks, (P.row_hi - P.row_lo + kMfmaRows - 1) / kMfmaRows + 1);
+  }
+  const int per_chunk = nreq * bw;
   const int64_t qlen = (int64_t)per_chunk * chunks;
 
-  const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, l4 = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const char* ckv = reinterpret_cast<const char*>(P.ckv);
   const char* qb = reinterpret_cast<const char*>(P.q_idx);
@@ -183,10 +200,11 @@ __global__ __launch_bounds__(512) void logits_mfma_kernel(SelectParams P, int ro
     uint32_t next = 0;
     if (tid == 0) next = claim_async(&P.work[0]);
     const int chunk = (int)(item / per_chunk), jj = (int)(item % per_chunk);
-    const int r = jj % P.R;
-    const int rb = chunk == 0 ? jj / P.R : row_blocks - 1 - jj / P.R;
+    const int r = r_lo + jj % nreq;
     const int q0 = max(0, min(qsl_c[r], P.T));
     const int n = max(0, min(qsl_c[r + 1], P.T) - q0), L = sl_c[r];
+    const int rb_first = r == r_lo ? max(P.row_lo - q0, 0) / kMfmaRows : 0;
+    const int rb = rb_first + (chunk == 0 ? jj / nreq : bw - 1 - jj / nreq);
     int t0 = 0, t1 = 0, nrows = 0, pbase = 0, wlo = 0, whi = 0;
     if (n > P.mfma_min_rows && n <= L && rb * kMfmaRows < n) {
       nrows = min(kMfmaRows, n - rb * kMfmaRows);
