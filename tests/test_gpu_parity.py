@@ -226,6 +226,11 @@ def _cap_for_rows(wl, rows: int) -> int:
     ("decode_32k", 4, dict(rows=3)),
     ("fp8_decode", 3, dict(rows=2)),
     ("chunked_prefill_fp8", 100, {}),              # e4m3 max |k| pass in windows
+    # Decode and prefill requests in one call under a cap: windows that hold only decode rows,
+    # windows that start inside a prefill request (past its first 128-row block too), and
+    # windows holding the end of one prefill request and the start of the next.
+    ("decode_32k", 3, dict(num_requests=6, rows=(1, 1, 1, 1, 40, 24))),
+    ("decode_32k", 200, dict(num_requests=5, rows=(1, 1, 300, 1, 260))),
 ])
 def test_logits_cap_runs_in_windows_with_the_same_selection(name, rows, kw):
     """With a logits memory cap the call scores and selects window by window, reusing a
